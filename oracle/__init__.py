@@ -1,0 +1,200 @@
+"""fp64 CPU oracle for the KDA token mixer -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this package.  The product path (the HIP library under
+``gated_delta_rule_106_amd`` and its binding) never imports it, and the two
+share no code.
+
+The arithmetic lives in ``kda_oracle.c``: the plain token-by-token recurrence
+of Kimi Delta Attention in double precision (page "3T models are no longer
+magic", section "Gate 1: KDA makes it computable": forget per channel, delta
+rule corrective write, read the new state with the query, sigmoid output
+gate).  This module only builds that file with gcc and marshals arguments.
+
+Every input is passed as the exact bit pattern the GPU receives (float32 or
+bfloat16) and is widened exactly inside the C code; nothing here rounds,
+normalises or rescales.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import time
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "kda_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "libkda_oracle.so")
+_lib = None
+
+ORC_F32 = 0
+ORC_BF16 = 1
+LOG_ALPHA_MIN = -5.005647752585217  # ln 0.0067, the per-step retention floor
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (-O2, IEEE semantics, OpenMP)."""
+    global _lib
+    if force or not os.path.exists(_LIB_PATH):
+        tmp = _LIB_PATH + ".tmp"
+        cmd = ["gcc", "-O2", "-std=c99", "-fno-fast-math", "-ffp-contract=off", "-fopenmp",
+               "-shared", "-fPIC", _SRC, "-o", tmp, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB_PATH)
+        _lib = None
+    return _LIB_PATH
+
+
+def _open(path):
+    lib = ctypes.CDLL(path)
+    i64, vp, dp, ci = ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int
+    lib.kda_oracle_fwd.argtypes = [i64, i64, i64, i64, i64, ci, vp, vp, vp, vp, vp, vp,
+                                   dp, dp, dp, ci, ci]
+    lib.kda_oracle_fwd.restype = ci
+    lib.kda_oracle_decode.argtypes = [i64, i64, i64, i64, ci, vp, vp, vp, vp, vp, vp,
+                                      dp, dp, ci, ci]
+    lib.kda_oracle_decode.restype = ci
+    lib.kda_oracle_default_threads.argtypes = []
+    lib.kda_oracle_default_threads.restype = ci
+    return lib
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            build()
+        _lib = _open(_LIB_PATH)
+    return _lib
+
+
+def compile_variant(src_text: str, out_path: str):
+    """Compile a (modified) copy of the oracle source to ``out_path`` and return a
+    handle whose ``fwd``/``decode`` behave like this module's.  Used by the tests
+    that plant mistakes in the oracle and check that the pins catch them."""
+    src = out_path + ".c"
+    with open(src, "w") as f:
+        f.write(src_text)
+    subprocess.run(["gcc", "-O2", "-std=c99", "-fno-fast-math", "-ffp-contract=off", "-fopenmp",
+                    "-shared", "-fPIC", src, "-o", out_path, "-lm"], check=True)
+    lib = _open(out_path)
+
+    class _Handle:
+        def fwd(self, *a, **kw):
+            return fwd(*a, _lib_handle=lib, **kw)
+
+        def decode(self, *a, **kw):
+            return decode(*a, _lib_handle=lib, **kw)
+    return _Handle()
+
+
+def source_text() -> str:
+    with open(_SRC) as f:
+        return f.read()
+
+
+def default_threads() -> int:
+    return int(_load().kda_oracle_default_threads())
+
+
+def _raw(x):
+    """Return (contiguous numpy array of raw bits, dtype code) for a CPU tensor/array."""
+    try:
+        import torch
+        if isinstance(x, torch.Tensor):
+            x = x.detach().cpu().contiguous()
+            if x.dtype == torch.bfloat16:
+                return np.ascontiguousarray(x.view(torch.int16).numpy().view(np.uint16)), ORC_BF16
+            if x.dtype == torch.float32:
+                return np.ascontiguousarray(x.numpy()), ORC_F32
+            raise TypeError(f"oracle accepts float32 or bfloat16 tensors, got {x.dtype}")
+    except ImportError:  # pragma: no cover - torch is always present here
+        pass
+    x = np.asarray(x)
+    if x.dtype == np.float32:
+        return np.ascontiguousarray(x), ORC_F32
+    if x.dtype == np.uint16:  # raw bfloat16 bits
+        return np.ascontiguousarray(x), ORC_BF16
+    raise TypeError(f"oracle accepts float32 arrays or uint16 bfloat16 bits, got {x.dtype}")
+
+
+def _state64(s, shape):
+    if s is None:
+        return None
+    try:
+        import torch
+        if isinstance(s, torch.Tensor):
+            s = s.detach().cpu().to(torch.float64).numpy()
+    except ImportError:  # pragma: no cover
+        pass
+    s = np.ascontiguousarray(np.asarray(s, dtype=np.float64))
+    if s.shape != tuple(shape):
+        raise ValueError(f"state shape {s.shape} != {tuple(shape)}")
+    return s
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def fwd(q, k, v, log_alpha, beta, gate, initial_state=None, clamp=True, threads=0,
+        return_seconds=False, _lib_handle=None):
+    """Sequential fp64 recurrence over [B, T, H].
+
+    Returns ``(y, final_state)`` as float64 numpy arrays of shapes [B, T, H, Dv]
+    and [B, H, Dk, Dv] (and the wall time of the C call when
+    ``return_seconds``).
+    """
+    qa, dt = _raw(q)
+    ka, dt_k = _raw(k)
+    va, dt_v = _raw(v)
+    la, dt_l = _raw(log_alpha)
+    ba, dt_b = _raw(beta)
+    ga, dt_g = _raw(gate)
+    if len({dt, dt_k, dt_v, dt_l, dt_b, dt_g}) != 1:
+        raise TypeError("all oracle inputs must share one dtype")
+    B, T, H, Dk = qa.shape
+    Dv = va.shape[-1]
+    if ka.shape != (B, T, H, Dk) or la.shape != (B, T, H, Dk):
+        raise ValueError("q, k, log_alpha must be [B, T, H, Dk]")
+    if va.shape != (B, T, H, Dv) or ga.shape != (B, T, H, Dv) or ba.shape != (B, T, H):
+        raise ValueError("v, gate must be [B, T, H, Dv] and beta [B, T, H]")
+    s0 = _state64(initial_state, (B, H, Dk, Dv))
+    y = np.zeros((B, T, H, Dv), dtype=np.float64)
+    sT = np.zeros((B, H, Dk, Dv), dtype=np.float64)
+    t0 = time.perf_counter()
+    lib = _lib_handle if _lib_handle is not None else _load()
+    rc = lib.kda_oracle_fwd(B, T, H, Dk, Dv, dt, _ptr(qa), _ptr(ka), _ptr(va), _ptr(la),
+                            _ptr(ba), _ptr(ga), _ptr(s0), _ptr(y), _ptr(sT),
+                            1 if clamp else 0, int(threads))
+    secs = time.perf_counter() - t0
+    if rc != 0:
+        raise RuntimeError(f"kda_oracle_fwd failed with code {rc}")
+    return (y, sT, secs) if return_seconds else (y, sT)
+
+
+def decode(q, k, v, log_alpha, beta, gate, state, clamp=True, threads=0, _lib_handle=None):
+    """One recurrent step for every (b, h): inputs [B, H, D], beta [B, H].
+
+    ``state`` is [B, H, Dk, Dv] (any float type); returns ``(y, new_state)`` in
+    float64 without modifying the argument.
+    """
+    qa, dt = _raw(q)
+    ka, _ = _raw(k)
+    va, _ = _raw(v)
+    la, _ = _raw(log_alpha)
+    ba, _ = _raw(beta)
+    ga, _ = _raw(gate)
+    B, H, Dk = qa.shape
+    Dv = va.shape[-1]
+    s = _state64(state, (B, H, Dk, Dv)).copy()
+    y = np.zeros((B, H, Dv), dtype=np.float64)
+    lib = _lib_handle if _lib_handle is not None else _load()
+    rc = lib.kda_oracle_decode(B, H, Dk, Dv, dt, _ptr(qa), _ptr(ka), _ptr(va), _ptr(la),
+                               _ptr(ba), _ptr(ga), _ptr(s), _ptr(y), 1 if clamp else 0,
+                               int(threads))
+    if rc != 0:
+        raise RuntimeError(f"kda_oracle_decode failed with code {rc}")
+    return y, s

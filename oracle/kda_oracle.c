@@ -1,0 +1,187 @@
+/*
+ * KDA fp64 reference oracle -- TEST INFRASTRUCTURE ONLY.
+ *
+ * Only tests/, __graft_entry__.smoke() and bench.py's cpu_baseline leg may load
+ * or call this library.  The product path (the HIP library and its Python
+ * binding) never does; it shares no code, header, table or helper with it.
+ *
+ * What it computes: the Kimi Delta Attention (KDA) token mixer as the plain
+ * sequential token-by-token recurrence, in IEEE double precision, one
+ * (batch, head) sequence at a time.  Sources, by page and section:
+ *
+ *  - "3T models are no longer magic" (affta.cn/jrzx/86753.html), section
+ *    "Gate 1: KDA makes it computable": the per-token order of work is
+ *    control signals -> forget the old state -> corrective write scaled by
+ *    the update strength -> read the *new* state -> output gate.  The forget
+ *    gate is channel-wise (each state direction decays at its own rate), the
+ *    per-step retention has a floor of about 0.67 %, the write uses the delta
+ *    rule (read the state with the current key, compare with the new value,
+ *    write the correction), and the output gate filters the read-out channel
+ *    by channel.
+ *  - The algebraic form of that description: with D_t = Diag(alpha_t),
+ *        S_t = (I - beta_t k_t k_t^T) D_t S_{t-1} + beta_t k_t v_t^T,
+ *        o_t = S_t^T q_t,   y_t = o_t (.) sigmoid(z_t),
+ *    where S is a d_k x d_v matrix whose rows are indexed by key channels.
+ *
+ * Readings taken where the pages are silent (each is listed in the design doc):
+ *  - log alpha is clamped to [ln 0.0067, 0] when `clamp` is non-zero
+ *    (the retention floor, and retention never above 1);
+ *  - the gate is the logistic sigmoid of the given logits, no normalisation
+ *    of o before it;
+ *  - q and k arrive already normalised/scaled; nothing is applied here;
+ *  - a NULL initial state means zeros.
+ *
+ * Inputs are read as the exact bit patterns the GPU receives (fp32 or bf16)
+ * and widened exactly to double.  No blocking, chunking or reordering: the
+ * loop below is the definition.
+ *
+ * Layouts (row-major, contiguous):
+ *   q, k, log_alpha: [B, T, H, Dk]    v, gate, out: [B, T, H, Dv]
+ *   beta: [B, T, H]                   states: [B, H, Dk, Dv]
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define ORC_F32 0
+#define ORC_BF16 1
+
+/* Retention floor: per-step alpha >= 0.0067, so log alpha >= ln 0.0067. */
+static const double ORC_LOG_ALPHA_MIN = -5.005647752585217; /* log(0.0067) */
+
+/* Widen element i of a float32 or bfloat16 array to double (exact). */
+static double orc_load(const void *p, int dtype, int64_t i) {
+    if (dtype == ORC_F32) return (double)((const float *)p)[i];
+    uint32_t w = ((uint32_t)((const uint16_t *)p)[i]) << 16;
+    float f;
+    memcpy(&f, &w, sizeof f);
+    return (double)f;
+}
+
+/*
+ * Run the recurrence for one (b, h) sequence over tokens [0, T).
+ * S is d_k x d_v, updated in place.  Scratch r/u/o have d_v entries.
+ */
+static void orc_sequence(int64_t b, int64_t h, int64_t T, int64_t H, int64_t Dk,
+                         int64_t Dv, int dtype, const void *q, const void *k,
+                         const void *v, const void *la, const void *beta,
+                         const void *gate, double *S, double *out, int clamp,
+                         double *kv, double *qv, double *r, double *u, double *o) {
+    for (int64_t t = 0; t < T; ++t) {
+        const int64_t tok = (b * T + t) * H + h; /* index of (b, t, h) */
+        const double bt = orc_load(beta, dtype, tok);
+        for (int64_t c = 0; c < Dk; ++c) {
+            kv[c] = orc_load(k, dtype, tok * Dk + c);
+            qv[c] = orc_load(q, dtype, tok * Dk + c);
+        }
+        /* forget: S <- Diag(alpha_t) S, alpha_t = exp(log alpha_t) per key channel */
+        for (int64_t c = 0; c < Dk; ++c) {
+            double l = orc_load(la, dtype, tok * Dk + c);
+            if (clamp) {
+                if (l < ORC_LOG_ALPHA_MIN) l = ORC_LOG_ALPHA_MIN;
+                if (l > 0.0) l = 0.0;
+            }
+            const double a = exp(l);
+            double *row = S + c * Dv;
+            for (int64_t j = 0; j < Dv; ++j) row[j] *= a;
+        }
+        /* delta rule: read the decayed state with the key, r = S^T k */
+        for (int64_t j = 0; j < Dv; ++j) r[j] = 0.0;
+        for (int64_t c = 0; c < Dk; ++c) {
+            const double *row = S + c * Dv;
+            for (int64_t j = 0; j < Dv; ++j) r[j] += row[j] * kv[c];
+        }
+        /* compare with the new value, scale by the update strength */
+        for (int64_t j = 0; j < Dv; ++j)
+            u[j] = bt * (orc_load(v, dtype, tok * Dv + j) - r[j]);
+        /* corrective write: S <- S + k u^T */
+        for (int64_t c = 0; c < Dk; ++c) {
+            double *row = S + c * Dv;
+            for (int64_t j = 0; j < Dv; ++j) row[j] += kv[c] * u[j];
+        }
+        /* read the new state with the query, o = S^T q */
+        for (int64_t j = 0; j < Dv; ++j) o[j] = 0.0;
+        for (int64_t c = 0; c < Dk; ++c) {
+            const double *row = S + c * Dv;
+            for (int64_t j = 0; j < Dv; ++j) o[j] += row[j] * qv[c];
+        }
+        /* output gate: y = o * sigmoid(z), channel by channel */
+        for (int64_t j = 0; j < Dv; ++j) {
+            const double z = orc_load(gate, dtype, tok * Dv + j);
+            out[tok * Dv + j] = o[j] / (1.0 + exp(-z));
+        }
+    }
+}
+
+/* Number of OpenMP threads a call with nthreads <= 0 would use. */
+int kda_oracle_default_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+/*
+ * Full forward over [B, T, H].  init_state may be NULL (zeros); final_state
+ * may be NULL (not returned) and may alias init_state.  out is [B, T, H, Dv].
+ * Returns 0, or -1 on bad sizes / dtype, -2 on allocation failure.
+ */
+int kda_oracle_fwd(int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv,
+                   int dtype, const void *q, const void *k, const void *v,
+                   const void *log_alpha, const void *beta, const void *gate,
+                   const double *init_state, double *out, double *final_state,
+                   int clamp, int nthreads) {
+    if (B < 0 || T < 0 || H < 0 || Dk <= 0 || Dv <= 0) return -1;
+    if (dtype != ORC_F32 && dtype != ORC_BF16) return -1;
+    const int64_t units = B * H;
+    int failed = 0;
+#ifdef _OPENMP
+    if (nthreads <= 0) nthreads = omp_get_max_threads();
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads)
+#endif
+    for (int64_t unit = 0; unit < units; ++unit) {
+        const int64_t b = unit / H, h = unit % H;
+        double *S = (double *)malloc(sizeof(double) * (size_t)(Dk * Dv));
+        double *scratch = (double *)malloc(sizeof(double) * (size_t)(2 * Dk + 3 * Dv));
+        if (!S || !scratch) {
+            free(S);
+            free(scratch);
+#ifdef _OPENMP
+#pragma omp atomic write
+#endif
+            failed = 1;
+            continue;
+        }
+        const int64_t soff = unit * Dk * Dv;
+        if (init_state)
+            memcpy(S, init_state + soff, sizeof(double) * (size_t)(Dk * Dv));
+        else
+            memset(S, 0, sizeof(double) * (size_t)(Dk * Dv));
+        double *kv = scratch, *qv = kv + Dk, *r = qv + Dk, *u = r + Dv, *o = u + Dv;
+        orc_sequence(b, h, T, H, Dk, Dv, dtype, q, k, v, log_alpha, beta, gate, S,
+                     out, clamp, kv, qv, r, u, o);
+        if (final_state) memcpy(final_state + soff, S, sizeof(double) * (size_t)(Dk * Dv));
+        free(S);
+        free(scratch);
+    }
+    return failed ? -2 : 0;
+}
+
+/*
+ * One recurrent decode step for every (b, h): the same per-token update as
+ * above with T = 1.  q, k, log_alpha: [B, H, Dk]; v, gate, out: [B, H, Dv];
+ * beta: [B, H]; state: [B, H, Dk, Dv], read and written in place.
+ */
+int kda_oracle_decode(int64_t B, int64_t H, int64_t Dk, int64_t Dv, int dtype,
+                      const void *q, const void *k, const void *v,
+                      const void *log_alpha, const void *beta, const void *gate,
+                      double *state, double *out, int clamp, int nthreads) {
+    if (!state) return -1;
+    return kda_oracle_fwd(B, 1, H, Dk, Dv, dtype, q, k, v, log_alpha, beta, gate,
+                          state, out, state, clamp, nthreads);
+}

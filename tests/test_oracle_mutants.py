@@ -1,0 +1,68 @@
+"""Plant plausible mistakes in a copy of the oracle (on the CPU) and check that
+the pins catch every one of them, while the real oracle passes.
+
+Each mutant is a textual edit of ``oracle/kda_oracle.c`` compiled to a
+temporary library; the pins are the brute-force expansion (tests/_brute.py),
+the clamp semantics and the decode/prefill agreement.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from tests._brute import brute_fwd
+
+MUTANTS = {
+    "decay dropped": ("row[j] *= a;", "row[j] *= 1.0;"),
+    "wrong sign in the correction": ("- r[j]);", "+ r[j]);"),
+    "update strength dropped": ("u[j] = bt * (", "u[j] = ("),
+    "read with the key instead of the query": ("o[j] += row[j] * qv[c];",
+                                               "o[j] += row[j] * kv[c];"),
+    "query reads the state before the write": ("o[j] += row[j] * qv[c];",
+                                               "o[j] += (row[j] - kv[c] * u[j]) * qv[c];"),
+    "transposed corrective write": ("row[j] += kv[c] * u[j];",
+                                    "row[j] += kv[j % Dk] * u[c % Dv];"),
+    "delta read before the forget": ("r[j] += row[j] * kv[c];",
+                                     "r[j] += row[j] / exp(fmax(orc_load(la, dtype, tok * Dk + c),"
+                                     " ORC_LOG_ALPHA_MIN)) * kv[c];"),
+    "gate sign flipped": ("(1.0 + exp(-z))", "(1.0 + exp(z))"),
+    "retention floor missing": ("if (l < ORC_LOG_ALPHA_MIN) l = ORC_LOG_ALPHA_MIN;", ""),
+    "key of the previous token": ("kv[c] = orc_load(k, dtype, tok * Dk + c);",
+                                  "kv[c] = orc_load(k, dtype, (t > 0 ? tok - H : tok) * Dk + c);"),
+}
+
+
+def _pins_pass(handle) -> bool:
+    rng = np.random.default_rng(77)
+    B, T, H, Dk, Dv = 1, 6, 2, 4, 3
+    q = (rng.standard_normal((B, T, H, Dk)) * 0.5).astype(np.float32)
+    k = (rng.standard_normal((B, T, H, Dk)) * 0.5).astype(np.float32)
+    v = rng.standard_normal((B, T, H, Dv)).astype(np.float32)
+    la = rng.uniform(-8.0, 0.0, (B, T, H, Dk)).astype(np.float32)  # some below the floor
+    beta = rng.uniform(0.1, 0.9, (B, T, H)).astype(np.float32)
+    gate = rng.standard_normal((B, T, H, Dv)).astype(np.float32)
+    s0 = rng.standard_normal((B, H, Dk, Dv))
+    y, sT = handle.fwd(q, k, v, la, beta, gate, initial_state=s0)
+    yb, sb = brute_fwd(q, k, v, la, beta, gate, s0=s0)
+    if not (np.abs(y - yb).max() <= 1e-12 * np.abs(yb).max()
+            and np.abs(sT - sb).max() <= 1e-12 * np.abs(sb).max()):
+        return False
+    y1, s1 = handle.decode(*(np.ascontiguousarray(a[:, 0]) for a in (q, k, v, la, beta, gate)), s0)
+    yb1, sb1 = brute_fwd(*(a[:, :1] for a in (q, k, v, la, beta, gate)), s0=s0)
+    return bool(np.abs(y1 - yb1[:, 0]).max() <= 1e-12 * np.abs(yb1).max()
+                and np.abs(s1 - sb1).max() <= 1e-12 * np.abs(sb1).max())
+
+
+def test_real_oracle_passes_the_pins(oracle_lib):
+    class _Real:
+        fwd = staticmethod(oracle.fwd)
+        decode = staticmethod(oracle.decode)
+    assert _pins_pass(_Real())
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_planted_mistake_is_caught(tmp_path, name):
+    old, new = MUTANTS[name]
+    src = oracle.source_text()
+    assert src.count(old) == 1, f"mutation anchor for '{name}' must occur exactly once"
+    handle = oracle.compile_variant(src.replace(old, new), str(tmp_path / "mutant.so"))
+    assert not _pins_pass(handle), f"pins did not catch: {name}"
