@@ -1,0 +1,173 @@
+"""Kimi Delta Attention (KDA) token mixer on MI355X (gfx950).
+
+Thin Python binding over the C ABI in include/kda.h.  Every step of the
+computation runs in the HIP kernels of ``libkda.so``; this module only checks
+tensor metadata, allocates outputs and workspace with torch, and passes raw
+device pointers plus the current HIP stream.  There is no fallback: if the
+library is missing or a tensor is not on a GPU, the call raises.
+
+    y, final_state = chunk_fwd(q, k, v, log_alpha, beta, gate,
+                               initial_state=None, output_final_state=False, chunk=0)
+    y = decode_step(q, k, v, log_alpha, beta, gate, state)   # state updated in place
+
+Outputs are fp32 by default (``out_dtype``); bf16 outputs are available but
+their rounding alone exceeds a 2e-2 max-error-to-RMS budget on typical data.
+"""
+from __future__ import annotations
+
+import ctypes
+
+import torch
+
+from . import _abi
+
+__all__ = ["chunk_fwd", "decode_step", "workspace_bytes", "library_path", "KDAError"]
+
+
+class KDAError(RuntimeError):
+    def __init__(self, code: int, what: str):
+        super().__init__(f"{what}: {_abi.status_str(code)} (status {code})")
+        self.code = code
+
+
+def library_path() -> str:
+    return _abi.LIB_PATH
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return _abi.KDA_BF16
+    if t.dtype == torch.float32:
+        return _abi.KDA_F32
+    raise TypeError(f"KDA tensors must be bfloat16 or float32, got {t.dtype}")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _check_dev(ts, device):
+    for name, t in ts.items():
+        if t is None:
+            continue
+        if t.device != device:
+            raise ValueError(f"{name} is on {t.device}, expected {device}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+
+
+def _out_code(dt) -> int:
+    if dt == torch.float32:
+        return _abi.KDA_F32
+    if dt == torch.bfloat16:
+        return _abi.KDA_BF16
+    raise TypeError(f"out_dtype must be float32 or bfloat16, got {dt}")
+
+
+def _fwd_args(q, k, v, log_alpha, beta, gate, chunk, clamp, out_dtype):
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    if k.shape != q.shape or log_alpha.shape != q.shape:
+        raise ValueError("q, k, log_alpha must share the shape [B, T, H, Dk]")
+    if v.shape != (B, T, H, Dv) or gate.shape != (B, T, H, Dv) or beta.shape != (B, T, H):
+        raise ValueError("v, gate must be [B, T, H, Dv] and beta [B, T, H]")
+    code = _dtype_code(q)
+    for t in (k, v, log_alpha, beta, gate):
+        if t.dtype != q.dtype:
+            raise TypeError("q, k, v, log_alpha, beta and gate must share one dtype")
+    a = _abi.FwdArgs()
+    a.B, a.T, a.H, a.Dk, a.Dv = B, T, H, Dk, Dv
+    a.dtype, a.out_dtype, a.chunk = code, _out_code(out_dtype), int(chunk)
+    a.flags = 0 if clamp else _abi.KDA_FLAG_NO_CLAMP
+    return a
+
+
+def workspace_bytes(B, T, H, D, dtype=torch.bfloat16, chunk=0) -> int:
+    a = _abi.FwdArgs()
+    a.B, a.T, a.H, a.Dk, a.Dv = B, T, H, D, D
+    a.dtype = _abi.KDA_BF16 if dtype == torch.bfloat16 else _abi.KDA_F32
+    a.chunk = chunk
+    n = ctypes.c_size_t(0)
+    rc = _abi.load().kda_chunk_fwd_workspace_size(ctypes.byref(a), ctypes.byref(n))
+    if rc != _abi.KDA_OK:
+        raise KDAError(rc, "kda_chunk_fwd_workspace_size")
+    return int(n.value)
+
+
+def chunk_fwd(q, k, v, log_alpha, beta, gate, initial_state=None, output_final_state=False,
+              chunk=0, clamp=True, out_dtype=torch.float32, out=None, final_state=None,
+              workspace=None):
+    """Chunkwise-parallel KDA forward on the current HIP stream.
+
+    q, k, log_alpha: [B, T, H, Dk]; v, gate: [B, T, H, Dv]; beta: [B, T, H];
+    all bf16 or all fp32, contiguous, on one GPU.  initial_state: fp32
+    [B, H, Dk, Dv] or None.  Returns (y, final_state or None); y has
+    ``out_dtype`` (fp32 by default).
+    """
+    lib = _abi.load()
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("chunk_fwd needs GPU tensors (the HIP kernels are the only implementation)")
+    a = _fwd_args(q, k, v, log_alpha, beta, gate, chunk, clamp, out_dtype)
+    B, T, H, Dk, Dv = a.B, a.T, a.H, a.Dk, a.Dv
+    if initial_state is not None and (initial_state.dtype != torch.float32 or
+                                      tuple(initial_state.shape) != (B, H, Dk, Dv)):
+        raise ValueError("initial_state must be fp32 [B, H, Dk, Dv]")
+    if out is None:
+        out = torch.empty((B, T, H, Dv), dtype=out_dtype, device=dev)
+    elif out.dtype != out_dtype or tuple(out.shape) != (B, T, H, Dv):
+        raise ValueError("out must be [B, T, H, Dv] of out_dtype")
+    if output_final_state and final_state is None:
+        final_state = torch.empty((B, H, Dk, Dv), dtype=torch.float32, device=dev)
+    n = ctypes.c_size_t(0)
+    rc = lib.kda_chunk_fwd_workspace_size(ctypes.byref(a), ctypes.byref(n))
+    if rc != _abi.KDA_OK:
+        raise KDAError(rc, "kda_chunk_fwd_workspace_size")
+    if workspace is None or workspace.numel() < n.value:
+        workspace = torch.empty(max(int(n.value), 16), dtype=torch.uint8, device=dev)
+    _check_dev(dict(q=q, k=k, v=v, log_alpha=log_alpha, beta=beta, gate=gate, out=out,
+                    initial_state=initial_state, final_state=final_state), dev)
+    a.q, a.k, a.v = _ptr(q), _ptr(k), _ptr(v)
+    a.log_alpha, a.beta, a.gate, a.out = _ptr(log_alpha), _ptr(beta), _ptr(gate), _ptr(out)
+    a.initial_state = _ptr(initial_state)
+    a.final_state = _ptr(final_state) if output_final_state else None
+    a.workspace, a.workspace_bytes = _ptr(workspace), workspace.numel()
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    rc = lib.kda_chunk_fwd(ctypes.byref(a), ctypes.c_void_p(stream))
+    if rc != _abi.KDA_OK:
+        raise KDAError(rc, "kda_chunk_fwd")
+    return out, (final_state if output_final_state else None)
+
+
+def decode_step(q, k, v, log_alpha, beta, gate, state, clamp=True, out_dtype=torch.float32,
+                out=None):
+    """One recurrent KDA token per (b, h) on the current HIP stream.
+
+    q, k, log_alpha: [B, H, Dk]; v, gate: [B, H, Dv]; beta: [B, H]; state: fp32
+    [B, H, Dk, Dv], updated in place.  Returns y [B, H, Dv].
+    """
+    lib = _abi.load()
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("decode_step needs GPU tensors (the HIP kernels are the only implementation)")
+    B, H, Dk = q.shape
+    Dv = v.shape[-1]
+    if state.dtype != torch.float32 or tuple(state.shape) != (B, H, Dk, Dv):
+        raise ValueError("state must be fp32 [B, H, Dk, Dv]")
+    code = _dtype_code(q)
+    if out is None:
+        out = torch.empty((B, H, Dv), dtype=out_dtype, device=dev)
+    elif out.dtype != out_dtype or tuple(out.shape) != (B, H, Dv):
+        raise ValueError("out must be [B, H, Dv] of out_dtype")
+    _check_dev(dict(q=q, k=k, v=v, log_alpha=log_alpha, beta=beta, gate=gate, state=state, out=out), dev)
+    a = _abi.DecodeArgs()
+    a.B, a.H, a.Dk, a.Dv, a.dtype, a.out_dtype = B, H, Dk, Dv, code, _out_code(out_dtype)
+    a.flags = 0 if clamp else _abi.KDA_FLAG_NO_CLAMP
+    a.q, a.k, a.v = _ptr(q), _ptr(k), _ptr(v)
+    a.log_alpha, a.beta, a.gate = _ptr(log_alpha), _ptr(beta), _ptr(gate)
+    a.out, a.state = _ptr(out), _ptr(state)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    rc = lib.kda_decode_step(ctypes.byref(a), ctypes.c_void_p(stream))
+    if rc != _abi.KDA_OK:
+        raise KDAError(rc, "kda_decode_step")
+    return out

@@ -1,0 +1,140 @@
+// C ABI of the KDA library: host-side validation, workspace sizing, dispatch.
+// Every check runs before the first HIP call; see include/kda.h for the contract.
+#include <limits.h>
+
+#include "../../include/kda.h"
+#include "kda_decode.h"
+#include "kda_prefill.h"
+
+namespace {
+
+constexpr int kDefaultChunkBf16 = 64;
+constexpr int kDefaultChunkF32 = 16;
+
+bool mul_ok(int64_t a, int64_t b, int64_t* out) {
+    if (a < 0 || b < 0) return false;
+    if (a != 0 && b > INT64_MAX / a) return false;
+    *out = a * b;
+    return true;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int resolve_chunk(const kda_fwd_args* a) {
+    if (a->chunk != 0) return a->chunk;
+    return a->dtype == KDA_BF16 ? kDefaultChunkBf16 : kDefaultChunkF32;
+}
+
+// Sizes, dtype, head size, chunk and flags; fills the chunk count and card size.
+int check_shape(const kda_fwd_args* a, int* chunk, int64_t* nchunks, int64_t* card) {
+    if (!a) return KDA_ERR_NULL;
+    if (a->B < 0 || a->T < 0 || a->H < 0 || a->Dk <= 0 || a->Dv <= 0) return KDA_ERR_SHAPE;
+    if (a->dtype != KDA_F32 && a->dtype != KDA_BF16) return KDA_ERR_UNSUPPORTED;
+    if (a->Dk != a->Dv || (a->Dk != 64 && a->Dk != 128)) return KDA_ERR_UNSUPPORTED;
+    if (a->out_dtype != KDA_F32 && a->out_dtype != KDA_BF16) return KDA_ERR_UNSUPPORTED;
+    if ((a->flags & ~KDA_FLAG_NO_CLAMP) != 0) return KDA_ERR_UNSUPPORTED;
+    const int c = resolve_chunk(a);
+    if (!kda::prefill_supported(a->dtype == KDA_BF16, c, (int)a->Dk)) return KDA_ERR_UNSUPPORTED;
+    // every element index of every tensor must fit in int64
+    int64_t bt, bth, elems, bh, st;
+    if (!mul_ok(a->B, a->T, &bt) || !mul_ok(bt, a->H, &bth) || !mul_ok(bth, a->Dk, &elems) ||
+        !mul_ok(a->B, a->H, &bh) || !mul_ok(bh, a->Dk * a->Dv, &st))
+        return KDA_ERR_SHAPE;
+    if (a->H > INT_MAX || bh > INT_MAX) return KDA_ERR_SHAPE;  // grid dimensions
+    const int64_t nc = (a->T + c - 1) / c;
+    if (nc > INT_MAX) return KDA_ERR_SHAPE;
+    const int64_t cb = kda::prefill_card_bytes(a->dtype == KDA_BF16, c, (int)a->Dk);
+    int64_t tmp, total;
+    if (cb <= 0 || !mul_ok(bh, nc, &tmp) || !mul_ok(tmp, cb, &total)) return KDA_ERR_SHAPE;
+    *chunk = c;
+    *nchunks = nc;
+    *card = cb;
+    return KDA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int kda_version(void) { return KDA_VERSION; }
+
+const char* kda_status_str(int status) {
+    switch (status) {
+        case KDA_OK: return "ok";
+        case KDA_ERR_NULL: return "a required pointer is NULL";
+        case KDA_ERR_SHAPE: return "negative or overflowing sizes";
+        case KDA_ERR_UNSUPPORTED: return "unsupported head size, dtype, chunk size or flag";
+        case KDA_ERR_WORKSPACE: return "workspace missing or too small";
+        case KDA_ERR_ALIGN: return "a pointer is not 16-byte aligned";
+        case KDA_ERR_HIP: return "the HIP runtime reported a launch error";
+        default: return "unknown status";
+    }
+}
+
+int kda_chunk_fwd_workspace_size(const kda_fwd_args* a, size_t* bytes) {
+    if (!a || !bytes) return KDA_ERR_NULL;
+    int c;
+    int64_t nc, cb;
+    const int st = check_shape(a, &c, &nc, &cb);
+    if (st != KDA_OK) return st;
+    *bytes = (size_t)(a->B * a->H * nc * cb);
+    return KDA_OK;
+}
+
+int kda_chunk_fwd(const kda_fwd_args* a, hipStream_t stream) {
+    if (!a) return KDA_ERR_NULL;
+    int c;
+    int64_t nc, cb;
+    int st = check_shape(a, &c, &nc, &cb);
+    if (st != KDA_OK) return st;
+    const bool has_tokens = a->B * a->T * a->H > 0;
+    if (has_tokens) {
+        const void* req[] = {a->q, a->k, a->v, a->log_alpha, a->beta, a->gate, a->out};
+        for (const void* p : req)
+            if (!p) return KDA_ERR_NULL;
+        for (const void* p : req)
+            if (!aligned16(p)) return KDA_ERR_ALIGN;
+    }
+    if (!aligned16(a->initial_state) || !aligned16(a->final_state)) return KDA_ERR_ALIGN;
+    const int64_t need = a->B * a->H * nc * cb;
+    if (need > 0) {
+        if (!a->workspace) return KDA_ERR_WORKSPACE;
+        if ((int64_t)a->workspace_bytes < need) return KDA_ERR_WORKSPACE;
+        if (!aligned16(a->workspace)) return KDA_ERR_ALIGN;
+    }
+    if (a->B * a->H == 0) return KDA_OK;
+    if (!has_tokens && !a->final_state) return KDA_OK;
+
+    kda::PrepParams pp{a->q, a->k, a->v, a->log_alpha, a->beta, a->workspace,
+                       a->B, a->T, a->H, nc, (a->flags & KDA_FLAG_NO_CLAMP) ? 0 : 1};
+    kda::RecurParams rp{a->gate, a->out, a->initial_state, a->final_state, a->workspace,
+                        a->B, a->T, a->H, nc};
+    const hipError_t e = kda::launch_prefill(a->dtype == KDA_BF16, a->out_dtype == KDA_BF16, c,
+                                             (int)a->Dk, pp, rp, stream);
+    return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+int kda_decode_step(const kda_decode_args* a, hipStream_t stream) {
+    if (!a) return KDA_ERR_NULL;
+    if (a->B < 0 || a->H < 0 || a->Dk <= 0 || a->Dv <= 0) return KDA_ERR_SHAPE;
+    if (a->dtype != KDA_F32 && a->dtype != KDA_BF16) return KDA_ERR_UNSUPPORTED;
+    if (a->Dk != a->Dv || (a->Dk != 64 && a->Dk != 128)) return KDA_ERR_UNSUPPORTED;
+    if (a->out_dtype != KDA_F32 && a->out_dtype != KDA_BF16) return KDA_ERR_UNSUPPORTED;
+    if ((a->flags & ~KDA_FLAG_NO_CLAMP) != 0 || a->reserved != 0) return KDA_ERR_UNSUPPORTED;
+    int64_t bh, st;
+    if (!mul_ok(a->B, a->H, &bh) || !mul_ok(bh, a->Dk * a->Dv, &st)) return KDA_ERR_SHAPE;
+    if (bh > INT_MAX) return KDA_ERR_SHAPE;
+    if (bh == 0) return KDA_OK;
+    const void* req[] = {a->q, a->k, a->v, a->log_alpha, a->beta, a->gate, a->out, a->state};
+    for (const void* p : req)
+        if (!p) return KDA_ERR_NULL;
+    for (const void* p : req)
+        if (!aligned16(p)) return KDA_ERR_ALIGN;
+    kda::DecodeParams p{a->q, a->k, a->v, a->log_alpha, a->beta, a->gate, a->out, a->state,
+                        bh, (a->flags & KDA_FLAG_NO_CLAMP) ? 0 : 1};
+    const hipError_t e =
+        kda::launch_decode(a->dtype == KDA_BF16, a->out_dtype == KDA_BF16, (int)a->Dk, p, stream);
+    return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,88 @@
+// Device-side building blocks shared by the KDA kernels (gfx950 / CDNA4).
+//
+// MFMA lane layouts used throughout (wave64, lane l, row-of-16 m = l % 16,
+// lane group g = l / 16):
+//   v_mfma_f32_16x16x32_{f16,bf16}: A[m][8g + j], B[8g + j][m], j = 0..7
+//   v_mfma_f32_16x16x16_f16       : A[m][4g + j], B[4g + j][m], j = 0..3
+//   v_mfma_f32_16x16x4_f32        : A[m][g],      B[g][m]
+//   accumulator (all of the above): acc[i] = D[4g + i][m], i = 0..3
+// Because a contraction may visit its K index in any order as long as both
+// operands agree, a 16x16 accumulator tile (rows 4g..4g+3 held by lane group
+// g) can feed the next MFMA as its K-major operand directly: two stacked tiles
+// form one K = 32 step whose logical k = 8g + j maps to physical row
+// 4g + j (j < 4, first tile) or 16 + 4g + (j - 4) (second tile).  The other
+// operand is then read with the same permutation.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kda {
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef _Float16 half4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+// ln(0.0067): the per-step retention floor, in natural-log units.
+constexpr float kLogAlphaMin = -5.005647752585217f;
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+__device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
+
+// exp2 on the hardware transcendental unit (v_exp_f32).
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ float bf16_bits_to_float(uint16_t u) {
+    return __uint_as_float(static_cast<uint32_t>(u) << 16);
+}
+
+// Input element loaders: the public dtypes are fp32 and bf16 (raw 16-bit words).
+struct InF32 {
+    using raw_t = float;
+    static __device__ __forceinline__ float load(const raw_t* p, int64_t i) { return p[i]; }
+    static __device__ __forceinline__ raw_t from_float(float x) { return x; }
+};
+struct InBF16 {
+    using raw_t = uint16_t;
+    static __device__ __forceinline__ float load(const raw_t* p, int64_t i) {
+        return bf16_bits_to_float(p[i]);
+    }
+    static __device__ __forceinline__ raw_t from_float(float x) {
+        __bf16 h = static_cast<__bf16>(x);  // round to nearest even
+        return __builtin_bit_cast(uint16_t, h);
+    }
+};
+
+__device__ __forceinline__ floatx4 zero4() { return floatx4{0.f, 0.f, 0.f, 0.f}; }
+
+__device__ __forceinline__ floatx4 mma_f16_k32(const half8& a, const half8& b, floatx4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ floatx4 mma_f16_k16(const half4& a, const half4& b, floatx4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ floatx4 mma_bf16_k32(const bf16x8& a, const bf16x8& b, floatx4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ floatx4 mma_f32_k4(float a, float b, floatx4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// Split x into bf16 hi + lo with x ~= hi + lo to about 16 significant bits.
+__device__ __forceinline__ void split_bf16(float x, __bf16& hi, __bf16& lo) {
+    hi = static_cast<__bf16>(x);
+    lo = static_cast<__bf16>(x - static_cast<float>(hi));
+}
+
+__device__ __forceinline__ float sigmoidf_(float z) {
+    return 1.0f / (1.0f + fast_exp2(-z * kLog2e));
+}
+
+// Clamp of log(alpha) to [ln 0.0067, 0] (retention floor and retention <= 1).
+__device__ __forceinline__ float clamp_log_alpha(float l, bool clamp) {
+    return clamp ? fminf(fmaxf(l, kLogAlphaMin), 0.0f) : l;
+}
+
+}  // namespace kda

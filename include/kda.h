@@ -1,0 +1,155 @@
+/*
+ * kda.h -- C ABI of the MI355X (gfx950) Kimi Delta Attention (KDA) token mixer.
+ *
+ * What is computed (page "3T models are no longer magic", affta.cn/jrzx/86753.html,
+ * section "Gate 1: KDA makes it computable"): for every (batch b, head h) a
+ * fixed-size d_k x d_v fp32 state S is carried over the tokens.  Each token
+ *   1. forgets channel-wise:      S <- Diag(alpha_t) S, alpha_t = exp(log_alpha_t),
+ *                                 with per-step retention floored at 0.67 %
+ *                                 (log_alpha clamped to [ln 0.0067, 0]);
+ *   2. writes with the delta rule: u_t = beta_t (v_t - S^T k_t),  S <- S + k_t u_t^T,
+ *                                 i.e. S_t = (I - beta_t k_t k_t^T) Diag(alpha_t) S_{t-1}
+ *                                           + beta_t k_t v_t^T;
+ *   3. reads the new state:        o_t = S_t^T q_t;
+ *   4. gates the read-out:         y_t = o_t * sigmoid(z_t), channel by channel.
+ * The rows of S are key channels (d_k), the columns value channels (d_v).
+ *
+ * kda_chunk_fwd evaluates this over whole sequences in the chunkwise-parallel
+ * form (page "Kimi K3 report walk-through", prism.simon-ai.net/article/6740,
+ * sections "Compute paradigm" and "Hierarchical chunking of linear attention":
+ * parallel inside a chunk, recurrent across chunks, with the result independent
+ * of the chunk size; decay factors are kept inside the BF16 range by 16-token
+ * tiles, section "Numerical stability & co-design").  kda_decode_step performs
+ * one recurrent token step on a stored state.
+ *
+ * Conventions shared by every entry point
+ *  - Tensors are dense, row-major, device-resident and 16-byte aligned.
+ *  - Token tensors are token-major: q, k, log_alpha [B, T, H, Dk];
+ *    v, gate, out [B, T, H, Dv]; beta [B, T, H] (decode: the same without T).
+ *  - dtype applies to q, k, v, log_alpha, beta and gate (all the same type);
+ *    out_dtype selects the type of out independently (KDA_F32 = 0 is the
+ *    zero-initialised default).  With bf16 inputs an fp32 output is what
+ *    meets a max-abs error of 2e-2 of the output RMS: rounding even the exact
+ *    result to bf16 already costs about 2.8e-2 on these outputs, whose peaks
+ *    are ~10x their RMS.  States are always fp32 [B, H, Dk, Dv].
+ *  - Supported head sizes: Dk == Dv, 64 or 128.
+ *  - The caller owns every buffer.  The library allocates nothing, keeps no
+ *    global mutable state and is reentrant; calls on distinct streams may run
+ *    concurrently.  Work is enqueued on `stream` and the call returns without
+ *    synchronising; results are valid once the stream has completed.
+ *  - Arguments are validated on the host before any HIP call; on failure the
+ *    call returns a negative status and touches no memory.  A launch error
+ *    reported by the runtime returns KDA_ERR_HIP.  The library never aborts,
+ *    prints or throws.
+ *  - Non-finite inputs are not checked for; they propagate.
+ */
+#ifndef KDA_H
+#define KDA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KDA_VERSION 1
+
+/* element types */
+#define KDA_F32 0  /* IEEE binary32 */
+#define KDA_BF16 1 /* bfloat16 */
+
+/* status codes */
+#define KDA_OK 0
+#define KDA_ERR_NULL (-1)        /* a required pointer is NULL */
+#define KDA_ERR_SHAPE (-2)       /* negative or overflowing sizes */
+#define KDA_ERR_UNSUPPORTED (-3) /* head size, dtype, chunk or flag not supported */
+#define KDA_ERR_WORKSPACE (-4)   /* workspace missing or too small */
+#define KDA_ERR_ALIGN (-5)       /* a pointer is not 16-byte aligned */
+#define KDA_ERR_HIP (-6)         /* the HIP runtime reported a launch error */
+
+/* flags */
+#define KDA_FLAG_NO_CLAMP 1u /* use log_alpha as given (no clamp to [ln 0.0067, 0]) */
+
+/*
+ * Arguments of kda_chunk_fwd.
+ *   chunk: tokens per chunk; 0 selects the default (64 for bf16 inputs, 16 for
+ *     fp32 inputs); otherwise 16, 32 or 64 (fp32 inputs with Dk = 128 allow 16
+ *     and 32).  The result does not depend on it beyond rounding.
+ *   initial_state: fp32 [B, H, Dk, Dv] or NULL (zeros).
+ *   final_state:   fp32 [B, H, Dk, Dv] or NULL (not returned).  It may alias
+ *     initial_state (in-place continuation).
+ *   workspace: device scratch of at least kda_chunk_fwd_workspace_size()
+ *     bytes (may be NULL when that size is 0).  Its contents on entry do not
+ *     matter and on return are unspecified.
+ *   T may be any value >= 0; a last partial chunk is handled exactly.  For
+ *   T == 0 nothing is written to out and final_state receives initial_state
+ *   (or zeros).
+ */
+typedef struct kda_fwd_args {
+    int64_t B, T, H, Dk, Dv;
+    int32_t dtype;     /* KDA_F32 or KDA_BF16: q, k, v, log_alpha, beta, gate */
+    int32_t out_dtype; /* KDA_F32 or KDA_BF16: out */
+    int32_t chunk;
+    uint32_t flags;
+    const void *q;
+    const void *k;
+    const void *v;
+    const void *log_alpha;
+    const void *beta;
+    const void *gate; /* output-gate logits; sigmoid is applied inside */
+    void *out;
+    const float *initial_state;
+    float *final_state;
+    void *workspace;
+    size_t workspace_bytes;
+} kda_fwd_args;
+
+/*
+ * Host-only query: bytes of device workspace kda_chunk_fwd needs for these
+ * sizes, dtype and chunk (pointers in *a are not inspected).  Returns a status.
+ */
+int kda_chunk_fwd_workspace_size(const kda_fwd_args *a, size_t *bytes);
+
+/* Chunkwise-parallel forward over whole sequences (prefill).  Returns a status. */
+int kda_chunk_fwd(const kda_fwd_args *a, hipStream_t stream);
+
+/*
+ * Arguments of kda_decode_step: one token per (b, h).
+ *   q, k, log_alpha: [B, H, Dk]; v, gate, out: [B, H, Dv]; beta: [B, H];
+ *   state: fp32 [B, H, Dk, Dv], required, read and overwritten in place with
+ *   the state after this token (same layout as kda_fwd_args' states, so a
+ *   prefill's final state continues directly into decode).
+ */
+typedef struct kda_decode_args {
+    int64_t B, H, Dk, Dv;
+    int32_t dtype;     /* inputs */
+    int32_t out_dtype; /* out */
+    uint32_t flags;
+    uint32_t reserved; /* must be 0 */
+    const void *q;
+    const void *k;
+    const void *v;
+    const void *log_alpha;
+    const void *beta;
+    const void *gate;
+    void *out;
+    float *state;
+} kda_decode_args;
+
+/* Single-token recurrent step, state updated in place.  Returns a status. */
+int kda_decode_step(const kda_decode_args *a, hipStream_t stream);
+
+/* Static description of a status code (never NULL). */
+const char *kda_status_str(int status);
+
+/* KDA_VERSION of the built library. */
+int kda_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H */

@@ -1,0 +1,173 @@
+"""The C-ABI library: it loads, exports every symbol include/kda.h declares, its
+structs match the header byte for byte, and host-side validation rejects bad
+arguments before any HIP call (so these run without a GPU)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from gated_delta_rule_106_amd import _abi
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kda.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _abi.load()
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:int|const char \*)\s*(kda_\w+)\s*\(", text, re.M)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = _declared()
+    assert set(names) == set(_abi.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", _abi.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (kda_\w+)", out))
+    assert set(names) <= exported
+
+
+def test_version_and_status_strings(lib):
+    assert lib.kda_version() == 1
+    for code in range(-6, 1):
+        assert lib.kda_status_str(code).decode()
+    assert lib.kda_status_str(12345).decode() == "unknown status"
+
+
+def test_struct_layout_matches_header(tmp_path):
+    src = tmp_path / "layout.c"
+    src.write_text(r'''
+#include <stdio.h>
+#include <stddef.h>
+#include "kda.h"
+int main(void) {
+  printf("%zu %zu %zu %zu %zu %zu\n", sizeof(kda_fwd_args), offsetof(kda_fwd_args, q),
+         offsetof(kda_fwd_args, workspace_bytes), sizeof(kda_decode_args),
+         offsetof(kda_decode_args, q), offsetof(kda_decode_args, state));
+  return 0;
+}''')
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-D__HIP_PLATFORM_AMD__", "-I" + os.path.join(ROOT, "include"),
+                    "-I/opt/rocm/include", str(src), "-o", str(exe)], check=True)
+    got = [int(x) for x in subprocess.run([str(exe)], capture_output=True, text=True,
+                                          check=True).stdout.split()]
+    want = [ctypes.sizeof(_abi.FwdArgs), _abi.FwdArgs.q.offset, _abi.FwdArgs.workspace_bytes.offset,
+            ctypes.sizeof(_abi.DecodeArgs), _abi.DecodeArgs.q.offset, _abi.DecodeArgs.state.offset]
+    assert got == want
+
+
+def _good_fwd(B=1, T=64, H=2, D=128, dtype=_abi.KDA_BF16, chunk=0):
+    a = _abi.FwdArgs()
+    a.B, a.T, a.H, a.Dk, a.Dv, a.dtype, a.chunk = B, T, H, D, D, dtype, chunk
+    fake = 0x10000  # aligned, never dereferenced: every case below fails validation first
+    for f in ("q", "k", "v", "log_alpha", "beta", "gate", "out"):
+        setattr(a, f, fake)
+    return a
+
+
+def _ws(lib, a):
+    n = ctypes.c_size_t(0)
+    rc = lib.kda_chunk_fwd_workspace_size(ctypes.byref(a), ctypes.byref(n))
+    return rc, n.value
+
+
+def test_workspace_size_query(lib):
+    a = _good_fwd(B=1, T=4096, H=8)
+    rc, n = _ws(lib, a)
+    assert rc == 0
+    # one card per (b, h, chunk): 5 fp16 C x D tiles + fp32 Gamma
+    assert n == 8 * 64 * (5 * 64 * 128 * 2 + 128 * 4)
+    a.T = 4095
+    assert _ws(lib, a) == (0, n)  # ragged tail still needs 64 chunks
+    a.T = 0
+    assert _ws(lib, a) == (0, 0)
+    a32 = _good_fwd(B=1, T=256, H=2, D=64, dtype=_abi.KDA_F32, chunk=16)
+    assert _ws(lib, a32) == (0, 2 * 16 * (5 * 16 * 64 * 4 + 64 * 4))
+    assert lib.kda_chunk_fwd_workspace_size(None, None) == _abi.KDA_ERR_NULL
+
+
+@pytest.mark.parametrize("mutate,code", [
+    (lambda a: setattr(a, "B", -1), _abi.KDA_ERR_SHAPE),
+    (lambda a: setattr(a, "T", -5), _abi.KDA_ERR_SHAPE),
+    (lambda a: setattr(a, "Dk", 0), _abi.KDA_ERR_SHAPE),
+    (lambda a: setattr(a, "Dk", 96), _abi.KDA_ERR_UNSUPPORTED),
+    (lambda a: (setattr(a, "Dk", 64)), _abi.KDA_ERR_UNSUPPORTED),  # Dk != Dv
+    (lambda a: setattr(a, "dtype", 7), _abi.KDA_ERR_UNSUPPORTED),
+    (lambda a: setattr(a, "chunk", 48), _abi.KDA_ERR_UNSUPPORTED),
+    (lambda a: setattr(a, "chunk", 128), _abi.KDA_ERR_UNSUPPORTED),
+    (lambda a: setattr(a, "flags", 2), _abi.KDA_ERR_UNSUPPORTED),
+    (lambda a: setattr(a, "out_dtype", 2), _abi.KDA_ERR_UNSUPPORTED),
+    (lambda a: setattr(a, "T", 2 ** 62), _abi.KDA_ERR_SHAPE),
+    (lambda a: setattr(a, "q", None), _abi.KDA_ERR_NULL),
+    (lambda a: setattr(a, "gate", None), _abi.KDA_ERR_NULL),
+    (lambda a: setattr(a, "out", None), _abi.KDA_ERR_NULL),
+    (lambda a: setattr(a, "v", 0x10008), _abi.KDA_ERR_ALIGN),
+    (lambda a: setattr(a, "initial_state", 0x10004), _abi.KDA_ERR_ALIGN),
+    (lambda a: None, _abi.KDA_ERR_WORKSPACE),  # no workspace given
+    (lambda a: (setattr(a, "workspace", 0x20000), setattr(a, "workspace_bytes", 100)),
+     _abi.KDA_ERR_WORKSPACE),
+])
+def test_fwd_validation_rejects_before_any_hip_call(lib, mutate, code):
+    a = _good_fwd()
+    mutate(a)
+    assert lib.kda_chunk_fwd(ctypes.byref(a), None) == code
+
+
+def test_fp32_chunk64_d128_is_unsupported(lib):
+    a = _good_fwd(dtype=_abi.KDA_F32, chunk=64)
+    assert _ws(lib, a)[0] == _abi.KDA_ERR_UNSUPPORTED
+    assert lib.kda_chunk_fwd(None, None) == _abi.KDA_ERR_NULL
+
+
+def _good_dec():
+    a = _abi.DecodeArgs()
+    a.B, a.H, a.Dk, a.Dv, a.dtype = 4, 2, 128, 128, _abi.KDA_BF16
+    for f in ("q", "k", "v", "log_alpha", "beta", "gate", "out", "state"):
+        setattr(a, f, 0x10000)
+    return a
+
+
+@pytest.mark.parametrize("mutate,code", [
+    (lambda a: setattr(a, "H", -1), _abi.KDA_ERR_SHAPE),
+    (lambda a: setattr(a, "Dv", 64), _abi.KDA_ERR_UNSUPPORTED),
+    (lambda a: setattr(a, "dtype", 3), _abi.KDA_ERR_UNSUPPORTED),
+    (lambda a: setattr(a, "flags", 8), _abi.KDA_ERR_UNSUPPORTED),
+    (lambda a: setattr(a, "reserved", 1), _abi.KDA_ERR_UNSUPPORTED),
+    (lambda a: setattr(a, "out_dtype", -1), _abi.KDA_ERR_UNSUPPORTED),
+    (lambda a: setattr(a, "state", None), _abi.KDA_ERR_NULL),
+    (lambda a: setattr(a, "beta", None), _abi.KDA_ERR_NULL),
+    (lambda a: setattr(a, "k", 0x10002), _abi.KDA_ERR_ALIGN),
+])
+def test_decode_validation(lib, mutate, code):
+    a = _good_dec()
+    mutate(a)
+    assert lib.kda_decode_step(ctypes.byref(a), None) == code
+
+
+def test_empty_problems_are_no_ops(lib):
+    a = _good_dec()
+    a.B = 0
+    assert lib.kda_decode_step(ctypes.byref(a), None) == 0
+    f = _good_fwd(B=0)
+    assert lib.kda_chunk_fwd(ctypes.byref(f), None) == 0
+    f = _good_fwd(T=0)  # no final state requested: nothing to do
+    assert lib.kda_chunk_fwd(ctypes.byref(f), None) == 0
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    import gated_delta_rule_106_amd as kda
+    x = torch.zeros(1, 16, 1, 64)
+    with pytest.raises(ValueError):
+        kda.chunk_fwd(x, x, x, x, torch.zeros(1, 16, 1), x)
+    with pytest.raises(ValueError):
+        kda.decode_step(x[:, 0], x[:, 0], x[:, 0], x[:, 0], torch.zeros(1, 1), x[:, 0],
+                        torch.zeros(1, 1, 64, 64))
