@@ -1,0 +1,310 @@
+#!/usr/bin/env python3
+"""Throughput of the KDA token mixer on one MI355X (gfx950).
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+One step is one chunkwise prefill (cumulative log-decay, q/k rescaling, the
+intra-chunk UT transform, the sequential state pass with the fused output read
+and gate) over the headline workload: B=1, H=8, T=4096, d_k = d_v = 128, bf16
+inputs, fp32 state, chunk 64 built from 16-token tiles.  The same run also
+times the single-token decode step on B=512, H=32 (fp32 128x128 state per head,
+updated in place) and reports it in the ``decode`` object; the two larger
+prefill shapes (B2 H32 T8192 with state in/out, B1 H16 T65536 with 30 % of the
+key channels at the retention floor) are timed for context under ``configs``.
+
+Inputs are synthetic and seeded (kda_workloads); they are resident in device
+memory before the timed region starts.  The headline prefill rotates through
+several input sets whose total size exceeds the 256 MB Infinity Cache, so its
+reads come from HBM.  Kernel durations come from HIP events recorded on the
+stream the library launches on.  Rank 0 prints one JSON line on stdout;
+progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "KDA prefill tokens/s + % bf16 MFMA peak; decode steps/s + % HBM BW"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16/fp16 MFMA, TFLOP/s
+KEYS = ("q", "k", "v", "log_alpha", "beta", "gate")
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+# ----------------------------------------------------------- algorithmic work
+def prefill_bytes(wl) -> int:
+    """Algorithmic HBM bytes of one prefill: bf16 q, k, v, log alpha and gate
+    (2 B per element), beta (2 B per head-token), a bf16 output (256 B per
+    head-token at d = 128), plus one read of the initial and one write of the
+    final fp32 state when present.  1538 B per head-token at d = 128."""
+    esz = 2 if wl.dtype == "bf16" else 4
+    per_tok = esz * (3 * wl.Dk + 2 * wl.Dv + 1) + esz * wl.Dv
+    n = wl.B * wl.T * wl.H * per_tok
+    st = wl.B * wl.H * wl.Dk * wl.Dv * 4
+    return n + (st if wl.init_state else 0) + (st if wl.final_state else 0)
+
+
+def prefill_flops(wl) -> int:
+    """Algorithmic flops of the chunkwise form per head-token, causal triangles
+    counted exactly: 2d[(C-1)/2 + 4(C+1)/2] + C^2/3 + 6 d^2 (A, P, W, U~ and
+    P U triangles; the triangular solve; W S, Q~ S and Kbar^T U)."""
+    C, d = wl.chunk, wl.Dk
+    per = 2 * d * ((C - 1) / 2 + 4 * (C + 1) / 2) + C * C / 3 + 6 * d * d
+    return int(round(per * wl.B * wl.T * wl.H))
+
+
+def decode_bytes(wl) -> int:
+    """Per (b, h): read and write of the fp32 state, bf16 q, k, v, log alpha,
+    gate and beta, and a bf16 output."""
+    esz = 2 if wl.dtype == "bf16" else 4
+    per = 2 * wl.Dk * wl.Dv * 4 + esz * (3 * wl.Dk + 2 * wl.Dv + 1) + esz * wl.Dv
+    return wl.B * wl.H * per
+
+
+def decode_flops(wl) -> int:
+    return 7 * wl.Dk * wl.Dv * wl.B * wl.H
+
+
+# ------------------------------------------------------------------ helpers
+def source_digest() -> str:
+    """Digest of the HIP sources, used to tell whether stored counter readings
+    still describe the kernels being timed."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "gated_delta_rule_106_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".h")):
+            with open(os.path.join(csrc, name), "rb") as f:
+                h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(kernel_tag: str):
+    """HBM bytes per launch from the committed counter summary, or None when it
+    is absent or was taken on other kernel sources."""
+    path = os.path.join(PROFILES, "traffic_" + kernel_tag + ".md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_src = re.search(r"^source_digest:\s*(\w+)", text, re.M)
+    m_b = re.search(r"^hbm_bytes_per_launch:\s*([0-9.eE+]+)", text, re.M)
+    if not m_src or not m_b or m_src.group(1) != source_digest():
+        return None
+    return float(m_b.group(1))
+
+
+def to_dev(x, dev):
+    import torch
+    return {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in x.items()}
+
+
+def time_calls(fn, sets, steps, warmup, stream):
+    """Run fn(set) W times untimed, then K times between two synchronisations
+    with a HIP event pair around every call.  Returns (wall seconds, per-call
+    event milliseconds)."""
+    import torch
+    for i in range(warmup):
+        fn(sets[i % len(sets)])
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        ev[i][0].record(stream)
+        fn(sets[i % len(sets)])
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return wall, [a.elapsed_time(b) for a, b in ev]
+
+
+def prefill_sets(kda, wl, n_sets, dev):
+    import torch
+    from kda_workloads import make_inputs
+    sets = []
+    ws_n = kda.workspace_bytes(wl.B, wl.T, wl.H, wl.Dk, dtype=wl.torch_dtype, chunk=wl.chunk)
+    for i in range(n_sets):
+        x = to_dev(make_inputs(wl, seed=wl.seed + 100 * i), dev)
+        x["out"] = torch.empty((wl.B, wl.T, wl.H, wl.Dv), dtype=torch.float32, device=dev)
+        x["ws"] = torch.empty(max(ws_n, 16), dtype=torch.uint8, device=dev)
+        x["final"] = (torch.empty((wl.B, wl.H, wl.Dk, wl.Dv), dtype=torch.float32, device=dev)
+                      if wl.final_state else None)
+        sets.append(x)
+    return sets
+
+
+def prefill_call(kda, wl):
+    def fn(x):
+        kda.chunk_fwd(*(x[k] for k in KEYS), initial_state=x.get("initial_state"),
+                      output_final_state=wl.final_state, chunk=wl.chunk, out=x["out"],
+                      final_state=x["final"], workspace=x["ws"])
+    return fn
+
+
+# ---------------------------------------------------------------- the legs
+def bench_prefill(kda, wl, steps, warmup, n_sets, dev, stream):
+    log(f"prefill {wl.name}: building {n_sets} input set(s)")
+    sets = prefill_sets(kda, wl, n_sets, dev)
+    wall, ms = time_calls(prefill_call(kda, wl), sets, steps, warmup, stream)
+    ev_ms = sum(ms) / len(ms)
+    toks = wl.B * wl.T
+    nbytes, flops = prefill_bytes(wl), prefill_flops(wl)
+    res = {
+        "workload": wl.name, "B": wl.B, "H": wl.H, "T": wl.T, "d": wl.Dk, "chunk": wl.chunk,
+        "input_sets": n_sets, "ms_per_step_wall": 1e3 * wall / steps, "kernel_ms_mean": ev_ms,
+        "kernel_ms_min": min(ms), "tokens_per_s": toks / (wall / steps),
+        "kernel_tokens_per_s": toks / (ev_ms / 1e3),
+        "alg_bytes": nbytes, "alg_flops": flops,
+        "hbm_gbs": nbytes / (ev_ms / 1e3) / 1e9, "mfma_tflops": flops / (ev_ms / 1e3) / 1e12,
+    }
+    res["hbm_frac"] = res["hbm_gbs"] / HBM_PEAK_GBS
+    res["mfma_frac"] = res["mfma_tflops"] / BF16_MFMA_PEAK_TFLOPS
+    log(f"prefill {wl.name}: {ev_ms * 1e3:.1f} us/call (events), "
+        f"{res['tokens_per_s']:.3e} tok/s wall, {res['hbm_gbs']:.0f} GB/s alg, "
+        f"{100 * res['mfma_frac']:.2f} % MFMA alg")
+    del sets
+    return res, wall
+
+
+def bench_decode(kda, wl, steps, warmup, dev, stream):
+    import torch
+    from kda_workloads import make_inputs
+    log(f"decode {wl.name}: building inputs")
+    x = to_dev(make_inputs(wl), dev)
+    x["out"] = torch.empty((wl.B, wl.H, wl.Dv), dtype=torch.float32, device=dev)
+    state = x["state"]  # working copy, updated in place step after step
+
+    def fn(_):
+        kda.decode_step(*(x[k] for k in KEYS), state, out=x["out"])
+    wall, ms = time_calls(fn, [None], steps, warmup, stream)
+    ev_ms = sum(ms) / len(ms)
+    nbytes, flops = decode_bytes(wl), decode_flops(wl)
+    res = {
+        "workload": wl.name, "B": wl.B, "H": wl.H, "d": wl.Dk,
+        "steps_per_s": 1e3 / ev_ms, "steps_per_s_wall": steps / wall,
+        "tokens_per_s": wl.B * 1e3 / ev_ms, "kernel_ms_mean": ev_ms, "kernel_ms_min": min(ms),
+        "alg_bytes": nbytes, "alg_flops": flops,
+        "hbm_gbs": nbytes / (ev_ms / 1e3) / 1e9,
+    }
+    res["hbm_frac"] = res["hbm_gbs"] / HBM_PEAK_GBS
+    log(f"decode: {ev_ms * 1e3:.1f} us/step, {res['hbm_gbs']:.0f} GB/s "
+        f"({100 * res['hbm_frac']:.1f} % of HBM peak)")
+    return res
+
+
+def cpu_baseline(wl, budget_s):
+    """The fp64 oracle, as it stands, on the host cores: whole passes over the
+    headline workload until about budget_s seconds have been spent."""
+    import oracle
+    from kda_workloads import make_inputs
+    oracle.build(force=False)
+    x = make_inputs(wl)
+    threads = oracle.default_threads()
+    used = max(1, min(threads, wl.B * wl.H))  # parallel over (batch, head) only
+    secs, reps = 0.0, 0
+    while secs < budget_s and reps < 50:
+        _, _, s = oracle.fwd(*(x[k] for k in KEYS), initial_state=x.get("initial_state"),
+                             threads=threads, return_seconds=True)
+        secs += s
+        reps += 1
+    per = secs / reps
+    log(f"cpu baseline: {per:.3f} s per pass over {wl.name} with {used} thread(s), {reps} pass(es)")
+    return {"value": wl.B * wl.T / per, "unit": "tokens/s", "cores": used, "kind": "oracle",
+            "sample": f"{reps} whole pass(es) of the fp64 sequential oracle over {wl.name} "
+                      f"(B={wl.B} H={wl.H} T={wl.T}); OpenMP over (batch, head), "
+                      f"{threads} thread(s) available, {len(os.sched_getaffinity(0))} host core(s)",
+            "seconds_per_pass": per}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--sets", type=int, default=8, help="rotating prefill input sets")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="time budget of the oracle baseline (0 skips it)")
+    ap.add_argument("--no-context", action="store_true",
+                    help="skip the context timings of the two larger prefill shapes")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: the KDA path here has no multi-GPU mode "
+              "(its (batch, head) units shard with no communication; see the design notes). "
+              "Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import gated_delta_rule_106_amd as kda
+    from kda_workloads import CONFIGS
+
+    kda._abi.load()  # raises if the HIP library is missing: there is no fallback
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+    log(f"device {torch.cuda.get_device_name(dev)}; library {kda.library_path()}")
+
+    head = CONFIGS[1]
+    pre, wall = bench_prefill(kda, head, args.steps, args.warmup, args.sets, dev, stream)
+    dec = bench_decode(kda, CONFIGS[4], max(args.steps, 10), args.warmup, dev, stream)
+    ctx = {}
+    if not args.no_context:
+        for cid in (2, 3):
+            r, _ = bench_prefill(kda, CONFIGS[cid], max(5, args.steps // 10), 2, 1, dev, stream)
+            ctx[CONFIGS[cid].name] = r
+            torch.cuda.empty_cache()
+
+    traffic = stored_traffic("prefill_" + head.name)
+    roof = {"kernel": "kda_chunk_fwd (kda_prep_kernel + kda_recur_kernel)", "bound": "hbm",
+            "achieved": pre["hbm_gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": pre["hbm_gbs"] / HBM_PEAK_GBS, "traffic": traffic}
+    out = {
+        "metric": METRIC, "value": pre["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": pre["ms_per_step_wall"],
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "compute": "bf16 inputs; fp16/bf16 MFMA operands with fp32 accumulation; fp32 state; fp32 output",
+        "data": "synthetic (seeded; q,k L2-normalised, q/sqrt(d), v~N(0,1), beta=sigmoid(N(0,1)), "
+                "log alpha=max(logsigmoid(N(2,1)), ln 0.0067), gate~N(0,1))",
+        "config": {"workload": head.name, "B": head.B, "H": head.H, "T": head.T, "d_k": head.Dk,
+                   "d_v": head.Dv, "chunk": head.chunk, "global_batch": head.B,
+                   "seq_len": head.T, "parallelism": "single GPU"},
+        "mfma": {"achieved": pre["mfma_tflops"], "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                 "frac": pre["mfma_frac"], "alg_flops_per_step": pre["alg_flops"]},
+        "roofline": roof,
+        "decode": {"metric": "decode steps/s", "value": dec["steps_per_s"], "unit": "steps/s",
+                   "tokens_per_s": dec["tokens_per_s"], "kernel_ms": dec["kernel_ms_mean"],
+                   "roofline": {"kernel": "kda_decode_kernel", "bound": "hbm",
+                                "achieved": dec["hbm_gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                "frac": dec["hbm_frac"],
+                                "traffic": stored_traffic("decode_" + CONFIGS[4].name)},
+                   "workload": dec["workload"]},
+        "prefill_detail": pre,
+        "configs": ctx,
+        "source_digest": source_digest(),
+    }
+    if args.cpu_seconds > 0:
+        out["cpu_baseline"] = cpu_baseline(head, args.cpu_seconds)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
