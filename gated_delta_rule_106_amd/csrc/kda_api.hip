@@ -46,6 +46,7 @@ int check_shape(const kda_fwd_args* a, int* chunk, int64_t* nchunks, int64_t* ca
     const int64_t cb = kda::prefill_card_bytes(a->dtype == KDA_BF16, c, (int)a->Dk);
     int64_t tmp, total;
     if (cb <= 0 || !mul_ok(bh, nc, &tmp) || !mul_ok(tmp, cb, &total)) return KDA_ERR_SHAPE;
+    if (tmp > INT_MAX) return KDA_ERR_SHAPE;  // one workgroup per (b, h, chunk)
     *chunk = c;
     *nchunks = nc;
     *card = cb;

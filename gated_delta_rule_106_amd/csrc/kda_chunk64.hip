@@ -1,0 +1,712 @@
+// Chunkwise KDA forward for bf16 inputs with 64-token chunks (gfx950).
+//
+// Same algebra as the general kernels (the per-token recurrence of page "3T
+// models are no longer magic", section "Gate 1: KDA makes it computable",
+// evaluated chunk by chunk as on page "Kimi K3 report walk-through", sections
+// "Compute paradigm" and "Hierarchical chunking of linear attention"), laid out
+// for throughput on CDNA4:
+//
+// kda_prep64_kernel  one workgroup (4 waves) per (b, h, chunk).  Wave a owns the
+//   16-token tile a of the chunk and keeps it in registers in MFMA operand
+//   layout (lane = token, 4 consecutive key channels per 16-channel tile).  The
+//   cumulative log-decay is a DPP prefix scan across the 16 lanes of a row.
+//   Decay is folded into q and k as an absolute-position rescaling measured
+//   from the start of each 16-token tile (page "Kimi K3 report walk-through",
+//   section "Numerical stability & co-design": inside one tile the inverse
+//   factor stays below 2^116 given the 0.67 % retention floor):
+//       KR = k 2^{P},  QR = q 2^{P},  KC = k 2^{-P},  KE = k 2^{tau - P},
+//   P = prefix sum of log2(alpha) inside the tile, tau = its total.  Pair
+//   products inside a tile use KR.KC^T with a three-pass bf16 hi/lo split (the
+//   operands span 2^{+-116}); across tiles both operands are <= |k| and one
+//   fp16 pass suffices.  The unit-lower-triangular system (I + A) is solved
+//   with register forward substitution on the four 16x16 diagonal blocks and
+//   fp32 MFMA block products for the rest.  The remaining contractions are
+//   arranged so that their accumulators come out in exactly the fragment
+//   layout the sequential kernel consumes, so the "update card" of the chunk
+//   is written with coalesced 16-byte stores.
+//
+// kda_rec64_kernel  one workgroup per (b, h, group of NCONS 16-column value
+//   tiles): NCONS consumer waves carry the fp32 state of their columns in MFMA
+//   accumulators across all chunks; one producer wave streams the next card
+//   into a double-buffered LDS ring with direct global->LDS loads.  Workgroups
+//   of one head are placed on one XCD so its cards are fetched into one L2.
+//
+// Card of one (b, h, chunk), fp16 unless noted (lane l = 16 g + m):
+//   W   [mt][kb] 64 lanes x 8: -W[16mt + m][c(kb, g, j)]
+//   QE  [mt][kb] 64 lanes x 8:  Qe[16mt + m][c(kb, g, j)]        Qe = Q~ - P W
+//   KBT [ct][u]  64 lanes x 8:  Kbar[c(u, g, j)][16ct + m]
+//   UT  [nt][mt] 64 lanes x 4:  U~[16mt + 4g + i][16nt + m]
+//   UO  [nt][mt] 64 lanes x 4:  Uo[16mt + 4g + i][16nt + m]       Uo = P U~
+//   GAM [D] fp32: 2^{gamma_C}, the decay of the whole chunk per key channel
+// with c(x, g, j) = 32x + 4g + j (j < 4), 32x + 16 + 4g + (j - 4) (j >= 4):
+// the K-index order in which two stacked accumulator tiles (rows 4g .. 4g+3
+// in lane group g) feed the next MFMA directly as its B operand.
+#include "kda_device.h"
+#include "kda_prefill.h"
+
+namespace kda {
+namespace c64 {
+
+constexpr int C = 64;
+constexpr int NSUB = 4;
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, true));
+}
+
+// inclusive prefix sum over the 16 lanes of a DPP row (lanes 16g .. 16g+15)
+__device__ __forceinline__ float row_scan16(float x) {
+    x += dpp_mov<0x111>(x);  // row_shr:1
+    x += dpp_mov<0x112>(x);  // row_shr:2
+    x += dpp_mov<0x114>(x);  // row_shr:4
+    x += dpp_mov<0x118>(x);  // row_shr:8
+    return x;
+}
+
+// value held by lane 15 of this lane's 16-lane row
+__device__ __forceinline__ float row_last(float x) {
+    return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x1F0));
+}
+
+// physical index of logical K element j (0..7) of lane group g in K-step x
+__device__ __forceinline__ constexpr int cmap(int x, int g, int j) {
+    return 32 * x + 4 * g + (j & 3) + ((j >> 2) << 4);
+}
+
+__device__ __forceinline__ half4 ld_h4(const _Float16* p) { return *reinterpret_cast<const half4*>(p); }
+__device__ __forceinline__ half8 ld_h8(const _Float16* p) { return *reinterpret_cast<const half8*>(p); }
+
+__device__ __forceinline__ half8 cat_h8(const half4& lo, const half4& hi) {
+    half8 r;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        r[j] = lo[j];
+        r[4 + j] = hi[j];
+    }
+    return r;
+}
+
+__device__ __forceinline__ half8 pack_h8(const floatx4& lo, const floatx4& hi) {
+    half8 r;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        r[j] = static_cast<_Float16>(lo[j]);
+        r[4 + j] = static_cast<_Float16>(hi[j]);
+    }
+    return r;
+}
+
+__device__ __forceinline__ half4 pack_h4(const floatx4& x) {
+    half4 r;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) r[j] = static_cast<_Float16>(x[j]);
+    return r;
+}
+
+__device__ __forceinline__ floatx4 unpack_h4(const half4& x) {
+    floatx4 r;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) r[j] = static_cast<float>(x[j]);
+    return r;
+}
+
+__device__ __forceinline__ floatx4 mma_f32_k16(const float4& a, const floatx4& b, floatx4 acc) {
+    acc = mma_f32_k4(a.x, b[0], acc);
+    acc = mma_f32_k4(a.y, b[1], acc);
+    acc = mma_f32_k4(a.z, b[2], acc);
+    acc = mma_f32_k4(a.w, b[3], acc);
+    return acc;
+}
+
+// ---------------------------------------------------------------------------
+template <int D>
+struct Card {
+    static constexpr int KB = D / 32, NCT = D / 16;
+    static constexpr int64_t FRAG = 1024;  // 64 lanes x 16 B
+    static constexpr int64_t HFRAG = 512;  // 64 lanes x 8 B
+    static constexpr int64_t W = 0;
+    static constexpr int64_t QE = W + 4 * KB * FRAG;
+    static constexpr int64_t KBT = QE + 4 * KB * FRAG;
+    static constexpr int64_t UT = KBT + NCT * 2 * FRAG;
+    static constexpr int64_t UO = UT + NCT * 4 * HFRAG;
+    static constexpr int64_t GAM = UO + NCT * 4 * HFRAG;
+    static constexpr int64_t BYTES = GAM + D * 4;
+    static_assert(BYTES % 16 == 0, "card alignment");
+};
+
+template <int D>
+struct PrepL {
+    static constexpr int KB = D / 32;
+    static constexpr int SR = D + 8;  // fp16 [token][channel] row stride (halves)
+    static constexpr int ST = C + 8;  // fp16 [channel][token] row stride (halves)
+    static constexpr int SA = C + 4;  // fp32 [64][64] row stride (floats)
+    static constexpr int SP = C + 8;  // fp16 [64][64] row stride (halves)
+    static constexpr int64_t B_KEF = (int64_t)NSUB * KB * 64 * 16;  // KE fragments
+    static constexpr int64_t B_LINV = 64 * SA * 4;
+    static constexpr int64_t B_KE = B_KEF > B_LINV ? B_KEF : B_LINV;
+    static constexpr int64_t OFF_BETA = 0;                     // fp32 [64]
+    static constexpr int64_t OFF_TAU = 256;                    // fp32 [4][D]: log2 decay of each tile
+    static constexpr int64_t OFF_KE = OFF_TAU + 4 * D * 4;     // KE fragments; later Linv fp32 [64][SA]
+    static constexpr int64_t OFF_KT = OFF_KE + B_KE;           // fp16 K~^T [D][ST]; later -W^T
+    static constexpr int64_t OFF_KBT = OFF_KT + D * ST * 2;    // fp16 Kbar^T [D][ST]
+    static constexpr int64_t OFF_VT = OFF_KBT + D * ST * 2;    // fp16 V^T [D][ST]
+    static constexpr int64_t OFF_Q = OFF_VT + D * ST * 2;      // fp16 Q~ [64][SR]
+    static constexpr int64_t OFF_A = OFF_Q + 64 * SR * 2;      // fp32 A [64][SA]; later T fp16 [64][SP]
+    static constexpr int64_t OFF_P = OFF_A + 64 * SA * 4;      // fp16 P [64][SP]
+    static constexpr int64_t TOTAL = OFF_P + 64 * SP * 2;
+    static_assert(TOTAL <= 160 * 1024, "prep LDS budget");
+    static_assert(OFF_KE % 16 == 0 && OFF_KT % 16 == 0 && OFF_KBT % 16 == 0 && OFF_VT % 16 == 0 &&
+                      OFF_Q % 16 == 0 && OFF_A % 16 == 0 && OFF_P % 16 == 0,
+                  "prep LDS alignment");
+};
+
+// ---------------------------------------------------------------------------
+// kernel 1: the update card of one (b, h, chunk)
+template <int D>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void kda_prep64_kernel(PrepParams p) {
+    using L = PrepL<D>;
+    using CD = Card<D>;
+    constexpr int NCT = D / 16, KB = D / 32;
+    constexpr int SR = L::SR, ST = L::ST, SA = L::SA, SP = L::SP;
+    extern __shared__ __align__(16) unsigned char smem[];
+    float* s_beta = reinterpret_cast<float*>(smem + L::OFF_BETA);
+    float* s_tau = reinterpret_cast<float*>(smem + L::OFF_TAU);
+    _Float16* s_ke = reinterpret_cast<_Float16*>(smem + L::OFF_KE);
+    float* s_linv = reinterpret_cast<float*>(smem + L::OFF_KE);
+    _Float16* s_kt = reinterpret_cast<_Float16*>(smem + L::OFF_KT);
+    _Float16* s_kbt = reinterpret_cast<_Float16*>(smem + L::OFF_KBT);
+    _Float16* s_vt = reinterpret_cast<_Float16*>(smem + L::OFF_VT);
+    _Float16* s_q = reinterpret_cast<_Float16*>(smem + L::OFF_Q);
+    float* s_a = reinterpret_cast<float*>(smem + L::OFF_A);
+    _Float16* s_t = reinterpret_cast<_Float16*>(smem + L::OFF_A);
+    _Float16* s_p = reinterpret_cast<_Float16*>(smem + L::OFF_P);
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int m16 = lane & 15, g4 = lane >> 4;
+    const int64_t NC = p.NC, T = p.T, H = p.H;
+    const int64_t blk = blockIdx.x;
+    const int64_t n = blk % NC, unit = blk / NC;
+    const int64_t b = unit / H, h = unit % H;
+    const int64_t t0 = n * C;
+    const uint16_t* gq = static_cast<const uint16_t*>(p.q);
+    const uint16_t* gk = static_cast<const uint16_t*>(p.k);
+    const uint16_t* gv = static_cast<const uint16_t*>(p.v);
+    const uint16_t* gla = static_cast<const uint16_t*>(p.la);
+    const uint16_t* gbeta = static_cast<const uint16_t*>(p.beta);
+    const bool clamp = p.clamp != 0;
+    unsigned char* card = static_cast<unsigned char*>(p.ws) + (unit * NC + n) * CD::BYTES;
+
+    // ---- phase 1 (per tile): wave a holds token 16a + m16 and, per 32-channel
+    //      K-step kb, the 8 key channels cmap(kb, g4, 0..7)
+    const int a = wave;
+    const int rl = 16 * a + m16;
+    const int64_t tok = t0 + rl;
+    const bool valid = tok < T;
+    const int64_t row = (b * T + (valid ? tok : 0)) * H + h;
+    uint2 rq[NCT], rk[NCT], rv[NCT], rla[NCT];
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+        const int64_t off = row * D + 16 * ct + 4 * g4;
+        if (valid) {
+            rq[ct] = *reinterpret_cast<const uint2*>(gq + off);
+            rk[ct] = *reinterpret_cast<const uint2*>(gk + off);
+            rv[ct] = *reinterpret_cast<const uint2*>(gv + off);
+            rla[ct] = *reinterpret_cast<const uint2*>(gla + off);
+        } else {
+            rq[ct] = rk[ct] = rv[ct] = rla[ct] = make_uint2(0u, 0u);
+        }
+    }
+    const float beta_mine = valid ? bf16_bits_to_float(gbeta[row]) : 0.f;
+    if (g4 == 0) s_beta[rl] = beta_mine;
+
+    auto elem = [](const uint2& w, int i) -> float {
+        const uint32_t x = (i < 2) ? w.x : w.y;
+        return (i & 1) ? __uint_as_float(x & 0xffff0000u) : __uint_as_float(x << 16);
+    };
+
+    half8 kr16[KB], qr16[KB];
+    floatx4 accA = zero4(), accP = zero4();
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+        bf16x8 krh, krl, qrh, qrl, kch, kcl;
+        half8 ke;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int ct = 2 * kb + (j >> 2), i = j & 3;
+            const float l = clamp_log_alpha(elem(rla[ct], i), clamp) * kLog2e;
+            const float P = row_scan16(l);       // log2 decay from the tile start, inclusive
+            const float tau = row_last(P);       // log2 decay over the whole tile
+            const float E = fast_exp2(P);        // <= 1
+            const float Einv = fast_exp2(-P);    // >= 1 and < 2^116 under the floor
+            const float F = fast_exp2(tau - P);  // decay from after this token to the tile end, <= 1
+            const float kf = elem(rk[ct], i), qf = elem(rq[ct], i);
+            const float KR = kf * E, QR = qf * E, KC = kf * Einv;
+            kr16[kb][j] = static_cast<_Float16>(KR);
+            qr16[kb][j] = static_cast<_Float16>(QR);
+            ke[j] = static_cast<_Float16>(kf * F);
+            __bf16 hi, lo;
+            split_bf16(KR, hi, lo);
+            krh[j] = hi;
+            krl[j] = lo;
+            split_bf16(QR, hi, lo);
+            qrh[j] = hi;
+            qrl[j] = lo;
+            split_bf16(KC, hi, lo);
+            kch[j] = hi;
+            kcl[j] = lo;
+            const int c = cmap(kb, g4, j);
+            if (m16 == 0) s_tau[a * D + c] = tau;
+            s_vt[c * ST + rl] = static_cast<_Float16>(elem(rv[ct], i));
+        }
+        // pair products inside the tile: A_rs ~ KR_r . KC_s, P_rs ~ QR_r . KC_s
+        accA = mma_bf16_k32(krh, kch, accA);
+        accA = mma_bf16_k32(krh, kcl, accA);
+        accA = mma_bf16_k32(krl, kch, accA);
+        accP = mma_bf16_k32(qrh, kch, accP);
+        accP = mma_bf16_k32(qrh, kcl, accP);
+        accP = mma_bf16_k32(qrl, kch, accP);
+        // KE fragment of this tile: the B operand of the pairs (later tile, this tile)
+        *reinterpret_cast<half8*>(s_ke + ((a * KB + kb) * 64 + lane) * 8) = ke;
+    }
+    // diagonal blocks of A (strictly lower, rows scaled by beta) and P (lower)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int r = 4 * g4 + i, s = m16;
+        const float br = __shfl(beta_mine, r);
+        s_a[(16 * a + r) * SA + 16 * a + s] = (s < r) ? br * accA[i] : 0.f;
+        s_p[(16 * a + r) * SP + 16 * a + s] = static_cast<_Float16>((s <= r) ? accP[i] : 0.f);
+#pragma unroll
+        for (int bb = 0; bb < NSUB; ++bb)
+            if (bb > a) s_p[(16 * a + r) * SP + 16 * bb + s] = static_cast<_Float16>(0.f);
+    }
+    __syncthreads();  // (1) tile decays, KE fragments, V^T and beta are in LDS
+
+    // ---- phase 2 (per tile): chunk-relative operands and the pairs with earlier tiles
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+        half4 q_lo, q_hi;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int c = cmap(kb, g4, j);
+            float before = 0.f, after = 0.f;
+#pragma unroll
+            for (int a2 = 0; a2 < NSUB; ++a2) {
+                const float tv = s_tau[a2 * D + c];
+                if (a2 < a) before += tv;
+                if (a2 > a) after += tv;
+            }
+            const float erho = fast_exp2(before);  // decay from the chunk start to the tile start
+            const float eaft = fast_exp2(after);   // decay from the tile end to the chunk end
+            const _Float16 kt = static_cast<_Float16>(static_cast<float>(kr16[kb][j]) * erho);
+            const _Float16 qt = static_cast<_Float16>(static_cast<float>(qr16[kb][j]) * erho);
+            const float ke = static_cast<float>(s_ke[((a * KB + kb) * 64 + lane) * 8 + j]);
+            s_kt[c * ST + rl] = kt;                                          // K~ = k 2^{g}
+            s_kbt[c * ST + rl] = static_cast<_Float16>(ke * eaft);           // Kbar = k 2^{g_C - g}
+            if (j < 4) q_lo[j] = qt; else q_hi[j - 4] = qt;
+        }
+        *reinterpret_cast<half4*>(s_q + rl * SR + 32 * kb + 4 * g4) = q_lo;       // Q~ = q 2^{g}
+        *reinterpret_cast<half4*>(s_q + rl * SR + 32 * kb + 16 + 4 * g4) = q_hi;
+    }
+    // Gamma = 2^{g_C} per key channel
+    if (tid < D) {
+        float gsum = 0.f;
+#pragma unroll
+        for (int a2 = 0; a2 < NSUB; ++a2) gsum += s_tau[a2 * D + tid];
+        reinterpret_cast<float*>(card + CD::GAM)[tid] = fast_exp2(gsum);
+    }
+    // pairs (a, bb), bb < a: reference point at the end of tile a-1, both operands <= |k|
+    for (int bb = 0; bb < a; ++bb) {
+        floatx4 pa = zero4(), pp = zero4();
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+            const half8 ke = ld_h8(s_ke + ((bb * KB + kb) * 64 + lane) * 8);
+            half8 col;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int c = cmap(kb, g4, j);
+                float mid = 0.f;  // decay over the tiles strictly between bb and a
+                for (int a2 = bb + 1; a2 < a; ++a2) mid += s_tau[a2 * D + c];
+                col[j] = static_cast<_Float16>(static_cast<float>(ke[j]) * fast_exp2(mid));
+            }
+            pa = mma_f16_k32(kr16[kb], col, pa);
+            pp = mma_f16_k32(qr16[kb], col, pp);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = 4 * g4 + i;
+            s_a[(16 * a + r) * SA + 16 * bb + m16] = s_beta[16 * a + r] * pa[i];
+            s_p[(16 * a + r) * SP + 16 * bb + m16] = static_cast<_Float16>(pp[i]);
+        }
+    }
+    __syncthreads();  // (2) A, P, K~^T, Kbar^T, Q~ complete
+
+    // ---- phase 3: Linv = (I + A)^{-1}, unit lower triangular, blocked by 16
+    if (wave == 0) {  // diagonal blocks: lane group g4 = block, lane m16 = column
+        const int ab = g4, j = m16;
+        const float* Ab = s_a + (16 * ab) * SA + 16 * ab;
+        float x[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) x[r] = (r == j) ? 1.f : 0.f;
+#pragma unroll
+        for (int r = 1; r < 16; ++r) {
+            float acc = x[r];
+#pragma unroll
+            for (int q = 0; q < r; ++q) acc -= Ab[r * SA + q] * x[q];
+            x[r] = acc;
+        }
+        float* Xb = s_linv + (16 * ab) * SA + 16 * ab;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) Xb[r * SA + j] = x[r];
+    }
+    __syncthreads();
+    // off-diagonal blocks by block diagonal d: Linv_{a,a-d} = -X_a sum_c A_{a,c} Linv_{c,a-d}
+    auto blk_a = [&](int r, int c) { return s_a + (16 * r) * SA + 16 * c; };
+    auto blk_x = [&](int r, int c) { return s_linv + (16 * r) * SA + 16 * c; };
+    auto mm = [&](const float* mp, const float* np, floatx4 acc) {  // acc += M N (row-major blocks)
+        const float4 av = *reinterpret_cast<const float4*>(mp + m16 * SA + 4 * g4);
+        floatx4 bv;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) bv[s] = np[(4 * g4 + s) * SA + m16];
+        return mma_f32_k16(av, bv, acc);
+    };
+#pragma unroll
+    for (int d = 1; d < NSUB; ++d) {
+        if (wave >= d) {
+            floatx4 y = zero4();
+            for (int c = wave - d; c < wave; ++c) y = mm(blk_a(wave, c), blk_x(c, wave - d), y);
+            const float4 xv = *reinterpret_cast<const float4*>(blk_x(wave, wave) + m16 * SA + 4 * g4);
+            const floatx4 z = mma_f32_k16(xv, y, zero4());
+            float* dst = blk_x(wave, wave - d);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) dst[(4 * g4 + i) * SA + m16] = -z[i];
+        }
+        __syncthreads();
+    }
+    // T = Linv diag(beta), fp16, zero above the diagonal
+    for (int e = tid; e < C * C; e += 256) {
+        const int r = e >> 6, s = e & 63;
+        const float v = (s <= r) ? s_linv[r * SA + s] * s_beta[s] : 0.f;
+        s_t[r * SP + s] = static_cast<_Float16>(v);
+    }
+    __syncthreads();  // (3) T complete
+
+    // ---- phase 4: card.  Jobs 0..KB-1: key-channel pair kb (W, Qe, Kbar^T);
+    //      jobs KB..2KB-1: value-column pair (U~, Uo)
+    // sum over tokens s < 16 (mt + 1) of A_row[s] * B_row[s] (rows in LDS, tokens contiguous).
+    // A trailing 16-token step is a K = 32 step with its upper half zeroed: one MFMA shape
+    // per accumulator chain.
+    auto kloop = [&](const _Float16* arow, const _Float16* brow, int mt, floatx4 acc) {
+        const int kend = 16 * (mt + 1);
+        int s0 = 0;
+        for (; s0 + 32 <= kend; s0 += 32)
+            acc = mma_f16_k32(ld_h8(arow + s0 + 8 * g4), ld_h8(brow + s0 + 8 * g4), acc);
+        if (s0 < kend) {
+            const half4 z4 = {0, 0, 0, 0};
+            acc = mma_f16_k32(cat_h8(ld_h4(arow + s0 + 4 * g4), z4), cat_h8(ld_h4(brow + s0 + 4 * g4), z4), acc);
+        }
+        return acc;
+    };
+    for (int job = wave; job < 2 * KB; job += 4) {
+        if (job < KB) {
+            const int kb = job;
+            floatx4 wt[2][4];
+#pragma unroll
+            for (int cl = 0; cl < 2; ++cl)
+#pragma unroll
+                for (int mt = 0; mt < 4; ++mt)  // W^T tile = K~^T T^T
+                    wt[cl][mt] = kloop(s_kt + (16 * (2 * kb + cl) + m16) * ST, s_t + (16 * mt + m16) * SP, mt,
+                                       zero4());
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) {
+                floatx4 n0, n1;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    n0[i] = -wt[0][mt][i];
+                    n1[i] = -wt[1][mt][i];
+                }
+                *reinterpret_cast<half8*>(card + CD::W + ((mt * KB + kb) * 64 + lane) * 16) = pack_h8(n0, n1);
+            }
+            // -W^T over this pair's rows of K~^T (only this wave reads them)
+#pragma unroll
+            for (int cl = 0; cl < 2; ++cl)
+#pragma unroll
+                for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        s_kt[(16 * (2 * kb + cl) + 4 * g4 + i) * ST + 16 * mt + m16] =
+                            static_cast<_Float16>(-wt[cl][mt][i]);
+            // Qe^T tile = Q~^T + (-W^T) P^T
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) {
+                floatx4 qe[2];
+#pragma unroll
+                for (int cl = 0; cl < 2; ++cl) {
+                    const floatx4 init = unpack_h4(ld_h4(s_q + (16 * mt + m16) * SR + 16 * (2 * kb + cl) + 4 * g4));
+                    qe[cl] = kloop(s_kt + (16 * (2 * kb + cl) + m16) * ST, s_p + (16 * mt + m16) * SP, mt, init);
+                }
+                *reinterpret_cast<half8*>(card + CD::QE + ((mt * KB + kb) * 64 + lane) * 16) = pack_h8(qe[0], qe[1]);
+            }
+            // Kbar^T fragments of the two 16-channel tiles
+#pragma unroll
+            for (int cl = 0; cl < 2; ++cl) {
+                const int ct = 2 * kb + cl;
+                const _Float16* kr = s_kbt + (16 * ct + m16) * ST;
+#pragma unroll
+                for (int u = 0; u < 2; ++u)
+                    *reinterpret_cast<half8*>(card + CD::KBT + ((ct * 2 + u) * 64 + lane) * 16) =
+                        cat_h8(ld_h4(kr + 32 * u + 4 * g4), ld_h4(kr + 32 * u + 16 + 4 * g4));
+            }
+        } else {
+            const int np = job - KB;
+            floatx4 ut[2][4];
+#pragma unroll
+            for (int cl = 0; cl < 2; ++cl) {
+                const int nt = 2 * np + cl;
+#pragma unroll
+                for (int mt = 0; mt < 4; ++mt) {  // U~ tile = T V
+                    ut[cl][mt] = kloop(s_t + (16 * mt + m16) * SP, s_vt + (16 * nt + m16) * ST, mt, zero4());
+                    *reinterpret_cast<half4*>(card + CD::UT + ((nt * 4 + mt) * 64 + lane) * 8) = pack_h4(ut[cl][mt]);
+                }
+#pragma unroll
+                for (int mt = 0; mt < 4; ++mt) {  // Uo tile = P U~ (U~ accumulators as the B operand)
+                    floatx4 acc = zero4();
+                    const _Float16* prow = s_p + (16 * mt + m16) * SP;
+#pragma unroll
+                    for (int u = 0; u < 2; ++u)
+                        if (2 * u <= mt)
+                            acc = mma_f16_k32(cat_h8(ld_h4(prow + 32 * u + 4 * g4), ld_h4(prow + 32 * u + 16 + 4 * g4)),
+                                              pack_h8(ut[cl][2 * u], ut[cl][2 * u + 1]), acc);
+                    *reinterpret_cast<half4*>(card + CD::UO + ((nt * 4 + mt) * 64 + lane) * 8) = pack_h4(acc);
+                }
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// kernel 2: sequential pass over the cards
+template <int D, int NCONS>
+struct RecL {
+    using CD = Card<D>;
+    static constexpr int64_t SH = CD::UT;                 // W, QE, KBT: shared by all consumers
+    static constexpr int64_t PER = 2 * 4 * CD::HFRAG;     // UT + UO of one 16-column tile
+    static constexpr int64_t ZB = 64 * 16 * 2;           // gate logits of one 16-column tile (bf16)
+    static constexpr int64_t OFF_U = SH;
+    static constexpr int64_t OFF_Z = SH + NCONS * PER;
+    static constexpr int64_t OFF_G = OFF_Z + NCONS * ZB;
+    static constexpr int64_t STAGE = OFF_G + D * 4;
+    static constexpr int NSTAGE = 2;
+    static constexpr int64_t TOTAL = NSTAGE * STAGE;
+    static constexpr int LOADS = (int)(SH / 1024) + NCONS * 6 + 1;  // direct-to-LDS instructions per stage
+    static_assert(TOTAL <= 160 * 1024, "recurrence LDS budget");
+    static_assert(STAGE % 16 == 0, "stage alignment");
+    static_assert(LOADS <= 63, "one stage must fit the wave's outstanding-load counter");
+};
+
+__device__ __forceinline__ void lds_dma16(const void* g, void* l) {
+    __builtin_amdgcn_global_load_lds(g, reinterpret_cast<__attribute__((address_space(3))) void*>(
+                                            reinterpret_cast<uintptr_t>(l)),
+                                     16, 0, 0);
+}
+
+__device__ __forceinline__ void wait_vm_zero() { __builtin_amdgcn_s_waitcnt(0x0F70); }   // vmcnt(0)
+__device__ __forceinline__ void wait_lgkm_zero() { __builtin_amdgcn_s_waitcnt(0xC07F); } // lgkmcnt(0)
+// workgroup barrier without the implicit memory fence of __syncthreads():
+// each wave waits explicitly for exactly what the next phase needs
+__device__ __forceinline__ void bare_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+template <int D, class Out, int NCONS>
+__global__ __launch_bounds__((NCONS + 1) * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void kda_rec64_kernel(RecurParams p) {
+    using CD = Card<D>;
+    using L = RecL<D, NCONS>;
+    constexpr int NCT = D / 16, KB = D / 32;
+    constexpr int G = D / (16 * NCONS);  // workgroups per head
+    extern __shared__ __align__(16) unsigned char smem[];
+
+    const int lane = lane_id(), wave = wave_id();
+    const int m16 = lane & 15, g4 = lane >> 4;
+    // XCD-aware placement: the G workgroups of one head share bid % 8
+    const int nblk = gridDim.x, bid = blockIdx.x;
+    const int logical = (bid % 8) * (nblk / 8) + bid / 8;
+    const int64_t unit = logical / G;
+    const int grp = logical % G;
+    const int64_t units = p.B * p.H;
+    if (unit >= units) return;  // padding workgroup (the whole group leaves together)
+    const int64_t H = p.H, T = p.T, NC = p.NC;
+    const int64_t b = unit / H, h = unit % H;
+    const unsigned char* cards = static_cast<const unsigned char*>(p.ws) + unit * NC * CD::BYTES;
+    const bool producer = wave == NCONS;
+    const uint16_t* gz = static_cast<const uint16_t*>(p.gate);
+
+    auto issue = [&](int64_t c) {  // producer: card c -> ring slot c % NSTAGE
+        const unsigned char* src = cards + c * CD::BYTES;
+        unsigned char* dst = smem + (c % L::NSTAGE) * L::STAGE;
+#pragma unroll
+        for (int i = 0; i < (int)(L::SH / 1024); ++i) lds_dma16(src + i * 1024 + lane * 16, dst + i * 1024);
+#pragma unroll
+        for (int cs = 0; cs < NCONS; ++cs) {
+            const int nt = grp * NCONS + cs;
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                lds_dma16(src + CD::UT + nt * 2048 + i * 1024 + lane * 16, dst + L::OFF_U + cs * L::PER + i * 1024);
+                lds_dma16(src + CD::UO + nt * 2048 + i * 1024 + lane * 16,
+                          dst + L::OFF_U + cs * L::PER + 2048 + i * 1024);
+            }
+        }
+        if (lane < D / 4) lds_dma16(src + CD::GAM + lane * 16, dst + L::OFF_G);
+        // gate logits [token][16 columns] of each consumer's tile: lane -> (token, half row)
+#pragma unroll
+        for (int cs = 0; cs < NCONS; ++cs) {
+            const int nt = grp * NCONS + cs;
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int64_t t = c * C + 32 * i + (lane >> 1);
+                if (t < T)
+                    lds_dma16(gz + ((b * T + t) * H + h) * D + 16 * nt + 8 * (lane & 1),
+                              dst + L::OFF_Z + cs * L::ZB + i * 1024);
+            }
+        }
+    };
+
+    // consumer state: S[ct][i] = S[16ct + 4g4 + i][col]
+    const int nt = grp * NCONS + (producer ? 0 : wave);
+    const int col = 16 * nt + m16;
+    floatx4 S[NCT];
+    if (!producer) {
+        const float* s0 = p.s0 ? p.s0 + unit * (int64_t)D * D : nullptr;
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) S[ct][i] = s0 ? s0[(16 * ct + 4 * g4 + i) * D + col] : 0.f;
+    }
+    typename Out::raw_t* gy = static_cast<typename Out::raw_t*>(p.out);
+    auto yrow = [&](int64_t t) { return ((b * T + t) * H + h) * D + col; };
+
+    if (producer) {
+        if (NC > 0) issue(0);
+        wait_vm_zero();
+    }
+    bare_barrier();
+
+    for (int64_t ci = 0; ci < NC; ++ci) {
+        if (producer) {
+            if (ci + 1 < NC) issue(ci + 1);  // the slot of chunk ci - 1, released by the last barrier
+            wait_vm_zero();                   // chunk ci + 1 resident before the barrier below
+        } else {
+            const unsigned char* st = smem + (ci % L::NSTAGE) * L::STAGE;
+            const _Float16* sw = reinterpret_cast<const _Float16*>(st + CD::W);
+            const _Float16* sq = reinterpret_cast<const _Float16*>(st + CD::QE);
+            const _Float16* sk = reinterpret_cast<const _Float16*>(st + CD::KBT);
+            const _Float16* su = reinterpret_cast<const _Float16*>(st + L::OFF_U + wave * L::PER);
+            const float* sg = reinterpret_cast<const float*>(st + L::OFF_G);
+            const uint16_t* sz = reinterpret_cast<const uint16_t*>(st + L::OFF_Z + wave * L::ZB);
+            const int64_t tbase = ci * C;
+            // state as the B operand: logical k = 8g4 + j of step kb is channel cmap(kb, g4, j)
+            half8 Sb[KB];
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) Sb[kb] = pack_h8(S[2 * kb], S[2 * kb + 1]);
+            floatx4 U[4], O[4];
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) {
+                U[mt] = unpack_h4(ld_h4(su + (mt * 64 + lane) * 4));        // U~
+                O[mt] = unpack_h4(ld_h4(su + 1024 + (mt * 64 + lane) * 4)); // Uo
+#pragma unroll
+                for (int kb = 0; kb < KB; ++kb) {
+                    U[mt] = mma_f16_k32(ld_h8(sw + ((mt * KB + kb) * 64 + lane) * 8), Sb[kb], U[mt]);  // U~ - W S
+                    O[mt] = mma_f16_k32(ld_h8(sq + ((mt * KB + kb) * 64 + lane) * 8), Sb[kb], O[mt]);  // Uo + Qe S
+                }
+            }
+            // S <- Diag(Gamma) S + Kbar^T U
+            half8 Ub[2];
+#pragma unroll
+            for (int u = 0; u < 2; ++u) Ub[u] = pack_h8(U[2 * u], U[2 * u + 1]);
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct) {
+                const float4 gm = *reinterpret_cast<const float4*>(sg + 16 * ct + 4 * g4);
+                floatx4 acc;
+                acc[0] = gm.x * S[ct][0];
+                acc[1] = gm.y * S[ct][1];
+                acc[2] = gm.z * S[ct][2];
+                acc[3] = gm.w * S[ct][3];
+#pragma unroll
+                for (int u = 0; u < 2; ++u) acc = mma_f16_k32(ld_h8(sk + ((ct * 2 + u) * 64 + lane) * 8), Ub[u], acc);
+                S[ct] = acc;
+            }
+            // gated output
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int64_t t = tbase + 16 * mt + 4 * g4 + i;
+                    const int tl = 16 * mt + 4 * g4 + i;
+                    if (t < T) gy[yrow(t)] = Out::from_float(O[mt][i] * sigmoidf_(bf16_bits_to_float(sz[tl * 16 + m16])));
+                }
+            wait_lgkm_zero();  // every LDS read of this slot has returned
+        }
+        bare_barrier();
+    }
+
+    if (!producer && p.sT) {
+        float* sT = p.sT + unit * (int64_t)D * D;
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sT[(16 * ct + 4 * g4 + i) * D + col] = S[ct][i];
+    }
+}
+
+// ---------------------------------------------------------------------------
+template <int D, class Out, int NCONS>
+static hipError_t launch_d(const PrepParams& pp, const RecurParams& rp, hipStream_t stream) {
+    using LP = PrepL<D>;
+    using LR = RecL<D, NCONS>;
+    const int64_t units = rp.B * rp.H;
+    if (pp.NC > 0) {
+        auto kp = kda_prep64_kernel<D>;
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kp),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)LP::TOTAL);
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(kp, dim3((unsigned)(units * pp.NC)), dim3(256), LP::TOTAL, stream, pp);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    auto kr = kda_rec64_kernel<D, Out, NCONS>;
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kr),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)LR::TOTAL);
+    if (e != hipSuccess) return e;
+    constexpr int G = D / (16 * NCONS);
+    const int64_t blocks = (units * G + 7) / 8 * 8;
+    hipLaunchKernelGGL(kr, dim3((unsigned)blocks), dim3((NCONS + 1) * 64), LR::TOTAL, stream, rp);
+    return hipGetLastError();
+}
+
+}  // namespace c64
+
+int64_t prefill64_card_bytes(int D) {
+    return D == 128 ? c64::Card<128>::BYTES : D == 64 ? c64::Card<64>::BYTES : -1;
+}
+
+int64_t prefill64_blocks(int D, int64_t units, int64_t nc) {
+    (void)D;
+    return units * nc;
+}
+
+hipError_t launch_prefill64(int D, int out_bf16, const PrepParams& pp, const RecurParams& rp,
+                            hipStream_t stream) {
+    if (D == 128)
+        return out_bf16 ? c64::launch_d<128, InBF16, 1>(pp, rp, stream)
+                        : c64::launch_d<128, InF32, 1>(pp, rp, stream);
+    if (D == 64)
+        return out_bf16 ? c64::launch_d<64, InBF16, 1>(pp, rp, stream)
+                        : c64::launch_d<64, InF32, 1>(pp, rp, stream);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace kda

@@ -32,4 +32,9 @@ bool prefill_supported(int bf16, int C, int D);
 hipError_t launch_prefill(int bf16, int out_bf16, int C, int D, const PrepParams& pp,
                           const RecurParams& rp, hipStream_t stream);
 
+// bf16 inputs, 64-token chunks (kda_chunk64.hip)
+int64_t prefill64_card_bytes(int D);
+hipError_t launch_prefill64(int D, int out_bf16, const PrepParams& pp, const RecurParams& rp,
+                            hipStream_t stream);
+
 }  // namespace kda

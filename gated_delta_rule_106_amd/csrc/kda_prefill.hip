@@ -138,8 +138,8 @@ void kda_prep_kernel(PrepParams p) {
 
     const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
     const int m16 = lane & 15, g4 = lane >> 4;
-    const int n = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int64_t T = p.T, H = p.H;
+    const int64_t n = blockIdx.x % p.NC, b = (blockIdx.x / p.NC) / H, h = (blockIdx.x / p.NC) % H;
     const int64_t t0 = (int64_t)n * C;
     const raw_t* gq = static_cast<const raw_t*>(p.q);
     const raw_t* gk = static_cast<const raw_t*>(p.k);
@@ -712,7 +712,7 @@ static hipError_t launch_t(const PrepParams& pp, const RecurParams& rp, hipStrea
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kp),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)LP::TOTAL);
         if (e != hipSuccess) return e;
-        dim3 grid((unsigned)pp.NC, (unsigned)pp.H, (unsigned)pp.B);
+        dim3 grid((unsigned)(pp.NC * pp.H * pp.B));
         hipLaunchKernelGGL(kp, grid, dim3(256), LP::TOTAL, stream, pp);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
@@ -747,9 +747,10 @@ hipError_t launch_prefill(int bf16, int out_bf16, int C, int D, const PrepParams
     if (C == CC && D == DD)                                                        \
         return bf16 ? launch_o<CC, DD, false, InBF16>(out_bf16, pp, rp, stream)   \
                     : launch_o<CC, DD, true, InF32>(out_bf16, pp, rp, stream);
+    if (C == 64 && bf16) return launch_prefill64(D, out_bf16, pp, rp, stream);
     KDA_L(16, 64) KDA_L(32, 64) KDA_L(64, 64) KDA_L(16, 128) KDA_L(32, 128)
 #undef KDA_L
-    if (C == 64 && D == 128 && bf16) return launch_o<64, 128, false, InBF16>(out_bf16, pp, rp, stream);
+    if (C == 64 && bf16) return launch_prefill64(D, out_bf16, pp, rp, stream);
     return hipErrorInvalidValue;
 }
 
