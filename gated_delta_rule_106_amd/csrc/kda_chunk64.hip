@@ -6,7 +6,8 @@
 // "Compute paradigm" and "Hierarchical chunking of linear attention"), laid out
 // for throughput on CDNA4:
 //
-// kda_prep64_kernel  one workgroup (4 waves) per (b, h, chunk).  Wave a owns the
+// kda_prep64_kernel  persistent workgroups of 4 waves, one (b, h, chunk) item at a
+//   time with the next item's inputs prefetched into registers.  Wave a owns the
 //   16-token tile a of the chunk and keeps it in registers in MFMA operand
 //   layout (lane = token, 4 consecutive key channels per 16-channel tile).  The
 //   cumulative log-decay is a DPP prefix scan across the 16 lanes of a row.
@@ -16,9 +17,9 @@
 //   factor stays below 2^116 given the 0.67 % retention floor):
 //       KR = k 2^{P},  QR = q 2^{P},  KC = k 2^{-P},  KE = k 2^{tau - P},
 //   P = prefix sum of log2(alpha) inside the tile, tau = its total.  Pair
-//   products inside a tile use KR.KC^T with a three-pass bf16 hi/lo split (the
-//   operands span 2^{+-116}); across tiles both operands are <= |k| and one
-//   fp16 pass suffices.  The unit-lower-triangular system (I + A) is solved
+//   products inside a tile use KR.KC^T on the fp32 MFMA (the operands span
+//   2^{+-116}); across tiles both operands are <= |k| and one fp16 pass
+//   suffices.  The unit-lower-triangular system (I + A) is solved
 //   with register forward substitution on the four 16x16 diagonal blocks and
 //   fp32 MFMA block products for the rest.  The remaining contractions are
 //   arranged so that their accumulators come out in exactly the fragment
@@ -119,6 +120,21 @@ __device__ __forceinline__ floatx4 mma_f32_k16(const float4& a, const floatx4& b
     return acc;
 }
 
+__device__ __forceinline__ void wait_vm_zero() { __builtin_amdgcn_s_waitcnt(0x0F70); }   // vmcnt(0)
+__device__ __forceinline__ void wait_lgkm_zero() { __builtin_amdgcn_s_waitcnt(0xC07F); } // lgkmcnt(0)
+// workgroup barrier without the implicit memory fence of __syncthreads():
+// each wave waits explicitly for exactly what the next phase needs
+__device__ __forceinline__ void bare_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+// barrier that orders LDS only: global stores issued before it keep draining
+__device__ __forceinline__ void lds_barrier() {
+    wait_lgkm_zero();
+    bare_barrier();
+}
+
 // ---------------------------------------------------------------------------
 template <int D>
 struct Card {
@@ -146,23 +162,26 @@ struct PrepL {
     static constexpr int64_t B_LINV = 64 * SA * 4;
     static constexpr int64_t B_KE = B_KEF > B_LINV ? B_KEF : B_LINV;
     static constexpr int64_t OFF_BETA = 0;                     // fp32 [64]
-    static constexpr int64_t OFF_TAU = 256;                    // fp32 [4][D]: log2 decay of each tile
-    static constexpr int64_t OFF_KE = OFF_TAU + 4 * D * 4;     // KE fragments; later Linv fp32 [64][SA]
+    static constexpr int64_t OFF_ETAU = 256;                   // fp32 [4][D]: decay over each tile
+    static constexpr int64_t OFF_KE = OFF_ETAU + 4 * D * 4;    // KE fragments; later Linv fp32 [64][SA]
     static constexpr int64_t OFF_KT = OFF_KE + B_KE;           // fp16 K~^T [D][ST]; later -W^T
     static constexpr int64_t OFF_KBT = OFF_KT + D * ST * 2;    // fp16 Kbar^T [D][ST]
     static constexpr int64_t OFF_VT = OFF_KBT + D * ST * 2;    // fp16 V^T [D][ST]
     static constexpr int64_t OFF_Q = OFF_VT + D * ST * 2;      // fp16 Q~ [64][SR]
-    static constexpr int64_t OFF_A = OFF_Q + 64 * SR * 2;      // fp32 A [64][SA]; later T fp16 [64][SP]
+    static constexpr int64_t OFF_A = OFF_Q + 64 * SR * 2;      // fp32 A [64][SA]
     static constexpr int64_t OFF_P = OFF_A + 64 * SA * 4;      // fp16 P [64][SP]
-    static constexpr int64_t TOTAL = OFF_P + 64 * SP * 2;
+    static constexpr int64_t OFF_T = OFF_P + 64 * SP * 2;      // fp16 T [64][SP]
+    static constexpr int64_t TOTAL = OFF_T + 64 * SP * 2;
     static_assert(TOTAL <= 160 * 1024, "prep LDS budget");
     static_assert(OFF_KE % 16 == 0 && OFF_KT % 16 == 0 && OFF_KBT % 16 == 0 && OFF_VT % 16 == 0 &&
-                      OFF_Q % 16 == 0 && OFF_A % 16 == 0 && OFF_P % 16 == 0,
+                      OFF_Q % 16 == 0 && OFF_A % 16 == 0 && OFF_P % 16 == 0 && OFF_T % 16 == 0,
                   "prep LDS alignment");
 };
 
 // ---------------------------------------------------------------------------
-// kernel 1: the update card of one (b, h, chunk)
+// kernel 1: update cards.  Persistent: each workgroup walks (b, h, chunk) items
+// with a stride of the grid size and prefetches the next item's raw inputs into
+// registers while it builds the current card.
 template <int D>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void kda_prep64_kernel(PrepParams p) {
@@ -172,7 +191,7 @@ void kda_prep64_kernel(PrepParams p) {
     constexpr int SR = L::SR, ST = L::ST, SA = L::SA, SP = L::SP;
     extern __shared__ __align__(16) unsigned char smem[];
     float* s_beta = reinterpret_cast<float*>(smem + L::OFF_BETA);
-    float* s_tau = reinterpret_cast<float*>(smem + L::OFF_TAU);
+    float* s_etau = reinterpret_cast<float*>(smem + L::OFF_ETAU);
     _Float16* s_ke = reinterpret_cast<_Float16*>(smem + L::OFF_KE);
     float* s_linv = reinterpret_cast<float*>(smem + L::OFF_KE);
     _Float16* s_kt = reinterpret_cast<_Float16*>(smem + L::OFF_KT);
@@ -180,313 +199,346 @@ void kda_prep64_kernel(PrepParams p) {
     _Float16* s_vt = reinterpret_cast<_Float16*>(smem + L::OFF_VT);
     _Float16* s_q = reinterpret_cast<_Float16*>(smem + L::OFF_Q);
     float* s_a = reinterpret_cast<float*>(smem + L::OFF_A);
-    _Float16* s_t = reinterpret_cast<_Float16*>(smem + L::OFF_A);
     _Float16* s_p = reinterpret_cast<_Float16*>(smem + L::OFF_P);
+    _Float16* s_t = reinterpret_cast<_Float16*>(smem + L::OFF_T);
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int m16 = lane & 15, g4 = lane >> 4;
+    const int a = wave;             // this wave's 16-token tile
+    const int rl = 16 * a + m16;    // this lane's token within the chunk
     const int64_t NC = p.NC, T = p.T, H = p.H;
-    const int64_t blk = blockIdx.x;
-    const int64_t n = blk % NC, unit = blk / NC;
-    const int64_t b = unit / H, h = unit % H;
-    const int64_t t0 = n * C;
+    const int64_t items = p.B * H * NC;
     const uint16_t* gq = static_cast<const uint16_t*>(p.q);
     const uint16_t* gk = static_cast<const uint16_t*>(p.k);
     const uint16_t* gv = static_cast<const uint16_t*>(p.v);
     const uint16_t* gla = static_cast<const uint16_t*>(p.la);
     const uint16_t* gbeta = static_cast<const uint16_t*>(p.beta);
     const bool clamp = p.clamp != 0;
-    unsigned char* card = static_cast<unsigned char*>(p.ws) + (unit * NC + n) * CD::BYTES;
 
-    // ---- phase 1 (per tile): wave a holds token 16a + m16 and, per 32-channel
-    //      K-step kb, the 8 key channels cmap(kb, g4, 0..7)
-    const int a = wave;
-    const int rl = 16 * a + m16;
-    const int64_t tok = t0 + rl;
-    const bool valid = tok < T;
-    const int64_t row = (b * T + (valid ? tok : 0)) * H + h;
-    uint2 rq[NCT], rk[NCT], rv[NCT], rla[NCT];
+    // raw inputs of token rl: per 16-channel tile ct, the 4 bf16 channels 16ct + 4g4 .. +3
+    uint2 nq[NCT], nk[NCT], nv[NCT], nla[NCT];
+    uint16_t nbeta;
+    auto fetch = [&](int64_t it) {
+        const int64_t n = it % NC, unit = it / NC;
+        const int64_t b = unit / H, h = unit % H;
+        const int64_t tok = n * C + rl;
+        const int64_t row = (b * T + (tok < T ? tok : T - 1)) * H + h;  // in bounds; zeroed below
 #pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) {
-        const int64_t off = row * D + 16 * ct + 4 * g4;
-        if (valid) {
-            rq[ct] = *reinterpret_cast<const uint2*>(gq + off);
-            rk[ct] = *reinterpret_cast<const uint2*>(gk + off);
-            rv[ct] = *reinterpret_cast<const uint2*>(gv + off);
-            rla[ct] = *reinterpret_cast<const uint2*>(gla + off);
-        } else {
-            rq[ct] = rk[ct] = rv[ct] = rla[ct] = make_uint2(0u, 0u);
+        for (int ct = 0; ct < NCT; ++ct) {
+            const int64_t off = row * D + 16 * ct + 4 * g4;
+            nq[ct] = *reinterpret_cast<const uint2*>(gq + off);
+            nk[ct] = *reinterpret_cast<const uint2*>(gk + off);
+            nv[ct] = *reinterpret_cast<const uint2*>(gv + off);
+            nla[ct] = *reinterpret_cast<const uint2*>(gla + off);
         }
-    }
-    const float beta_mine = valid ? bf16_bits_to_float(gbeta[row]) : 0.f;
-    if (g4 == 0) s_beta[rl] = beta_mine;
-
+        nbeta = gbeta[row];
+    };
     auto elem = [](const uint2& w, int i) -> float {
         const uint32_t x = (i < 2) ? w.x : w.y;
         return (i & 1) ? __uint_as_float(x & 0xffff0000u) : __uint_as_float(x << 16);
     };
 
-    half8 kr16[KB], qr16[KB];
-    floatx4 accA = zero4(), accP = zero4();
+    int64_t item = blockIdx.x;
+    if (item < items) fetch(item);
+    for (; item < items; item += gridDim.x) {
+        const int64_t n = item % NC;
+        const int64_t t0 = n * C;
+        const bool valid = t0 + rl < T;
+        unsigned char* card = static_cast<unsigned char*>(p.ws) + item * CD::BYTES;
+        uint2 rq[NCT], rk[NCT], rv[NCT], rla[NCT];
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-        bf16x8 krh, krl, qrh, qrl, kch, kcl;
-        half8 ke;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int ct = 2 * kb + (j >> 2), i = j & 3;
-            const float l = clamp_log_alpha(elem(rla[ct], i), clamp) * kLog2e;
-            const float P = row_scan16(l);       // log2 decay from the tile start, inclusive
-            const float tau = row_last(P);       // log2 decay over the whole tile
-            const float E = fast_exp2(P);        // <= 1
-            const float Einv = fast_exp2(-P);    // >= 1 and < 2^116 under the floor
-            const float F = fast_exp2(tau - P);  // decay from after this token to the tile end, <= 1
-            const float kf = elem(rk[ct], i), qf = elem(rq[ct], i);
-            const float KR = kf * E, QR = qf * E, KC = kf * Einv;
-            kr16[kb][j] = static_cast<_Float16>(KR);
-            qr16[kb][j] = static_cast<_Float16>(QR);
-            ke[j] = static_cast<_Float16>(kf * F);
-            __bf16 hi, lo;
-            split_bf16(KR, hi, lo);
-            krh[j] = hi;
-            krl[j] = lo;
-            split_bf16(QR, hi, lo);
-            qrh[j] = hi;
-            qrl[j] = lo;
-            split_bf16(KC, hi, lo);
-            kch[j] = hi;
-            kcl[j] = lo;
-            const int c = cmap(kb, g4, j);
-            if (m16 == 0) s_tau[a * D + c] = tau;
-            s_vt[c * ST + rl] = static_cast<_Float16>(elem(rv[ct], i));
+        for (int ct = 0; ct < NCT; ++ct) {  // identity tokens past the end: q = k = v = log alpha = 0
+            const uint2 z2 = make_uint2(0u, 0u);
+            rq[ct] = valid ? nq[ct] : z2;
+            rk[ct] = valid ? nk[ct] : z2;
+            rv[ct] = valid ? nv[ct] : z2;
+            rla[ct] = valid ? nla[ct] : z2;
         }
-        // pair products inside the tile: A_rs ~ KR_r . KC_s, P_rs ~ QR_r . KC_s
-        accA = mma_bf16_k32(krh, kch, accA);
-        accA = mma_bf16_k32(krh, kcl, accA);
-        accA = mma_bf16_k32(krl, kch, accA);
-        accP = mma_bf16_k32(qrh, kch, accP);
-        accP = mma_bf16_k32(qrh, kcl, accP);
-        accP = mma_bf16_k32(qrl, kch, accP);
-        // KE fragment of this tile: the B operand of the pairs (later tile, this tile)
-        *reinterpret_cast<half8*>(s_ke + ((a * KB + kb) * 64 + lane) * 8) = ke;
-    }
-    // diagonal blocks of A (strictly lower, rows scaled by beta) and P (lower)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int r = 4 * g4 + i, s = m16;
-        const float br = __shfl(beta_mine, r);
-        s_a[(16 * a + r) * SA + 16 * a + s] = (s < r) ? br * accA[i] : 0.f;
-        s_p[(16 * a + r) * SP + 16 * a + s] = static_cast<_Float16>((s <= r) ? accP[i] : 0.f);
-#pragma unroll
-        for (int bb = 0; bb < NSUB; ++bb)
-            if (bb > a) s_p[(16 * a + r) * SP + 16 * bb + s] = static_cast<_Float16>(0.f);
-    }
-    __syncthreads();  // (1) tile decays, KE fragments, V^T and beta are in LDS
+        const float beta_mine = valid ? bf16_bits_to_float(nbeta) : 0.f;
+        if (item + gridDim.x < items) fetch(item + gridDim.x);
 
-    // ---- phase 2 (per tile): chunk-relative operands and the pairs with earlier tiles
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-        half4 q_lo, q_hi;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int c = cmap(kb, g4, j);
-            float before = 0.f, after = 0.f;
-#pragma unroll
-            for (int a2 = 0; a2 < NSUB; ++a2) {
-                const float tv = s_tau[a2 * D + c];
-                if (a2 < a) before += tv;
-                if (a2 > a) after += tv;
-            }
-            const float erho = fast_exp2(before);  // decay from the chunk start to the tile start
-            const float eaft = fast_exp2(after);   // decay from the tile end to the chunk end
-            const _Float16 kt = static_cast<_Float16>(static_cast<float>(kr16[kb][j]) * erho);
-            const _Float16 qt = static_cast<_Float16>(static_cast<float>(qr16[kb][j]) * erho);
-            const float ke = static_cast<float>(s_ke[((a * KB + kb) * 64 + lane) * 8 + j]);
-            s_kt[c * ST + rl] = kt;                                          // K~ = k 2^{g}
-            s_kbt[c * ST + rl] = static_cast<_Float16>(ke * eaft);           // Kbar = k 2^{g_C - g}
-            if (j < 4) q_lo[j] = qt; else q_hi[j - 4] = qt;
-        }
-        *reinterpret_cast<half4*>(s_q + rl * SR + 32 * kb + 4 * g4) = q_lo;       // Q~ = q 2^{g}
-        *reinterpret_cast<half4*>(s_q + rl * SR + 32 * kb + 16 + 4 * g4) = q_hi;
-    }
-    // Gamma = 2^{g_C} per key channel
-    if (tid < D) {
-        float gsum = 0.f;
-#pragma unroll
-        for (int a2 = 0; a2 < NSUB; ++a2) gsum += s_tau[a2 * D + tid];
-        reinterpret_cast<float*>(card + CD::GAM)[tid] = fast_exp2(gsum);
-    }
-    // pairs (a, bb), bb < a: reference point at the end of tile a-1, both operands <= |k|
-    for (int bb = 0; bb < a; ++bb) {
-        floatx4 pa = zero4(), pp = zero4();
+        // ---- phase 1 (per tile): decay inside the tile, in-tile pair products
+        if (g4 == 0) s_beta[rl] = beta_mine;
+        half8 kr16[KB], qr16[KB];
+        floatx4 accA = zero4(), accP = zero4();
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
-            const half8 ke = ld_h8(s_ke + ((bb * KB + kb) * 64 + lane) * 8);
-            half8 col;
+            half8 ke;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int ct = 2 * kb + (j >> 2), i = j & 3;
+                const float l = clamp_log_alpha(elem(rla[ct], i), clamp) * kLog2e;
+                const float P = row_scan16(l);      // log2 decay from the tile start, inclusive
+                const float E = fast_exp2(P);       // <= 1
+                const float Einv = fast_exp2(-P);   // >= 1, < 2^116 under the floor
+                const float Et = row_last(E);       // decay over the whole tile
+                const float kf = elem(rk[ct], i), qf = elem(rq[ct], i);
+                const float KR = kf * E, QR = qf * E, KC = kf * Einv;
+                // K-step (kb, j): lane group g4 supplies channel cmap(kb, g4, j) to both operands
+                accA = mma_f32_k4(KR, KC, accA);
+                accP = mma_f32_k4(QR, KC, accP);
+                kr16[kb][j] = static_cast<_Float16>(KR);
+                qr16[kb][j] = static_cast<_Float16>(QR);
+                ke[j] = static_cast<_Float16>(kf * (Einv * Et));  // decay from after this token to the tile end
+                const int c = cmap(kb, g4, j);
+                if (m16 == 0) s_etau[a * D + c] = Et;
+                s_vt[c * ST + rl] = static_cast<_Float16>(elem(rv[ct], i));
+            }
+            // KE fragment of this tile: the B operand of the pairs (later tile, this tile)
+            *reinterpret_cast<half8*>(s_ke + ((a * KB + kb) * 64 + lane) * 8) = ke;
+        }
+        // diagonal blocks of A (strictly lower, rows scaled by beta) and P (lower)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = 4 * g4 + i, s = m16;
+            const float br = __shfl(beta_mine, r);
+            s_a[(16 * a + r) * SA + 16 * a + s] = (s < r) ? br * accA[i] : 0.f;
+            s_p[(16 * a + r) * SP + 16 * a + s] = static_cast<_Float16>((s <= r) ? accP[i] : 0.f);
+#pragma unroll
+            for (int bb = 0; bb < NSUB; ++bb)
+                if (bb > a) s_p[(16 * a + r) * SP + 16 * bb + s] = static_cast<_Float16>(0.f);
+        }
+        lds_barrier();  // (1) tile decays, KE fragments, V^T and beta are in LDS
+
+        // ---- phase 2 (per tile): chunk-relative operands and the pairs with earlier tiles.
+        // Decay factors across tiles are products of the per-tile decays 2^{tau}.
+        floatx4 pa[NSUB - 1], pp[NSUB - 1];
+#pragma unroll
+        for (int bb = 0; bb < NSUB - 1; ++bb) pa[bb] = pp[bb] = zero4();
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+            float et[NSUB][8];
+#pragma unroll
+            for (int a2 = 0; a2 < NSUB; ++a2) {
+                const float4 lo = *reinterpret_cast<const float4*>(s_etau + a2 * D + 32 * kb + 4 * g4);
+                const float4 hi = *reinterpret_cast<const float4*>(s_etau + a2 * D + 32 * kb + 16 + 4 * g4);
+                et[a2][0] = lo.x; et[a2][1] = lo.y; et[a2][2] = lo.z; et[a2][3] = lo.w;
+                et[a2][4] = hi.x; et[a2][5] = hi.y; et[a2][6] = hi.z; et[a2][7] = hi.w;
+            }
+            half8 q8;
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
                 const int c = cmap(kb, g4, j);
-                float mid = 0.f;  // decay over the tiles strictly between bb and a
-                for (int a2 = bb + 1; a2 < a; ++a2) mid += s_tau[a2 * D + c];
-                col[j] = static_cast<_Float16>(static_cast<float>(ke[j]) * fast_exp2(mid));
+                float erho = 1.f, eaft = 1.f;  // decay before this tile / after this tile
+#pragma unroll
+                for (int a2 = 0; a2 < NSUB; ++a2) {
+                    if (a2 < a) erho *= et[a2][j];
+                    if (a2 > a) eaft *= et[a2][j];
+                }
+                const float ke = static_cast<float>(s_ke[((a * KB + kb) * 64 + lane) * 8 + j]);
+                s_kt[c * ST + rl] = static_cast<_Float16>(static_cast<float>(kr16[kb][j]) * erho);  // K~ = k 2^{g}
+                s_kbt[c * ST + rl] = static_cast<_Float16>(ke * eaft);                             // Kbar = k 2^{g_C - g}
+                q8[j] = static_cast<_Float16>(static_cast<float>(qr16[kb][j]) * erho);             // Q~ = q 2^{g}
             }
-            pa = mma_f16_k32(kr16[kb], col, pa);
-            pp = mma_f16_k32(qr16[kb], col, pp);
+            half4 qlo, qhi;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                qlo[j] = q8[j];
+                qhi[j] = q8[4 + j];
+            }
+            *reinterpret_cast<half4*>(s_q + rl * SR + 32 * kb + 4 * g4) = qlo;
+            *reinterpret_cast<half4*>(s_q + rl * SR + 32 * kb + 16 + 4 * g4) = qhi;
+            // pairs (a, bb), bb < a: reference point at the end of tile a-1; both operands <= |k|
+#pragma unroll
+            for (int bb = 0; bb < NSUB - 1; ++bb) {
+                if (bb < a) {
+                    const half8 keb = ld_h8(s_ke + ((bb * KB + kb) * 64 + lane) * 8);
+                    half8 col;
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) {
+                        float f = 1.f;  // decay over the tiles strictly between bb and a
+#pragma unroll
+                        for (int a2 = 1; a2 < NSUB - 1; ++a2)
+                            if (a2 > bb && a2 < a) f *= et[a2][j];
+                        col[j] = static_cast<_Float16>(static_cast<float>(keb[j]) * f);
+                    }
+                    pa[bb] = mma_f16_k32(kr16[kb], col, pa[bb]);
+                    pp[bb] = mma_f16_k32(qr16[kb], col, pp[bb]);
+                }
+            }
         }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int r = 4 * g4 + i;
-            s_a[(16 * a + r) * SA + 16 * bb + m16] = s_beta[16 * a + r] * pa[i];
-            s_p[(16 * a + r) * SP + 16 * bb + m16] = static_cast<_Float16>(pp[i]);
-        }
-    }
-    __syncthreads();  // (2) A, P, K~^T, Kbar^T, Q~ complete
-
-    // ---- phase 3: Linv = (I + A)^{-1}, unit lower triangular, blocked by 16
-    if (wave == 0) {  // diagonal blocks: lane group g4 = block, lane m16 = column
-        const int ab = g4, j = m16;
-        const float* Ab = s_a + (16 * ab) * SA + 16 * ab;
-        float x[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) x[r] = (r == j) ? 1.f : 0.f;
-#pragma unroll
-        for (int r = 1; r < 16; ++r) {
-            float acc = x[r];
-#pragma unroll
-            for (int q = 0; q < r; ++q) acc -= Ab[r * SA + q] * x[q];
-            x[r] = acc;
-        }
-        float* Xb = s_linv + (16 * ab) * SA + 16 * ab;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) Xb[r * SA + j] = x[r];
-    }
-    __syncthreads();
-    // off-diagonal blocks by block diagonal d: Linv_{a,a-d} = -X_a sum_c A_{a,c} Linv_{c,a-d}
-    auto blk_a = [&](int r, int c) { return s_a + (16 * r) * SA + 16 * c; };
-    auto blk_x = [&](int r, int c) { return s_linv + (16 * r) * SA + 16 * c; };
-    auto mm = [&](const float* mp, const float* np, floatx4 acc) {  // acc += M N (row-major blocks)
-        const float4 av = *reinterpret_cast<const float4*>(mp + m16 * SA + 4 * g4);
-        floatx4 bv;
-#pragma unroll
-        for (int s = 0; s < 4; ++s) bv[s] = np[(4 * g4 + s) * SA + m16];
-        return mma_f32_k16(av, bv, acc);
-    };
-#pragma unroll
-    for (int d = 1; d < NSUB; ++d) {
-        if (wave >= d) {
-            floatx4 y = zero4();
-            for (int c = wave - d; c < wave; ++c) y = mm(blk_a(wave, c), blk_x(c, wave - d), y);
-            const float4 xv = *reinterpret_cast<const float4*>(blk_x(wave, wave) + m16 * SA + 4 * g4);
-            const floatx4 z = mma_f32_k16(xv, y, zero4());
-            float* dst = blk_x(wave, wave - d);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) dst[(4 * g4 + i) * SA + m16] = -z[i];
-        }
-        __syncthreads();
-    }
-    // T = Linv diag(beta), fp16, zero above the diagonal
-    for (int e = tid; e < C * C; e += 256) {
-        const int r = e >> 6, s = e & 63;
-        const float v = (s <= r) ? s_linv[r * SA + s] * s_beta[s] : 0.f;
-        s_t[r * SP + s] = static_cast<_Float16>(v);
-    }
-    __syncthreads();  // (3) T complete
-
-    // ---- phase 4: card.  Jobs 0..KB-1: key-channel pair kb (W, Qe, Kbar^T);
-    //      jobs KB..2KB-1: value-column pair (U~, Uo)
-    // sum over tokens s < 16 (mt + 1) of A_row[s] * B_row[s] (rows in LDS, tokens contiguous).
-    // A trailing 16-token step is a K = 32 step with its upper half zeroed: one MFMA shape
-    // per accumulator chain.
-    auto kloop = [&](const _Float16* arow, const _Float16* brow, int mt, floatx4 acc) {
-        const int kend = 16 * (mt + 1);
-        int s0 = 0;
-        for (; s0 + 32 <= kend; s0 += 32)
-            acc = mma_f16_k32(ld_h8(arow + s0 + 8 * g4), ld_h8(brow + s0 + 8 * g4), acc);
-        if (s0 < kend) {
-            const half4 z4 = {0, 0, 0, 0};
-            acc = mma_f16_k32(cat_h8(ld_h4(arow + s0 + 4 * g4), z4), cat_h8(ld_h4(brow + s0 + 4 * g4), z4), acc);
-        }
-        return acc;
-    };
-    for (int job = wave; job < 2 * KB; job += 4) {
-        if (job < KB) {
-            const int kb = job;
-            floatx4 wt[2][4];
-#pragma unroll
-            for (int cl = 0; cl < 2; ++cl)
-#pragma unroll
-                for (int mt = 0; mt < 4; ++mt)  // W^T tile = K~^T T^T
-                    wt[cl][mt] = kloop(s_kt + (16 * (2 * kb + cl) + m16) * ST, s_t + (16 * mt + m16) * SP, mt,
-                                       zero4());
-#pragma unroll
-            for (int mt = 0; mt < 4; ++mt) {
-                floatx4 n0, n1;
+        for (int bb = 0; bb < NSUB - 1; ++bb) {
+            if (bb < a) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    n0[i] = -wt[0][mt][i];
-                    n1[i] = -wt[1][mt][i];
-                }
-                *reinterpret_cast<half8*>(card + CD::W + ((mt * KB + kb) * 64 + lane) * 16) = pack_h8(n0, n1);
-            }
-            // -W^T over this pair's rows of K~^T (only this wave reads them)
-#pragma unroll
-            for (int cl = 0; cl < 2; ++cl)
-#pragma unroll
-                for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        s_kt[(16 * (2 * kb + cl) + 4 * g4 + i) * ST + 16 * mt + m16] =
-                            static_cast<_Float16>(-wt[cl][mt][i]);
-            // Qe^T tile = Q~^T + (-W^T) P^T
-#pragma unroll
-            for (int mt = 0; mt < 4; ++mt) {
-                floatx4 qe[2];
-#pragma unroll
-                for (int cl = 0; cl < 2; ++cl) {
-                    const floatx4 init = unpack_h4(ld_h4(s_q + (16 * mt + m16) * SR + 16 * (2 * kb + cl) + 4 * g4));
-                    qe[cl] = kloop(s_kt + (16 * (2 * kb + cl) + m16) * ST, s_p + (16 * mt + m16) * SP, mt, init);
-                }
-                *reinterpret_cast<half8*>(card + CD::QE + ((mt * KB + kb) * 64 + lane) * 16) = pack_h8(qe[0], qe[1]);
-            }
-            // Kbar^T fragments of the two 16-channel tiles
-#pragma unroll
-            for (int cl = 0; cl < 2; ++cl) {
-                const int ct = 2 * kb + cl;
-                const _Float16* kr = s_kbt + (16 * ct + m16) * ST;
-#pragma unroll
-                for (int u = 0; u < 2; ++u)
-                    *reinterpret_cast<half8*>(card + CD::KBT + ((ct * 2 + u) * 64 + lane) * 16) =
-                        cat_h8(ld_h4(kr + 32 * u + 4 * g4), ld_h4(kr + 32 * u + 16 + 4 * g4));
-            }
-        } else {
-            const int np = job - KB;
-            floatx4 ut[2][4];
-#pragma unroll
-            for (int cl = 0; cl < 2; ++cl) {
-                const int nt = 2 * np + cl;
-#pragma unroll
-                for (int mt = 0; mt < 4; ++mt) {  // U~ tile = T V
-                    ut[cl][mt] = kloop(s_t + (16 * mt + m16) * SP, s_vt + (16 * nt + m16) * ST, mt, zero4());
-                    *reinterpret_cast<half4*>(card + CD::UT + ((nt * 4 + mt) * 64 + lane) * 8) = pack_h4(ut[cl][mt]);
-                }
-#pragma unroll
-                for (int mt = 0; mt < 4; ++mt) {  // Uo tile = P U~ (U~ accumulators as the B operand)
-                    floatx4 acc = zero4();
-                    const _Float16* prow = s_p + (16 * mt + m16) * SP;
-#pragma unroll
-                    for (int u = 0; u < 2; ++u)
-                        if (2 * u <= mt)
-                            acc = mma_f16_k32(cat_h8(ld_h4(prow + 32 * u + 4 * g4), ld_h4(prow + 32 * u + 16 + 4 * g4)),
-                                              pack_h8(ut[cl][2 * u], ut[cl][2 * u + 1]), acc);
-                    *reinterpret_cast<half4*>(card + CD::UO + ((nt * 4 + mt) * 64 + lane) * 8) = pack_h4(acc);
+                    const int r = 4 * g4 + i;
+                    s_a[(16 * a + r) * SA + 16 * bb + m16] = s_beta[16 * a + r] * pa[bb][i];
+                    s_p[(16 * a + r) * SP + 16 * bb + m16] = static_cast<_Float16>(pp[bb][i]);
                 }
             }
         }
+        // Gamma = 2^{g_C} per key channel
+        if (tid < D) {
+            float gm = 1.f;
+#pragma unroll
+            for (int a2 = 0; a2 < NSUB; ++a2) gm *= s_etau[a2 * D + tid];
+            reinterpret_cast<float*>(card + CD::GAM)[tid] = gm;
+        }
+        lds_barrier();  // (2) A, P, K~^T, Kbar^T, Q~ complete
+
+        // ---- phase 3: Linv = (I + A)^{-1} (unit lower triangular, blocked by 16) and
+        //      T = Linv diag(beta) in fp16
+        if (wave == 0) {  // diagonal blocks: lane group g4 = block, lane m16 = column
+            const int ab = g4, j = m16;
+            const float* Ab = s_a + (16 * ab) * SA + 16 * ab;
+            float x[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) x[r] = (r == j) ? 1.f : 0.f;
+#pragma unroll
+            for (int r = 1; r < 16; ++r) {
+                float acc = x[r];
+#pragma unroll
+                for (int q = 0; q < r; ++q) acc -= Ab[r * SA + q] * x[q];
+                x[r] = acc;
+            }
+            const float bj = s_beta[16 * ab + j];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                s_linv[(16 * ab + r) * SA + 16 * ab + j] = x[r];
+                s_t[(16 * ab + r) * SP + 16 * ab + j] = static_cast<_Float16>(x[r] * bj);
+            }
+        }
+        lds_barrier();
+        // off-diagonal blocks by block diagonal d: Linv_{a,a-d} = -X_a sum_c A_{a,c} Linv_{c,a-d}
+        auto blk_a = [&](int r, int c) { return s_a + (16 * r) * SA + 16 * c; };
+        auto blk_x = [&](int r, int c) { return s_linv + (16 * r) * SA + 16 * c; };
+        auto mm = [&](const float* mp, const float* np, floatx4 acc) {  // acc += M N (row-major blocks)
+            const float4 av = *reinterpret_cast<const float4*>(mp + m16 * SA + 4 * g4);
+            floatx4 bv;
+#pragma unroll
+            for (int s = 0; s < 4; ++s) bv[s] = np[(4 * g4 + s) * SA + m16];
+            return mma_f32_k16(av, bv, acc);
+        };
+#pragma unroll
+        for (int d = 1; d < NSUB; ++d) {
+            if (wave >= d) {
+                floatx4 y = zero4();
+                for (int c = wave - d; c < wave; ++c) y = mm(blk_a(wave, c), blk_x(c, wave - d), y);
+                const float4 xv = *reinterpret_cast<const float4*>(blk_x(wave, wave) + m16 * SA + 4 * g4);
+                const floatx4 z = mma_f32_k16(xv, y, zero4());
+                float* dst = blk_x(wave, wave - d);
+                const float bcol = s_beta[16 * (wave - d) + m16];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    dst[(4 * g4 + i) * SA + m16] = -z[i];
+                    s_t[(16 * wave + 4 * g4 + i) * SP + 16 * (wave - d) + m16] = static_cast<_Float16>(-z[i] * bcol);
+                }
+            }
+            lds_barrier();
+        }
+
+        // ---- phase 4: card.  Jobs 0..KB-1: key-channel pair kb (W, Qe, Kbar^T);
+        //      jobs KB..2KB-1: value-column pair (U~, Uo)
+        // sum over tokens s < 16 (mt + 1) of A_row[s] * B_row[s] (rows in LDS, tokens contiguous).
+        // A trailing 16-token step is a K = 32 step with its upper half zeroed: one MFMA shape
+        // per accumulator chain.
+        auto kloop = [&](const _Float16* arow, const _Float16* brow, int mt, floatx4 acc) {
+            const int kend = 16 * (mt + 1);
+            int s0 = 0;
+            for (; s0 + 32 <= kend; s0 += 32)
+                acc = mma_f16_k32(ld_h8(arow + s0 + 8 * g4), ld_h8(brow + s0 + 8 * g4), acc);
+            if (s0 < kend) {
+                const half4 z4 = {0, 0, 0, 0};
+                acc = mma_f16_k32(cat_h8(ld_h4(arow + s0 + 4 * g4), z4), cat_h8(ld_h4(brow + s0 + 4 * g4), z4), acc);
+            }
+            return acc;
+        };
+        for (int job = wave; job < 2 * KB; job += 4) {
+            if (job < KB) {
+                const int kb = job;
+                floatx4 wt[2][4];
+#pragma unroll
+                for (int cl = 0; cl < 2; ++cl)
+#pragma unroll
+                    for (int mt = 0; mt < 4; ++mt)  // W^T tile = K~^T T^T
+                        wt[cl][mt] = kloop(s_kt + (16 * (2 * kb + cl) + m16) * ST, s_t + (16 * mt + m16) * SP, mt,
+                                           zero4());
+#pragma unroll
+                for (int mt = 0; mt < 4; ++mt) {
+                    floatx4 n0, n1;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        n0[i] = -wt[0][mt][i];
+                        n1[i] = -wt[1][mt][i];
+                    }
+                    *reinterpret_cast<half8*>(card + CD::W + ((mt * KB + kb) * 64 + lane) * 16) = pack_h8(n0, n1);
+                }
+                // -W^T over this pair's rows of K~^T (only this wave reads them)
+#pragma unroll
+                for (int cl = 0; cl < 2; ++cl)
+#pragma unroll
+                    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            s_kt[(16 * (2 * kb + cl) + 4 * g4 + i) * ST + 16 * mt + m16] =
+                                static_cast<_Float16>(-wt[cl][mt][i]);
+                // Qe^T tile = Q~^T + (-W^T) P^T
+#pragma unroll
+                for (int mt = 0; mt < 4; ++mt) {
+                    floatx4 qe[2];
+#pragma unroll
+                    for (int cl = 0; cl < 2; ++cl) {
+                        const floatx4 init =
+                            unpack_h4(ld_h4(s_q + (16 * mt + m16) * SR + 16 * (2 * kb + cl) + 4 * g4));
+                        qe[cl] = kloop(s_kt + (16 * (2 * kb + cl) + m16) * ST, s_p + (16 * mt + m16) * SP, mt, init);
+                    }
+                    *reinterpret_cast<half8*>(card + CD::QE + ((mt * KB + kb) * 64 + lane) * 16) =
+                        pack_h8(qe[0], qe[1]);
+                }
+                // Kbar^T fragments of the two 16-channel tiles
+#pragma unroll
+                for (int cl = 0; cl < 2; ++cl) {
+                    const int ct = 2 * kb + cl;
+                    const _Float16* kr = s_kbt + (16 * ct + m16) * ST;
+#pragma unroll
+                    for (int u = 0; u < 2; ++u)
+                        *reinterpret_cast<half8*>(card + CD::KBT + ((ct * 2 + u) * 64 + lane) * 16) =
+                            cat_h8(ld_h4(kr + 32 * u + 4 * g4), ld_h4(kr + 32 * u + 16 + 4 * g4));
+                }
+            } else {
+                const int np = job - KB;
+                floatx4 ut[2][4];
+#pragma unroll
+                for (int cl = 0; cl < 2; ++cl) {
+                    const int nt = 2 * np + cl;
+#pragma unroll
+                    for (int mt = 0; mt < 4; ++mt) {  // U~ tile = T V
+                        ut[cl][mt] = kloop(s_t + (16 * mt + m16) * SP, s_vt + (16 * nt + m16) * ST, mt, zero4());
+                        *reinterpret_cast<half4*>(card + CD::UT + ((nt * 4 + mt) * 64 + lane) * 8) =
+                            pack_h4(ut[cl][mt]);
+                    }
+#pragma unroll
+                    for (int mt = 0; mt < 4; ++mt) {  // Uo tile = P U~ (U~ accumulators as the B operand)
+                        floatx4 acc = zero4();
+                        const _Float16* prow = s_p + (16 * mt + m16) * SP;
+#pragma unroll
+                        for (int u = 0; u < 2; ++u)
+                            if (2 * u <= mt)
+                                acc = mma_f16_k32(
+                                    cat_h8(ld_h4(prow + 32 * u + 4 * g4), ld_h4(prow + 32 * u + 16 + 4 * g4)),
+                                    pack_h8(ut[cl][2 * u], ut[cl][2 * u + 1]), acc);
+                        *reinterpret_cast<half4*>(card + CD::UO + ((nt * 4 + mt) * 64 + lane) * 8) = pack_h4(acc);
+                    }
+                }
+            }
+        }
+        lds_barrier();  // LDS is reused by the next item
     }
 }
 
 // ---------------------------------------------------------------------------
 // kernel 2: sequential pass over the cards
+//
+// Per workgroup: NCONS consumer waves (one 16-column value tile each), one
+// producer wave and one epilogue wave.  In iteration n
+//   - the consumers run chunk n out of LDS slot n % 2 and leave the chunk's
+//     read-out O in an LDS tile,
+//   - the producer streams the card of chunk n+1 into slot (n+1) % 2 (direct
+//     global->LDS) and touches the card of chunk n+1+PD so that it is in L2
+//     when streamed,
+//   - the epilogue computes sigmoid(z) of chunk n and stores the gated output
+//     of chunk n-1 (y = O * sigmoid(z), 16-byte stores).
 template <int D, int NCONS>
 struct RecL {
     using CD = Card<D>;
@@ -498,11 +550,18 @@ struct RecL {
     static constexpr int64_t OFF_G = OFF_Z + NCONS * ZB;
     static constexpr int64_t STAGE = OFF_G + D * 4;
     static constexpr int NSTAGE = 2;
-    static constexpr int64_t TOTAL = NSTAGE * STAGE;
+    static constexpr int OST = 20;                        // fp32 [token][16 columns] row stride (floats)
+    static constexpr int64_t OTILE = 64 * OST * 4;        // one consumer's 64 x 16 fp32 tile
+    static constexpr int64_t OFF_O = NSTAGE * STAGE;      // read-out O  [2][NCONS] tiles
+    static constexpr int64_t OFF_S = OFF_O + 2 * NCONS * OTILE;  // sigmoid(z) [2][NCONS] tiles
+    static constexpr int64_t OFF_TRASH = OFF_S + 2 * NCONS * OTILE;  // target of the L2-warming loads
+    static constexpr int64_t TOTAL = OFF_TRASH + 256;
     static constexpr int LOADS = (int)(SH / 1024) + NCONS * 6 + 1;  // direct-to-LDS instructions per stage
+    static constexpr int PD = 4;                                     // L2 prefetch distance (chunks)
+    static constexpr int TOUCH = (int)((SH + 8191) / 8192) + NCONS * 2 + 1 + NCONS;  // touches per chunk
     static_assert(TOTAL <= 160 * 1024, "recurrence LDS budget");
-    static_assert(STAGE % 16 == 0, "stage alignment");
-    static_assert(LOADS <= 63, "one stage must fit the wave's outstanding-load counter");
+    static_assert(STAGE % 16 == 0 && OFF_O % 16 == 0, "stage alignment");
+    static_assert(LOADS <= 63 && TOUCH <= 63, "outstanding-load counter");
 };
 
 __device__ __forceinline__ void lds_dma16(const void* g, void* l) {
@@ -510,24 +569,26 @@ __device__ __forceinline__ void lds_dma16(const void* g, void* l) {
                                             reinterpret_cast<uintptr_t>(l)),
                                      16, 0, 0);
 }
-
-__device__ __forceinline__ void wait_vm_zero() { __builtin_amdgcn_s_waitcnt(0x0F70); }   // vmcnt(0)
-__device__ __forceinline__ void wait_lgkm_zero() { __builtin_amdgcn_s_waitcnt(0xC07F); } // lgkmcnt(0)
-// workgroup barrier without the implicit memory fence of __syncthreads():
-// each wave waits explicitly for exactly what the next phase needs
-__device__ __forceinline__ void bare_barrier() {
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
+__device__ __forceinline__ void lds_dma4(const void* g, void* l) {
+    __builtin_amdgcn_global_load_lds(g, reinterpret_cast<__attribute__((address_space(3))) void*>(
+                                            reinterpret_cast<uintptr_t>(l)),
+                                     4, 0, 0);
+}
+// vmcnt(n) for small compile-time n (expcnt and lgkmcnt left unconstrained)
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(N >= 0 && N <= 63, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
 }
 
 template <int D, class Out, int NCONS>
-__global__ __launch_bounds__((NCONS + 1) * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__((NCONS + 2) * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void kda_rec64_kernel(RecurParams p) {
     using CD = Card<D>;
     using L = RecL<D, NCONS>;
     constexpr int NCT = D / 16, KB = D / 32;
     constexpr int G = D / (16 * NCONS);  // workgroups per head
+    constexpr int OST = L::OST;
     extern __shared__ __align__(16) unsigned char smem[];
 
     const int lane = lane_id(), wave = wave_id();
@@ -543,9 +604,15 @@ void kda_rec64_kernel(RecurParams p) {
     const int64_t b = unit / H, h = unit % H;
     const unsigned char* cards = static_cast<const unsigned char*>(p.ws) + unit * NC * CD::BYTES;
     const bool producer = wave == NCONS;
+    const bool epilogue = wave == NCONS + 1;
+    const bool consumer = wave < NCONS;
     const uint16_t* gz = static_cast<const uint16_t*>(p.gate);
+    float* obuf = reinterpret_cast<float*>(smem + L::OFF_O);
+    float* sbuf = reinterpret_cast<float*>(smem + L::OFF_S);
+    auto zrow = [&](int64_t t) { return ((b * T + t) * H + h) * D; };  // element offset of (b, t, h, 0)
 
-    auto issue = [&](int64_t c) {  // producer: card c -> ring slot c % NSTAGE
+    // ---- producer helpers
+    auto issue = [&](int64_t c) {  // card c -> ring slot c % NSTAGE
         const unsigned char* src = cards + c * CD::BYTES;
         unsigned char* dst = smem + (c % L::NSTAGE) * L::STAGE;
 #pragma unroll
@@ -568,37 +635,116 @@ void kda_rec64_kernel(RecurParams p) {
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
                 const int64_t t = c * C + 32 * i + (lane >> 1);
-                if (t < T)
-                    lds_dma16(gz + ((b * T + t) * H + h) * D + 16 * nt + 8 * (lane & 1),
-                              dst + L::OFF_Z + cs * L::ZB + i * 1024);
+                if (t < T) lds_dma16(gz + zrow(t) + 16 * nt + 8 * (lane & 1), dst + L::OFF_Z + cs * L::ZB + i * 1024);
+            }
+        }
+    };
+    auto touch = [&](int64_t c) {  // bring card c (this group's part) and its gate rows into L2
+        const unsigned char* src = cards + c * CD::BYTES;
+        void* trash = smem + L::OFF_TRASH;
+#pragma unroll
+        for (int i = 0; i < (int)((L::SH + 8191) / 8192); ++i)
+            if (i * 8192 + lane * 128 < L::SH) lds_dma4(src + i * 8192 + lane * 128, trash);
+#pragma unroll
+        for (int cs = 0; cs < NCONS; ++cs) {
+            const int nt = grp * NCONS + cs;
+            if (lane < 16) lds_dma4(src + CD::UT + nt * 2048 + lane * 128, trash);
+            if (lane < 16) lds_dma4(src + CD::UO + nt * 2048 + lane * 128, trash);
+        }
+        if (lane * 128 < D * 4) lds_dma4(src + CD::GAM + lane * 128, trash);
+#pragma unroll
+        for (int cs = 0; cs < NCONS; ++cs) {
+            const int64_t t = c * C + lane;
+            if (t < T) lds_dma4(gz + zrow(t) + 16 * (grp * NCONS + cs), trash);
+        }
+    };
+    auto sigmoid_tile = [&](int64_t c) {  // sigmoid(z) of chunk c: lane = token
+        const unsigned char* st = smem + (c % L::NSTAGE) * L::STAGE;
+#pragma unroll
+        for (int cs = 0; cs < NCONS; ++cs) {
+            const uint4* zr = reinterpret_cast<const uint4*>(st + L::OFF_Z + cs * L::ZB + lane * 32);
+            const uint4 z0 = zr[0], z1 = zr[1];
+            const uint32_t w[8] = {z0.x, z0.y, z0.z, z0.w, z1.x, z1.y, z1.z, z1.w};
+            float* srow = sbuf + ((c & 1) * NCONS + cs) * (64 * OST) + lane * OST;
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                float4 sg;
+                sg.x = sigmoidf_(__uint_as_float(w[2 * q4] << 16));
+                sg.y = sigmoidf_(__uint_as_float(w[2 * q4] & 0xffff0000u));
+                sg.z = sigmoidf_(__uint_as_float(w[2 * q4 + 1] << 16));
+                sg.w = sigmoidf_(__uint_as_float(w[2 * q4 + 1] & 0xffff0000u));
+                *reinterpret_cast<float4*>(srow + 4 * q4) = sg;
+            }
+        }
+    };
+    typename Out::raw_t* gy = static_cast<typename Out::raw_t*>(p.out);
+    auto output = [&](int64_t c) {  // y = O * sigmoid(z) of chunk c: lane = token, 16 columns per tile
+        const int64_t t = c * C + lane;
+#pragma unroll
+        for (int cs = 0; cs < NCONS; ++cs) {
+            const float* orow = obuf + ((c & 1) * NCONS + cs) * (64 * OST) + lane * OST;
+            const float* srow = sbuf + ((c & 1) * NCONS + cs) * (64 * OST) + lane * OST;
+            float y[16];
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                const float4 o = *reinterpret_cast<const float4*>(orow + 4 * q4);
+                const float4 s = *reinterpret_cast<const float4*>(srow + 4 * q4);
+                y[4 * q4 + 0] = o.x * s.x;
+                y[4 * q4 + 1] = o.y * s.y;
+                y[4 * q4 + 2] = o.z * s.z;
+                y[4 * q4 + 3] = o.w * s.w;
+            }
+            if (t < T) {
+                typename Out::raw_t* dst = gy + zrow(t) + 16 * (grp * NCONS + cs);
+                if constexpr (sizeof(typename Out::raw_t) == 4) {
+#pragma unroll
+                    for (int q4 = 0; q4 < 4; ++q4)
+                        reinterpret_cast<float4*>(dst)[q4] = make_float4(y[4 * q4], y[4 * q4 + 1], y[4 * q4 + 2], y[4 * q4 + 3]);
+                } else {
+                    uint32_t w[8];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        w[e] = (uint32_t)Out::from_float(y[2 * e]) | ((uint32_t)Out::from_float(y[2 * e + 1]) << 16);
+                    reinterpret_cast<uint4*>(dst)[0] = make_uint4(w[0], w[1], w[2], w[3]);
+                    reinterpret_cast<uint4*>(dst)[1] = make_uint4(w[4], w[5], w[6], w[7]);
+                }
             }
         }
     };
 
     // consumer state: S[ct][i] = S[16ct + 4g4 + i][col]
-    const int nt = grp * NCONS + (producer ? 0 : wave);
+    const int nt = grp * NCONS + (consumer ? wave : 0);
     const int col = 16 * nt + m16;
     floatx4 S[NCT];
-    if (!producer) {
+    if (consumer) {
         const float* s0 = p.s0 ? p.s0 + unit * (int64_t)D * D : nullptr;
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
             for (int i = 0; i < 4; ++i) S[ct][i] = s0 ? s0[(16 * ct + 4 * g4 + i) * D + col] : 0.f;
     }
-    typename Out::raw_t* gy = static_cast<typename Out::raw_t*>(p.out);
-    auto yrow = [&](int64_t t) { return ((b * T + t) * H + h) * D + col; };
 
-    if (producer) {
-        if (NC > 0) issue(0);
+    if (producer && NC > 0) {
+        issue(0);
+        for (int64_t c = 1; c <= L::PD && c < NC; ++c) touch(c);
         wait_vm_zero();
     }
-    bare_barrier();
+    lds_barrier();
 
     for (int64_t ci = 0; ci < NC; ++ci) {
         if (producer) {
-            if (ci + 1 < NC) issue(ci + 1);  // the slot of chunk ci - 1, released by the last barrier
-            wait_vm_zero();                   // chunk ci + 1 resident before the barrier below
+            if (ci + 1 < NC) {
+                issue(ci + 1);  // the slot of chunk ci - 1, released by the last barrier
+                if (ci + 1 + L::PD < NC) {
+                    touch(ci + 1 + L::PD);
+                    wait_vm<L::TOUCH>();  // the card of chunk ci + 1 has landed
+                } else {
+                    wait_vm_zero();
+                }
+            }
+        } else if (epilogue) {
+            sigmoid_tile(ci);
+            if (ci >= 1) output(ci - 1);
         } else {
             const unsigned char* st = smem + (ci % L::NSTAGE) * L::STAGE;
             const _Float16* sw = reinterpret_cast<const _Float16*>(st + CD::W);
@@ -606,8 +752,26 @@ void kda_rec64_kernel(RecurParams p) {
             const _Float16* sk = reinterpret_cast<const _Float16*>(st + CD::KBT);
             const _Float16* su = reinterpret_cast<const _Float16*>(st + L::OFF_U + wave * L::PER);
             const float* sg = reinterpret_cast<const float*>(st + L::OFF_G);
-            const uint16_t* sz = reinterpret_cast<const uint16_t*>(st + L::OFF_Z + wave * L::ZB);
-            const int64_t tbase = ci * C;
+            // every operand of the chunk into registers first, then the MFMA chains
+            half8 wf[4][KB], qf[4][KB], kf[NCT][2];
+            half4 ut[4], uo[4];
+            float4 gm[NCT];
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) {
+#pragma unroll
+                for (int kb = 0; kb < KB; ++kb) {
+                    wf[mt][kb] = ld_h8(sw + ((mt * KB + kb) * 64 + lane) * 8);
+                    qf[mt][kb] = ld_h8(sq + ((mt * KB + kb) * 64 + lane) * 8);
+                }
+                ut[mt] = ld_h4(su + (mt * 64 + lane) * 4);
+                uo[mt] = ld_h4(su + 1024 + (mt * 64 + lane) * 4);
+            }
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct) {
+                kf[ct][0] = ld_h8(sk + ((ct * 2 + 0) * 64 + lane) * 8);
+                kf[ct][1] = ld_h8(sk + ((ct * 2 + 1) * 64 + lane) * 8);
+                gm[ct] = *reinterpret_cast<const float4*>(sg + 16 * ct + 4 * g4);
+            }
             // state as the B operand: logical k = 8g4 + j of step kb is channel cmap(kb, g4, j)
             half8 Sb[KB];
 #pragma unroll
@@ -615,45 +779,43 @@ void kda_rec64_kernel(RecurParams p) {
             floatx4 U[4], O[4];
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt) {
-                U[mt] = unpack_h4(ld_h4(su + (mt * 64 + lane) * 4));        // U~
-                O[mt] = unpack_h4(ld_h4(su + 1024 + (mt * 64 + lane) * 4)); // Uo
-#pragma unroll
-                for (int kb = 0; kb < KB; ++kb) {
-                    U[mt] = mma_f16_k32(ld_h8(sw + ((mt * KB + kb) * 64 + lane) * 8), Sb[kb], U[mt]);  // U~ - W S
-                    O[mt] = mma_f16_k32(ld_h8(sq + ((mt * KB + kb) * 64 + lane) * 8), Sb[kb], O[mt]);  // Uo + Qe S
-                }
+                U[mt] = unpack_h4(ut[mt]);  // U~
+                O[mt] = unpack_h4(uo[mt]);  // Uo
             }
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                for (int mt = 0; mt < 4; ++mt) {
+                    U[mt] = mma_f16_k32(wf[mt][kb], Sb[kb], U[mt]);  // U~ - W S
+                    O[mt] = mma_f16_k32(qf[mt][kb], Sb[kb], O[mt]);  // Uo + Qe S
+                }
             // S <- Diag(Gamma) S + Kbar^T U
             half8 Ub[2];
 #pragma unroll
             for (int u = 0; u < 2; ++u) Ub[u] = pack_h8(U[2 * u], U[2 * u + 1]);
 #pragma unroll
             for (int ct = 0; ct < NCT; ++ct) {
-                const float4 gm = *reinterpret_cast<const float4*>(sg + 16 * ct + 4 * g4);
-                floatx4 acc;
-                acc[0] = gm.x * S[ct][0];
-                acc[1] = gm.y * S[ct][1];
-                acc[2] = gm.z * S[ct][2];
-                acc[3] = gm.w * S[ct][3];
-#pragma unroll
-                for (int u = 0; u < 2; ++u) acc = mma_f16_k32(ld_h8(sk + ((ct * 2 + u) * 64 + lane) * 8), Ub[u], acc);
-                S[ct] = acc;
+                S[ct][0] *= gm[ct].x;
+                S[ct][1] *= gm[ct].y;
+                S[ct][2] *= gm[ct].z;
+                S[ct][3] *= gm[ct].w;
             }
-            // gated output
+#pragma unroll
+            for (int u = 0; u < 2; ++u)
+#pragma unroll
+                for (int ct = 0; ct < NCT; ++ct) S[ct] = mma_f16_k32(kf[ct][u], Ub[u], S[ct]);
+            // read-out O -> LDS tile [token][column] for the epilogue
+            float* orow = obuf + ((ci & 1) * NCONS + wave) * (64 * OST);
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int64_t t = tbase + 16 * mt + 4 * g4 + i;
-                    const int tl = 16 * mt + 4 * g4 + i;
-                    if (t < T) gy[yrow(t)] = Out::from_float(O[mt][i] * sigmoidf_(bf16_bits_to_float(sz[tl * 16 + m16])));
-                }
-            wait_lgkm_zero();  // every LDS read of this slot has returned
+                for (int i = 0; i < 4; ++i) orow[(16 * mt + 4 * g4 + i) * OST + m16] = O[mt][i];
         }
-        bare_barrier();
+        lds_barrier();
     }
+    if (epilogue && NC > 0) output(NC - 1);
 
-    if (!producer && p.sT) {
+    if (consumer && p.sT) {
         float* sT = p.sT + unit * (int64_t)D * D;
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct)
@@ -673,7 +835,13 @@ static hipError_t launch_d(const PrepParams& pp, const RecurParams& rp, hipStrea
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kp),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)LP::TOTAL);
         if (e != hipSuccess) return e;
-        hipLaunchKernelGGL(kp, dim3((unsigned)(units * pp.NC)), dim3(256), LP::TOTAL, stream, pp);
+        int dev = 0, cus = 256;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+            cus = 256;
+        const int64_t items = units * pp.NC;
+        const int64_t grid = items < cus ? items : cus;  // one persistent workgroup per CU (LDS-bound)
+        hipLaunchKernelGGL(kp, dim3((unsigned)grid), dim3(256), LP::TOTAL, stream, pp);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
@@ -683,7 +851,7 @@ static hipError_t launch_d(const PrepParams& pp, const RecurParams& rp, hipStrea
     if (e != hipSuccess) return e;
     constexpr int G = D / (16 * NCONS);
     const int64_t blocks = (units * G + 7) / 8 * 8;
-    hipLaunchKernelGGL(kr, dim3((unsigned)blocks), dim3((NCONS + 1) * 64), LR::TOTAL, stream, rp);
+    hipLaunchKernelGGL(kr, dim3((unsigned)blocks), dim3((NCONS + 2) * 64), LR::TOTAL, stream, rp);
     return hipGetLastError();
 }
 

@@ -76,8 +76,9 @@ __device__ __forceinline__ void split_bf16(float x, __bf16& hi, __bf16& lo) {
     lo = static_cast<__bf16>(x - static_cast<float>(hi));
 }
 
+// logistic sigmoid with the hardware exp2 and reciprocal (v_rcp_f32, about 1 ulp)
 __device__ __forceinline__ float sigmoidf_(float z) {
-    return 1.0f / (1.0f + fast_exp2(-z * kLog2e));
+    return __builtin_amdgcn_rcpf(1.0f + fast_exp2(-z * kLog2e));
 }
 
 // Clamp of log(alpha) to [ln 0.0067, 0] (retention floor and retention <= 1).
