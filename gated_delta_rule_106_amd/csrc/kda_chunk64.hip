@@ -42,6 +42,8 @@
 // with c(x, g, j) = 32x + 4g + j (j < 4), 32x + 16 + 4g + (j - 4) (j >= 4):
 // the K-index order in which two stacked accumulator tiles (rows 4g .. 4g+3
 // in lane group g) feed the next MFMA directly as its B operand.
+#include <type_traits>
+
 #include "kda_device.h"
 #include "kda_prefill.h"
 
@@ -553,8 +555,12 @@ struct RecL {
     static constexpr int OST = 20;                        // fp32 [token][16 columns] row stride (floats)
     static constexpr int64_t OTILE = 64 * OST * 4;        // one consumer's 64 x 16 fp32 tile
     static constexpr int64_t OFF_O = NSTAGE * STAGE;      // read-out O  [2][NCONS] tiles
+    // sigmoid(z) tiles: fp32 with one consumer; fp16 (relative error 2^-11) when two consumers
+    // must share the LDS budget
+    using sig_t = typename std::conditional<NCONS == 1, float, _Float16>::type;
+    static constexpr int64_t STILE = 64 * OST * (int64_t)sizeof(sig_t);
     static constexpr int64_t OFF_S = OFF_O + 2 * NCONS * OTILE;  // sigmoid(z) [2][NCONS] tiles
-    static constexpr int64_t OFF_TRASH = OFF_S + 2 * NCONS * OTILE;  // target of the L2-warming loads
+    static constexpr int64_t OFF_TRASH = OFF_S + 2 * NCONS * STILE;  // target of the L2-warming loads
     static constexpr int64_t TOTAL = OFF_TRASH + 256;
     static constexpr int LOADS = (int)(SH / 1024) + NCONS * 6 + 1;  // direct-to-LDS instructions per stage
     static constexpr int PD = 4;                                     // L2 prefetch distance (chunks)
@@ -608,7 +614,8 @@ void kda_rec64_kernel(RecurParams p) {
     const bool consumer = wave < NCONS;
     const uint16_t* gz = static_cast<const uint16_t*>(p.gate);
     float* obuf = reinterpret_cast<float*>(smem + L::OFF_O);
-    float* sbuf = reinterpret_cast<float*>(smem + L::OFF_S);
+    using sig_t = typename L::sig_t;
+    sig_t* sbuf = reinterpret_cast<sig_t*>(smem + L::OFF_S);
     auto zrow = [&](int64_t t) { return ((b * T + t) * H + h) * D; };  // element offset of (b, t, h, 0)
 
     // ---- producer helpers
@@ -665,15 +672,12 @@ void kda_rec64_kernel(RecurParams p) {
             const uint4* zr = reinterpret_cast<const uint4*>(st + L::OFF_Z + cs * L::ZB + lane * 32);
             const uint4 z0 = zr[0], z1 = zr[1];
             const uint32_t w[8] = {z0.x, z0.y, z0.z, z0.w, z1.x, z1.y, z1.z, z1.w};
-            float* srow = sbuf + ((c & 1) * NCONS + cs) * (64 * OST) + lane * OST;
+            sig_t* srow = sbuf + ((c & 1) * NCONS + cs) * (64 * OST) + lane * OST;
 #pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) {
-                float4 sg;
-                sg.x = sigmoidf_(__uint_as_float(w[2 * q4] << 16));
-                sg.y = sigmoidf_(__uint_as_float(w[2 * q4] & 0xffff0000u));
-                sg.z = sigmoidf_(__uint_as_float(w[2 * q4 + 1] << 16));
-                sg.w = sigmoidf_(__uint_as_float(w[2 * q4 + 1] & 0xffff0000u));
-                *reinterpret_cast<float4*>(srow + 4 * q4) = sg;
+            for (int e = 0; e < 16; ++e) {
+                const uint32_t word = w[e >> 1];
+                const float z = (e & 1) ? __uint_as_float(word & 0xffff0000u) : __uint_as_float(word << 16);
+                srow[e] = static_cast<sig_t>(sigmoidf_(z));
             }
         }
     };
@@ -683,16 +687,15 @@ void kda_rec64_kernel(RecurParams p) {
 #pragma unroll
         for (int cs = 0; cs < NCONS; ++cs) {
             const float* orow = obuf + ((c & 1) * NCONS + cs) * (64 * OST) + lane * OST;
-            const float* srow = sbuf + ((c & 1) * NCONS + cs) * (64 * OST) + lane * OST;
+            const sig_t* srow = sbuf + ((c & 1) * NCONS + cs) * (64 * OST) + lane * OST;
             float y[16];
 #pragma unroll
             for (int q4 = 0; q4 < 4; ++q4) {
                 const float4 o = *reinterpret_cast<const float4*>(orow + 4 * q4);
-                const float4 s = *reinterpret_cast<const float4*>(srow + 4 * q4);
-                y[4 * q4 + 0] = o.x * s.x;
-                y[4 * q4 + 1] = o.y * s.y;
-                y[4 * q4 + 2] = o.z * s.z;
-                y[4 * q4 + 3] = o.w * s.w;
+                y[4 * q4 + 0] = o.x * static_cast<float>(srow[4 * q4 + 0]);
+                y[4 * q4 + 1] = o.y * static_cast<float>(srow[4 * q4 + 1]);
+                y[4 * q4 + 2] = o.z * static_cast<float>(srow[4 * q4 + 2]);
+                y[4 * q4 + 3] = o.w * static_cast<float>(srow[4 * q4 + 3]);
             }
             if (t < T) {
                 typename Out::raw_t* dst = gy + zrow(t) + 16 * (grp * NCONS + cs);
@@ -868,9 +871,16 @@ int64_t prefill64_blocks(int D, int64_t units, int64_t nc) {
 
 hipError_t launch_prefill64(int D, int out_bf16, const PrepParams& pp, const RecurParams& rp,
                             hipStream_t stream) {
-    if (D == 128)
+    // one consumer per workgroup has the shortest chain per chunk; with enough (b, h)
+    // sequences to fill the GPU, two consumers share each streamed card instead
+    const bool wide = rp.B * rp.H >= 64;
+    if (D == 128) {
+        if (wide)
+            return out_bf16 ? c64::launch_d<128, InBF16, 2>(pp, rp, stream)
+                            : c64::launch_d<128, InF32, 2>(pp, rp, stream);
         return out_bf16 ? c64::launch_d<128, InBF16, 1>(pp, rp, stream)
                         : c64::launch_d<128, InF32, 1>(pp, rp, stream);
+    }
     if (D == 64)
         return out_bf16 ? c64::launch_d<64, InBF16, 1>(pp, rp, stream)
                         : c64::launch_d<64, InF32, 1>(pp, rp, stream);

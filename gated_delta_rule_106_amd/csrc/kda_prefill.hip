@@ -358,14 +358,15 @@ void kda_prep_kernel(PrepParams p) {
                     }
                     acc = mma_f16_k32(av, bv, acc);
                 }
-                if (k0 < kend) {
-                    half4 av, bv;
+                if (k0 < kend) {  // last 16 tokens: a K = 32 step with its upper half zeroed
+                    half8 av, bv;
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
                         av[j] = static_cast<_Float16>(arow[k0 + 4 * g4 + j]);
                         bv[j] = static_cast<_Float16>(bval(k0 + 4 * g4 + j));
+                        av[4 + j] = bv[4 + j] = static_cast<_Float16>(0.f);
                     }
-                    acc = mma_f16_k16(av, bv, acc);
+                    acc = mma_f16_k32(av, bv, acc);
                 }
             }
         }
@@ -427,14 +428,15 @@ void kda_prep_kernel(PrepParams p) {
                 }
                 acc = mma_f16_k32(av, bv, acc);
             }
-            if (k0 < kend) {
-                half4 av, bv;
+            if (k0 < kend) {  // last 16 tokens: a K = 32 step with its upper half zeroed
+                half8 av, bv;
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     av[j] = static_cast<_Float16>(arow[k0 + 4 * g4 + j]);
                     bv[j] = static_cast<_Float16>(bval(k0 + 4 * g4 + j));
+                    av[4 + j] = bv[4 + j] = static_cast<_Float16>(0.f);
                 }
-                acc = mma_f16_k16(av, bv, acc);
+                acc = mma_f16_k32(av, bv, acc);
             }
         }
         if (!isU) {
@@ -660,13 +662,17 @@ void kda_recur_kernel(RecurParams p) {
                     }
                     acc = mma_f16_k32(av, bv, acc);
                 }
-                if constexpr (NMT % 2 == 1) {
+                if constexpr (NMT % 2 == 1) {  // odd tile count: a K = 32 step with its upper half zeroed
                     const int u = NMT - 1;
-                    const half4 av = *reinterpret_cast<const half4*>(kr + 16 * u + 4 * g4);
-                    half4 bv;
+                    const half4 a4 = *reinterpret_cast<const half4*>(kr + 16 * u + 4 * g4);
+                    half8 av, bv;
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) bv[j] = static_cast<_Float16>(U[u][j]);
-                    acc = mma_f16_k16(av, bv, acc);
+                    for (int j = 0; j < 4; ++j) {
+                        av[j] = a4[j];
+                        bv[j] = static_cast<_Float16>(U[u][j]);
+                        av[4 + j] = bv[4 + j] = static_cast<_Float16>(0.f);
+                    }
+                    acc = mma_f16_k32(av, bv, acc);
                 }
                 S[ct] = acc;
             }
