@@ -272,7 +272,8 @@ def main():
             torch.cuda.empty_cache()
 
     traffic = stored_traffic("prefill_" + head.name)
-    roof = {"kernel": "kda_chunk_fwd (kda_prep_kernel + kda_recur_kernel)", "bound": "hbm",
+    roof = {"kernel": "kda_chunk_fwd = kda_prep64_kernel + kda_rec64_kernel (one call, two launches)",
+            "bound": "hbm",
             "achieved": pre["hbm_gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": pre["hbm_gbs"] / HBM_PEAK_GBS, "traffic": traffic}
     out = {
