@@ -27,10 +27,12 @@
 //   is written with coalesced 16-byte stores.
 //
 // kda_rec64_kernel  one workgroup per (b, h, group of NCONS 16-column value
-//   tiles): NCONS consumer waves carry the fp32 state of their columns in MFMA
-//   accumulators across all chunks; one producer wave streams the next card
-//   into a double-buffered LDS ring with direct global->LDS loads.  Workgroups
-//   of one head are placed on one XCD so its cards are fetched into one L2.
+//   tiles): per tile a chain wave carries the fp32 state of its columns in MFMA
+//   accumulators across all chunks and an output wave forms the chunk's
+//   read-out; four producer waves stage the next cards through registers into
+//   a double-buffered LDS ring and gate and store y.
+//   Workgroups of one head are placed on one XCD so its cards are fetched
+//   into one L2.
 //
 // Card of one (b, h, chunk), fp16 unless noted (lane l = 16 g + m):
 //   W   [mt][kb] 64 lanes x 8: -W[16mt + m][c(kb, g, j)]
@@ -52,6 +54,8 @@ namespace c64 {
 
 constexpr int C = 64;
 constexpr int NSUB = 4;
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 template <int CTRL>
 __device__ __forceinline__ float dpp_mov(float x) {
@@ -532,54 +536,50 @@ void kda_prep64_kernel(PrepParams p) {
 // ---------------------------------------------------------------------------
 // kernel 2: sequential pass over the cards
 //
-// Per workgroup: NCONS consumer waves (one 16-column value tile each), one
-// producer wave and one epilogue wave.  In iteration n
-//   - the consumers run chunk n out of LDS slot n % 2 and leave the chunk's
-//     read-out O in an LDS tile,
-//   - the producer streams the card of chunk n+1 into slot (n+1) % 2 (direct
-//     global->LDS) and touches the card of chunk n+1+PD so that it is in L2
-//     when streamed,
-//   - the epilogue computes sigmoid(z) of chunk n and stores the gated output
-//     of chunk n-1 (y = O * sigmoid(z), 16-byte stores).
+// Per workgroup, for each of its NCONS 16-column value tiles, a chain wave and an
+// output wave, plus NP producer waves.  Iteration n, around the barriers A and B:
+//   chain     S_n (fp16 copy) -> LDS before A; after A: U = U~ - W S_n,
+//             S_{n+1} = Diag(Gamma) S_n + Kbar^T U (fp32 state in accumulators)
+//   output    after A: O = Uo + Qe S_n -> LDS tile
+//   producers before A: issue the loads of chunk n+2 into one of two register
+//             sets, compute sigmoid(z) of chunk n and store y = O * sigmoid(z) of
+//             chunk n-1 (a quarter of the tokens each, 16-byte stores);
+//             after A: wait for chunk n+1 (loaded one iteration earlier) and
+//             write it into LDS ring slot (n+1) % 2.
+// A card is therefore in flight for two iterations, while LDS holds only two.
 template <int D, int NCONS>
 struct RecL {
     using CD = Card<D>;
-    static constexpr int64_t SH = CD::UT;                 // W, QE, KBT: shared by all consumers
-    static constexpr int64_t PER = 2 * 4 * CD::HFRAG;     // UT + UO of one 16-column tile
-    static constexpr int64_t ZB = 64 * 16 * 2;           // gate logits of one 16-column tile (bf16)
-    static constexpr int64_t OFF_U = SH;
-    static constexpr int64_t OFF_Z = SH + NCONS * PER;
-    static constexpr int64_t OFF_G = OFF_Z + NCONS * ZB;
-    static constexpr int64_t STAGE = OFF_G + D * 4;
+    static constexpr int KB = D / 32;
+    static constexpr int NP = 4;                          // producer waves
+    static constexpr int64_t SH = CD::UT;                 // W, QE, KBT: shared by all tiles
+    // per 16-column tile: U~ slice (2 KiB), Uo slice (2 KiB), gate logits [64][16] bf16 (2 KiB)
+    static constexpr int64_t PER = 6 * 1024;
+    static constexpr int64_t OFF_U = SH;                  // tile t2 at OFF_U + t2 * PER
+    static constexpr int64_t UO_IN = 2048, Z_IN = 4096;   // offsets inside a tile block
+    static constexpr int64_t OFF_G = SH + NCONS * PER;
+    static constexpr int64_t STAGE = OFF_G + 1024;        // Gamma (D * 4 bytes) in a 1 KiB piece
     static constexpr int NSTAGE = 2;
-    static constexpr int OST = 20;                        // fp32 [token][16 columns] row stride (floats)
-    static constexpr int64_t OTILE = 64 * OST * 4;        // one consumer's 64 x 16 fp32 tile
-    static constexpr int64_t OFF_O = NSTAGE * STAGE;      // read-out O  [2][NCONS] tiles
-    // sigmoid(z) tiles: fp32 with one consumer; fp16 (relative error 2^-11) when two consumers
+    static constexpr int NPC = (int)(STAGE / 1024);       // 1 KiB pieces per card
+    static constexpr int KP = (NPC + NP - 1) / NP;        // pieces per producer
+    static constexpr int OST = 20;                        // [token][16 columns] row stride (elements)
+    static constexpr int64_t OTILE = 64 * OST * 4;        // one tile's 64 x 16 fp32 read-out
+    // sigmoid(z) tiles: fp32 with one tile; fp16 (relative error 2^-11) when two tiles
     // must share the LDS budget
     using sig_t = typename std::conditional<NCONS == 1, float, _Float16>::type;
     static constexpr int64_t STILE = 64 * OST * (int64_t)sizeof(sig_t);
-    static constexpr int64_t OFF_S = OFF_O + 2 * NCONS * OTILE;  // sigmoid(z) [2][NCONS] tiles
-    static constexpr int64_t OFF_TRASH = OFF_S + 2 * NCONS * STILE;  // target of the L2-warming loads
-    static constexpr int64_t TOTAL = OFF_TRASH + 256;
-    static constexpr int LOADS = (int)(SH / 1024) + NCONS * 6 + 1;  // direct-to-LDS instructions per stage
-    static constexpr int PD = 4;                                     // L2 prefetch distance (chunks)
-    static constexpr int TOUCH = (int)((SH + 8191) / 8192) + NCONS * 2 + 1 + NCONS;  // touches per chunk
+    static constexpr int64_t SBX = (int64_t)KB * 64 * 16;  // fp16 copy of one tile's state (B operand)
+    static constexpr int64_t OFF_O = NSTAGE * STAGE;                 // read-out O [2][NCONS]
+    static constexpr int64_t OFF_S = OFF_O + 2 * NCONS * OTILE;      // sigmoid(z) [2][NCONS]
+    static constexpr int64_t OFF_X = OFF_S + 2 * NCONS * STILE;      // state copies [NCONS]
+    static constexpr int64_t TOTAL = OFF_X + NCONS * SBX;
+    static constexpr int WAVES = 2 * NCONS + NP;
+    static_assert(STAGE % 1024 == 0 && D * 4 <= 1024, "card pieces");
     static_assert(TOTAL <= 160 * 1024, "recurrence LDS budget");
-    static_assert(STAGE % 16 == 0 && OFF_O % 16 == 0, "stage alignment");
-    static_assert(LOADS <= 63 && TOUCH <= 63, "outstanding-load counter");
+    static_assert(OFF_O % 16 == 0 && OFF_X % 16 == 0, "alignment");
+    static_assert(KP <= 63, "outstanding-load counter");
 };
 
-__device__ __forceinline__ void lds_dma16(const void* g, void* l) {
-    __builtin_amdgcn_global_load_lds(g, reinterpret_cast<__attribute__((address_space(3))) void*>(
-                                            reinterpret_cast<uintptr_t>(l)),
-                                     16, 0, 0);
-}
-__device__ __forceinline__ void lds_dma4(const void* g, void* l) {
-    __builtin_amdgcn_global_load_lds(g, reinterpret_cast<__attribute__((address_space(3))) void*>(
-                                            reinterpret_cast<uintptr_t>(l)),
-                                     4, 0, 0);
-}
 // vmcnt(n) for small compile-time n (expcnt and lgkmcnt left unconstrained)
 template <int N>
 __device__ __forceinline__ void wait_vm() {
@@ -587,14 +587,20 @@ __device__ __forceinline__ void wait_vm() {
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
 }
 
+template <int I>
+struct Int {
+    static constexpr int value = I;
+};
+
 template <int D, class Out, int NCONS>
-__global__ __launch_bounds__((NCONS + 2) * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__((2 * NCONS + 4) * 64) __attribute__((amdgpu_waves_per_eu(1, 2)))
 void kda_rec64_kernel(RecurParams p) {
     using CD = Card<D>;
     using L = RecL<D, NCONS>;
-    constexpr int NCT = D / 16, KB = D / 32;
+    constexpr int NCT = D / 16, KB = D / 32, NP = L::NP, KP = L::KP;
     constexpr int G = D / (16 * NCONS);  // workgroups per head
     constexpr int OST = L::OST;
+    static_assert(L::WAVES == 2 * NCONS + 4, "launch bounds");
     extern __shared__ __align__(16) unsigned char smem[];
 
     const int lane = lane_id(), wave = wave_id();
@@ -609,117 +615,82 @@ void kda_rec64_kernel(RecurParams p) {
     const int64_t H = p.H, T = p.T, NC = p.NC;
     const int64_t b = unit / H, h = unit % H;
     const unsigned char* cards = static_cast<const unsigned char*>(p.ws) + unit * NC * CD::BYTES;
-    const bool producer = wave == NCONS;
-    const bool epilogue = wave == NCONS + 1;
-    const bool consumer = wave < NCONS;
+    const bool chain = wave < NCONS;
+    const bool outw = wave >= NCONS && wave < 2 * NCONS;
+    const bool prod = wave >= 2 * NCONS;
+    const int pw = prod ? wave - 2 * NCONS : 0;               // producer index
+    const int cs = chain ? wave : (outw ? wave - NCONS : 0);  // value tile of a chain / output wave
     const uint16_t* gz = static_cast<const uint16_t*>(p.gate);
     float* obuf = reinterpret_cast<float*>(smem + L::OFF_O);
     using sig_t = typename L::sig_t;
     sig_t* sbuf = reinterpret_cast<sig_t*>(smem + L::OFF_S);
+    _Float16* sbx = reinterpret_cast<_Float16*>(smem + L::OFF_X + cs * L::SBX);
     auto zrow = [&](int64_t t) { return ((b * T + t) * H + h) * D; };  // element offset of (b, t, h, 0)
 
-    // ---- producer helpers
-    auto issue = [&](int64_t c) {  // card c -> ring slot c % NSTAGE
-        const unsigned char* src = cards + c * CD::BYTES;
-        unsigned char* dst = smem + (c % L::NSTAGE) * L::STAGE;
-#pragma unroll
-        for (int i = 0; i < (int)(L::SH / 1024); ++i) lds_dma16(src + i * 1024 + lane * 16, dst + i * 1024);
-#pragma unroll
-        for (int cs = 0; cs < NCONS; ++cs) {
-            const int nt = grp * NCONS + cs;
-#pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                lds_dma16(src + CD::UT + nt * 2048 + i * 1024 + lane * 16, dst + L::OFF_U + cs * L::PER + i * 1024);
-                lds_dma16(src + CD::UO + nt * 2048 + i * 1024 + lane * 16,
-                          dst + L::OFF_U + cs * L::PER + 2048 + i * 1024);
-            }
+    // ---- producers: 1 KiB pieces of a card, piece j handled by producer j % NP.
+    // Every piece is one 16-byte load per lane from a valid address (gate rows past T
+    // are clamped to the last token; their values are never stored).
+    // every producer moves exactly KP pieces; a producer short of work repeats the last
+    // piece (same data to the same LDS address), which keeps its load count uniform
+    auto piece_of = [&](int k) { const int j = pw + k * NP; return j < L::NPC ? j : L::NPC - 1; };
+    auto piece_src = [&](int64_t c, int j) __attribute__((always_inline)) -> const u32x4* {
+        const unsigned char* card = cards + c * CD::BYTES;
+        if (j < (int)(L::SH / 1024)) return reinterpret_cast<const u32x4*>(card + j * 1024) + lane;
+        int r = j - (int)(L::SH / 1024);
+        if (r < NCONS * 6) {
+            const int t2 = r / 6, q = r % 6, nt = grp * NCONS + t2;
+            if (q < 4)  // U~ (q = 0, 1) and Uo (q = 2, 3) slices of tile nt
+                return reinterpret_cast<const u32x4*>(card + (q < 2 ? CD::UT : CD::UO) + nt * 2048 + (q & 1) * 1024) + lane;
+            int64_t t = c * C + 32 * (q - 4) + (lane >> 1);
+            t = t < T ? t : T - 1;
+            return reinterpret_cast<const u32x4*>(gz + zrow(t) + 16 * nt + 8 * (lane & 1));
         }
-        if (lane < D / 4) lds_dma16(src + CD::GAM + lane * 16, dst + L::OFF_G);
-        // gate logits [token][16 columns] of each consumer's tile: lane -> (token, half row)
-#pragma unroll
-        for (int cs = 0; cs < NCONS; ++cs) {
-            const int nt = grp * NCONS + cs;
-#pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                const int64_t t = c * C + 32 * i + (lane >> 1);
-                if (t < T) lds_dma16(gz + zrow(t) + 16 * nt + 8 * (lane & 1), dst + L::OFF_Z + cs * L::ZB + i * 1024);
-            }
-        }
+        return reinterpret_cast<const u32x4*>(card + CD::GAM) + (lane % (D / 4));  // Gamma, replicated
     };
-    auto touch = [&](int64_t c) {  // bring card c (this group's part) and its gate rows into L2
-        const unsigned char* src = cards + c * CD::BYTES;
-        void* trash = smem + L::OFF_TRASH;
-#pragma unroll
-        for (int i = 0; i < (int)((L::SH + 8191) / 8192); ++i)
-            if (i * 8192 + lane * 128 < L::SH) lds_dma4(src + i * 8192 + lane * 128, trash);
-#pragma unroll
-        for (int cs = 0; cs < NCONS; ++cs) {
-            const int nt = grp * NCONS + cs;
-            if (lane < 16) lds_dma4(src + CD::UT + nt * 2048 + lane * 128, trash);
-            if (lane < 16) lds_dma4(src + CD::UO + nt * 2048 + lane * 128, trash);
-        }
-        if (lane * 128 < D * 4) lds_dma4(src + CD::GAM + lane * 128, trash);
-#pragma unroll
-        for (int cs = 0; cs < NCONS; ++cs) {
-            const int64_t t = c * C + lane;
-            if (t < T) lds_dma4(gz + zrow(t) + 16 * (grp * NCONS + cs), trash);
-        }
+    auto piece_dst = [&](int64_t c, int j) __attribute__((always_inline)) -> u32x4* {
+        return reinterpret_cast<u32x4*>(smem + (c % L::NSTAGE) * L::STAGE + (int64_t)j * 1024) + lane;
     };
-    auto sigmoid_tile = [&](int64_t c) {  // sigmoid(z) of chunk c: lane = token
+    // sigmoid and output work of one producer: 16 tokens x 4 columns per lane group
+    const int tq = 16 * pw + (lane >> 2), cq = 4 * (lane & 3);
+    auto sigmoid_part = [&](int64_t c) __attribute__((always_inline)) {
         const unsigned char* st = smem + (c % L::NSTAGE) * L::STAGE;
 #pragma unroll
-        for (int cs = 0; cs < NCONS; ++cs) {
-            const uint4* zr = reinterpret_cast<const uint4*>(st + L::OFF_Z + cs * L::ZB + lane * 32);
-            const uint4 z0 = zr[0], z1 = zr[1];
-            const uint32_t w[8] = {z0.x, z0.y, z0.z, z0.w, z1.x, z1.y, z1.z, z1.w};
-            sig_t* srow = sbuf + ((c & 1) * NCONS + cs) * (64 * OST) + lane * OST;
-#pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const uint32_t word = w[e >> 1];
-                const float z = (e & 1) ? __uint_as_float(word & 0xffff0000u) : __uint_as_float(word << 16);
-                srow[e] = static_cast<sig_t>(sigmoidf_(z));
-            }
+        for (int t2 = 0; t2 < NCONS; ++t2) {
+            const uint2 zw = *reinterpret_cast<const uint2*>(st + L::OFF_U + t2 * L::PER + L::Z_IN + tq * 32 + cq * 2);
+            sig_t* srow = sbuf + ((c & 1) * NCONS + t2) * (64 * OST) + tq * OST + cq;
+            srow[0] = static_cast<sig_t>(sigmoidf_(__uint_as_float(zw.x << 16)));
+            srow[1] = static_cast<sig_t>(sigmoidf_(__uint_as_float(zw.x & 0xffff0000u)));
+            srow[2] = static_cast<sig_t>(sigmoidf_(__uint_as_float(zw.y << 16)));
+            srow[3] = static_cast<sig_t>(sigmoidf_(__uint_as_float(zw.y & 0xffff0000u)));
         }
     };
     typename Out::raw_t* gy = static_cast<typename Out::raw_t*>(p.out);
-    auto output = [&](int64_t c) {  // y = O * sigmoid(z) of chunk c: lane = token, 16 columns per tile
-        const int64_t t = c * C + lane;
+    auto output_part = [&](int64_t c) __attribute__((always_inline)) {
+        const int64_t t = c * C + tq;
 #pragma unroll
-        for (int cs = 0; cs < NCONS; ++cs) {
-            const float* orow = obuf + ((c & 1) * NCONS + cs) * (64 * OST) + lane * OST;
-            const sig_t* srow = sbuf + ((c & 1) * NCONS + cs) * (64 * OST) + lane * OST;
-            float y[16];
-#pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) {
-                const float4 o = *reinterpret_cast<const float4*>(orow + 4 * q4);
-                y[4 * q4 + 0] = o.x * static_cast<float>(srow[4 * q4 + 0]);
-                y[4 * q4 + 1] = o.y * static_cast<float>(srow[4 * q4 + 1]);
-                y[4 * q4 + 2] = o.z * static_cast<float>(srow[4 * q4 + 2]);
-                y[4 * q4 + 3] = o.w * static_cast<float>(srow[4 * q4 + 3]);
-            }
+        for (int t2 = 0; t2 < NCONS; ++t2) {
+            const float4 o = *reinterpret_cast<const float4*>(obuf + ((c & 1) * NCONS + t2) * (64 * OST) + tq * OST + cq);
+            const sig_t* srow = sbuf + ((c & 1) * NCONS + t2) * (64 * OST) + tq * OST + cq;
+            const float y0 = o.x * static_cast<float>(srow[0]), y1 = o.y * static_cast<float>(srow[1]);
+            const float y2 = o.z * static_cast<float>(srow[2]), y3 = o.w * static_cast<float>(srow[3]);
             if (t < T) {
-                typename Out::raw_t* dst = gy + zrow(t) + 16 * (grp * NCONS + cs);
+                typename Out::raw_t* dst = gy + zrow(t) + 16 * (grp * NCONS + t2) + cq;
                 if constexpr (sizeof(typename Out::raw_t) == 4) {
-#pragma unroll
-                    for (int q4 = 0; q4 < 4; ++q4)
-                        reinterpret_cast<float4*>(dst)[q4] = make_float4(y[4 * q4], y[4 * q4 + 1], y[4 * q4 + 2], y[4 * q4 + 3]);
+                    *reinterpret_cast<float4*>(dst) = make_float4(y0, y1, y2, y3);
                 } else {
-                    uint32_t w[8];
-#pragma unroll
-                    for (int e = 0; e < 8; ++e)
-                        w[e] = (uint32_t)Out::from_float(y[2 * e]) | ((uint32_t)Out::from_float(y[2 * e + 1]) << 16);
-                    reinterpret_cast<uint4*>(dst)[0] = make_uint4(w[0], w[1], w[2], w[3]);
-                    reinterpret_cast<uint4*>(dst)[1] = make_uint4(w[4], w[5], w[6], w[7]);
+                    *reinterpret_cast<uint2*>(dst) =
+                        make_uint2((uint32_t)Out::from_float(y0) | ((uint32_t)Out::from_float(y1) << 16),
+                                   (uint32_t)Out::from_float(y2) | ((uint32_t)Out::from_float(y3) << 16));
                 }
             }
         }
     };
 
-    // consumer state: S[ct][i] = S[16ct + 4g4 + i][col]
-    const int nt = grp * NCONS + (consumer ? wave : 0);
+    // chain state: S[ct][i] = S[16ct + 4g4 + i][col]
+    const int nt = grp * NCONS + cs;
     const int col = 16 * nt + m16;
     floatx4 S[NCT];
-    if (consumer) {
+    if (chain) {
         const float* s0 = p.s0 ? p.s0 + unit * (int64_t)D * D : nullptr;
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct)
@@ -727,98 +698,136 @@ void kda_rec64_kernel(RecurParams p) {
             for (int i = 0; i < 4; ++i) S[ct][i] = s0 ? s0[(16 * ct + 4 * g4 + i) * D + col] : 0.f;
     }
 
-    if (producer && NC > 0) {
-        issue(0);
-        for (int64_t c = 1; c <= L::PD && c < NC; ++c) touch(c);
-        wait_vm_zero();
-    }
-    lds_barrier();
 
-    for (int64_t ci = 0; ci < NC; ++ci) {
-        if (producer) {
-            if (ci + 1 < NC) {
-                issue(ci + 1);  // the slot of chunk ci - 1, released by the last barrier
-                if (ci + 1 + L::PD < NC) {
-                    touch(ci + 1 + L::PD);
-                    wait_vm<L::TOUCH>();  // the card of chunk ci + 1 has landed
-                } else {
-                    wait_vm_zero();
-                }
-            }
-        } else if (epilogue) {
-            sigmoid_tile(ci);
-            if (ci >= 1) output(ci - 1);
-        } else {
+    // each role runs its own loop (so that no role carries another's registers); all of them
+    // pass the same barriers: A and B once per chunk
+    if (chain) {
+        lds_barrier();  // the first card is resident
+        for (int64_t ci = 0; ci < NC; ++ci) {
             const unsigned char* st = smem + (ci % L::NSTAGE) * L::STAGE;
             const _Float16* sw = reinterpret_cast<const _Float16*>(st + CD::W);
-            const _Float16* sq = reinterpret_cast<const _Float16*>(st + CD::QE);
             const _Float16* sk = reinterpret_cast<const _Float16*>(st + CD::KBT);
-            const _Float16* su = reinterpret_cast<const _Float16*>(st + L::OFF_U + wave * L::PER);
+            const _Float16* su = reinterpret_cast<const _Float16*>(st + L::OFF_U + cs * L::PER);
             const float* sg = reinterpret_cast<const float*>(st + L::OFF_G);
-            // every operand of the chunk into registers first, then the MFMA chains
-            half8 wf[4][KB], qf[4][KB], kf[NCT][2];
-            half4 ut[4], uo[4];
+            // the state at the chunk start, as the B operand (logical k = 8g4 + j of step kb is
+            // channel cmap(kb, g4, j)), for this wave and for the output wave
+            half8 Sb[KB];
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) {
+                Sb[kb] = pack_h8(S[2 * kb], S[2 * kb + 1]);
+                *reinterpret_cast<half8*>(sbx + (kb * 64 + lane) * 8) = Sb[kb];
+            }
+            half8 wf[4][KB];
+            half4 ut[4];
             float4 gm[NCT];
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt) {
 #pragma unroll
-                for (int kb = 0; kb < KB; ++kb) {
-                    wf[mt][kb] = ld_h8(sw + ((mt * KB + kb) * 64 + lane) * 8);
-                    qf[mt][kb] = ld_h8(sq + ((mt * KB + kb) * 64 + lane) * 8);
-                }
+                for (int kb = 0; kb < KB; ++kb) wf[mt][kb] = ld_h8(sw + ((mt * KB + kb) * 64 + lane) * 8);
                 ut[mt] = ld_h4(su + (mt * 64 + lane) * 4);
-                uo[mt] = ld_h4(su + 1024 + (mt * 64 + lane) * 4);
             }
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct) gm[ct] = *reinterpret_cast<const float4*>(sg + 16 * ct + 4 * g4);
+            lds_barrier();  // A: the state copy is visible to the output wave
+            half8 kf[NCT][2];  // read while the U chain runs
 #pragma unroll
             for (int ct = 0; ct < NCT; ++ct) {
                 kf[ct][0] = ld_h8(sk + ((ct * 2 + 0) * 64 + lane) * 8);
                 kf[ct][1] = ld_h8(sk + ((ct * 2 + 1) * 64 + lane) * 8);
-                gm[ct] = *reinterpret_cast<const float4*>(sg + 16 * ct + 4 * g4);
             }
-            // state as the B operand: logical k = 8g4 + j of step kb is channel cmap(kb, g4, j)
-            half8 Sb[KB];
+            floatx4 U[4];
 #pragma unroll
-            for (int kb = 0; kb < KB; ++kb) Sb[kb] = pack_h8(S[2 * kb], S[2 * kb + 1]);
-            floatx4 U[4], O[4];
+            for (int mt = 0; mt < 4; ++mt) U[mt] = unpack_h4(ut[mt]);  // U~
 #pragma unroll
-            for (int mt = 0; mt < 4; ++mt) {
-                U[mt] = unpack_h4(ut[mt]);  // U~
-                O[mt] = unpack_h4(uo[mt]);  // Uo
-            }
-#pragma unroll
-            for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-                for (int mt = 0; mt < 4; ++mt) {
-                    U[mt] = mma_f16_k32(wf[mt][kb], Sb[kb], U[mt]);  // U~ - W S
-                    O[mt] = mma_f16_k32(qf[mt][kb], Sb[kb], O[mt]);  // Uo + Qe S
-                }
-            // S <- Diag(Gamma) S + Kbar^T U
-            half8 Ub[2];
-#pragma unroll
-            for (int u = 0; u < 2; ++u) Ub[u] = pack_h8(U[2 * u], U[2 * u + 1]);
-#pragma unroll
-            for (int ct = 0; ct < NCT; ++ct) {
+            for (int ct = 0; ct < NCT; ++ct) {  // Diag(Gamma) S, off the U chain
                 S[ct][0] *= gm[ct].x;
                 S[ct][1] *= gm[ct].y;
                 S[ct][2] *= gm[ct].z;
                 S[ct][3] *= gm[ct].w;
             }
 #pragma unroll
+            for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                for (int mt = 0; mt < 4; ++mt) U[mt] = mma_f16_k32(wf[mt][kb], Sb[kb], U[mt]);  // U~ - W S
+            half8 Ub[2];
+#pragma unroll
+            for (int u = 0; u < 2; ++u) Ub[u] = pack_h8(U[2 * u], U[2 * u + 1]);
+#pragma unroll
             for (int u = 0; u < 2; ++u)
 #pragma unroll
-                for (int ct = 0; ct < NCT; ++ct) S[ct] = mma_f16_k32(kf[ct][u], Ub[u], S[ct]);
-            // read-out O -> LDS tile [token][column] for the epilogue
-            float* orow = obuf + ((ci & 1) * NCONS + wave) * (64 * OST);
+                for (int ct = 0; ct < NCT; ++ct) S[ct] = mma_f16_k32(kf[ct][u], Ub[u], S[ct]);  // + Kbar^T U
+            lds_barrier();  // B
+        }
+    } else if (outw) {
+        lds_barrier();  // the first card is resident
+        for (int64_t ci = 0; ci < NC; ++ci) {
+            const unsigned char* st = smem + (ci % L::NSTAGE) * L::STAGE;
+            const _Float16* sq = reinterpret_cast<const _Float16*>(st + CD::QE);
+            const _Float16* su = reinterpret_cast<const _Float16*>(st + L::OFF_U + cs * L::PER);
+            half8 qf[4][KB];
+            half4 uo[4];
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) {
+#pragma unroll
+                for (int kb = 0; kb < KB; ++kb) qf[mt][kb] = ld_h8(sq + ((mt * KB + kb) * 64 + lane) * 8);
+                uo[mt] = ld_h4(su + L::UO_IN / 2 + (mt * 64 + lane) * 4);
+            }
+            lds_barrier();  // A
+            half8 Sb[KB];
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) Sb[kb] = ld_h8(sbx + (kb * 64 + lane) * 8);
+            floatx4 O[4];
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) O[mt] = unpack_h4(uo[mt]);  // Uo
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                for (int mt = 0; mt < 4; ++mt) O[mt] = mma_f16_k32(qf[mt][kb], Sb[kb], O[mt]);  // + Qe S
+            float* orow = obuf + ((ci & 1) * NCONS + cs) * (64 * OST);
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) orow[(16 * mt + 4 * g4 + i) * OST + m16] = O[mt][i];
+            lds_barrier();  // B
         }
-        lds_barrier();
+    } else {
+        // two register sets: while one is in flight (chunk n+2), the other (chunk n+1,
+        // loaded one iteration earlier) is written to LDS
+        u32x4 ra[KP], rb[KP];
+        auto load_set = [&](u32x4 (&r)[KP], int64_t c) __attribute__((always_inline)) {
+#pragma unroll
+            for (int k = 0; k < KP; ++k) r[k] = *piece_src(c, piece_of(k));
+        };
+        auto store_set = [&](const u32x4 (&r)[KP], int64_t c) __attribute__((always_inline)) {
+#pragma unroll
+            for (int k = 0; k < KP; ++k) *piece_dst(c, piece_of(k)) = r[k];
+        };
+        // Branch-free: past the end the producers reload the last chunk and rewrite the slot
+        // that nobody reads any more, so both register sets follow the same code path.
+        auto step = [&](u32x4 (&ld)[KP], const u32x4 (&wr)[KP], int64_t ci) __attribute__((always_inline)) {
+            load_set(ld, ci + 2 < NC ? ci + 2 : NC - 1);  // the set that held chunk ci
+            sigmoid_part(ci);
+            if (ci >= 1) output_part(ci - 1);
+            lds_barrier();  // A
+            wait_vm<KP>();          // chunk ci + 1, loaded one iteration ago into the other set
+            store_set(wr, ci + 1);  // the slot of chunk ci - 1, released by barrier B
+            lds_barrier();  // B
+        };
+        if (NC > 0) {
+            load_set(ra, 0);
+            load_set(rb, NC > 1 ? 1 : 0);
+            wait_vm<KP>();
+            store_set(ra, 0);
+        }
+        lds_barrier();  // the first card is resident
+        for (int64_t ci = 0; ci < NC; ci += 2) {
+            step(ra, rb, ci);
+            if (ci + 1 < NC) step(rb, ra, ci + 1);
+        }
     }
-    if (epilogue && NC > 0) output(NC - 1);
+    if (prod && NC > 0) output_part(NC - 1);
 
-    if (consumer && p.sT) {
+    if (chain && p.sT) {
         float* sT = p.sT + unit * (int64_t)D * D;
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct)
@@ -854,7 +863,7 @@ static hipError_t launch_d(const PrepParams& pp, const RecurParams& rp, hipStrea
     if (e != hipSuccess) return e;
     constexpr int G = D / (16 * NCONS);
     const int64_t blocks = (units * G + 7) / 8 * 8;
-    hipLaunchKernelGGL(kr, dim3((unsigned)blocks), dim3((NCONS + 2) * 64), LR::TOTAL, stream, rp);
+    hipLaunchKernelGGL(kr, dim3((unsigned)blocks), dim3(LR::WAVES * 64), LR::TOTAL, stream, rp);
     return hipGetLastError();
 }
 
