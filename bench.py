@@ -46,13 +46,14 @@ def log(*a):
 
 
 # ----------------------------------------------------------- algorithmic work
-def prefill_bytes(wl) -> int:
+def prefill_bytes(wl, out_esz=4) -> int:
     """Algorithmic HBM bytes of one prefill: bf16 q, k, v, log alpha and gate
-    (2 B per element), beta (2 B per head-token), a bf16 output (256 B per
-    head-token at d = 128), plus one read of the initial and one write of the
-    final fp32 state when present.  1538 B per head-token at d = 128."""
+    (2 B per element), beta (2 B per head-token), the output (out_esz B per
+    element; fp32 here), plus one read of the initial and one write of the
+    final fp32 state when present.  At d = 128: 1794 B per head-token with an
+    fp32 output, 1538 B with a bf16 one."""
     esz = 2 if wl.dtype == "bf16" else 4
-    per_tok = esz * (3 * wl.Dk + 2 * wl.Dv + 1) + esz * wl.Dv
+    per_tok = esz * (3 * wl.Dk + 2 * wl.Dv + 1) + out_esz * wl.Dv
     n = wl.B * wl.T * wl.H * per_tok
     st = wl.B * wl.H * wl.Dk * wl.Dv * 4
     return n + (st if wl.init_state else 0) + (st if wl.final_state else 0)
@@ -67,11 +68,11 @@ def prefill_flops(wl) -> int:
     return int(round(per * wl.B * wl.T * wl.H))
 
 
-def decode_bytes(wl) -> int:
+def decode_bytes(wl, out_esz=4) -> int:
     """Per (b, h): read and write of the fp32 state, bf16 q, k, v, log alpha,
-    gate and beta, and a bf16 output."""
+    gate and beta, and the output (fp32 here)."""
     esz = 2 if wl.dtype == "bf16" else 4
-    per = 2 * wl.Dk * wl.Dv * 4 + esz * (3 * wl.Dk + 2 * wl.Dv + 1) + esz * wl.Dv
+    per = 2 * wl.Dk * wl.Dv * 4 + esz * (3 * wl.Dk + 2 * wl.Dv + 1) + out_esz * wl.Dv
     return wl.B * wl.H * per
 
 
@@ -215,7 +216,7 @@ def cpu_baseline(wl, budget_s):
     threads = oracle.default_threads()
     used = max(1, min(threads, wl.B * wl.H))  # parallel over (batch, head) only
     secs, reps = 0.0, 0
-    while secs < budget_s and reps < 50:
+    while secs < budget_s and reps < 1000:
         _, _, s = oracle.fwd(*(x[k] for k in KEYS), initial_state=x.get("initial_state"),
                              threads=threads, return_seconds=True)
         secs += s
@@ -229,6 +230,30 @@ def cpu_baseline(wl, budget_s):
             "seconds_per_pass": per}
 
 
+def counter_pass(kda, head, dec_wl, n_sets, dev, stream):
+    """A short run for hardware-counter collection (FETCH_SIZE / WRITE_SIZE):
+    a copy-shaped elementwise kernel of known size (1 GiB read, 1 GiB
+    written) to calibrate the counters, then the headline prefill over the
+    rotating input sets and a few decode steps."""
+    import torch
+    n = 1 << 28
+    src = torch.randn(n, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.neg(src, out=dst)  # reads 4n bytes, writes 4n bytes
+    torch.cuda.synchronize()
+    del src, dst
+    torch.cuda.empty_cache()
+    pre, _ = bench_prefill(kda, head, n_sets, 0, n_sets, dev, stream)
+    dec = bench_decode(kda, dec_wl, 4, 0, dev, stream)
+    return {"counter_pass": True, "calibration": {"kernel": "torch.neg fp32, 2^28 elements",
+                                                  "bytes_read": 4 * n, "bytes_written": 4 * n},
+            "prefill_calls": n_sets, "prefill_workload": head.name,
+            "decode_calls": 4, "decode_workload": dec_wl.name,
+            "prefill_kernel_ms": pre["kernel_ms_mean"], "decode_kernel_ms": dec["kernel_ms_mean"],
+            "source_digest": source_digest()}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -239,6 +264,9 @@ def main():
                     help="time budget of the oracle baseline (0 skips it)")
     ap.add_argument("--no-context", action="store_true",
                     help="skip the context timings of the two larger prefill shapes")
+    ap.add_argument("--counter-pass", action="store_true",
+                    help="short run for rocprofv3 --pmc: counter calibration copy, the "
+                         "headline prefill once per input set, four decode steps")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -262,6 +290,9 @@ def main():
     log(f"device {torch.cuda.get_device_name(dev)}; library {kda.library_path()}")
 
     head = CONFIGS[1]
+    if args.counter_pass:
+        print(json.dumps(counter_pass(kda, head, CONFIGS[4], args.sets, dev, stream)), flush=True)
+        return
     pre, wall = bench_prefill(kda, head, args.steps, args.warmup, args.sets, dev, stream)
     dec = bench_decode(kda, CONFIGS[4], max(args.steps, 10), args.warmup, dev, stream)
     ctx = {}
