@@ -6,10 +6,10 @@
 // "Compute paradigm" and "Hierarchical chunking of linear attention"), laid out
 // for throughput on CDNA4:
 //
-// kda_prep64_kernel  persistent workgroups of 4 waves, one (b, h, chunk) item at a
-//   time with the next item's inputs prefetched into registers.  Wave a owns the
-//   16-token tile a of the chunk and keeps it in registers in MFMA operand
-//   layout (lane = token, 4 consecutive key channels per 16-channel tile).  The
+// kda_prep64_kernel  one workgroup of 4 waves per (b, h, chunk) card, two
+//   workgroups per CU.  Wave a owns the 16-token tile a of the chunk, keeps it
+//   in registers in MFMA operand layout (lane = token, 4 consecutive key
+//   channels per 16-channel tile) and is compiled for its tile index.  The
 //   cumulative log-decay is a DPP prefix scan across the 16 lanes of a row.
 //   Decay is folded into q and k as an absolute-position rescaling measured
 //   from the start of each 16-token tile (page "Kimi K3 report walk-through",
@@ -19,12 +19,13 @@
 //   P = prefix sum of log2(alpha) inside the tile, tau = its total.  Pair
 //   products inside a tile use KR.KC^T on the fp32 MFMA (the operands span
 //   2^{+-116}); across tiles both operands are <= |k| and one fp16 pass
-//   suffices.  The unit-lower-triangular system (I + A) is solved
-//   with register forward substitution on the four 16x16 diagonal blocks and
-//   fp32 MFMA block products for the rest.  The remaining contractions are
-//   arranged so that their accumulators come out in exactly the fragment
-//   layout the sequential kernel consumes, so the "update card" of the chunk
-//   is written with coalesced 16-byte stores.
+//   suffices.  The unit-lower-triangular system (I + A) is solved with
+//   register forward substitution on the four 16x16 diagonal blocks and fp32
+//   MFMA block products for the rest.  Tiles are turned to lane = channel by
+//   an MFMA against a 0/1 selection operand.  With M = P T, every card block of
+//   the tile is one product of its T or M rows with the K~ or V fragments:
+//       U~ = T V,  Uo = M V,  W^T = K~^T T^T,  Qe^T = Q~^T - K~^T M^T,
+//   whose accumulators are the card's fragments (coalesced stores).
 //
 // kda_rec64_kernel  one workgroup per (b, h, group of NCONS 16-column value
 //   tiles): per tile a chain wave carries the fp32 state of its columns in MFMA
@@ -37,7 +38,8 @@
 // Card of one (b, h, chunk), fp16 unless noted (lane l = 16 g + m):
 //   W   [mt][kb] 64 lanes x 8: -W[16mt + m][c(kb, g, j)]
 //   QE  [mt][kb] 64 lanes x 8:  Qe[16mt + m][c(kb, g, j)]        Qe = Q~ - P W
-//   KBT [ct][u]  64 lanes x 8:  Kbar[c(u, g, j)][16ct + m]
+//   KBT [ct][u][h] 64 lanes x 4: Kbar[32u + 16h + 4g + i][16ct + m]; the two
+//                halves h = 0, 1 concatenated are the 8 K-elements c(u, g, j)
 //   UT  [nt][mt] 64 lanes x 4:  U~[16mt + 4g + i][16nt + m]
 //   UO  [nt][mt] 64 lanes x 4:  Uo[16mt + 4g + i][16nt + m]       Uo = P U~
 //   GAM [D] fp32: 2^{gamma_C}, the decay of the whole chunk per key channel
@@ -56,6 +58,7 @@ constexpr int C = 64;
 constexpr int NSUB = 4;
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 template <int CTRL>
 __device__ __forceinline__ float dpp_mov(float x) {
@@ -159,377 +162,371 @@ struct Card {
 
 template <int D>
 struct PrepL {
-    static constexpr int KB = D / 32;
-    static constexpr int SR = D + 8;  // fp16 [token][channel] row stride (halves)
-    static constexpr int ST = C + 8;  // fp16 [channel][token] row stride (halves)
-    static constexpr int SA = C + 4;  // fp32 [64][64] row stride (floats)
-    static constexpr int SP = C + 8;  // fp16 [64][64] row stride (halves)
-    static constexpr int64_t B_KEF = (int64_t)NSUB * KB * 64 * 16;  // KE fragments
-    static constexpr int64_t B_LINV = 64 * SA * 4;
-    static constexpr int64_t B_KE = B_KEF > B_LINV ? B_KEF : B_LINV;
-    static constexpr int64_t OFF_BETA = 0;                     // fp32 [64]
-    static constexpr int64_t OFF_ETAU = 256;                   // fp32 [4][D]: decay over each tile
-    static constexpr int64_t OFF_KE = OFF_ETAU + 4 * D * 4;    // KE fragments; later Linv fp32 [64][SA]
-    static constexpr int64_t OFF_KT = OFF_KE + B_KE;           // fp16 K~^T [D][ST]; later -W^T
-    static constexpr int64_t OFF_KBT = OFF_KT + D * ST * 2;    // fp16 Kbar^T [D][ST]
-    static constexpr int64_t OFF_VT = OFF_KBT + D * ST * 2;    // fp16 V^T [D][ST]
-    static constexpr int64_t OFF_Q = OFF_VT + D * ST * 2;      // fp16 Q~ [64][SR]
-    static constexpr int64_t OFF_A = OFF_Q + 64 * SR * 2;      // fp32 A [64][SA]
-    static constexpr int64_t OFF_P = OFF_A + 64 * SA * 4;      // fp16 P [64][SP]
-    static constexpr int64_t OFF_T = OFF_P + 64 * SP * 2;      // fp16 T [64][SP]
-    static constexpr int64_t TOTAL = OFF_T + 64 * SP * 2;
-    static_assert(TOTAL <= 160 * 1024, "prep LDS budget");
-    static_assert(OFF_KE % 16 == 0 && OFF_KT % 16 == 0 && OFF_KBT % 16 == 0 && OFF_VT % 16 == 0 &&
-                      OFF_Q % 16 == 0 && OFF_A % 16 == 0 && OFF_P % 16 == 0 && OFF_T % 16 == 0,
+    static constexpr int KB = D / 32, NCT = D / 16;
+    static constexpr int SAB = 17;                         // fp32 16x16 block row stride (floats)
+    static constexpr int BLK = 16 * SAB;                   // floats per block
+    static constexpr int NBLK = NSUB * (NSUB + 1) / 2;     // blocks on and below the diagonal
+    static constexpr int SP = C + 8;                       // fp16 [64][64] row stride (halves)
+    static constexpr int64_t FR = 1024;                    // 64 lanes x 16 B
+    static constexpr int64_t B_BLK = (int64_t)NBLK * BLK * 4;
+    static constexpr int64_t B_KEF = (int64_t)NSUB * KB * FR;
+    static constexpr int64_t B_R1 = B_KEF > B_BLK ? B_KEF : B_BLK;
+    static constexpr int64_t B_MAT = 64 * SP * 2;
+    static constexpr int64_t B_R2 = B_BLK > B_MAT ? B_BLK : B_MAT;
+    static constexpr int64_t OFF_BETA = 0;                      // fp32 [64]
+    static constexpr int64_t OFF_ETAU = 256;                    // fp32 [NSUB][D]: decay over each tile
+    static constexpr int64_t OFF_KE = OFF_ETAU + NSUB * D * 4;  // KE fragments [tile][kb]; later Linv blocks
+    static constexpr int64_t OFF_KF = OFF_KE + B_R1;            // K~ fragments [ct][u][half][lane] 8 B
+    static constexpr int64_t OFF_VF = OFF_KF + NCT * 2 * FR;    // V fragments, same layout
+    static constexpr int64_t OFF_A = OFF_VF + NCT * 2 * FR;     // fp32 A blocks; later fp16 M [64][SP]
+    static constexpr int64_t OFF_P = OFF_A + B_R2;              // fp16 P [64][SP]
+    static constexpr int64_t OFF_T = OFF_P + B_MAT;             // fp16 T [64][SP]
+    static constexpr int64_t TOTAL = OFF_T + B_MAT;
+    // two workgroups per CU
+    static_assert(2 * TOTAL <= 160 * 1024, "prep LDS budget");
+    static_assert(OFF_KE % 16 == 0 && OFF_KF % 16 == 0 && OFF_VF % 16 == 0 && OFF_A % 16 == 0 &&
+                      OFF_P % 16 == 0 && OFF_T % 16 == 0,
                   "prep LDS alignment");
 };
 
+// index of the 16x16 block (r, c), c <= r, among the blocks on and below the diagonal
+__device__ __forceinline__ constexpr int bidx(int r, int c) { return r * (r + 1) / 2 + c; }
+
+// B operand of a K = 32 step that picks the 16 channels 16 cl .. 16 cl + 15 of the
+// step: with a tile in A-operand layout (lane = token), D = A Sel holds the same
+// 16x16 block with lane = channel and the four registers = tokens 4g .. 4g + 3.
+// Products with 1.0 and sums with zeros keep fp16 values exact.
+__device__ __forceinline__ half8 sel_operand(int cl, int lane) {
+    const int g = lane >> 4, n = lane & 15;
+    half8 r;
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+        r[j] = static_cast<_Float16>(((j >> 2) == cl && (n >> 2) == g && (j & 3) == (n & 3)) ? 1.f : 0.f);
+    return r;
+}
+
+// 64 lanes x 8 B fragment piece [ct][u][half]: lane (g, n) holds rows
+// 32u + 16 half + 4g .. +3 of column 16 ct + n
+__device__ __forceinline__ constexpr int64_t frag_piece(int ct, int u, int hf) { return ((ct * 2 + u) * 2 + hf) * 512; }
+
 // ---------------------------------------------------------------------------
-// kernel 1: update cards.  Persistent: each workgroup walks (b, h, chunk) items
-// with a stride of the grid size and prefetches the next item's raw inputs into
-// registers while it builds the current card.
-template <int D>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void kda_prep64_kernel(PrepParams p) {
+// kernel 1: one update card per workgroup.  Wave A owns the 16-token tile A of the
+// chunk; everything that depends on A is resolved at compile time.
+template <int D, int A>
+__device__ __forceinline__ void prep_tile(const PrepParams& p, unsigned char* smem) {
     using L = PrepL<D>;
     using CD = Card<D>;
-    constexpr int NCT = D / 16, KB = D / 32;
-    constexpr int SR = L::SR, ST = L::ST, SA = L::SA, SP = L::SP;
-    extern __shared__ __align__(16) unsigned char smem[];
+    constexpr int NCT = D / 16, KB = D / 32, SAB = L::SAB, BLK = L::BLK, SP = L::SP;
     float* s_beta = reinterpret_cast<float*>(smem + L::OFF_BETA);
     float* s_etau = reinterpret_cast<float*>(smem + L::OFF_ETAU);
     _Float16* s_ke = reinterpret_cast<_Float16*>(smem + L::OFF_KE);
     float* s_linv = reinterpret_cast<float*>(smem + L::OFF_KE);
-    _Float16* s_kt = reinterpret_cast<_Float16*>(smem + L::OFF_KT);
-    _Float16* s_kbt = reinterpret_cast<_Float16*>(smem + L::OFF_KBT);
-    _Float16* s_vt = reinterpret_cast<_Float16*>(smem + L::OFF_VT);
-    _Float16* s_q = reinterpret_cast<_Float16*>(smem + L::OFF_Q);
-    float* s_a = reinterpret_cast<float*>(smem + L::OFF_A);
+    unsigned char* s_kf = smem + L::OFF_KF;
+    unsigned char* s_vf = smem + L::OFF_VF;
+    float* s_ab = reinterpret_cast<float*>(smem + L::OFF_A);
+    _Float16* s_m = reinterpret_cast<_Float16*>(smem + L::OFF_A);
     _Float16* s_p = reinterpret_cast<_Float16*>(smem + L::OFF_P);
     _Float16* s_t = reinterpret_cast<_Float16*>(smem + L::OFF_T);
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int lane = threadIdx.x & 63;
     const int m16 = lane & 15, g4 = lane >> 4;
-    const int a = wave;             // this wave's 16-token tile
-    const int rl = 16 * a + m16;    // this lane's token within the chunk
+    const int rl = 16 * A + m16;  // this lane's token within the chunk
     const int64_t NC = p.NC, T = p.T, H = p.H;
-    const int64_t items = p.B * H * NC;
-    const uint16_t* gq = static_cast<const uint16_t*>(p.q);
-    const uint16_t* gk = static_cast<const uint16_t*>(p.k);
-    const uint16_t* gv = static_cast<const uint16_t*>(p.v);
-    const uint16_t* gla = static_cast<const uint16_t*>(p.la);
-    const uint16_t* gbeta = static_cast<const uint16_t*>(p.beta);
     const bool clamp = p.clamp != 0;
 
     // raw inputs of token rl: per 16-channel tile ct, the 4 bf16 channels 16ct + 4g4 .. +3
-    uint2 nq[NCT], nk[NCT], nv[NCT], nla[NCT];
-    uint16_t nbeta;
-    auto fetch = [&](int64_t it) {
+    u32x2 rq[NCT], rk[NCT], rv[NCT], rla[NCT];
+    uint32_t rbeta;
+    auto fetch = [&](int64_t it) __attribute__((always_inline)) {
         const int64_t n = it % NC, unit = it / NC;
         const int64_t b = unit / H, h = unit % H;
         const int64_t tok = n * C + rl;
-        const int64_t row = (b * T + (tok < T ? tok : T - 1)) * H + h;  // in bounds; zeroed below
+        const int64_t row = (b * T + (tok < T ? tok : T - 1)) * H + h;  // in bounds; zeroed at use
+        const uint16_t* gq = static_cast<const uint16_t*>(p.q);
+        const uint16_t* gk = static_cast<const uint16_t*>(p.k);
+        const uint16_t* gv = static_cast<const uint16_t*>(p.v);
+        const uint16_t* gla = static_cast<const uint16_t*>(p.la);
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct) {
             const int64_t off = row * D + 16 * ct + 4 * g4;
-            nq[ct] = *reinterpret_cast<const uint2*>(gq + off);
-            nk[ct] = *reinterpret_cast<const uint2*>(gk + off);
-            nv[ct] = *reinterpret_cast<const uint2*>(gv + off);
-            nla[ct] = *reinterpret_cast<const uint2*>(gla + off);
+            rla[ct] = *reinterpret_cast<const u32x2*>(gla + off);
+            rk[ct] = *reinterpret_cast<const u32x2*>(gk + off);
         }
-        nbeta = gbeta[row];
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) {
+            const int64_t off = row * D + 16 * ct + 4 * g4;
+            rq[ct] = *reinterpret_cast<const u32x2*>(gq + off);
+            rv[ct] = *reinterpret_cast<const u32x2*>(gv + off);
+        }
+        rbeta = static_cast<const uint16_t*>(p.beta)[row];
     };
-    auto elem = [](const uint2& w, int i) -> float {
-        const uint32_t x = (i < 2) ? w.x : w.y;
+    auto elem = [](const u32x2 w, int i) -> float {
+        const uint32_t x = w[i >> 1];
         return (i & 1) ? __uint_as_float(x & 0xffff0000u) : __uint_as_float(x << 16);
     };
+    const half8 sel0 = sel_operand(0, lane), sel1 = sel_operand(1, lane);
+    // a 16 x 32 tile in operand layout -> two transposed 16 x 16 pieces of a fragment
+    auto put_transposed = [&](unsigned char* base, int kb, const half8& x) __attribute__((always_inline)) {
+        const floatx4 t0 = mma_f16_k32(x, sel0, zero4());
+        const floatx4 t1 = mma_f16_k32(x, sel1, zero4());
+        *reinterpret_cast<half4*>(base + frag_piece(2 * kb, A >> 1, A & 1) + lane * 8) = pack_h4(t0);
+        *reinterpret_cast<half4*>(base + frag_piece(2 * kb + 1, A >> 1, A & 1) + lane * 8) = pack_h4(t1);
+    };
 
-    int64_t item = blockIdx.x;
-    if (item < items) fetch(item);
-    for (; item < items; item += gridDim.x) {
-        const int64_t n = item % NC;
-        const int64_t t0 = n * C;
-        const bool valid = t0 + rl < T;
-        unsigned char* card = static_cast<unsigned char*>(p.ws) + item * CD::BYTES;
-        uint2 rq[NCT], rk[NCT], rv[NCT], rla[NCT];
+    const int64_t item = blockIdx.x;
+    fetch(item);
+    const bool valid = (item % NC) * C + rl < T;  // tokens past the end are identity tokens
+    unsigned char* card = static_cast<unsigned char*>(p.ws) + item * CD::BYTES;
+    const float beta_mine = valid ? bf16_bits_to_float(static_cast<uint16_t>(rbeta)) : 0.f;
+
+    // ---- phase 1: decay inside the tile, in-tile pair products, V fragments
+    s_beta[rl] = beta_mine;  // the four lane groups store the same value
+    half8 kr16[KB], qr16[KB], ke16[KB];
+    floatx4 accA = zero4(), accP = zero4();
 #pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) {  // identity tokens past the end: q = k = v = log alpha = 0
-            const uint2 z2 = make_uint2(0u, 0u);
-            rq[ct] = valid ? nq[ct] : z2;
-            rk[ct] = valid ? nk[ct] : z2;
-            rv[ct] = valid ? nv[ct] : z2;
-            rla[ct] = valid ? nla[ct] : z2;
+    for (int kb = 0; kb < KB; ++kb) {
+        half8 v16;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int ct = 2 * kb + (j >> 2), i = j & 3;
+            const float l = valid ? clamp_log_alpha(elem(rla[ct], i), clamp) * kLog2e : 0.f;
+            const float P = row_scan16(l);      // log2 decay from the tile start, inclusive
+            const float E = fast_exp2(P);       // <= 1
+            const float Einv = fast_exp2(-P);   // >= 1, < 2^116 under the floor
+            const float Et = row_last(E);       // decay over the whole tile
+            const float kf = valid ? elem(rk[ct], i) : 0.f, qf = valid ? elem(rq[ct], i) : 0.f;
+            const float KR = kf * E, QR = qf * E, KC = kf * Einv;
+            // K-step (kb, j): lane group g4 supplies channel cmap(kb, g4, j) to both operands
+            accA = mma_f32_k4(KR, KC, accA);
+            accP = mma_f32_k4(QR, KC, accP);
+            kr16[kb][j] = static_cast<_Float16>(KR);
+            qr16[kb][j] = static_cast<_Float16>(QR);
+            ke16[kb][j] = static_cast<_Float16>(kf * (Einv * Et));  // decay from after this token to the tile end
+            v16[j] = static_cast<_Float16>(valid ? elem(rv[ct], i) : 0.f);
+            s_etau[A * D + cmap(kb, g4, j)] = Et;  // the 16 lanes of a row store the same value
         }
-        const float beta_mine = valid ? bf16_bits_to_float(nbeta) : 0.f;
-        if (item + gridDim.x < items) fetch(item + gridDim.x);
+        // KE fragment of this tile: the B operand of the pairs (later tile, this tile)
+        *reinterpret_cast<half8*>(s_ke + ((A * KB + kb) * 64 + lane) * 8) = ke16[kb];
+        put_transposed(s_vf, kb, v16);
+        __builtin_amdgcn_sched_barrier(0);  // one K-block at a time: bounded register lifetimes
+    }
+    // diagonal blocks of A (strictly lower, rows scaled by beta) and P (lower)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int r = 4 * g4 + i, s = m16;
+        const float br = __shfl(beta_mine, r);
+        s_ab[bidx(A, A) * BLK + r * SAB + s] = (s < r) ? br * accA[i] : 0.f;
+        s_p[(16 * A + r) * SP + 16 * A + s] = static_cast<_Float16>((s <= r) ? accP[i] : 0.f);
+    }
+    lds_barrier();  // (1) tile decays, KE and V fragments, beta
 
-        // ---- phase 1 (per tile): decay inside the tile, in-tile pair products
-        if (g4 == 0) s_beta[rl] = beta_mine;
-        half8 kr16[KB], qr16[KB];
-        floatx4 accA = zero4(), accP = zero4();
+    // ---- phase 2: chunk-relative operands and the pairs with earlier tiles.  Decay
+    //      factors across tiles are products of the per-tile decays 2^{tau}.
+    half8 q16[KB];  // Q~ of this tile: the initial value of its Qe rows
+    floatx4 pa[NSUB - 1], pp[NSUB - 1];
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-            half8 ke;
+    for (int bb = 0; bb < NSUB - 1; ++bb) pa[bb] = pp[bb] = zero4();
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const int ct = 2 * kb + (j >> 2), i = j & 3;
-                const float l = clamp_log_alpha(elem(rla[ct], i), clamp) * kLog2e;
-                const float P = row_scan16(l);      // log2 decay from the tile start, inclusive
-                const float E = fast_exp2(P);       // <= 1
-                const float Einv = fast_exp2(-P);   // >= 1, < 2^116 under the floor
-                const float Et = row_last(E);       // decay over the whole tile
-                const float kf = elem(rk[ct], i), qf = elem(rq[ct], i);
-                const float KR = kf * E, QR = qf * E, KC = kf * Einv;
-                // K-step (kb, j): lane group g4 supplies channel cmap(kb, g4, j) to both operands
-                accA = mma_f32_k4(KR, KC, accA);
-                accP = mma_f32_k4(QR, KC, accP);
-                kr16[kb][j] = static_cast<_Float16>(KR);
-                qr16[kb][j] = static_cast<_Float16>(QR);
-                ke[j] = static_cast<_Float16>(kf * (Einv * Et));  // decay from after this token to the tile end
-                const int c = cmap(kb, g4, j);
-                if (m16 == 0) s_etau[a * D + c] = Et;
-                s_vt[c * ST + rl] = static_cast<_Float16>(elem(rv[ct], i));
+    for (int kb = 0; kb < KB; ++kb) {
+        float et[NSUB][8];
+#pragma unroll
+        for (int a2 = 0; a2 < NSUB; ++a2) {
+            if (a2 == A) continue;
+            const float4 lo = *reinterpret_cast<const float4*>(s_etau + a2 * D + 32 * kb + 4 * g4);
+            const float4 hi = *reinterpret_cast<const float4*>(s_etau + a2 * D + 32 * kb + 16 + 4 * g4);
+            et[a2][0] = lo.x; et[a2][1] = lo.y; et[a2][2] = lo.z; et[a2][3] = lo.w;
+            et[a2][4] = hi.x; et[a2][5] = hi.y; et[a2][6] = hi.z; et[a2][7] = hi.w;
+        }
+        half8 kt, kbar;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            float erho = 1.f, eaft = 1.f;  // decay before this tile / after this tile
+#pragma unroll
+            for (int a2 = 0; a2 < A; ++a2) erho *= et[a2][j];
+#pragma unroll
+            for (int a2 = A + 1; a2 < NSUB; ++a2) eaft *= et[a2][j];
+            kt[j] = static_cast<_Float16>(static_cast<float>(kr16[kb][j]) * erho);    // K~ = k 2^{g}
+            q16[kb][j] = static_cast<_Float16>(static_cast<float>(qr16[kb][j]) * erho);  // Q~ = q 2^{g}
+            kbar[j] = static_cast<_Float16>(static_cast<float>(ke16[kb][j]) * eaft);  // Kbar = k 2^{g_C - g}
+        }
+        put_transposed(s_kf, kb, kt);
+        put_transposed(card + CD::KBT, kb, kbar);
+        // pairs (A, bb), bb < A: reference point at the end of tile A-1; both operands <= |k|
+        float f[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) f[j] = 1.f;
+#pragma unroll
+        for (int bb = A - 1; bb >= 0; --bb) {  // f = decay over the tiles strictly between bb and A
+            const half8 keb = ld_h8(s_ke + ((bb * KB + kb) * 64 + lane) * 8);
+            half8 col;
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                col[j] = (bb == A - 1) ? keb[j] : static_cast<_Float16>(static_cast<float>(keb[j]) * f[j]);
+            pa[bb] = mma_f16_k32(kr16[kb], col, pa[bb]);
+            pp[bb] = mma_f16_k32(qr16[kb], col, pp[bb]);
+            if (bb > 0) {
+#pragma unroll
+                for (int j = 0; j < 8; ++j) f[j] *= et[bb][j];
             }
-            // KE fragment of this tile: the B operand of the pairs (later tile, this tile)
-            *reinterpret_cast<half8*>(s_ke + ((a * KB + kb) * 64 + lane) * 8) = ke;
         }
-        // diagonal blocks of A (strictly lower, rows scaled by beta) and P (lower)
+    }
+#pragma unroll
+    for (int bb = 0; bb < A; ++bb) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int r = 4 * g4 + i, s = m16;
+            const int r = 4 * g4 + i;
             const float br = __shfl(beta_mine, r);
-            s_a[(16 * a + r) * SA + 16 * a + s] = (s < r) ? br * accA[i] : 0.f;
-            s_p[(16 * a + r) * SP + 16 * a + s] = static_cast<_Float16>((s <= r) ? accP[i] : 0.f);
-#pragma unroll
-            for (int bb = 0; bb < NSUB; ++bb)
-                if (bb > a) s_p[(16 * a + r) * SP + 16 * bb + s] = static_cast<_Float16>(0.f);
+            s_ab[bidx(A, bb) * BLK + r * SAB + m16] = br * pa[bb][i];
+            s_p[(16 * A + r) * SP + 16 * bb + m16] = static_cast<_Float16>(pp[bb][i]);
         }
-        lds_barrier();  // (1) tile decays, KE fragments, V^T and beta are in LDS
+    }
+    // Gamma = 2^{g_C} per key channel
+    if (64 * A < D) {
+        const int c = 64 * A + lane;
+        float gm = 1.f;
+#pragma unroll
+        for (int a2 = 0; a2 < NSUB; ++a2) gm *= s_etau[a2 * D + c];
+        reinterpret_cast<float*>(card + CD::GAM)[c] = gm;
+    }
+    lds_barrier();  // (2) A, P, K~ fragments complete; KE fragments no longer needed
 
-        // ---- phase 2 (per tile): chunk-relative operands and the pairs with earlier tiles.
-        // Decay factors across tiles are products of the per-tile decays 2^{tau}.
-        floatx4 pa[NSUB - 1], pp[NSUB - 1];
+    // ---- phase 3: Linv = (I + A)^{-1} (unit lower triangular, blocked by 16) and
+    //      T = Linv diag(beta) in fp16
+    if constexpr (A == 0) {  // diagonal blocks: lane group g4 = block, lane m16 = column
+        const int ab = g4, j = m16;
+        const float* Ab = s_ab + bidx(ab, ab) * BLK;
+        float x[16];
 #pragma unroll
-        for (int bb = 0; bb < NSUB - 1; ++bb) pa[bb] = pp[bb] = zero4();
+        for (int r = 0; r < 16; ++r) x[r] = (r == j) ? 1.f : 0.f;
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-            float et[NSUB][8];
+        for (int r = 1; r < 16; ++r) {
+            float acc = x[r];
 #pragma unroll
-            for (int a2 = 0; a2 < NSUB; ++a2) {
-                const float4 lo = *reinterpret_cast<const float4*>(s_etau + a2 * D + 32 * kb + 4 * g4);
-                const float4 hi = *reinterpret_cast<const float4*>(s_etau + a2 * D + 32 * kb + 16 + 4 * g4);
-                et[a2][0] = lo.x; et[a2][1] = lo.y; et[a2][2] = lo.z; et[a2][3] = lo.w;
-                et[a2][4] = hi.x; et[a2][5] = hi.y; et[a2][6] = hi.z; et[a2][7] = hi.w;
+            for (int q = 0; q < r; ++q) acc -= Ab[r * SAB + q] * x[q];
+            x[r] = acc;
+        }
+        const float bj = s_beta[16 * ab + j];
+        float* Xb = s_linv + bidx(ab, ab) * BLK;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            Xb[r * SAB + j] = x[r];
+            s_t[(16 * ab + r) * SP + 16 * ab + j] = static_cast<_Float16>(x[r] * bj);
+        }
+    }
+    lds_barrier();  // (3)
+    // off-diagonal blocks by block diagonal d: Linv_{A,A-d} = -X_A sum_c A_{A,c} Linv_{c,A-d}
+    auto mm = [&](const float* mp, const float* np, floatx4 acc) {  // acc += M N (16x16 blocks)
+        float4 av;
+        av.x = mp[m16 * SAB + 4 * g4 + 0];
+        av.y = mp[m16 * SAB + 4 * g4 + 1];
+        av.z = mp[m16 * SAB + 4 * g4 + 2];
+        av.w = mp[m16 * SAB + 4 * g4 + 3];
+        floatx4 bv;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) bv[s] = np[(4 * g4 + s) * SAB + m16];
+        return mma_f32_k16(av, bv, acc);
+    };
+#pragma unroll
+    for (int d = 1; d < NSUB; ++d) {
+        if (A >= d) {
+            floatx4 y = zero4();
+#pragma unroll
+            for (int c = A - d; c < A; ++c) y = mm(s_ab + bidx(A, c) * BLK, s_linv + bidx(c, A - d) * BLK, y);
+            const float* Xa = s_linv + bidx(A, A) * BLK;
+            float4 xv;
+            xv.x = Xa[m16 * SAB + 4 * g4 + 0];
+            xv.y = Xa[m16 * SAB + 4 * g4 + 1];
+            xv.z = Xa[m16 * SAB + 4 * g4 + 2];
+            xv.w = Xa[m16 * SAB + 4 * g4 + 3];
+            const floatx4 zz = mma_f32_k16(xv, y, zero4());
+            float* dst = s_linv + bidx(A, A - d) * BLK;
+            const float bcol = s_beta[16 * (A - d) + m16];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                dst[(4 * g4 + i) * SAB + m16] = -zz[i];
+                s_t[(16 * A + 4 * g4 + i) * SP + 16 * (A - d) + m16] = static_cast<_Float16>(-zz[i] * bcol);
             }
-            half8 q8;
+        }
+        lds_barrier();  // (4), (5), (6)
+    }
+
+    // ---- M = P T (rows of this tile; lower triangular), fp16, over the dead A blocks.
+    //      K-steps of 32 tokens; a 16-token half outside [16c, 16A + 16) is zero.
+    const half4 z4 = {0, 0, 0, 0};
+#pragma unroll
+    for (int c = 0; c <= A; ++c) {
+        floatx4 acc = zero4();
+#pragma unroll
+        for (int u = c >> 1; u <= (A >> 1); ++u) {
+            const bool lo_ok = c <= 2 * u, hi_ok = 2 * u + 1 <= A;
+            const _Float16* prow = s_p + (16 * A + m16) * SP + 32 * u + 4 * g4;
+            const half8 pa8 = cat_h8(lo_ok ? ld_h4(prow) : z4, hi_ok ? ld_h4(prow + 16) : z4);
+            half8 tb;
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
-                const int c = cmap(kb, g4, j);
-                float erho = 1.f, eaft = 1.f;  // decay before this tile / after this tile
-#pragma unroll
-                for (int a2 = 0; a2 < NSUB; ++a2) {
-                    if (a2 < a) erho *= et[a2][j];
-                    if (a2 > a) eaft *= et[a2][j];
-                }
-                const float ke = static_cast<float>(s_ke[((a * KB + kb) * 64 + lane) * 8 + j]);
-                s_kt[c * ST + rl] = static_cast<_Float16>(static_cast<float>(kr16[kb][j]) * erho);  // K~ = k 2^{g}
-                s_kbt[c * ST + rl] = static_cast<_Float16>(ke * eaft);                             // Kbar = k 2^{g_C - g}
-                q8[j] = static_cast<_Float16>(static_cast<float>(qr16[kb][j]) * erho);             // Q~ = q 2^{g}
+                const int s = 32 * u + 16 * (j >> 2) + 4 * g4 + (j & 3);
+                const bool ok = (j < 4) ? lo_ok : hi_ok;
+                tb[j] = ok ? s_t[s * SP + 16 * c + m16] : static_cast<_Float16>(0.f);
             }
-            half4 qlo, qhi;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                qlo[j] = q8[j];
-                qhi[j] = q8[4 + j];
-            }
-            *reinterpret_cast<half4*>(s_q + rl * SR + 32 * kb + 4 * g4) = qlo;
-            *reinterpret_cast<half4*>(s_q + rl * SR + 32 * kb + 16 + 4 * g4) = qhi;
-            // pairs (a, bb), bb < a: reference point at the end of tile a-1; both operands <= |k|
-#pragma unroll
-            for (int bb = 0; bb < NSUB - 1; ++bb) {
-                if (bb < a) {
-                    const half8 keb = ld_h8(s_ke + ((bb * KB + kb) * 64 + lane) * 8);
-                    half8 col;
-#pragma unroll
-                    for (int j = 0; j < 8; ++j) {
-                        float f = 1.f;  // decay over the tiles strictly between bb and a
-#pragma unroll
-                        for (int a2 = 1; a2 < NSUB - 1; ++a2)
-                            if (a2 > bb && a2 < a) f *= et[a2][j];
-                        col[j] = static_cast<_Float16>(static_cast<float>(keb[j]) * f);
-                    }
-                    pa[bb] = mma_f16_k32(kr16[kb], col, pa[bb]);
-                    pp[bb] = mma_f16_k32(qr16[kb], col, pp[bb]);
-                }
-            }
+            acc = mma_f16_k32(pa8, tb, acc);
         }
+        // lane (g4, m16) holds M[16A + 4g4 + i][16c + m16]
 #pragma unroll
-        for (int bb = 0; bb < NSUB - 1; ++bb) {
-            if (bb < a) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int r = 4 * g4 + i;
-                    s_a[(16 * a + r) * SA + 16 * bb + m16] = s_beta[16 * a + r] * pa[bb][i];
-                    s_p[(16 * a + r) * SP + 16 * bb + m16] = static_cast<_Float16>(pp[bb][i]);
-                }
-            }
-        }
-        // Gamma = 2^{g_C} per key channel
-        if (tid < D) {
-            float gm = 1.f;
-#pragma unroll
-            for (int a2 = 0; a2 < NSUB; ++a2) gm *= s_etau[a2 * D + tid];
-            reinterpret_cast<float*>(card + CD::GAM)[tid] = gm;
-        }
-        lds_barrier();  // (2) A, P, K~^T, Kbar^T, Q~ complete
+        for (int i = 0; i < 4; ++i) s_m[(16 * A + 4 * g4 + i) * SP + 16 * c + m16] = static_cast<_Float16>(acc[i]);
+    }
+    lds_barrier();  // (7)
 
-        // ---- phase 3: Linv = (I + A)^{-1} (unit lower triangular, blocked by 16) and
-        //      T = Linv diag(beta) in fp16
-        if (wave == 0) {  // diagonal blocks: lane group g4 = block, lane m16 = column
-            const int ab = g4, j = m16;
-            const float* Ab = s_a + (16 * ab) * SA + 16 * ab;
-            float x[16];
+    // ---- phase 4: the card rows of this tile.  With the T and M rows of the tile as
+    //      operands (A side for T V and M V, B side for the transposed products):
+    //      U~ = T V, Uo = M V, W^T = K~^T T^T, Qe^T = Q~^T - K~^T M^T.
+    half8 ta[2], ma[2];
 #pragma unroll
-            for (int r = 0; r < 16; ++r) x[r] = (r == j) ? 1.f : 0.f;
+    for (int u = 0; u <= (A >> 1); ++u) {
+        const bool hi_ok = 2 * u + 1 <= A;
+        const _Float16* trow = s_t + (16 * A + m16) * SP + 32 * u + 4 * g4;
+        const _Float16* mrow = s_m + (16 * A + m16) * SP + 32 * u + 4 * g4;
+        ta[u] = cat_h8(ld_h4(trow), hi_ok ? ld_h4(trow + 16) : z4);
+        ma[u] = cat_h8(ld_h4(mrow), hi_ok ? ld_h4(mrow + 16) : z4);
+    }
+    floatx4 wt[2], qe[2];
 #pragma unroll
-            for (int r = 1; r < 16; ++r) {
-                float acc = x[r];
+    for (int x = 0; x < NCT; ++x) {
+        floatx4 ut = zero4(), uo = zero4(), w = zero4(), qm = zero4();
 #pragma unroll
-                for (int q = 0; q < r; ++q) acc -= Ab[r * SA + q] * x[q];
-                x[r] = acc;
-            }
-            const float bj = s_beta[16 * ab + j];
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                s_linv[(16 * ab + r) * SA + 16 * ab + j] = x[r];
-                s_t[(16 * ab + r) * SP + 16 * ab + j] = static_cast<_Float16>(x[r] * bj);
-            }
+        for (int u = 0; u <= (A >> 1); ++u) {
+            const half8 vf = cat_h8(*reinterpret_cast<const half4*>(s_vf + frag_piece(x, u, 0) + lane * 8),
+                                    *reinterpret_cast<const half4*>(s_vf + frag_piece(x, u, 1) + lane * 8));
+            const half8 kf = cat_h8(*reinterpret_cast<const half4*>(s_kf + frag_piece(x, u, 0) + lane * 8),
+                                    *reinterpret_cast<const half4*>(s_kf + frag_piece(x, u, 1) + lane * 8));
+            ut = mma_f16_k32(ta[u], vf, ut);
+            uo = mma_f16_k32(ma[u], vf, uo);
+            w = mma_f16_k32(kf, ta[u], w);
+            qm = mma_f16_k32(kf, ma[u], qm);
         }
-        lds_barrier();
-        // off-diagonal blocks by block diagonal d: Linv_{a,a-d} = -X_a sum_c A_{a,c} Linv_{c,a-d}
-        auto blk_a = [&](int r, int c) { return s_a + (16 * r) * SA + 16 * c; };
-        auto blk_x = [&](int r, int c) { return s_linv + (16 * r) * SA + 16 * c; };
-        auto mm = [&](const float* mp, const float* np, floatx4 acc) {  // acc += M N (row-major blocks)
-            const float4 av = *reinterpret_cast<const float4*>(mp + m16 * SA + 4 * g4);
-            floatx4 bv;
+        *reinterpret_cast<half4*>(card + CD::UT + ((x * 4 + A) * 64 + lane) * 8) = pack_h4(ut);
+        *reinterpret_cast<half4*>(card + CD::UO + ((x * 4 + A) * 64 + lane) * 8) = pack_h4(uo);
+        const int kb = x >> 1, cl = x & 1;
 #pragma unroll
-            for (int s = 0; s < 4; ++s) bv[s] = np[(4 * g4 + s) * SA + m16];
-            return mma_f32_k16(av, bv, acc);
-        };
-#pragma unroll
-        for (int d = 1; d < NSUB; ++d) {
-            if (wave >= d) {
-                floatx4 y = zero4();
-                for (int c = wave - d; c < wave; ++c) y = mm(blk_a(wave, c), blk_x(c, wave - d), y);
-                const float4 xv = *reinterpret_cast<const float4*>(blk_x(wave, wave) + m16 * SA + 4 * g4);
-                const floatx4 z = mma_f32_k16(xv, y, zero4());
-                float* dst = blk_x(wave, wave - d);
-                const float bcol = s_beta[16 * (wave - d) + m16];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    dst[(4 * g4 + i) * SA + m16] = -z[i];
-                    s_t[(16 * wave + 4 * g4 + i) * SP + 16 * (wave - d) + m16] = static_cast<_Float16>(-z[i] * bcol);
-                }
-            }
-            lds_barrier();
+        for (int i = 0; i < 4; ++i) {
+            wt[cl][i] = -w[i];
+            qe[cl][i] = static_cast<float>(q16[kb][4 * cl + i]) - qm[i];
         }
+        if (cl == 1) {
+            *reinterpret_cast<half8*>(card + CD::W + ((A * KB + kb) * 64 + lane) * 16) = pack_h8(wt[0], wt[1]);
+            *reinterpret_cast<half8*>(card + CD::QE + ((A * KB + kb) * 64 + lane) * 16) = pack_h8(qe[0], qe[1]);
+        }
+    }
+}
 
-        // ---- phase 4: card.  Jobs 0..KB-1: key-channel pair kb (W, Qe, Kbar^T);
-        //      jobs KB..2KB-1: value-column pair (U~, Uo)
-        // sum over tokens s < 16 (mt + 1) of A_row[s] * B_row[s] (rows in LDS, tokens contiguous).
-        // A trailing 16-token step is a K = 32 step with its upper half zeroed: one MFMA shape
-        // per accumulator chain.
-        auto kloop = [&](const _Float16* arow, const _Float16* brow, int mt, floatx4 acc) {
-            const int kend = 16 * (mt + 1);
-            int s0 = 0;
-            for (; s0 + 32 <= kend; s0 += 32)
-                acc = mma_f16_k32(ld_h8(arow + s0 + 8 * g4), ld_h8(brow + s0 + 8 * g4), acc);
-            if (s0 < kend) {
-                const half4 z4 = {0, 0, 0, 0};
-                acc = mma_f16_k32(cat_h8(ld_h4(arow + s0 + 4 * g4), z4), cat_h8(ld_h4(brow + s0 + 4 * g4), z4), acc);
-            }
-            return acc;
-        };
-        for (int job = wave; job < 2 * KB; job += 4) {
-            if (job < KB) {
-                const int kb = job;
-                floatx4 wt[2][4];
-#pragma unroll
-                for (int cl = 0; cl < 2; ++cl)
-#pragma unroll
-                    for (int mt = 0; mt < 4; ++mt)  // W^T tile = K~^T T^T
-                        wt[cl][mt] = kloop(s_kt + (16 * (2 * kb + cl) + m16) * ST, s_t + (16 * mt + m16) * SP, mt,
-                                           zero4());
-#pragma unroll
-                for (int mt = 0; mt < 4; ++mt) {
-                    floatx4 n0, n1;
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        n0[i] = -wt[0][mt][i];
-                        n1[i] = -wt[1][mt][i];
-                    }
-                    *reinterpret_cast<half8*>(card + CD::W + ((mt * KB + kb) * 64 + lane) * 16) = pack_h8(n0, n1);
-                }
-                // -W^T over this pair's rows of K~^T (only this wave reads them)
-#pragma unroll
-                for (int cl = 0; cl < 2; ++cl)
-#pragma unroll
-                    for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-                        for (int i = 0; i < 4; ++i)
-                            s_kt[(16 * (2 * kb + cl) + 4 * g4 + i) * ST + 16 * mt + m16] =
-                                static_cast<_Float16>(-wt[cl][mt][i]);
-                // Qe^T tile = Q~^T + (-W^T) P^T
-#pragma unroll
-                for (int mt = 0; mt < 4; ++mt) {
-                    floatx4 qe[2];
-#pragma unroll
-                    for (int cl = 0; cl < 2; ++cl) {
-                        const floatx4 init =
-                            unpack_h4(ld_h4(s_q + (16 * mt + m16) * SR + 16 * (2 * kb + cl) + 4 * g4));
-                        qe[cl] = kloop(s_kt + (16 * (2 * kb + cl) + m16) * ST, s_p + (16 * mt + m16) * SP, mt, init);
-                    }
-                    *reinterpret_cast<half8*>(card + CD::QE + ((mt * KB + kb) * 64 + lane) * 16) =
-                        pack_h8(qe[0], qe[1]);
-                }
-                // Kbar^T fragments of the two 16-channel tiles
-#pragma unroll
-                for (int cl = 0; cl < 2; ++cl) {
-                    const int ct = 2 * kb + cl;
-                    const _Float16* kr = s_kbt + (16 * ct + m16) * ST;
-#pragma unroll
-                    for (int u = 0; u < 2; ++u)
-                        *reinterpret_cast<half8*>(card + CD::KBT + ((ct * 2 + u) * 64 + lane) * 16) =
-                            cat_h8(ld_h4(kr + 32 * u + 4 * g4), ld_h4(kr + 32 * u + 16 + 4 * g4));
-                }
-            } else {
-                const int np = job - KB;
-                floatx4 ut[2][4];
-#pragma unroll
-                for (int cl = 0; cl < 2; ++cl) {
-                    const int nt = 2 * np + cl;
-#pragma unroll
-                    for (int mt = 0; mt < 4; ++mt) {  // U~ tile = T V
-                        ut[cl][mt] = kloop(s_t + (16 * mt + m16) * SP, s_vt + (16 * nt + m16) * ST, mt, zero4());
-                        *reinterpret_cast<half4*>(card + CD::UT + ((nt * 4 + mt) * 64 + lane) * 8) =
-                            pack_h4(ut[cl][mt]);
-                    }
-#pragma unroll
-                    for (int mt = 0; mt < 4; ++mt) {  // Uo tile = P U~ (U~ accumulators as the B operand)
-                        floatx4 acc = zero4();
-                        const _Float16* prow = s_p + (16 * mt + m16) * SP;
-#pragma unroll
-                        for (int u = 0; u < 2; ++u)
-                            if (2 * u <= mt)
-                                acc = mma_f16_k32(
-                                    cat_h8(ld_h4(prow + 32 * u + 4 * g4), ld_h4(prow + 32 * u + 16 + 4 * g4)),
-                                    pack_h8(ut[cl][2 * u], ut[cl][2 * u + 1]), acc);
-                        *reinterpret_cast<half4*>(card + CD::UO + ((nt * 4 + mt) * 64 + lane) * 8) = pack_h4(acc);
-                    }
-                }
-            }
-        }
-        lds_barrier();  // LDS is reused by the next item
+template <int D>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void kda_prep64_kernel(PrepParams p) {
+    extern __shared__ __align__(16) unsigned char smem[];
+    switch (__builtin_amdgcn_readfirstlane(threadIdx.x >> 6)) {
+        case 0: prep_tile<D, 0>(p, smem); break;
+        case 1: prep_tile<D, 1>(p, smem); break;
+        case 2: prep_tile<D, 2>(p, smem); break;
+        default: prep_tile<D, 3>(p, smem); break;
     }
 }
 
@@ -732,8 +729,10 @@ void kda_rec64_kernel(RecurParams p) {
             half8 kf[NCT][2];  // read while the U chain runs
 #pragma unroll
             for (int ct = 0; ct < NCT; ++ct) {
-                kf[ct][0] = ld_h8(sk + ((ct * 2 + 0) * 64 + lane) * 8);
-                kf[ct][1] = ld_h8(sk + ((ct * 2 + 1) * 64 + lane) * 8);
+#pragma unroll
+                for (int u = 0; u < 2; ++u)
+                    kf[ct][u] = cat_h8(ld_h4(sk + frag_piece(ct, u, 0) / 2 + lane * 4),
+                                       ld_h4(sk + frag_piece(ct, u, 1) / 2 + lane * 4));
             }
             floatx4 U[4];
 #pragma unroll
@@ -820,10 +819,14 @@ void kda_rec64_kernel(RecurParams p) {
             store_set(ra, 0);
         }
         lds_barrier();  // the first card is resident
-        for (int64_t ci = 0; ci < NC; ci += 2) {
+        // both steps in every trip: on a path that left one set's loads in flight at the
+        // back edge, the compiler would have to wait for them before reusing its registers
+        int64_t ci = 0;
+        for (; ci + 1 < NC; ci += 2) {
             step(ra, rb, ci);
-            if (ci + 1 < NC) step(rb, ra, ci + 1);
+            step(rb, ra, ci + 1);
         }
+        if (ci < NC) step(ra, rb, ci);
     }
     if (prod && NC > 0) output_part(NC - 1);
 
@@ -847,13 +850,8 @@ static hipError_t launch_d(const PrepParams& pp, const RecurParams& rp, hipStrea
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kp),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)LP::TOTAL);
         if (e != hipSuccess) return e;
-        int dev = 0, cus = 256;
-        if (hipGetDevice(&dev) != hipSuccess ||
-            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-            cus = 256;
-        const int64_t items = units * pp.NC;
-        const int64_t grid = items < cus ? items : cus;  // one persistent workgroup per CU (LDS-bound)
-        hipLaunchKernelGGL(kp, dim3((unsigned)grid), dim3(256), LP::TOTAL, stream, pp);
+        const int64_t items = units * pp.NC;  // one workgroup per card, two per CU
+        hipLaunchKernelGGL(kp, dim3((unsigned)items), dim3(256), LP::TOTAL, stream, pp);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
@@ -871,11 +869,6 @@ static hipError_t launch_d(const PrepParams& pp, const RecurParams& rp, hipStrea
 
 int64_t prefill64_card_bytes(int D) {
     return D == 128 ? c64::Card<128>::BYTES : D == 64 ? c64::Card<64>::BYTES : -1;
-}
-
-int64_t prefill64_blocks(int D, int64_t units, int64_t nc) {
-    (void)D;
-    return units * nc;
 }
 
 hipError_t launch_prefill64(int D, int out_bf16, const PrepParams& pp, const RecurParams& rp,
