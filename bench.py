@@ -113,23 +113,23 @@ def to_dev(x, dev):
 
 
 def time_calls(fn, sets, steps, warmup, stream):
-    """Run fn(set) W times untimed, then K times between two synchronisations
-    with a HIP event pair around every call.  Returns (wall seconds, per-call
-    event milliseconds)."""
+    """Run fn(set) W times untimed, then K times back to back between two
+    synchronisations, with one HIP event pair on the launch stream around the
+    K calls (an event between calls would itself cost GPU time).  Returns
+    (wall seconds, event milliseconds per call)."""
     import torch
     for i in range(warmup):
         fn(sets[i % len(sets)])
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(steps)]
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    e0.record(stream)
     for i in range(steps):
-        ev[i][0].record(stream)
         fn(sets[i % len(sets)])
-        ev[i][1].record(stream)
+    e1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    return wall, [a.elapsed_time(b) for a, b in ev]
+    return wall, e0.elapsed_time(e1) / steps
 
 
 def prefill_sets(kda, wl, n_sets, dev):
@@ -159,14 +159,13 @@ def prefill_call(kda, wl):
 def bench_prefill(kda, wl, steps, warmup, n_sets, dev, stream):
     log(f"prefill {wl.name}: building {n_sets} input set(s)")
     sets = prefill_sets(kda, wl, n_sets, dev)
-    wall, ms = time_calls(prefill_call(kda, wl), sets, steps, warmup, stream)
-    ev_ms = sum(ms) / len(ms)
+    wall, ev_ms = time_calls(prefill_call(kda, wl), sets, steps, warmup, stream)
     toks = wl.B * wl.T
     nbytes, flops = prefill_bytes(wl), prefill_flops(wl)
     res = {
         "workload": wl.name, "B": wl.B, "H": wl.H, "T": wl.T, "d": wl.Dk, "chunk": wl.chunk,
         "input_sets": n_sets, "ms_per_step_wall": 1e3 * wall / steps, "kernel_ms_mean": ev_ms,
-        "kernel_ms_min": min(ms), "tokens_per_s": toks / (wall / steps),
+        "tokens_per_s": toks / (wall / steps),
         "kernel_tokens_per_s": toks / (ev_ms / 1e3),
         "alg_bytes": nbytes, "alg_flops": flops,
         "hbm_gbs": nbytes / (ev_ms / 1e3) / 1e9, "mfma_tflops": flops / (ev_ms / 1e3) / 1e12,
@@ -190,13 +189,12 @@ def bench_decode(kda, wl, steps, warmup, dev, stream):
 
     def fn(_):
         kda.decode_step(*(x[k] for k in KEYS), state, out=x["out"])
-    wall, ms = time_calls(fn, [None], steps, warmup, stream)
-    ev_ms = sum(ms) / len(ms)
+    wall, ev_ms = time_calls(fn, [None], steps, warmup, stream)
     nbytes, flops = decode_bytes(wl), decode_flops(wl)
     res = {
         "workload": wl.name, "B": wl.B, "H": wl.H, "d": wl.Dk,
         "steps_per_s": 1e3 / ev_ms, "steps_per_s_wall": steps / wall,
-        "tokens_per_s": wl.B * 1e3 / ev_ms, "kernel_ms_mean": ev_ms, "kernel_ms_min": min(ms),
+        "tokens_per_s": wl.B * 1e3 / ev_ms, "kernel_ms_mean": ev_ms,
         "alg_bytes": nbytes, "alg_flops": flops,
         "hbm_gbs": nbytes / (ev_ms / 1e3) / 1e9,
     }

@@ -624,64 +624,7 @@ void kda_rec64_kernel(RecurParams p) {
     _Float16* sbx = reinterpret_cast<_Float16*>(smem + L::OFF_X + cs * L::SBX);
     auto zrow = [&](int64_t t) { return ((b * T + t) * H + h) * D; };  // element offset of (b, t, h, 0)
 
-    // ---- producers: 1 KiB pieces of a card, piece j handled by producer j % NP.
-    // Every piece is one 16-byte load per lane from a valid address (gate rows past T
-    // are clamped to the last token; their values are never stored).
-    // every producer moves exactly KP pieces; a producer short of work repeats the last
-    // piece (same data to the same LDS address), which keeps its load count uniform
-    auto piece_of = [&](int k) { const int j = pw + k * NP; return j < L::NPC ? j : L::NPC - 1; };
-    auto piece_src = [&](int64_t c, int j) __attribute__((always_inline)) -> const u32x4* {
-        const unsigned char* card = cards + c * CD::BYTES;
-        if (j < (int)(L::SH / 1024)) return reinterpret_cast<const u32x4*>(card + j * 1024) + lane;
-        int r = j - (int)(L::SH / 1024);
-        if (r < NCONS * 6) {
-            const int t2 = r / 6, q = r % 6, nt = grp * NCONS + t2;
-            if (q < 4)  // U~ (q = 0, 1) and Uo (q = 2, 3) slices of tile nt
-                return reinterpret_cast<const u32x4*>(card + (q < 2 ? CD::UT : CD::UO) + nt * 2048 + (q & 1) * 1024) + lane;
-            int64_t t = c * C + 32 * (q - 4) + (lane >> 1);
-            t = t < T ? t : T - 1;
-            return reinterpret_cast<const u32x4*>(gz + zrow(t) + 16 * nt + 8 * (lane & 1));
-        }
-        return reinterpret_cast<const u32x4*>(card + CD::GAM) + (lane % (D / 4));  // Gamma, replicated
-    };
-    auto piece_dst = [&](int64_t c, int j) __attribute__((always_inline)) -> u32x4* {
-        return reinterpret_cast<u32x4*>(smem + (c % L::NSTAGE) * L::STAGE + (int64_t)j * 1024) + lane;
-    };
-    // sigmoid and output work of one producer: 16 tokens x 4 columns per lane group
-    const int tq = 16 * pw + (lane >> 2), cq = 4 * (lane & 3);
-    auto sigmoid_part = [&](int64_t c) __attribute__((always_inline)) {
-        const unsigned char* st = smem + (c % L::NSTAGE) * L::STAGE;
-#pragma unroll
-        for (int t2 = 0; t2 < NCONS; ++t2) {
-            const uint2 zw = *reinterpret_cast<const uint2*>(st + L::OFF_U + t2 * L::PER + L::Z_IN + tq * 32 + cq * 2);
-            sig_t* srow = sbuf + ((c & 1) * NCONS + t2) * (64 * OST) + tq * OST + cq;
-            srow[0] = static_cast<sig_t>(sigmoidf_(__uint_as_float(zw.x << 16)));
-            srow[1] = static_cast<sig_t>(sigmoidf_(__uint_as_float(zw.x & 0xffff0000u)));
-            srow[2] = static_cast<sig_t>(sigmoidf_(__uint_as_float(zw.y << 16)));
-            srow[3] = static_cast<sig_t>(sigmoidf_(__uint_as_float(zw.y & 0xffff0000u)));
-        }
-    };
     typename Out::raw_t* gy = static_cast<typename Out::raw_t*>(p.out);
-    auto output_part = [&](int64_t c) __attribute__((always_inline)) {
-        const int64_t t = c * C + tq;
-#pragma unroll
-        for (int t2 = 0; t2 < NCONS; ++t2) {
-            const float4 o = *reinterpret_cast<const float4*>(obuf + ((c & 1) * NCONS + t2) * (64 * OST) + tq * OST + cq);
-            const sig_t* srow = sbuf + ((c & 1) * NCONS + t2) * (64 * OST) + tq * OST + cq;
-            const float y0 = o.x * static_cast<float>(srow[0]), y1 = o.y * static_cast<float>(srow[1]);
-            const float y2 = o.z * static_cast<float>(srow[2]), y3 = o.w * static_cast<float>(srow[3]);
-            if (t < T) {
-                typename Out::raw_t* dst = gy + zrow(t) + 16 * (grp * NCONS + t2) + cq;
-                if constexpr (sizeof(typename Out::raw_t) == 4) {
-                    *reinterpret_cast<float4*>(dst) = make_float4(y0, y1, y2, y3);
-                } else {
-                    *reinterpret_cast<uint2*>(dst) =
-                        make_uint2((uint32_t)Out::from_float(y0) | ((uint32_t)Out::from_float(y1) << 16),
-                                   (uint32_t)Out::from_float(y2) | ((uint32_t)Out::from_float(y3) << 16));
-                }
-            }
-        }
-    };
 
     // chain state: S[ct][i] = S[16ct + 4g4 + i][col]
     const int nt = grp * NCONS + cs;
@@ -790,45 +733,114 @@ void kda_rec64_kernel(RecurParams p) {
             lds_barrier();  // B
         }
     } else {
-        // two register sets: while one is in flight (chunk n+2), the other (chunk n+1,
-        // loaded one iteration earlier) is written to LDS
-        u32x4 ra[KP], rb[KP];
-        auto load_set = [&](u32x4 (&r)[KP], int64_t c) __attribute__((always_inline)) {
-#pragma unroll
-            for (int k = 0; k < KP; ++k) r[k] = *piece_src(c, piece_of(k));
+        // Each producer is compiled for its index, so that the source of every piece it
+        // moves is fixed at compile time (straight-line address arithmetic, no branches).
+        auto producer = [&](auto pwc) __attribute__((always_inline)) {
+            constexpr int PW = decltype(pwc)::value;
+        // ---- producers: 1 KiB pieces of a card, piece j handled by producer j % NP.
+        // Every piece is one 16-byte load per lane from a valid address (gate rows past T
+        // are clamped to the last token; their values are never stored).
+        // every producer moves exactly KP pieces; a producer short of work repeats the last
+        // piece (same data to the same LDS address), which keeps its load count uniform
+        auto piece_of = [&](int k) { const int j = PW + k * NP; return j < L::NPC ? j : L::NPC - 1; };
+        auto piece_src = [&](int64_t c, int j) __attribute__((always_inline)) -> const u32x4* {
+            const unsigned char* card = cards + c * CD::BYTES;
+            if (j < (int)(L::SH / 1024)) return reinterpret_cast<const u32x4*>(card + j * 1024) + lane;
+            int r = j - (int)(L::SH / 1024);
+            if (r < NCONS * 6) {
+                const int t2 = r / 6, q = r % 6, nt = grp * NCONS + t2;
+                if (q < 4)  // U~ (q = 0, 1) and Uo (q = 2, 3) slices of tile nt
+                    return reinterpret_cast<const u32x4*>(card + (q < 2 ? CD::UT : CD::UO) + nt * 2048 + (q & 1) * 1024) + lane;
+                int64_t t = c * C + 32 * (q - 4) + (lane >> 1);
+                t = t < T ? t : T - 1;
+                return reinterpret_cast<const u32x4*>(gz + zrow(t) + 16 * nt + 8 * (lane & 1));
+            }
+            return reinterpret_cast<const u32x4*>(card + CD::GAM) + (lane % (D / 4));  // Gamma, replicated
         };
-        auto store_set = [&](const u32x4 (&r)[KP], int64_t c) __attribute__((always_inline)) {
-#pragma unroll
-            for (int k = 0; k < KP; ++k) *piece_dst(c, piece_of(k)) = r[k];
+        auto piece_dst = [&](int64_t c, int j) __attribute__((always_inline)) -> u32x4* {
+            return reinterpret_cast<u32x4*>(smem + (c % L::NSTAGE) * L::STAGE + (int64_t)j * 1024) + lane;
         };
-        // Branch-free: past the end the producers reload the last chunk and rewrite the slot
-        // that nobody reads any more, so both register sets follow the same code path.
-        auto step = [&](u32x4 (&ld)[KP], const u32x4 (&wr)[KP], int64_t ci) __attribute__((always_inline)) {
-            load_set(ld, ci + 2 < NC ? ci + 2 : NC - 1);  // the set that held chunk ci
-            sigmoid_part(ci);
-            if (ci >= 1) output_part(ci - 1);
-            lds_barrier();  // A
-            wait_vm<KP>();          // chunk ci + 1, loaded one iteration ago into the other set
-            store_set(wr, ci + 1);  // the slot of chunk ci - 1, released by barrier B
-            lds_barrier();  // B
+        // sigmoid and output work of one producer: 16 tokens x 4 columns per lane group
+        const int tq = 16 * PW + (lane >> 2), cq = 4 * (lane & 3);
+        auto sigmoid_part = [&](int64_t c) __attribute__((always_inline)) {
+            const unsigned char* st = smem + (c % L::NSTAGE) * L::STAGE;
+    #pragma unroll
+            for (int t2 = 0; t2 < NCONS; ++t2) {
+                const uint2 zw = *reinterpret_cast<const uint2*>(st + L::OFF_U + t2 * L::PER + L::Z_IN + tq * 32 + cq * 2);
+                sig_t* srow = sbuf + ((c & 1) * NCONS + t2) * (64 * OST) + tq * OST + cq;
+                srow[0] = static_cast<sig_t>(sigmoidf_(__uint_as_float(zw.x << 16)));
+                srow[1] = static_cast<sig_t>(sigmoidf_(__uint_as_float(zw.x & 0xffff0000u)));
+                srow[2] = static_cast<sig_t>(sigmoidf_(__uint_as_float(zw.y << 16)));
+                srow[3] = static_cast<sig_t>(sigmoidf_(__uint_as_float(zw.y & 0xffff0000u)));
+            }
         };
-        if (NC > 0) {
-            load_set(ra, 0);
-            load_set(rb, NC > 1 ? 1 : 0);
-            wait_vm<KP>();
-            store_set(ra, 0);
+        auto output_part = [&](int64_t c) __attribute__((always_inline)) {
+            const int64_t t = c * C + tq;
+    #pragma unroll
+            for (int t2 = 0; t2 < NCONS; ++t2) {
+                const float4 o = *reinterpret_cast<const float4*>(obuf + ((c & 1) * NCONS + t2) * (64 * OST) + tq * OST + cq);
+                const sig_t* srow = sbuf + ((c & 1) * NCONS + t2) * (64 * OST) + tq * OST + cq;
+                const float y0 = o.x * static_cast<float>(srow[0]), y1 = o.y * static_cast<float>(srow[1]);
+                const float y2 = o.z * static_cast<float>(srow[2]), y3 = o.w * static_cast<float>(srow[3]);
+                if (t < T) {
+                    typename Out::raw_t* dst = gy + zrow(t) + 16 * (grp * NCONS + t2) + cq;
+                    if constexpr (sizeof(typename Out::raw_t) == 4) {
+                        *reinterpret_cast<float4*>(dst) = make_float4(y0, y1, y2, y3);
+                    } else {
+                        *reinterpret_cast<uint2*>(dst) =
+                            make_uint2((uint32_t)Out::from_float(y0) | ((uint32_t)Out::from_float(y1) << 16),
+                                       (uint32_t)Out::from_float(y2) | ((uint32_t)Out::from_float(y3) << 16));
+                    }
+                }
+            }
+        };
+            // two register sets: while one is in flight (chunk n+2), the other (chunk n+1,
+            // loaded one iteration earlier) is written to LDS
+            u32x4 ra[KP], rb[KP];
+            auto load_set = [&](u32x4 (&r)[KP], int64_t c) __attribute__((always_inline)) {
+    #pragma unroll
+                for (int k = 0; k < KP; ++k) r[k] = *piece_src(c, piece_of(k));
+            };
+            auto store_set = [&](const u32x4 (&r)[KP], int64_t c) __attribute__((always_inline)) {
+    #pragma unroll
+                for (int k = 0; k < KP; ++k) *piece_dst(c, piece_of(k)) = r[k];
+            };
+            // Branch-free: past the end the producers reload the last chunk and rewrite the slot
+            // that nobody reads any more, so both register sets follow the same code path.
+            auto step = [&](u32x4 (&ld)[KP], const u32x4 (&wr)[KP], int64_t ci) __attribute__((always_inline)) {
+                load_set(ld, ci + 2 < NC ? ci + 2 : NC - 1);  // the set that held chunk ci
+                sigmoid_part(ci);
+                if (ci >= 1) output_part(ci - 1);
+                lds_barrier();  // A
+                wait_vm<KP>();          // chunk ci + 1, loaded one iteration ago into the other set
+                store_set(wr, ci + 1);  // the slot of chunk ci - 1, released by barrier B
+                lds_barrier();  // B
+            };
+            if (NC > 0) {
+                load_set(ra, 0);
+                load_set(rb, NC > 1 ? 1 : 0);
+                wait_vm<KP>();
+                store_set(ra, 0);
+            }
+            lds_barrier();  // the first card is resident
+            // both steps in every trip: on a path that left one set's loads in flight at the
+            // back edge, the compiler would have to wait for them before reusing its registers
+            int64_t ci = 0;
+            for (; ci + 1 < NC; ci += 2) {
+                step(ra, rb, ci);
+                step(rb, ra, ci + 1);
+            }
+            if (ci < NC) step(ra, rb, ci);
+            if (NC > 0) output_part(NC - 1);
+        };
+        static_assert(NP == 4, "producer dispatch");
+        switch (__builtin_amdgcn_readfirstlane(pw)) {
+            case 0: producer(Int<0>{}); break;
+            case 1: producer(Int<1>{}); break;
+            case 2: producer(Int<2>{}); break;
+            default: producer(Int<3>{}); break;
         }
-        lds_barrier();  // the first card is resident
-        // both steps in every trip: on a path that left one set's loads in flight at the
-        // back edge, the compiler would have to wait for them before reusing its registers
-        int64_t ci = 0;
-        for (; ci + 1 < NC; ci += 2) {
-            step(ra, rb, ci);
-            step(rb, ra, ci + 1);
-        }
-        if (ci < NC) step(ra, rb, ci);
     }
-    if (prod && NC > 0) output_part(NC - 1);
 
     if (chain && p.sT) {
         float* sT = p.sT + unit * (int64_t)D * D;
