@@ -535,46 +535,44 @@ void kda_prep64_kernel(PrepParams p) {
 //
 // Per workgroup, for each of its NCONS 16-column value tiles, a chain wave and an
 // output wave, plus NP producer waves.  Iteration n, around the barriers A and B:
-//   chain     S_n (fp16 copy) -> LDS before A; after A: U = U~ - W S_n,
+//   chain     before A: S_n (fp16 copy) -> LDS; after A: U = U~ - W S_n,
 //             S_{n+1} = Diag(Gamma) S_n + Kbar^T U (fp32 state in accumulators)
-//   output    after A: O = Uo + Qe S_n -> LDS tile
-//   producers before A: issue the loads of chunk n+2 into one of two register
-//             sets, compute sigmoid(z) of chunk n and store y = O * sigmoid(z) of
+//   output    before A: load Qe and Uo of chunk n+1 into its other register set;
+//             after A: O = Uo + Qe S_n -> LDS tile
+//   producers before A: start the direct-to-LDS copies of chunk n+2 (W, Kbar^T, the
+//             U~ slices, Gamma) into ring slot (n+2) % 3, load the gate logits of
+//             chunk n+1, compute sigmoid(z) of chunk n and store y = O sigmoid(z) of
 //             chunk n-1 (a quarter of the tokens each, 16-byte stores);
-//             after A: wait for chunk n+1 (loaded one iteration earlier) and
-//             write it into LDS ring slot (n+1) % 2.
-// A card is therefore in flight for two iterations, while LDS holds only two.
+//             after A: wait for the copies of chunk n+1 (issued one iteration earlier).
+// A chunk's copy is in flight for about two iterations; the LDS ring holds three.
 template <int D, int NCONS>
 struct RecL {
     using CD = Card<D>;
     static constexpr int KB = D / 32;
-    static constexpr int NP = 4;                          // producer waves
-    static constexpr int64_t SH = CD::UT;                 // W, QE, KBT: shared by all tiles
-    // per 16-column tile: U~ slice (2 KiB), Uo slice (2 KiB), gate logits [64][16] bf16 (2 KiB)
-    static constexpr int64_t PER = 6 * 1024;
-    static constexpr int64_t OFF_U = SH;                  // tile t2 at OFF_U + t2 * PER
-    static constexpr int64_t UO_IN = 2048, Z_IN = 4096;   // offsets inside a tile block
-    static constexpr int64_t OFF_G = SH + NCONS * PER;
-    static constexpr int64_t STAGE = OFF_G + 1024;        // Gamma (D * 4 bytes) in a 1 KiB piece
-    static constexpr int NSTAGE = 2;
-    static constexpr int NPC = (int)(STAGE / 1024);       // 1 KiB pieces per card
-    static constexpr int KP = (NPC + NP - 1) / NP;        // pieces per producer
-    static constexpr int OST = 20;                        // [token][16 columns] row stride (elements)
-    static constexpr int64_t OTILE = 64 * OST * 4;        // one tile's 64 x 16 fp32 read-out
-    // sigmoid(z) tiles: fp32 with one tile; fp16 (relative error 2^-11) when two tiles
-    // must share the LDS budget
-    using sig_t = typename std::conditional<NCONS == 1, float, _Float16>::type;
-    static constexpr int64_t STILE = 64 * OST * (int64_t)sizeof(sig_t);
-    static constexpr int64_t SBX = (int64_t)KB * 64 * 16;  // fp16 copy of one tile's state (B operand)
-    static constexpr int64_t OFF_O = NSTAGE * STAGE;                 // read-out O [2][NCONS]
-    static constexpr int64_t OFF_S = OFF_O + 2 * NCONS * OTILE;      // sigmoid(z) [2][NCONS]
-    static constexpr int64_t OFF_X = OFF_S + 2 * NCONS * STILE;      // state copies [NCONS]
+    static constexpr int NP = 4;                              // producer waves
+    static constexpr int NW = 4 * KB;                         // 1 KiB pieces of W; as many of Kbar^T
+    static constexpr int64_t OFF_WS = 0;                      // W fragments (card order)
+    static constexpr int64_t OFF_KS = (int64_t)NW * 1024;     // Kbar^T fragments (card order)
+    static constexpr int64_t OFF_US = 2 * OFF_KS;             // U~ slices, 2 KiB per tile
+    static constexpr int64_t OFF_ZS = OFF_US + NCONS * 2048;  // gate logits [64][16] bf16, 2 KiB per tile
+    static constexpr int64_t OFF_GS = OFF_ZS + NCONS * 2048;  // Gamma (D * 4 bytes) in a 1 KiB piece
+    static constexpr int64_t STAGE = OFF_GS + 1024;
+    static constexpr int NSTAGE = 3;
+    static constexpr int NPC = (int)(STAGE / 1024);           // pieces per stage
+    static constexpr int KP = (NPC + NP - 1) / NP;            // pieces per producer
+    static constexpr int OST = 20;                            // [token][16 columns] fp32 row stride
+    static constexpr int64_t OTILE = 64 * OST * 4;            // one tile's 64 x 16 fp32 tile
+    static constexpr int64_t SBX = (int64_t)KB * 64 * 16;     // fp16 copy of one tile's state (B operand)
+    static constexpr int64_t OFF_O = NSTAGE * STAGE;          // read-out O [NCONS]
+    static constexpr int64_t OFF_S = OFF_O + NCONS * OTILE;   // sigmoid(z) [NCONS]
+    static constexpr int64_t OFF_X = OFF_S + NCONS * OTILE;   // state copies [NCONS]
     static constexpr int64_t TOTAL = OFF_X + NCONS * SBX;
     static constexpr int WAVES = 2 * NCONS + NP;
     static_assert(STAGE % 1024 == 0 && D * 4 <= 1024, "card pieces");
     static_assert(TOTAL <= 160 * 1024, "recurrence LDS budget");
     static_assert(OFF_O % 16 == 0 && OFF_X % 16 == 0, "alignment");
-    static_assert(KP <= 63, "outstanding-load counter");
+    static_assert(KP + NCONS <= 63, "outstanding-load counter");
+    static_assert(NP == 4 && C == 64, "gate pieces: 32 tokens x 32 bytes per piece");
 };
 
 // vmcnt(n) for small compile-time n (expcnt and lgkmcnt left unconstrained)
@@ -588,6 +586,21 @@ template <int I>
 struct Int {
     static constexpr int value = I;
 };
+
+// 16 bytes per lane from global memory straight into LDS: lane l's bytes land at LDS
+// byte offset lds + 16 l (lds is the same for the whole wave).  Written as inline
+// assembly so that the compiler does not treat the copy as a pending LDS store: it
+// would otherwise wait for every copy in flight before this wave's next LDS access.
+// The copy is counted by vmcnt like any load; its completion is awaited explicitly
+// (wait_vm) before the barrier that hands the slot to the consumers.  M0 holds the
+// LDS base (the kernels keep nothing else in M0).
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void lds_copy16(const void* g, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+__device__ __forceinline__ uint32_t lds_offset(const void* p) { return (uint32_t)(uintptr_t)p; }
 
 template <int D, class Out, int NCONS>
 __global__ __launch_bounds__((2 * NCONS + 4) * 64) __attribute__((amdgpu_waves_per_eu(1, 2)))
@@ -614,41 +627,35 @@ void kda_rec64_kernel(RecurParams p) {
     const unsigned char* cards = static_cast<const unsigned char*>(p.ws) + unit * NC * CD::BYTES;
     const bool chain = wave < NCONS;
     const bool outw = wave >= NCONS && wave < 2 * NCONS;
-    const bool prod = wave >= 2 * NCONS;
-    const int pw = prod ? wave - 2 * NCONS : 0;               // producer index
+    const int pw = wave - 2 * NCONS;                          // producer index (producers only)
     const int cs = chain ? wave : (outw ? wave - NCONS : 0);  // value tile of a chain / output wave
     const uint16_t* gz = static_cast<const uint16_t*>(p.gate);
     float* obuf = reinterpret_cast<float*>(smem + L::OFF_O);
-    using sig_t = typename L::sig_t;
-    sig_t* sbuf = reinterpret_cast<sig_t*>(smem + L::OFF_S);
+    float* sbuf = reinterpret_cast<float*>(smem + L::OFF_S);
     _Float16* sbx = reinterpret_cast<_Float16*>(smem + L::OFF_X + cs * L::SBX);
-    auto zrow = [&](int64_t t) { return ((b * T + t) * H + h) * D; };  // element offset of (b, t, h, 0)
-
+    const int64_t zrow0 = (b * T * H + h) * D, zstride = H * D;  // element offset of (b, t, h, 0)
     typename Out::raw_t* gy = static_cast<typename Out::raw_t*>(p.out);
+    auto slot = [&](int64_t c) { return smem + (c % L::NSTAGE) * L::STAGE; };
 
-    // chain state: S[ct][i] = S[16ct + 4g4 + i][col]
-    const int nt = grp * NCONS + cs;
-    const int col = 16 * nt + m16;
-    floatx4 S[NCT];
+    // each role runs its own loop (so that no role carries another's registers); all of them
+    // pass the same barriers: one before the first chunk, then A and B once per chunk
     if (chain) {
+        // chain state: S[ct][i] = S[16ct + 4g4 + i][col]
+        const int nt = grp * NCONS + cs;
+        const int col = 16 * nt + m16;
+        floatx4 S[NCT];
         const float* s0 = p.s0 ? p.s0 + unit * (int64_t)D * D : nullptr;
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
             for (int i = 0; i < 4; ++i) S[ct][i] = s0 ? s0[(16 * ct + 4 * g4 + i) * D + col] : 0.f;
-    }
-
-
-    // each role runs its own loop (so that no role carries another's registers); all of them
-    // pass the same barriers: A and B once per chunk
-    if (chain) {
         lds_barrier();  // the first card is resident
         for (int64_t ci = 0; ci < NC; ++ci) {
-            const unsigned char* st = smem + (ci % L::NSTAGE) * L::STAGE;
-            const _Float16* sw = reinterpret_cast<const _Float16*>(st + CD::W);
-            const _Float16* sk = reinterpret_cast<const _Float16*>(st + CD::KBT);
-            const _Float16* su = reinterpret_cast<const _Float16*>(st + L::OFF_U + cs * L::PER);
-            const float* sg = reinterpret_cast<const float*>(st + L::OFF_G);
+            const unsigned char* st = slot(ci);
+            const _Float16* sw = reinterpret_cast<const _Float16*>(st + L::OFF_WS);
+            const _Float16* sk = reinterpret_cast<const _Float16*>(st + L::OFF_KS);
+            const _Float16* su = reinterpret_cast<const _Float16*>(st + L::OFF_US + cs * 2048);
+            const float* sg = reinterpret_cast<const float*>(st + L::OFF_GS);
             // the state at the chunk start, as the B operand (logical k = 8g4 + j of step kb is
             // channel cmap(kb, g4, j)), for this wave and for the output wave
             half8 Sb[KB];
@@ -700,20 +707,30 @@ void kda_rec64_kernel(RecurParams p) {
                 for (int ct = 0; ct < NCT; ++ct) S[ct] = mma_f16_k32(kf[ct][u], Ub[u], S[ct]);  // + Kbar^T U
             lds_barrier();  // B
         }
+        if (p.sT) {
+            float* sT = p.sT + unit * (int64_t)D * D;
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) sT[(16 * ct + 4 * g4 + i) * D + col] = S[ct][i];
+        }
     } else if (outw) {
-        lds_barrier();  // the first card is resident
-        for (int64_t ci = 0; ci < NC; ++ci) {
-            const unsigned char* st = smem + (ci % L::NSTAGE) * L::STAGE;
-            const _Float16* sq = reinterpret_cast<const _Float16*>(st + CD::QE);
-            const _Float16* su = reinterpret_cast<const _Float16*>(st + L::OFF_U + cs * L::PER);
-            half8 qf[4][KB];
-            half4 uo[4];
+        // Qe and Uo of one chunk, straight from the card into registers; two sets, the next
+        // chunk's in flight while this one is used
+        const int nt = grp * NCONS + cs;
+        auto load_q = [&](half8 (&qf)[4][KB], half4 (&uo)[4], int64_t c) __attribute__((always_inline)) {
+            const unsigned char* card = cards + (c < NC ? c : NC - 1) * CD::BYTES;
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt) {
 #pragma unroll
-                for (int kb = 0; kb < KB; ++kb) qf[mt][kb] = ld_h8(sq + ((mt * KB + kb) * 64 + lane) * 8);
-                uo[mt] = ld_h4(su + L::UO_IN / 2 + (mt * 64 + lane) * 4);
+                for (int kb = 0; kb < KB; ++kb)
+                    qf[mt][kb] = *reinterpret_cast<const half8*>(card + CD::QE + ((mt * KB + kb) * 64 + lane) * 16);
+                uo[mt] = *reinterpret_cast<const half4*>(card + CD::UO + ((nt * 4 + mt) * 64 + lane) * 8);
             }
+        };
+        auto step = [&](half8 (&qf)[4][KB], half4 (&uo)[4], half8 (&qn)[4][KB], half4 (&un)[4], int64_t ci)
+                        __attribute__((always_inline)) {
+            load_q(qn, un, ci + 1);
             lds_barrier();  // A
             half8 Sb[KB];
 #pragma unroll
@@ -725,112 +742,114 @@ void kda_rec64_kernel(RecurParams p) {
             for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
                 for (int mt = 0; mt < 4; ++mt) O[mt] = mma_f16_k32(qf[mt][kb], Sb[kb], O[mt]);  // + Qe S
-            float* orow = obuf + ((ci & 1) * NCONS + cs) * (64 * OST);
+            float* orow = obuf + cs * (64 * OST);
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) orow[(16 * mt + 4 * g4 + i) * OST + m16] = O[mt][i];
             lds_barrier();  // B
+        };
+        half8 qa[4][KB], qb[4][KB];
+        half4 ua[4], ub[4];
+        load_q(qa, ua, 0);
+        lds_barrier();  // the first card is resident
+        // both steps in every trip (see the producers)
+        int64_t ci = 0;
+        for (; ci + 1 < NC; ci += 2) {
+            step(qa, ua, qb, ub, ci);
+            step(qb, ub, qa, ua, ci + 1);
         }
+        if (ci < NC) step(qa, ua, qb, ub, ci);
     } else {
         // Each producer is compiled for its index, so that the source of every piece it
-        // moves is fixed at compile time (straight-line address arithmetic, no branches).
+        // copies is fixed at compile time (straight-line address arithmetic, no branches).
         auto producer = [&](auto pwc) __attribute__((always_inline)) {
             constexpr int PW = decltype(pwc)::value;
-        // ---- producers: 1 KiB pieces of a card, piece j handled by producer j % NP.
-        // Every piece is one 16-byte load per lane from a valid address (gate rows past T
-        // are clamped to the last token; their values are never stored).
-        // every producer moves exactly KP pieces; a producer short of work repeats the last
-        // piece (same data to the same LDS address), which keeps its load count uniform
-        auto piece_of = [&](int k) { const int j = PW + k * NP; return j < L::NPC ? j : L::NPC - 1; };
-        auto piece_src = [&](int64_t c, int j) __attribute__((always_inline)) -> const u32x4* {
-            const unsigned char* card = cards + c * CD::BYTES;
-            if (j < (int)(L::SH / 1024)) return reinterpret_cast<const u32x4*>(card + j * 1024) + lane;
-            int r = j - (int)(L::SH / 1024);
-            if (r < NCONS * 6) {
-                const int t2 = r / 6, q = r % 6, nt = grp * NCONS + t2;
-                if (q < 4)  // U~ (q = 0, 1) and Uo (q = 2, 3) slices of tile nt
-                    return reinterpret_cast<const u32x4*>(card + (q < 2 ? CD::UT : CD::UO) + nt * 2048 + (q & 1) * 1024) + lane;
-                int64_t t = c * C + 32 * (q - 4) + (lane >> 1);
-                t = t < T ? t : T - 1;
-                return reinterpret_cast<const u32x4*>(gz + zrow(t) + 16 * nt + 8 * (lane & 1));
-            }
-            return reinterpret_cast<const u32x4*>(card + CD::GAM) + (lane % (D / 4));  // Gamma, replicated
-        };
-        auto piece_dst = [&](int64_t c, int j) __attribute__((always_inline)) -> u32x4* {
-            return reinterpret_cast<u32x4*>(smem + (c % L::NSTAGE) * L::STAGE + (int64_t)j * 1024) + lane;
-        };
-        // sigmoid and output work of one producer: 16 tokens x 4 columns per lane group
-        const int tq = 16 * PW + (lane >> 2), cq = 4 * (lane & 3);
-        auto sigmoid_part = [&](int64_t c) __attribute__((always_inline)) {
-            const unsigned char* st = smem + (c % L::NSTAGE) * L::STAGE;
-    #pragma unroll
-            for (int t2 = 0; t2 < NCONS; ++t2) {
-                const uint2 zw = *reinterpret_cast<const uint2*>(st + L::OFF_U + t2 * L::PER + L::Z_IN + tq * 32 + cq * 2);
-                sig_t* srow = sbuf + ((c & 1) * NCONS + t2) * (64 * OST) + tq * OST + cq;
-                srow[0] = static_cast<sig_t>(sigmoidf_(__uint_as_float(zw.x << 16)));
-                srow[1] = static_cast<sig_t>(sigmoidf_(__uint_as_float(zw.x & 0xffff0000u)));
-                srow[2] = static_cast<sig_t>(sigmoidf_(__uint_as_float(zw.y << 16)));
-                srow[3] = static_cast<sig_t>(sigmoidf_(__uint_as_float(zw.y & 0xffff0000u)));
-            }
-        };
-        auto output_part = [&](int64_t c) __attribute__((always_inline)) {
-            const int64_t t = c * C + tq;
-    #pragma unroll
-            for (int t2 = 0; t2 < NCONS; ++t2) {
-                const float4 o = *reinterpret_cast<const float4*>(obuf + ((c & 1) * NCONS + t2) * (64 * OST) + tq * OST + cq);
-                const sig_t* srow = sbuf + ((c & 1) * NCONS + t2) * (64 * OST) + tq * OST + cq;
-                const float y0 = o.x * static_cast<float>(srow[0]), y1 = o.y * static_cast<float>(srow[1]);
-                const float y2 = o.z * static_cast<float>(srow[2]), y3 = o.w * static_cast<float>(srow[3]);
-                if (t < T) {
-                    typename Out::raw_t* dst = gy + zrow(t) + 16 * (grp * NCONS + t2) + cq;
-                    if constexpr (sizeof(typename Out::raw_t) == 4) {
-                        *reinterpret_cast<float4*>(dst) = make_float4(y0, y1, y2, y3);
-                    } else {
-                        *reinterpret_cast<uint2*>(dst) =
-                            make_uint2((uint32_t)Out::from_float(y0) | ((uint32_t)Out::from_float(y1) << 16),
-                                       (uint32_t)Out::from_float(y2) | ((uint32_t)Out::from_float(y3) << 16));
+            // piece j of a stage is copied by producer j % NP; every producer issues exactly
+            // KP copies per chunk (one short of work repeats its last piece: same bytes to
+            // the same place), so that its count of outstanding loads is fixed
+            auto piece = [&](int64_t c, int k) __attribute__((always_inline)) {
+                const int j0 = PW + k * NP, j = j0 < L::NPC ? j0 : L::NPC - 1;
+                const unsigned char* card = cards + c * CD::BYTES;
+                const void* src;
+                if (j < L::NW) {
+                    src = card + CD::W + j * 1024 + lane * 16;
+                } else if (j < 2 * L::NW) {
+                    src = card + CD::KBT + (j - L::NW) * 1024 + lane * 16;
+                } else if (j < 2 * L::NW + 2 * NCONS) {
+                    const int r = j - 2 * L::NW;
+                    src = card + CD::UT + (grp * NCONS + r / 2) * 2048 + (r % 2) * 1024 + lane * 16;
+                } else if (j < 2 * L::NW + 4 * NCONS) {
+                    // gate logits: 32 tokens per piece, lane pair (2m, 2m+1) = token m's 16 columns
+                    const int r = j - 2 * L::NW - 2 * NCONS;
+                    int64_t t = c * C + 32 * (r % 2) + (lane >> 1);
+                    t = t < T ? t : T - 1;  // in bounds; rows past the end are never stored
+                    src = gz + zrow0 + t * zstride + 16 * (grp * NCONS + r / 2) + 8 * (lane & 1);
+                } else {
+                    src = card + CD::GAM + (lane % (D / 4)) * 16;  // Gamma, replicated
+                }
+                lds_copy16(src, lds_offset(slot(c) + (int64_t)j * 1024));
+            };
+            auto copy_chunk = [&](int64_t c) __attribute__((always_inline)) {
+                const int64_t cc = c < NC ? c : NC - 1;  // past the end: the last chunk again
+#pragma unroll
+                for (int k = 0; k < KP; ++k) piece(cc, k);
+            };
+            // gate and output: 16 tokens x 4 columns per lane group, per tile
+            const int tq = 16 * PW + (lane >> 2), cq = 4 * (lane & 3);
+            auto sigmoid_part = [&](int64_t c) __attribute__((always_inline)) {
+                const unsigned char* st = slot(c);
+#pragma unroll
+                for (int t2 = 0; t2 < NCONS; ++t2) {
+                    const uint2 z = *reinterpret_cast<const uint2*>(st + L::OFF_ZS + t2 * 2048 + tq * 32 + cq * 2);
+                    float4 sg;
+                    sg.x = sigmoidf_(__uint_as_float(z.x << 16));
+                    sg.y = sigmoidf_(__uint_as_float(z.x & 0xffff0000u));
+                    sg.z = sigmoidf_(__uint_as_float(z.y << 16));
+                    sg.w = sigmoidf_(__uint_as_float(z.y & 0xffff0000u));
+                    *reinterpret_cast<float4*>(sbuf + t2 * (64 * OST) + tq * OST + cq) = sg;
+                }
+            };
+            auto output_part = [&](int64_t c) __attribute__((always_inline)) {
+                const int64_t t = c * C + tq;
+#pragma unroll
+                for (int t2 = 0; t2 < NCONS; ++t2) {
+                    const int tile = t2 * (64 * OST) + tq * OST + cq;
+                    const float4 o = *reinterpret_cast<const float4*>(obuf + tile);
+                    const float4 sg = *reinterpret_cast<const float4*>(sbuf + tile);
+                    const float y0 = o.x * sg.x, y1 = o.y * sg.y, y2 = o.z * sg.z, y3 = o.w * sg.w;
+                    if (t < T) {
+                        typename Out::raw_t* dst = gy + zrow0 + t * zstride + 16 * (grp * NCONS + t2) + cq;
+                        if constexpr (sizeof(typename Out::raw_t) == 4) {
+                            *reinterpret_cast<float4*>(dst) = make_float4(y0, y1, y2, y3);
+                        } else {
+                            *reinterpret_cast<uint2*>(dst) =
+                                make_uint2((uint32_t)Out::from_float(y0) | ((uint32_t)Out::from_float(y1) << 16),
+                                           (uint32_t)Out::from_float(y2) | ((uint32_t)Out::from_float(y3) << 16));
+                        }
                     }
                 }
-            }
-        };
-            // two register sets: while one is in flight (chunk n+2), the other (chunk n+1,
-            // loaded one iteration earlier) is written to LDS
-            u32x4 ra[KP], rb[KP];
-            auto load_set = [&](u32x4 (&r)[KP], int64_t c) __attribute__((always_inline)) {
-    #pragma unroll
-                for (int k = 0; k < KP; ++k) r[k] = *piece_src(c, piece_of(k));
             };
-            auto store_set = [&](const u32x4 (&r)[KP], int64_t c) __attribute__((always_inline)) {
-    #pragma unroll
-                for (int k = 0; k < KP; ++k) *piece_dst(c, piece_of(k)) = r[k];
-            };
-            // Branch-free: past the end the producers reload the last chunk and rewrite the slot
-            // that nobody reads any more, so both register sets follow the same code path.
-            auto step = [&](u32x4 (&ld)[KP], const u32x4 (&wr)[KP], int64_t ci) __attribute__((always_inline)) {
-                load_set(ld, ci + 2 < NC ? ci + 2 : NC - 1);  // the set that held chunk ci
-                sigmoid_part(ci);
+            // Iteration ci (vmcnt is in order): y of chunk ci-1 (at most NCONS stores; O from
+            // the output wave, sigmoid(z) written by this wave one iteration earlier), sigmoid(z)
+            // of chunk ci, then the KP copies of chunk ci+2 into the slot of chunk ci-1.  After
+            // barrier A, vmcnt(KP) leaves only this iteration's copies in flight: chunk ci+1's,
+            // issued one iteration earlier, have landed before barrier B publishes them.
+            auto step = [&](int64_t ci) __attribute__((always_inline)) {
                 if (ci >= 1) output_part(ci - 1);
+                sigmoid_part(ci);
+                copy_chunk(ci + 2);  // slot of chunk ci - 1, released by barrier B
                 lds_barrier();  // A
-                wait_vm<KP>();          // chunk ci + 1, loaded one iteration ago into the other set
-                store_set(wr, ci + 1);  // the slot of chunk ci - 1, released by barrier B
-                lds_barrier();  // B
+                wait_vm<KP>();
+                lds_barrier();  // B: chunk ci + 1 is resident
             };
             if (NC > 0) {
-                load_set(ra, 0);
-                load_set(rb, NC > 1 ? 1 : 0);
-                wait_vm<KP>();
-                store_set(ra, 0);
+                copy_chunk(0);
+                copy_chunk(1);
+                wait_vm<KP>();  // chunk 0
             }
             lds_barrier();  // the first card is resident
-            // both steps in every trip: on a path that left one set's loads in flight at the
-            // back edge, the compiler would have to wait for them before reusing its registers
-            int64_t ci = 0;
-            for (; ci + 1 < NC; ci += 2) {
-                step(ra, rb, ci);
-                step(rb, ra, ci + 1);
-            }
-            if (ci < NC) step(ra, rb, ci);
+            for (int64_t ci = 0; ci < NC; ++ci) step(ci);
             if (NC > 0) output_part(NC - 1);
         };
         static_assert(NP == 4, "producer dispatch");
@@ -840,14 +859,6 @@ void kda_rec64_kernel(RecurParams p) {
             case 2: producer(Int<2>{}); break;
             default: producer(Int<3>{}); break;
         }
-    }
-
-    if (chain && p.sT) {
-        float* sT = p.sT + unit * (int64_t)D * D;
-#pragma unroll
-        for (int ct = 0; ct < NCT; ++ct)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) sT[(16 * ct + 4 * g4 + i) * D + col] = S[ct][i];
     }
 }
 
