@@ -252,6 +252,33 @@ def counter_pass(kda, head, dec_wl, n_sets, dev, stream):
             "source_digest": source_digest()}
 
 
+SEGMENT_SHAPES = ((1, 8, 4096), (1, 1, 16384), (1, 2, 32768), (1, 4, 16384), (2, 2, 8192))
+
+
+def segment_sweep(kda, dev, stream, steps=20):
+    """The segment scan against one sequential pass per (b, h), on few long
+    sequences (bf16, d = 128, the headline's distributions): kernel time per call."""
+    import torch
+    from kda_workloads import CONFIGS, make_inputs
+    rows = []
+    for (B, H, T) in SEGMENT_SHAPES:
+        wl = CONFIGS[1].scaled(B=B, H=H, T=T)
+        x = to_dev(make_inputs(wl), dev)
+        ws = torch.empty(kda.workspace_bytes(B, T, H, 128), dtype=torch.uint8, device=dev)
+        out = torch.empty((B, T, H, 128), dtype=torch.float32, device=dev)
+        r = {"B": B, "H": H, "T": T}
+        for seg in (True, False):
+            def fn(_):
+                kda.chunk_fwd(*(x[k] for k in KEYS), out=out, workspace=ws, segment_scan=seg)
+            _, ms = time_calls(fn, [None], steps, 3, stream)
+            r["segments_us" if seg else "single_pass_us"] = 1e3 * ms
+        log(f"segments B{B} H{H} T{T}: {r['segments_us']:.1f} us with, {r['single_pass_us']:.1f} us without")
+        rows.append(r)
+        del x, ws, out
+        torch.cuda.empty_cache()
+    return {"segment_sweep": rows, "source_digest": source_digest()}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -262,6 +289,8 @@ def main():
                     help="time budget of the oracle baseline (0 skips it)")
     ap.add_argument("--no-context", action="store_true",
                     help="skip the context timings of the two larger prefill shapes")
+    ap.add_argument("--segment-sweep", action="store_true",
+                    help="time the segment scan against one pass per sequence on few long sequences")
     ap.add_argument("--counter-pass", action="store_true",
                     help="short run for rocprofv3 --pmc: counter calibration copy, the "
                          "headline prefill once per input set, four decode steps")
@@ -288,6 +317,9 @@ def main():
     log(f"device {torch.cuda.get_device_name(dev)}; library {kda.library_path()}")
 
     head = CONFIGS[1]
+    if args.segment_sweep:
+        print(json.dumps(segment_sweep(kda, dev, stream)), flush=True)
+        return
     if args.counter_pass:
         print(json.dumps(counter_pass(kda, head, CONFIGS[4], args.sets, dev, stream)), flush=True)
         return

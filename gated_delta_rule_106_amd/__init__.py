@@ -96,19 +96,23 @@ def workspace_bytes(B, T, H, D, dtype=torch.bfloat16, chunk=0) -> int:
 
 def chunk_fwd(q, k, v, log_alpha, beta, gate, initial_state=None, output_final_state=False,
               chunk=0, clamp=True, out_dtype=torch.float32, out=None, final_state=None,
-              workspace=None):
+              workspace=None, segment_scan=True):
     """Chunkwise-parallel KDA forward on the current HIP stream.
 
     q, k, log_alpha: [B, T, H, Dk]; v, gate: [B, T, H, Dv]; beta: [B, T, H];
     all bf16 or all fp32, contiguous, on one GPU.  initial_state: fp32
     [B, H, Dk, Dv] or None.  Returns (y, final_state or None); y has
-    ``out_dtype`` (fp32 by default).
+    ``out_dtype`` (fp32 by default).  ``segment_scan=False`` keeps one sequential
+    pass per (b, h) where the library would otherwise cut few, long sequences
+    into segments (the same result up to rounding).
     """
     lib = _abi.load()
     dev = q.device
     if dev.type != "cuda":
         raise ValueError("chunk_fwd needs GPU tensors (the HIP kernels are the only implementation)")
     a = _fwd_args(q, k, v, log_alpha, beta, gate, chunk, clamp, out_dtype)
+    if not segment_scan:
+        a.flags |= _abi.KDA_FLAG_NO_SEGMENT_SCAN
     B, T, H, Dk, Dv = a.B, a.T, a.H, a.Dk, a.Dv
     if initial_state is not None and (initial_state.dtype != torch.float32 or
                                       tuple(initial_state.shape) != (B, H, Dk, Dv)):

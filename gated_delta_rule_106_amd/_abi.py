@@ -16,6 +16,7 @@ KDA_ERR_WORKSPACE = -4
 KDA_ERR_ALIGN = -5
 KDA_ERR_HIP = -6
 KDA_FLAG_NO_CLAMP = 1
+KDA_FLAG_NO_SEGMENT_SCAN = 2
 
 # every extern "C" entry point of include/kda.h
 EXPORTS = ("kda_chunk_fwd_workspace_size", "kda_chunk_fwd", "kda_decode_step",

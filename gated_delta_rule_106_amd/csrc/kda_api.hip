@@ -20,19 +20,22 @@ bool mul_ok(int64_t a, int64_t b, int64_t* out) {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// elements of one state tensor [B, H, Dk, Dv] (sizes already checked not to overflow)
+int64_t bh_elems(const kda_fwd_args* a) { return a->B * a->H * a->Dk * a->Dv; }
+
 int resolve_chunk(const kda_fwd_args* a) {
     if (a->chunk != 0) return a->chunk;
     return a->dtype == KDA_BF16 ? kDefaultChunkBf16 : kDefaultChunkF32;
 }
 
 // Sizes, dtype, head size, chunk and flags; fills the chunk count and card size.
-int check_shape(const kda_fwd_args* a, int* chunk, int64_t* nchunks, int64_t* card) {
+int check_shape(const kda_fwd_args* a, int* chunk, int64_t* nchunks, int64_t* card, int64_t* ws_total) {
     if (!a) return KDA_ERR_NULL;
     if (a->B < 0 || a->T < 0 || a->H < 0 || a->Dk <= 0 || a->Dv <= 0) return KDA_ERR_SHAPE;
     if (a->dtype != KDA_F32 && a->dtype != KDA_BF16) return KDA_ERR_UNSUPPORTED;
     if (a->Dk != a->Dv || (a->Dk != 64 && a->Dk != 128)) return KDA_ERR_UNSUPPORTED;
     if (a->out_dtype != KDA_F32 && a->out_dtype != KDA_BF16) return KDA_ERR_UNSUPPORTED;
-    if ((a->flags & ~KDA_FLAG_NO_CLAMP) != 0) return KDA_ERR_UNSUPPORTED;
+    if ((a->flags & ~(KDA_FLAG_NO_CLAMP | KDA_FLAG_NO_SEGMENT_SCAN)) != 0) return KDA_ERR_UNSUPPORTED;
     const int c = resolve_chunk(a);
     if (!kda::prefill_supported(a->dtype == KDA_BF16, c, (int)a->Dk)) return KDA_ERR_UNSUPPORTED;
     // every element index of every tensor must fit in int64
@@ -47,9 +50,13 @@ int check_shape(const kda_fwd_args* a, int* chunk, int64_t* nchunks, int64_t* ca
     int64_t tmp, total;
     if (cb <= 0 || !mul_ok(bh, nc, &tmp) || !mul_ok(tmp, cb, &total)) return KDA_ERR_SHAPE;
     if (tmp > INT_MAX) return KDA_ERR_SHAPE;  // one workgroup per (b, h, chunk)
+    // segment-scan summaries (chunk-64 bf16 path; small only when B*H is small)
+    const int64_t extra = (a->dtype == KDA_BF16 && c == 64) ? kda::prefill64_extra_bytes((int)a->Dk, bh, nc) : 0;
+    if (extra > INT64_MAX - total) return KDA_ERR_SHAPE;
     *chunk = c;
     *nchunks = nc;
     *card = cb;
+    *ws_total = total + extra;
     return KDA_OK;
 }
 
@@ -75,18 +82,18 @@ const char* kda_status_str(int status) {
 int kda_chunk_fwd_workspace_size(const kda_fwd_args* a, size_t* bytes) {
     if (!a || !bytes) return KDA_ERR_NULL;
     int c;
-    int64_t nc, cb;
-    const int st = check_shape(a, &c, &nc, &cb);
+    int64_t nc, cb, ws;
+    const int st = check_shape(a, &c, &nc, &cb, &ws);
     if (st != KDA_OK) return st;
-    *bytes = (size_t)(a->B * a->H * nc * cb);
+    *bytes = (size_t)ws;
     return KDA_OK;
 }
 
 int kda_chunk_fwd(const kda_fwd_args* a, hipStream_t stream) {
     if (!a) return KDA_ERR_NULL;
     int c;
-    int64_t nc, cb;
-    int st = check_shape(a, &c, &nc, &cb);
+    int64_t nc, cb, need;
+    int st = check_shape(a, &c, &nc, &cb, &need);
     if (st != KDA_OK) return st;
     const bool has_tokens = a->B * a->T * a->H > 0;
     if (has_tokens) {
@@ -97,7 +104,6 @@ int kda_chunk_fwd(const kda_fwd_args* a, hipStream_t stream) {
             if (!aligned16(p)) return KDA_ERR_ALIGN;
     }
     if (!aligned16(a->initial_state) || !aligned16(a->final_state)) return KDA_ERR_ALIGN;
-    const int64_t need = a->B * a->H * nc * cb;
     if (need > 0) {
         if (!a->workspace) return KDA_ERR_WORKSPACE;
         if ((int64_t)a->workspace_bytes < need) return KDA_ERR_WORKSPACE;
@@ -109,7 +115,20 @@ int kda_chunk_fwd(const kda_fwd_args* a, hipStream_t stream) {
     kda::PrepParams pp{a->q, a->k, a->v, a->log_alpha, a->beta, a->workspace,
                        a->B, a->T, a->H, nc, (a->flags & KDA_FLAG_NO_CLAMP) ? 0 : 1};
     kda::RecurParams rp{a->gate, a->out, a->initial_state, a->final_state, a->workspace,
-                        a->B, a->T, a->H, nc};
+                        a->B, a->T, a->H, nc, nc, 1, nullptr};
+    // the state pass of every segment reads initial_state at its start while the last
+    // segment writes final_state at its end: no segments when the two overlap
+    const bool states_overlap =
+        a->initial_state && a->final_state &&
+        a->final_state < a->initial_state + bh_elems(a) && a->initial_state < a->final_state + bh_elems(a);
+    if (a->dtype == KDA_BF16 && c == 64 && !(a->flags & KDA_FLAG_NO_SEGMENT_SCAN) && !states_overlap) {
+        const int P = kda::prefill64_segments((int)a->Dk, a->B * a->H, nc);
+        if (P > 1) {
+            rp.nseg = P;
+            rp.seg_len = (nc + P - 1) / P;
+            rp.sums = reinterpret_cast<float*>(static_cast<unsigned char*>(a->workspace) + a->B * a->H * nc * cb);
+        }
+    }
     const hipError_t e = kda::launch_prefill(a->dtype == KDA_BF16, a->out_dtype == KDA_BF16, c,
                                              (int)a->Dk, pp, rp, stream);
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;

@@ -618,11 +618,14 @@ void kda_rec64_kernel(RecurParams p) {
     // XCD-aware placement: the G workgroups of one head share bid % 8
     const int nblk = gridDim.x, bid = blockIdx.x;
     const int logical = (bid % 8) * (nblk / 8) + bid / 8;
-    const int64_t unit = logical / G;
+    const int64_t useg = logical / G;  // (b, h) * nseg + segment
     const int grp = logical % G;
-    const int64_t units = p.B * p.H;
-    if (unit >= units) return;  // padding workgroup (the whole group leaves together)
+    const int64_t units = p.B * p.H, nseg = p.nseg;
+    if (useg >= units * nseg) return;  // padding workgroup (the whole group leaves together)
+    const int64_t unit = useg / nseg, seg = useg % nseg;
     const int64_t H = p.H, T = p.T, NC = p.NC;
+    // this workgroup's chunks: [c0, c0 + NL) of its (b, h)
+    const int64_t c0 = seg * p.seg_len, NL = (c0 + p.seg_len < NC ? c0 + p.seg_len : NC) - c0;
     const int64_t b = unit / H, h = unit % H;
     const unsigned char* cards = static_cast<const unsigned char*>(p.ws) + unit * NC * CD::BYTES;
     const bool chain = wave < NCONS;
@@ -635,7 +638,7 @@ void kda_rec64_kernel(RecurParams p) {
     _Float16* sbx = reinterpret_cast<_Float16*>(smem + L::OFF_X + cs * L::SBX);
     const int64_t zrow0 = (b * T * H + h) * D, zstride = H * D;  // element offset of (b, t, h, 0)
     typename Out::raw_t* gy = static_cast<typename Out::raw_t*>(p.out);
-    auto slot = [&](int64_t c) { return smem + (c % L::NSTAGE) * L::STAGE; };
+    auto slot = [&](int64_t ci) { return smem + (ci % L::NSTAGE) * L::STAGE; };  // local chunk index
 
     // each role runs its own loop (so that no role carries another's registers); all of them
     // pass the same barriers: one before the first chunk, then A and B once per chunk
@@ -649,8 +652,37 @@ void kda_rec64_kernel(RecurParams p) {
         for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
             for (int i = 0; i < 4; ++i) S[ct][i] = s0 ? s0[(16 * ct + 4 * g4 + i) * D + col] : 0.f;
+        // segment scan: the state entering segment seg, S_{q+1} = M_q S_q + b_q for q < seg
+        // (page "Kimi K3 report walk-through", section "KDA Context Parallelism"),
+        // M_q S_q on the fp16 MFMA like every state product of the chain
+        for (int64_t q = 0; q < seg; ++q) {
+            const float* bq = p.sums + ((unit * (nseg - 1) + q) * 2) * (int64_t)D * D;
+            const float* Mq = bq + (int64_t)D * D;
+            half8 Sb[KB];
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) Sb[kb] = pack_h8(S[2 * kb], S[2 * kb + 1]);
+#pragma unroll
+            for (int mt = 0; mt < NCT; ++mt) {
+                floatx4 acc;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc[i] = bq[(16 * mt + 4 * g4 + i) * D + col];
+#pragma unroll
+                for (int kb = 0; kb < KB; ++kb) {
+                    const float* mrow = Mq + (16 * mt + m16) * D + 32 * kb + 4 * g4;  // channels cmap(kb, g4, j)
+                    const float4 lo = *reinterpret_cast<const float4*>(mrow);
+                    const float4 hi = *reinterpret_cast<const float4*>(mrow + 16);
+                    half8 a;
+                    a[0] = static_cast<_Float16>(lo.x); a[1] = static_cast<_Float16>(lo.y);
+                    a[2] = static_cast<_Float16>(lo.z); a[3] = static_cast<_Float16>(lo.w);
+                    a[4] = static_cast<_Float16>(hi.x); a[5] = static_cast<_Float16>(hi.y);
+                    a[6] = static_cast<_Float16>(hi.z); a[7] = static_cast<_Float16>(hi.w);
+                    acc = mma_f16_k32(a, Sb[kb], acc);
+                }
+                S[mt] = acc;  // S[mt] is not read again in this step: Sb holds the old state
+            }
+        }
         lds_barrier();  // the first card is resident
-        for (int64_t ci = 0; ci < NC; ++ci) {
+        for (int64_t ci = 0; ci < NL; ++ci) {
             const unsigned char* st = slot(ci);
             const _Float16* sw = reinterpret_cast<const _Float16*>(st + L::OFF_WS);
             const _Float16* sk = reinterpret_cast<const _Float16*>(st + L::OFF_KS);
@@ -707,7 +739,7 @@ void kda_rec64_kernel(RecurParams p) {
                 for (int ct = 0; ct < NCT; ++ct) S[ct] = mma_f16_k32(kf[ct][u], Ub[u], S[ct]);  // + Kbar^T U
             lds_barrier();  // B
         }
-        if (p.sT) {
+        if (p.sT && seg == nseg - 1) {
             float* sT = p.sT + unit * (int64_t)D * D;
 #pragma unroll
             for (int ct = 0; ct < NCT; ++ct)
@@ -719,7 +751,7 @@ void kda_rec64_kernel(RecurParams p) {
         // chunk's in flight while this one is used
         const int nt = grp * NCONS + cs;
         auto load_q = [&](half8 (&qf)[4][KB], half4 (&uo)[4], int64_t c) __attribute__((always_inline)) {
-            const unsigned char* card = cards + (c < NC ? c : NC - 1) * CD::BYTES;
+            const unsigned char* card = cards + (c0 + (c < NL ? c : NL - 1)) * CD::BYTES;
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt) {
 #pragma unroll
@@ -755,11 +787,11 @@ void kda_rec64_kernel(RecurParams p) {
         lds_barrier();  // the first card is resident
         // both steps in every trip (see the producers)
         int64_t ci = 0;
-        for (; ci + 1 < NC; ci += 2) {
+        for (; ci + 1 < NL; ci += 2) {
             step(qa, ua, qb, ub, ci);
             step(qb, ub, qa, ua, ci + 1);
         }
-        if (ci < NC) step(qa, ua, qb, ub, ci);
+        if (ci < NL) step(qa, ua, qb, ub, ci);
     } else {
         // Each producer is compiled for its index, so that the source of every piece it
         // copies is fixed at compile time (straight-line address arithmetic, no branches).
@@ -768,8 +800,9 @@ void kda_rec64_kernel(RecurParams p) {
             // piece j of a stage is copied by producer j % NP; every producer issues exactly
             // KP copies per chunk (one short of work repeats its last piece: same bytes to
             // the same place), so that its count of outstanding loads is fixed
-            auto piece = [&](int64_t c, int k) __attribute__((always_inline)) {
+            auto piece = [&](int64_t ci, int k) __attribute__((always_inline)) {
                 const int j0 = PW + k * NP, j = j0 < L::NPC ? j0 : L::NPC - 1;
+                const int64_t c = c0 + ci;  // chunk of the sequence
                 const unsigned char* card = cards + c * CD::BYTES;
                 const void* src;
                 if (j < L::NW) {
@@ -788,10 +821,10 @@ void kda_rec64_kernel(RecurParams p) {
                 } else {
                     src = card + CD::GAM + (lane % (D / 4)) * 16;  // Gamma, replicated
                 }
-                lds_copy16(src, lds_offset(slot(c) + (int64_t)j * 1024));
+                lds_copy16(src, lds_offset(slot(ci) + (int64_t)j * 1024));
             };
-            auto copy_chunk = [&](int64_t c) __attribute__((always_inline)) {
-                const int64_t cc = c < NC ? c : NC - 1;  // past the end: the last chunk again
+            auto copy_chunk = [&](int64_t ci) __attribute__((always_inline)) {
+                const int64_t cc = ci < NL ? ci : NL - 1;  // past the end: the last chunk again
 #pragma unroll
                 for (int k = 0; k < KP; ++k) piece(cc, k);
             };
@@ -810,8 +843,8 @@ void kda_rec64_kernel(RecurParams p) {
                     *reinterpret_cast<float4*>(sbuf + t2 * (64 * OST) + tq * OST + cq) = sg;
                 }
             };
-            auto output_part = [&](int64_t c) __attribute__((always_inline)) {
-                const int64_t t = c * C + tq;
+            auto output_part = [&](int64_t ci) __attribute__((always_inline)) {
+                const int64_t t = (c0 + ci) * C + tq;
 #pragma unroll
                 for (int t2 = 0; t2 < NCONS; ++t2) {
                     const int tile = t2 * (64 * OST) + tq * OST + cq;
@@ -843,14 +876,14 @@ void kda_rec64_kernel(RecurParams p) {
                 wait_vm<KP>();
                 lds_barrier();  // B: chunk ci + 1 is resident
             };
-            if (NC > 0) {
+            if (NL > 0) {
                 copy_chunk(0);
                 copy_chunk(1);
                 wait_vm<KP>();  // chunk 0
             }
             lds_barrier();  // the first card is resident
-            for (int64_t ci = 0; ci < NC; ++ci) step(ci);
-            if (NC > 0) output_part(NC - 1);
+            for (int64_t ci = 0; ci < NL; ++ci) step(ci);
+            if (NL > 0) output_part(NL - 1);
         };
         static_assert(NP == 4, "producer dispatch");
         switch (__builtin_amdgcn_readfirstlane(pw)) {
@@ -863,11 +896,183 @@ void kda_rec64_kernel(RecurParams p) {
 }
 
 // ---------------------------------------------------------------------------
+// kernel 3 (segment scan): the summary of one segment of chunks.  Page "Kimi K3
+// report walk-through", section "KDA Context Parallelism": a segment acts on the
+// state it receives as an affine map S -> M S + b, where b is the state the segment
+// ends in from a zero start and M = prod (I - beta k k^T) Diag(alpha) over its tokens.
+// Chunkwise, both follow the state recurrence of the cards: b with U = U~ - W S from
+// S = 0, and M (d_k columns) with U = -W M from M = I.  One workgroup per (b, h,
+// segment, NS of the 2 D/16 column tiles of [b | M]); per tile a chain wave, plus
+// two copier waves streaming W, Kbar^T, the U~ slices and Gamma into a three-slot LDS
+// ring (one barrier per chunk: the copies of chunk n+2 go into the slot of chunk n-1).
+template <int D, int NS>
+struct SumL {
+    using CD = Card<D>;
+    static constexpr int KB = D / 32, NCT = D / 16;
+    static constexpr int NPW = 2;                             // copier waves
+    static constexpr int NW = 4 * KB;                         // 1 KiB pieces of W; as many of Kbar^T
+    static constexpr int64_t OFF_WS = 0;
+    static constexpr int64_t OFF_KS = (int64_t)NW * 1024;
+    static constexpr int64_t OFF_US = 2 * OFF_KS;             // U~ slices of the b tiles, 2 KiB each
+    static constexpr int64_t OFF_GS = OFF_US + NS * 2048;
+    static constexpr int64_t STAGE = OFF_GS + 1024;
+    static constexpr int NSTAGE = 3;
+    static constexpr int NPC = (int)(STAGE / 1024);
+    static constexpr int KP = (NPC + NPW - 1) / NPW;
+    static constexpr int64_t TOTAL = NSTAGE * STAGE;
+    static constexpr int WAVES = NS + NPW;
+    static constexpr int GW = 2 * NCT / NS;                   // workgroups per (b, h, segment)
+    static_assert(NCT % NS == 0, "a workgroup's tiles are all b or all M");
+    static_assert(TOTAL <= 160 * 1024 && KP <= 63, "summary budget");
+};
+
+template <int D, int NS>
+__global__ __launch_bounds__((NS + 2) * 64) __attribute__((amdgpu_waves_per_eu(1, 2)))
+void kda_sum64_kernel(RecurParams p) {
+    using CD = Card<D>;
+    using L = SumL<D, NS>;
+    constexpr int NCT = D / 16, KB = D / 32, KP = L::KP;
+    constexpr int GW = L::GW;
+    extern __shared__ __align__(16) unsigned char smem[];
+
+    const int lane = lane_id(), wave = wave_id();
+    const int g4 = lane >> 4, m16 = lane & 15;
+    // the GW workgroups of one (b, h, segment) share bid % 8, so their card reads meet in one L2
+    const int nblk = gridDim.x, bid = blockIdx.x;
+    const int logical = (bid % 8) * (nblk / 8) + bid / 8;
+    const int64_t useg = logical / GW;  // (b, h) * (nseg - 1) + segment
+    const int grp = logical % GW;
+    const int64_t units = p.B * p.H, nsum = p.nseg - 1;
+    if (useg >= units * nsum) return;  // padding workgroup (the whole group leaves together)
+    const int64_t unit = useg / nsum, seg = useg % nsum;
+    const int64_t NC = p.NC, c0 = seg * p.seg_len;
+    const int64_t nloc = p.seg_len;  // every summarised segment is a full one
+    const unsigned char* cards = static_cast<const unsigned char*>(p.ws) + unit * NC * CD::BYTES;
+    const bool mtile = grp * NS >= NCT;  // this workgroup's tiles are columns of M (else of b)
+    auto slot = [&](int64_t ci) { return smem + (ci % L::NSTAGE) * L::STAGE; };
+
+    if (wave < NS) {
+        const int tt = grp * NS + wave;           // tile of [b | M]
+        const int col = 16 * (tt % NCT) + m16;    // column within b or M
+        floatx4 S[NCT];
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) S[ct][i] = (mtile && 16 * ct + 4 * g4 + i == col) ? 1.f : 0.f;
+        lds_barrier();  // the first card is resident
+        for (int64_t ci = 0; ci < nloc; ++ci) {
+            const unsigned char* st = slot(ci);
+            const _Float16* sw = reinterpret_cast<const _Float16*>(st + L::OFF_WS);
+            const _Float16* sk = reinterpret_cast<const _Float16*>(st + L::OFF_KS);
+            const _Float16* su = reinterpret_cast<const _Float16*>(st + L::OFF_US + wave * 2048);
+            const float* sg = reinterpret_cast<const float*>(st + L::OFF_GS);
+            half8 Sb[KB];
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) Sb[kb] = pack_h8(S[2 * kb], S[2 * kb + 1]);
+            floatx4 U[4];
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) U[mt] = mtile ? zero4() : unpack_h4(ld_h4(su + (mt * 64 + lane) * 4));
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct) {
+                const float4 gm = *reinterpret_cast<const float4*>(sg + 16 * ct + 4 * g4);
+                S[ct][0] *= gm.x;
+                S[ct][1] *= gm.y;
+                S[ct][2] *= gm.z;
+                S[ct][3] *= gm.w;
+            }
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                for (int mt = 0; mt < 4; ++mt)
+                    U[mt] = mma_f16_k32(ld_h8(sw + ((mt * KB + kb) * 64 + lane) * 8), Sb[kb], U[mt]);
+            half8 Ub[2];
+#pragma unroll
+            for (int u = 0; u < 2; ++u) Ub[u] = pack_h8(U[2 * u], U[2 * u + 1]);
+#pragma unroll
+            for (int u = 0; u < 2; ++u)
+#pragma unroll
+                for (int ct = 0; ct < NCT; ++ct)
+                    S[ct] = mma_f16_k32(cat_h8(ld_h4(sk + frag_piece(ct, u, 0) / 2 + lane * 4),
+                                               ld_h4(sk + frag_piece(ct, u, 1) / 2 + lane * 4)),
+                                        Ub[u], S[ct]);
+            lds_barrier();  // the slot of chunk ci is free; chunk ci + 1 is resident
+        }
+        float* dst = p.sums + (useg * 2 + (mtile ? 1 : 0)) * (int64_t)D * D;
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) dst[(16 * ct + 4 * g4 + i) * D + col] = S[ct][i];
+    } else {
+        auto copier = [&](auto pwc) __attribute__((always_inline)) {
+            constexpr int PW = decltype(pwc)::value;
+            auto piece = [&](int64_t ci, int k) __attribute__((always_inline)) {
+                const int j0 = PW + k * L::NPW, j = j0 < L::NPC ? j0 : L::NPC - 1;
+                const unsigned char* card = cards + (c0 + ci) * CD::BYTES;
+                const void* src;
+                if (j < L::NW) {
+                    src = card + CD::W + j * 1024 + lane * 16;
+                } else if (j < 2 * L::NW) {
+                    src = card + CD::KBT + (j - L::NW) * 1024 + lane * 16;
+                } else if (j < 2 * L::NW + 2 * NS) {
+                    // U~ slices (unused by M tiles, copied all the same: fixed counts)
+                    const int r = j - 2 * L::NW;
+                    src = card + CD::UT + ((grp * NS) % NCT + r / 2) * 2048 + (r % 2) * 1024 + lane * 16;
+                } else {
+                    src = card + CD::GAM + (lane % (D / 4)) * 16;  // Gamma, replicated
+                }
+                lds_copy16(src, lds_offset(slot(ci) + (int64_t)j * 1024));
+            };
+            auto copy_chunk = [&](int64_t ci) __attribute__((always_inline)) {
+                const int64_t cc = ci < nloc ? ci : nloc - 1;  // past the end: the last chunk again
+#pragma unroll
+                for (int k = 0; k < KP; ++k) piece(cc, k);
+            };
+            copy_chunk(0);
+            copy_chunk(1);
+            wait_vm<KP>();  // chunk 0
+            lds_barrier();  // the first card is resident
+            for (int64_t ci = 0; ci < nloc; ++ci) {
+                copy_chunk(ci + 2);  // the slot of chunk ci - 1, released by the previous barrier
+                wait_vm<KP>();       // chunk ci + 1, issued one iteration earlier
+                lds_barrier();
+            }
+        };
+        if (__builtin_amdgcn_readfirstlane(wave - NS) == 0)
+            copier(Int<0>{});
+        else
+            copier(Int<1>{});
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Segment scan: worth it only when the state pass alone leaves most of the GPU idle.
+// With P segments the sequential depth becomes about 2 NC / P chunks (summaries, then
+// the re-run), on P times the workgroups, plus a fixed cost (a third launch, the
+// ordered combination of the summaries, two pipeline fills) of roughly 30 us on
+// MI355X; measured, it pays off from segments of about 32 chunks.  The rule depends
+// on the shape only, so that the workspace size is known on the host without a
+// device query.
+constexpr int kSumTiles = 2;  // column tiles of [b | M] per summary workgroup
+constexpr int64_t kSlots = 256;  // workgroups one round may hold (one per CU)
+
+int segments(int D, int64_t units, int64_t nc) {
+    const int64_t g = D / 16;  // state-pass workgroups per (b, h) with one tile each
+    for (int P = 8; P >= 2; P /= 2) {
+        const int64_t len = (nc + P - 1) / P;
+        if (P * units * g <= kSlots && (P - 1) * units * (2 * g / kSumTiles) <= kSlots && len >= 32 &&
+            (P - 1) * len < nc && 2 * len + 4 < nc)
+            return P;
+    }
+    return 1;
+}
+
 template <int D, class Out, int NCONS>
-static hipError_t launch_d(const PrepParams& pp, const RecurParams& rp, hipStream_t stream) {
+static hipError_t launch_d(const PrepParams& pp, const RecurParams& rp0, hipStream_t stream) {
     using LP = PrepL<D>;
     using LR = RecL<D, NCONS>;
-    const int64_t units = rp.B * rp.H;
+    using LS = SumL<D, kSumTiles>;
+    const int64_t units = rp0.B * rp0.H;
+    RecurParams rp = rp0;
     if (pp.NC > 0) {
         auto kp = kda_prep64_kernel<D>;
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kp),
@@ -878,12 +1083,22 @@ static hipError_t launch_d(const PrepParams& pp, const RecurParams& rp, hipStrea
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
+    if (rp.nseg > 1) {
+        auto ks = kda_sum64_kernel<D, kSumTiles>;
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(ks),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)LS::TOTAL);
+        if (e != hipSuccess) return e;
+        const int64_t blocks = (units * (rp.nseg - 1) * LS::GW + 7) / 8 * 8;
+        hipLaunchKernelGGL(ks, dim3((unsigned)blocks), dim3(LS::WAVES * 64), LS::TOTAL, stream, rp);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
     auto kr = kda_rec64_kernel<D, Out, NCONS>;
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kr),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)LR::TOTAL);
     if (e != hipSuccess) return e;
     constexpr int G = D / (16 * NCONS);
-    const int64_t blocks = (units * G + 7) / 8 * 8;
+    const int64_t blocks = (units * rp.nseg * G + 7) / 8 * 8;
     hipLaunchKernelGGL(kr, dim3((unsigned)blocks), dim3(LR::WAVES * 64), LR::TOTAL, stream, rp);
     return hipGetLastError();
 }
@@ -894,8 +1109,21 @@ int64_t prefill64_card_bytes(int D) {
     return D == 128 ? c64::Card<128>::BYTES : D == 64 ? c64::Card<64>::BYTES : -1;
 }
 
-hipError_t launch_prefill64(int D, int out_bf16, const PrepParams& pp, const RecurParams& rp,
+int prefill64_segments(int D, int64_t units, int64_t nc) { return c64::segments(D, units, nc); }
+
+int64_t prefill64_extra_bytes(int D, int64_t units, int64_t nc) {
+    const int P = c64::segments(D, units, nc);
+    return P > 1 ? units * (P - 1) * 2 * (int64_t)D * D * 4 : 0;  // b_p and M_p, fp32
+}
+
+hipError_t launch_prefill64(int D, int out_bf16, const PrepParams& pp, const RecurParams& rp0,
                             hipStream_t stream) {
+    // the caller fills seg_len / nseg / sums only when it wants the segment scan
+    RecurParams rp = rp0;
+    if (rp.nseg < 1 || !rp.sums) {
+        rp.nseg = 1;
+        rp.seg_len = rp.NC;
+    }
     // one consumer per workgroup has the shortest chain per chunk; with enough (b, h)
     // sequences to fill the GPU, two consumers share each streamed card instead
     const bool wide = rp.B * rp.H >= 64;

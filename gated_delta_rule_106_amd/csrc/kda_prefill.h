@@ -24,6 +24,13 @@ struct RecurParams {
     float* sT;        // may be NULL; may alias s0
     const void* ws;
     int64_t B, T, H, NC;
+    // segment scan (chunk-64 bf16 path): the sequence is cut into nseg segments of
+    // seg_len chunks (the last one may be shorter); sums holds, per (b, h) and per
+    // segment p < nseg - 1, the zero-start end state b_p and the transition M_p
+    // (fp32 [D][D] each).  nseg = 1: one pass over the whole sequence.
+    int64_t seg_len;
+    int nseg;
+    float* sums;
 };
 
 // bytes of one per-chunk card in the workspace (or -1 if unsupported)
@@ -34,6 +41,10 @@ hipError_t launch_prefill(int bf16, int out_bf16, int C, int D, const PrepParams
 
 // bf16 inputs, 64-token chunks (kda_chunk64.hip)
 int64_t prefill64_card_bytes(int D);
+// segments the chunk-64 path cuts a sequence into (1 = none); a function of the shape only
+int prefill64_segments(int D, int64_t units, int64_t nc);
+// workspace bytes beyond the cards: the per-segment summaries
+int64_t prefill64_extra_bytes(int D, int64_t units, int64_t nc);
 hipError_t launch_prefill64(int D, int out_bf16, const PrepParams& pp, const RecurParams& rp,
                             hipStream_t stream);
 

@@ -72,6 +72,10 @@ extern "C" {
 
 /* flags */
 #define KDA_FLAG_NO_CLAMP 1u /* use log_alpha as given (no clamp to [ln 0.0067, 0]) */
+/* One sequential pass per (b, h) even where the segment scan would be used (see
+ * kda_chunk_fwd).  The result is the same up to rounding; the flag exists for
+ * comparisons. */
+#define KDA_FLAG_NO_SEGMENT_SCAN 2u
 
 /*
  * Arguments of kda_chunk_fwd.
@@ -84,6 +88,15 @@ extern "C" {
  *   workspace: device scratch of at least kda_chunk_fwd_workspace_size()
  *     bytes (may be NULL when that size is 0).  Its contents on entry do not
  *     matter and on return are unspecified.
+ *   Segment scan (bf16 inputs, chunk 64): when B*H is small against the GPU and
+ *   the sequence is long, each (b, h) sequence is cut into P segments (P is a
+ *   function of B*H, T and Dk only).  A first kernel summarises every segment but
+ *   the last as the affine map it applies to the incoming state (page "Kimi K3
+ *   report walk-through", section "KDA Context Parallelism": the state a zero
+ *   start ends in, and the product of the per-token transitions); the state pass
+ *   then runs all segments at once, each from the exact incoming state that the
+ *   ordered combination of the summaries gives.  The workspace then also holds
+ *   the summaries (2 * Dk * Dv * 4 bytes per (b, h) and summarised segment).
  *   T may be any value >= 0; a last partial chunk is handled exactly.  For
  *   T == 0 nothing is written to out and final_state receives initial_state
  *   (or zeros).

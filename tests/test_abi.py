@@ -94,6 +94,21 @@ def test_workspace_size_query(lib):
     assert lib.kda_chunk_fwd_workspace_size(None, None) == _abi.KDA_ERR_NULL
 
 
+def test_workspace_size_includes_segment_summaries(lib):
+    """A single long sequence takes the segment scan: the workspace adds, per summarised
+    segment, the zero-start end state and the transition (fp32 Dk x Dv each); shapes
+    with enough (b, h) sequences or short ones add nothing."""
+    card = 5 * 64 * 128 * 2 + 128 * 4
+    a = _good_fwd(B=1, T=8192, H=1, D=128)
+    assert _ws(lib, a)[1] == 128 * card + 3 * 2 * 128 * 128 * 4  # 4 segments of 32 chunks
+    a = _good_fwd(B=1, T=32768, H=2, D=128)
+    assert _ws(lib, a)[1] == 2 * 512 * card + 2 * 7 * 2 * 128 * 128 * 4  # 8 segments
+    a = _good_fwd(B=2, T=65536, H=32, D=128)
+    assert _ws(lib, a)[1] == 64 * 1024 * card
+    a = _good_fwd(B=1, T=4096, H=8, D=128)
+    assert _ws(lib, a)[1] == 8 * 64 * card
+
+
 @pytest.mark.parametrize("mutate,code", [
     (lambda a: setattr(a, "B", -1), _abi.KDA_ERR_SHAPE),
     (lambda a: setattr(a, "T", -5), _abi.KDA_ERR_SHAPE),
@@ -103,7 +118,8 @@ def test_workspace_size_query(lib):
     (lambda a: setattr(a, "dtype", 7), _abi.KDA_ERR_UNSUPPORTED),
     (lambda a: setattr(a, "chunk", 48), _abi.KDA_ERR_UNSUPPORTED),
     (lambda a: setattr(a, "chunk", 128), _abi.KDA_ERR_UNSUPPORTED),
-    (lambda a: setattr(a, "flags", 2), _abi.KDA_ERR_UNSUPPORTED),
+    (lambda a: setattr(a, "flags", 4), _abi.KDA_ERR_UNSUPPORTED),
+    (lambda a: setattr(a, "flags", 3), _abi.KDA_ERR_WORKSPACE),  # both known flags: accepted
     (lambda a: setattr(a, "out_dtype", 2), _abi.KDA_ERR_UNSUPPORTED),
     (lambda a: setattr(a, "T", 2 ** 62), _abi.KDA_ERR_SHAPE),
     (lambda a: setattr(a, "q", None), _abi.KDA_ERR_NULL),

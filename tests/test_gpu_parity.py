@@ -192,6 +192,31 @@ def test_split_and_chain_matches_whole():
     assert rel_err(y_all, yo) <= 2e-2
 
 
+@pytest.mark.parametrize("B,H,T,D", [(1, 1, 8192, 128), (1, 2, 9000, 128), (1, 2, 8300, 64)])
+def test_segment_scan_matches_oracle_and_single_pass(B, H, T, D):
+    """Few, long sequences take the segment scan (summaries, ordered combination,
+    re-run): with an initial state and a ragged last segment it matches the oracle and
+    the single sequential pass."""
+    wl = CONFIGS[2].scaled(B=B, H=H, T=T, Dk=D, Dv=D)
+    x = make_inputs(wl)
+    d = dev(x)
+    nc = (T + 63) // 64
+    cards = B * H * nc * {128: 82432, 64: 41216}[D]
+    assert kda().workspace_bytes(B, T, H, D) > cards, "shape expected to take the segment scan"
+    say(f"[parity] segment scan B={B} H={H} T={T} D={D}")
+    args = [d[k] for k in KEYS]
+    y_s, s_s = kda().chunk_fwd(*args, initial_state=d["initial_state"], output_final_state=True)
+    y_1, s_1 = kda().chunk_fwd(*args, initial_state=d["initial_state"], output_final_state=True,
+                               segment_scan=False)
+    torch.cuda.synchronize()
+    yo, so = run_oracle(x)
+    ey, es = rel_err(y_s, yo), rel_err(s_s, so)
+    ey1, es1 = rel_err(y_1, yo), rel_err(s_1, so)
+    say(f"[parity] segment scan: y err/rms={ey:.3e} state {es:.3e}; single pass y {ey1:.3e} state {es1:.3e}")
+    assert ey <= 2e-2 and es <= 2e-2 and ey1 <= 2e-2 and es1 <= 2e-2
+    assert rel_err(y_s, y_1.double().cpu().numpy()) <= 2e-2
+
+
 def test_decode_chain_equals_prefill_and_handoff():
     """T decode steps equal one prefill; a prefill's final state continues in decode."""
     wl = CONFIGS[2].scaled(B=2, H=4, T=24, Dk=64, Dv=64)
