@@ -192,16 +192,18 @@ struct PrepL {
 // index of the 16x16 block (r, c), c <= r, among the blocks on and below the diagonal
 __device__ __forceinline__ constexpr int bidx(int r, int c) { return r * (r + 1) / 2 + c; }
 
-// B operand of a K = 32 step that picks the 16 channels 16 cl .. 16 cl + 15 of the
-// step: with a tile in A-operand layout (lane = token), D = A Sel holds the same
-// 16x16 block with lane = channel and the four registers = tokens 4g .. 4g + 3.
-// Products with 1.0 and sums with zeros keep fp16 values exact.
+// Operand of a K = 32 step over the channels 32 kb .. 32 kb + 31 (lane group g
+// supplies 8 g .. 8 g + 7) that picks the 16 channels 32 kb + 16 cl + n: as the B
+// operand, D = A Sel holds a tile in A-operand layout (lane = token) transposed, with
+// lane = channel and the four registers = tokens 4g .. 4g + 3; as the A operand,
+// D = Sel B turns a B-operand tile (lane = token) into the accumulator layout (lane =
+// token, registers = channels 16 (2 kb + cl) + 4g .. +3).  Products with 1.0 and sums
+// with zeros keep fp16 values exact.
 __device__ __forceinline__ half8 sel_operand(int cl, int lane) {
     const int g = lane >> 4, n = lane & 15;
     half8 r;
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
-        r[j] = static_cast<_Float16>(((j >> 2) == cl && (n >> 2) == g && (j & 3) == (n & 3)) ? 1.f : 0.f);
+    for (int j = 0; j < 8; ++j) r[j] = static_cast<_Float16>((g == 2 * cl + (n >> 3) && j == (n & 7)) ? 1.f : 0.f);
     return r;
 }
 
@@ -234,8 +236,9 @@ __device__ __forceinline__ void prep_tile(const PrepParams& p, unsigned char* sm
     const int64_t NC = p.NC, T = p.T, H = p.H;
     const bool clamp = p.clamp != 0;
 
-    // raw inputs of token rl: per 16-channel tile ct, the 4 bf16 channels 16ct + 4g4 .. +3
-    u32x2 rq[NCT], rk[NCT], rv[NCT], rla[NCT];
+    // raw inputs of token rl: per 32-channel block kb, the 8 bf16 channels 32 kb + 8 g4 .. +7
+    // (16 bytes; the four lane groups of a token cover 64 contiguous bytes of its row)
+    u32x4 rq[KB], rk[KB], rv[KB], rla[KB];
     uint32_t rbeta;
     auto fetch = [&](int64_t it) __attribute__((always_inline)) {
         const int64_t n = it % NC, unit = it / NC;
@@ -247,22 +250,22 @@ __device__ __forceinline__ void prep_tile(const PrepParams& p, unsigned char* sm
         const uint16_t* gv = static_cast<const uint16_t*>(p.v);
         const uint16_t* gla = static_cast<const uint16_t*>(p.la);
 #pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) {
-            const int64_t off = row * D + 16 * ct + 4 * g4;
-            rla[ct] = *reinterpret_cast<const u32x2*>(gla + off);
-            rk[ct] = *reinterpret_cast<const u32x2*>(gk + off);
+        for (int kb = 0; kb < KB; ++kb) {
+            const int64_t off = row * D + 32 * kb + 8 * g4;
+            rla[kb] = *reinterpret_cast<const u32x4*>(gla + off);
+            rk[kb] = *reinterpret_cast<const u32x4*>(gk + off);
         }
 #pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) {
-            const int64_t off = row * D + 16 * ct + 4 * g4;
-            rq[ct] = *reinterpret_cast<const u32x2*>(gq + off);
-            rv[ct] = *reinterpret_cast<const u32x2*>(gv + off);
+        for (int kb = 0; kb < KB; ++kb) {
+            const int64_t off = row * D + 32 * kb + 8 * g4;
+            rq[kb] = *reinterpret_cast<const u32x4*>(gq + off);
+            rv[kb] = *reinterpret_cast<const u32x4*>(gv + off);
         }
         rbeta = static_cast<const uint16_t*>(p.beta)[row];
     };
-    auto elem = [](const u32x2 w, int i) -> float {
-        const uint32_t x = w[i >> 1];
-        return (i & 1) ? __uint_as_float(x & 0xffff0000u) : __uint_as_float(x << 16);
+    auto elem = [](const u32x4 w, int j) -> float {  // bf16 element j of 8
+        const uint32_t x = w[j >> 1];
+        return (j & 1) ? __uint_as_float(x & 0xffff0000u) : __uint_as_float(x << 16);
     };
     const half8 sel0 = sel_operand(0, lane), sel1 = sel_operand(1, lane);
     // a 16 x 32 tile in operand layout -> two transposed 16 x 16 pieces of a fragment
@@ -288,22 +291,21 @@ __device__ __forceinline__ void prep_tile(const PrepParams& p, unsigned char* sm
         half8 v16;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            const int ct = 2 * kb + (j >> 2), i = j & 3;
-            const float l = valid ? clamp_log_alpha(elem(rla[ct], i), clamp) * kLog2e : 0.f;
+            const float l = valid ? clamp_log_alpha(elem(rla[kb], j), clamp) * kLog2e : 0.f;
             const float P = row_scan16(l);      // log2 decay from the tile start, inclusive
             const float E = fast_exp2(P);       // <= 1
             const float Einv = fast_exp2(-P);   // >= 1, < 2^116 under the floor
             const float Et = row_last(E);       // decay over the whole tile
-            const float kf = valid ? elem(rk[ct], i) : 0.f, qf = valid ? elem(rq[ct], i) : 0.f;
+            const float kf = valid ? elem(rk[kb], j) : 0.f, qf = valid ? elem(rq[kb], j) : 0.f;
             const float KR = kf * E, QR = qf * E, KC = kf * Einv;
-            // K-step (kb, j): lane group g4 supplies channel cmap(kb, g4, j) to both operands
+            // K-step (kb, j): lane group g4 supplies channel 32 kb + 8 g4 + j to both operands
             accA = mma_f32_k4(KR, KC, accA);
             accP = mma_f32_k4(QR, KC, accP);
             kr16[kb][j] = static_cast<_Float16>(KR);
             qr16[kb][j] = static_cast<_Float16>(QR);
             ke16[kb][j] = static_cast<_Float16>(kf * (Einv * Et));  // decay from after this token to the tile end
-            v16[j] = static_cast<_Float16>(valid ? elem(rv[ct], i) : 0.f);
-            s_etau[A * D + cmap(kb, g4, j)] = Et;  // the 16 lanes of a row store the same value
+            v16[j] = static_cast<_Float16>(valid ? elem(rv[kb], j) : 0.f);
+            s_etau[A * D + 32 * kb + 8 * g4 + j] = Et;  // the 16 lanes of a row store the same value
         }
         // KE fragment of this tile: the B operand of the pairs (later tile, this tile)
         *reinterpret_cast<half8*>(s_ke + ((A * KB + kb) * 64 + lane) * 8) = ke16[kb];
@@ -322,7 +324,7 @@ __device__ __forceinline__ void prep_tile(const PrepParams& p, unsigned char* sm
 
     // ---- phase 2: chunk-relative operands and the pairs with earlier tiles.  Decay
     //      factors across tiles are products of the per-tile decays 2^{tau}.
-    half8 q16[KB];  // Q~ of this tile: the initial value of its Qe rows
+    half8 q16[KB];  // Q~ of this tile (B-operand layout): the initial value of its Qe rows
     floatx4 pa[NSUB - 1], pp[NSUB - 1];
 #pragma unroll
     for (int bb = 0; bb < NSUB - 1; ++bb) pa[bb] = pp[bb] = zero4();
@@ -332,8 +334,8 @@ __device__ __forceinline__ void prep_tile(const PrepParams& p, unsigned char* sm
 #pragma unroll
         for (int a2 = 0; a2 < NSUB; ++a2) {
             if (a2 == A) continue;
-            const float4 lo = *reinterpret_cast<const float4*>(s_etau + a2 * D + 32 * kb + 4 * g4);
-            const float4 hi = *reinterpret_cast<const float4*>(s_etau + a2 * D + 32 * kb + 16 + 4 * g4);
+            const float4 lo = *reinterpret_cast<const float4*>(s_etau + a2 * D + 32 * kb + 8 * g4);
+            const float4 hi = *reinterpret_cast<const float4*>(s_etau + a2 * D + 32 * kb + 8 * g4 + 4);
             et[a2][0] = lo.x; et[a2][1] = lo.y; et[a2][2] = lo.z; et[a2][3] = lo.w;
             et[a2][4] = hi.x; et[a2][5] = hi.y; et[a2][6] = hi.z; et[a2][7] = hi.w;
         }
@@ -506,10 +508,11 @@ __device__ __forceinline__ void prep_tile(const PrepParams& p, unsigned char* sm
         *reinterpret_cast<half4*>(card + CD::UT + ((x * 4 + A) * 64 + lane) * 8) = pack_h4(ut);
         *reinterpret_cast<half4*>(card + CD::UO + ((x * 4 + A) * 64 + lane) * 8) = pack_h4(uo);
         const int kb = x >> 1, cl = x & 1;
+        const floatx4 q0 = mma_f16_k32(cl ? sel1 : sel0, q16[kb], zero4());  // Q~^T rows of this tile
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             wt[cl][i] = -w[i];
-            qe[cl][i] = static_cast<float>(q16[kb][4 * cl + i]) - qm[i];
+            qe[cl][i] = q0[i] - qm[i];
         }
         if (cl == 1) {
             *reinterpret_cast<half8*>(card + CD::W + ((A * KB + kb) * 64 + lane) * 16) = pack_h8(wt[0], wt[1]);
