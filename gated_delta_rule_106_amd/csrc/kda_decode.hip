@@ -12,7 +12,9 @@
 // The state is read once and written once: the step is HBM-bound (about
 // 0.86 flop per byte), so it runs on the vector ALUs with coalesced 16-byte
 // accesses, one workgroup per (b, h) and the 64 KiB state held in registers
-// between the read and the write.
+// between the read and the write.  The state moves with non-temporal loads and
+// stores: it is touched once per step, and keeping it out of the caches lets the
+// read-modify-write stream closer to the HBM rate.
 #include "kda_device.h"
 #include "kda_decode.h"
 
@@ -50,7 +52,10 @@ __global__ __launch_bounds__(256) void kda_decode_kernel(DecodeParams p) {
     float4* st = reinterpret_cast<float4*>(p.state + unit * (int64_t)DK * DV);
     float4 s[RPT];
 #pragma unroll
-    for (int i = 0; i < RPT; ++i) s[i] = st[(rg * RPT + i) * COLS + cg];
+    for (int i = 0; i < RPT; ++i) {
+        const floatx4 v = __builtin_nontemporal_load(reinterpret_cast<const floatx4*>(st) + (rg * RPT + i) * COLS + cg);
+        s[i] = make_float4(v[0], v[1], v[2], v[3]);
+    }
     __syncthreads();
 
     // q . k on wave 0
@@ -94,7 +99,8 @@ __global__ __launch_bounds__(256) void kda_decode_kernel(DecodeParams p) {
     for (int i = 0; i < RPT; ++i) {
         const float kr = s_k[rg * RPT + i];
         s[i].x += kr * u4.x; s[i].y += kr * u4.y; s[i].z += kr * u4.z; s[i].w += kr * u4.w;
-        st[(rg * RPT + i) * COLS + cg] = s[i];
+        const floatx4 v = {s[i].x, s[i].y, s[i].z, s[i].w};
+        __builtin_nontemporal_store(v, reinterpret_cast<floatx4*>(st) + (rg * RPT + i) * COLS + cg);
     }
 }
 
