@@ -537,16 +537,16 @@ void kda_prep64_kernel(PrepParams p) {
 // kernel 2: sequential pass over the cards
 //
 // Per workgroup, for each of its NCONS 16-column value tiles, a chain wave and an
-// output wave, plus NP producer waves.  Iteration n, around the barriers A and B:
-//   chain     before A: S_n (fp16 copy) -> LDS; after A: U = U~ - W S_n,
+// output wave, plus NP producer waves, pipelined around one barrier X(n) per chunk:
+//   chain     iteration n: S_n (fp16 copy) -> LDS buffer n % 2, U = U~ - W S_n,
 //             S_{n+1} = Diag(Gamma) S_n + Kbar^T U (fp32 state in accumulators)
-//   output    before A: load Qe and Uo of chunk n+1 into its other register set;
-//             after A: O = Uo + Qe S_n -> LDS tile
-//   producers before A: start the direct-to-LDS copies of chunk n+2 (W, Kbar^T, the
-//             U~ slices, Gamma) into ring slot (n+2) % 3, load the gate logits of
-//             chunk n+1, compute sigmoid(z) of chunk n and store y = O sigmoid(z) of
-//             chunk n-1 (a quarter of the tokens each, 16-byte stores);
-//             after A: wait for the copies of chunk n+1 (issued one iteration earlier).
+//   output    iteration n + 1: O_n = Uo + Qe S_n from that copy -> LDS buffer n % 2
+//             (Qe and Uo loaded into registers one chunk ahead)
+//   producers iteration n: y_{n-2} = O_{n-2} sigmoid(z_{n-2}) (a quarter of the
+//             tokens each, 16-byte stores), direct-to-LDS copies of chunk n+2 (W,
+//             Kbar^T, the U~ slices, the gate logits, Gamma) into ring slot
+//             (n+2) % 3, the gate logits of chunk n into registers; before X(n) they
+//             wait for the copies of chunk n+1 (issued one iteration earlier).
 // A chunk's copy is in flight for about two iterations; the LDS ring holds three.
 template <int D, int NCONS>
 struct RecL {
@@ -566,10 +566,9 @@ struct RecL {
     static constexpr int OST = 20;                            // [token][16 columns] fp32 row stride
     static constexpr int64_t OTILE = 64 * OST * 4;            // one tile's 64 x 16 fp32 tile
     static constexpr int64_t SBX = (int64_t)KB * 64 * 16;     // fp16 copy of one tile's state (B operand)
-    static constexpr int64_t OFF_O = NSTAGE * STAGE;          // read-out O [NCONS]
-    static constexpr int64_t OFF_S = OFF_O + NCONS * OTILE;   // sigmoid(z) [NCONS]
-    static constexpr int64_t OFF_X = OFF_S + NCONS * OTILE;   // state copies [NCONS]
-    static constexpr int64_t TOTAL = OFF_X + NCONS * SBX;
+    static constexpr int64_t OFF_O = NSTAGE * STAGE;          // read-out O [2][NCONS]
+    static constexpr int64_t OFF_X = OFF_O + 2 * NCONS * OTILE;  // state copies [2][NCONS]
+    static constexpr int64_t TOTAL = OFF_X + 2 * NCONS * SBX;
     static constexpr int WAVES = 2 * NCONS + NP;
     static_assert(STAGE % 1024 == 0 && D * 4 <= 1024, "card pieces");
     static_assert(TOTAL <= 160 * 1024, "recurrence LDS budget");
@@ -636,9 +635,9 @@ void kda_rec64_kernel(RecurParams p) {
     const int pw = wave - 2 * NCONS;                          // producer index (producers only)
     const int cs = chain ? wave : (outw ? wave - NCONS : 0);  // value tile of a chain / output wave
     const uint16_t* gz = static_cast<const uint16_t*>(p.gate);
-    float* obuf = reinterpret_cast<float*>(smem + L::OFF_O);
-    float* sbuf = reinterpret_cast<float*>(smem + L::OFF_S);
-    _Float16* sbx = reinterpret_cast<_Float16*>(smem + L::OFF_X + cs * L::SBX);
+    // O read-out and fp16 state copy of tile t2 for chunk n: buffer n % 2
+    auto obuf = [&](int64_t n, int t2) { return reinterpret_cast<float*>(smem + L::OFF_O + ((n & 1) * NCONS + t2) * L::OTILE); };
+    auto sbx = [&](int64_t n) { return reinterpret_cast<_Float16*>(smem + L::OFF_X + ((n & 1) * NCONS + cs) * L::SBX); };
     const int64_t zrow0 = (b * T * H + h) * D, zstride = H * D;  // element offset of (b, t, h, 0)
     typename Out::raw_t* gy = static_cast<typename Out::raw_t*>(p.out);
     auto slot = [&](int64_t ci) { return smem + (ci % L::NSTAGE) * L::STAGE; };  // local chunk index
@@ -694,10 +693,11 @@ void kda_rec64_kernel(RecurParams p) {
             // the state at the chunk start, as the B operand (logical k = 8g4 + j of step kb is
             // channel cmap(kb, g4, j)), for this wave and for the output wave
             half8 Sb[KB];
+            _Float16* sx = sbx(ci);
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb) {
                 Sb[kb] = pack_h8(S[2 * kb], S[2 * kb + 1]);
-                *reinterpret_cast<half8*>(sbx + (kb * 64 + lane) * 8) = Sb[kb];
+                *reinterpret_cast<half8*>(sx + (kb * 64 + lane) * 8) = Sb[kb];
             }
             half8 wf[4][KB];
             half4 ut[4];
@@ -710,7 +710,6 @@ void kda_rec64_kernel(RecurParams p) {
             }
 #pragma unroll
             for (int ct = 0; ct < NCT; ++ct) gm[ct] = *reinterpret_cast<const float4*>(sg + 16 * ct + 4 * g4);
-            lds_barrier();  // A: the state copy is visible to the output wave
             half8 kf[NCT][2];  // read while the U chain runs
 #pragma unroll
             for (int ct = 0; ct < NCT; ++ct) {
@@ -740,8 +739,9 @@ void kda_rec64_kernel(RecurParams p) {
             for (int u = 0; u < 2; ++u)
 #pragma unroll
                 for (int ct = 0; ct < NCT; ++ct) S[ct] = mma_f16_k32(kf[ct][u], Ub[u], S[ct]);  // + Kbar^T U
-            lds_barrier();  // B
+            lds_barrier();  // X(ci): the state copy is visible to the output wave
         }
+        lds_barrier();  // X(NL): the output wave forms its last read-out
         if (p.sT && seg == nseg - 1) {
             float* sT = p.sT + unit * (int64_t)D * D;
 #pragma unroll
@@ -763,13 +763,15 @@ void kda_rec64_kernel(RecurParams p) {
                 uo[mt] = *reinterpret_cast<const half4*>(card + CD::UO + ((nt * 4 + mt) * 64 + lane) * 8);
             }
         };
-        auto step = [&](half8 (&qf)[4][KB], half4 (&uo)[4], half8 (&qn)[4][KB], half4 (&un)[4], int64_t ci)
+        // iteration n (1 .. NL): the read-out of chunk n - 1 from the state copy the chain
+        // wave left before X(n - 1); the next chunk's Qe and Uo load meanwhile
+        auto step = [&](half8 (&qf)[4][KB], half4 (&uo)[4], half8 (&qn)[4][KB], half4 (&un)[4], int64_t n)
                         __attribute__((always_inline)) {
-            load_q(qn, un, ci + 1);
-            lds_barrier();  // A
+            load_q(qn, un, n);
+            const _Float16* sx = sbx(n - 1);
             half8 Sb[KB];
 #pragma unroll
-            for (int kb = 0; kb < KB; ++kb) Sb[kb] = ld_h8(sbx + (kb * 64 + lane) * 8);
+            for (int kb = 0; kb < KB; ++kb) Sb[kb] = ld_h8(sx + (kb * 64 + lane) * 8);
             floatx4 O[4];
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt) O[mt] = unpack_h4(uo[mt]);  // Uo
@@ -777,24 +779,25 @@ void kda_rec64_kernel(RecurParams p) {
             for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
                 for (int mt = 0; mt < 4; ++mt) O[mt] = mma_f16_k32(qf[mt][kb], Sb[kb], O[mt]);  // + Qe S
-            float* orow = obuf + cs * (64 * OST);
+            float* orow = obuf(n - 1, cs);
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) orow[(16 * mt + 4 * g4 + i) * OST + m16] = O[mt][i];
-            lds_barrier();  // B
+            lds_barrier();  // X(n)
         };
         half8 qa[4][KB], qb[4][KB];
         half4 ua[4], ub[4];
         load_q(qa, ua, 0);
         lds_barrier();  // the first card is resident
+        lds_barrier();  // X(0): the first state copy
         // both steps in every trip (see the producers)
-        int64_t ci = 0;
-        for (; ci + 1 < NL; ci += 2) {
-            step(qa, ua, qb, ub, ci);
-            step(qb, ub, qa, ua, ci + 1);
+        int64_t n = 1;
+        for (; n + 1 <= NL; n += 2) {
+            step(qa, ua, qb, ub, n);
+            step(qb, ub, qa, ua, n + 1);
         }
-        if (ci < NL) step(qa, ua, qb, ub, ci);
+        if (n <= NL) step(qa, ua, qb, ub, n);
     } else {
         // Each producer is compiled for its index, so that the source of every piece it
         // copies is fixed at compile time (straight-line address arithmetic, no branches).
@@ -827,33 +830,28 @@ void kda_rec64_kernel(RecurParams p) {
                 lds_copy16(src, lds_offset(slot(ci) + (int64_t)j * 1024));
             };
             auto copy_chunk = [&](int64_t ci) __attribute__((always_inline)) {
+                if (NL == 0) return;                       // no tokens: nothing to stream
                 const int64_t cc = ci < NL ? ci : NL - 1;  // past the end: the last chunk again
 #pragma unroll
                 for (int k = 0; k < KP; ++k) piece(cc, k);
             };
             // gate and output: 16 tokens x 4 columns per lane group, per tile
             const int tq = 16 * PW + (lane >> 2), cq = 4 * (lane & 3);
-            auto sigmoid_part = [&](int64_t c) __attribute__((always_inline)) {
-                const unsigned char* st = slot(c);
+            auto load_z = [&](uint2 (&z)[NCONS], int64_t n) __attribute__((always_inline)) {
+                const unsigned char* st = slot(n);
 #pragma unroll
-                for (int t2 = 0; t2 < NCONS; ++t2) {
-                    const uint2 z = *reinterpret_cast<const uint2*>(st + L::OFF_ZS + t2 * 2048 + tq * 32 + cq * 2);
-                    float4 sg;
-                    sg.x = sigmoidf_(__uint_as_float(z.x << 16));
-                    sg.y = sigmoidf_(__uint_as_float(z.x & 0xffff0000u));
-                    sg.z = sigmoidf_(__uint_as_float(z.y << 16));
-                    sg.w = sigmoidf_(__uint_as_float(z.y & 0xffff0000u));
-                    *reinterpret_cast<float4*>(sbuf + t2 * (64 * OST) + tq * OST + cq) = sg;
-                }
+                for (int t2 = 0; t2 < NCONS; ++t2)
+                    z[t2] = *reinterpret_cast<const uint2*>(st + L::OFF_ZS + t2 * 2048 + tq * 32 + cq * 2);
             };
-            auto output_part = [&](int64_t ci) __attribute__((always_inline)) {
-                const int64_t t = (c0 + ci) * C + tq;
+            auto output_part = [&](const uint2 (&z)[NCONS], int64_t n) __attribute__((always_inline)) {
+                const int64_t t = (c0 + n) * C + tq;
 #pragma unroll
                 for (int t2 = 0; t2 < NCONS; ++t2) {
-                    const int tile = t2 * (64 * OST) + tq * OST + cq;
-                    const float4 o = *reinterpret_cast<const float4*>(obuf + tile);
-                    const float4 sg = *reinterpret_cast<const float4*>(sbuf + tile);
-                    const float y0 = o.x * sg.x, y1 = o.y * sg.y, y2 = o.z * sg.z, y3 = o.w * sg.w;
+                    const float4 o = *reinterpret_cast<const float4*>(obuf(n, t2) + tq * OST + cq);
+                    const float y0 = o.x * sigmoidf_(__uint_as_float(z[t2].x << 16));
+                    const float y1 = o.y * sigmoidf_(__uint_as_float(z[t2].x & 0xffff0000u));
+                    const float y2 = o.z * sigmoidf_(__uint_as_float(z[t2].y << 16));
+                    const float y3 = o.w * sigmoidf_(__uint_as_float(z[t2].y & 0xffff0000u));
                     if (t < T) {
                         typename Out::raw_t* dst = gy + zrow0 + t * zstride + 16 * (grp * NCONS + t2) + cq;
                         if constexpr (sizeof(typename Out::raw_t) == 4) {
@@ -866,27 +864,28 @@ void kda_rec64_kernel(RecurParams p) {
                     }
                 }
             };
-            // Iteration ci (vmcnt is in order): y of chunk ci-1 (at most NCONS stores; O from
-            // the output wave, sigmoid(z) written by this wave one iteration earlier), sigmoid(z)
-            // of chunk ci, then the KP copies of chunk ci+2 into the slot of chunk ci-1.  After
-            // barrier A, vmcnt(KP) leaves only this iteration's copies in flight: chunk ci+1's,
-            // issued one iteration earlier, have landed before barrier B publishes them.
-            auto step = [&](int64_t ci) __attribute__((always_inline)) {
-                if (ci >= 1) output_part(ci - 1);
-                sigmoid_part(ci);
-                copy_chunk(ci + 2);  // slot of chunk ci - 1, released by barrier B
-                lds_barrier();  // A
+            // Iteration n (vmcnt is in order): y of chunk n-2 (at most NCONS stores; O from the
+            // output wave before X(n-1), z held in registers since iteration n-2), then the KP
+            // copies of chunk n+2 into the slot of chunk n-1 (released by X(n-1)), then the gate
+            // logits of chunk n.  vmcnt(KP) before X(n) leaves only this iteration's copies in
+            // flight: chunk n+1's, issued one iteration earlier, have landed.
+            uint2 z1[NCONS], z2[NCONS];  // gate logits of chunks n-1 and n-2
+            auto step = [&](int64_t n) __attribute__((always_inline)) {
+                if (n >= 2) output_part(z2, n - 2);
+                copy_chunk(n + 2);
+#pragma unroll
+                for (int t2 = 0; t2 < NCONS; ++t2) z2[t2] = z1[t2];
+                if (n < NL) load_z(z1, n);
                 wait_vm<KP>();
-                lds_barrier();  // B: chunk ci + 1 is resident
+                lds_barrier();  // X(n)
             };
-            if (NL > 0) {
-                copy_chunk(0);
-                copy_chunk(1);
-                wait_vm<KP>();  // chunk 0
-            }
+            copy_chunk(0);
+            copy_chunk(1);
+            wait_vm<KP>();  // chunk 0
             lds_barrier();  // the first card is resident
-            for (int64_t ci = 0; ci < NL; ++ci) step(ci);
-            if (NL > 0) output_part(NL - 1);
+            for (int64_t n = 0; n <= NL; ++n) step(n);
+            if (NL > 0) output_part(z1, NL - 1);
+            wait_vm_zero();  // the last (redundant) copies land before the workgroup's LDS is released
         };
         static_assert(NP == 4, "producer dispatch");
         switch (__builtin_amdgcn_readfirstlane(pw)) {
