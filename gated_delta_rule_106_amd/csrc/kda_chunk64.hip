@@ -279,6 +279,10 @@ __device__ __forceinline__ void prep_tile(const PrepParams& p, unsigned char* sm
     const int64_t item = blockIdx.x;
     fetch(item);
     const bool valid = (item % NC) * C + rl < T;  // tokens past the end are identity tokens
+    if (!valid) {  // all of their inputs count as zero (log alpha 0: no decay)
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) rla[kb] = rk[kb] = rq[kb] = rv[kb] = u32x4{0u, 0u, 0u, 0u};
+    }
     unsigned char* card = static_cast<unsigned char*>(p.ws) + item * CD::BYTES;
     const float beta_mine = valid ? bf16_bits_to_float(static_cast<uint16_t>(rbeta)) : 0.f;
 
@@ -291,12 +295,13 @@ __device__ __forceinline__ void prep_tile(const PrepParams& p, unsigned char* sm
         half8 v16;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            const float l = valid ? clamp_log_alpha(elem(rla[kb], j), clamp) * kLog2e : 0.f;
+            const float la = elem(rla[kb], j);
+            const float l = (clamp ? __builtin_amdgcn_fmed3f(la, kLogAlphaMin, 0.f) : la) * kLog2e;
             const float P = row_scan16(l);      // log2 decay from the tile start, inclusive
             const float E = fast_exp2(P);       // <= 1
             const float Einv = fast_exp2(-P);   // >= 1, < 2^116 under the floor
             const float Et = row_last(E);       // decay over the whole tile
-            const float kf = valid ? elem(rk[kb], j) : 0.f, qf = valid ? elem(rq[kb], j) : 0.f;
+            const float kf = elem(rk[kb], j), qf = elem(rq[kb], j);
             const float KR = kf * E, QR = qf * E, KC = kf * Einv;
             // K-step (kb, j): lane group g4 supplies channel 32 kb + 8 g4 + j to both operands
             accA = mma_f32_k4(KR, KC, accA);
@@ -304,7 +309,7 @@ __device__ __forceinline__ void prep_tile(const PrepParams& p, unsigned char* sm
             kr16[kb][j] = static_cast<_Float16>(KR);
             qr16[kb][j] = static_cast<_Float16>(QR);
             ke16[kb][j] = static_cast<_Float16>(kf * (Einv * Et));  // decay from after this token to the tile end
-            v16[j] = static_cast<_Float16>(valid ? elem(rv[kb], j) : 0.f);
+            v16[j] = static_cast<_Float16>(elem(rv[kb], j));
             s_etau[A * D + 32 * kb + 8 * g4 + j] = Et;  // the 16 lanes of a row store the same value
         }
         // KE fragment of this tile: the B operand of the pairs (later tile, this tile)
