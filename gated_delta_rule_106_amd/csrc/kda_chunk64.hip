@@ -249,19 +249,17 @@ __device__ __forceinline__ void prep_tile(const PrepParams& p, unsigned char* sm
         const uint16_t* gk = static_cast<const uint16_t*>(p.k);
         const uint16_t* gv = static_cast<const uint16_t*>(p.v);
         const uint16_t* gla = static_cast<const uint16_t*>(p.la);
+        rbeta = static_cast<const uint16_t*>(p.beta)[row];
+        // in the order the decay phase consumes them, so that it starts on the first channel
+        // block while the later ones are still arriving
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
             const int64_t off = row * D + 32 * kb + 8 * g4;
             rla[kb] = *reinterpret_cast<const u32x4*>(gla + off);
             rk[kb] = *reinterpret_cast<const u32x4*>(gk + off);
-        }
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-            const int64_t off = row * D + 32 * kb + 8 * g4;
             rq[kb] = *reinterpret_cast<const u32x4*>(gq + off);
             rv[kb] = *reinterpret_cast<const u32x4*>(gv + off);
         }
-        rbeta = static_cast<const uint16_t*>(p.beta)[row];
     };
     auto elem = [](const u32x4 w, int j) -> float {  // bf16 element j of 8
         const uint32_t x = w[j >> 1];
