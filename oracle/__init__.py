@@ -9,7 +9,11 @@ The arithmetic lives in ``kda_oracle.c``: the plain token-by-token recurrence
 of Kimi Delta Attention in double precision (page "3T models are no longer
 magic", section "Gate 1: KDA makes it computable": forget per channel, delta
 rule corrective write, read the new state with the query, sigmoid output
-gate).  This module only builds that file with gcc and marshals arguments.
+gate), and the segment summary of a run of tokens (same page, section "KDA
+context parallelism").  This module builds that file with gcc and marshals
+arguments; the one computation done here is ``combine``, the ordered
+composition of segment summaries, written as a plain fp64 matrix product per
+segment.
 
 Every input is passed as the exact bit pattern the GPU receives (float32 or
 bfloat16) and is widened exactly inside the C code; nothing here rounds,
@@ -56,6 +60,8 @@ def _open(path):
     lib.kda_oracle_decode.argtypes = [i64, i64, i64, i64, ci, vp, vp, vp, vp, vp, vp,
                                       dp, dp, ci, ci]
     lib.kda_oracle_decode.restype = ci
+    lib.kda_oracle_summary.argtypes = [i64, i64, i64, i64, i64, ci, vp, vp, vp, vp, dp, dp, ci, ci]
+    lib.kda_oracle_summary.restype = ci
     lib.kda_oracle_default_threads.argtypes = []
     lib.kda_oracle_default_threads.restype = ci
     return lib
@@ -87,6 +93,9 @@ def compile_variant(src_text: str, out_path: str):
 
         def decode(self, *a, **kw):
             return decode(*a, _lib_handle=lib, **kw)
+
+        def summary(self, *a, **kw):
+            return summary(*a, _lib_handle=lib, **kw)
     return _Handle()
 
 
@@ -198,3 +207,53 @@ def decode(q, k, v, log_alpha, beta, gate, state, clamp=True, threads=0, _lib_ha
     if rc != 0:
         raise RuntimeError(f"kda_oracle_decode failed with code {rc}")
     return y, s
+
+
+def summary(k, v, log_alpha, beta, clamp=True, threads=0, _lib_handle=None):
+    """Segment summary of every (b, h) run over [B, T, H] (page "3T models are no
+    longer magic", section "KDA context parallelism"): the run maps an incoming
+    state S to ``M @ S + b``, with ``M`` the product of the per-token transitions
+    (I - beta k k^T) Diag(alpha), latest on the left, and ``b`` the state reached
+    from zero.  Returns ``(M, b)`` as float64 arrays [B, H, Dk, Dk], [B, H, Dk, Dv].
+    """
+    ka, dt = _raw(k)
+    va, dt_v = _raw(v)
+    la, dt_l = _raw(log_alpha)
+    ba, dt_b = _raw(beta)
+    if len({dt, dt_v, dt_l, dt_b}) != 1:
+        raise TypeError("all oracle inputs must share one dtype")
+    B, T, H, Dk = ka.shape
+    Dv = va.shape[-1]
+    if la.shape != (B, T, H, Dk) or va.shape != (B, T, H, Dv) or ba.shape != (B, T, H):
+        raise ValueError("k, log_alpha must be [B, T, H, Dk], v [B, T, H, Dv], beta [B, T, H]")
+    M = np.zeros((B, H, Dk, Dk), dtype=np.float64)
+    b = np.zeros((B, H, Dk, Dv), dtype=np.float64)
+    lib = _lib_handle if _lib_handle is not None else _load()
+    rc = lib.kda_oracle_summary(B, T, H, Dk, Dv, dt, _ptr(ka), _ptr(va), _ptr(la), _ptr(ba),
+                                _ptr(M), _ptr(b), 1 if clamp else 0, int(threads))
+    if rc != 0:
+        raise RuntimeError(f"kda_oracle_summary failed with code {rc}")
+    return M, b
+
+
+def combine(M, b, initial_state=None):
+    """Ordered composition of P consecutive segment summaries (page "Kimi K3
+    report walk-through", section "KDA Context Parallelism": the state handed to
+    segment p + 1 is what segment p makes of the state it received).
+
+    ``M`` is [P, B, H, Dk, Dk] and ``b`` [P, B, H, Dk, Dv]; the state entering
+    segment 0 is ``initial_state`` (zeros when None).  Returns
+    ``(segment_states, final_state)``: the state entering each segment,
+    [P, B, H, Dk, Dv], and the state after the last one, [B, H, Dk, Dv], all
+    float64.  S_{p+1} = M_p S_p + b_p, one matrix product per segment.
+    """
+    M = np.asarray(M, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    P, B, H, Dk, _ = M.shape
+    Dv = b.shape[-1]
+    S = np.zeros((B, H, Dk, Dv)) if initial_state is None else _state64(initial_state, (B, H, Dk, Dv)).copy()
+    seg = np.zeros((P, B, H, Dk, Dv))
+    for p in range(P):
+        seg[p] = S
+        S = np.matmul(M[p], S) + b[p]
+    return seg, S

@@ -185,3 +185,79 @@ int kda_oracle_decode(int64_t B, int64_t H, int64_t Dk, int64_t Dv, int dtype,
     return kda_oracle_fwd(B, 1, H, Dk, Dv, dtype, q, k, v, log_alpha, beta, gate,
                           state, out, state, clamp, nthreads);
 }
+
+/*
+ * Segment summary.  Page "3T models are no longer magic", section "KDA context
+ * parallelism", and page "Kimi K3 report walk-through", section "KDA Context
+ * Parallelism": a run of tokens is summarised by how it transforms the state it
+ * receives and by the state it produces from a zero start.  Because every token
+ * maps S to A_t S + beta_t k_t v_t^T with A_t = (I - beta_t k_t k_t^T) Diag(alpha_t),
+ * a whole run maps S_0 to M S_0 + b:
+ *   M = A_T ... A_1                (d_k x d_k, latest token on the left),
+ *   b = the state the run reaches from S_0 = 0 (d_k x d_v).
+ * Both are built here token by token in double precision: M by applying each
+ * A_t to the identity, b by the plain recurrence (the same steps as the forward
+ * above, without the query read and the gate).
+ * k, log_alpha: [B, T, H, Dk]; v: [B, T, H, Dv]; beta: [B, T, H];
+ * M: [B, H, Dk, Dk]; b: [B, H, Dk, Dv].  Returns 0, -1 on bad sizes, -2 on
+ * allocation failure.
+ */
+
+/* X <- (I - bt k k^T) Diag(a) X (+ bt k v^T when v is given); X has n columns. */
+static void orc_transition(double *X, int64_t Dk, int64_t n, const double *kv,
+                           const double *a, double bt, const double *vv, double *r) {
+    for (int64_t c = 0; c < Dk; ++c)
+        for (int64_t j = 0; j < n; ++j) X[c * n + j] *= a[c];
+    for (int64_t j = 0; j < n; ++j) r[j] = 0.0;
+    for (int64_t c = 0; c < Dk; ++c)
+        for (int64_t j = 0; j < n; ++j) r[j] += X[c * n + j] * kv[c];
+    for (int64_t j = 0; j < n; ++j) r[j] = (vv ? bt * vv[j] : 0.0) - bt * r[j];
+    for (int64_t c = 0; c < Dk; ++c)
+        for (int64_t j = 0; j < n; ++j) X[c * n + j] += kv[c] * r[j];
+}
+
+int kda_oracle_summary(int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv,
+                       int dtype, const void *k, const void *v,
+                       const void *log_alpha, const void *beta, double *M,
+                       double *bstate, int clamp, int nthreads) {
+    if (B < 0 || T < 0 || H < 0 || Dk <= 0 || Dv <= 0 || !M || !bstate) return -1;
+    if (dtype != ORC_F32 && dtype != ORC_BF16) return -1;
+    const int64_t units = B * H;
+    int failed = 0;
+#ifdef _OPENMP
+    if (nthreads <= 0) nthreads = omp_get_max_threads();
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads)
+#endif
+    for (int64_t unit = 0; unit < units; ++unit) {
+        const int64_t b = unit / H, h = unit % H;
+        const int64_t nmax = Dk > Dv ? Dk : Dv;
+        double *scratch = (double *)malloc(sizeof(double) * (size_t)(2 * Dk + Dv + nmax));
+        if (!scratch) {
+#ifdef _OPENMP
+#pragma omp atomic write
+#endif
+            failed = 1;
+            continue;
+        }
+        double *kk = scratch, *a = kk + Dk, *vv = a + Dk, *r = vv + Dv;
+        double *Mu = M + unit * Dk * Dk, *bu = bstate + unit * Dk * Dv;
+        for (int64_t i = 0; i < Dk; ++i)
+            for (int64_t j = 0; j < Dk; ++j) Mu[i * Dk + j] = (i == j) ? 1.0 : 0.0;
+        memset(bu, 0, sizeof(double) * (size_t)(Dk * Dv));
+        for (int64_t t = 0; t < T; ++t) {
+            const int64_t tok = (b * T + t) * H + h;
+            const double bt = orc_load(beta, dtype, tok);
+            for (int64_t c = 0; c < Dk; ++c) {
+                kk[c] = orc_load(k, dtype, tok * Dk + c);
+                const double l = orc_load(log_alpha, dtype, tok * Dk + c);
+                /* retention floor and retention <= 1, as in the forward */
+                a[c] = exp(clamp ? fmin(fmax(l, ORC_LOG_ALPHA_MIN), 0.0) : l);
+            }
+            for (int64_t j = 0; j < Dv; ++j) vv[j] = orc_load(v, dtype, tok * Dv + j);
+            orc_transition(Mu, Dk, Dk, kk, a, bt, NULL, r);
+            orc_transition(bu, Dk, Dv, kk, a, bt, vv, r);
+        }
+        free(scratch);
+    }
+    return failed ? -2 : 0;
+}

@@ -47,3 +47,33 @@ def brute_fwd(q, k, v, log_alpha, beta, gate, s0=None, clamp=True):
             if T == 0:
                 sT[b, h] = S0
     return y, sT
+
+
+def brute_summary(k, v, log_alpha, beta, clamp=True):
+    """Segment summary by explicit matrices: M = A_T ... A_1 as a product of the
+    d_k x d_k transition matrices, and b = sum_s (A_T ... A_{s+1}) beta_s k_s v_s^T
+    (the closed form of the state reached from zero), products recomputed per s."""
+    k, v = (np.asarray(a, dtype=np.float64) for a in (k, v))
+    la, beta = (np.asarray(a, dtype=np.float64) for a in (log_alpha, beta))
+    B, T, H, Dk = k.shape
+    Dv = v.shape[-1]
+    if clamp:
+        la = np.clip(la, LOG_ALPHA_MIN, 0.0)
+    eye = np.eye(Dk)
+    M = np.zeros((B, H, Dk, Dk))
+    bs = np.zeros((B, H, Dk, Dv))
+    for b in range(B):
+        for h in range(H):
+            A = [(eye - beta[b, t, h] * np.outer(k[b, t, h], k[b, t, h])) @ np.diag(np.exp(la[b, t, h]))
+                 for t in range(T)]
+
+            def prod(lo):  # A_{T-1} ... A_lo, 0-based (empty product = I)
+                P = eye.copy()
+                for j in range(lo, T):
+                    P = A[j] @ P
+                return P
+
+            M[b, h] = prod(0)
+            for s in range(T):
+                bs[b, h] += prod(s + 1) @ (beta[b, s, h] * np.outer(k[b, s, h], v[b, s, h]))
+    return M, bs

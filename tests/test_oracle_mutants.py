@@ -3,13 +3,14 @@ the pins catch every one of them, while the real oracle passes.
 
 Each mutant is a textual edit of ``oracle/kda_oracle.c`` compiled to a
 temporary library; the pins are the brute-force expansion (tests/_brute.py),
-the clamp semantics and the decode/prefill agreement.
+the clamp semantics, the decode/prefill agreement and the explicit-matrix
+segment summary.
 """
 import numpy as np
 import pytest
 
 import oracle
-from tests._brute import brute_fwd
+from tests._brute import brute_fwd, brute_summary
 
 MUTANTS = {
     "decay dropped": ("row[j] *= a;", "row[j] *= 1.0;"),
@@ -28,6 +29,12 @@ MUTANTS = {
     "retention floor missing": ("if (l < ORC_LOG_ALPHA_MIN) l = ORC_LOG_ALPHA_MIN;", ""),
     "key of the previous token": ("kv[c] = orc_load(k, dtype, tok * Dk + c);",
                                   "kv[c] = orc_load(k, dtype, (t > 0 ? tok - H : tok) * Dk + c);"),
+    # segment summary (transition product and zero-start state)
+    "summary decay dropped": ("X[c * n + j] *= a[c];", "X[c * n + j] *= 1.0;"),
+    "summary correction sign flipped": ("- bt * r[j];", "+ bt * r[j];"),
+    "summary transposed write": ("X[c * n + j] += kv[c] * r[j];", "X[c * n + j] += kv[j % Dk] * r[c % n];"),
+    "summary starts from zero instead of the identity": ("(i == j) ? 1.0 : 0.0", "0.0"),
+    "summary value dropped": ("(vv ? bt * vv[j] : 0.0)", "0.0"),
 }
 
 
@@ -46,6 +53,11 @@ def _pins_pass(handle) -> bool:
     if not (np.abs(y - yb).max() <= 1e-12 * np.abs(yb).max()
             and np.abs(sT - sb).max() <= 1e-12 * np.abs(sb).max()):
         return False
+    M, bs = handle.summary(k, v, la, beta)
+    Mb, bb = brute_summary(k, v, la, beta)
+    if not (np.abs(M - Mb).max() <= 1e-12 * np.abs(Mb).max()
+            and np.abs(bs - bb).max() <= 1e-12 * np.abs(bb).max()):
+        return False
     y1, s1 = handle.decode(*(np.ascontiguousarray(a[:, 0]) for a in (q, k, v, la, beta, gate)), s0)
     yb1, sb1 = brute_fwd(*(a[:, :1] for a in (q, k, v, la, beta, gate)), s0=s0)
     return bool(np.abs(y1 - yb1[:, 0]).max() <= 1e-12 * np.abs(yb1).max()
@@ -56,6 +68,7 @@ def test_real_oracle_passes_the_pins(oracle_lib):
     class _Real:
         fwd = staticmethod(oracle.fwd)
         decode = staticmethod(oracle.decode)
+        summary = staticmethod(oracle.summary)
     assert _pins_pass(_Real())
 
 
