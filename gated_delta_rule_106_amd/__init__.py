@@ -9,6 +9,8 @@ library is missing or a tensor is not on a GPU, the call raises.
     y, final_state = chunk_fwd(q, k, v, log_alpha, beta, gate,
                                initial_state=None, output_final_state=False, chunk=0)
     y = decode_step(q, k, v, log_alpha, beta, gate, state)   # state updated in place
+    M, b = chunk_summary(k, v, log_alpha, beta)                # segment summary
+    seg_states, final = combine_states(M_stack, b_stack, initial_state)
 
 Outputs are fp32 by default (``out_dtype``); bf16 outputs are available but
 their rounding alone exceeds a 2e-2 max-error-to-RMS budget on typical data.
@@ -21,7 +23,8 @@ import torch
 
 from . import _abi
 
-__all__ = ["chunk_fwd", "decode_step", "workspace_bytes", "library_path", "KDAError"]
+__all__ = ["chunk_fwd", "chunk_summary", "combine_states", "decode_step", "workspace_bytes",
+           "library_path", "KDAError"]
 
 
 class KDAError(RuntimeError):
@@ -141,6 +144,89 @@ def chunk_fwd(q, k, v, log_alpha, beta, gate, initial_state=None, output_final_s
     if rc != _abi.KDA_OK:
         raise KDAError(rc, "kda_chunk_fwd")
     return out, (final_state if output_final_state else None)
+
+
+def chunk_summary(k, v, log_alpha, beta, clamp=True, transition=None, offset=None, workspace=None):
+    """Segment summary of every (b, h) sequence on the current HIP stream.
+
+    The T tokens map an incoming state S to ``M @ S + b`` (``M`` the product of the
+    per-token transitions, ``b`` the state reached from zero).  k, log_alpha:
+    bf16 [B, T, H, Dk]; v: bf16 [B, T, H, Dv]; beta: bf16 [B, T, H].  Returns
+    ``(M, b)``: fp32 [B, H, Dk, Dk] and [B, H, Dk, Dv].
+    """
+    lib = _abi.load()
+    dev = k.device
+    if dev.type != "cuda":
+        raise ValueError("chunk_summary needs GPU tensors (the HIP kernels are the only implementation)")
+    B, T, H, Dk = k.shape
+    Dv = v.shape[-1]
+    if log_alpha.shape != k.shape or v.shape != (B, T, H, Dv) or beta.shape != (B, T, H):
+        raise ValueError("k, log_alpha must be [B, T, H, Dk], v [B, T, H, Dv] and beta [B, T, H]")
+    code = _dtype_code(k)
+    for t in (v, log_alpha, beta):
+        if t.dtype != k.dtype:
+            raise TypeError("k, v, log_alpha and beta must share one dtype")
+    a = _abi.FwdArgs()
+    a.B, a.T, a.H, a.Dk, a.Dv, a.dtype = B, T, H, Dk, Dv, code
+    a.flags = 0 if clamp else _abi.KDA_FLAG_NO_CLAMP
+    if transition is None:
+        transition = torch.empty((B, H, Dk, Dk), dtype=torch.float32, device=dev)
+    if offset is None:
+        offset = torch.empty((B, H, Dk, Dv), dtype=torch.float32, device=dev)
+    if transition.dtype != torch.float32 or tuple(transition.shape) != (B, H, Dk, Dk):
+        raise ValueError("transition must be fp32 [B, H, Dk, Dk]")
+    if offset.dtype != torch.float32 or tuple(offset.shape) != (B, H, Dk, Dv):
+        raise ValueError("offset must be fp32 [B, H, Dk, Dv]")
+    n = ctypes.c_size_t(0)
+    rc = lib.kda_chunk_fwd_workspace_size(ctypes.byref(a), ctypes.byref(n))
+    if rc != _abi.KDA_OK:
+        raise KDAError(rc, "kda_chunk_fwd_workspace_size")
+    if workspace is None or workspace.numel() < n.value:
+        workspace = torch.empty(max(int(n.value), 16), dtype=torch.uint8, device=dev)
+    _check_dev(dict(k=k, v=v, log_alpha=log_alpha, beta=beta, transition=transition, offset=offset), dev)
+    a.k, a.v, a.log_alpha, a.beta = _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta)
+    a.final_state = _ptr(offset)
+    a.workspace, a.workspace_bytes = _ptr(workspace), workspace.numel()
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    rc = lib.kda_chunk_summary(ctypes.byref(a), _ptr(transition), ctypes.c_void_p(stream))
+    if rc != _abi.KDA_OK:
+        raise KDAError(rc, "kda_chunk_summary")
+    return transition, offset
+
+
+def combine_states(transition, offset, initial_state=None, segment_states=True, final_state=None):
+    """Ordered combination of P segment summaries on the current HIP stream:
+    S_{p+1} = M_p S_p + b_p from S_0 = ``initial_state`` (zeros when None).
+
+    transition: fp32 [P, B, H, Dk, Dk]; offset: fp32 [P, B, H, Dk, Dv].  Returns
+    ``(segment_states or None, final_state)``: the state entering each segment,
+    [P, B, H, Dk, Dv], and the state after the last, [B, H, Dk, Dv].
+    """
+    lib = _abi.load()
+    dev = transition.device
+    if dev.type != "cuda":
+        raise ValueError("combine_states needs GPU tensors (the HIP kernels are the only implementation)")
+    P, B, H, Dk, _ = transition.shape
+    Dv = offset.shape[-1]
+    for name, t, shape in (("transition", transition, (P, B, H, Dk, Dk)), ("offset", offset, (P, B, H, Dk, Dv)),
+                           ("initial_state", initial_state, (B, H, Dk, Dv)),
+                           ("final_state", final_state, (B, H, Dk, Dv))):
+        if t is not None and (t.dtype != torch.float32 or tuple(t.shape) != shape):
+            raise ValueError(f"{name} must be fp32 {list(shape)}")
+    seg = torch.empty((P, B, H, Dk, Dv), dtype=torch.float32, device=dev) if segment_states else None
+    if final_state is None:
+        final_state = torch.empty((B, H, Dk, Dv), dtype=torch.float32, device=dev)
+    _check_dev(dict(transition=transition, offset=offset, initial_state=initial_state,
+                    segment_states=seg, final_state=final_state), dev)
+    a = _abi.CombineArgs()
+    a.P, a.B, a.H, a.Dk, a.Dv = P, B, H, Dk, Dv
+    a.transition, a.offset = _ptr(transition), _ptr(offset)
+    a.initial_state, a.segment_states, a.final_state = _ptr(initial_state), _ptr(seg), _ptr(final_state)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    rc = lib.kda_combine_states(ctypes.byref(a), ctypes.c_void_p(stream))
+    if rc != _abi.KDA_OK:
+        raise KDAError(rc, "kda_combine_states")
+    return seg, final_state
 
 
 def decode_step(q, k, v, log_alpha, beta, gate, state, clamp=True, out_dtype=torch.float32,

@@ -19,8 +19,8 @@ KDA_FLAG_NO_CLAMP = 1
 KDA_FLAG_NO_SEGMENT_SCAN = 2
 
 # every extern "C" entry point of include/kda.h
-EXPORTS = ("kda_chunk_fwd_workspace_size", "kda_chunk_fwd", "kda_decode_step",
-           "kda_status_str", "kda_version")
+EXPORTS = ("kda_chunk_fwd_workspace_size", "kda_chunk_fwd", "kda_chunk_summary",
+           "kda_combine_states", "kda_decode_step", "kda_status_str", "kda_version")
 
 
 class FwdArgs(ctypes.Structure):
@@ -34,6 +34,16 @@ class FwdArgs(ctypes.Structure):
         ("out", ctypes.c_void_p), ("initial_state", ctypes.c_void_p),
         ("final_state", ctypes.c_void_p), ("workspace", ctypes.c_void_p),
         ("workspace_bytes", ctypes.c_size_t),
+    ]
+
+
+class CombineArgs(ctypes.Structure):
+    _fields_ = [
+        ("P", ctypes.c_int64), ("B", ctypes.c_int64), ("H", ctypes.c_int64),
+        ("Dk", ctypes.c_int64), ("Dv", ctypes.c_int64),
+        ("transition", ctypes.c_void_p), ("offset", ctypes.c_void_p),
+        ("initial_state", ctypes.c_void_p), ("segment_states", ctypes.c_void_p),
+        ("final_state", ctypes.c_void_p),
     ]
 
 
@@ -64,6 +74,10 @@ def load(path: str = LIB_PATH):
     lib.kda_chunk_fwd_workspace_size.restype = ctypes.c_int
     lib.kda_chunk_fwd.argtypes = [ctypes.POINTER(FwdArgs), ctypes.c_void_p]
     lib.kda_chunk_fwd.restype = ctypes.c_int
+    lib.kda_chunk_summary.argtypes = [ctypes.POINTER(FwdArgs), ctypes.c_void_p, ctypes.c_void_p]
+    lib.kda_chunk_summary.restype = ctypes.c_int
+    lib.kda_combine_states.argtypes = [ctypes.POINTER(CombineArgs), ctypes.c_void_p]
+    lib.kda_combine_states.restype = ctypes.c_int
     lib.kda_decode_step.argtypes = [ctypes.POINTER(DecodeArgs), ctypes.c_void_p]
     lib.kda_decode_step.restype = ctypes.c_int
     lib.kda_status_str.argtypes = [ctypes.c_int]

@@ -5,6 +5,7 @@
 #include "../../include/kda.h"
 #include "kda_decode.h"
 #include "kda_prefill.h"
+#include "kda_segment.h"
 
 namespace {
 
@@ -131,6 +132,60 @@ int kda_chunk_fwd(const kda_fwd_args* a, hipStream_t stream) {
     }
     const hipError_t e = kda::launch_prefill(a->dtype == KDA_BF16, a->out_dtype == KDA_BF16, c,
                                              (int)a->Dk, pp, rp, stream);
+    return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+int kda_chunk_summary(const kda_fwd_args* a, float* transition, hipStream_t stream) {
+    if (!a) return KDA_ERR_NULL;
+    int c;
+    int64_t nc, cb, need;
+    int st = check_shape(a, &c, &nc, &cb, &need);
+    if (st != KDA_OK) return st;
+    if (a->dtype != KDA_BF16 || c != 64) return KDA_ERR_UNSUPPORTED;
+    if (a->flags & ~KDA_FLAG_NO_CLAMP) return KDA_ERR_UNSUPPORTED;
+    const int64_t units = a->B * a->H;
+    if (units == 0) return KDA_OK;
+    if (units * (a->Dk / 16) > INT_MAX) return KDA_ERR_SHAPE;  // combine-style grids
+    if (!transition || !a->final_state) return KDA_ERR_NULL;
+    if (!aligned16(transition) || !aligned16(a->final_state)) return KDA_ERR_ALIGN;
+    const int D = (int)a->Dk;
+    if (a->T == 0) {
+        const hipError_t e = kda::launch_identity_summary(D, transition, a->final_state, units, stream);
+        return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+    }
+    const void* req[] = {a->k, a->v, a->log_alpha, a->beta};
+    for (const void* p : req)
+        if (!p) return KDA_ERR_NULL;
+    for (const void* p : req)
+        if (!aligned16(p)) return KDA_ERR_ALIGN;
+    const int64_t cards = units * nc * cb;  // only the cards: no segment-scan summaries here
+    if (!a->workspace || (int64_t)a->workspace_bytes < cards) return KDA_ERR_WORKSPACE;
+    if (!aligned16(a->workspace)) return KDA_ERR_ALIGN;
+    // the card builder also forms the query-side blocks of each card, which the summary
+    // never reads: k stands in for q
+    kda::PrepParams pp{a->k, a->k, a->v, a->log_alpha, a->beta, a->workspace,
+                       a->B, a->T, a->H, nc, (a->flags & KDA_FLAG_NO_CLAMP) ? 0 : 1};
+    const hipError_t e = kda::launch_summary64(D, pp, transition, a->final_state, stream);
+    return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+int kda_combine_states(const kda_combine_args* a, hipStream_t stream) {
+    if (!a) return KDA_ERR_NULL;
+    if (a->P < 0 || a->B < 0 || a->H < 0 || a->Dk <= 0 || a->Dv <= 0) return KDA_ERR_SHAPE;
+    if (a->Dk != a->Dv || (a->Dk != 64 && a->Dk != 128)) return KDA_ERR_UNSUPPORTED;
+    int64_t bh, st, pst;
+    if (!mul_ok(a->B, a->H, &bh) || !mul_ok(bh, a->Dk * a->Dv, &st) || !mul_ok(st, a->P, &pst))
+        return KDA_ERR_SHAPE;
+    if (bh * (a->Dk / 16) > INT_MAX) return KDA_ERR_SHAPE;  // one workgroup per (b, h, 16 columns)
+    if (bh == 0) return KDA_OK;
+    if (a->P > 0 && (!a->transition || !a->offset)) return KDA_ERR_NULL;
+    const void* ptrs[] = {a->transition, a->offset, a->initial_state, a->segment_states, a->final_state};
+    for (const void* p : ptrs)
+        if (!aligned16(p)) return KDA_ERR_ALIGN;
+    if (!a->segment_states && !a->final_state) return KDA_OK;
+    kda::CombineParams p{a->transition, a->offset, a->initial_state, a->segment_states, a->final_state,
+                         a->P, bh};
+    const hipError_t e = kda::launch_combine((int)a->Dk, p, stream);
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 

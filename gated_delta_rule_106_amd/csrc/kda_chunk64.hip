@@ -1002,7 +1002,7 @@ void kda_sum64_kernel(RecurParams p) {
                                         Ub[u], S[ct]);
             lds_barrier();  // the slot of chunk ci is free; chunk ci + 1 is resident
         }
-        float* dst = p.sums + (useg * 2 + (mtile ? 1 : 0)) * (int64_t)D * D;
+        float* dst = (mtile ? p.sum_m : p.sum_b) + useg * p.sum_stride;
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
@@ -1071,8 +1071,11 @@ int segments(int D, int64_t units, int64_t nc) {
     return 1;
 }
 
+// Launches the card builder, the segment summaries (rp.nseg > 1) and, unless
+// summary_only, the state pass.
 template <int D, class Out, int NCONS>
-static hipError_t launch_d(const PrepParams& pp, const RecurParams& rp0, hipStream_t stream) {
+static hipError_t launch_d(const PrepParams& pp, const RecurParams& rp0, hipStream_t stream,
+                           bool summary_only = false) {
     using LP = PrepL<D>;
     using LR = RecL<D, NCONS>;
     using LS = SumL<D, kSumTiles>;
@@ -1089,6 +1092,11 @@ static hipError_t launch_d(const PrepParams& pp, const RecurParams& rp0, hipStre
         if (e != hipSuccess) return e;
     }
     if (rp.nseg > 1) {
+        if (!rp.sum_b) {  // the state pass's layout: b_p then M_p per segment
+            rp.sum_b = rp.sums;
+            rp.sum_m = rp.sums + (int64_t)D * D;
+            rp.sum_stride = 2 * (int64_t)D * D;
+        }
         auto ks = kda_sum64_kernel<D, kSumTiles>;
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(ks),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)LS::TOTAL);
@@ -1098,6 +1106,7 @@ static hipError_t launch_d(const PrepParams& pp, const RecurParams& rp0, hipStre
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
+    if (summary_only) return hipSuccess;
     auto kr = kda_rec64_kernel<D, Out, NCONS>;
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kr),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)LR::TOTAL);
@@ -1142,6 +1151,27 @@ hipError_t launch_prefill64(int D, int out_bf16, const PrepParams& pp, const Rec
     if (D == 64)
         return out_bf16 ? c64::launch_d<64, InBF16, 1>(pp, rp, stream)
                         : c64::launch_d<64, InF32, 1>(pp, rp, stream);
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_summary64(int D, const PrepParams& pp, float* M, float* b, hipStream_t stream) {
+    // one summarised segment spanning all NC chunks: the summary kernel's segment 0 of
+    // nseg = 2 (the second, never summarised, segment is empty); the padding tokens of
+    // a last partial chunk are identity steps, so the summary is exact for any T
+    RecurParams rp{};
+    rp.B = pp.B;
+    rp.T = pp.T;
+    rp.H = pp.H;
+    rp.NC = pp.NC;
+    rp.ws = pp.ws;
+    rp.nseg = 2;
+    rp.seg_len = pp.NC;
+    rp.sum_b = b;
+    rp.sum_m = M;
+    rp.sum_stride = (int64_t)D * D;
+    if (pp.NC < 1) return hipErrorInvalidValue;
+    if (D == 128) return c64::launch_d<128, InF32, 1>(pp, rp, stream, true);
+    if (D == 64) return c64::launch_d<64, InF32, 1>(pp, rp, stream, true);
     return hipErrorInvalidValue;
 }
 

@@ -31,6 +31,12 @@ struct RecurParams {
     int64_t seg_len;
     int nseg;
     float* sums;
+    // where the summary kernel writes b_p and M_p of summarised segment u (= (b, h) *
+    // (nseg - 1) + p): sum_b + u * sum_stride and sum_m + u * sum_stride.  Left NULL,
+    // they follow `sums` (b_p then M_p per segment, stride 2 D^2).
+    float* sum_b;
+    float* sum_m;
+    int64_t sum_stride;
 };
 
 // bytes of one per-chunk card in the workspace (or -1 if unsupported)
@@ -47,5 +53,8 @@ int prefill64_segments(int D, int64_t units, int64_t nc);
 int64_t prefill64_extra_bytes(int D, int64_t units, int64_t nc);
 hipError_t launch_prefill64(int D, int out_bf16, const PrepParams& pp, const RecurParams& rp,
                             hipStream_t stream);
+// summary of whole sequences (NC >= 1): cards, then one summarised segment of NC chunks
+// per (b, h); M [units, D, D] and b [units, D, D] in fp32
+hipError_t launch_summary64(int D, const PrepParams& pp, float* M, float* b, hipStream_t stream);
 
 }  // namespace kda

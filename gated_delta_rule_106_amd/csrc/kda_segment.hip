@@ -1,0 +1,135 @@
+// Ordered combination of segment summaries on gfx950.
+//
+// Page "Kimi K3 report walk-through", section "KDA Context Parallelism" (and page
+// "3T models are no longer magic", section "KDA context parallelism"): a segment of
+// tokens acts on the state it receives as an affine map S -> M S + b, so once every
+// segment has been summarised, the state entering segment p + 1 follows from the one
+// entering segment p as S_{p+1} = M_p S_p + b_p.  This is the only sequential step
+// between segments; it costs one D x D by D x D product per segment and (b, h),
+// independent of the segment lengths.
+//
+// One workgroup per ((b, h), 16-column tile of the state): the tile (D x 16 fp32)
+// stays in LDS across the segments; four waves each own D / 64 blocks of 16 rows and
+// form them with the fp32 MFMA (v_mfma_f32_16x16x4_f32), M_p streamed from memory as
+// float4 rows and b_p as the starting accumulator.  Everything stays in fp32: the
+// state keeps its full precision from segment to segment.
+#include "kda_device.h"
+#include "kda_segment.h"
+
+namespace kda {
+namespace seg {
+
+constexpr int kPad = 20;  // LDS row pitch (floats): lane groups land on disjoint banks
+
+// 16 k-steps of the fp32 MFMA: k = 16 kk + 4 g + c, c = 0..3 (A[m][k] from a.c,
+// B[k][m] from b[c]); both operands use the same assignment of k.
+__device__ __forceinline__ floatx4 mma16(const float4& a, const floatx4& b, floatx4 acc) {
+    acc = mma_f32_k4(a.x, b[0], acc);
+    acc = mma_f32_k4(a.y, b[1], acc);
+    acc = mma_f32_k4(a.z, b[2], acc);
+    acc = mma_f32_k4(a.w, b[3], acc);
+    return acc;
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void kda_combine_kernel(CombineParams p) {
+    constexpr int NT = D / 16;        // column tiles per state
+    constexpr int RBW = D / 64;       // row blocks per wave
+    __shared__ __align__(16) float S[D * kPad];
+    const int lane = lane_id(), wave = wave_id();
+    const int m = lane & 15, g = lane >> 4;
+    const int64_t unit = blockIdx.x / NT;
+    const int col0 = 16 * (int)(blockIdx.x % NT);
+    const int64_t DD = (int64_t)D * D;
+
+    // the tile of the incoming state (read before anything of this tile is written,
+    // so the final state may alias it)
+    for (int e = threadIdx.x; e < D * 16; e += 256) {
+        const int r = e >> 4, c = e & 15;
+        S[r * kPad + c] = p.s0 ? p.s0[unit * DD + (int64_t)r * D + col0 + c] : 0.f;
+    }
+    __syncthreads();
+    for (int64_t s = 0; s < p.P; ++s) {
+        const float* Mp = p.M + (s * p.units + unit) * DD;
+        const float* bp = p.b + (s * p.units + unit) * DD;
+        if (p.seg) {
+            float* dst = p.seg + (s * p.units + unit) * DD;
+            for (int e = threadIdx.x; e < D * 16; e += 256) {
+                const int r = e >> 4, c = e & 15;
+                dst[(int64_t)r * D + col0 + c] = S[r * kPad + c];
+            }
+        }
+        floatx4 acc[RBW];
+#pragma unroll
+        for (int rb = 0; rb < RBW; ++rb) {
+            const int row = 16 * (wave * RBW + rb) + 4 * g;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[rb][i] = bp[(int64_t)(row + i) * D + col0 + m];
+        }
+#pragma unroll 4
+        for (int kk = 0; kk < D / 16; ++kk) {
+            const int k0 = 16 * kk + 4 * g;
+            const floatx4 sv = {S[(k0 + 0) * kPad + m], S[(k0 + 1) * kPad + m], S[(k0 + 2) * kPad + m],
+                                S[(k0 + 3) * kPad + m]};
+#pragma unroll
+            for (int rb = 0; rb < RBW; ++rb) {
+                const int row = 16 * (wave * RBW + rb) + m;
+                const float4 a = *reinterpret_cast<const float4*>(Mp + (int64_t)row * D + k0);
+                acc[rb] = mma16(a, sv, acc[rb]);
+            }
+        }
+        __syncthreads();  // every wave has read S_p
+#pragma unroll
+        for (int rb = 0; rb < RBW; ++rb) {
+            const int row = 16 * (wave * RBW + rb) + 4 * g;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) S[(row + i) * kPad + m] = acc[rb][i];
+        }
+        __syncthreads();  // S_{p+1} is complete
+    }
+    if (p.sT) {
+        for (int e = threadIdx.x; e < D * 16; e += 256) {
+            const int r = e >> 4, c = e & 15;
+            p.sT[unit * DD + (int64_t)r * D + col0 + c] = S[r * kPad + c];
+        }
+    }
+}
+
+// M = I and b = 0 for every (b, h): one workgroup per (b, h)
+template <int D>
+__global__ __launch_bounds__(256) void kda_identity_summary_kernel(float* M, float* b) {
+    const int64_t base = (int64_t)blockIdx.x * D * D;
+    for (int e = threadIdx.x; e < D * D; e += 256) {
+        M[base + e] = (e / D == e % D) ? 1.f : 0.f;
+        b[base + e] = 0.f;
+    }
+}
+
+}  // namespace seg
+
+hipError_t launch_combine(int D, const CombineParams& p, hipStream_t stream) {
+    if (p.units <= 0) return hipSuccess;
+    const int64_t blocks = p.units * (D / 16);
+    if (D == 128)
+        hipLaunchKernelGGL(seg::kda_combine_kernel<128>, dim3((unsigned)blocks), dim3(256), 0, stream, p);
+    else if (D == 64)
+        hipLaunchKernelGGL(seg::kda_combine_kernel<64>, dim3((unsigned)blocks), dim3(256), 0, stream, p);
+    else
+        return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
+hipError_t launch_identity_summary(int D, float* M, float* b, int64_t units, hipStream_t stream) {
+    if (units <= 0) return hipSuccess;
+    if (D == 128)
+        hipLaunchKernelGGL(seg::kda_identity_summary_kernel<128>, dim3((unsigned)units), dim3(256), 0, stream,
+                           M, b);
+    else if (D == 64)
+        hipLaunchKernelGGL(seg::kda_identity_summary_kernel<64>, dim3((unsigned)units), dim3(256), 0, stream,
+                           M, b);
+    else
+        return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
+}  // namespace kda

@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define KDA_VERSION 1
+#define KDA_VERSION 2
 
 /* element types */
 #define KDA_F32 0  /* IEEE binary32 */
@@ -128,6 +128,54 @@ int kda_chunk_fwd_workspace_size(const kda_fwd_args *a, size_t *bytes);
 
 /* Chunkwise-parallel forward over whole sequences (prefill).  Returns a status. */
 int kda_chunk_fwd(const kda_fwd_args *a, hipStream_t stream);
+
+/*
+ * Segment summary of whole sequences.  Page "3T models are no longer magic",
+ * section "KDA context parallelism", and page "Kimi K3 report walk-through",
+ * section "KDA Context Parallelism": a run of tokens is summarised by how it
+ * transforms the state it receives and by the state it produces from a zero
+ * start, so that runs computed apart (on other devices, or as segments of one
+ * long sequence) can be chained afterwards.  For every (b, h) the T tokens map
+ * an incoming state S_0 to
+ *     S_T = M S_0 + b,   M = A_T ... A_1,   A_t = (I - beta_t k_t k_t^T) Diag(alpha_t),
+ * with b the state reached from S_0 = 0.
+ *   Reads k, v, log_alpha, beta and the clamp flag of *a; q, gate, out and
+ *   initial_state are not read and may be NULL.
+ *   transition: fp32 [B, H, Dk, Dk], receives M (required).
+ *   a->final_state: fp32 [B, H, Dk, Dv], receives b (required).
+ *   The two outputs must not overlap each other, the inputs or the workspace.
+ *   Supported: bf16 inputs, chunk 0 or 64, Dk == Dv in {64, 128}; flags other
+ *   than KDA_FLAG_NO_CLAMP return KDA_ERR_UNSUPPORTED.  The workspace that
+ *   kda_chunk_fwd_workspace_size() reports for the same *a is sufficient.
+ *   T == 0 gives M = I and b = 0.  M and b are accumulated in fp32 from fp16
+ *   MFMA operands, like the state of kda_chunk_fwd.
+ */
+int kda_chunk_summary(const kda_fwd_args *a, float *transition, hipStream_t stream);
+
+/*
+ * Ordered combination of P consecutive segment summaries (same pages and
+ * sections): the state entering segment p + 1 is S_{p+1} = M_p S_p + b_p, with
+ * S_0 the state entering segment 0.  Computed in fp32 (fp32 MFMA).
+ *   transition: fp32 [P, B, H, Dk, Dk] (M_p); offset: fp32 [P, B, H, Dk, Dv] (b_p);
+ *     both required when P > 0.
+ *   initial_state: fp32 [B, H, Dk, Dv] or NULL (zeros).
+ *   segment_states: fp32 [P, B, H, Dk, Dv] or NULL; receives S_0 .. S_{P-1}, the
+ *     state each segment starts from (to re-run it with kda_chunk_fwd).
+ *   final_state: fp32 [B, H, Dk, Dv] or NULL; receives S_P.  It may alias
+ *     initial_state; no other output may overlap an input.
+ *   Dk == Dv in {64, 128}.  P == 0 copies initial_state (or zeros) to
+ *   final_state.
+ */
+typedef struct kda_combine_args {
+    int64_t P, B, H, Dk, Dv;
+    const float *transition;
+    const float *offset;
+    const float *initial_state;
+    float *segment_states;
+    float *final_state;
+} kda_combine_args;
+
+int kda_combine_states(const kda_combine_args *a, hipStream_t stream);
 
 /*
  * Arguments of kda_decode_step: one token per (b, h).

@@ -36,7 +36,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.kda_version() == 1
+    assert lib.kda_version() == 2
     for code in range(-6, 1):
         assert lib.kda_status_str(code).decode()
     assert lib.kda_status_str(12345).decode() == "unknown status"
@@ -49,9 +49,11 @@ def test_struct_layout_matches_header(tmp_path):
 #include <stddef.h>
 #include "kda.h"
 int main(void) {
-  printf("%zu %zu %zu %zu %zu %zu\n", sizeof(kda_fwd_args), offsetof(kda_fwd_args, q),
+  printf("%zu %zu %zu %zu %zu %zu %zu %zu %zu\n", sizeof(kda_fwd_args), offsetof(kda_fwd_args, q),
          offsetof(kda_fwd_args, workspace_bytes), sizeof(kda_decode_args),
-         offsetof(kda_decode_args, q), offsetof(kda_decode_args, state));
+         offsetof(kda_decode_args, q), offsetof(kda_decode_args, state),
+         sizeof(kda_combine_args), offsetof(kda_combine_args, transition),
+         offsetof(kda_combine_args, final_state));
   return 0;
 }''')
     exe = tmp_path / "layout"
@@ -60,7 +62,9 @@ int main(void) {
     got = [int(x) for x in subprocess.run([str(exe)], capture_output=True, text=True,
                                           check=True).stdout.split()]
     want = [ctypes.sizeof(_abi.FwdArgs), _abi.FwdArgs.q.offset, _abi.FwdArgs.workspace_bytes.offset,
-            ctypes.sizeof(_abi.DecodeArgs), _abi.DecodeArgs.q.offset, _abi.DecodeArgs.state.offset]
+            ctypes.sizeof(_abi.DecodeArgs), _abi.DecodeArgs.q.offset, _abi.DecodeArgs.state.offset,
+            ctypes.sizeof(_abi.CombineArgs), _abi.CombineArgs.transition.offset,
+            _abi.CombineArgs.final_state.offset]
     assert got == want
 
 
@@ -178,6 +182,69 @@ def test_empty_problems_are_no_ops(lib):
     assert lib.kda_chunk_fwd(ctypes.byref(f), None) == 0
 
 
+def _good_sum():
+    a = _good_fwd(T=300, H=2)
+    a.final_state = 0x30000
+    return a
+
+
+@pytest.mark.parametrize("mutate,code", [
+    (lambda a: setattr(a, "dtype", _abi.KDA_F32), _abi.KDA_ERR_UNSUPPORTED),
+    (lambda a: setattr(a, "chunk", 32), _abi.KDA_ERR_UNSUPPORTED),
+    (lambda a: setattr(a, "flags", _abi.KDA_FLAG_NO_SEGMENT_SCAN), _abi.KDA_ERR_UNSUPPORTED),
+    (lambda a: setattr(a, "Dk", 96), _abi.KDA_ERR_UNSUPPORTED),
+    (lambda a: setattr(a, "T", -1), _abi.KDA_ERR_SHAPE),
+    (lambda a: setattr(a, "final_state", None), _abi.KDA_ERR_NULL),
+    (lambda a: setattr(a, "final_state", 0x30008), _abi.KDA_ERR_ALIGN),
+    (lambda a: setattr(a, "k", None), _abi.KDA_ERR_NULL),
+    (lambda a: setattr(a, "beta", 0x10002), _abi.KDA_ERR_ALIGN),
+    (lambda a: None, _abi.KDA_ERR_WORKSPACE),  # no workspace given
+    (lambda a: (setattr(a, "workspace", 0x20000), setattr(a, "workspace_bytes", 4096)),
+     _abi.KDA_ERR_WORKSPACE),
+])
+def test_summary_validation(lib, mutate, code):
+    a = _good_sum()
+    a.q = a.gate = a.out = None  # not read by the summary
+    mutate(a)
+    assert lib.kda_chunk_summary(ctypes.byref(a), ctypes.c_void_p(0x40000), None) == code
+
+
+def test_summary_needs_transition_and_empty_batch_is_a_no_op(lib):
+    a = _good_sum()
+    assert lib.kda_chunk_summary(ctypes.byref(a), None, None) == _abi.KDA_ERR_NULL
+    assert lib.kda_chunk_summary(ctypes.byref(a), ctypes.c_void_p(0x40004), None) == _abi.KDA_ERR_ALIGN
+    assert lib.kda_chunk_summary(None, None, None) == _abi.KDA_ERR_NULL
+    a.H = 0
+    assert lib.kda_chunk_summary(ctypes.byref(a), None, None) == 0
+
+
+def _good_comb():
+    a = _abi.CombineArgs()
+    a.P, a.B, a.H, a.Dk, a.Dv = 4, 1, 8, 128, 128
+    a.transition, a.offset, a.final_state = 0x10000, 0x20000, 0x30000
+    return a
+
+
+@pytest.mark.parametrize("mutate,code", [
+    (lambda a: setattr(a, "P", -1), _abi.KDA_ERR_SHAPE),
+    (lambda a: setattr(a, "H", -2), _abi.KDA_ERR_SHAPE),
+    (lambda a: setattr(a, "P", 2 ** 60), _abi.KDA_ERR_SHAPE),
+    (lambda a: setattr(a, "Dv", 64), _abi.KDA_ERR_UNSUPPORTED),
+    (lambda a: (setattr(a, "Dk", 32), setattr(a, "Dv", 32)), _abi.KDA_ERR_UNSUPPORTED),
+    (lambda a: setattr(a, "transition", None), _abi.KDA_ERR_NULL),
+    (lambda a: setattr(a, "offset", None), _abi.KDA_ERR_NULL),
+    (lambda a: setattr(a, "initial_state", 0x40004), _abi.KDA_ERR_ALIGN),
+    (lambda a: setattr(a, "segment_states", 0x50008), _abi.KDA_ERR_ALIGN),
+    (lambda a: setattr(a, "final_state", None), _abi.KDA_OK),  # no output requested: nothing to do
+    (lambda a: setattr(a, "B", 0), _abi.KDA_OK),
+])
+def test_combine_validation(lib, mutate, code):
+    a = _good_comb()
+    mutate(a)
+    assert lib.kda_combine_states(ctypes.byref(a), None) == code
+    assert lib.kda_combine_states(None, None) == _abi.KDA_ERR_NULL
+
+
 def test_binding_refuses_cpu_tensors():
     import torch
     import gated_delta_rule_106_amd as kda
@@ -187,3 +254,7 @@ def test_binding_refuses_cpu_tensors():
     with pytest.raises(ValueError):
         kda.decode_step(x[:, 0], x[:, 0], x[:, 0], x[:, 0], torch.zeros(1, 1), x[:, 0],
                         torch.zeros(1, 1, 64, 64))
+    with pytest.raises(ValueError):
+        kda.chunk_summary(x, x, x, torch.zeros(1, 16, 1))
+    with pytest.raises(ValueError):
+        kda.combine_states(torch.zeros(2, 1, 1, 64, 64), torch.zeros(2, 1, 1, 64, 64))
