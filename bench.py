@@ -10,7 +10,9 @@ inputs, fp32 state, chunk 64 built from 16-token tiles.  The same run also
 times the single-token decode step on B=512, H=32 (fp32 128x128 state per head,
 updated in place) and reports it in the ``decode`` object; the two larger
 prefill shapes (B2 H32 T8192 with state in/out, B1 H16 T65536 with 30 % of the
-key channels at the retention floor) are timed for context under ``configs``.
+key channels at the retention floor) are timed for context under ``configs``,
+and ``context_parallel`` times one GPU's share of an 8-way split along T of the
+floor-stress workload (segment summary, ordered combination, re-run).
 
 Inputs are synthetic and seeded (kda_workloads); they are resident in device
 memory before the timed region starts.  The headline prefill rotates through
@@ -252,6 +254,56 @@ def counter_pass(kda, head, dec_wl, n_sets, dev, stream):
             "source_digest": source_digest()}
 
 
+def bench_context_parallel(kda, steps, warmup, dev, stream, P=8):
+    """One GPU's share of a P-way split along T of the floor-stress workload (pages:
+    "KDA context parallelism"): the summary of its T/P tokens, the ordered
+    combination of the P summaries (P - 1 of which another GPU would deliver), and
+    the re-run of its segment from the incoming state.  Kernel time of each stage."""
+    import torch
+    from kda_workloads import CONFIGS, make_inputs
+    full = CONFIGS[3]
+    wl = full.scaled(T=full.T // P, init_state=True)
+    log(f"context parallel: share of {P}-way split of {full.name}: T={wl.T} per GPU")
+    x = to_dev(make_inputs(wl), dev)
+    ws = torch.empty(kda.workspace_bytes(wl.B, wl.T, wl.H, wl.Dk), dtype=torch.uint8, device=dev)
+    out = torch.empty((wl.B, wl.T, wl.H, wl.Dv), dtype=torch.float32, device=dev)
+    M = torch.empty((wl.B, wl.H, wl.Dk, wl.Dk), dtype=torch.float32, device=dev)
+    b = torch.empty((wl.B, wl.H, wl.Dk, wl.Dv), dtype=torch.float32, device=dev)
+    kda.chunk_summary(x["k"], x["v"], x["log_alpha"], x["beta"], transition=M, offset=b, workspace=ws)
+    Ms, bs = M.expand(P, *M.shape).contiguous(), b.expand(P, *b.shape).contiguous()
+    fin = torch.empty_like(b)
+
+    def f_sum(_):
+        kda.chunk_summary(x["k"], x["v"], x["log_alpha"], x["beta"], transition=M, offset=b, workspace=ws)
+
+    def f_comb(_):
+        kda.combine_states(Ms, bs, x["initial_state"], segment_states=False, final_state=fin)
+
+    def f_rerun(_):
+        kda.chunk_fwd(*(x[k] for k in KEYS), initial_state=fin, out=out, workspace=ws)
+    _, t_sum = time_calls(f_sum, [None], steps, warmup, stream)
+    _, t_comb = time_calls(f_comb, [None], steps, warmup, stream)
+    _, t_rerun = time_calls(f_rerun, [None], steps, warmup, stream)
+    units, d = wl.B * wl.H, wl.Dk
+    # summary: reads k, v, log alpha (bf16) and beta; writes M and b (fp32)
+    sum_bytes = wl.B * wl.T * wl.H * 2 * (2 * d + wl.Dv + 1) + units * 4 * d * (d + wl.Dv)
+    # combination: per segment reads M_p and b_p, plus the initial and final state
+    comb_bytes = units * 4 * d * (P * (d + wl.Dv) + 2 * wl.Dv)
+    res = {"workload": full.name, "split": P, "tokens_per_gpu": wl.T, "B": wl.B, "H": wl.H, "d": d,
+           "summary_us": 1e3 * t_sum, "combine_us": 1e3 * t_comb, "rerun_us": 1e3 * t_rerun,
+           "share_total_us": 1e3 * (t_sum + t_comb + t_rerun),
+           "summary_alg_gbs": sum_bytes / (t_sum / 1e3) / 1e9,
+           "combine_alg_gbs": comb_bytes / (t_comb / 1e3) / 1e9,
+           "combine_tflops": units * P * 2 * d * d * wl.Dv / (t_comb / 1e3) / 1e12,
+           "note": "per-GPU share only; the all-gather of the summaries between GPUs is not part "
+                   "of this single-GPU measurement"}
+    log(f"context parallel: summary {res['summary_us']:.1f} us, combine {res['combine_us']:.1f} us, "
+        f"re-run {res['rerun_us']:.1f} us per GPU share")
+    del x, ws, out
+    torch.cuda.empty_cache()
+    return res
+
+
 SEGMENT_SHAPES = ((1, 8, 4096), (1, 1, 16384), (1, 2, 32768), (1, 4, 16384), (2, 2, 8192))
 
 
@@ -289,6 +341,8 @@ def main():
                     help="time budget of the oracle baseline (0 skips it)")
     ap.add_argument("--no-context", action="store_true",
                     help="skip the context timings of the two larger prefill shapes")
+    ap.add_argument("--no-context-parallel", action="store_true",
+                    help="skip the per-GPU share of the context-parallel split")
     ap.add_argument("--segment-sweep", action="store_true",
                     help="time the segment scan against one pass per sequence on few long sequences")
     ap.add_argument("--counter-pass", action="store_true",
@@ -331,6 +385,9 @@ def main():
             r, _ = bench_prefill(kda, CONFIGS[cid], max(5, args.steps // 10), 2, 1, dev, stream)
             ctx[CONFIGS[cid].name] = r
             torch.cuda.empty_cache()
+    kcp = None
+    if not args.no_context_parallel:
+        kcp = bench_context_parallel(kda, max(5, args.steps // 5), 2, dev, stream)
 
     traffic = stored_traffic("prefill_" + head.name)
     roof = {"kernel": "kda_chunk_fwd = kda_prep64_kernel + kda_rec64_kernel (one call, two launches)",
@@ -359,6 +416,7 @@ def main():
                    "workload": dec["workload"]},
         "prefill_detail": pre,
         "configs": ctx,
+        "context_parallel": kcp,
         "source_digest": source_digest(),
     }
     if args.cpu_seconds > 0:

@@ -129,20 +129,6 @@ __device__ __forceinline__ floatx4 mma_f32_k16(const float4& a, const floatx4& b
     return acc;
 }
 
-__device__ __forceinline__ void wait_vm_zero() { __builtin_amdgcn_s_waitcnt(0x0F70); }   // vmcnt(0)
-__device__ __forceinline__ void wait_lgkm_zero() { __builtin_amdgcn_s_waitcnt(0xC07F); } // lgkmcnt(0)
-// workgroup barrier without the implicit memory fence of __syncthreads():
-// each wave waits explicitly for exactly what the next phase needs
-__device__ __forceinline__ void bare_barrier() {
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-}
-// barrier that orders LDS only: global stores issued before it keep draining
-__device__ __forceinline__ void lds_barrier() {
-    wait_lgkm_zero();
-    bare_barrier();
-}
 
 // ---------------------------------------------------------------------------
 template <int D>

@@ -70,6 +70,21 @@ __device__ __forceinline__ floatx4 mma_f32_k4(float a, float b, floatx4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
+__device__ __forceinline__ void wait_vm_zero() { __builtin_amdgcn_s_waitcnt(0x0F70); }   // vmcnt(0)
+__device__ __forceinline__ void wait_lgkm_zero() { __builtin_amdgcn_s_waitcnt(0xC07F); } // lgkmcnt(0)
+// workgroup barrier without the implicit memory fence of __syncthreads():
+// each wave waits explicitly for exactly what the next phase needs
+__device__ __forceinline__ void bare_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+// barrier that orders LDS only: global loads and stores issued before it stay in flight
+__device__ __forceinline__ void lds_barrier() {
+    wait_lgkm_zero();
+    bare_barrier();
+}
+
 // Split x into bf16 hi + lo with x ~= hi + lo to about 16 significant bits.
 __device__ __forceinline__ void split_bf16(float x, __bf16& hi, __bf16& lo) {
     hi = static_cast<__bf16>(x);

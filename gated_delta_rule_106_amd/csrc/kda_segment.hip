@@ -9,10 +9,12 @@
 // independent of the segment lengths.
 //
 // One workgroup per ((b, h), 16-column tile of the state): the tile (D x 16 fp32)
-// stays in LDS across the segments; four waves each own D / 64 blocks of 16 rows and
-// form them with the fp32 MFMA (v_mfma_f32_16x16x4_f32), M_p streamed from memory as
-// float4 rows and b_p as the starting accumulator.  Everything stays in fp32: the
-// state keeps its full precision from segment to segment.
+// stays in LDS across the segments; D / 16 waves each own one block of 16 rows and
+// form it with the fp32 MFMA (v_mfma_f32_16x16x4_f32) from its rows of M_p (held in
+// registers as float4 A operands) and b_p (the starting accumulator).  The rows of
+// M_{p+1} and b_{p+1} are loaded while segment p is combined, so each step waits on
+// memory at most once.  Everything stays in fp32: the state keeps its full
+// precision from segment to segment.
 #include "kda_device.h"
 #include "kda_segment.h"
 
@@ -32,63 +34,74 @@ __device__ __forceinline__ floatx4 mma16(const float4& a, const floatx4& b, floa
 }
 
 template <int D>
-__global__ __launch_bounds__(256) void kda_combine_kernel(CombineParams p) {
-    constexpr int NT = D / 16;        // column tiles per state
-    constexpr int RBW = D / 64;       // row blocks per wave
+__global__ __launch_bounds__(D * 4) void kda_combine_kernel(CombineParams p) {
+    constexpr int NT = D / 16;  // column tiles per state; also waves per workgroup
+    constexpr int NK = D / 16;  // 16-wide k steps of one row block
+    constexpr int NTH = D * 4;  // threads
     __shared__ __align__(16) float S[D * kPad];
     const int lane = lane_id(), wave = wave_id();
     const int m = lane & 15, g = lane >> 4;
-    const int64_t unit = blockIdx.x / NT;
-    const int col0 = 16 * (int)(blockIdx.x % NT);
+    // consecutive workgroups go to different XCDs; the NT tiles of one (b, h), which all
+    // stream the same M_p, are given blocks that share bid % 8 and so one XCD's L2
+    const int nblk = gridDim.x, bid = blockIdx.x;
+    const int64_t logical = (int64_t)(bid % 8) * (nblk / 8) + bid / 8;
+    const int64_t unit = logical / NT;
+    if (unit >= p.units) return;  // padding workgroup (the whole group leaves together)
+    const int col0 = 16 * (int)(logical % NT);
     const int64_t DD = (int64_t)D * D;
+    const int arow = 16 * wave + m;      // row of M this lane streams
+    const int crow = 16 * wave + 4 * g;  // first accumulator row of this lane
 
-    // the tile of the incoming state (read before anything of this tile is written,
-    // so the final state may alias it)
-    for (int e = threadIdx.x; e < D * 16; e += 256) {
-        const int r = e >> 4, c = e & 15;
-        S[r * kPad + c] = p.s0 ? p.s0[unit * DD + (int64_t)r * D + col0 + c] : 0.f;
-    }
-    __syncthreads();
-    for (int64_t s = 0; s < p.P; ++s) {
-        const float* Mp = p.M + (s * p.units + unit) * DD;
-        const float* bp = p.b + (s * p.units + unit) * DD;
+    // this wave's 16 rows of M_s (as MFMA A operands) and its b_s accumulator start,
+    // in two register sets: segment s + 1 loads while segment s is combined
+    float4 MA[NK], MB[NK];
+    floatx4 bA, bB;
+    auto load_seg = [&](int64_t s, float4(&Ma)[NK], floatx4& bb) __attribute__((always_inline)) {
+        const float* Mp = p.M + (s * p.units + unit) * DD + (int64_t)arow * D + 4 * g;
+        const float* bp = p.b + (s * p.units + unit) * DD + (int64_t)crow * D + col0 + m;
+#pragma unroll
+        for (int kk = 0; kk < NK; ++kk) Ma[kk] = *reinterpret_cast<const float4*>(Mp + 16 * kk);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) bb[i] = bp[(int64_t)i * D];
+    };
+    auto step = [&](int64_t s, const float4(&Ma)[NK], const floatx4& bb, float4(&Mn)[NK], floatx4& bn)
+        __attribute__((always_inline)) {
+        if (s + 1 < p.P) load_seg(s + 1, Mn, bn);
         if (p.seg) {
             float* dst = p.seg + (s * p.units + unit) * DD;
-            for (int e = threadIdx.x; e < D * 16; e += 256) {
+            for (int e = threadIdx.x; e < D * 16; e += NTH) {
                 const int r = e >> 4, c = e & 15;
                 dst[(int64_t)r * D + col0 + c] = S[r * kPad + c];
             }
         }
-        floatx4 acc[RBW];
+        floatx4 acc = bb;
 #pragma unroll
-        for (int rb = 0; rb < RBW; ++rb) {
-            const int row = 16 * (wave * RBW + rb) + 4 * g;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) acc[rb][i] = bp[(int64_t)(row + i) * D + col0 + m];
-        }
-#pragma unroll 4
-        for (int kk = 0; kk < D / 16; ++kk) {
+        for (int kk = 0; kk < NK; ++kk) {
             const int k0 = 16 * kk + 4 * g;
             const floatx4 sv = {S[(k0 + 0) * kPad + m], S[(k0 + 1) * kPad + m], S[(k0 + 2) * kPad + m],
                                 S[(k0 + 3) * kPad + m]};
-#pragma unroll
-            for (int rb = 0; rb < RBW; ++rb) {
-                const int row = 16 * (wave * RBW + rb) + m;
-                const float4 a = *reinterpret_cast<const float4*>(Mp + (int64_t)row * D + k0);
-                acc[rb] = mma16(a, sv, acc[rb]);
-            }
+            acc = mma16(Ma[kk], sv, acc);
         }
-        __syncthreads();  // every wave has read S_p
+        lds_barrier();  // every wave has read S_s (loads of segment s + 1 stay in flight)
 #pragma unroll
-        for (int rb = 0; rb < RBW; ++rb) {
-            const int row = 16 * (wave * RBW + rb) + 4 * g;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) S[(row + i) * kPad + m] = acc[rb][i];
-        }
-        __syncthreads();  // S_{p+1} is complete
+        for (int i = 0; i < 4; ++i) S[(crow + i) * kPad + m] = acc[i];
+        lds_barrier();  // S_{s+1} is complete
+    };
+    if (p.P > 0) load_seg(0, MA, bA);
+
+    // the tile of the incoming state (read before anything of this tile is written,
+    // so the final state may alias it)
+    for (int e = threadIdx.x; e < D * 16; e += NTH) {
+        const int r = e >> 4, c = e & 15;
+        S[r * kPad + c] = p.s0 ? p.s0[unit * DD + (int64_t)r * D + col0 + c] : 0.f;
+    }
+    __syncthreads();
+    for (int64_t s = 0; s < p.P; s += 2) {
+        step(s, MA, bA, MB, bB);
+        if (s + 1 < p.P) step(s + 1, MB, bB, MA, bA);
     }
     if (p.sT) {
-        for (int e = threadIdx.x; e < D * 16; e += 256) {
+        for (int e = threadIdx.x; e < D * 16; e += NTH) {
             const int r = e >> 4, c = e & 15;
             p.sT[unit * DD + (int64_t)r * D + col0 + c] = S[r * kPad + c];
         }
@@ -109,9 +122,9 @@ __global__ __launch_bounds__(256) void kda_identity_summary_kernel(float* M, flo
 
 hipError_t launch_combine(int D, const CombineParams& p, hipStream_t stream) {
     if (p.units <= 0) return hipSuccess;
-    const int64_t blocks = p.units * (D / 16);
+    const int64_t blocks = (p.units * (D / 16) + 7) / 8 * 8;  // a multiple of 8 (XCD mapping)
     if (D == 128)
-        hipLaunchKernelGGL(seg::kda_combine_kernel<128>, dim3((unsigned)blocks), dim3(256), 0, stream, p);
+        hipLaunchKernelGGL(seg::kda_combine_kernel<128>, dim3((unsigned)blocks), dim3(512), 0, stream, p);
     else if (D == 64)
         hipLaunchKernelGGL(seg::kda_combine_kernel<64>, dim3((unsigned)blocks), dim3(256), 0, stream, p);
     else
