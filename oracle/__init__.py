@@ -57,10 +57,13 @@ def _open(path):
     lib.kda_oracle_fwd.argtypes = [i64, i64, i64, i64, i64, ci, vp, vp, vp, vp, vp, vp,
                                    dp, dp, dp, ci, ci]
     lib.kda_oracle_fwd.restype = ci
+    lib.kda_oracle_fwd_ex.argtypes = [i64, i64, i64, i64, i64, ci, vp, vp, vp, vp, vp, vp,
+                                      dp, dp, dp, ci, ci, ci, ci]
+    lib.kda_oracle_fwd_ex.restype = ci
     lib.kda_oracle_decode.argtypes = [i64, i64, i64, i64, ci, vp, vp, vp, vp, vp, vp,
-                                      dp, dp, ci, ci]
+                                      dp, dp, ci, ci, ci, ci]
     lib.kda_oracle_decode.restype = ci
-    lib.kda_oracle_summary.argtypes = [i64, i64, i64, i64, i64, ci, vp, vp, vp, vp, dp, dp, ci, ci]
+    lib.kda_oracle_summary.argtypes = [i64, i64, i64, i64, i64, ci, vp, vp, vp, vp, dp, dp, ci, ci, ci, ci]
     lib.kda_oracle_summary.restype = ci
     lib.kda_oracle_default_threads.argtypes = []
     lib.kda_oracle_default_threads.restype = ci
@@ -149,8 +152,12 @@ def _ptr(a):
 
 
 def fwd(q, k, v, log_alpha, beta, gate, initial_state=None, clamp=True, threads=0,
-        return_seconds=False, _lib_handle=None):
+        return_seconds=False, qk_norm=False, gate_logits=False, _lib_handle=None):
     """Sequential fp64 recurrence over [B, T, H].
+
+    ``qk_norm``: q and k are raw; each token's k is divided by its L2 norm and q
+    by its L2 norm times sqrt(d_k).  ``gate_logits``: log_alpha holds forget-gate
+    logits x and log alpha = logsigmoid(x) (then the floor clamp as usual).
 
     Returns ``(y, final_state)`` as float64 numpy arrays of shapes [B, T, H, Dv]
     and [B, H, Dk, Dv] (and the wall time of the C call when
@@ -175,16 +182,18 @@ def fwd(q, k, v, log_alpha, beta, gate, initial_state=None, clamp=True, threads=
     sT = np.zeros((B, H, Dk, Dv), dtype=np.float64)
     t0 = time.perf_counter()
     lib = _lib_handle if _lib_handle is not None else _load()
-    rc = lib.kda_oracle_fwd(B, T, H, Dk, Dv, dt, _ptr(qa), _ptr(ka), _ptr(va), _ptr(la),
-                            _ptr(ba), _ptr(ga), _ptr(s0), _ptr(y), _ptr(sT),
-                            1 if clamp else 0, int(threads))
+    rc = lib.kda_oracle_fwd_ex(B, T, H, Dk, Dv, dt, _ptr(qa), _ptr(ka), _ptr(va), _ptr(la),
+                               _ptr(ba), _ptr(ga), _ptr(s0), _ptr(y), _ptr(sT),
+                               1 if clamp else 0, 1 if qk_norm else 0, 1 if gate_logits else 0,
+                               int(threads))
     secs = time.perf_counter() - t0
     if rc != 0:
         raise RuntimeError(f"kda_oracle_fwd failed with code {rc}")
     return (y, sT, secs) if return_seconds else (y, sT)
 
 
-def decode(q, k, v, log_alpha, beta, gate, state, clamp=True, threads=0, _lib_handle=None):
+def decode(q, k, v, log_alpha, beta, gate, state, clamp=True, threads=0, qk_norm=False,
+           gate_logits=False, _lib_handle=None):
     """One recurrent step for every (b, h): inputs [B, H, D], beta [B, H].
 
     ``state`` is [B, H, Dk, Dv] (any float type); returns ``(y, new_state)`` in
@@ -203,13 +212,14 @@ def decode(q, k, v, log_alpha, beta, gate, state, clamp=True, threads=0, _lib_ha
     lib = _lib_handle if _lib_handle is not None else _load()
     rc = lib.kda_oracle_decode(B, H, Dk, Dv, dt, _ptr(qa), _ptr(ka), _ptr(va), _ptr(la),
                                _ptr(ba), _ptr(ga), _ptr(s), _ptr(y), 1 if clamp else 0,
-                               int(threads))
+                               1 if qk_norm else 0, 1 if gate_logits else 0, int(threads))
     if rc != 0:
         raise RuntimeError(f"kda_oracle_decode failed with code {rc}")
     return y, s
 
 
-def summary(k, v, log_alpha, beta, clamp=True, threads=0, _lib_handle=None):
+def summary(k, v, log_alpha, beta, clamp=True, threads=0, qk_norm=False, gate_logits=False,
+            _lib_handle=None):
     """Segment summary of every (b, h) run over [B, T, H] (page "3T models are no
     longer magic", section "KDA context parallelism"): the run maps an incoming
     state S to ``M @ S + b``, with ``M`` the product of the per-token transitions
@@ -230,7 +240,8 @@ def summary(k, v, log_alpha, beta, clamp=True, threads=0, _lib_handle=None):
     b = np.zeros((B, H, Dk, Dv), dtype=np.float64)
     lib = _lib_handle if _lib_handle is not None else _load()
     rc = lib.kda_oracle_summary(B, T, H, Dk, Dv, dt, _ptr(ka), _ptr(va), _ptr(la), _ptr(ba),
-                                _ptr(M), _ptr(b), 1 if clamp else 0, int(threads))
+                                _ptr(M), _ptr(b), 1 if clamp else 0, 1 if qk_norm else 0,
+                                1 if gate_logits else 0, int(threads))
     if rc != 0:
         raise RuntimeError(f"kda_oracle_summary failed with code {rc}")
     return M, b

@@ -28,7 +28,14 @@
  *    (the retention floor, and retention never above 1);
  *  - the gate is the logistic sigmoid of the given logits, no normalisation
  *    of o before it;
- *  - q and k arrive already normalised/scaled; nothing is applied here;
+ *  - q and k arrive already normalised/scaled unless `qk_norm` is set; with
+ *    it, every token's k is divided by its L2 norm and q by its L2 norm times
+ *    sqrt(d_k) (the normalisation and query scale of the inputs the kernel is
+ *    specified on, done inside; page "3T models are no longer magic", section
+ *    "FlashKDA", puts Q and K normalisation into the preparation step);
+ *  - with `logits` set, log_alpha holds forget-gate logits x and
+ *    log alpha = logsigmoid(x) = -log(1 + e^-x), the parameterisation of the
+ *    inputs the kernel is specified on; the floor clamp follows as usual;
  *  - a NULL initial state means zeros.
  *
  * Inputs are read as the exact bit patterns the GPU receives (fp32 or bf16)
@@ -53,6 +60,20 @@
 /* Retention floor: per-step alpha >= 0.0067, so log alpha >= ln 0.0067. */
 static const double ORC_LOG_ALPHA_MIN = -5.005647752585217; /* log(0.0067) */
 
+/* log(sigmoid(x)) without overflow: -log1p(e^-x) for x >= 0, x - log1p(e^x) below. */
+static double orc_logsigmoid(double x) {
+    return x >= 0.0 ? -log1p(exp(-x)) : x - log1p(exp(x));
+}
+
+/* Divide x (n entries) by max(||x||_2, 1e-12) * extra. */
+static void orc_unit(double *x, int64_t n, double extra) {
+    double ss = 0.0;
+    for (int64_t c = 0; c < n; ++c) ss += x[c] * x[c];
+    double nrm = sqrt(ss);
+    if (nrm < 1e-12) nrm = 1e-12;
+    for (int64_t c = 0; c < n; ++c) x[c] /= nrm * extra;
+}
+
 /* Widen element i of a float32 or bfloat16 array to double (exact). */
 static double orc_load(const void *p, int dtype, int64_t i) {
     if (dtype == ORC_F32) return (double)((const float *)p)[i];
@@ -70,6 +91,7 @@ static void orc_sequence(int64_t b, int64_t h, int64_t T, int64_t H, int64_t Dk,
                          int64_t Dv, int dtype, const void *q, const void *k,
                          const void *v, const void *la, const void *beta,
                          const void *gate, double *S, double *out, int clamp,
+                         int qk_norm, int logits,
                          double *kv, double *qv, double *r, double *u, double *o) {
     for (int64_t t = 0; t < T; ++t) {
         const int64_t tok = (b * T + t) * H + h; /* index of (b, t, h) */
@@ -78,9 +100,14 @@ static void orc_sequence(int64_t b, int64_t h, int64_t T, int64_t H, int64_t Dk,
             kv[c] = orc_load(k, dtype, tok * Dk + c);
             qv[c] = orc_load(q, dtype, tok * Dk + c);
         }
+        if (qk_norm) { /* unit key; query of norm 1/sqrt(d_k) */
+            orc_unit(kv, Dk, 1.0);
+            orc_unit(qv, Dk, sqrt((double)Dk));
+        }
         /* forget: S <- Diag(alpha_t) S, alpha_t = exp(log alpha_t) per key channel */
         for (int64_t c = 0; c < Dk; ++c) {
             double l = orc_load(la, dtype, tok * Dk + c);
+            if (logits) l = orc_logsigmoid(l); /* forget-gate logit -> log alpha */
             if (clamp) {
                 if (l < ORC_LOG_ALPHA_MIN) l = ORC_LOG_ALPHA_MIN;
                 if (l > 0.0) l = 0.0;
@@ -131,11 +158,11 @@ int kda_oracle_default_threads(void) {
  * may be NULL (not returned) and may alias init_state.  out is [B, T, H, Dv].
  * Returns 0, or -1 on bad sizes / dtype, -2 on allocation failure.
  */
-int kda_oracle_fwd(int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv,
-                   int dtype, const void *q, const void *k, const void *v,
-                   const void *log_alpha, const void *beta, const void *gate,
-                   const double *init_state, double *out, double *final_state,
-                   int clamp, int nthreads) {
+int kda_oracle_fwd_ex(int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv,
+                      int dtype, const void *q, const void *k, const void *v,
+                      const void *log_alpha, const void *beta, const void *gate,
+                      const double *init_state, double *out, double *final_state,
+                      int clamp, int qk_norm, int logits, int nthreads) {
     if (B < 0 || T < 0 || H < 0 || Dk <= 0 || Dv <= 0) return -1;
     if (dtype != ORC_F32 && dtype != ORC_BF16) return -1;
     const int64_t units = B * H;
@@ -164,12 +191,21 @@ int kda_oracle_fwd(int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv,
             memset(S, 0, sizeof(double) * (size_t)(Dk * Dv));
         double *kv = scratch, *qv = kv + Dk, *r = qv + Dk, *u = r + Dv, *o = u + Dv;
         orc_sequence(b, h, T, H, Dk, Dv, dtype, q, k, v, log_alpha, beta, gate, S,
-                     out, clamp, kv, qv, r, u, o);
+                     out, clamp, qk_norm, logits, kv, qv, r, u, o);
         if (final_state) memcpy(final_state + soff, S, sizeof(double) * (size_t)(Dk * Dv));
         free(S);
         free(scratch);
     }
     return failed ? -2 : 0;
+}
+
+int kda_oracle_fwd(int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv,
+                   int dtype, const void *q, const void *k, const void *v,
+                   const void *log_alpha, const void *beta, const void *gate,
+                   const double *init_state, double *out, double *final_state,
+                   int clamp, int nthreads) {
+    return kda_oracle_fwd_ex(B, T, H, Dk, Dv, dtype, q, k, v, log_alpha, beta, gate,
+                             init_state, out, final_state, clamp, 0, 0, nthreads);
 }
 
 /*
@@ -180,10 +216,11 @@ int kda_oracle_fwd(int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv,
 int kda_oracle_decode(int64_t B, int64_t H, int64_t Dk, int64_t Dv, int dtype,
                       const void *q, const void *k, const void *v,
                       const void *log_alpha, const void *beta, const void *gate,
-                      double *state, double *out, int clamp, int nthreads) {
+                      double *state, double *out, int clamp, int qk_norm, int logits,
+                      int nthreads) {
     if (!state) return -1;
-    return kda_oracle_fwd(B, 1, H, Dk, Dv, dtype, q, k, v, log_alpha, beta, gate,
-                          state, out, state, clamp, nthreads);
+    return kda_oracle_fwd_ex(B, 1, H, Dk, Dv, dtype, q, k, v, log_alpha, beta, gate,
+                             state, out, state, clamp, qk_norm, logits, nthreads);
 }
 
 /*
@@ -219,7 +256,7 @@ static void orc_transition(double *X, int64_t Dk, int64_t n, const double *kv,
 int kda_oracle_summary(int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv,
                        int dtype, const void *k, const void *v,
                        const void *log_alpha, const void *beta, double *M,
-                       double *bstate, int clamp, int nthreads) {
+                       double *bstate, int clamp, int qk_norm, int logits, int nthreads) {
     if (B < 0 || T < 0 || H < 0 || Dk <= 0 || Dv <= 0 || !M || !bstate) return -1;
     if (dtype != ORC_F32 && dtype != ORC_BF16) return -1;
     const int64_t units = B * H;
@@ -249,10 +286,12 @@ int kda_oracle_summary(int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv,
             const double bt = orc_load(beta, dtype, tok);
             for (int64_t c = 0; c < Dk; ++c) {
                 kk[c] = orc_load(k, dtype, tok * Dk + c);
-                const double l = orc_load(log_alpha, dtype, tok * Dk + c);
+                const double x = orc_load(log_alpha, dtype, tok * Dk + c);
+                const double l = logits ? orc_logsigmoid(x) : x;
                 /* retention floor and retention <= 1, as in the forward */
                 a[c] = exp(clamp ? fmin(fmax(l, ORC_LOG_ALPHA_MIN), 0.0) : l);
             }
+            if (qk_norm) orc_unit(kk, Dk, 1.0);
             for (int64_t j = 0; j < Dv; ++j) vv[j] = orc_load(v, dtype, tok * Dv + j);
             orc_transition(Mu, Dk, Dk, kk, a, bt, NULL, r);
             orc_transition(bu, Dk, Dv, kk, a, bt, vv, r);

@@ -10,7 +10,8 @@ import numpy as np
 import pytest
 
 import oracle
-from tests._brute import brute_fwd, brute_summary
+from tests._brute import LOG_ALPHA_MIN, brute_fwd, brute_summary
+from scipy.special import log_expit
 
 MUTANTS = {
     "decay dropped": ("row[j] *= a;", "row[j] *= 1.0;"),
@@ -35,6 +36,11 @@ MUTANTS = {
     "summary transposed write": ("X[c * n + j] += kv[c] * r[j];", "X[c * n + j] += kv[j % Dk] * r[c % n];"),
     "summary starts from zero instead of the identity": ("(i == j) ? 1.0 : 0.0", "0.0"),
     "summary value dropped": ("(vv ? bt * vv[j] : 0.0)", "0.0"),
+    # fused preprocessing (raw q/k normalisation, forget-gate logits)
+    "query scale dropped": ("orc_unit(qv, Dk, sqrt((double)Dk));", "orc_unit(qv, Dk, 1.0);"),
+    "key not normalised": ("orc_unit(kv, Dk, 1.0);", ""),
+    "logsigmoid sign flipped": ("return x >= 0.0 ? -log1p(exp(-x))", "return x >= 0.0 ? log1p(exp(-x))"),
+    "summary key not normalised": ("if (qk_norm) orc_unit(kk, Dk, 1.0);", ""),
 }
 
 
@@ -55,6 +61,23 @@ def _pins_pass(handle) -> bool:
         return False
     M, bs = handle.summary(k, v, la, beta)
     Mb, bb = brute_summary(k, v, la, beta)
+    if not (np.abs(M - Mb).max() <= 1e-12 * np.abs(Mb).max()
+            and np.abs(bs - bb).max() <= 1e-12 * np.abs(bb).max()):
+        return False
+    # fused preprocessing: raw q, k of arbitrary size and forget logits
+    qr = q * rng.uniform(0.1, 9, (B, T, H, 1)).astype(np.float32)
+    kr = k * rng.uniform(0.1, 9, (B, T, H, 1)).astype(np.float32)
+    x = (rng.standard_normal((B, T, H, Dk)) * 3).astype(np.float32)
+    qn = qr.astype(np.float64) / np.linalg.norm(qr.astype(np.float64), axis=-1, keepdims=True) / np.sqrt(Dk)
+    kn = kr.astype(np.float64) / np.linalg.norm(kr.astype(np.float64), axis=-1, keepdims=True)
+    lx = np.maximum(log_expit(x.astype(np.float64)), LOG_ALPHA_MIN)
+    y, sT = handle.fwd(qr, kr, v, x, beta, gate, initial_state=s0, qk_norm=True, gate_logits=True)
+    yb, sb = brute_fwd(qn, kn, v, lx, beta, gate, s0=s0, clamp=False)
+    if not (np.abs(y - yb).max() <= 1e-12 * np.abs(yb).max()
+            and np.abs(sT - sb).max() <= 1e-12 * np.abs(sb).max()):
+        return False
+    M, bs = handle.summary(kr, v, x, beta, qk_norm=True, gate_logits=True)
+    Mb, bb = brute_summary(kn, v, lx, beta, clamp=False)
     if not (np.abs(M - Mb).max() <= 1e-12 * np.abs(Mb).max()
             and np.abs(bs - bb).max() <= 1e-12 * np.abs(bb).max()):
         return False
