@@ -11,7 +11,8 @@ times the single-token decode step on B=512, H=32 (fp32 128x128 state per head,
 updated in place) and reports it in the ``decode`` object; the two larger
 prefill shapes (B2 H32 T8192 with state in/out, B1 H16 T65536 with 30 % of the
 key channels at the retention floor) are timed for context under ``configs``,
-and ``context_parallel`` times one GPU's share of an 8-way split along T of the
+``fused_prep`` times the headline on raw q, k and forget logits with the
+preparation fused into the card builder, and ``context_parallel`` times one GPU's share of an 8-way split along T of the
 floor-stress workload (segment summary, ordered combination, re-run).
 
 Inputs are synthetic and seeded (kda_workloads); they are resident in device
@@ -304,6 +305,42 @@ def bench_context_parallel(kda, steps, warmup, dev, stream, P=8):
     return res
 
 
+def bench_fused_prep(kda, wl, steps, warmup, n_sets, dev, stream):
+    """The headline prefill on raw projections with the preparation fused into the
+    card builder (q/k L2 normalisation, log alpha from forget logits), against the
+    same call on prepared inputs, and against preparing the raw inputs with separate
+    torch ops before the plain call (the HBM round trip the fusion removes)."""
+    import torch
+    from kda_workloads import make_raw_inputs
+    sets = prefill_sets(kda, wl, n_sets, dev)
+    for i, x in enumerate(sets):  # same shapes; raw tensors in place of the prepared ones
+        raw = to_dev(make_raw_inputs(wl, seed=wl.seed + 100 * i), dev)
+        x.update({k: raw[k] for k in ("q", "k", "log_alpha")})
+
+    def fused(x):
+        kda.chunk_fwd(*(x[k] for k in KEYS), chunk=wl.chunk, out=x["out"], workspace=x["ws"],
+                      qk_norm=True, gate_logits=True)
+
+    def unfused(x):
+        q, k = x["q"].float(), x["k"].float()
+        qn = (q / q.norm(dim=-1, keepdim=True) / math.sqrt(wl.Dk)).to(x["q"].dtype)
+        kn = (k / k.norm(dim=-1, keepdim=True)).to(x["k"].dtype)
+        la = torch.nn.functional.logsigmoid(x["log_alpha"].float()).clamp_min(math.log(0.0067))
+        kda.chunk_fwd(qn, kn, x["v"], la.to(x["log_alpha"].dtype), x["beta"], x["gate"], chunk=wl.chunk,
+                      out=x["out"], workspace=x["ws"])
+    _, t_f = time_calls(fused, sets, steps, warmup, stream)
+    _, t_u = time_calls(unfused, sets, steps, warmup, stream)
+    toks = wl.B * wl.T
+    res = {"workload": wl.name, "fused_us": 1e3 * t_f, "host_prepared_then_plain_us": 1e3 * t_u,
+           "fused_tokens_per_s": toks / (t_f / 1e3), "input_sets": n_sets,
+           "fused_alg_gbs": prefill_bytes(wl) / (t_f / 1e3) / 1e9}
+    log(f"fused preparation {wl.name}: {res['fused_us']:.1f} us/call fused, "
+        f"{res['host_prepared_then_plain_us']:.1f} us with separate torch preparation")
+    del sets
+    torch.cuda.empty_cache()
+    return res
+
+
 SEGMENT_SHAPES = ((1, 8, 4096), (1, 1, 16384), (1, 2, 32768), (1, 4, 16384), (2, 2, 8192))
 
 
@@ -341,6 +378,8 @@ def main():
                     help="time budget of the oracle baseline (0 skips it)")
     ap.add_argument("--no-context", action="store_true",
                     help="skip the context timings of the two larger prefill shapes")
+    ap.add_argument("--no-fused-prep", action="store_true",
+                    help="skip the headline prefill with the preparation fused in")
     ap.add_argument("--no-context-parallel", action="store_true",
                     help="skip the per-GPU share of the context-parallel split")
     ap.add_argument("--segment-sweep", action="store_true",
@@ -385,6 +424,9 @@ def main():
             r, _ = bench_prefill(kda, CONFIGS[cid], max(5, args.steps // 10), 2, 1, dev, stream)
             ctx[CONFIGS[cid].name] = r
             torch.cuda.empty_cache()
+    fprep = None
+    if not args.no_fused_prep:
+        fprep = bench_fused_prep(kda, head, args.steps, args.warmup, args.sets, dev, stream)
     kcp = None
     if not args.no_context_parallel:
         kcp = bench_context_parallel(kda, max(5, args.steps // 5), 2, dev, stream)
@@ -417,6 +459,7 @@ def main():
         "prefill_detail": pre,
         "configs": ctx,
         "context_parallel": kcp,
+        "fused_prep": fprep,
         "source_digest": source_digest(),
     }
     if args.cpu_seconds > 0:

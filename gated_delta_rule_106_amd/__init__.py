@@ -67,6 +67,15 @@ def _out_code(dt) -> int:
     raise TypeError(f"out_dtype must be float32 or bfloat16, got {dt}")
 
 
+def _prep_flags(clamp, qk_norm, gate_logits) -> int:
+    f = 0 if clamp else _abi.KDA_FLAG_NO_CLAMP
+    if qk_norm:
+        f |= _abi.KDA_FLAG_QK_L2NORM
+    if gate_logits:
+        f |= _abi.KDA_FLAG_GATE_LOGITS
+    return f
+
+
 def _fwd_args(q, k, v, log_alpha, beta, gate, chunk, clamp, out_dtype):
     B, T, H, Dk = q.shape
     Dv = v.shape[-1]
@@ -99,7 +108,7 @@ def workspace_bytes(B, T, H, D, dtype=torch.bfloat16, chunk=0) -> int:
 
 def chunk_fwd(q, k, v, log_alpha, beta, gate, initial_state=None, output_final_state=False,
               chunk=0, clamp=True, out_dtype=torch.float32, out=None, final_state=None,
-              workspace=None, segment_scan=True):
+              workspace=None, segment_scan=True, qk_norm=False, gate_logits=False):
     """Chunkwise-parallel KDA forward on the current HIP stream.
 
     q, k, log_alpha: [B, T, H, Dk]; v, gate: [B, T, H, Dv]; beta: [B, T, H];
@@ -107,13 +116,17 @@ def chunk_fwd(q, k, v, log_alpha, beta, gate, initial_state=None, output_final_s
     [B, H, Dk, Dv] or None.  Returns (y, final_state or None); y has
     ``out_dtype`` (fp32 by default).  ``segment_scan=False`` keeps one sequential
     pass per (b, h) where the library would otherwise cut few, long sequences
-    into segments (the same result up to rounding).
+    into segments (the same result up to rounding).  ``qk_norm``: q and k are raw
+    projections, L2-normalised per token inside (q also scaled by 1/sqrt(Dk)).
+    ``gate_logits``: ``log_alpha`` holds forget-gate logits x and the kernel uses
+    max(logsigmoid(x), ln 0.0067).
     """
     lib = _abi.load()
     dev = q.device
     if dev.type != "cuda":
         raise ValueError("chunk_fwd needs GPU tensors (the HIP kernels are the only implementation)")
     a = _fwd_args(q, k, v, log_alpha, beta, gate, chunk, clamp, out_dtype)
+    a.flags = _prep_flags(clamp, qk_norm, gate_logits)
     if not segment_scan:
         a.flags |= _abi.KDA_FLAG_NO_SEGMENT_SCAN
     B, T, H, Dk, Dv = a.B, a.T, a.H, a.Dk, a.Dv
@@ -146,7 +159,8 @@ def chunk_fwd(q, k, v, log_alpha, beta, gate, initial_state=None, output_final_s
     return out, (final_state if output_final_state else None)
 
 
-def chunk_summary(k, v, log_alpha, beta, clamp=True, transition=None, offset=None, workspace=None):
+def chunk_summary(k, v, log_alpha, beta, clamp=True, transition=None, offset=None, workspace=None,
+                  qk_norm=False, gate_logits=False):
     """Segment summary of every (b, h) sequence on the current HIP stream.
 
     The T tokens map an incoming state S to ``M @ S + b`` (``M`` the product of the
@@ -168,7 +182,7 @@ def chunk_summary(k, v, log_alpha, beta, clamp=True, transition=None, offset=Non
             raise TypeError("k, v, log_alpha and beta must share one dtype")
     a = _abi.FwdArgs()
     a.B, a.T, a.H, a.Dk, a.Dv, a.dtype = B, T, H, Dk, Dv, code
-    a.flags = 0 if clamp else _abi.KDA_FLAG_NO_CLAMP
+    a.flags = _prep_flags(clamp, qk_norm, gate_logits)
     if transition is None:
         transition = torch.empty((B, H, Dk, Dk), dtype=torch.float32, device=dev)
     if offset is None:
@@ -230,7 +244,7 @@ def combine_states(transition, offset, initial_state=None, segment_states=True, 
 
 
 def decode_step(q, k, v, log_alpha, beta, gate, state, clamp=True, out_dtype=torch.float32,
-                out=None):
+                out=None, qk_norm=False, gate_logits=False):
     """One recurrent KDA token per (b, h) on the current HIP stream.
 
     q, k, log_alpha: [B, H, Dk]; v, gate: [B, H, Dv]; beta: [B, H]; state: fp32
@@ -252,7 +266,7 @@ def decode_step(q, k, v, log_alpha, beta, gate, state, clamp=True, out_dtype=tor
     _check_dev(dict(q=q, k=k, v=v, log_alpha=log_alpha, beta=beta, gate=gate, state=state, out=out), dev)
     a = _abi.DecodeArgs()
     a.B, a.H, a.Dk, a.Dv, a.dtype, a.out_dtype = B, H, Dk, Dv, code, _out_code(out_dtype)
-    a.flags = 0 if clamp else _abi.KDA_FLAG_NO_CLAMP
+    a.flags = _prep_flags(clamp, qk_norm, gate_logits)
     a.q, a.k, a.v = _ptr(q), _ptr(k), _ptr(v)
     a.log_alpha, a.beta, a.gate = _ptr(log_alpha), _ptr(beta), _ptr(gate)
     a.out, a.state = _ptr(out), _ptr(state)

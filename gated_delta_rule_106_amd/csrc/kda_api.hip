@@ -10,6 +10,7 @@
 namespace {
 
 constexpr int kDefaultChunkBf16 = 64;
+constexpr uint32_t kPrepFlags = KDA_FLAG_QK_L2NORM | KDA_FLAG_GATE_LOGITS;
 constexpr int kDefaultChunkF32 = 16;
 
 bool mul_ok(int64_t a, int64_t b, int64_t* out) {
@@ -36,7 +37,7 @@ int check_shape(const kda_fwd_args* a, int* chunk, int64_t* nchunks, int64_t* ca
     if (a->dtype != KDA_F32 && a->dtype != KDA_BF16) return KDA_ERR_UNSUPPORTED;
     if (a->Dk != a->Dv || (a->Dk != 64 && a->Dk != 128)) return KDA_ERR_UNSUPPORTED;
     if (a->out_dtype != KDA_F32 && a->out_dtype != KDA_BF16) return KDA_ERR_UNSUPPORTED;
-    if ((a->flags & ~(KDA_FLAG_NO_CLAMP | KDA_FLAG_NO_SEGMENT_SCAN)) != 0) return KDA_ERR_UNSUPPORTED;
+    if ((a->flags & ~(KDA_FLAG_NO_CLAMP | KDA_FLAG_NO_SEGMENT_SCAN | kPrepFlags)) != 0) return KDA_ERR_UNSUPPORTED;
     const int c = resolve_chunk(a);
     if (!kda::prefill_supported(a->dtype == KDA_BF16, c, (int)a->Dk)) return KDA_ERR_UNSUPPORTED;
     // every element index of every tensor must fit in int64
@@ -114,7 +115,8 @@ int kda_chunk_fwd(const kda_fwd_args* a, hipStream_t stream) {
     if (!has_tokens && !a->final_state) return KDA_OK;
 
     kda::PrepParams pp{a->q, a->k, a->v, a->log_alpha, a->beta, a->workspace,
-                       a->B, a->T, a->H, nc, (a->flags & KDA_FLAG_NO_CLAMP) ? 0 : 1};
+                       a->B, a->T, a->H, nc, (a->flags & KDA_FLAG_NO_CLAMP) ? 0 : 1,
+                       (a->flags & KDA_FLAG_QK_L2NORM) ? 1 : 0, (a->flags & KDA_FLAG_GATE_LOGITS) ? 1 : 0};
     kda::RecurParams rp{a->gate, a->out, a->initial_state, a->final_state, a->workspace,
                         a->B, a->T, a->H, nc, nc, 1, nullptr};
     // the state pass of every segment reads initial_state at its start while the last
@@ -142,7 +144,7 @@ int kda_chunk_summary(const kda_fwd_args* a, float* transition, hipStream_t stre
     int st = check_shape(a, &c, &nc, &cb, &need);
     if (st != KDA_OK) return st;
     if (a->dtype != KDA_BF16 || c != 64) return KDA_ERR_UNSUPPORTED;
-    if (a->flags & ~KDA_FLAG_NO_CLAMP) return KDA_ERR_UNSUPPORTED;
+    if (a->flags & ~(KDA_FLAG_NO_CLAMP | kPrepFlags)) return KDA_ERR_UNSUPPORTED;
     const int64_t units = a->B * a->H;
     if (units == 0) return KDA_OK;
     if (units * (a->Dk / 16) > INT_MAX) return KDA_ERR_SHAPE;  // combine-style grids
@@ -164,7 +166,8 @@ int kda_chunk_summary(const kda_fwd_args* a, float* transition, hipStream_t stre
     // the card builder also forms the query-side blocks of each card, which the summary
     // never reads: k stands in for q
     kda::PrepParams pp{a->k, a->k, a->v, a->log_alpha, a->beta, a->workspace,
-                       a->B, a->T, a->H, nc, (a->flags & KDA_FLAG_NO_CLAMP) ? 0 : 1};
+                       a->B, a->T, a->H, nc, (a->flags & KDA_FLAG_NO_CLAMP) ? 0 : 1,
+                       (a->flags & KDA_FLAG_QK_L2NORM) ? 1 : 0, (a->flags & KDA_FLAG_GATE_LOGITS) ? 1 : 0};
     const hipError_t e = kda::launch_summary64(D, pp, transition, a->final_state, stream);
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
@@ -195,7 +198,7 @@ int kda_decode_step(const kda_decode_args* a, hipStream_t stream) {
     if (a->dtype != KDA_F32 && a->dtype != KDA_BF16) return KDA_ERR_UNSUPPORTED;
     if (a->Dk != a->Dv || (a->Dk != 64 && a->Dk != 128)) return KDA_ERR_UNSUPPORTED;
     if (a->out_dtype != KDA_F32 && a->out_dtype != KDA_BF16) return KDA_ERR_UNSUPPORTED;
-    if ((a->flags & ~KDA_FLAG_NO_CLAMP) != 0 || a->reserved != 0) return KDA_ERR_UNSUPPORTED;
+    if ((a->flags & ~(KDA_FLAG_NO_CLAMP | kPrepFlags)) != 0 || a->reserved != 0) return KDA_ERR_UNSUPPORTED;
     int64_t bh, st;
     if (!mul_ok(a->B, a->H, &bh) || !mul_ok(bh, a->Dk * a->Dv, &st)) return KDA_ERR_SHAPE;
     if (bh > INT_MAX) return KDA_ERR_SHAPE;
@@ -206,7 +209,8 @@ int kda_decode_step(const kda_decode_args* a, hipStream_t stream) {
     for (const void* p : req)
         if (!aligned16(p)) return KDA_ERR_ALIGN;
     kda::DecodeParams p{a->q, a->k, a->v, a->log_alpha, a->beta, a->gate, a->out, a->state,
-                        bh, (a->flags & KDA_FLAG_NO_CLAMP) ? 0 : 1};
+                        bh, (a->flags & KDA_FLAG_NO_CLAMP) ? 0 : 1, (a->flags & KDA_FLAG_QK_L2NORM) ? 1 : 0,
+                        (a->flags & KDA_FLAG_GATE_LOGITS) ? 1 : 0};
     const hipError_t e =
         kda::launch_decode(a->dtype == KDA_BF16, a->out_dtype == KDA_BF16, (int)a->Dk, p, stream);
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;

@@ -200,7 +200,11 @@ __device__ __forceinline__ constexpr int64_t frag_piece(int ct, int u, int hf) {
 // ---------------------------------------------------------------------------
 // kernel 1: one update card per workgroup.  Wave A owns the 16-token tile A of the
 // chunk; everything that depends on A is resolved at compile time.
-template <int D, int A>
+// MODE bit 0: raw q, k (per-token L2 normalisation); bit 1: log_alpha holds forget
+// logits.  Compile-time, so the decay loop of the plain mode carries no extra work.
+constexpr int kModeQkNorm = 1, kModeLogits = 2;
+
+template <int D, int A, int MODE>
 __device__ __forceinline__ void prep_tile(const PrepParams& p, unsigned char* smem) {
     using L = PrepL<D>;
     using CD = Card<D>;
@@ -221,6 +225,7 @@ __device__ __forceinline__ void prep_tile(const PrepParams& p, unsigned char* sm
     const int rl = 16 * A + m16;  // this lane's token within the chunk
     const int64_t NC = p.NC, T = p.T, H = p.H;
     const bool clamp = p.clamp != 0;
+    constexpr bool logits = (MODE & kModeLogits) != 0, qk_norm = (MODE & kModeQkNorm) != 0;
 
     // raw inputs of token rl: per 32-channel block kb, the 8 bf16 channels 32 kb + 8 g4 .. +7
     // (16 bytes; the four lane groups of a token cover 64 contiguous bytes of its row)
@@ -264,8 +269,33 @@ __device__ __forceinline__ void prep_tile(const PrepParams& p, unsigned char* sm
     fetch(item);
     const bool valid = (item % NC) * C + rl < T;  // tokens past the end are identity tokens
     if (!valid) {  // all of their inputs count as zero (log alpha 0: no decay)
+        // a forget-gate logit of +inf (bf16 0x7f80) has log-sigmoid 0
+        constexpr uint32_t la0 = logits ? 0x7f807f80u : 0u;
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) rla[kb] = rk[kb] = rq[kb] = rv[kb] = u32x4{0u, 0u, 0u, 0u};
+        for (int kb = 0; kb < KB; ++kb) {
+            rk[kb] = rq[kb] = rv[kb] = u32x4{0u, 0u, 0u, 0u};
+            rla[kb] = u32x4{la0, la0, la0, la0};
+        }
+    }
+    // per-token L2 normalisation of raw q and k: the four lane groups of a token hold
+    // its channels; factors stay 1 for inputs that arrive normalised
+    float ks = 1.f, qs = 1.f;
+    if constexpr (qk_norm) {
+        float sk = 0.f, sq = 0.f;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const float kf = elem(rk[kb], j), qf = elem(rq[kb], j);
+                sk += kf * kf;
+                sq += qf * qf;
+            }
+        sk += __shfl_xor(sk, 16);
+        sq += __shfl_xor(sq, 16);
+        sk += __shfl_xor(sk, 32);
+        sq += __shfl_xor(sq, 32);
+        ks = inv_norm(sk);
+        qs = inv_norm(sq) * (1.0f / __builtin_sqrtf((float)D));
     }
     unsigned char* card = static_cast<unsigned char*>(p.ws) + item * CD::BYTES;
     const float beta_mine = valid ? bf16_bits_to_float(static_cast<uint16_t>(rbeta)) : 0.f;
@@ -279,13 +309,19 @@ __device__ __forceinline__ void prep_tile(const PrepParams& p, unsigned char* sm
         half8 v16;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            const float la = elem(rla[kb], j);
+            const float x = elem(rla[kb], j);
+            float la = x;
+            if constexpr (logits) la = log_sigmoid(x);
             const float l = (clamp ? __builtin_amdgcn_fmed3f(la, kLogAlphaMin, 0.f) : la) * kLog2e;
             const float P = row_scan16(l);      // log2 decay from the tile start, inclusive
             const float E = fast_exp2(P);       // <= 1
             const float Einv = fast_exp2(-P);   // >= 1, < 2^116 under the floor
             const float Et = row_last(E);       // decay over the whole tile
-            const float kf = elem(rk[kb], j), qf = elem(rq[kb], j);
+            float kf = elem(rk[kb], j), qf = elem(rq[kb], j);
+            if constexpr (qk_norm) {
+                kf *= ks;
+                qf *= qs;
+            }
             const float KR = kf * E, QR = qf * E, KC = kf * Einv;
             // K-step (kb, j): lane group g4 supplies channel 32 kb + 8 g4 + j to both operands
             accA = mma_f32_k4(KR, KC, accA);
@@ -510,15 +546,15 @@ __device__ __forceinline__ void prep_tile(const PrepParams& p, unsigned char* sm
     }
 }
 
-template <int D>
+template <int D, int MODE>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void kda_prep64_kernel(PrepParams p) {
     extern __shared__ __align__(16) unsigned char smem[];
     switch (__builtin_amdgcn_readfirstlane(threadIdx.x >> 6)) {
-        case 0: prep_tile<D, 0>(p, smem); break;
-        case 1: prep_tile<D, 1>(p, smem); break;
-        case 2: prep_tile<D, 2>(p, smem); break;
-        default: prep_tile<D, 3>(p, smem); break;
+        case 0: prep_tile<D, 0, MODE>(p, smem); break;
+        case 1: prep_tile<D, 1, MODE>(p, smem); break;
+        case 2: prep_tile<D, 2, MODE>(p, smem); break;
+        default: prep_tile<D, 3, MODE>(p, smem); break;
     }
 }
 
@@ -1068,7 +1104,11 @@ static hipError_t launch_d(const PrepParams& pp, const RecurParams& rp0, hipStre
     const int64_t units = rp0.B * rp0.H;
     RecurParams rp = rp0;
     if (pp.NC > 0) {
-        auto kp = kda_prep64_kernel<D>;
+        const int mode = (pp.qk_norm ? kModeQkNorm : 0) | (pp.logits ? kModeLogits : 0);
+        auto kp = mode == 0   ? kda_prep64_kernel<D, 0>
+                  : mode == 1 ? kda_prep64_kernel<D, 1>
+                  : mode == 2 ? kda_prep64_kernel<D, 2>
+                              : kda_prep64_kernel<D, 3>;
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kp),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)LP::TOTAL);
         if (e != hipSuccess) return e;

@@ -17,6 +17,8 @@ struct DecodeParams {
     float* state;
     int64_t units;  // B * H
     int clamp;
+    int qk_norm;  // q, k are raw: k / |k|, q / (|q| sqrt(D))
+    int logits;   // la holds forget-gate logits: log alpha = logsigmoid(la)
 };
 
 hipError_t launch_decode(int dtype_bf16, int out_bf16, int D, const DecodeParams& p,

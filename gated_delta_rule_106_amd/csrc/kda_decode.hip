@@ -33,6 +33,7 @@ __global__ __launch_bounds__(256) void kda_decode_kernel(DecodeParams p) {
     __shared__ float s_red_r[RG][DV], s_red_o[RG][DV];
     __shared__ float s_u[DV];
     __shared__ float s_qk;
+    __shared__ float s_ss[2][DK / 64 > 0 ? DK / 64 : 1];  // per-wave partial |q|^2, |k|^2
 
     const int64_t unit = blockIdx.x;
     if (unit >= p.units) return;
@@ -42,10 +43,23 @@ __global__ __launch_bounds__(256) void kda_decode_kernel(DecodeParams p) {
     const raw_t* la = static_cast<const raw_t*>(p.la);
 
     if (tid < DK) {
-        s_q[tid] = In::load(q, unit * DK + tid);
-        s_k[tid] = In::load(k, unit * DK + tid);
-        const float l = clamp_log_alpha(In::load(la, unit * DK + tid), p.clamp != 0);
+        const float qv = In::load(q, unit * DK + tid), kv = In::load(k, unit * DK + tid);
+        s_q[tid] = qv;
+        s_k[tid] = kv;
+        const float l = log_alpha_in(In::load(la, unit * DK + tid), p.logits != 0, p.clamp != 0);
         s_a[tid] = fast_exp2(l * kLog2e);
+        if (p.qk_norm) {  // squared norms of raw q and k, one partial per wave
+            float sq = qv * qv, sk = kv * kv;
+#pragma unroll
+            for (int off = 32; off > 0; off >>= 1) {
+                sq += __shfl_xor(sq, off);
+                sk += __shfl_xor(sk, off);
+            }
+            if ((tid & 63) == 0) {
+                s_ss[0][tid >> 6] = sq;
+                s_ss[1][tid >> 6] = sk;
+            }
+        }
     }
 
     const int cg = tid % COLS, rg = tid / COLS;
@@ -58,20 +72,33 @@ __global__ __launch_bounds__(256) void kda_decode_kernel(DecodeParams p) {
     }
     __syncthreads();
 
+    // normalisation factors of raw q and k (1 for inputs that arrive normalised)
+    float qs = 1.f, ks = 1.f;
+    if (p.qk_norm) {
+        float sq = 0.f, sk = 0.f;
+#pragma unroll
+        for (int w = 0; w < (DK / 64 > 0 ? DK / 64 : 1); ++w) {
+            sq += s_ss[0][w];
+            sk += s_ss[1][w];
+        }
+        qs = inv_norm(sq) * (1.0f / __builtin_sqrtf((float)DK));
+        ks = inv_norm(sk);
+    }
+
     // q . k on wave 0
     if (tid < 64) {
         float part = 0.f;
         for (int c = tid; c < DK; c += 64) part += s_q[c] * s_k[c];
 #pragma unroll
         for (int off = 32; off > 0; off >>= 1) part += __shfl_xor(part, off);
-        if (tid == 0) s_qk = part;
+        if (tid == 0) s_qk = part * (qs * ks);
     }
 
     float4 pr = {0.f, 0.f, 0.f, 0.f}, po = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
         const int r = rg * RPT + i;
-        const float a = s_a[r], kr = s_k[r], qr = s_q[r];
+        const float a = s_a[r], kr = s_k[r] * ks, qr = s_q[r] * qs;
         s[i].x *= a; s[i].y *= a; s[i].z *= a; s[i].w *= a;
         pr.x += s[i].x * kr; pr.y += s[i].y * kr; pr.z += s[i].z * kr; pr.w += s[i].w * kr;
         po.x += s[i].x * qr; po.y += s[i].y * qr; po.z += s[i].z * qr; po.w += s[i].w * qr;
@@ -97,7 +124,7 @@ __global__ __launch_bounds__(256) void kda_decode_kernel(DecodeParams p) {
     const float4 u4 = *reinterpret_cast<const float4*>(&s_u[4 * cg]);
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
-        const float kr = s_k[rg * RPT + i];
+        const float kr = s_k[rg * RPT + i] * ks;
         s[i].x += kr * u4.x; s[i].y += kr * u4.y; s[i].z += kr * u4.z; s[i].w += kr * u4.w;
         const floatx4 v = {s[i].x, s[i].y, s[i].z, s[i].w};
         __builtin_nontemporal_store(v, reinterpret_cast<floatx4*>(st) + (rg * RPT + i) * COLS + cg);

@@ -101,4 +101,31 @@ __device__ __forceinline__ float clamp_log_alpha(float l, bool clamp) {
     return clamp ? fminf(fmaxf(l, kLogAlphaMin), 0.0f) : l;
 }
 
+// log(1 + e) for e in [0, 1] by Kahan's correction (D. Goldberg, "What every computer
+// scientist should know about floating-point arithmetic", 1991, Theorem 4): with
+// u = fl(1 + e), log1p(e) = e when u == 1, else log(u) * e / (u - 1), which cancels the
+// rounding of 1 + e.  log(u) from the hardware log2 (v_log_f32).
+__device__ __forceinline__ float log1p_unit(float e) {
+    const float u = 1.0f + e;
+    const float d = u - 1.0f;
+    const float l = __builtin_amdgcn_logf(u) * 0.6931471805599453f;  // ln(u)
+    return d == 0.0f ? e : l * (e * __builtin_amdgcn_rcpf(d));
+}
+
+// log(sigmoid(x)) = min(x, 0) - log(1 + e^-|x|): the log retention of a forget-gate
+// logit x, finite for every finite x, 0 at x = +inf; the small decays of large logits
+// (about -e^-x) keep their relative accuracy.
+__device__ __forceinline__ float log_sigmoid(float x) {
+    return fminf(x, 0.0f) - log1p_unit(fast_exp2(-fabsf(x) * kLog2e));
+}
+
+// log(alpha) from the log_alpha input: the value itself or, for forget-gate logits,
+// its log-sigmoid; then the clamp.
+__device__ __forceinline__ float log_alpha_in(float x, bool logits, bool clamp) {
+    return clamp_log_alpha(logits ? log_sigmoid(x) : x, clamp);
+}
+
+// 1 / max(sqrt(ss), 1e-12): the L2 normalisation factor of a vector with squared norm ss
+__device__ __forceinline__ float inv_norm(float ss) { return rsqrtf(fmaxf(ss, 1e-24f)); }
+
 }  // namespace kda

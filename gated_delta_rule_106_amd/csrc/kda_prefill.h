@@ -15,6 +15,8 @@ struct PrepParams {
     void* ws;
     int64_t B, T, H, NC;
     int clamp;
+    int qk_norm;  // q, k are raw: k / |k|, q / (|q| sqrt(D)) per token
+    int logits;   // la holds forget-gate logits: log alpha = logsigmoid(la)
 };
 
 struct RecurParams {

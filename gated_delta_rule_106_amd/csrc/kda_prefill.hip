@@ -105,7 +105,8 @@ struct PrepLds {
     static constexpr int64_t OFF_EA = OFF_ML + align16((int64_t)NSUB * D * 4);   // e^{m_a}
     static constexpr int64_t OFF_GE = OFF_EA + align16((int64_t)NSUB * D * 4);   // log2 g_C
     static constexpr int64_t OFF_BT = OFF_GE + align16((int64_t)D * 4);          // beta
-    static constexpr int64_t TOTAL = OFF_BT + align16((int64_t)C * 4);
+    static constexpr int64_t OFF_NS = OFF_BT + align16((int64_t)C * 4);          // q, k scales [2][C]
+    static constexpr int64_t TOTAL = OFF_NS + align16((int64_t)2 * C * 4);
     static_assert(TOTAL <= 160 * 1024, "prep LDS budget");
 };
 
@@ -146,9 +147,33 @@ void kda_prep_kernel(PrepParams p) {
     const raw_t* gv = static_cast<const raw_t*>(p.v);
     const raw_t* gla = static_cast<const raw_t*>(p.la);
     const raw_t* gbeta = static_cast<const raw_t*>(p.beta);
-    const bool clamp = p.clamp != 0;
+    const bool clamp = p.clamp != 0, logits = p.logits != 0;
+    float* NS = reinterpret_cast<float*>(smem + L::OFF_NS);  // [0][r]: q scale, [1][r]: k scale
     // token (b, t, h) row offset in a [B, T, H, D] tensor
     auto row = [&](int64_t t) { return ((int64_t)b * T + t) * H + h; };
+
+    // per-token L2 normalisation factors of raw q and k (one wave per token, visible
+    // after the first barrier below; 1 for inputs that arrive normalised)
+    for (int r = wave; r < C; r += NW) {
+        const int64_t t = t0 + r;
+        float sq = 0.f, sk = 0.f;
+        if (p.qk_norm && t < T) {
+            for (int cc = lane; cc < D; cc += 64) {
+                const float qv = In::load(gq, row(t) * D + cc), kv = In::load(gk, row(t) * D + cc);
+                sq += qv * qv;
+                sk += kv * kv;
+            }
+#pragma unroll
+            for (int off = 32; off > 0; off >>= 1) {
+                sq += __shfl_xor(sq, off);
+                sk += __shfl_xor(sk, off);
+            }
+        }
+        if (lane == 0) {
+            NS[r] = p.qk_norm ? inv_norm(sq) * (1.0f / __builtin_sqrtf((float)D)) : 1.f;
+            NS[C + r] = p.qk_norm ? inv_norm(sk) : 1.f;
+        }
+    }
 
     // ---- phase 0: cumulative log-decay (log2 units), references, rescaled tiles
     constexpr int TPC = L::TPC;        // threads per channel
@@ -162,7 +187,7 @@ void kda_prep_kernel(PrepParams p) {
         for (int j = 0; j < TPT; ++j) {
             const int64_t t = t0 + r0 + j;
             float l = 0.f;
-            if (t < T) l = clamp_log_alpha(In::load(gla, row(t) * D + c), clamp);
+            if (t < T) l = log_alpha_in(In::load(gla, row(t) * D + c), logits, clamp);
             acc += l * kLog2e;
             gl[j] = acc;
         }
@@ -195,8 +220,8 @@ void kda_prep_kernel(PrepParams p) {
         float kk = 0.f, qq = 0.f;
         raw_t vv = In::from_float(0.f);
         if (t < T) {
-            kk = In::load(gk, row(t) * D + c);
-            qq = In::load(gq, row(t) * D + c);
+            kk = In::load(gk, row(t) * D + c) * NS[C + r];
+            qq = In::load(gq, row(t) * D + c) * NS[r];
             vv = gv[row(t) * D + c];
         }
         XF[r * SX + c] = kk * F;

@@ -76,6 +76,18 @@ extern "C" {
  * kda_chunk_fwd).  The result is the same up to rounding; the flag exists for
  * comparisons. */
 #define KDA_FLAG_NO_SEGMENT_SCAN 2u
+/* Fused preprocessing (page "3T models are no longer magic", section "FlashKDA":
+ * the preparation step includes the forget-gate computation and Q and K
+ * normalisation), accepted by kda_chunk_fwd, kda_chunk_summary and
+ * kda_decode_step:
+ *  KDA_FLAG_QK_L2NORM: q and k are raw projections; every token's k is divided
+ *    by its L2 norm and q by its L2 norm times sqrt(Dk) (norms below 1e-12
+ *    count as 1e-12), computed in fp32 from the given values.
+ *  KDA_FLAG_GATE_LOGITS: log_alpha holds forget-gate logits x; the log
+ *    retention is logsigmoid(x) = -log(1 + e^-x), then clamped as usual (so
+ *    log alpha = max(logsigmoid(x), ln 0.0067) by default). */
+#define KDA_FLAG_QK_L2NORM 4u
+#define KDA_FLAG_GATE_LOGITS 8u
 
 /*
  * Arguments of kda_chunk_fwd.
@@ -144,8 +156,9 @@ int kda_chunk_fwd(const kda_fwd_args *a, hipStream_t stream);
  *   transition: fp32 [B, H, Dk, Dk], receives M (required).
  *   a->final_state: fp32 [B, H, Dk, Dv], receives b (required).
  *   The two outputs must not overlap each other, the inputs or the workspace.
- *   Supported: bf16 inputs, chunk 0 or 64, Dk == Dv in {64, 128}; flags other
- *   than KDA_FLAG_NO_CLAMP return KDA_ERR_UNSUPPORTED.  The workspace that
+ *   Supported: bf16 inputs, chunk 0 or 64, Dk == Dv in {64, 128};
+ *   KDA_FLAG_NO_CLAMP, KDA_FLAG_QK_L2NORM and KDA_FLAG_GATE_LOGITS apply as in
+ *   kda_chunk_fwd, KDA_FLAG_NO_SEGMENT_SCAN returns KDA_ERR_UNSUPPORTED.  The workspace that
  *   kda_chunk_fwd_workspace_size() reports for the same *a is sufficient.
  *   T == 0 gives M = I and b = 0.  M and b are accumulated in fp32 from fp16
  *   MFMA operands, like the state of kda_chunk_fwd.

@@ -123,6 +123,42 @@ def make_inputs(wl: Workload, seed: int | None = None) -> dict:
     return out
 
 
+def make_raw_inputs(wl: Workload, seed: int | None = None) -> dict:
+    """Raw projections for the fused-preprocessing path: the same sampling as
+    ``make_inputs`` up to, but not including, the per-token normalisation of q and
+    k and the log-sigmoid of the forget logits.  Each token's q and k are also
+    multiplied by a random factor in [0.1, 10) (projections come at any size).
+    log_alpha holds the forget-gate logits x ~ N(mu_alpha, 1); channels pinned at
+    the floor get x = -12 (log-sigmoid about -12, below ln 0.0067)."""
+    gen = torch.Generator(device="cpu")
+    gen.manual_seed(wl.seed if seed is None else seed)
+    B, H, T, Dk, Dv = wl.B, wl.H, wl.T, wl.Dk, wl.Dv
+    lead = (B, H) if wl.kind == "decode" else (B, T, H)
+    q = _normal(gen, lead + (Dk,))
+    k = _normal(gen, lead + (Dk,))
+    v = _normal(gen, lead + (Dv,))
+    beta = torch.sigmoid(_normal(gen, lead, mu=wl.beta_mu))
+    x = _normal(gen, lead + (Dk,), mu=wl.alpha_mu)
+    if wl.floor_frac > 0.0:
+        n_floor = int(round(wl.floor_frac * Dk))
+        for h in range(H):
+            perm = torch.randperm(Dk, generator=gen)[:n_floor]
+            x[..., h, perm] = -12.0
+    gate = _normal(gen, lead + (Dv,))
+    state = _normal(gen, (B, H, Dk, Dv), std=0.02) if wl.init_state else None
+    fq = torch.rand(lead + (1,), generator=gen) * 9.9 + 0.1
+    fk = torch.rand(lead + (1,), generator=gen) * 9.9 + 0.1
+    dt = wl.torch_dtype
+    out = dict(q=(q * fq).to(dt).contiguous(), k=(k * fk).to(dt).contiguous(), v=v.to(dt).contiguous(),
+               log_alpha=x.to(dt).contiguous(), beta=beta.to(dt).contiguous(),
+               gate=gate.to(dt).contiguous())
+    if wl.kind == "decode":
+        out["state"] = state if state is not None else torch.zeros(B, H, Dk, Dv)
+    else:
+        out["initial_state"] = state
+    return out
+
+
 def small(wl: Workload, **kw) -> Workload:
     """A reduced copy of a workload (same recipe) for parity at oracle-friendly sizes."""
     return wl.scaled(**kw)

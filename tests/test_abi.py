@@ -122,8 +122,8 @@ def test_workspace_size_includes_segment_summaries(lib):
     (lambda a: setattr(a, "dtype", 7), _abi.KDA_ERR_UNSUPPORTED),
     (lambda a: setattr(a, "chunk", 48), _abi.KDA_ERR_UNSUPPORTED),
     (lambda a: setattr(a, "chunk", 128), _abi.KDA_ERR_UNSUPPORTED),
-    (lambda a: setattr(a, "flags", 4), _abi.KDA_ERR_UNSUPPORTED),
-    (lambda a: setattr(a, "flags", 3), _abi.KDA_ERR_WORKSPACE),  # both known flags: accepted
+    (lambda a: setattr(a, "flags", 16), _abi.KDA_ERR_UNSUPPORTED),
+    (lambda a: setattr(a, "flags", 15), _abi.KDA_ERR_WORKSPACE),  # every known flag: accepted
     (lambda a: setattr(a, "out_dtype", 2), _abi.KDA_ERR_UNSUPPORTED),
     (lambda a: setattr(a, "T", 2 ** 62), _abi.KDA_ERR_SHAPE),
     (lambda a: setattr(a, "q", None), _abi.KDA_ERR_NULL),
@@ -159,7 +159,9 @@ def _good_dec():
     (lambda a: setattr(a, "H", -1), _abi.KDA_ERR_SHAPE),
     (lambda a: setattr(a, "Dv", 64), _abi.KDA_ERR_UNSUPPORTED),
     (lambda a: setattr(a, "dtype", 3), _abi.KDA_ERR_UNSUPPORTED),
-    (lambda a: setattr(a, "flags", 8), _abi.KDA_ERR_UNSUPPORTED),
+    (lambda a: setattr(a, "flags", 16), _abi.KDA_ERR_UNSUPPORTED),
+    (lambda a: setattr(a, "flags", 2), _abi.KDA_ERR_UNSUPPORTED),  # no segments in a decode step
+    (lambda a: (setattr(a, "flags", 13), setattr(a, "state", None)), _abi.KDA_ERR_NULL),  # flags accepted
     (lambda a: setattr(a, "reserved", 1), _abi.KDA_ERR_UNSUPPORTED),
     (lambda a: setattr(a, "out_dtype", -1), _abi.KDA_ERR_UNSUPPORTED),
     (lambda a: setattr(a, "state", None), _abi.KDA_ERR_NULL),
@@ -192,6 +194,8 @@ def _good_sum():
     (lambda a: setattr(a, "dtype", _abi.KDA_F32), _abi.KDA_ERR_UNSUPPORTED),
     (lambda a: setattr(a, "chunk", 32), _abi.KDA_ERR_UNSUPPORTED),
     (lambda a: setattr(a, "flags", _abi.KDA_FLAG_NO_SEGMENT_SCAN), _abi.KDA_ERR_UNSUPPORTED),
+    (lambda a: setattr(a, "flags", 16), _abi.KDA_ERR_UNSUPPORTED),
+    (lambda a: setattr(a, "flags", 13), _abi.KDA_ERR_WORKSPACE),  # clamp off, q/k norm, logits: accepted
     (lambda a: setattr(a, "Dk", 96), _abi.KDA_ERR_UNSUPPORTED),
     (lambda a: setattr(a, "T", -1), _abi.KDA_ERR_SHAPE),
     (lambda a: setattr(a, "final_state", None), _abi.KDA_ERR_NULL),
