@@ -11,7 +11,9 @@ times the single-token decode step on B=512, H=32 (fp32 128x128 state per head,
 updated in place) and reports it in the ``decode`` object; the two larger
 prefill shapes (B2 H32 T8192 with state in/out, B1 H16 T65536 with 30 % of the
 key channels at the retention floor) are timed for context under ``configs``,
-``fused_prep`` times the headline on raw q, k and forget logits with the
+``varlen`` times a mixed-length batch through the variable-length call (with
+and without state snapshots) against padding it to one length, ``fused_prep``
+times the headline on raw q, k and forget logits with the
 preparation fused into the card builder, and ``context_parallel`` times one GPU's share of an 8-way split along T of the
 floor-stress workload (segment summary, ordered combination, re-run).
 
@@ -341,6 +343,50 @@ def bench_fused_prep(kda, wl, steps, warmup, n_sets, dev, stream):
     return res
 
 
+def bench_varlen(kda, steps, warmup, dev, stream, N=32, H=8, snapshot_every=512):
+    """A mixed-length batch (N sequences, lengths log-uniform in [64, 8192), seeded; the
+    headline's distributions and head size) through the variable-length call, with and
+    without state snapshots every snapshot_every tokens, against padding every sequence
+    to the longest and running the batch call."""
+    import torch
+    from kda_workloads import CONFIGS, make_inputs
+    g = torch.Generator().manual_seed(7)
+    lengths = [int(64 * 2 ** (7 * float(u))) for u in torch.rand(N, generator=g)]
+    rows, Tmax = sum(lengths), max(lengths)
+    wl = CONFIGS[1].scaled(B=1, H=H, T=rows)
+    x = {k: v[0] for k, v in to_dev(make_inputs(wl, seed=11), dev).items() if v is not None}
+    cu = torch.tensor([0] + list(torch.tensor(lengths).cumsum(0)), dtype=torch.int64, device=dev)
+    out = torch.empty((rows, H, wl.Dv), dtype=torch.float32, device=dev)
+    pad = {k: torch.zeros((N, Tmax) + tuple(x[k].shape[1:]), dtype=x[k].dtype, device=dev) for k in KEYS}
+    for i, L in enumerate(lengths):
+        o = int(cu[i])
+        for k in KEYS:
+            pad[k][i, :L] = x[k][o:o + L]
+    pws = torch.empty(kda.workspace_bytes(N, Tmax, H, wl.Dk), dtype=torch.uint8, device=dev)
+    pout = torch.empty((N, Tmax, H, wl.Dv), dtype=torch.float32, device=dev)
+
+    def var(_):
+        kda.chunk_fwd_varlen(*(x[k] for k in KEYS), cu, out=out)
+
+    def var_snap(_):
+        kda.chunk_fwd_varlen(*(x[k] for k in KEYS), cu, out=out, snapshot_every=snapshot_every)
+
+    def padded(_):
+        kda.chunk_fwd(*(pad[k] for k in KEYS), out=pout, workspace=pws)
+    _, t_v = time_calls(var, [None], steps, warmup, stream)
+    _, t_s = time_calls(var_snap, [None], steps, warmup, stream)
+    _, t_p = time_calls(padded, [None], steps, warmup, stream)
+    res = {"sequences": N, "H": H, "d": wl.Dk, "tokens": rows, "longest": Tmax,
+           "varlen_us": 1e3 * t_v, "varlen_snapshots_us": 1e3 * t_s, "snapshot_every": snapshot_every,
+           "padded_batch_us": 1e3 * t_p, "varlen_tokens_per_s": rows / (t_v / 1e3),
+           "note": "event time per call including the binding's allocations of outputs and workspace"}
+    log(f"varlen: {N} sequences, {rows} tokens (longest {Tmax}): {res['varlen_us']:.1f} us, with snapshots every "
+        f"{snapshot_every}: {res['varlen_snapshots_us']:.1f} us, padded batch {res['padded_batch_us']:.1f} us")
+    del x, pad, pws, pout, out
+    torch.cuda.empty_cache()
+    return res
+
+
 SEGMENT_SHAPES = ((1, 8, 4096), (1, 1, 16384), (1, 2, 32768), (1, 4, 16384), (2, 2, 8192))
 
 
@@ -378,6 +424,8 @@ def main():
                     help="time budget of the oracle baseline (0 skips it)")
     ap.add_argument("--no-context", action="store_true",
                     help="skip the context timings of the two larger prefill shapes")
+    ap.add_argument("--no-varlen", action="store_true",
+                    help="skip the mixed-length batch (variable-length call, snapshots)")
     ap.add_argument("--no-fused-prep", action="store_true",
                     help="skip the headline prefill with the preparation fused in")
     ap.add_argument("--no-context-parallel", action="store_true",
@@ -427,6 +475,9 @@ def main():
     fprep = None
     if not args.no_fused_prep:
         fprep = bench_fused_prep(kda, head, args.steps, args.warmup, args.sets, dev, stream)
+    vlen = None
+    if not args.no_varlen:
+        vlen = bench_varlen(kda, max(5, args.steps // 5), 2, dev, stream)
     kcp = None
     if not args.no_context_parallel:
         kcp = bench_context_parallel(kda, max(5, args.steps // 5), 2, dev, stream)
@@ -460,6 +511,7 @@ def main():
         "configs": ctx,
         "context_parallel": kcp,
         "fused_prep": fprep,
+        "varlen": vlen,
         "source_digest": source_digest(),
     }
     if args.cpu_seconds > 0:

@@ -23,7 +23,7 @@ import torch
 
 from . import _abi
 
-__all__ = ["chunk_fwd", "chunk_summary", "combine_states", "decode_step", "workspace_bytes",
+__all__ = ["chunk_fwd", "chunk_fwd_varlen", "snapshot_slot", "chunk_summary", "combine_states", "decode_step", "workspace_bytes",
            "library_path", "KDAError"]
 
 
@@ -157,6 +157,76 @@ def chunk_fwd(q, k, v, log_alpha, beta, gate, initial_state=None, output_final_s
     if rc != _abi.KDA_OK:
         raise KDAError(rc, "kda_chunk_fwd")
     return out, (final_state if output_final_state else None)
+
+
+def snapshot_slot(cu_seqlens, i: int, k: int, snapshot_every: int) -> int:
+    """Slot of the k-th snapshot of sequence i in ``chunk_fwd_varlen``'s snapshot tensor
+    (host arithmetic on well-formed offsets): start_i // P + i + k."""
+    return int(cu_seqlens[i]) // snapshot_every + i + k
+
+
+def chunk_fwd_varlen(q, k, v, log_alpha, beta, gate, cu_seqlens, initial_state=None,
+                     output_final_state=False, snapshot_every=0, clamp=True, out_dtype=torch.float32,
+                     qk_norm=False, gate_logits=False, out=None, workspace=None):
+    """Variable-length batch on the current HIP stream: N sequences packed along the
+    rows of q, k, log_alpha [rows, H, Dk], v, gate [rows, H, Dv], beta [rows, H]
+    (bf16), sequence i being rows cu_seqlens[i] .. cu_seqlens[i+1] - 1 (int64 device
+    tensor [N + 1]).  initial_state: fp32 [N, H, Dk, Dv] or None.  With
+    ``snapshot_every`` P > 0 (a multiple of 64) the state after every P tokens of
+    each sequence is returned in an fp32 [rows // P + N, H, Dk, Dv] tensor, the k-th
+    of sequence i in slot ``snapshot_slot(cu_seqlens, i, k, P)``.  Returns
+    (y [rows, H, Dv], final_state or None, snapshots or None); rows outside the
+    sequences are left as they are in ``out``.
+    """
+    lib = _abi.load()
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("chunk_fwd_varlen needs GPU tensors (the HIP kernels are the only implementation)")
+    rows, H, Dk = q.shape
+    Dv = v.shape[-1]
+    if k.shape != q.shape or log_alpha.shape != q.shape or v.shape != (rows, H, Dv) or \
+            gate.shape != (rows, H, Dv) or beta.shape != (rows, H):
+        raise ValueError("q, k, log_alpha must be [rows, H, Dk], v, gate [rows, H, Dv], beta [rows, H]")
+    if cu_seqlens.dtype != torch.int64 or cu_seqlens.dim() != 1 or cu_seqlens.device != dev:
+        raise ValueError("cu_seqlens must be an int64 vector [N + 1] on the same GPU")
+    N = cu_seqlens.numel() - 1
+    code = _dtype_code(q)
+    for t in (k, v, log_alpha, beta, gate):
+        if t.dtype != q.dtype:
+            raise TypeError("q, k, v, log_alpha, beta and gate must share one dtype")
+    if initial_state is not None and (initial_state.dtype != torch.float32 or
+                                      tuple(initial_state.shape) != (N, H, Dk, Dv)):
+        raise ValueError("initial_state must be fp32 [N, H, Dk, Dv]")
+    if out is None:
+        out = torch.empty((rows, H, Dv), dtype=out_dtype, device=dev)
+    final = torch.empty((N, H, Dk, Dv), dtype=torch.float32, device=dev) if output_final_state else None
+    snaps = None
+    if snapshot_every:
+        snaps = torch.empty((rows // snapshot_every + N, H, Dk, Dv), dtype=torch.float32, device=dev)
+    a = _abi.VarlenArgs()
+    a.N, a.rows, a.H, a.Dk, a.Dv = N, rows, H, Dk, Dv
+    a.dtype, a.out_dtype, a.chunk = code, _out_code(out_dtype), 0
+    a.flags = _prep_flags(clamp, qk_norm, gate_logits)
+    a.snapshot_every = int(snapshot_every)
+    n = ctypes.c_size_t(0)
+    rc = lib.kda_chunk_fwd_varlen_workspace_size(ctypes.byref(a), ctypes.byref(n))
+    if rc != _abi.KDA_OK:
+        raise KDAError(rc, "kda_chunk_fwd_varlen_workspace_size")
+    if workspace is None or workspace.numel() < n.value:
+        workspace = torch.empty(max(int(n.value), 16), dtype=torch.uint8, device=dev)
+    _check_dev(dict(q=q, k=k, v=v, log_alpha=log_alpha, beta=beta, gate=gate, out=out,
+                    initial_state=initial_state, final_state=final, snapshots=snaps,
+                    cu_seqlens=cu_seqlens), dev)
+    a.cu_seqlens = _ptr(cu_seqlens)
+    a.q, a.k, a.v = _ptr(q), _ptr(k), _ptr(v)
+    a.log_alpha, a.beta, a.gate, a.out = _ptr(log_alpha), _ptr(beta), _ptr(gate), _ptr(out)
+    a.initial_state, a.final_state, a.snapshots = _ptr(initial_state), _ptr(final), _ptr(snaps)
+    a.workspace, a.workspace_bytes = _ptr(workspace), workspace.numel()
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    rc = lib.kda_chunk_fwd_varlen(ctypes.byref(a), ctypes.c_void_p(stream))
+    if rc != _abi.KDA_OK:
+        raise KDAError(rc, "kda_chunk_fwd_varlen")
+    return out, final, snaps
 
 
 def chunk_summary(k, v, log_alpha, beta, clamp=True, transition=None, offset=None, workspace=None,

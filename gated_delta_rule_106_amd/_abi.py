@@ -21,7 +21,8 @@ KDA_FLAG_QK_L2NORM = 4
 KDA_FLAG_GATE_LOGITS = 8
 
 # every extern "C" entry point of include/kda.h
-EXPORTS = ("kda_chunk_fwd_workspace_size", "kda_chunk_fwd", "kda_chunk_summary",
+EXPORTS = ("kda_chunk_fwd_workspace_size", "kda_chunk_fwd", "kda_chunk_fwd_varlen_workspace_size",
+           "kda_chunk_fwd_varlen", "kda_chunk_summary",
            "kda_combine_states", "kda_decode_step", "kda_status_str", "kda_version")
 
 
@@ -35,6 +36,22 @@ class FwdArgs(ctypes.Structure):
         ("log_alpha", ctypes.c_void_p), ("beta", ctypes.c_void_p), ("gate", ctypes.c_void_p),
         ("out", ctypes.c_void_p), ("initial_state", ctypes.c_void_p),
         ("final_state", ctypes.c_void_p), ("workspace", ctypes.c_void_p),
+        ("workspace_bytes", ctypes.c_size_t),
+    ]
+
+
+class VarlenArgs(ctypes.Structure):
+    _fields_ = [
+        ("N", ctypes.c_int64), ("rows", ctypes.c_int64), ("H", ctypes.c_int64),
+        ("Dk", ctypes.c_int64), ("Dv", ctypes.c_int64),
+        ("dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32),
+        ("chunk", ctypes.c_int32), ("flags", ctypes.c_uint32),
+        ("cu_seqlens", ctypes.c_void_p),
+        ("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+        ("log_alpha", ctypes.c_void_p), ("beta", ctypes.c_void_p), ("gate", ctypes.c_void_p),
+        ("out", ctypes.c_void_p), ("initial_state", ctypes.c_void_p),
+        ("final_state", ctypes.c_void_p), ("snapshot_every", ctypes.c_int64),
+        ("snapshots", ctypes.c_void_p), ("workspace", ctypes.c_void_p),
         ("workspace_bytes", ctypes.c_size_t),
     ]
 
@@ -76,6 +93,11 @@ def load(path: str = LIB_PATH):
     lib.kda_chunk_fwd_workspace_size.restype = ctypes.c_int
     lib.kda_chunk_fwd.argtypes = [ctypes.POINTER(FwdArgs), ctypes.c_void_p]
     lib.kda_chunk_fwd.restype = ctypes.c_int
+    lib.kda_chunk_fwd_varlen_workspace_size.argtypes = [ctypes.POINTER(VarlenArgs),
+                                                        ctypes.POINTER(ctypes.c_size_t)]
+    lib.kda_chunk_fwd_varlen_workspace_size.restype = ctypes.c_int
+    lib.kda_chunk_fwd_varlen.argtypes = [ctypes.POINTER(VarlenArgs), ctypes.c_void_p]
+    lib.kda_chunk_fwd_varlen.restype = ctypes.c_int
     lib.kda_chunk_summary.argtypes = [ctypes.POINTER(FwdArgs), ctypes.c_void_p, ctypes.c_void_p]
     lib.kda_chunk_summary.restype = ctypes.c_int
     lib.kda_combine_states.argtypes = [ctypes.POINTER(CombineArgs), ctypes.c_void_p]

@@ -6,6 +6,7 @@
 #include "kda_decode.h"
 #include "kda_prefill.h"
 #include "kda_segment.h"
+#include "kda_varlen.h"
 
 namespace {
 
@@ -62,9 +63,98 @@ int check_shape(const kda_fwd_args* a, int* chunk, int64_t* nchunks, int64_t* ca
     return KDA_OK;
 }
 
+// Varlen: sizes, dtype, chunk, flags and snapshot interval; fills the workspace
+// layout (cards, then the sequence map).
+struct VarlenLayout {
+    int64_t max_chunks, card, cards_bytes, off_s, off_co, off_soc, total;
+};
+
+int64_t align256(int64_t x) { return (x + 255) / 256 * 256; }
+
+int check_varlen(const kda_varlen_args* a, VarlenLayout* L) {
+    if (!a) return KDA_ERR_NULL;
+    if (a->N < 0 || a->rows < 0 || a->H < 0 || a->Dk <= 0 || a->Dv <= 0 || a->snapshot_every < 0)
+        return KDA_ERR_SHAPE;
+    if (a->dtype != KDA_BF16) return KDA_ERR_UNSUPPORTED;
+    if (a->chunk != 0 && a->chunk != 64) return KDA_ERR_UNSUPPORTED;
+    if (a->Dk != a->Dv || (a->Dk != 64 && a->Dk != 128)) return KDA_ERR_UNSUPPORTED;
+    if (a->out_dtype != KDA_F32 && a->out_dtype != KDA_BF16) return KDA_ERR_UNSUPPORTED;
+    if ((a->flags & ~(KDA_FLAG_NO_CLAMP | KDA_FLAG_NO_SEGMENT_SCAN | kPrepFlags)) != 0) return KDA_ERR_UNSUPPORTED;
+    if (a->snapshot_every % 64 != 0) return KDA_ERR_UNSUPPORTED;
+    int64_t elems, nh, st;
+    if (!mul_ok(a->rows, a->H, &elems) || !mul_ok(elems, a->Dk, &elems) || !mul_ok(a->N, a->H, &nh) ||
+        !mul_ok(nh, a->Dk * a->Dv, &st))
+        return KDA_ERR_SHAPE;
+    if (a->N >= INT32_MAX || a->H > INT_MAX || nh > INT_MAX) return KDA_ERR_SHAPE;
+    const int64_t mc = kda::varlen_max_chunks(a->N, a->rows, 64);
+    const int64_t cb = kda::prefill64_card_bytes((int)a->Dk);
+    int64_t items, cards;
+    if (!mul_ok(mc, a->H, &items) || items > INT_MAX || !mul_ok(items, cb, &cards)) return KDA_ERR_SHAPE;
+    if (a->snapshot_every > 0) {
+        int64_t slots = a->rows / a->snapshot_every + a->N, sb;
+        if (!mul_ok(slots, st / (a->N > 0 ? a->N : 1), &sb)) return KDA_ERR_SHAPE;
+    }
+    L->max_chunks = mc;
+    L->card = cb;
+    L->cards_bytes = align256(cards);
+    L->off_s = L->cards_bytes;
+    L->off_co = L->off_s + align256((a->N + 1) * 8);
+    L->off_soc = L->off_co + align256((a->N + 1) * 8);
+    L->total = L->off_soc + align256(mc * 4);
+    return KDA_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+int kda_chunk_fwd_varlen_workspace_size(const kda_varlen_args* a, size_t* bytes) {
+    if (!a || !bytes) return KDA_ERR_NULL;
+    VarlenLayout L;
+    const int st = check_varlen(a, &L);
+    if (st != KDA_OK) return st;
+    *bytes = (size_t)L.total;
+    return KDA_OK;
+}
+
+int kda_chunk_fwd_varlen(const kda_varlen_args* a, hipStream_t stream) {
+    VarlenLayout L;
+    const int st = check_varlen(a, &L);
+    if (st != KDA_OK) return st;
+    if (a->N == 0 || a->H == 0) return KDA_OK;
+    if (!a->cu_seqlens) return KDA_ERR_NULL;
+    if (a->rows > 0) {
+        const void* req[] = {a->q, a->k, a->v, a->log_alpha, a->beta, a->gate, a->out};
+        for (const void* p : req)
+            if (!p) return KDA_ERR_NULL;
+        for (const void* p : req)
+            if (!aligned16(p)) return KDA_ERR_ALIGN;
+    }
+    if (a->snapshot_every > 0 && !a->snapshots) return KDA_ERR_NULL;
+    const void* opt[] = {a->initial_state, a->final_state, a->snapshots, a->workspace};
+    for (const void* p : opt)
+        if (!aligned16(p)) return KDA_ERR_ALIGN;
+    if ((reinterpret_cast<uintptr_t>(a->cu_seqlens) & 7u) != 0) return KDA_ERR_ALIGN;
+    if (!a->workspace || (int64_t)a->workspace_bytes < L.total) return KDA_ERR_WORKSPACE;
+
+    unsigned char* ws = static_cast<unsigned char*>(a->workspace);
+    kda::VarlenMap m{reinterpret_cast<int64_t*>(ws + L.off_s), reinterpret_cast<int64_t*>(ws + L.off_co),
+                     reinterpret_cast<int32_t*>(ws + L.off_soc)};
+    hipError_t e = kda::launch_varlen_map(m, a->cu_seqlens, a->N, a->rows, 64, stream);
+    if (e != hipSuccess) return KDA_ERR_HIP;
+    kda::PrepParams pp{a->q, a->k, a->v, a->log_alpha, a->beta, a->workspace,
+                       1, a->rows, a->H, 0, (a->flags & KDA_FLAG_NO_CLAMP) ? 0 : 1,
+                       (a->flags & KDA_FLAG_QK_L2NORM) ? 1 : 0, (a->flags & KDA_FLAG_GATE_LOGITS) ? 1 : 0,
+                       m.s, m.co, m.soc, a->N};
+    kda::RecurParams rp{a->gate, a->out, a->initial_state, a->final_state, a->workspace,
+                        a->N, 0, a->H, 0, 0, 1, nullptr};
+    rp.vs = m.s;
+    rp.vco = m.co;
+    rp.snap = a->snapshot_every > 0 ? a->snapshots : nullptr;
+    rp.snap_chunks = a->snapshot_every > 0 ? a->snapshot_every / 64 : 1;
+    e = kda::launch_prefill64((int)a->Dk, a->out_dtype == KDA_BF16, pp, rp, stream);
+    return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
 
 int kda_version(void) { return KDA_VERSION; }
 

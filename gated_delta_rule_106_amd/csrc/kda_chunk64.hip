@@ -50,6 +50,7 @@
 
 #include "kda_device.h"
 #include "kda_prefill.h"
+#include "kda_varlen.h"
 
 namespace kda {
 namespace c64 {
@@ -204,8 +205,16 @@ __device__ __forceinline__ constexpr int64_t frag_piece(int ct, int u, int hf) {
 // logits.  Compile-time, so the decay loop of the plain mode carries no extra work.
 constexpr int kModeQkNorm = 1, kModeLogits = 2;
 
+// Where a card's tokens are: chunk n of a sequence of slen tokens starting at packed
+// row tb, head h; item is the card's index in the workspace.  Formed once per
+// workgroup, outside the four per-tile bodies (the kernel's code is about the size of
+// the instruction cache, so nothing is repeated in them that need not be).
+struct CardPos {
+    int64_t item, n, h, tb, slen;
+};
+
 template <int D, int A, int MODE>
-__device__ __forceinline__ void prep_tile(const PrepParams& p, unsigned char* smem) {
+__device__ __forceinline__ void prep_tile(const PrepParams& p, unsigned char* smem, const CardPos& cp) {
     using L = PrepL<D>;
     using CD = Card<D>;
     constexpr int NCT = D / 16, KB = D / 32, SAB = L::SAB, BLK = L::BLK, SP = L::SP;
@@ -223,7 +232,7 @@ __device__ __forceinline__ void prep_tile(const PrepParams& p, unsigned char* sm
     const int lane = threadIdx.x & 63;
     const int m16 = lane & 15, g4 = lane >> 4;
     const int rl = 16 * A + m16;  // this lane's token within the chunk
-    const int64_t NC = p.NC, T = p.T, H = p.H;
+    const int64_t H = p.H;
     const bool clamp = p.clamp != 0;
     constexpr bool logits = (MODE & kModeLogits) != 0, qk_norm = (MODE & kModeQkNorm) != 0;
 
@@ -231,11 +240,10 @@ __device__ __forceinline__ void prep_tile(const PrepParams& p, unsigned char* sm
     // (16 bytes; the four lane groups of a token cover 64 contiguous bytes of its row)
     u32x4 rq[KB], rk[KB], rv[KB], rla[KB];
     uint32_t rbeta;
-    auto fetch = [&](int64_t it) __attribute__((always_inline)) {
-        const int64_t n = it % NC, unit = it / NC;
-        const int64_t b = unit / H, h = unit % H;
+    const int64_t item = cp.item, n = cp.n, h = cp.h, tb = cp.tb, slen = cp.slen;
+    auto fetch = [&]() __attribute__((always_inline)) {
         const int64_t tok = n * C + rl;
-        const int64_t row = (b * T + (tok < T ? tok : T - 1)) * H + h;  // in bounds; zeroed at use
+        const int64_t row = (tb + (tok < slen ? tok : slen - 1)) * H + h;  // in bounds; zeroed at use
         const uint16_t* gq = static_cast<const uint16_t*>(p.q);
         const uint16_t* gk = static_cast<const uint16_t*>(p.k);
         const uint16_t* gv = static_cast<const uint16_t*>(p.v);
@@ -265,9 +273,8 @@ __device__ __forceinline__ void prep_tile(const PrepParams& p, unsigned char* sm
         *reinterpret_cast<half4*>(base + frag_piece(2 * kb + 1, A >> 1, A & 1) + lane * 8) = pack_h4(t1);
     };
 
-    const int64_t item = blockIdx.x;
-    fetch(item);
-    const bool valid = (item % NC) * C + rl < T;  // tokens past the end are identity tokens
+    fetch();
+    const bool valid = n * C + rl < slen;  // tokens past the end are identity tokens
     if (!valid) {  // all of their inputs count as zero (log alpha 0: no decay)
         // a forget-gate logit of +inf (bf16 0x7f80) has log-sigmoid 0
         constexpr uint32_t la0 = logits ? 0x7f807f80u : 0u;
@@ -550,11 +557,30 @@ template <int D, int MODE>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void kda_prep64_kernel(PrepParams p) {
     extern __shared__ __align__(16) unsigned char smem[];
+    // a variable-length grid is sized for the most chunks the offsets can give
+    CardPos cp;
+    cp.item = blockIdx.x;
+    if (p.vco) {  // variable-length batch: card (co_i + n) H + h
+        const int64_t g = cp.item / p.H;
+        if (g >= p.vco[p.vN]) return;  // the whole group leaves
+        const int64_t i = p.vsoc[g];
+        cp.h = cp.item - g * p.H;
+        cp.n = g - p.vco[i];
+        cp.tb = p.vs[i];
+        cp.slen = p.vs[i + 1] - cp.tb;  // >= 1: the sequence owns this chunk
+    } else {  // B sequences of T tokens: card unit NC + n
+        const int64_t unit = cp.item / p.NC;
+        cp.n = cp.item - unit * p.NC;
+        const int64_t b = unit / p.H;
+        cp.h = unit - b * p.H;
+        cp.tb = b * p.T;
+        cp.slen = p.T;
+    }
     switch (__builtin_amdgcn_readfirstlane(threadIdx.x >> 6)) {
-        case 0: prep_tile<D, 0, MODE>(p, smem); break;
-        case 1: prep_tile<D, 1, MODE>(p, smem); break;
-        case 2: prep_tile<D, 2, MODE>(p, smem); break;
-        default: prep_tile<D, 3, MODE>(p, smem); break;
+        case 0: prep_tile<D, 0, MODE>(p, smem, cp); break;
+        case 1: prep_tile<D, 1, MODE>(p, smem, cp); break;
+        case 2: prep_tile<D, 2, MODE>(p, smem, cp); break;
+        default: prep_tile<D, 3, MODE>(p, smem, cp); break;
     }
 }
 
@@ -650,11 +676,28 @@ void kda_rec64_kernel(RecurParams p) {
     const int64_t units = p.B * p.H, nseg = p.nseg;
     if (useg >= units * nseg) return;  // padding workgroup (the whole group leaves together)
     const int64_t unit = useg / nseg, seg = useg % nseg;
-    const int64_t H = p.H, T = p.T, NC = p.NC;
-    // this workgroup's chunks: [c0, c0 + NL) of its (b, h)
-    const int64_t c0 = seg * p.seg_len, NL = (c0 + p.seg_len < NC ? c0 + p.seg_len : NC) - c0;
+    const int64_t H = p.H;
     const int64_t b = unit / H, h = unit % H;
-    const unsigned char* cards = static_cast<const unsigned char*>(p.ws) + unit * NC * CD::BYTES;
+    // the sequence of this (b, h): T tokens from row tb, NC chunks; its chunk c is card
+    // cbase + c * cstride (B sequences of p.T tokens, or a variable-length batch)
+    int64_t T, NC, tb, cbase, cstride;
+    if (p.vco) {
+        tb = p.vs[b];
+        T = p.vs[b + 1] - tb;
+        NC = (T + C - 1) / C;
+        cbase = p.vco[b] * H + h;
+        cstride = H;
+    } else {
+        T = p.T;
+        NC = p.NC;
+        tb = b * T;
+        cbase = unit * NC;
+        cstride = 1;
+    }
+    // this workgroup's chunks: [c0, c0 + NL) of its (b, h)
+    const int64_t c0 = seg * p.seg_len, NL = p.vco ? NC : (c0 + p.seg_len < NC ? c0 + p.seg_len : NC) - c0;
+    const unsigned char* cards = static_cast<const unsigned char*>(p.ws) + cbase * CD::BYTES;
+    const int64_t cbytes = cstride * CD::BYTES;  // from one chunk's card to the next
     const bool chain = wave < NCONS;
     const bool outw = wave >= NCONS && wave < 2 * NCONS;
     const int pw = wave - 2 * NCONS;                          // producer index (producers only)
@@ -663,7 +706,7 @@ void kda_rec64_kernel(RecurParams p) {
     // O read-out and fp16 state copy of tile t2 for chunk n: buffer n % 2
     auto obuf = [&](int64_t n, int t2) { return reinterpret_cast<float*>(smem + L::OFF_O + ((n & 1) * NCONS + t2) * L::OTILE); };
     auto sbx = [&](int64_t n) { return reinterpret_cast<_Float16*>(smem + L::OFF_X + ((n & 1) * NCONS + cs) * L::SBX); };
-    const int64_t zrow0 = (b * T * H + h) * D, zstride = H * D;  // element offset of (b, t, h, 0)
+    const int64_t zrow0 = (tb * H + h) * D, zstride = H * D;  // element offset of (b, t, h, 0)
     typename Out::raw_t* gy = static_cast<typename Out::raw_t*>(p.out);
     auto slot = [&](int64_t ci) { return smem + (ci % L::NSTAGE) * L::STAGE; };  // local chunk index
 
@@ -764,6 +807,15 @@ void kda_rec64_kernel(RecurParams p) {
             for (int u = 0; u < 2; ++u)
 #pragma unroll
                 for (int ct = 0; ct < NCT; ++ct) S[ct] = mma_f16_k32(kf[ct][u], Ub[u], S[ct]);  // + Kbar^T U
+            if (p.snap && (ci + 1) % p.snap_chunks == 0 && (ci + 1) * C <= T) {
+                // block-granular snapshot: the state after (ci + 1) C tokens of the sequence
+                const int64_t slot = tb / (C * p.snap_chunks) + b + (ci + 1) / p.snap_chunks - 1;
+                float* dst = p.snap + (slot * H + h) * (int64_t)D * D;
+#pragma unroll
+                for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) dst[(16 * ct + 4 * g4 + i) * D + col] = S[ct][i];
+            }
             lds_barrier();  // X(ci): the state copy is visible to the output wave
         }
         lds_barrier();  // X(NL): the output wave forms its last read-out
@@ -779,7 +831,8 @@ void kda_rec64_kernel(RecurParams p) {
         // chunk's in flight while this one is used
         const int nt = grp * NCONS + cs;
         auto load_q = [&](half8 (&qf)[4][KB], half4 (&uo)[4], int64_t c) __attribute__((always_inline)) {
-            const unsigned char* card = cards + (c0 + (c < NL ? c : NL - 1)) * CD::BYTES;
+            if (NL == 0) return;  // an empty sequence has no card to read (nothing is read out)
+            const unsigned char* card = cards + (c0 + (c < NL ? c : NL - 1)) * cbytes;
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt) {
 #pragma unroll
@@ -834,7 +887,7 @@ void kda_rec64_kernel(RecurParams p) {
             auto piece = [&](int64_t ci, int k) __attribute__((always_inline)) {
                 const int j0 = PW + k * NP, j = j0 < L::NPC ? j0 : L::NPC - 1;
                 const int64_t c = c0 + ci;  // chunk of the sequence
-                const unsigned char* card = cards + c * CD::BYTES;
+                const unsigned char* card = cards + c * cbytes;
                 const void* src;
                 if (j < L::NW) {
                     src = card + CD::W + j * 1024 + lane * 16;
@@ -1103,7 +1156,10 @@ static hipError_t launch_d(const PrepParams& pp, const RecurParams& rp0, hipStre
     using LS = SumL<D, kSumTiles>;
     const int64_t units = rp0.B * rp0.H;
     RecurParams rp = rp0;
-    if (pp.NC > 0) {
+    // one workgroup per card, two per CU; a variable-length grid covers the most chunks
+    // its offsets can give (pp.T = packed rows) and the surplus groups leave at once
+    const int64_t items = pp.vco ? varlen_max_chunks(pp.vN, pp.T, C) * pp.H : units * pp.NC;
+    if (items > 0) {
         const int mode = (pp.qk_norm ? kModeQkNorm : 0) | (pp.logits ? kModeLogits : 0);
         auto kp = mode == 0   ? kda_prep64_kernel<D, 0>
                   : mode == 1 ? kda_prep64_kernel<D, 1>
@@ -1112,7 +1168,6 @@ static hipError_t launch_d(const PrepParams& pp, const RecurParams& rp0, hipStre
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kp),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)LP::TOTAL);
         if (e != hipSuccess) return e;
-        const int64_t items = units * pp.NC;  // one workgroup per card, two per CU
         hipLaunchKernelGGL(kp, dim3((unsigned)items), dim3(256), LP::TOTAL, stream, pp);
         e = hipGetLastError();
         if (e != hipSuccess) return e;

@@ -17,6 +17,13 @@ struct PrepParams {
     int clamp;
     int qk_norm;  // q, k are raw: k / |k|, q / (|q| sqrt(D)) per token
     int logits;   // la holds forget-gate logits: log alpha = logsigmoid(la)
+    // variable-length batch (chunk-64 path; NULL: B sequences of T tokens): the map of
+    // kda_varlen.h.  Card of chunk j of sequence i, head h: (co_i + j) H + h; tokens are
+    // rows s_i .. s_{i+1} - 1 of the packed [rows, H, D] tensors.
+    const int64_t* vs;
+    const int64_t* vco;
+    const int32_t* vsoc;
+    int64_t vN;
 };
 
 struct RecurParams {
@@ -39,6 +46,13 @@ struct RecurParams {
     float* sum_b;
     float* sum_m;
     int64_t sum_stride;
+    // variable-length batch (as in PrepParams; B = N, T unused)
+    const int64_t* vs;
+    const int64_t* vco;
+    // block-granular state snapshots: after every snap_chunks chunks of a sequence the
+    // state goes to slot floor(s_i / (64 snap_chunks)) + i + k of snap [slots, H, D, D]
+    float* snap;
+    int64_t snap_chunks;
 };
 
 // bytes of one per-chunk card in the workspace (or -1 if unsupported)

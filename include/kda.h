@@ -142,6 +142,61 @@ int kda_chunk_fwd_workspace_size(const kda_fwd_args *a, size_t *bytes);
 int kda_chunk_fwd(const kda_fwd_args *a, hipStream_t stream);
 
 /*
+ * Variable-length batch with block-granular state snapshots.  N independent
+ * sequences are packed along the rows of [rows, H, D] tensors (for q, k, v,
+ * log_alpha, gate, out; beta is [rows, H]); sequence i is rows
+ * cu_seqlens[i] .. cu_seqlens[i+1] - 1.  Page "Kimi K3 report walk-through",
+ * section on RL infrastructure and the prefix-cache trade-off of linear
+ * attention: storing the state after every token gives up the linear cost, not
+ * storing it rules out reusing a cached prefix, so the state is kept at block
+ * granularity.  With snapshot_every = P > 0 the state after every P tokens of a
+ * sequence (the state a continuation from that token would start with) is
+ * written to snapshots.
+ *   cu_seqlens: int64 [N + 1] in device memory, non-decreasing from 0 to at most
+ *     rows.  Offsets that break this are not an error: they are read as
+ *     s_i = max_{j <= i} clamp(cu_seqlens[j], 0, rows), and sequence i is rows
+ *     s_i .. s_{i+1} - 1 (so nothing outside the tensors is ever touched).  Rows
+ *     outside [s_0, s_N) are not read, and out is not written there.
+ *   initial_state / final_state: fp32 [N, H, Dk, Dv] or NULL, as in kda_chunk_fwd
+ *     (final_state may alias initial_state).
+ *   snapshot_every: 0 (none) or a positive multiple of 64.  snapshots: fp32
+ *     [rows / snapshot_every + N, H, Dk, Dv], required when snapshot_every > 0:
+ *     the k-th snapshot of sequence i (after (k + 1) * snapshot_every of its
+ *     tokens, k < len_i / snapshot_every) is slot
+ *     s_i / snapshot_every + i + k (integer division).  Other slots are not written.
+ *   Supported: bf16 inputs, chunk 0 or 64, Dk == Dv in {64, 128}; flags as in
+ *   kda_chunk_fwd (KDA_FLAG_NO_SEGMENT_SCAN has no effect: no segments here).
+ *   The workspace size comes from kda_chunk_fwd_varlen_workspace_size() (it
+ *   depends on N, rows, H and Dk only).
+ * The packed layout with cu_seqlens[i] = i T is the memory of a [N, T, H, D]
+ * batch, so this also adds snapshots to ordinary batches.
+ */
+typedef struct kda_varlen_args {
+    int64_t N, rows, H, Dk, Dv;
+    int32_t dtype;
+    int32_t out_dtype;
+    int32_t chunk;
+    uint32_t flags;
+    const int64_t *cu_seqlens;
+    const void *q;
+    const void *k;
+    const void *v;
+    const void *log_alpha;
+    const void *beta;
+    const void *gate;
+    void *out;
+    const float *initial_state;
+    float *final_state;
+    int64_t snapshot_every;
+    float *snapshots;
+    void *workspace;
+    size_t workspace_bytes;
+} kda_varlen_args;
+
+int kda_chunk_fwd_varlen_workspace_size(const kda_varlen_args *a, size_t *bytes);
+int kda_chunk_fwd_varlen(const kda_varlen_args *a, hipStream_t stream);
+
+/*
  * Segment summary of whole sequences.  Page "3T models are no longer magic",
  * section "KDA context parallelism", and page "Kimi K3 report walk-through",
  * section "KDA Context Parallelism": a run of tokens is summarised by how it

@@ -49,11 +49,13 @@ def test_struct_layout_matches_header(tmp_path):
 #include <stddef.h>
 #include "kda.h"
 int main(void) {
-  printf("%zu %zu %zu %zu %zu %zu %zu %zu %zu\n", sizeof(kda_fwd_args), offsetof(kda_fwd_args, q),
+  printf("%zu %zu %zu %zu %zu %zu %zu %zu %zu ", sizeof(kda_fwd_args), offsetof(kda_fwd_args, q),
          offsetof(kda_fwd_args, workspace_bytes), sizeof(kda_decode_args),
          offsetof(kda_decode_args, q), offsetof(kda_decode_args, state),
          sizeof(kda_combine_args), offsetof(kda_combine_args, transition),
          offsetof(kda_combine_args, final_state));
+  printf("%zu %zu %zu %zu\n", sizeof(kda_varlen_args), offsetof(kda_varlen_args, cu_seqlens),
+         offsetof(kda_varlen_args, snapshot_every), offsetof(kda_varlen_args, workspace_bytes));
   return 0;
 }''')
     exe = tmp_path / "layout"
@@ -64,7 +66,9 @@ int main(void) {
     want = [ctypes.sizeof(_abi.FwdArgs), _abi.FwdArgs.q.offset, _abi.FwdArgs.workspace_bytes.offset,
             ctypes.sizeof(_abi.DecodeArgs), _abi.DecodeArgs.q.offset, _abi.DecodeArgs.state.offset,
             ctypes.sizeof(_abi.CombineArgs), _abi.CombineArgs.transition.offset,
-            _abi.CombineArgs.final_state.offset]
+            _abi.CombineArgs.final_state.offset,
+            ctypes.sizeof(_abi.VarlenArgs), _abi.VarlenArgs.cu_seqlens.offset,
+            _abi.VarlenArgs.snapshot_every.offset, _abi.VarlenArgs.workspace_bytes.offset]
     assert got == want
 
 
@@ -247,6 +251,50 @@ def test_combine_validation(lib, mutate, code):
     mutate(a)
     assert lib.kda_combine_states(ctypes.byref(a), None) == code
     assert lib.kda_combine_states(None, None) == _abi.KDA_ERR_NULL
+
+
+def _good_var():
+    a = _abi.VarlenArgs()
+    a.N, a.rows, a.H, a.Dk, a.Dv, a.dtype = 3, 1000, 2, 128, 128, _abi.KDA_BF16
+    for f in ("cu_seqlens", "q", "k", "v", "log_alpha", "beta", "gate", "out"):
+        setattr(a, f, 0x10000)
+    return a
+
+
+def test_varlen_workspace_size(lib):
+    a = _good_var()
+    n = ctypes.c_size_t(0)
+    assert lib.kda_chunk_fwd_varlen_workspace_size(ctypes.byref(a), ctypes.byref(n)) == 0
+    card = 5 * 64 * 128 * 2 + 128 * 4
+    chunks = (1000 + 63) // 64 + 3  # the most chunks any offsets can give
+    r256 = lambda x: (x + 255) // 256 * 256
+    assert n.value == r256(chunks * 2 * card) + 2 * r256(4 * 8) + r256(chunks * 4)
+
+
+@pytest.mark.parametrize("mutate,code", [
+    (lambda a: setattr(a, "N", -1), _abi.KDA_ERR_SHAPE),
+    (lambda a: setattr(a, "rows", -1), _abi.KDA_ERR_SHAPE),
+    (lambda a: setattr(a, "snapshot_every", -64), _abi.KDA_ERR_SHAPE),
+    (lambda a: setattr(a, "snapshot_every", 100), _abi.KDA_ERR_UNSUPPORTED),
+    (lambda a: setattr(a, "dtype", _abi.KDA_F32), _abi.KDA_ERR_UNSUPPORTED),
+    (lambda a: setattr(a, "chunk", 32), _abi.KDA_ERR_UNSUPPORTED),
+    (lambda a: setattr(a, "Dv", 64), _abi.KDA_ERR_UNSUPPORTED),
+    (lambda a: setattr(a, "flags", 16), _abi.KDA_ERR_UNSUPPORTED),
+    (lambda a: setattr(a, "cu_seqlens", None), _abi.KDA_ERR_NULL),
+    (lambda a: setattr(a, "cu_seqlens", 0x10004), _abi.KDA_ERR_ALIGN),
+    (lambda a: setattr(a, "gate", None), _abi.KDA_ERR_NULL),
+    (lambda a: setattr(a, "snapshot_every", 128), _abi.KDA_ERR_NULL),  # no snapshot buffer
+    (lambda a: setattr(a, "final_state", 0x10008), _abi.KDA_ERR_ALIGN),
+    (lambda a: None, _abi.KDA_ERR_WORKSPACE),
+    (lambda a: (setattr(a, "workspace", 0x20000), setattr(a, "workspace_bytes", 4096)), _abi.KDA_ERR_WORKSPACE),
+    (lambda a: setattr(a, "N", 0), _abi.KDA_OK),
+    (lambda a: setattr(a, "H", 0), _abi.KDA_OK),
+])
+def test_varlen_validation(lib, mutate, code):
+    a = _good_var()
+    mutate(a)
+    assert lib.kda_chunk_fwd_varlen(ctypes.byref(a), None) == code
+    assert lib.kda_chunk_fwd_varlen(None, None) == _abi.KDA_ERR_NULL
 
 
 def test_binding_refuses_cpu_tensors():

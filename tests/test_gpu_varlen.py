@@ -1,0 +1,164 @@
+"""GPU parity of the variable-length batch and the block-granular state snapshots
+(through the C ABI) against the fp64 oracle.
+
+Page "Kimi K3 report walk-through", section on RL infrastructure and the prefix
+cache of linear attention: the state is kept at block granularity, so a cached
+prefix can be continued.  The oracle needs nothing new: every packed sequence is
+an independent run (oracle.fwd on it alone), and a snapshot is the state the
+oracle reaches after that many tokens of the sequence.  Error measure and limit as
+for kda_chunk_fwd: max |gpu - oracle| / rms(oracle) <= 2e-2 (bf16 inputs).
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from kda_workloads import CONFIGS, make_inputs, make_raw_inputs
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-2
+KEYS = ("q", "k", "v", "log_alpha", "beta", "gate")
+
+
+def kda():
+    import gated_delta_rule_106_amd as m
+    return m
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def rel_err(got, ref):
+    got = got.detach().double().cpu().numpy() if isinstance(got, torch.Tensor) else np.asarray(got)
+    ref = np.asarray(ref, dtype=np.float64)
+    if ref.size == 0:
+        return 0.0
+    return float(np.abs(got - ref).max()) / max(math.sqrt(float((ref ** 2).mean())), 1e-30)
+
+
+def packed(lengths, H, D, seed, wl_id=2, raw=False, pad_rows=0):
+    """Sequences of the given lengths from one recipe, packed along rows (plus unused
+    trailing rows), with per-sequence initial states."""
+    rows = sum(lengths) + pad_rows
+    wl = CONFIGS[wl_id].scaled(B=1, H=H, T=rows, Dk=D, Dv=D, init_state=False)
+    x = (make_raw_inputs if raw else make_inputs)(wl, seed=seed)
+    x = {k: x[k][0] for k in KEYS}  # [rows, H, D]
+    g = torch.Generator().manual_seed(seed)
+    s0 = torch.randn(len(lengths), H, D, D, generator=g) * 0.02
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int64)
+    return x, s0, cu
+
+
+def run(x, s0, cu, snapshot_every=0, **opts):
+    d = {k: x[k].cuda() for k in KEYS}
+    y, fin, snaps = kda().chunk_fwd_varlen(*(d[k] for k in KEYS), torch.from_numpy(cu).cuda(),
+                                           initial_state=s0.cuda(), output_final_state=True,
+                                           snapshot_every=snapshot_every, **opts)
+    torch.cuda.synchronize()
+    return y, fin, snaps
+
+
+def oracle_seq(x, s0, cu, i, upto=None, **opts):
+    lo, hi = int(cu[i]), int(cu[i + 1])
+    if upto is not None:
+        hi = lo + upto
+    xs = {k: x[k][lo:hi].unsqueeze(0).contiguous() for k in KEYS}
+    return oracle.fwd(*(xs[k] for k in KEYS), initial_state=s0[i:i + 1], **opts)
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_varlen_matches_oracle_per_sequence(D):
+    lengths = [0, 1, 63, 64, 65, 700, 130]
+    x, s0, cu = packed(lengths, 3, D, seed=200 + D)
+    say(f"[varlen] D={D} lengths={lengths}")
+    y, fin, _ = run(x, s0, cu)
+    for i in range(len(lengths)):
+        yo, so = oracle_seq(x, s0, cu, i)
+        ey = rel_err(y[cu[i]:cu[i + 1]], yo[0])
+        es = rel_err(fin[i], so[0])
+        say(f"[varlen] seq {i} len {lengths[i]}: y err/rms={ey:.3e} final err/rms={es:.3e}")
+        assert ey <= TOL and es <= TOL
+
+
+def test_equal_lengths_bitwise_equal_to_batch():
+    """cu = i T over a [N, T, H, D] batch is the same memory: the results are the
+    batch call's, bit for bit (the same card arithmetic, another card order)."""
+    N, T, H = 3, 300, 2
+    wl = CONFIGS[2].scaled(B=N, H=H, T=T)
+    x = {k: v.cuda() for k, v in make_inputs(wl, seed=210).items() if v is not None}
+    s0 = x["initial_state"]
+    yb, sb = kda().chunk_fwd(*(x[k] for k in KEYS), initial_state=s0, output_final_state=True)
+    cu = torch.arange(0, (N + 1) * T, T, dtype=torch.int64, device="cuda")
+    flat = {k: x[k].reshape(N * T, *x[k].shape[2:]) for k in KEYS}
+    yv, sv, _ = kda().chunk_fwd_varlen(*(flat[k] for k in KEYS), cu, initial_state=s0, output_final_state=True)
+    torch.cuda.synchronize()
+    say("[varlen] equal lengths vs batch: identical y", torch.equal(yv.reshape(N, T, H, -1), yb),
+        "identical final", torch.equal(sv, sb))
+    assert torch.equal(yv.reshape(N, T, H, -1), yb) and torch.equal(sv, sb)
+
+
+@pytest.mark.parametrize("every", [64, 128])
+def test_snapshots_match_oracle_prefix_states(every):
+    lengths = [700, 130, 0, 256, 64]
+    x, s0, cu = packed(lengths, 2, 128, seed=220 + every, wl_id=3)
+    say(f"[snap] every={every} lengths={lengths}")
+    y, fin, snaps = run(x, s0, cu, snapshot_every=every)
+    assert snaps.shape[0] == sum(lengths) // every + len(lengths)
+    worst = 0.0
+    for i, L in enumerate(lengths):
+        for kk in range(L // every):
+            slot = kda().snapshot_slot(cu, i, kk, every)
+            _, so = oracle_seq(x, s0, cu, i, upto=(kk + 1) * every)
+            e = rel_err(snaps[slot], so[0])
+            worst = max(worst, e)
+            assert e <= TOL, (i, kk, e)
+    say(f"[snap] every={every}: worst snapshot err/rms={worst:.3e}")
+
+
+def test_continuing_from_a_snapshot_reproduces_the_rest():
+    """Prefix cache: the state cached after P tokens continues the sequence exactly as
+    the whole run does."""
+    lengths = [900, 333]
+    x, s0, cu = packed(lengths, 2, 128, seed=230)
+    y, fin, snaps = run(x, s0, cu, snapshot_every=256)
+    i, kk = 0, 2  # after 768 tokens of sequence 0
+    p = (kk + 1) * 256
+    slot = kda().snapshot_slot(cu, i, kk, 256)
+    rest = {k: x[k][p:lengths[0]].unsqueeze(0).contiguous().cuda() for k in KEYS}
+    y2, s2 = kda().chunk_fwd(*(rest[k] for k in KEYS), initial_state=snaps[slot:slot + 1].contiguous(),
+                             output_final_state=True)
+    torch.cuda.synchronize()
+    yo, so = oracle_seq(x, s0, cu, 0)
+    ey, es = rel_err(y2[0], yo[0, p:]), rel_err(s2[0], so[0])
+    say(f"[snap] continuation from token {p}: y err/rms={ey:.3e} final err/rms={es:.3e}")
+    assert ey <= TOL and es <= TOL
+
+
+def test_rows_outside_the_sequences_are_left_alone():
+    lengths = [100, 50]
+    x, s0, cu = packed(lengths, 2, 64, seed=240, pad_rows=40)
+    d = {k: x[k].cuda() for k in KEYS}
+    out = torch.full((sum(lengths) + 40, 2, 64), 7.0, device="cuda")
+    y, fin, _ = kda().chunk_fwd_varlen(*(d[k] for k in KEYS), torch.from_numpy(cu).cuda(),
+                                       initial_state=s0.cuda(), output_final_state=True, out=out)
+    torch.cuda.synchronize()
+    assert torch.equal(y[150:].cpu(), torch.full((40, 2, 64), 7.0))
+    for i in range(2):
+        yo, so = oracle_seq(x, s0, cu, i)
+        assert rel_err(y[cu[i]:cu[i + 1]], yo[0]) <= TOL and rel_err(fin[i], so[0]) <= TOL
+
+
+def test_varlen_with_fused_preparation():
+    lengths = [77, 300, 1]
+    x, s0, cu = packed(lengths, 2, 128, seed=250, raw=True)
+    opts = dict(qk_norm=True, gate_logits=True)
+    y, fin, _ = run(x, s0, cu, **opts)
+    for i in range(len(lengths)):
+        yo, so = oracle_seq(x, s0, cu, i, **opts)
+        ey, es = rel_err(y[cu[i]:cu[i + 1]], yo[0]), rel_err(fin[i], so[0])
+        say(f"[varlen] fused seq {i}: y err/rms={ey:.3e} final err/rms={es:.3e}")
+        assert ey <= TOL and es <= TOL
