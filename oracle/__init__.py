@@ -65,6 +65,9 @@ def _open(path):
     lib.kda_oracle_decode.restype = ci
     lib.kda_oracle_summary.argtypes = [i64, i64, i64, i64, i64, ci, vp, vp, vp, vp, dp, dp, ci, ci, ci, ci]
     lib.kda_oracle_summary.restype = ci
+    lib.kda_oracle_bwd.argtypes = [i64, i64, i64, i64, i64, ci, vp, vp, vp, vp, vp, vp, dp, dp, dp,
+                                   dp, dp, dp, dp, dp, dp, dp, ci, ci]
+    lib.kda_oracle_bwd.restype = ci
     lib.kda_oracle_default_threads.argtypes = []
     lib.kda_oracle_default_threads.restype = ci
     return lib
@@ -99,6 +102,9 @@ def compile_variant(src_text: str, out_path: str):
 
         def summary(self, *a, **kw):
             return summary(*a, _lib_handle=lib, **kw)
+
+        def bwd(self, *a, **kw):
+            return bwd(*a, _lib_handle=lib, **kw)
     return _Handle()
 
 
@@ -268,3 +274,40 @@ def combine(M, b, initial_state=None):
         seg[p] = S
         S = np.matmul(M[p], S) + b[p]
     return seg, S
+
+
+def bwd(q, k, v, log_alpha, beta, gate, dy, initial_state=None, d_final_state=None, clamp=True,
+        threads=0, _lib_handle=None):
+    """Gradients of L = sum(dy * y) + sum(d_final_state * S_T) for the forward above
+    (reverse mode through the token steps; page "3T models are no longer magic",
+    section "Gate 1: KDA makes it computable", taken backwards).
+
+    Returns a dict of float64 arrays: dq, dk, dlog_alpha [B, T, H, Dk]; dv, dgate
+    [B, T, H, Dv]; dbeta [B, T, H]; dinitial_state [B, H, Dk, Dv].  Keeps every
+    state of a sequence: small cases only.
+    """
+    qa, dt = _raw(q)
+    ka, _ = _raw(k)
+    va, _ = _raw(v)
+    la, _ = _raw(log_alpha)
+    ba, _ = _raw(beta)
+    ga, _ = _raw(gate)
+    B, T, H, Dk = qa.shape
+    Dv = va.shape[-1]
+    s0 = _state64(initial_state, (B, H, Dk, Dv))
+    dST = _state64(d_final_state, (B, H, Dk, Dv))
+    dya = np.ascontiguousarray(np.asarray(dy, dtype=np.float64))
+    if dya.shape != (B, T, H, Dv):
+        raise ValueError("dy must be [B, T, H, Dv]")
+    out = dict(dq=np.zeros((B, T, H, Dk)), dk=np.zeros((B, T, H, Dk)), dv=np.zeros((B, T, H, Dv)),
+               dlog_alpha=np.zeros((B, T, H, Dk)), dbeta=np.zeros((B, T, H)),
+               dgate=np.zeros((B, T, H, Dv)), dinitial_state=np.zeros((B, H, Dk, Dv)))
+    lib = _lib_handle if _lib_handle is not None else _load()
+    rc = lib.kda_oracle_bwd(B, T, H, Dk, Dv, dt, _ptr(qa), _ptr(ka), _ptr(va), _ptr(la), _ptr(ba),
+                            _ptr(ga), _ptr(s0), _ptr(dya), _ptr(dST), _ptr(out["dq"]), _ptr(out["dk"]),
+                            _ptr(out["dv"]), _ptr(out["dlog_alpha"]), _ptr(out["dbeta"]),
+                            _ptr(out["dgate"]), _ptr(out["dinitial_state"]), 1 if clamp else 0,
+                            int(threads))
+    if rc != 0:
+        raise RuntimeError(f"kda_oracle_bwd failed with code {rc}")
+    return out

@@ -40,7 +40,9 @@
  *
  * Inputs are read as the exact bit patterns the GPU receives (fp32 or bf16)
  * and widened exactly to double.  No blocking, chunking or reordering: the
- * loop below is the definition.
+ * loop below is the definition.  Further down: the segment summary (the affine
+ * map a run of tokens applies to its incoming state) and the gradients of the
+ * forward (the same token steps taken backwards, reverse mode).
  *
  * Layouts (row-major, contiguous):
  *   q, k, log_alpha: [B, T, H, Dk]    v, gate, out: [B, T, H, Dv]
@@ -297,6 +299,158 @@ int kda_oracle_summary(int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv,
             orc_transition(bu, Dk, Dv, kk, a, bt, vv, r);
         }
         free(scratch);
+    }
+    return failed ? -2 : 0;
+}
+
+/*
+ * Gradients of the forward above (reverse mode, the steps of the recurrence taken
+ * backwards).  For the scalar loss L = sum(dy * y) + sum(dS_T * S_T), given dy
+ * [B, T, H, Dv] and dS_T [B, H, Dk, Dv] (or NULL: zero), returns dL/dq, dL/dk
+ * [B, T, H, Dk], dL/dv, dL/dgate [B, T, H, Dv], dL/dbeta [B, T, H], dL/dlog_alpha
+ * [B, T, H, Dk] and dL/dS_0 [B, H, Dk, Dv], all in double.  Per token, forward:
+ *   S^ = Diag(e^l) S_{t-1};  r = S^T k;  u = beta (v - r);  S_t = S^ + k u^T;
+ *   o = S_t^T q;  y = o * sigmoid(z),
+ * so, backwards from G = dL/dS_t:
+ *   do = dy * sigmoid(z);  dz = dy * o * sigmoid(z) (1 - sigmoid(z));
+ *   dq = S_t do;  G += q do^T;
+ *   dk = G u;  du = G^T k;  dbeta = du . (v - r);  dv = beta du;  dr = -beta du;
+ *   dS^ = G + k dr^T;  dk += S^ dr;
+ *   dl_c = sum_j S^[c, j] dS^[c, j];  dS_{t-1} = Diag(e^l) dS^.
+ * The clamp of log alpha passes the gradient where it leaves the value unchanged
+ * (ln 0.0067 <= x <= 0) and stops it where it clips.  Every state S_t of a sequence
+ * is kept (T * Dk * Dv doubles per (b, h)): meant for small cases.
+ * Returns 0, -1 on bad sizes, -2 on allocation failure.
+ */
+int kda_oracle_bwd(int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv, int dtype,
+                   const void *q, const void *k, const void *v, const void *log_alpha,
+                   const void *beta, const void *gate, const double *init_state,
+                   const double *dy, const double *dST, double *dq, double *dk, double *dv,
+                   double *dla, double *dbeta, double *dgate, double *dS0, int clamp,
+                   int nthreads) {
+    if (B < 0 || T < 0 || H < 0 || Dk <= 0 || Dv <= 0) return -1;
+    if (dtype != ORC_F32 && dtype != ORC_BF16) return -1;
+    const int64_t units = B * H, SZ = Dk * Dv;
+    int failed = 0;
+#ifdef _OPENMP
+    if (nthreads <= 0) nthreads = omp_get_max_threads();
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads)
+#endif
+    for (int64_t unit = 0; unit < units; ++unit) {
+        const int64_t b = unit / H, h = unit % H;
+        /* states S_0 .. S_T, then per-token scratch */
+        double *Sall = (double *)malloc(sizeof(double) * (size_t)((T + 1) * SZ));
+        double *G = (double *)malloc(sizeof(double) * (size_t)SZ);
+        double *Sh = (double *)malloc(sizeof(double) * (size_t)SZ);
+        double *w = (double *)malloc(sizeof(double) * (size_t)(4 * Dk + 6 * Dv));
+        if (!Sall || !G || !Sh || !w) {
+            free(Sall); free(G); free(Sh); free(w);
+#ifdef _OPENMP
+#pragma omp atomic write
+#endif
+            failed = 1;
+            continue;
+        }
+        double *kk = w, *qv = kk + Dk, *a = qv + Dk, *xg = a + Dk;  /* xg: raw log alpha */
+        double *r = xg + Dk, *u = r + Dv, *o = u + Dv, *dov = o + Dv, *duv = dov + Dv, *drv = duv + Dv;
+        if (init_state)
+            memcpy(Sall, init_state + unit * SZ, sizeof(double) * (size_t)SZ);
+        else
+            memset(Sall, 0, sizeof(double) * (size_t)SZ);
+        /* forward, keeping every state */
+        for (int64_t t = 0; t < T; ++t) {
+            const int64_t tok = (b * T + t) * H + h;
+            const double bt = orc_load(beta, dtype, tok);
+            const double *Sp = Sall + t * SZ;
+            double *Sn = Sall + (t + 1) * SZ;
+            for (int64_t c = 0; c < Dk; ++c) {
+                kk[c] = orc_load(k, dtype, tok * Dk + c);
+                const double x = orc_load(log_alpha, dtype, tok * Dk + c);
+                a[c] = exp(clamp ? fmin(fmax(x, ORC_LOG_ALPHA_MIN), 0.0) : x);
+            }
+            for (int64_t c = 0; c < Dk; ++c)
+                for (int64_t j = 0; j < Dv; ++j) Sn[c * Dv + j] = a[c] * Sp[c * Dv + j];
+            for (int64_t j = 0; j < Dv; ++j) {
+                double acc = 0.0;
+                for (int64_t c = 0; c < Dk; ++c) acc += Sn[c * Dv + j] * kk[c];
+                u[j] = bt * orc_load(v, dtype, tok * Dv + j) - bt * acc;
+            }
+            for (int64_t c = 0; c < Dk; ++c)
+                for (int64_t j = 0; j < Dv; ++j) Sn[c * Dv + j] += kk[c] * u[j];
+        }
+        /* backwards */
+        if (dST)
+            memcpy(G, dST + unit * SZ, sizeof(double) * (size_t)SZ);
+        else
+            memset(G, 0, sizeof(double) * (size_t)SZ);
+        for (int64_t t = T - 1; t >= 0; --t) {
+            const int64_t tok = (b * T + t) * H + h;
+            const double bt = orc_load(beta, dtype, tok);
+            const double *Sp = Sall + t * SZ, *St = Sall + (t + 1) * SZ;
+            for (int64_t c = 0; c < Dk; ++c) {
+                kk[c] = orc_load(k, dtype, tok * Dk + c);
+                qv[c] = orc_load(q, dtype, tok * Dk + c);
+                xg[c] = orc_load(log_alpha, dtype, tok * Dk + c);
+                a[c] = exp(clamp ? fmin(fmax(xg[c], ORC_LOG_ALPHA_MIN), 0.0) : xg[c]);
+            }
+            /* recompute S^ = Diag(a) S_{t-1}, r = S^T k, u = beta (v - r), o = S_t^T q */
+            for (int64_t c = 0; c < Dk; ++c)
+                for (int64_t j = 0; j < Dv; ++j) Sh[c * Dv + j] = a[c] * Sp[c * Dv + j];
+            for (int64_t j = 0; j < Dv; ++j) {
+                double rr = 0.0, oo = 0.0;
+                for (int64_t c = 0; c < Dk; ++c) {
+                    rr += Sh[c * Dv + j] * kk[c];
+                    oo += St[c * Dv + j] * qv[c];
+                }
+                r[j] = rr;
+                o[j] = oo;
+                u[j] = bt * orc_load(v, dtype, tok * Dv + j) - bt * rr;
+            }
+            /* output gate and the query read */
+            for (int64_t j = 0; j < Dv; ++j) {
+                const double z = orc_load(gate, dtype, tok * Dv + j);
+                const double sg = 1.0 / (exp(-z) + 1.0);
+                const double g_y = dy[tok * Dv + j];
+                dov[j] = g_y * sg;
+                dgate[tok * Dv + j] = g_y * o[j] * sg * (1.0 - sg);
+            }
+            for (int64_t c = 0; c < Dk; ++c) {
+                double acc = 0.0;
+                for (int64_t j = 0; j < Dv; ++j) acc += St[c * Dv + j] * dov[j];
+                dq[tok * Dk + c] = acc;
+            }
+            for (int64_t c = 0; c < Dk; ++c)
+                for (int64_t j = 0; j < Dv; ++j) G[c * Dv + j] += qv[c] * dov[j];
+            /* the corrective write S_t = S^ + k u^T */
+            double dbt = 0.0;
+            for (int64_t j = 0; j < Dv; ++j) {
+                double acc = 0.0;
+                for (int64_t c = 0; c < Dk; ++c) acc += G[c * Dv + j] * kk[c];
+                duv[j] = acc;
+                dbt += acc * orc_load(v, dtype, tok * Dv + j) - acc * r[j];
+                dv[tok * Dv + j] = bt * acc;
+                drv[j] = -bt * acc;
+            }
+            dbeta[tok] = dbt;
+            for (int64_t c = 0; c < Dk; ++c) {
+                double acc = 0.0;
+                for (int64_t j = 0; j < Dv; ++j) acc += G[c * Dv + j] * u[j] + Sh[c * Dv + j] * drv[j];
+                dk[tok * Dk + c] = acc;
+            }
+            /* the key read r = S^T k adds k dr^T to dS^; then the decay */
+            for (int64_t c = 0; c < Dk; ++c) {
+                double dl = 0.0;
+                for (int64_t j = 0; j < Dv; ++j) {
+                    const double dsh = G[c * Dv + j] + kk[c] * drv[j];
+                    dl += Sh[c * Dv + j] * dsh;
+                    G[c * Dv + j] = a[c] * dsh;
+                }
+                const int pass = !clamp || (xg[c] >= ORC_LOG_ALPHA_MIN && xg[c] <= 0.0);
+                dla[tok * Dk + c] = pass ? dl : 0.0;
+            }
+        }
+        memcpy(dS0 + unit * SZ, G, sizeof(double) * (size_t)SZ);
+        free(Sall); free(G); free(Sh); free(w);
     }
     return failed ? -2 : 0;
 }

@@ -43,6 +43,48 @@ MUTANTS = {
     "summary key not normalised": ("if (qk_norm) orc_unit(kk, Dk, 1.0);", ""),
 }
 
+# mistakes planted in the gradients (reverse mode); caught by differences of the forward
+BWD_MUTANTS = {
+    "backward: key-read term dropped": ("acc += G[c * Dv + j] * u[j] + Sh[c * Dv + j] * drv[j];",
+                                        "acc += G[c * Dv + j] * u[j];"),
+    "backward: decay missing on the state gradient": ("G[c * Dv + j] = a[c] * dsh;", "G[c * Dv + j] = dsh;"),
+    "backward: gate derivative": ("dgate[tok * Dv + j] = g_y * o[j] * sg * (1.0 - sg);",
+                                  "dgate[tok * Dv + j] = g_y * o[j] * sg;"),
+    "backward: query gradient added after the write": ("G[c * Dv + j] += qv[c] * dov[j];",
+                                                       "G[c * Dv + j] += 0.0 * qv[c] * dov[j];"),
+    "backward: update strength dropped from dv": ("dv[tok * Dv + j] = bt * acc;", "dv[tok * Dv + j] = acc;"),
+}
+
+
+def _bwd_pins_pass(handle) -> bool:
+    """Gradients against central differences of the variant's own (unchanged) forward."""
+    rng = np.random.default_rng(78)
+    B, T, H, Dk, Dv = 1, 3, 1, 2, 2
+    x = dict(q=rng.standard_normal((B, T, H, Dk)) * 0.5, k=rng.standard_normal((B, T, H, Dk)) * 0.5,
+             v=rng.standard_normal((B, T, H, Dv)), log_alpha=rng.uniform(-2, -0.1, (B, T, H, Dk)),
+             beta=rng.uniform(0.1, 0.9, (B, T, H)), gate=rng.standard_normal((B, T, H, Dv)))
+    x = {k: a.astype(np.float32) for k, a in x.items()}
+    keys = ("q", "k", "v", "log_alpha", "beta", "gate")
+    s0 = rng.standard_normal((B, H, Dk, Dv))
+    dy = rng.standard_normal((B, T, H, Dv))
+    g = handle.bwd(*(x[n] for n in keys), dy, initial_state=s0)
+
+    def loss(xx):
+        y, _ = handle.fwd(*(xx[n] for n in keys), initial_state=s0)
+        return float((y * dy).sum())
+    h = np.float32(2.0 ** -10)
+    for name, gname in (("q", "dq"), ("k", "dk"), ("v", "dv"), ("log_alpha", "dlog_alpha"),
+                        ("beta", "dbeta"), ("gate", "dgate")):
+        for idx in np.ndindex(x[name].shape):
+            xp = {n: a.copy() for n, a in x.items()}
+            xm = {n: a.copy() for n, a in x.items()}
+            xp[name][idx] += h
+            xm[name][idx] -= h
+            fd = (loss(xp) - loss(xm)) / (2 * float(h))
+            if abs(fd - g[gname][idx]) > 2e-5 * (1 + abs(fd)):
+                return False
+    return True
+
 
 def _pins_pass(handle) -> bool:
     rng = np.random.default_rng(77)
@@ -93,6 +135,20 @@ def test_real_oracle_passes_the_pins(oracle_lib):
         decode = staticmethod(oracle.decode)
         summary = staticmethod(oracle.summary)
     assert _pins_pass(_Real())
+
+    class _RealB:
+        fwd = staticmethod(oracle.fwd)
+        bwd = staticmethod(oracle.bwd)
+    assert _bwd_pins_pass(_RealB())
+
+
+@pytest.mark.parametrize("name", sorted(BWD_MUTANTS))
+def test_planted_gradient_mistake_is_caught(tmp_path, name):
+    old, new = BWD_MUTANTS[name]
+    src = oracle.source_text()
+    assert src.count(old) == 1, f"mutation anchor for '{name}' must occur exactly once"
+    handle = oracle.compile_variant(src.replace(old, new), str(tmp_path / "mutant.so"))
+    assert not _bwd_pins_pass(handle), f"gradient pins did not catch: {name}"
 
 
 @pytest.mark.parametrize("name", sorted(MUTANTS))
