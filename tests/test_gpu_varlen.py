@@ -162,3 +162,26 @@ def test_varlen_with_fused_preparation():
         ey, es = rel_err(y[cu[i]:cu[i + 1]], yo[0]), rel_err(fin[i], so[0])
         say(f"[varlen] fused seq {i}: y err/rms={ey:.3e} final err/rms={es:.3e}")
         assert ey <= TOL and es <= TOL
+
+
+def test_many_short_sequences():
+    """300 sequences (the sequence map spans two 256-entry blocks, and N H >= 64 takes the
+    two-value-tile state pass), lengths 0 .. 150 with a sample compared to the oracle,
+    snapshots every 64 tokens on the sampled sequences."""
+    g = np.random.default_rng(260)
+    lengths = [int(x) for x in g.integers(0, 151, 300)]
+    lengths[5] = 0
+    lengths[299] = 150
+    x, s0, cu = packed(lengths, 2, 128, seed=260)
+    say(f"[varlen] 300 sequences, {sum(lengths)} tokens")
+    y, fin, snaps = run(x, s0, cu, snapshot_every=64)
+    worst = 0.0
+    for i in (0, 1, 5, 17, 128, 255, 256, 257, 298, 299):
+        yo, so = oracle_seq(x, s0, cu, i)
+        ey, es = rel_err(y[cu[i]:cu[i + 1]], yo[0]), rel_err(fin[i], so[0])
+        worst = max(worst, ey, es)
+        assert ey <= TOL and es <= TOL, (i, ey, es)
+        for kk in range(lengths[i] // 64):
+            _, sp = oracle_seq(x, s0, cu, i, upto=(kk + 1) * 64)
+            assert rel_err(snaps[kda().snapshot_slot(cu, i, kk, 64)], sp[0]) <= TOL
+    say(f"[varlen] 300 sequences: worst sampled err/rms={worst:.3e}")
