@@ -112,6 +112,22 @@ def stored_traffic(kernel_tag: str):
     return float(m_b.group(1))
 
 
+def stored_mfma_counters(tag: str):
+    """MFMA utilisation (busy cycles over all SIMD cycles) and executed MFMA flops per
+    call from the committed counter summary, or None when it is missing or was taken
+    on other HIP sources."""
+    path = os.path.join(PROFILES, "pmc_mfma_" + tag + ".md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_src = re.search(r"^source_digest:\s*(\w+)", text, re.M)
+    m_u = re.search(r"^mfma_util_call:\s*([0-9.eE+-]+)", text, re.M)
+    m_f = re.search(r"^mfma_executed_flops_per_call:\s*([0-9.eE+]+)", text, re.M)
+    if not (m_src and m_u and m_f) or m_src.group(1) != source_digest():
+        return None
+    return {"mfma_util": float(m_u.group(1)), "executed_flops_per_call": float(m_f.group(1))}
+
+
 def to_dev(x, dev):
     import torch
     return {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in x.items()}
@@ -498,7 +514,8 @@ def main():
                    "d_v": head.Dv, "chunk": head.chunk, "global_batch": head.B,
                    "seq_len": head.T, "parallelism": "single GPU"},
         "mfma": {"achieved": pre["mfma_tflops"], "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
-                 "frac": pre["mfma_frac"], "alg_flops_per_step": pre["alg_flops"]},
+                 "frac": pre["mfma_frac"], "alg_flops_per_step": pre["alg_flops"],
+                 "counters": stored_mfma_counters(head.name)},
         "roofline": roof,
         "decode": {"metric": "decode steps/s", "value": dec["steps_per_s"], "unit": "steps/s",
                    "tokens_per_s": dec["tokens_per_s"], "kernel_ms": dec["kernel_ms_mean"],
