@@ -277,7 +277,8 @@ def bench_context_parallel(kda, steps, warmup, dev, stream, P=8):
     """One GPU's share of a P-way split along T of the floor-stress workload (pages:
     "KDA context parallelism"): the summary of its T/P tokens, the ordered
     combination of the P summaries (P - 1 of which another GPU would deliver), and
-    the re-run of its segment from the incoming state.  Kernel time of each stage."""
+    the re-run of its segment from the incoming state, on the cards the summary left
+    (the re-run that builds them again is timed too).  Kernel time of each stage."""
     import torch
     from kda_workloads import CONFIGS, make_inputs
     full = CONFIGS[3]
@@ -292,14 +293,19 @@ def bench_context_parallel(kda, steps, warmup, dev, stream, P=8):
     Ms, bs = M.expand(P, *M.shape).contiguous(), b.expand(P, *b.shape).contiguous()
     fin = torch.empty_like(b)
 
-    def f_sum(_):
-        kda.chunk_summary(x["k"], x["v"], x["log_alpha"], x["beta"], transition=M, offset=b, workspace=ws)
+    def f_sum(_):  # given q, it leaves complete cards for the re-run
+        kda.chunk_summary(x["k"], x["v"], x["log_alpha"], x["beta"], transition=M, offset=b, workspace=ws,
+                          q=x["q"])
 
     def f_comb(_):
         kda.combine_states(Ms, bs, x["initial_state"], segment_states=False, final_state=fin)
 
-    def f_rerun(_):
+    def f_rerun_build(_):
         kda.chunk_fwd(*(x[k] for k in KEYS), initial_state=fin, out=out, workspace=ws)
+
+    def f_rerun(_):  # the summary's cards, no card builder
+        kda.chunk_fwd(*(x[k] for k in KEYS), initial_state=fin, out=out, workspace=ws, cards_ready=True)
+    _, t_rb = time_calls(f_rerun_build, [None], steps, warmup, stream)
     _, t_sum = time_calls(f_sum, [None], steps, warmup, stream)
     _, t_comb = time_calls(f_comb, [None], steps, warmup, stream)
     _, t_rerun = time_calls(f_rerun, [None], steps, warmup, stream)
@@ -310,6 +316,7 @@ def bench_context_parallel(kda, steps, warmup, dev, stream, P=8):
     comb_bytes = units * 4 * d * (P * (d + wl.Dv) + 2 * wl.Dv)
     res = {"workload": full.name, "split": P, "tokens_per_gpu": wl.T, "B": wl.B, "H": wl.H, "d": d,
            "summary_us": 1e3 * t_sum, "combine_us": 1e3 * t_comb, "rerun_us": 1e3 * t_rerun,
+           "rerun_building_cards_us": 1e3 * t_rb,
            "share_total_us": 1e3 * (t_sum + t_comb + t_rerun),
            "summary_alg_gbs": sum_bytes / (t_sum / 1e3) / 1e9,
            "combine_alg_gbs": comb_bytes / (t_comb / 1e3) / 1e9,

@@ -108,7 +108,7 @@ def workspace_bytes(B, T, H, D, dtype=torch.bfloat16, chunk=0) -> int:
 
 def chunk_fwd(q, k, v, log_alpha, beta, gate, initial_state=None, output_final_state=False,
               chunk=0, clamp=True, out_dtype=torch.float32, out=None, final_state=None,
-              workspace=None, segment_scan=True, qk_norm=False, gate_logits=False):
+              workspace=None, segment_scan=True, qk_norm=False, gate_logits=False, cards_ready=False):
     """Chunkwise-parallel KDA forward on the current HIP stream.
 
     q, k, log_alpha: [B, T, H, Dk]; v, gate: [B, T, H, Dv]; beta: [B, T, H];
@@ -119,7 +119,9 @@ def chunk_fwd(q, k, v, log_alpha, beta, gate, initial_state=None, output_final_s
     into segments (the same result up to rounding).  ``qk_norm``: q and k are raw
     projections, L2-normalised per token inside (q also scaled by 1/sqrt(Dk)).
     ``gate_logits``: ``log_alpha`` holds forget-gate logits x and the kernel uses
-    max(logsigmoid(x), ln 0.0067).
+    max(logsigmoid(x), ln 0.0067).  ``cards_ready``: ``workspace`` already holds the
+    cards of these inputs (from ``chunk_summary(..., q=q, workspace=workspace)``), so
+    the card builder is skipped.
     """
     lib = _abi.load()
     dev = q.device
@@ -129,6 +131,10 @@ def chunk_fwd(q, k, v, log_alpha, beta, gate, initial_state=None, output_final_s
     a.flags = _prep_flags(clamp, qk_norm, gate_logits)
     if not segment_scan:
         a.flags |= _abi.KDA_FLAG_NO_SEGMENT_SCAN
+    if cards_ready:
+        if workspace is None:
+            raise ValueError("cards_ready needs the workspace that holds the cards")
+        a.flags |= _abi.KDA_FLAG_CARDS_READY
     B, T, H, Dk, Dv = a.B, a.T, a.H, a.Dk, a.Dv
     if initial_state is not None and (initial_state.dtype != torch.float32 or
                                       tuple(initial_state.shape) != (B, H, Dk, Dv)):
@@ -230,13 +236,15 @@ def chunk_fwd_varlen(q, k, v, log_alpha, beta, gate, cu_seqlens, initial_state=N
 
 
 def chunk_summary(k, v, log_alpha, beta, clamp=True, transition=None, offset=None, workspace=None,
-                  qk_norm=False, gate_logits=False):
+                  qk_norm=False, gate_logits=False, q=None):
     """Segment summary of every (b, h) sequence on the current HIP stream.
 
     The T tokens map an incoming state S to ``M @ S + b`` (``M`` the product of the
     per-token transitions, ``b`` the state reached from zero).  k, log_alpha:
     bf16 [B, T, H, Dk]; v: bf16 [B, T, H, Dv]; beta: bf16 [B, T, H].  Returns
-    ``(M, b)``: fp32 [B, H, Dk, Dk] and [B, H, Dk, Dv].
+    ``(M, b)``: fp32 [B, H, Dk, Dk] and [B, H, Dk, Dv].  Given ``q`` (and a
+    ``workspace``), the cards left in the workspace also serve a following
+    ``chunk_fwd(..., workspace=workspace, cards_ready=True)`` over the same inputs.
     """
     lib = _abi.load()
     dev = k.device
@@ -269,6 +277,10 @@ def chunk_summary(k, v, log_alpha, beta, clamp=True, transition=None, offset=Non
         workspace = torch.empty(max(int(n.value), 16), dtype=torch.uint8, device=dev)
     _check_dev(dict(k=k, v=v, log_alpha=log_alpha, beta=beta, transition=transition, offset=offset), dev)
     a.k, a.v, a.log_alpha, a.beta = _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta)
+    if q is not None:
+        if q.shape != k.shape or q.dtype != k.dtype or q.device != dev or not q.is_contiguous():
+            raise ValueError("q must match k (shape, dtype, device) and be contiguous")
+        a.q = _ptr(q)
     a.final_state = _ptr(offset)
     a.workspace, a.workspace_bytes = _ptr(workspace), workspace.numel()
     stream = torch.cuda.current_stream(dev).cuda_stream

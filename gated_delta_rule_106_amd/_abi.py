@@ -19,6 +19,7 @@ KDA_FLAG_NO_CLAMP = 1
 KDA_FLAG_NO_SEGMENT_SCAN = 2
 KDA_FLAG_QK_L2NORM = 4
 KDA_FLAG_GATE_LOGITS = 8
+KDA_FLAG_CARDS_READY = 16
 
 # every extern "C" entry point of include/kda.h
 EXPORTS = ("kda_chunk_fwd_workspace_size", "kda_chunk_fwd", "kda_chunk_fwd_varlen_workspace_size",

@@ -38,9 +38,12 @@ int check_shape(const kda_fwd_args* a, int* chunk, int64_t* nchunks, int64_t* ca
     if (a->dtype != KDA_F32 && a->dtype != KDA_BF16) return KDA_ERR_UNSUPPORTED;
     if (a->Dk != a->Dv || (a->Dk != 64 && a->Dk != 128)) return KDA_ERR_UNSUPPORTED;
     if (a->out_dtype != KDA_F32 && a->out_dtype != KDA_BF16) return KDA_ERR_UNSUPPORTED;
-    if ((a->flags & ~(KDA_FLAG_NO_CLAMP | KDA_FLAG_NO_SEGMENT_SCAN | kPrepFlags)) != 0) return KDA_ERR_UNSUPPORTED;
+    if ((a->flags & ~(KDA_FLAG_NO_CLAMP | KDA_FLAG_NO_SEGMENT_SCAN | kPrepFlags | KDA_FLAG_CARDS_READY)) != 0)
+        return KDA_ERR_UNSUPPORTED;
     const int c = resolve_chunk(a);
     if (!kda::prefill_supported(a->dtype == KDA_BF16, c, (int)a->Dk)) return KDA_ERR_UNSUPPORTED;
+    // cards can only have come from the chunk-64 bf16 path (summary or prefill)
+    if ((a->flags & KDA_FLAG_CARDS_READY) && (a->dtype != KDA_BF16 || c != 64)) return KDA_ERR_UNSUPPORTED;
     // every element index of every tensor must fit in int64
     int64_t bt, bth, elems, bh, st;
     if (!mul_ok(a->B, a->T, &bt) || !mul_ok(bt, a->H, &bth) || !mul_ok(bth, a->Dk, &elems) ||
@@ -207,6 +210,7 @@ int kda_chunk_fwd(const kda_fwd_args* a, hipStream_t stream) {
     kda::PrepParams pp{a->q, a->k, a->v, a->log_alpha, a->beta, a->workspace,
                        a->B, a->T, a->H, nc, (a->flags & KDA_FLAG_NO_CLAMP) ? 0 : 1,
                        (a->flags & KDA_FLAG_QK_L2NORM) ? 1 : 0, (a->flags & KDA_FLAG_GATE_LOGITS) ? 1 : 0};
+    pp.cards_ready = (a->flags & KDA_FLAG_CARDS_READY) ? 1 : 0;
     kda::RecurParams rp{a->gate, a->out, a->initial_state, a->final_state, a->workspace,
                         a->B, a->T, a->H, nc, nc, 1, nullptr};
     // the state pass of every segment reads initial_state at its start while the last
@@ -236,6 +240,7 @@ int kda_chunk_summary(const kda_fwd_args* a, float* transition, hipStream_t stre
     if (a->dtype != KDA_BF16 || c != 64) return KDA_ERR_UNSUPPORTED;
     if (a->flags & ~(KDA_FLAG_NO_CLAMP | kPrepFlags)) return KDA_ERR_UNSUPPORTED;
     const int64_t units = a->B * a->H;
+    if (!aligned16(a->q)) return KDA_ERR_ALIGN;
     if (units == 0) return KDA_OK;
     if (units * (a->Dk / 16) > INT_MAX) return KDA_ERR_SHAPE;  // combine-style grids
     if (!transition || !a->final_state) return KDA_ERR_NULL;
@@ -254,8 +259,8 @@ int kda_chunk_summary(const kda_fwd_args* a, float* transition, hipStream_t stre
     if (!a->workspace || (int64_t)a->workspace_bytes < cards) return KDA_ERR_WORKSPACE;
     if (!aligned16(a->workspace)) return KDA_ERR_ALIGN;
     // the card builder also forms the query-side blocks of each card, which the summary
-    // never reads: k stands in for q
-    kda::PrepParams pp{a->k, a->k, a->v, a->log_alpha, a->beta, a->workspace,
+    // never reads: without q, k stands in for it (and the cards serve the summary only)
+    kda::PrepParams pp{a->q ? a->q : a->k, a->k, a->v, a->log_alpha, a->beta, a->workspace,
                        a->B, a->T, a->H, nc, (a->flags & KDA_FLAG_NO_CLAMP) ? 0 : 1,
                        (a->flags & KDA_FLAG_QK_L2NORM) ? 1 : 0, (a->flags & KDA_FLAG_GATE_LOGITS) ? 1 : 0};
     const hipError_t e = kda::launch_summary64(D, pp, transition, a->final_state, stream);

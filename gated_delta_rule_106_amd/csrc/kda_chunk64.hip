@@ -1159,7 +1159,7 @@ static hipError_t launch_d(const PrepParams& pp, const RecurParams& rp0, hipStre
     // one workgroup per card, two per CU; a variable-length grid covers the most chunks
     // its offsets can give (pp.T = packed rows) and the surplus groups leave at once
     const int64_t items = pp.vco ? varlen_max_chunks(pp.vN, pp.T, C) * pp.H : units * pp.NC;
-    if (items > 0) {
+    if (items > 0 && !pp.cards_ready) {
         const int mode = (pp.qk_norm ? kModeQkNorm : 0) | (pp.logits ? kModeLogits : 0);
         auto kp = mode == 0   ? kda_prep64_kernel<D, 0>
                   : mode == 1 ? kda_prep64_kernel<D, 1>

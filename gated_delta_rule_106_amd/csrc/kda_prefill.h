@@ -24,6 +24,7 @@ struct PrepParams {
     const int64_t* vco;
     const int32_t* vsoc;
     int64_t vN;
+    int cards_ready;  // the workspace already holds these inputs' cards: no card builder
 };
 
 struct RecurParams {

@@ -88,6 +88,14 @@ extern "C" {
  *    log alpha = max(logsigmoid(x), ln 0.0067) by default). */
 #define KDA_FLAG_QK_L2NORM 4u
 #define KDA_FLAG_GATE_LOGITS 8u
+/* kda_chunk_fwd only (bf16 inputs, chunk 64): the workspace already holds the
+ * per-chunk cards of exactly these q, k, v, log_alpha, beta, sizes and
+ * preparation flags, written by a kda_chunk_summary call that was given q (or by
+ * an earlier kda_chunk_fwd); the card builder is skipped.  Context-parallel use:
+ * summarise a segment, combine, then re-run it from its incoming state without
+ * building its cards twice.  Stale or foreign workspace contents give wrong
+ * results; they are not detected. */
+#define KDA_FLAG_CARDS_READY 16u
 
 /*
  * Arguments of kda_chunk_fwd.
@@ -206,8 +214,10 @@ int kda_chunk_fwd_varlen(const kda_varlen_args *a, hipStream_t stream);
  * an incoming state S_0 to
  *     S_T = M S_0 + b,   M = A_T ... A_1,   A_t = (I - beta_t k_t k_t^T) Diag(alpha_t),
  * with b the state reached from S_0 = 0.
- *   Reads k, v, log_alpha, beta and the clamp flag of *a; q, gate, out and
- *   initial_state are not read and may be NULL.
+ *   Reads k, v, log_alpha, beta and the clamp flag of *a; gate, out and
+ *   initial_state are not read and may be NULL.  q may be NULL; when it is
+ *   given, the cards left in the workspace are complete, and a following
+ *   kda_chunk_fwd over the same inputs can take them with KDA_FLAG_CARDS_READY.
  *   transition: fp32 [B, H, Dk, Dk], receives M (required).
  *   a->final_state: fp32 [B, H, Dk, Dv], receives b (required).
  *   The two outputs must not overlap each other, the inputs or the workspace.

@@ -126,8 +126,11 @@ def test_workspace_size_includes_segment_summaries(lib):
     (lambda a: setattr(a, "dtype", 7), _abi.KDA_ERR_UNSUPPORTED),
     (lambda a: setattr(a, "chunk", 48), _abi.KDA_ERR_UNSUPPORTED),
     (lambda a: setattr(a, "chunk", 128), _abi.KDA_ERR_UNSUPPORTED),
-    (lambda a: setattr(a, "flags", 16), _abi.KDA_ERR_UNSUPPORTED),
-    (lambda a: setattr(a, "flags", 15), _abi.KDA_ERR_WORKSPACE),  # every known flag: accepted
+    (lambda a: setattr(a, "flags", 32), _abi.KDA_ERR_UNSUPPORTED),
+    (lambda a: setattr(a, "flags", 31), _abi.KDA_ERR_WORKSPACE),  # every known flag: accepted
+    (lambda a: (setattr(a, "flags", 16), setattr(a, "chunk", 32)), _abi.KDA_ERR_UNSUPPORTED),  # cards: chunk 64
+    (lambda a: (setattr(a, "flags", 16), setattr(a, "dtype", _abi.KDA_F32), setattr(a, "chunk", 16)),
+     _abi.KDA_ERR_UNSUPPORTED),
     (lambda a: setattr(a, "out_dtype", 2), _abi.KDA_ERR_UNSUPPORTED),
     (lambda a: setattr(a, "T", 2 ** 62), _abi.KDA_ERR_SHAPE),
     (lambda a: setattr(a, "q", None), _abi.KDA_ERR_NULL),

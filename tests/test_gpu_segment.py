@@ -164,3 +164,20 @@ def test_context_parallel_split_matches_whole(wl_id, cuts):
     say(f"[kcp] y err/rms={ey:.3e} final state err/rms={es:.3e}")
     assert np.isfinite(ey) and ey <= TOL_BF16
     assert np.isfinite(es) and es <= TOL_BF16
+
+
+@pytest.mark.parametrize("H,T", [(4, 1000), (1, 8192)])
+def test_rerun_takes_the_summary_cards(H, T):
+    """A summary given q leaves complete cards; the forward that takes them (card builder
+    skipped) is bit for bit the forward that builds them (T = 8192, H = 1 also takes
+    the segment scan)."""
+    wl = CONFIGS[3].scaled(B=1, H=H, T=T, init_state=True)
+    x = {k: v.cuda() for k, v in make_inputs(wl, seed=300 + T).items() if v is not None}
+    ws = torch.empty(kda().workspace_bytes(1, T, H, 128), dtype=torch.uint8, device="cuda")
+    y0, s0 = kda().chunk_fwd(*(x[k] for k in KEYS), initial_state=x["initial_state"], output_final_state=True)
+    M, b = kda().chunk_summary(x["k"], x["v"], x["log_alpha"], x["beta"], q=x["q"], workspace=ws)
+    y1, s1 = kda().chunk_fwd(*(x[k] for k in KEYS), initial_state=x["initial_state"], output_final_state=True,
+                             workspace=ws, cards_ready=True)
+    torch.cuda.synchronize()
+    say(f"[kcp] cards reused H={H} T={T}: identical y {torch.equal(y0, y1)}, final {torch.equal(s0, s1)}")
+    assert torch.equal(y0, y1) and torch.equal(s0, s1)
