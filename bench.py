@@ -491,7 +491,7 @@ def main():
     dec = bench_decode(kda, CONFIGS[4], max(args.steps, 10), args.warmup, dev, stream)
     ctx = {}
     if not args.no_context:
-        for cid in (2, 3):
+        for cid in (0, 2, 3):
             r, _ = bench_prefill(kda, CONFIGS[cid], max(5, args.steps // 10), 2, 1, dev, stream)
             ctx[CONFIGS[cid].name] = r
             torch.cuda.empty_cache()

@@ -569,8 +569,13 @@ void kda_prep64_kernel(PrepParams p) {
         cp.tb = p.vs[i];
         cp.slen = p.vs[i + 1] - cp.tb;  // >= 1: the sequence owns this chunk
     } else {  // B sequences of T tokens: card unit NC + n
-        const int64_t unit = cp.item / p.NC;
-        cp.n = cp.item - unit * p.NC;
+        // workgroups build the last chunks of every sequence first, so that the cards the
+        // state pass reads first are the most recently written (still in the Infinity Cache)
+        const int64_t units = p.B * p.H;
+        const int64_t back = cp.item / units;  // chunks from the end
+        const int64_t unit = cp.item - back * units;
+        cp.n = p.NC - 1 - back;
+        cp.item = unit * p.NC + cp.n;
         const int64_t b = unit / p.H;
         cp.h = unit - b * p.H;
         cp.tb = b * p.T;
