@@ -185,3 +185,26 @@ def test_many_short_sequences():
             _, sp = oracle_seq(x, s0, cu, i, upto=(kk + 1) * 64)
             assert rel_err(snaps[kda().snapshot_slot(cu, i, kk, 64)], sp[0]) <= TOL
     say(f"[varlen] 300 sequences: worst sampled err/rms={worst:.3e}")
+
+
+def test_full_size_batch_as_varlen_bitwise():
+    """B2 H32 T8192 (the state in/out workload at full size) as two packed sequences:
+    outputs and final states are the batch call's bit for bit, and the snapshot after
+    4096 tokens is bit for bit the batch call's final state over that prefix (the same
+    cards and arithmetic either way)."""
+    wl = CONFIGS[2]
+    x = {k: v.cuda() for k, v in make_inputs(wl).items() if v is not None}
+    B, T, H = wl.B, wl.T, wl.H
+    yb, sb = kda().chunk_fwd(*(x[k] for k in KEYS), initial_state=x["initial_state"], output_final_state=True)
+    cu = torch.arange(0, (B + 1) * T, T, dtype=torch.int64, device="cuda")
+    flat = {k: x[k].reshape(B * T, *x[k].shape[2:]) for k in KEYS}
+    yv, sv, snaps = kda().chunk_fwd_varlen(*(flat[k] for k in KEYS), cu, initial_state=x["initial_state"],
+                                           output_final_state=True, snapshot_every=4096)
+    half = {k: x[k][:, :4096].contiguous() for k in KEYS}
+    _, sh = kda().chunk_fwd(*(half[k] for k in KEYS), initial_state=x["initial_state"], output_final_state=True)
+    torch.cuda.synchronize()
+    same_y, same_s = torch.equal(yv.reshape(B, T, H, -1), yb), torch.equal(sv, sb)
+    same_snap = all(torch.equal(snaps[kda().snapshot_slot(cu.cpu(), i, 0, 4096)], sh[i]) for i in range(B))
+    last = all(torch.equal(snaps[kda().snapshot_slot(cu.cpu(), i, 1, 4096)], sb[i]) for i in range(B))
+    say(f"[varlen] full size B2 H32 T8192: y {same_y}, final {same_s}, snapshot@4096 {same_snap}, @8192 {last}")
+    assert same_y and same_s and same_snap and last
