@@ -51,6 +51,9 @@ __global__ __launch_bounds__(D * 4) void kda_combine_kernel(CombineParams p) {
     const int64_t DD = (int64_t)D * D;
     const int arow = 16 * wave + m;      // row of M this lane streams
     const int crow = 16 * wave + 4 * g;  // first accumulator row of this lane
+    // copies of the state tile: one float4 per thread (D x 16 = 4 NTH floats)
+    static_assert(D * 16 == 4 * NTH, "one float4 of the tile per thread");
+    const int tr = threadIdx.x >> 2, tc = 4 * (threadIdx.x & 3);  // row, first column
 
     // this wave's 16 rows of M_s (as MFMA A operands) and its b_s accumulator start,
     // in two register sets: segment s + 1 loads while segment s is combined
@@ -69,10 +72,8 @@ __global__ __launch_bounds__(D * 4) void kda_combine_kernel(CombineParams p) {
         if (s + 1 < p.P) load_seg(s + 1, Mn, bn);
         if (p.seg) {
             float* dst = p.seg + (s * p.units + unit) * DD;
-            for (int e = threadIdx.x; e < D * 16; e += NTH) {
-                const int r = e >> 4, c = e & 15;
-                dst[(int64_t)r * D + col0 + c] = S[r * kPad + c];
-            }
+            *reinterpret_cast<float4*>(dst + (int64_t)tr * D + col0 + tc) =
+                *reinterpret_cast<const float4*>(&S[tr * kPad + tc]);
         }
         floatx4 acc = bb;
 #pragma unroll
@@ -89,23 +90,21 @@ __global__ __launch_bounds__(D * 4) void kda_combine_kernel(CombineParams p) {
     };
     if (p.P > 0) load_seg(0, MA, bA);
 
-    // the tile of the incoming state (read before anything of this tile is written,
-    // so the final state may alias it)
-    for (int e = threadIdx.x; e < D * 16; e += NTH) {
-        const int r = e >> 4, c = e & 15;
-        S[r * kPad + c] = p.s0 ? p.s0[unit * DD + (int64_t)r * D + col0 + c] : 0.f;
+    // the tile of the incoming state, one float4 per thread (D x 16 = 4 NTH floats), read
+    // before anything of this tile is written, so the final state may alias it
+    {
+        const float4 v = p.s0 ? *reinterpret_cast<const float4*>(p.s0 + unit * DD + (int64_t)tr * D + col0 + tc)
+                              : make_float4(0.f, 0.f, 0.f, 0.f);
+        *reinterpret_cast<float4*>(&S[tr * kPad + tc]) = v;
     }
     __syncthreads();
     for (int64_t s = 0; s < p.P; s += 2) {
         step(s, MA, bA, MB, bB);
         if (s + 1 < p.P) step(s + 1, MB, bB, MA, bA);
     }
-    if (p.sT) {
-        for (int e = threadIdx.x; e < D * 16; e += NTH) {
-            const int r = e >> 4, c = e & 15;
-            p.sT[unit * DD + (int64_t)r * D + col0 + c] = S[r * kPad + c];
-        }
-    }
+    if (p.sT)
+        *reinterpret_cast<float4*>(p.sT + unit * DD + (int64_t)tr * D + col0 + tc) =
+            *reinterpret_cast<const float4*>(&S[tr * kPad + tc]);
 }
 
 // M = I and b = 0 for every (b, h): one workgroup per (b, h)
