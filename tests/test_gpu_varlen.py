@@ -208,3 +208,25 @@ def test_full_size_batch_as_varlen_bitwise():
     last = all(torch.equal(snaps[kda().snapshot_slot(cu.cpu(), i, 1, 4096)], sb[i]) for i in range(B))
     say(f"[varlen] full size B2 H32 T8192: y {same_y}, final {same_s}, snapshot@4096 {same_snap}, @8192 {last}")
     assert same_y and same_s and same_snap and last
+
+
+def test_sequences_may_start_after_row_zero():
+    """cu[0] > 0: the rows before the first sequence are not read and out is not written
+    there, exactly as for rows after the last one."""
+    lengths = [90, 0, 33]
+    x, s0, cu = packed(lengths, 2, 128, seed=270, pad_rows=50)
+    rows = sum(lengths) + 50
+    shift = 20  # sequences at rows 20 .. 143; rows 0..19 and 143.. are outside
+    xs = {k: torch.roll(x[k], shifts=shift, dims=0) for k in KEYS}
+    cu2 = cu + shift
+    d = {k: xs[k].cuda() for k in KEYS}
+    out = torch.full((rows, 2, 128), -3.0, device="cuda")
+    y, fin, _ = kda().chunk_fwd_varlen(*(d[k] for k in KEYS), torch.from_numpy(cu2).cuda(),
+                                       initial_state=s0.cuda(), output_final_state=True, out=out)
+    torch.cuda.synchronize()
+    assert torch.equal(y[:shift].cpu(), torch.full((shift, 2, 128), -3.0))
+    assert torch.equal(y[int(cu2[-1]):].cpu(), torch.full((rows - int(cu2[-1]), 2, 128), -3.0))
+    for i in range(len(lengths)):
+        yo, so = oracle_seq(x, s0, cu, i)
+        assert rel_err(y[cu2[i]:cu2[i + 1]], yo[0]) <= TOL and rel_err(fin[i], so[0]) <= TOL
+    say("[varlen] sequences starting at row 20: outside rows untouched, parity held")
