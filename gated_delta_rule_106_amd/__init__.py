@@ -23,7 +23,7 @@ import torch
 
 from . import _abi
 
-__all__ = ["chunk_fwd", "chunk_fwd_varlen", "snapshot_slot", "chunk_summary", "combine_states", "decode_step", "workspace_bytes",
+__all__ = ["chunk_fwd", "chunk_bwd", "chunk_fwd_varlen", "snapshot_slot", "chunk_summary", "combine_states", "decode_step", "workspace_bytes",
            "library_path", "KDAError"]
 
 
@@ -288,6 +288,60 @@ def chunk_summary(k, v, log_alpha, beta, clamp=True, transition=None, offset=Non
     if rc != _abi.KDA_OK:
         raise KDAError(rc, "kda_chunk_summary")
     return transition, offset
+
+
+def chunk_bwd(q, k, v, log_alpha, beta, gate, d_out, initial_state=None, d_final_state=None,
+              clamp=True, workspace=None, need_initial_state_grad=True):
+    """Gradients of ``sum(d_out * y) + sum(d_final_state * S_T)`` through ``chunk_fwd``
+    (fp32 output, no preparation options), on the current HIP stream.
+
+    Inputs as for ``chunk_fwd``; ``d_out`` has their shape [B, T, H, Dv] and dtype.
+    Returns a dict of fp32 tensors: dq, dk, dlog_alpha [B, T, H, Dk]; dv, dgate
+    [B, T, H, Dv]; dbeta [B, T, H]; dinitial_state [B, H, Dk, Dv] (or None).
+    """
+    lib = _abi.load()
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("chunk_bwd needs GPU tensors (the HIP kernels are the only implementation)")
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    if k.shape != q.shape or log_alpha.shape != q.shape or v.shape != (B, T, H, Dv) or \
+            gate.shape != v.shape or d_out.shape != v.shape or beta.shape != (B, T, H):
+        raise ValueError("q, k, log_alpha must be [B, T, H, Dk], v, gate, d_out [B, T, H, Dv], beta [B, T, H]")
+    code = _dtype_code(q)
+    for t in (k, v, log_alpha, beta, gate, d_out):
+        if t.dtype != q.dtype:
+            raise TypeError("q, k, v, log_alpha, beta, gate and d_out must share one dtype")
+    st_shape = (B, H, Dk, Dv)
+    for name, t in (("initial_state", initial_state), ("d_final_state", d_final_state)):
+        if t is not None and (t.dtype != torch.float32 or tuple(t.shape) != st_shape):
+            raise ValueError(f"{name} must be fp32 [B, H, Dk, Dv]")
+    a = _abi.BwdArgs()
+    a.B, a.T, a.H, a.Dk, a.Dv, a.dtype = B, T, H, Dk, Dv, code
+    a.flags = 0 if clamp else _abi.KDA_FLAG_NO_CLAMP
+    n = ctypes.c_size_t(0)
+    rc = lib.kda_chunk_bwd_workspace_size(ctypes.byref(a), ctypes.byref(n))
+    if rc != _abi.KDA_OK:
+        raise KDAError(rc, "kda_chunk_bwd_workspace_size")
+    if workspace is None or workspace.numel() < n.value:
+        workspace = torch.empty(max(int(n.value), 16), dtype=torch.uint8, device=dev)
+    f32 = dict(dtype=torch.float32, device=dev)
+    g = dict(dq=torch.empty((B, T, H, Dk), **f32), dk=torch.empty((B, T, H, Dk), **f32),
+             dv=torch.empty((B, T, H, Dv), **f32), dlog_alpha=torch.empty((B, T, H, Dk), **f32),
+             dbeta=torch.empty((B, T, H), **f32), dgate=torch.empty((B, T, H, Dv), **f32),
+             dinitial_state=torch.empty(st_shape, **f32) if need_initial_state_grad else None)
+    _check_dev(dict(q=q, k=k, v=v, log_alpha=log_alpha, beta=beta, gate=gate, d_out=d_out,
+                    initial_state=initial_state, d_final_state=d_final_state), dev)
+    a.q, a.k, a.v, a.log_alpha, a.beta, a.gate = (_ptr(t) for t in (q, k, v, log_alpha, beta, gate))
+    a.d_out, a.initial_state, a.d_final_state = _ptr(d_out), _ptr(initial_state), _ptr(d_final_state)
+    a.dq, a.dk, a.dv, a.dlog_alpha = _ptr(g["dq"]), _ptr(g["dk"]), _ptr(g["dv"]), _ptr(g["dlog_alpha"])
+    a.dbeta, a.dgate, a.d_initial_state = _ptr(g["dbeta"]), _ptr(g["dgate"]), _ptr(g["dinitial_state"])
+    a.workspace, a.workspace_bytes = _ptr(workspace), workspace.numel()
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    rc = lib.kda_chunk_bwd(ctypes.byref(a), ctypes.c_void_p(stream))
+    if rc != _abi.KDA_OK:
+        raise KDAError(rc, "kda_chunk_bwd")
+    return g
 
 
 def combine_states(transition, offset, initial_state=None, segment_states=True, final_state=None):

@@ -9,7 +9,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libkda.so")
-SOURCES = ["kda_api.hip", "kda_prefill.hip", "kda_chunk64.hip", "kda_decode.hip", "kda_segment.hip", "kda_varlen.hip"]
+SOURCES = ["kda_api.hip", "kda_prefill.hip", "kda_chunk64.hip", "kda_decode.hip", "kda_segment.hip", "kda_varlen.hip",
+           "kda_backward.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",

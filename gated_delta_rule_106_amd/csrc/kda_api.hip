@@ -3,6 +3,7 @@
 #include <limits.h>
 
 #include "../../include/kda.h"
+#include "kda_backward.h"
 #include "kda_decode.h"
 #include "kda_prefill.h"
 #include "kda_segment.h"
@@ -104,6 +105,26 @@ int check_varlen(const kda_varlen_args* a, VarlenLayout* L) {
     L->off_co = L->off_s + align256((a->N + 1) * 8);
     L->off_soc = L->off_co + align256((a->N + 1) * 8);
     L->total = L->off_soc + align256(mc * 4);
+    return KDA_OK;
+}
+
+// Backward: sizes, dtype, head size and flags; fills the chunk count and workspace bytes.
+int check_bwd(const kda_bwd_args* a, int64_t* nchunks, int64_t* ws_total) {
+    if (!a) return KDA_ERR_NULL;
+    if (a->B < 0 || a->T < 0 || a->H < 0 || a->Dk <= 0 || a->Dv <= 0) return KDA_ERR_SHAPE;
+    if (a->dtype != KDA_F32 && a->dtype != KDA_BF16) return KDA_ERR_UNSUPPORTED;
+    if (a->Dk != a->Dv || (a->Dk != 64 && a->Dk != 128)) return KDA_ERR_UNSUPPORTED;
+    if ((a->flags & ~KDA_FLAG_NO_CLAMP) != 0) return KDA_ERR_UNSUPPORTED;
+    int64_t bt, bth, elems, bh, st, items, tmp;
+    if (!mul_ok(a->B, a->T, &bt) || !mul_ok(bt, a->H, &bth) || !mul_ok(bth, a->Dk, &elems) ||
+        !mul_ok(a->B, a->H, &bh) || !mul_ok(bh, a->Dk * a->Dv, &st))
+        return KDA_ERR_SHAPE;
+    if (bh > INT_MAX / 8) return KDA_ERR_SHAPE;  // one sweep workgroup per (b, h, 16 value columns)
+    const int64_t nc = (a->T + 63) / 64;
+    // per chunk: a record, two states and their scratch share stay below 1 MiB
+    if (!mul_ok(bh, nc, &items) || !mul_ok(items, (int64_t)1 << 20, &tmp)) return KDA_ERR_SHAPE;
+    *nchunks = nc;
+    *ws_total = kda::bwd_workspace_bytes((int)a->Dk, bh, nc);
     return KDA_OK;
 }
 
@@ -284,6 +305,51 @@ int kda_combine_states(const kda_combine_args* a, hipStream_t stream) {
     kda::CombineParams p{a->transition, a->offset, a->initial_state, a->segment_states, a->final_state,
                          a->P, bh};
     const hipError_t e = kda::launch_combine((int)a->Dk, p, stream);
+    return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+int kda_chunk_bwd_workspace_size(const kda_bwd_args* a, size_t* bytes) {
+    if (!a || !bytes) return KDA_ERR_NULL;
+    int64_t nc, ws;
+    const int st = check_bwd(a, &nc, &ws);
+    if (st != KDA_OK) return st;
+    *bytes = (size_t)ws;
+    return KDA_OK;
+}
+
+int kda_chunk_bwd(const kda_bwd_args* a, hipStream_t stream) {
+    if (!a) return KDA_ERR_NULL;
+    int64_t nc, need;
+    const int st = check_bwd(a, &nc, &need);
+    if (st != KDA_OK) return st;
+    const bool has_tokens = a->B * a->T * a->H > 0;
+    if (has_tokens) {
+        const void* req[] = {a->q, a->k, a->v, a->log_alpha, a->beta, a->gate, a->d_out,
+                             a->dq, a->dk, a->dv, a->dlog_alpha, a->dbeta, a->dgate};
+        for (const void* p : req)
+            if (!p) return KDA_ERR_NULL;
+        for (const void* p : req)
+            if (!aligned16(p)) return KDA_ERR_ALIGN;
+    }
+    if (!aligned16(a->initial_state) || !aligned16(a->d_final_state) || !aligned16(a->d_initial_state))
+        return KDA_ERR_ALIGN;
+    if (need > 0) {
+        if (!a->workspace) return KDA_ERR_WORKSPACE;
+        if ((int64_t)a->workspace_bytes < need) return KDA_ERR_WORKSPACE;
+        if (!aligned16(a->workspace)) return KDA_ERR_ALIGN;
+    }
+    if (a->B * a->H == 0) return KDA_OK;
+    if (!has_tokens && !a->d_initial_state) return KDA_OK;
+    kda::BwdParams p{a->q, a->k, a->v, a->log_alpha, a->beta, a->gate, a->d_out,
+                     a->initial_state, a->d_final_state, a->dq, a->dk, a->dv, a->dlog_alpha,
+                     a->dbeta, a->dgate, a->d_initial_state};
+    p.B = a->B;
+    p.T = a->T;
+    p.H = a->H;
+    p.NC = nc;
+    p.clamp = (a->flags & KDA_FLAG_NO_CLAMP) ? 0 : 1;
+    kda::bwd_layout((int)a->Dk, a->B * a->H, nc, a->workspace, p);
+    const hipError_t e = kda::launch_bwd(a->dtype == KDA_BF16, (int)a->Dk, p, stream);
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 

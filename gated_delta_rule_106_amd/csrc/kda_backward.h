@@ -1,0 +1,42 @@
+// Internal launch interface of the chunkwise backward pass (fp32 arithmetic).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kda {
+
+struct BwdParams {
+    const void* q;
+    const void* k;
+    const void* v;
+    const void* la;
+    const void* beta;
+    const void* gate;
+    const void* dy;
+    const float* s0;   // initial state [B, H, D, D] or null (zeros)
+    const float* dsT;  // gradient of the final state or null (zeros)
+    float* dq;
+    float* dk;
+    float* dv;
+    float* dla;
+    float* dbeta;
+    float* dgate;
+    float* ds0;        // gradient of the initial state or null
+    float* trans;      // per chunk: W, K-bar, b, R, Gamma_C
+    float* states;     // per chunk: the state at the chunk's start
+    float* dstates;    // per chunk: the gradient of the state at the chunk's end
+    float* scratch;    // per workgroup slot of the chunk kernels
+    int64_t B, T, H;
+    int64_t NC;        // chunks per sequence
+    int64_t slots;     // workgroups of the chunk kernels
+    int clamp;
+};
+
+// Workspace bytes of one call (sections: trans, states, dstates, scratch).
+int64_t bwd_workspace_bytes(int D, int64_t bh, int64_t nc);
+// Splits the workspace into its sections and fills p.slots.
+void bwd_layout(int D, int64_t bh, int64_t nc, void* ws, BwdParams& p);
+hipError_t launch_bwd(int dtype_bf16, int D, const BwdParams& p, hipStream_t stream);
+
+}  // namespace kda

@@ -1,0 +1,490 @@
+// Chunkwise backward pass of KDA: gradients of L = <dY, Y> + <dS_T, S_T> with
+// respect to q, k, v, log alpha, beta, the gate logits and the initial state.
+//
+// The forward it differentiates is the chunk-recurrent form (page "Kimi K3 report
+// walk-through", section "Compute paradigm"; the per-token step is page "3T models
+// are no longer magic", section "Gate 1: KDA makes it computable").  For one chunk
+// of C tokens that starts from the state S0, with g the inclusive cumulative
+// (clamped) log-decay per token and key channel, E = e^g and Gc = e^{g_C}:
+//   Kt = K*E,  Qt = Q*E,  Kb = K*e^{g_C - g}
+//   Bm_rs = sum_c k_rc k_sc e^{g_rc - g_sc} (s < r),  P_rs = sum_c q_rc k_sc e^{g_rc - g_sc} (s <= r)
+//   Li = (I + diag(beta) Bm)^-1
+//   X = V - Kt S0,  U = Li diag(beta) X,  O = Qt S0 + P U,  Y = O * sigmoid(Z)
+//   S_C = Diag(Gc) S0 + Kb^T U
+// Every pair factor is e^{g_r - g_s} with r >= s, so none exceeds 1.
+//
+// Three launches:
+//  1. kda_bwd_prep_kernel, one chunk per workgroup: W = Li diag(beta) Kt, Kb, Gc,
+//     b = Kb^T Li diag(beta) V and R = (Qt - P W)^T dO with dO = dY * sigmoid(Z).
+//  2. kda_bwd_sweep_kernel, one (b, h, 16 value columns) per workgroup (columns of
+//     the state evolve independently): the states at every chunk start,
+//     S_{n+1} = Diag(Gc) S_n - Kb^T (W S_n) + b, then the state gradients in reverse,
+//     dS_n = Diag(Gc) dS_{n+1} - W^T (Kb dS_{n+1}) + R (the transposed map).
+//  3. kda_bwd_grad_kernel, one chunk per workgroup: the adjoint of the chunk's
+//     steps above from S_n and dS_{n+1}; log alpha's gradient is the reverse
+//     cumulative sum of g's gradient within the chunk.
+// All arithmetic is fp32; the chunk kernels keep their intermediates in a scratch
+// slot of the workspace (one per workgroup, reused chunk after chunk).
+#include "kda_backward.h"
+#include "kda_device.h"
+
+namespace kda {
+namespace {
+
+constexpr int C = 64;             // tokens per chunk
+constexpr int NT = 256;           // threads per workgroup
+constexpr int TILE = 16;          // value columns per sweep workgroup
+constexpr int64_t kMaxSlots = 512;
+
+__device__ __forceinline__ float ex(float x) { return fast_exp2(x * kLog2e); }
+
+// fp32 offsets of the per-chunk record written by the prep kernel.
+template <int D>
+struct Rec {
+    static constexpr int64_t CD = (int64_t)C * D, DD = (int64_t)D * D;
+    static constexpr int64_t W = 0, KBAR = CD, BV = 2 * CD, R = 2 * CD + DD, GC = 2 * CD + 2 * DD;
+    static constexpr int64_t SIZE = 2 * CD + 2 * DD + D;
+};
+
+// fp32 offsets inside one scratch slot.  C x D row-major blocks, then D x C
+// (channel-major) copies, then C x C blocks, then two C-vectors.
+template <int D>
+struct Scr {
+    static constexpr int64_t CD = (int64_t)C * D, CC = (int64_t)C * C;
+    static constexpr int64_t K = 0, Q = CD, V = 2 * CD, G = 3 * CD, DO = 4 * CD, EG = 5 * CD, KT = 6 * CD,
+                             QT = 7 * CD, KB = 8 * CD, X = 9 * CD, U = 10 * CD, O = 11 * CD, DU = 12 * CD,
+                             DW = 13 * CD, DKB = 14 * CD, DQ = 15 * CD, DKT = 16 * CD, KTR = 17 * CD,
+                             QTR = 18 * CD, GTR = 19 * CD;
+    static constexpr int64_t BM = 20 * CD, PM = BM + CC, LI = BM + 2 * CC, DP = BM + 3 * CC,
+                             DLI = BM + 4 * CC, EM = BM + 5 * CC, DA = BM + 6 * CC;
+    static constexpr int64_t BETA = BM + 7 * CC, DBX = BETA + C;
+    static constexpr int64_t SIZE = DBX + C;
+};
+
+// out(m, n) for m < M, n < N of sum_{k < K} a(m, k) b(k, n) over the workgroup:
+// each thread owns BM x 4 blocks of outputs and keeps them in registers.
+template <int M, int N, int BM, class FA, class FB, class FO>
+__device__ __forceinline__ void mm(int K, FA a, FB b, FO o) {
+    static_assert(M % BM == 0 && N % 4 == 0, "block shape");
+    constexpr int NB = (M / BM) * (N / 4);
+    for (int blk = threadIdx.x; blk < NB; blk += NT) {
+        const int m0 = (blk / (N / 4)) * BM, n0 = (blk % (N / 4)) * 4;
+        float acc[BM][4];
+#pragma unroll
+        for (int i = 0; i < BM; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[i][j] = 0.f;
+        for (int kk = 0; kk < K; ++kk) {
+            float bv[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) bv[j] = b(kk, n0 + j);
+#pragma unroll
+            for (int i = 0; i < BM; ++i) {
+                const float av = a(m0 + i, kk);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(av, bv[j], acc[i][j]);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < BM; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) o(m0 + i, n0 + j, acc[i][j]);
+    }
+}
+
+struct ChunkPos {
+    int64_t b, h, t0;
+    int L;  // tokens of the chunk inside the sequence (the rest is padding)
+};
+
+__device__ __forceinline__ ChunkPos chunk_pos(const BwdParams& p, int64_t item) {
+    ChunkPos cp;
+    const int64_t bh = item / p.NC, n = item - bh * p.NC;
+    cp.b = bh / p.H;
+    cp.h = bh - cp.b * p.H;
+    cp.t0 = n * C;
+    cp.L = (int)(p.T - cp.t0 < C ? p.T - cp.t0 : C);
+    return cp;
+}
+
+template <int D>
+__device__ __forceinline__ int64_t elem(const BwdParams& p, const ChunkPos& cp, int r, int c) {
+    return ((cp.b * p.T + cp.t0 + r) * p.H + cp.h) * D + c;
+}
+
+// Steps shared by the prep and gradient kernels: the chunk's inputs in fp32 (zero
+// past the sequence's end, which makes the padding tokens identity steps), g, the
+// decayed operands, Bm, P and Li.
+template <int D, class In>
+__device__ void chunk_common(const BwdParams& p, const ChunkPos& cp, float* s) {
+    using S = Scr<D>;
+    using raw = typename In::raw_t;
+    for (int idx = threadIdx.x; idx < C * D; idx += NT) {
+        const int r = idx / D, c = idx - r * D;
+        float kv = 0.f, qv = 0.f, vv = 0.f, lv = 0.f, dov = 0.f;
+        if (r < cp.L) {
+            const int64_t e = elem<D>(p, cp, r, c);
+            kv = In::load(static_cast<const raw*>(p.k), e);
+            qv = In::load(static_cast<const raw*>(p.q), e);
+            vv = In::load(static_cast<const raw*>(p.v), e);
+            lv = clamp_log_alpha(In::load(static_cast<const raw*>(p.la), e), p.clamp != 0);
+            dov = In::load(static_cast<const raw*>(p.dy), e) *
+                  sigmoidf_(In::load(static_cast<const raw*>(p.gate), e));
+        }
+        s[S::K + idx] = kv;
+        s[S::Q + idx] = qv;
+        s[S::V + idx] = vv;
+        s[S::G + idx] = lv;
+        s[S::DO + idx] = dov;
+        s[S::KTR + c * C + r] = kv;
+        s[S::QTR + c * C + r] = qv;
+    }
+    if (threadIdx.x < C) {
+        const int r = threadIdx.x;
+        s[S::BETA + r] =
+            r < cp.L ? In::load(static_cast<const raw*>(p.beta), (cp.b * p.T + cp.t0 + r) * p.H + cp.h) : 0.f;
+    }
+    __syncthreads();
+    // g_r = sum_{s <= r} lambda_s, per key channel
+    if (threadIdx.x < D) {
+        const int c = threadIdx.x;
+        float acc = 0.f;
+        for (int r = 0; r < C; ++r) {
+            acc += s[S::G + r * D + c];
+            s[S::G + r * D + c] = acc;
+            s[S::GTR + c * C + r] = acc;
+        }
+    }
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < C * D; idx += NT) {
+        const int c = idx % D;
+        const float g = s[S::G + idx], gc = s[S::G + (C - 1) * D + c];
+        const float eg = ex(g), kv = s[S::K + idx];
+        s[S::EG + idx] = eg;
+        s[S::KT + idx] = kv * eg;
+        s[S::QT + idx] = s[S::Q + idx] * eg;
+        s[S::KB + idx] = kv * ex(gc - g);
+    }
+    for (int idx = threadIdx.x; idx < C * C; idx += NT) {
+        const int r = idx / C, sc = idx - r * C;
+        float bs = 0.f, ps = 0.f;
+        if (sc <= r) {
+            for (int c = 0; c < D; ++c) {
+                const float e = ex(s[S::GTR + c * C + r] - s[S::GTR + c * C + sc]);
+                const float ks = s[S::KTR + c * C + sc] * e;
+                bs = fmaf(s[S::KTR + c * C + r], ks, bs);
+                ps = fmaf(s[S::QTR + c * C + r], ks, ps);
+            }
+        }
+        s[S::BM + idx] = sc < r ? bs : 0.f;
+        s[S::PM + idx] = sc <= r ? ps : 0.f;
+    }
+    __syncthreads();
+    // Li = (I + diag(beta) Bm)^-1 by forward substitution, one column per lane
+    if (threadIdx.x < C) {
+        const int sc = threadIdx.x;
+        for (int r = 0; r < C; ++r) {
+            float acc = 0.f;
+            for (int m = 0; m < r; ++m) acc = fmaf(s[S::BM + r * C + m], s[S::LI + m * C + sc], acc);
+            s[S::LI + r * C + sc] = r == sc ? 1.f : (r < sc ? 0.f : -s[S::BETA + r] * acc);
+        }
+    }
+    __syncthreads();
+}
+
+template <int D, class In>
+__global__ __launch_bounds__(NT) void kda_bwd_prep_kernel(BwdParams p) {
+    using S = Scr<D>;
+    using RC = Rec<D>;
+    float* s = p.scratch + (int64_t)blockIdx.x * S::SIZE;
+    const int64_t items = p.B * p.H * p.NC;
+    for (int64_t item = blockIdx.x; item < items; item += gridDim.x) {
+        const ChunkPos cp = chunk_pos(p, item);
+        chunk_common<D, In>(p, cp, s);
+        float* tr = p.trans + item * RC::SIZE;
+        const float* beta = s + S::BETA;
+        // W = Li diag(beta) Kt;  U~ = Li diag(beta) V (kept in the X block)
+        mm<C, D, 4>(C, [&](int m, int k) { return s[S::LI + m * C + k] * beta[k]; },
+                    [&](int k, int n) { return s[S::KT + k * D + n]; },
+                    [&](int m, int n, float a) { tr[RC::W + m * D + n] = a; });
+        mm<C, D, 4>(C, [&](int m, int k) { return s[S::LI + m * C + k] * beta[k]; },
+                    [&](int k, int n) { return s[S::V + k * D + n]; },
+                    [&](int m, int n, float a) { s[S::X + m * D + n] = a; });
+        for (int idx = threadIdx.x; idx < C * D; idx += NT) tr[RC::KBAR + idx] = s[S::KB + idx];
+        if (threadIdx.x < D) tr[RC::GC + threadIdx.x] = s[S::EG + (C - 1) * D + threadIdx.x];
+        __syncthreads();
+        // Qe = Qt - P W (kept in the U block);  b = Kb^T U~
+        mm<C, D, 4>(C, [&](int m, int k) { return s[S::PM + m * C + k]; },
+                    [&](int k, int n) { return tr[RC::W + k * D + n]; },
+                    [&](int m, int n, float a) { s[S::U + m * D + n] = s[S::QT + m * D + n] - a; });
+        mm<D, D, 4>(C, [&](int m, int k) { return s[S::KB + k * D + m]; },
+                    [&](int k, int n) { return s[S::X + k * D + n]; },
+                    [&](int m, int n, float a) { tr[RC::BV + m * D + n] = a; });
+        __syncthreads();
+        // R = Qe^T dO
+        mm<D, D, 4>(C, [&](int m, int k) { return s[S::U + k * D + m]; },
+                    [&](int k, int n) { return s[S::DO + k * D + n]; },
+                    [&](int m, int n, float a) { tr[RC::R + m * D + n] = a; });
+        __syncthreads();  // the slot is reused by the next chunk
+    }
+}
+
+template <int D>
+__global__ __launch_bounds__(NT) void kda_bwd_sweep_kernel(BwdParams p) {
+    using RC = Rec<D>;
+    __shared__ float St[D * TILE];
+    __shared__ float Y[C * TILE];
+    constexpr int tiles = D / TILE;
+    const int64_t bh = blockIdx.x / tiles;
+    const int col0 = (int)(blockIdx.x - bh * tiles) * TILE;
+    const int64_t DD = (int64_t)D * D;
+    for (int idx = threadIdx.x; idx < D * TILE; idx += NT) {
+        const int c = idx / TILE, j = idx - c * TILE;
+        St[idx] = p.s0 ? p.s0[bh * DD + c * D + col0 + j] : 0.f;
+    }
+    __syncthreads();
+    for (int64_t n = 0; n < p.NC; ++n) {
+        const float* tr = p.trans + (bh * p.NC + n) * RC::SIZE;
+        float* st = p.states + (bh * p.NC + n) * DD;
+        for (int idx = threadIdx.x; idx < D * TILE; idx += NT) {
+            const int c = idx / TILE, j = idx - c * TILE;
+            st[c * D + col0 + j] = St[idx];
+        }
+        mm<C, TILE, 1>(D, [&](int m, int k) { return tr[RC::W + m * D + k]; },
+                       [&](int k, int n2) { return St[k * TILE + n2]; },
+                       [&](int m, int n2, float a) { Y[m * TILE + n2] = a; });
+        __syncthreads();
+        mm<D, TILE, 1>(C, [&](int m, int k) { return tr[RC::KBAR + k * D + m]; },
+                       [&](int k, int n2) { return Y[k * TILE + n2]; },
+                       [&](int m, int n2, float a) {
+                           St[m * TILE + n2] = tr[RC::GC + m] * St[m * TILE + n2] - a + tr[RC::BV + m * D + col0 + n2];
+                       });
+        __syncthreads();
+    }
+    for (int idx = threadIdx.x; idx < D * TILE; idx += NT) {
+        const int c = idx / TILE, j = idx - c * TILE;
+        St[idx] = p.dsT ? p.dsT[bh * DD + c * D + col0 + j] : 0.f;
+    }
+    __syncthreads();
+    for (int64_t n = p.NC - 1; n >= 0; --n) {
+        const float* tr = p.trans + (bh * p.NC + n) * RC::SIZE;
+        float* dst = p.dstates + (bh * p.NC + n) * DD;
+        for (int idx = threadIdx.x; idx < D * TILE; idx += NT) {
+            const int c = idx / TILE, j = idx - c * TILE;
+            dst[c * D + col0 + j] = St[idx];
+        }
+        mm<C, TILE, 1>(D, [&](int m, int k) { return tr[RC::KBAR + m * D + k]; },
+                       [&](int k, int n2) { return St[k * TILE + n2]; },
+                       [&](int m, int n2, float a) { Y[m * TILE + n2] = a; });
+        __syncthreads();
+        mm<D, TILE, 1>(C, [&](int m, int k) { return tr[RC::W + k * D + m]; },
+                       [&](int k, int n2) { return Y[k * TILE + n2]; },
+                       [&](int m, int n2, float a) {
+                           St[m * TILE + n2] = tr[RC::GC + m] * St[m * TILE + n2] - a + tr[RC::R + m * D + col0 + n2];
+                       });
+        __syncthreads();
+    }
+    if (p.ds0) {
+        for (int idx = threadIdx.x; idx < D * TILE; idx += NT) {
+            const int c = idx / TILE, j = idx - c * TILE;
+            p.ds0[bh * DD + c * D + col0 + j] = St[idx];
+        }
+    }
+}
+
+template <int D, class In>
+__global__ __launch_bounds__(NT) void kda_bwd_grad_kernel(BwdParams p) {
+    using S = Scr<D>;
+    using raw = typename In::raw_t;
+    float* s = p.scratch + (int64_t)blockIdx.x * S::SIZE;
+    const int64_t items = p.B * p.H * p.NC;
+    const int64_t DD = (int64_t)D * D;
+    for (int64_t item = blockIdx.x; item < items; item += gridDim.x) {
+        const ChunkPos cp = chunk_pos(p, item);
+        chunk_common<D, In>(p, cp, s);
+        const float* S0 = p.states + item * DD;
+        const float* dSC = p.dstates + item * DD;
+        const float* beta = s + S::BETA;
+        // X = V - Kt S0
+        mm<C, D, 4>(D, [&](int m, int k) { return s[S::KT + m * D + k]; },
+                    [&](int k, int n) { return S0[k * D + n]; },
+                    [&](int m, int n, float a) { s[S::X + m * D + n] = s[S::V + m * D + n] - a; });
+        __syncthreads();
+        // U = Li diag(beta) X
+        mm<C, D, 4>(C, [&](int m, int k) { return s[S::LI + m * C + k] * beta[k]; },
+                    [&](int k, int n) { return s[S::X + k * D + n]; },
+                    [&](int m, int n, float a) { s[S::U + m * D + n] = a; });
+        __syncthreads();
+        // O = Qt S0 + P U;  dP = lower(dO U^T);  dKb = U dS_C^T;  dU = P^T dO + Kb dS_C
+        mm<C, D, 4>(D, [&](int m, int k) { return s[S::QT + m * D + k]; },
+                    [&](int k, int n) { return S0[k * D + n]; },
+                    [&](int m, int n, float a) { s[S::O + m * D + n] = a; });
+        mm<C, D, 4>(C, [&](int m, int k) { return s[S::PM + m * C + k]; },
+                    [&](int k, int n) { return s[S::U + k * D + n]; },
+                    [&](int m, int n, float a) { s[S::O + m * D + n] += a; });
+        mm<C, C, 4>(D, [&](int m, int k) { return s[S::DO + m * D + k]; },
+                    [&](int k, int n) { return s[S::U + n * D + k]; },
+                    [&](int m, int n, float a) { s[S::DP + m * C + n] = n <= m ? a : 0.f; });
+        mm<C, D, 4>(D, [&](int m, int k) { return s[S::U + m * D + k]; },
+                    [&](int k, int n) { return dSC[n * D + k]; },
+                    [&](int m, int n, float a) { s[S::DKB + m * D + n] = a; });
+        mm<C, D, 4>(C, [&](int m, int k) { return s[S::PM + k * C + m]; },
+                    [&](int k, int n) { return s[S::DO + k * D + n]; },
+                    [&](int m, int n, float a) { s[S::DU + m * D + n] = a; });
+        mm<C, D, 4>(D, [&](int m, int k) { return s[S::KB + m * D + k]; },
+                    [&](int k, int n) { return dSC[k * D + n]; },
+                    [&](int m, int n, float a) { s[S::DU + m * D + n] += a; });
+        __syncthreads();
+        // dZ = dY * O * sigmoid'(Z);  dLi = dU (diag(beta) X)^T, strictly lower part;  dW = Li^T dU
+        for (int idx = threadIdx.x; idx < cp.L * D; idx += NT) {
+            const int r = idx / D, c = idx - r * D;
+            const int64_t e = elem<D>(p, cp, r, c);
+            const float sg = sigmoidf_(In::load(static_cast<const raw*>(p.gate), e));
+            p.dgate[e] = In::load(static_cast<const raw*>(p.dy), e) * s[S::O + idx] * sg * (1.f - sg);
+        }
+        mm<C, C, 4>(D, [&](int m, int k) { return s[S::DU + m * D + k]; },
+                    [&](int k, int n) { return beta[n] * s[S::X + n * D + k]; },
+                    [&](int m, int n, float a) { s[S::DLI + m * C + n] = n < m ? a : 0.f; });
+        mm<C, D, 4>(C, [&](int m, int k) { return s[S::LI + k * C + m]; },
+                    [&](int k, int n) { return s[S::DU + k * D + n]; },
+                    [&](int m, int n, float a) { s[S::DW + m * D + n] = a; });
+        __syncthreads();
+        // dV = diag(beta) dW;  dbeta's X part;  E = Li^T dLi;  the S0 parts of dQ and dKt
+        for (int idx = threadIdx.x; idx < cp.L * D; idx += NT) {
+            const int r = idx / D, c = idx - r * D;
+            p.dv[elem<D>(p, cp, r, c)] = beta[r] * s[S::DW + idx];
+        }
+        if (threadIdx.x < C) {
+            const int r = threadIdx.x;
+            float acc = 0.f;
+            for (int j = 0; j < D; ++j) acc = fmaf(s[S::DW + r * D + j], s[S::X + r * D + j], acc);
+            s[S::DBX + r] = acc;
+        }
+        mm<C, C, 4>(C, [&](int m, int k) { return s[S::LI + k * C + m]; },
+                    [&](int k, int n) { return s[S::DLI + k * C + n]; },
+                    [&](int m, int n, float a) { s[S::EM + m * C + n] = a; });
+        mm<C, D, 4>(D, [&](int m, int k) { return s[S::DO + m * D + k]; },
+                    [&](int k, int n) { return S0[n * D + k]; },
+                    [&](int m, int n, float a) { s[S::DQ + m * D + n] = a * s[S::EG + m * D + n]; });
+        mm<C, D, 4>(D, [&](int m, int k) { return beta[m] * s[S::DW + m * D + k]; },
+                    [&](int k, int n) { return S0[n * D + k]; },
+                    [&](int m, int n, float a) { s[S::DKT + m * D + n] = -a * s[S::EG + m * D + n]; });
+        __syncthreads();
+        // dA = -(E Li^T), strictly lower part (the gradient with respect to diag(beta) Bm)
+        mm<C, C, 4>(C, [&](int m, int k) { return s[S::EM + m * C + k]; },
+                    [&](int k, int n) { return s[S::LI + n * C + k]; },
+                    [&](int m, int n, float a) { s[S::DA + m * C + n] = n < m ? -a : 0.f; });
+        __syncthreads();
+        // pair terms of dq and dk (through P and Bm), the K-bar term, dg; dbeta
+        for (int idx = threadIdx.x; idx < C * D; idx += NT) {
+            const int r = idx / D, c = idx - r * D;
+            const float gr = s[S::G + idx];
+            float pq = 0.f, aq = 0.f, ak = 0.f, pk = 0.f;
+            for (int j = 0; j <= r; ++j) {
+                const float ke = s[S::K + j * D + c] * ex(gr - s[S::G + j * D + c]);
+                pq = fmaf(s[S::DP + r * C + j], ke, pq);
+                aq = fmaf(s[S::DA + r * C + j], ke, aq);
+            }
+            for (int j = r; j < C; ++j) {
+                const float e = ex(s[S::G + j * D + c] - gr);
+                ak = fmaf(beta[j] * s[S::DA + j * C + r], s[S::K + j * D + c] * e, ak);
+                pk = fmaf(s[S::DP + j * C + r], s[S::Q + j * D + c] * e, pk);
+            }
+            const float dqf = s[S::DQ + idx] + pq;
+            const float dktf = s[S::DKT + idx] + beta[r] * aq;
+            const float dkif = ak + pk;
+            const float dkbf = s[S::DKB + idx] * ex(s[S::G + (C - 1) * D + c] - gr);
+            const float kv = s[S::K + idx], qv = s[S::Q + idx];
+            if (r < cp.L) {
+                const int64_t e = elem<D>(p, cp, r, c);
+                p.dq[e] = dqf;
+                p.dk[e] = dktf + dkif + dkbf;
+            }
+            s[S::DQ + idx] = qv * dqf + kv * (dktf - dkif - dkbf);  // gradient of g
+            s[S::DKT + idx] = kv * dkbf;                             // its g_C share
+        }
+        if (threadIdx.x < C) {
+            const int r = threadIdx.x;
+            float acc = s[S::DBX + r];
+            for (int j = 0; j < r; ++j) acc = fmaf(s[S::DA + r * C + j], s[S::BM + r * C + j], acc);
+            if (r < cp.L) p.dbeta[(cp.b * p.T + cp.t0 + r) * p.H + cp.h] = acc;
+        }
+        __syncthreads();
+        // dlambda_r = sum_{r' >= r} dg_r', with g_C's extra terms from Kb and Diag(Gc) S0
+        if (threadIdx.x < D) {
+            const int c = threadIdx.x;
+            float dgc = 0.f;
+            for (int j = 0; j < D; ++j) dgc = fmaf(dSC[c * D + j], S0[c * D + j], dgc);
+            float acc = dgc * s[S::EG + (C - 1) * D + c];
+            for (int r = 0; r < C; ++r) acc += s[S::DKT + r * D + c];
+            for (int r = C - 1; r >= 0; --r) {
+                acc += s[S::DQ + r * D + c];
+                if (r < cp.L) {
+                    const int64_t e = elem<D>(p, cp, r, c);
+                    const float l = In::load(static_cast<const raw*>(p.la), e);
+                    const bool live = p.clamp == 0 || (l >= kLogAlphaMin && l <= 0.f);
+                    p.dla[e] = live ? acc : 0.f;
+                }
+            }
+        }
+        __syncthreads();  // the slot is reused by the next chunk
+    }
+}
+
+int64_t align256(int64_t x) { return (x + 255) / 256 * 256; }
+
+template <int D>
+int64_t section_bytes(int64_t bh, int64_t nc, int64_t* trans, int64_t* states, int64_t* slots) {
+    const int64_t items = bh * nc;
+    *trans = align256(items * Rec<D>::SIZE * 4);
+    *states = align256(items * (int64_t)D * D * 4);
+    *slots = items < kMaxSlots ? items : kMaxSlots;
+    return *trans + 2 * *states + align256(*slots * Scr<D>::SIZE * 4);
+}
+
+template <int D, class In>
+hipError_t launch_d(const BwdParams& p, hipStream_t stream) {
+    const int64_t items = p.B * p.H * p.NC;
+    if (items > 0) {
+        hipLaunchKernelGGL((kda_bwd_prep_kernel<D, In>), dim3((unsigned)p.slots), dim3(NT), 0, stream, p);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    const int64_t bh = p.B * p.H;
+    if (bh > 0) {
+        hipLaunchKernelGGL((kda_bwd_sweep_kernel<D>), dim3((unsigned)(bh * (D / TILE))), dim3(NT), 0, stream, p);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    if (items > 0)
+        hipLaunchKernelGGL((kda_bwd_grad_kernel<D, In>), dim3((unsigned)p.slots), dim3(NT), 0, stream, p);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+int64_t bwd_workspace_bytes(int D, int64_t bh, int64_t nc) {
+    int64_t t, s, k;
+    return D == 64 ? section_bytes<64>(bh, nc, &t, &s, &k) : section_bytes<128>(bh, nc, &t, &s, &k);
+}
+
+void bwd_layout(int D, int64_t bh, int64_t nc, void* ws, BwdParams& p) {
+    int64_t t, s, k;
+    if (D == 64)
+        section_bytes<64>(bh, nc, &t, &s, &k);
+    else
+        section_bytes<128>(bh, nc, &t, &s, &k);
+    unsigned char* w = static_cast<unsigned char*>(ws);
+    p.trans = reinterpret_cast<float*>(w);
+    p.states = reinterpret_cast<float*>(w + t);
+    p.dstates = reinterpret_cast<float*>(w + t + s);
+    p.scratch = reinterpret_cast<float*>(w + t + 2 * s);
+    p.slots = k;
+}
+
+hipError_t launch_bwd(int dtype_bf16, int D, const BwdParams& p, hipStream_t stream) {
+    if (D == 64) return dtype_bf16 ? launch_d<64, InBF16>(p, stream) : launch_d<64, InF32>(p, stream);
+    return dtype_bf16 ? launch_d<128, InBF16>(p, stream) : launch_d<128, InF32>(p, stream);
+}
+
+}  // namespace kda

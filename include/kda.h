@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define KDA_VERSION 2
+#define KDA_VERSION 3
 
 /* element types */
 #define KDA_F32 0  /* IEEE binary32 */
@@ -254,6 +254,59 @@ typedef struct kda_combine_args {
 } kda_combine_args;
 
 int kda_combine_states(const kda_combine_args *a, hipStream_t stream);
+
+/*
+ * Arguments of kda_chunk_bwd: the gradients of a scalar loss
+ *   L = sum(d_out * out) + sum(d_final_state * S_T)
+ * through the forward that kda_chunk_fwd computes (fp32 out, no preparation
+ * flags), with respect to every input.  The reverse mode of the per-token step
+ * (page "3T models are no longer magic", section "Gate 1: KDA makes it
+ * computable") is taken over the chunk-recurrent form (page "Kimi K3 report
+ * walk-through", section "Compute paradigm") with 64-token chunks.
+ *   q, k, v, log_alpha, beta, gate: the forward's inputs, laid out as in
+ *     kda_fwd_args, all of `dtype`.
+ *   d_out: [B, T, H, Dv] of `dtype`, the gradient of L with respect to out.
+ *   initial_state: fp32 [B, H, Dk, Dv] or NULL (zeros), as in the forward.
+ *   d_final_state: fp32 [B, H, Dk, Dv] or NULL (zeros).
+ *   dq, dk, dlog_alpha: fp32 [B, T, H, Dk]; dv, dgate: fp32 [B, T, H, Dv];
+ *   dbeta: fp32 [B, T, H]; all required when B*T*H > 0.  dlog_alpha is zero
+ *     where the clamp of log alpha is active (outside [ln 0.0067, 0]).
+ *   d_initial_state: fp32 [B, H, Dk, Dv] or NULL (not returned).
+ *   flags: KDA_FLAG_NO_CLAMP only.
+ *   workspace: at least kda_chunk_bwd_workspace_size bytes, 256-byte aligned.
+ *     It holds a per-chunk record (two chunk x Dk blocks, two Dk x Dv blocks),
+ *     the state at every chunk start and its gradient at every chunk end, and
+ *     one scratch slot per workgroup of the chunk kernels (at most 512).
+ * No output may overlap an input or another output.
+ */
+typedef struct kda_bwd_args {
+    int64_t B, T, H, Dk, Dv;
+    int32_t dtype;  /* q, k, v, log_alpha, beta, gate, d_out */
+    uint32_t flags;
+    const void *q;
+    const void *k;
+    const void *v;
+    const void *log_alpha;
+    const void *beta;
+    const void *gate;
+    const void *d_out;
+    const float *initial_state;
+    const float *d_final_state;
+    float *dq;
+    float *dk;
+    float *dv;
+    float *dlog_alpha;
+    float *dbeta;
+    float *dgate;
+    float *d_initial_state;
+    void *workspace;
+    size_t workspace_bytes;
+} kda_bwd_args;
+
+/* Workspace bytes kda_chunk_bwd needs for these sizes (host only).  Returns a status. */
+int kda_chunk_bwd_workspace_size(const kda_bwd_args *a, size_t *bytes);
+/* Chunkwise backward pass.  Returns a status. */
+int kda_chunk_bwd(const kda_bwd_args *a, hipStream_t stream);
 
 /*
  * Arguments of kda_decode_step: one token per (b, h).

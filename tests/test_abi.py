@@ -36,7 +36,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.kda_version() == 2
+    assert lib.kda_version() == 3
     for code in range(-6, 1):
         assert lib.kda_status_str(code).decode()
     assert lib.kda_status_str(12345).decode() == "unknown status"
@@ -54,8 +54,11 @@ int main(void) {
          offsetof(kda_decode_args, q), offsetof(kda_decode_args, state),
          sizeof(kda_combine_args), offsetof(kda_combine_args, transition),
          offsetof(kda_combine_args, final_state));
-  printf("%zu %zu %zu %zu\n", sizeof(kda_varlen_args), offsetof(kda_varlen_args, cu_seqlens),
+  printf("%zu %zu %zu %zu ", sizeof(kda_varlen_args), offsetof(kda_varlen_args, cu_seqlens),
          offsetof(kda_varlen_args, snapshot_every), offsetof(kda_varlen_args, workspace_bytes));
+  printf("%zu %zu %zu %zu %zu\n", sizeof(kda_bwd_args), offsetof(kda_bwd_args, q),
+         offsetof(kda_bwd_args, d_final_state), offsetof(kda_bwd_args, d_initial_state),
+         offsetof(kda_bwd_args, workspace_bytes));
   return 0;
 }''')
     exe = tmp_path / "layout"
@@ -68,7 +71,9 @@ int main(void) {
             ctypes.sizeof(_abi.CombineArgs), _abi.CombineArgs.transition.offset,
             _abi.CombineArgs.final_state.offset,
             ctypes.sizeof(_abi.VarlenArgs), _abi.VarlenArgs.cu_seqlens.offset,
-            _abi.VarlenArgs.snapshot_every.offset, _abi.VarlenArgs.workspace_bytes.offset]
+            _abi.VarlenArgs.snapshot_every.offset, _abi.VarlenArgs.workspace_bytes.offset,
+            ctypes.sizeof(_abi.BwdArgs), _abi.BwdArgs.q.offset, _abi.BwdArgs.d_final_state.offset,
+            _abi.BwdArgs.d_initial_state.offset, _abi.BwdArgs.workspace_bytes.offset]
     assert got == want
 
 
@@ -313,3 +318,56 @@ def test_binding_refuses_cpu_tensors():
         kda.chunk_summary(x, x, x, torch.zeros(1, 16, 1))
     with pytest.raises(ValueError):
         kda.combine_states(torch.zeros(2, 1, 1, 64, 64), torch.zeros(2, 1, 1, 64, 64))
+    with pytest.raises(ValueError):
+        kda.chunk_bwd(x, x, x, x, torch.zeros(1, 16, 1), x, x)
+
+
+def _good_bwd(B=1, T=100, H=2, D=128):
+    a = _abi.BwdArgs()
+    a.B, a.T, a.H, a.Dk, a.Dv, a.dtype = B, T, H, D, D, _abi.KDA_BF16
+    for i, name in enumerate(("q", "k", "v", "log_alpha", "beta", "gate", "d_out", "dq", "dk", "dv",
+                              "dlog_alpha", "dbeta", "dgate")):
+        setattr(a, name, 0x100000 * (i + 1))
+    return a
+
+
+def test_bwd_workspace_size(lib):
+    """Per (b, h, chunk of 64): a record (2 x 64 x D + 2 x D x D + D floats), the state at
+    the chunk start and the gradient at its end (D x D floats each), and one scratch slot
+    per chunk-kernel workgroup (at most 512), every section rounded up to 256 bytes."""
+    r256 = lambda x: (x + 255) // 256 * 256
+    for B, T, H, D in ((1, 100, 2, 128), (2, 64, 3, 64), (1, 4096, 8, 128), (1, 1, 1, 64)):
+        a = _good_bwd(B, T, H, D)
+        n = ctypes.c_size_t(0)
+        assert lib.kda_chunk_bwd_workspace_size(ctypes.byref(a), ctypes.byref(n)) == _abi.KDA_OK
+        items = B * H * ((T + 63) // 64)
+        rec = 2 * 64 * D + 2 * D * D + D
+        slot = 20 * 64 * D + 7 * 64 * 64 + 2 * 64
+        want = r256(items * rec * 4) + 2 * r256(items * D * D * 4) + r256(min(items, 512) * slot * 4)
+        assert n.value == want
+    a = _good_bwd(T=0)
+    assert lib.kda_chunk_bwd_workspace_size(ctypes.byref(a), ctypes.byref(n)) == _abi.KDA_OK and n.value == 0
+    assert lib.kda_chunk_bwd_workspace_size(None, ctypes.byref(n)) == _abi.KDA_ERR_NULL
+
+
+@pytest.mark.parametrize("mutate,code", [
+    (lambda a: setattr(a, "T", -1), _abi.KDA_ERR_SHAPE),
+    (lambda a: setattr(a, "T", 2 ** 62), _abi.KDA_ERR_SHAPE),
+    (lambda a: setattr(a, "dtype", 7), _abi.KDA_ERR_UNSUPPORTED),
+    (lambda a: setattr(a, "Dv", 64), _abi.KDA_ERR_UNSUPPORTED),
+    (lambda a: setattr(a, "flags", _abi.KDA_FLAG_QK_L2NORM), _abi.KDA_ERR_UNSUPPORTED),
+    (lambda a: setattr(a, "flags", _abi.KDA_FLAG_NO_SEGMENT_SCAN), _abi.KDA_ERR_UNSUPPORTED),
+    (lambda a: setattr(a, "d_out", None), _abi.KDA_ERR_NULL),
+    (lambda a: setattr(a, "dbeta", None), _abi.KDA_ERR_NULL),
+    (lambda a: setattr(a, "dgate", 0x700008), _abi.KDA_ERR_ALIGN),
+    (lambda a: setattr(a, "d_initial_state", 0x900004), _abi.KDA_ERR_ALIGN),
+    (lambda a: None, _abi.KDA_ERR_WORKSPACE),  # no workspace given
+    (lambda a: (setattr(a, "workspace", 0x2000000), setattr(a, "workspace_bytes", 4096)), _abi.KDA_ERR_WORKSPACE),
+    (lambda a: setattr(a, "B", 0), _abi.KDA_OK),
+    (lambda a: setattr(a, "T", 0), _abi.KDA_OK),  # no tokens and no initial-state gradient asked for
+])
+def test_bwd_validation(lib, mutate, code):
+    a = _good_bwd()
+    mutate(a)
+    assert lib.kda_chunk_bwd(ctypes.byref(a), None) == code
+    assert lib.kda_chunk_bwd(None, None) == _abi.KDA_ERR_NULL
