@@ -366,6 +366,53 @@ def bench_fused_prep(kda, wl, steps, warmup, n_sets, dev, stream):
     return res
 
 
+def backward_bytes(wl) -> int:
+    """Algorithmic HBM bytes of one backward call: the forward's inputs and d_out read
+    once (bf16), the six fp32 gradients written once, plus the fp32 initial state and
+    its gradient when present."""
+    esz = 2 if wl.dtype == "bf16" else 4
+    per_tok = wl.H * ((4 * wl.Dk + 2 * wl.Dv) * esz + esz + 4 * (3 * wl.Dk + 2 * wl.Dv) + 4)
+    states = wl.B * wl.H * wl.Dk * wl.Dv * 4 * (2 if wl.init_state else 0)
+    return wl.B * wl.T * per_tok + states
+
+
+def bench_backward(kda, wl, steps, warmup, dev, stream):
+    """kda_chunk_bwd on the headline shape (gradients of sum(d_out * y) through the
+    forward; fp32 arithmetic), timed like the forward, and the forward call beside it."""
+    import torch
+    from kda_workloads import make_inputs
+    x = to_dev(make_inputs(wl, seed=wl.seed), dev)
+    g = torch.Generator(device="cpu").manual_seed(wl.seed + 7)
+    x["dy"] = torch.randn((wl.B, wl.T, wl.H, wl.Dv), generator=g).to(wl.torch_dtype).to(dev)
+    x["bws"] = None
+
+    def bwd(x):
+        kda.chunk_bwd(*(x[k] for k in KEYS), x["dy"], initial_state=x.get("initial_state"),
+                      workspace=x["bws"], need_initial_state_grad=False)
+    # first call sizes the workspace; keep it for the timed calls
+    out = kda.chunk_bwd(*(x[k] for k in KEYS), x["dy"], initial_state=x.get("initial_state"))
+    del out
+    import ctypes
+    from gated_delta_rule_106_amd import _abi
+    a = _abi.BwdArgs()
+    a.B, a.T, a.H, a.Dk, a.Dv = wl.B, wl.T, wl.H, wl.Dk, wl.Dv
+    a.dtype = _abi.KDA_BF16 if wl.dtype == "bf16" else _abi.KDA_F32
+    n = ctypes.c_size_t(0)
+    assert _abi.load().kda_chunk_bwd_workspace_size(ctypes.byref(a), ctypes.byref(n)) == 0
+    x["bws"] = torch.empty(int(n.value), dtype=torch.uint8, device=dev)
+    _, t_b = time_calls(bwd, [x], steps, warmup, stream)
+    toks = wl.B * wl.T
+    byt = backward_bytes(wl)
+    res = {"workload": wl.name, "us_per_call": 1e3 * t_b, "tokens_per_s": toks / (t_b / 1e3),
+           "alg_bytes_per_call": byt, "alg_gbs": byt / (t_b / 1e3) / 1e9,
+           "workspace_bytes": int(n.value),
+           "compute": "fp32 (inputs bf16, gradients fp32)"}
+    log(f"backward {wl.name}: {res['us_per_call']:.1f} us/call, {res['tokens_per_s']:.3e} tok/s")
+    del x
+    torch.cuda.empty_cache()
+    return res
+
+
 def bench_varlen(kda, steps, warmup, dev, stream, N=32, H=8, snapshot_every=512):
     """A mixed-length batch (N sequences, lengths log-uniform in [64, 8192), seeded; the
     headline's distributions and head size) through the variable-length call, with and
@@ -451,6 +498,8 @@ def main():
                     help="skip the mixed-length batch (variable-length call, snapshots)")
     ap.add_argument("--no-fused-prep", action="store_true",
                     help="skip the headline prefill with the preparation fused in")
+    ap.add_argument("--no-backward", action="store_true",
+                    help="skip the backward pass on the headline shape")
     ap.add_argument("--no-context-parallel", action="store_true",
                     help="skip the per-GPU share of the context-parallel split")
     ap.add_argument("--segment-sweep", action="store_true",
@@ -501,6 +550,9 @@ def main():
     vlen = None
     if not args.no_varlen:
         vlen = bench_varlen(kda, max(5, args.steps // 5), 2, dev, stream)
+    bwd = None
+    if not args.no_backward:
+        bwd = bench_backward(kda, head, max(5, args.steps // 5), 2, dev, stream)
     kcp = None
     if not args.no_context_parallel:
         kcp = bench_context_parallel(kda, max(5, args.steps // 5), 2, dev, stream)
@@ -536,6 +588,7 @@ def main():
         "context_parallel": kcp,
         "fused_prep": fprep,
         "varlen": vlen,
+        "backward": bwd,
         "source_digest": source_digest(),
     }
     if args.cpu_seconds > 0:

@@ -63,8 +63,8 @@ struct Scr {
 
 // out(m, n) for m < M, n < N of sum_{k < K} a(m, k) b(k, n) over the workgroup:
 // each thread owns BM x 4 blocks of outputs and keeps them in registers.
-template <int M, int N, int BM, class FA, class FB, class FO>
-__device__ __forceinline__ void mm(int K, FA a, FB b, FO o) {
+template <int M, int N, int K, int BM, class FA, class FB, class FO>
+__device__ __forceinline__ void mm(FA a, FB b, FO o) {
     static_assert(M % BM == 0 && N % 4 == 0, "block shape");
     constexpr int NB = (M / BM) * (N / 4);
     for (int blk = threadIdx.x; blk < NB; blk += NT) {
@@ -74,6 +74,7 @@ __device__ __forceinline__ void mm(int K, FA a, FB b, FO o) {
         for (int i = 0; i < BM; ++i)
 #pragma unroll
             for (int j = 0; j < 4; ++j) acc[i][j] = 0.f;
+#pragma unroll 8
         for (int kk = 0; kk < K; ++kk) {
             float bv[4];
 #pragma unroll
@@ -204,84 +205,120 @@ __global__ __launch_bounds__(NT) void kda_bwd_prep_kernel(BwdParams p) {
         float* tr = p.trans + item * RC::SIZE;
         const float* beta = s + S::BETA;
         // W = Li diag(beta) Kt;  U~ = Li diag(beta) V (kept in the X block)
-        mm<C, D, 4>(C, [&](int m, int k) { return s[S::LI + m * C + k] * beta[k]; },
+        mm<C, D, C, 4>([&](int m, int k) { return s[S::LI + m * C + k] * beta[k]; },
                     [&](int k, int n) { return s[S::KT + k * D + n]; },
                     [&](int m, int n, float a) { tr[RC::W + m * D + n] = a; });
-        mm<C, D, 4>(C, [&](int m, int k) { return s[S::LI + m * C + k] * beta[k]; },
+        mm<C, D, C, 4>([&](int m, int k) { return s[S::LI + m * C + k] * beta[k]; },
                     [&](int k, int n) { return s[S::V + k * D + n]; },
                     [&](int m, int n, float a) { s[S::X + m * D + n] = a; });
         for (int idx = threadIdx.x; idx < C * D; idx += NT) tr[RC::KBAR + idx] = s[S::KB + idx];
         if (threadIdx.x < D) tr[RC::GC + threadIdx.x] = s[S::EG + (C - 1) * D + threadIdx.x];
         __syncthreads();
         // Qe = Qt - P W (kept in the U block);  b = Kb^T U~
-        mm<C, D, 4>(C, [&](int m, int k) { return s[S::PM + m * C + k]; },
+        mm<C, D, C, 4>([&](int m, int k) { return s[S::PM + m * C + k]; },
                     [&](int k, int n) { return tr[RC::W + k * D + n]; },
                     [&](int m, int n, float a) { s[S::U + m * D + n] = s[S::QT + m * D + n] - a; });
-        mm<D, D, 4>(C, [&](int m, int k) { return s[S::KB + k * D + m]; },
+        mm<D, D, C, 4>([&](int m, int k) { return s[S::KB + k * D + m]; },
                     [&](int k, int n) { return s[S::X + k * D + n]; },
                     [&](int m, int n, float a) { tr[RC::BV + m * D + n] = a; });
         __syncthreads();
         // R = Qe^T dO
-        mm<D, D, 4>(C, [&](int m, int k) { return s[S::U + k * D + m]; },
+        mm<D, D, C, 4>([&](int m, int k) { return s[S::U + k * D + m]; },
                     [&](int k, int n) { return s[S::DO + k * D + n]; },
                     [&](int m, int n, float a) { tr[RC::R + m * D + n] = a; });
         __syncthreads();  // the slot is reused by the next chunk
     }
 }
 
+// LDS of the sweep kernel (fp32 offsets): the chunk's W and K-bar, the 16 columns of
+// its offset (b forwards, R backwards), Gamma_C, the state tile and Y.
+template <int D>
+struct SweepLds {
+    static constexpr int W = 0, KBAR = C * D, OFF = 2 * C * D, GC = OFF + D * TILE, ST = GC + D,
+                         Y = ST + D * TILE, TOTAL = Y + C * TILE;
+    static constexpr int NW4 = C * D / 4 / NT;    // float4 of W (and of K-bar) per thread
+    static constexpr int NO4 = D * TILE / 4 / NT; // float4 of the offset tile per thread
+};
+
+// Forwards: S <- Diag(Gc) S - Kb^T (W S) + b; backwards: dS <- Diag(Gc) dS - W^T (Kb dS) + R.
+// The record of the next chunk is read into registers while the current one is used.
 template <int D>
 __global__ __launch_bounds__(NT) void kda_bwd_sweep_kernel(BwdParams p) {
     using RC = Rec<D>;
-    __shared__ float St[D * TILE];
-    __shared__ float Y[C * TILE];
+    using L = SweepLds<D>;
+    extern __shared__ __align__(16) float lds[];
+    float* St = lds + L::ST;
+    float* Y = lds + L::Y;
     constexpr int tiles = D / TILE;
     const int64_t bh = blockIdx.x / tiles;
     const int col0 = (int)(blockIdx.x - bh * tiles) * TILE;
     const int64_t DD = (int64_t)D * D;
-    for (int idx = threadIdx.x; idx < D * TILE; idx += NT) {
-        const int c = idx / TILE, j = idx - c * TILE;
-        St[idx] = p.s0 ? p.s0[bh * DD + c * D + col0 + j] : 0.f;
-    }
-    __syncthreads();
-    for (int64_t n = 0; n < p.NC; ++n) {
-        const float* tr = p.trans + (bh * p.NC + n) * RC::SIZE;
-        float* st = p.states + (bh * p.NC + n) * DD;
+    const float* rec0 = p.trans + bh * p.NC * RC::SIZE;
+    // the next chunk's W, K-bar, offset tile and Gamma_C, in registers
+    float4 rw[L::NW4], rk[L::NW4], ro[L::NO4];
+    float4 rg = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int i = 0; i < L::NW4; ++i) rw[i] = rk[i] = rg;
+#pragma unroll
+    for (int i = 0; i < L::NO4; ++i) ro[i] = rg;
+    auto fetch = [&](const float* tr, int64_t off_base) {
+        const float4* w4 = reinterpret_cast<const float4*>(tr + RC::W);
+        const float4* k4 = reinterpret_cast<const float4*>(tr + RC::KBAR);
+#pragma unroll
+        for (int i = 0; i < L::NW4; ++i) {
+            rw[i] = w4[threadIdx.x + i * NT];
+            rk[i] = k4[threadIdx.x + i * NT];
+        }
+#pragma unroll
+        for (int i = 0; i < L::NO4; ++i) {
+            const int q = threadIdx.x + i * NT;  // row q / 4, columns col0 + 4 (q % 4) ..
+            ro[i] = *reinterpret_cast<const float4*>(tr + off_base + (q >> 2) * D + col0 + 4 * (q & 3));
+        }
+        if (threadIdx.x < D / 4) rg = reinterpret_cast<const float4*>(tr + RC::GC)[threadIdx.x];
+    };
+    auto stage = [&]() {
+#pragma unroll
+        for (int i = 0; i < L::NW4; ++i) {
+            reinterpret_cast<float4*>(lds + L::W)[threadIdx.x + i * NT] = rw[i];
+            reinterpret_cast<float4*>(lds + L::KBAR)[threadIdx.x + i * NT] = rk[i];
+        }
+#pragma unroll
+        for (int i = 0; i < L::NO4; ++i) reinterpret_cast<float4*>(lds + L::OFF)[threadIdx.x + i * NT] = ro[i];
+        if (threadIdx.x < D / 4) reinterpret_cast<float4*>(lds + L::GC)[threadIdx.x] = rg;
+    };
+#pragma unroll
+    for (int dir = 0; dir < 2; ++dir) {
+        const float* init = dir == 0 ? p.s0 : p.dsT;
         for (int idx = threadIdx.x; idx < D * TILE; idx += NT) {
             const int c = idx / TILE, j = idx - c * TILE;
-            st[c * D + col0 + j] = St[idx];
+            St[idx] = init ? init[bh * DD + c * D + col0 + j] : 0.f;
         }
-        mm<C, TILE, 1>(D, [&](int m, int k) { return tr[RC::W + m * D + k]; },
-                       [&](int k, int n2) { return St[k * TILE + n2]; },
-                       [&](int m, int n2, float a) { Y[m * TILE + n2] = a; });
-        __syncthreads();
-        mm<D, TILE, 1>(C, [&](int m, int k) { return tr[RC::KBAR + k * D + m]; },
-                       [&](int k, int n2) { return Y[k * TILE + n2]; },
-                       [&](int m, int n2, float a) {
-                           St[m * TILE + n2] = tr[RC::GC + m] * St[m * TILE + n2] - a + tr[RC::BV + m * D + col0 + n2];
-                       });
-        __syncthreads();
-    }
-    for (int idx = threadIdx.x; idx < D * TILE; idx += NT) {
-        const int c = idx / TILE, j = idx - c * TILE;
-        St[idx] = p.dsT ? p.dsT[bh * DD + c * D + col0 + j] : 0.f;
-    }
-    __syncthreads();
-    for (int64_t n = p.NC - 1; n >= 0; --n) {
-        const float* tr = p.trans + (bh * p.NC + n) * RC::SIZE;
-        float* dst = p.dstates + (bh * p.NC + n) * DD;
-        for (int idx = threadIdx.x; idx < D * TILE; idx += NT) {
-            const int c = idx / TILE, j = idx - c * TILE;
-            dst[c * D + col0 + j] = St[idx];
+        const int64_t off_base = dir == 0 ? RC::BV : RC::R;
+        if (p.NC > 0) fetch(rec0 + (dir == 0 ? 0 : p.NC - 1) * RC::SIZE, off_base);
+        for (int64_t i = 0; i < p.NC; ++i) {
+            const int64_t n = dir == 0 ? i : p.NC - 1 - i;
+            __syncthreads();  // the previous chunk's operands are no longer read
+            stage();
+            __syncthreads();
+            if (i + 1 < p.NC) fetch(rec0 + (dir == 0 ? n + 1 : n - 1) * RC::SIZE, off_base);
+            float* out = (dir == 0 ? p.states : p.dstates) + (bh * p.NC + n) * DD;
+            for (int idx = threadIdx.x; idx < D * TILE; idx += NT) {
+                const int c = idx / TILE, j = idx - c * TILE;
+                out[c * D + col0 + j] = St[idx];
+            }
+            // Y = W S (forwards) or Kb dS (backwards)
+            const float* A1 = lds + (dir == 0 ? L::W : L::KBAR);
+            const float* A2 = lds + (dir == 0 ? L::KBAR : L::W);
+            mm<C, TILE, D, 1>([&](int m, int k) { return A1[m * D + k]; },
+                              [&](int k, int n2) { return St[k * TILE + n2]; },
+                              [&](int m, int n2, float a) { Y[m * TILE + n2] = a; });
+            __syncthreads();
+            mm<D, TILE, C, 1>([&](int m, int k) { return A2[k * D + m]; },
+                              [&](int k, int n2) { return Y[k * TILE + n2]; },
+                              [&](int m, int n2, float a) {
+                                  St[m * TILE + n2] = lds[L::GC + m] * St[m * TILE + n2] - a + lds[L::OFF + m * TILE + n2];
+                              });
         }
-        mm<C, TILE, 1>(D, [&](int m, int k) { return tr[RC::KBAR + m * D + k]; },
-                       [&](int k, int n2) { return St[k * TILE + n2]; },
-                       [&](int m, int n2, float a) { Y[m * TILE + n2] = a; });
-        __syncthreads();
-        mm<D, TILE, 1>(C, [&](int m, int k) { return tr[RC::W + k * D + m]; },
-                       [&](int k, int n2) { return Y[k * TILE + n2]; },
-                       [&](int m, int n2, float a) {
-                           St[m * TILE + n2] = tr[RC::GC + m] * St[m * TILE + n2] - a + tr[RC::R + m * D + col0 + n2];
-                       });
         __syncthreads();
     }
     if (p.ds0) {
@@ -306,32 +343,32 @@ __global__ __launch_bounds__(NT) void kda_bwd_grad_kernel(BwdParams p) {
         const float* dSC = p.dstates + item * DD;
         const float* beta = s + S::BETA;
         // X = V - Kt S0
-        mm<C, D, 4>(D, [&](int m, int k) { return s[S::KT + m * D + k]; },
+        mm<C, D, D, 4>([&](int m, int k) { return s[S::KT + m * D + k]; },
                     [&](int k, int n) { return S0[k * D + n]; },
                     [&](int m, int n, float a) { s[S::X + m * D + n] = s[S::V + m * D + n] - a; });
         __syncthreads();
         // U = Li diag(beta) X
-        mm<C, D, 4>(C, [&](int m, int k) { return s[S::LI + m * C + k] * beta[k]; },
+        mm<C, D, C, 4>([&](int m, int k) { return s[S::LI + m * C + k] * beta[k]; },
                     [&](int k, int n) { return s[S::X + k * D + n]; },
                     [&](int m, int n, float a) { s[S::U + m * D + n] = a; });
         __syncthreads();
         // O = Qt S0 + P U;  dP = lower(dO U^T);  dKb = U dS_C^T;  dU = P^T dO + Kb dS_C
-        mm<C, D, 4>(D, [&](int m, int k) { return s[S::QT + m * D + k]; },
+        mm<C, D, D, 4>([&](int m, int k) { return s[S::QT + m * D + k]; },
                     [&](int k, int n) { return S0[k * D + n]; },
                     [&](int m, int n, float a) { s[S::O + m * D + n] = a; });
-        mm<C, D, 4>(C, [&](int m, int k) { return s[S::PM + m * C + k]; },
+        mm<C, D, C, 4>([&](int m, int k) { return s[S::PM + m * C + k]; },
                     [&](int k, int n) { return s[S::U + k * D + n]; },
                     [&](int m, int n, float a) { s[S::O + m * D + n] += a; });
-        mm<C, C, 4>(D, [&](int m, int k) { return s[S::DO + m * D + k]; },
+        mm<C, C, D, 4>([&](int m, int k) { return s[S::DO + m * D + k]; },
                     [&](int k, int n) { return s[S::U + n * D + k]; },
                     [&](int m, int n, float a) { s[S::DP + m * C + n] = n <= m ? a : 0.f; });
-        mm<C, D, 4>(D, [&](int m, int k) { return s[S::U + m * D + k]; },
+        mm<C, D, D, 4>([&](int m, int k) { return s[S::U + m * D + k]; },
                     [&](int k, int n) { return dSC[n * D + k]; },
                     [&](int m, int n, float a) { s[S::DKB + m * D + n] = a; });
-        mm<C, D, 4>(C, [&](int m, int k) { return s[S::PM + k * C + m]; },
+        mm<C, D, C, 4>([&](int m, int k) { return s[S::PM + k * C + m]; },
                     [&](int k, int n) { return s[S::DO + k * D + n]; },
                     [&](int m, int n, float a) { s[S::DU + m * D + n] = a; });
-        mm<C, D, 4>(D, [&](int m, int k) { return s[S::KB + m * D + k]; },
+        mm<C, D, D, 4>([&](int m, int k) { return s[S::KB + m * D + k]; },
                     [&](int k, int n) { return dSC[k * D + n]; },
                     [&](int m, int n, float a) { s[S::DU + m * D + n] += a; });
         __syncthreads();
@@ -342,10 +379,10 @@ __global__ __launch_bounds__(NT) void kda_bwd_grad_kernel(BwdParams p) {
             const float sg = sigmoidf_(In::load(static_cast<const raw*>(p.gate), e));
             p.dgate[e] = In::load(static_cast<const raw*>(p.dy), e) * s[S::O + idx] * sg * (1.f - sg);
         }
-        mm<C, C, 4>(D, [&](int m, int k) { return s[S::DU + m * D + k]; },
+        mm<C, C, D, 4>([&](int m, int k) { return s[S::DU + m * D + k]; },
                     [&](int k, int n) { return beta[n] * s[S::X + n * D + k]; },
                     [&](int m, int n, float a) { s[S::DLI + m * C + n] = n < m ? a : 0.f; });
-        mm<C, D, 4>(C, [&](int m, int k) { return s[S::LI + k * C + m]; },
+        mm<C, D, C, 4>([&](int m, int k) { return s[S::LI + k * C + m]; },
                     [&](int k, int n) { return s[S::DU + k * D + n]; },
                     [&](int m, int n, float a) { s[S::DW + m * D + n] = a; });
         __syncthreads();
@@ -360,18 +397,18 @@ __global__ __launch_bounds__(NT) void kda_bwd_grad_kernel(BwdParams p) {
             for (int j = 0; j < D; ++j) acc = fmaf(s[S::DW + r * D + j], s[S::X + r * D + j], acc);
             s[S::DBX + r] = acc;
         }
-        mm<C, C, 4>(C, [&](int m, int k) { return s[S::LI + k * C + m]; },
+        mm<C, C, C, 4>([&](int m, int k) { return s[S::LI + k * C + m]; },
                     [&](int k, int n) { return s[S::DLI + k * C + n]; },
                     [&](int m, int n, float a) { s[S::EM + m * C + n] = a; });
-        mm<C, D, 4>(D, [&](int m, int k) { return s[S::DO + m * D + k]; },
+        mm<C, D, D, 4>([&](int m, int k) { return s[S::DO + m * D + k]; },
                     [&](int k, int n) { return S0[n * D + k]; },
                     [&](int m, int n, float a) { s[S::DQ + m * D + n] = a * s[S::EG + m * D + n]; });
-        mm<C, D, 4>(D, [&](int m, int k) { return beta[m] * s[S::DW + m * D + k]; },
+        mm<C, D, D, 4>([&](int m, int k) { return beta[m] * s[S::DW + m * D + k]; },
                     [&](int k, int n) { return S0[n * D + k]; },
                     [&](int m, int n, float a) { s[S::DKT + m * D + n] = -a * s[S::EG + m * D + n]; });
         __syncthreads();
         // dA = -(E Li^T), strictly lower part (the gradient with respect to diag(beta) Bm)
-        mm<C, C, 4>(C, [&](int m, int k) { return s[S::EM + m * C + k]; },
+        mm<C, C, C, 4>([&](int m, int k) { return s[S::EM + m * C + k]; },
                     [&](int k, int n) { return s[S::LI + n * C + k]; },
                     [&](int m, int n, float a) { s[S::DA + m * C + n] = n < m ? -a : 0.f; });
         __syncthreads();
@@ -452,8 +489,13 @@ hipError_t launch_d(const BwdParams& p, hipStream_t stream) {
     }
     const int64_t bh = p.B * p.H;
     if (bh > 0) {
-        hipLaunchKernelGGL((kda_bwd_sweep_kernel<D>), dim3((unsigned)(bh * (D / TILE))), dim3(NT), 0, stream, p);
-        const hipError_t e = hipGetLastError();
+        auto ks = kda_bwd_sweep_kernel<D>;
+        constexpr int lds = SweepLds<D>::TOTAL * 4;
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(ks),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(ks, dim3((unsigned)(bh * (D / TILE))), dim3(NT), lds, stream, p);
+        e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
     if (items > 0)
