@@ -230,22 +230,36 @@ __global__ __launch_bounds__(NT) void kda_bwd_prep_kernel(BwdParams p) {
     }
 }
 
-// LDS of the sweep kernel (fp32 offsets): the chunk's W and K-bar, the 16 columns of
-// its offset (b forwards, R backwards), Gamma_C, the state tile and Y.
+// LDS of the sweep kernel (fp32 offsets): the chunk's W and K-bar (row pitch D + 4),
+// the 16 columns of its offset (b forwards, R backwards), Gamma_C, the state tile and
+// Y (row pitch 20).  The pitches put the four lane groups of an MFMA operand read on
+// disjoint banks.
 template <int D>
 struct SweepLds {
-    static constexpr int W = 0, KBAR = C * D, OFF = 2 * C * D, GC = OFF + D * TILE, ST = GC + D,
-                         Y = ST + D * TILE, TOTAL = Y + C * TILE;
+    static constexpr int DP = D + 4, TP = 20;
+    static constexpr int W = 0, KBAR = C * DP, OFF = 2 * C * DP, GC = OFF + D * TP, ST = GC + D,
+                         Y = ST + D * TP, TOTAL = Y + C * TP;
     static constexpr int NW4 = C * D / 4 / NT;    // float4 of W (and of K-bar) per thread
     static constexpr int NO4 = D * TILE / 4 / NT; // float4 of the offset tile per thread
 };
 
+// 16 k-steps of the fp32 MFMA: lane (m, g) gives A[m][k] and B[k][m] for
+// k = 16 kk + 4 g + c, c = 0..3, and accumulates D[4 g + i][m] in acc[i].
+__device__ __forceinline__ floatx4 mma16x4(const float (&a)[4], const float (&b)[4], floatx4 acc) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) acc = mma_f32_k4(a[c], b[c], acc);
+    return acc;
+}
+
 // Forwards: S <- Diag(Gc) S - Kb^T (W S) + b; backwards: dS <- Diag(Gc) dS - W^T (Kb dS) + R.
-// The record of the next chunk is read into registers while the current one is used.
+// Both products run on the fp32 MFMA: wave w forms rows 16 w .. 16 w + 15 of Y, then
+// row blocks w, w + 4, .. of the new state.  The record of the next chunk is read into
+// registers while the current one is used.
 template <int D>
 __global__ __launch_bounds__(NT) void kda_bwd_sweep_kernel(BwdParams p) {
     using RC = Rec<D>;
     using L = SweepLds<D>;
+    constexpr int DP = L::DP, TP = L::TP;
     extern __shared__ __align__(16) float lds[];
     float* St = lds + L::ST;
     float* Y = lds + L::Y;
@@ -254,6 +268,8 @@ __global__ __launch_bounds__(NT) void kda_bwd_sweep_kernel(BwdParams p) {
     const int col0 = (int)(blockIdx.x - bh * tiles) * TILE;
     const int64_t DD = (int64_t)D * D;
     const float* rec0 = p.trans + bh * p.NC * RC::SIZE;
+    const int lane = lane_id(), wave = wave_id();
+    const int m = lane & 15, g = lane >> 4;
     // the next chunk's W, K-bar, offset tile and Gamma_C, in registers
     float4 rw[L::NW4], rk[L::NW4], ro[L::NO4];
     float4 rg = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -279,11 +295,16 @@ __global__ __launch_bounds__(NT) void kda_bwd_sweep_kernel(BwdParams p) {
     auto stage = [&]() {
 #pragma unroll
         for (int i = 0; i < L::NW4; ++i) {
-            reinterpret_cast<float4*>(lds + L::W)[threadIdx.x + i * NT] = rw[i];
-            reinterpret_cast<float4*>(lds + L::KBAR)[threadIdx.x + i * NT] = rk[i];
+            const int q = threadIdx.x + i * NT;  // row q / (D / 4), columns 4 (q % (D / 4)) ..
+            const int at = (q / (D / 4)) * DP + 4 * (q % (D / 4));
+            *reinterpret_cast<float4*>(lds + L::W + at) = rw[i];
+            *reinterpret_cast<float4*>(lds + L::KBAR + at) = rk[i];
         }
 #pragma unroll
-        for (int i = 0; i < L::NO4; ++i) reinterpret_cast<float4*>(lds + L::OFF)[threadIdx.x + i * NT] = ro[i];
+        for (int i = 0; i < L::NO4; ++i) {
+            const int q = threadIdx.x + i * NT;
+            *reinterpret_cast<float4*>(lds + L::OFF + (q >> 2) * TP + 4 * (q & 3)) = ro[i];
+        }
         if (threadIdx.x < D / 4) reinterpret_cast<float4*>(lds + L::GC)[threadIdx.x] = rg;
     };
 #pragma unroll
@@ -291,7 +312,7 @@ __global__ __launch_bounds__(NT) void kda_bwd_sweep_kernel(BwdParams p) {
         const float* init = dir == 0 ? p.s0 : p.dsT;
         for (int idx = threadIdx.x; idx < D * TILE; idx += NT) {
             const int c = idx / TILE, j = idx - c * TILE;
-            St[idx] = init ? init[bh * DD + c * D + col0 + j] : 0.f;
+            St[c * TP + j] = init ? init[bh * DD + c * D + col0 + j] : 0.f;
         }
         const int64_t off_base = dir == 0 ? RC::BV : RC::R;
         if (p.NC > 0) fetch(rec0 + (dir == 0 ? 0 : p.NC - 1) * RC::SIZE, off_base);
@@ -304,27 +325,51 @@ __global__ __launch_bounds__(NT) void kda_bwd_sweep_kernel(BwdParams p) {
             float* out = (dir == 0 ? p.states : p.dstates) + (bh * p.NC + n) * DD;
             for (int idx = threadIdx.x; idx < D * TILE; idx += NT) {
                 const int c = idx / TILE, j = idx - c * TILE;
-                out[c * D + col0 + j] = St[idx];
+                out[c * D + col0 + j] = St[c * TP + j];
             }
-            // Y = W S (forwards) or Kb dS (backwards)
+            // Y = W S (forwards) or Kb dS (backwards): wave w owns rows 16 w ..
             const float* A1 = lds + (dir == 0 ? L::W : L::KBAR);
             const float* A2 = lds + (dir == 0 ? L::KBAR : L::W);
-            mm<C, TILE, D, 1>([&](int m, int k) { return A1[m * D + k]; },
-                              [&](int k, int n2) { return St[k * TILE + n2]; },
-                              [&](int m, int n2, float a) { Y[m * TILE + n2] = a; });
+            {
+                floatx4 acc = zero4();
+#pragma unroll
+                for (int kk = 0; kk < D / 16; ++kk) {
+                    const int k0 = 16 * kk + 4 * g;
+                    const float4 av = *reinterpret_cast<const float4*>(A1 + (16 * wave + m) * DP + k0);
+                    const float a[4] = {av.x, av.y, av.z, av.w};
+                    const float b[4] = {St[(k0 + 0) * TP + m], St[(k0 + 1) * TP + m], St[(k0 + 2) * TP + m],
+                                        St[(k0 + 3) * TP + m]};
+                    acc = mma16x4(a, b, acc);
+                }
+#pragma unroll
+                for (int r = 0; r < 4; ++r) Y[(16 * wave + 4 * g + r) * TP + m] = acc[r];
+            }
             __syncthreads();
-            mm<D, TILE, C, 1>([&](int m, int k) { return A2[k * D + m]; },
-                              [&](int k, int n2) { return Y[k * TILE + n2]; },
-                              [&](int m, int n2, float a) {
-                                  St[m * TILE + n2] = lds[L::GC + m] * St[m * TILE + n2] - a + lds[L::OFF + m * TILE + n2];
-                              });
+            // state <- Diag(Gc) state - A2^T Y + offset, row blocks wave, wave + 4, ..
+            for (int rb = wave; rb < D / 16; rb += NT / 64) {
+                floatx4 acc = zero4();
+#pragma unroll
+                for (int kk = 0; kk < C / 16; ++kk) {
+                    const int k0 = 16 * kk + 4 * g;
+                    const float a[4] = {A2[(k0 + 0) * DP + 16 * rb + m], A2[(k0 + 1) * DP + 16 * rb + m],
+                                        A2[(k0 + 2) * DP + 16 * rb + m], A2[(k0 + 3) * DP + 16 * rb + m]};
+                    const float b[4] = {Y[(k0 + 0) * TP + m], Y[(k0 + 1) * TP + m], Y[(k0 + 2) * TP + m],
+                                        Y[(k0 + 3) * TP + m]};
+                    acc = mma16x4(a, b, acc);
+                }
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int row = 16 * rb + 4 * g + r;
+                    St[row * TP + m] = lds[L::GC + row] * St[row * TP + m] - acc[r] + lds[L::OFF + row * TP + m];
+                }
+            }
         }
         __syncthreads();
     }
     if (p.ds0) {
         for (int idx = threadIdx.x; idx < D * TILE; idx += NT) {
             const int c = idx / TILE, j = idx - c * TILE;
-            p.ds0[bh * DD + c * D + col0 + j] = St[idx];
+            p.ds0[bh * DD + c * D + col0 + j] = St[c * TP + j];
         }
     }
 }
