@@ -61,35 +61,49 @@ struct Scr {
     static constexpr int64_t SIZE = DBX + C;
 };
 
-// out(m, n) for m < M, n < N of sum_{k < K} a(m, k) b(k, n) over the workgroup:
-// each thread owns BM x 4 blocks of outputs and keeps them in registers.
-template <int M, int N, int K, int BM, class FA, class FB, class FO>
-__device__ __forceinline__ void mm(FA a, FB b, FO o) {
-    static_assert(M % BM == 0 && N % 4 == 0, "block shape");
-    constexpr int NB = (M / BM) * (N / 4);
-    for (int blk = threadIdx.x; blk < NB; blk += NT) {
-        const int m0 = (blk / (N / 4)) * BM, n0 = (blk % (N / 4)) * 4;
-        float acc[BM][4];
-#pragma unroll
-        for (int i = 0; i < BM; ++i)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) acc[i][j] = 0.f;
+// out(m, n) for m < M, n < N of sum_{k < K} a(m, k) b(k, n) over the workgroup, on
+// the fp32 MFMA.  A and B are first copied into LDS (row pitches K + 4 and N + 4, so
+// the lane groups of an operand read fall on different banks); wave w then forms the
+// 16 x 16 output tiles w, w + 4, ..: lane (l, g) gives A[l][k] and B[k][l] for
+// k = 16 kk + 4 g + c in the c-th MFMA of a 16-wide k step and receives
+// out[4 g + i][l] in acc[i].  Starts with a barrier (LDS free) and ends without one.
+template <int D, int M, int N, int K, class FA, class FB, class FO>
+__device__ __forceinline__ void mm(FA a, FB b, FO o, float* lds) {
+    constexpr int KP = K + 4, NP = N + 4;
+    static_assert(M % 16 == 0 && N % 16 == 0 && K % 16 == 0, "16 x 16 tiles");
+    static_assert(M * KP + K * NP <= 3 * C * D + 2 * C * C, "fits the chunk kernels' LDS");
+    float* la = lds;
+    float* lb = lds + M * KP;
+    __syncthreads();
 #pragma unroll 8
-        for (int kk = 0; kk < K; ++kk) {
-            float bv[4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) bv[j] = b(kk, n0 + j);
-#pragma unroll
-            for (int i = 0; i < BM; ++i) {
-                const float av = a(m0 + i, kk);
-#pragma unroll
-                for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(av, bv[j], acc[i][j]);
-            }
+    for (int i = threadIdx.x; i < M * K; i += NT) {
+        const int m = i / K, k = i - m * K;
+        la[m * KP + k] = a(m, k);
+    }
+#pragma unroll 8
+    for (int i = threadIdx.x; i < K * N; i += NT) {
+        const int k = i / N, n = i - k * N;
+        lb[k * NP + n] = b(k, n);
+    }
+    __syncthreads();
+    const int lane = lane_id(), wave = wave_id();
+    const int l = lane & 15, g = lane >> 4;
+    constexpr int TN = N / 16, TILES = (M / 16) * TN;
+    for (int t = wave; t < TILES; t += NT / 64) {
+        const int tm = t / TN, tn = t - tm * TN;
+        floatx4 acc = zero4();
+#pragma unroll 4
+        for (int kk = 0; kk < K / 16; ++kk) {
+            const int k0 = 16 * kk + 4 * g;
+            const float4 av = *reinterpret_cast<const float4*>(la + (16 * tm + l) * KP + k0);
+            const float* bp = lb + k0 * NP + 16 * tn + l;
+            acc = mma_f32_k4(av.x, bp[0], acc);
+            acc = mma_f32_k4(av.y, bp[NP], acc);
+            acc = mma_f32_k4(av.z, bp[2 * NP], acc);
+            acc = mma_f32_k4(av.w, bp[3 * NP], acc);
         }
 #pragma unroll
-        for (int i = 0; i < BM; ++i)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) o(m0 + i, n0 + j, acc[i][j]);
+        for (int i = 0; i < 4; ++i) o(16 * tm + 4 * g + i, 16 * tn + l, acc[i]);
     }
 }
 
@@ -113,50 +127,99 @@ __device__ __forceinline__ int64_t elem(const BwdParams& p, const ChunkPos& cp, 
     return ((cp.b * p.T + cp.t0 + r) * p.H + cp.h) * D + c;
 }
 
+// LDS of the chunk kernels (fp32 offsets).  The pair products and the inverse read
+// three channel-major C x D blocks and two C x C blocks; the gradient's pair terms
+// read three row-major C x D blocks, two C x C blocks and beta.
+template <int D>
+struct ChunkLds {
+    static constexpr int CD = C * D, CC = C * C;
+    static constexpr int A0 = 0, A1 = CD, A2 = 2 * CD, B0 = 3 * CD, B1 = 3 * CD + CC, BETA = 3 * CD + 2 * CC;
+    static constexpr int TOTAL = BETA + C;
+};
+
+// Copies n floats (a multiple of 4 * NT) from global scratch to LDS, all loads of a
+// thread issued before its stores.
+template <int N>
+__device__ __forceinline__ void to_lds(float* dst, const float* src) {
+    constexpr int per = N / 4 / NT;
+    float4 v[per];
+#pragma unroll
+    for (int i = 0; i < per; ++i) v[i] = reinterpret_cast<const float4*>(src)[threadIdx.x + i * NT];
+#pragma unroll
+    for (int i = 0; i < per; ++i) reinterpret_cast<float4*>(dst)[threadIdx.x + i * NT] = v[i];
+}
+
 // Steps shared by the prep and gradient kernels: the chunk's inputs in fp32 (zero
 // past the sequence's end, which makes the padding tokens identity steps), g, the
 // decayed operands, Bm, P and Li.
 template <int D, class In>
-__device__ void chunk_common(const BwdParams& p, const ChunkPos& cp, float* s) {
+__device__ void chunk_common(const BwdParams& p, const ChunkPos& cp, float* s, float* lds) {
     using S = Scr<D>;
+    using LL = ChunkLds<D>;
     using raw = typename In::raw_t;
-    for (int idx = threadIdx.x; idx < C * D; idx += NT) {
-        const int r = idx / D, c = idx - r * D;
-        float kv = 0.f, qv = 0.f, vv = 0.f, lv = 0.f, dov = 0.f;
-        if (r < cp.L) {
-            const int64_t e = elem<D>(p, cp, r, c);
-            kv = In::load(static_cast<const raw*>(p.k), e);
-            qv = In::load(static_cast<const raw*>(p.q), e);
-            vv = In::load(static_cast<const raw*>(p.v), e);
-            lv = clamp_log_alpha(In::load(static_cast<const raw*>(p.la), e), p.clamp != 0);
-            dov = In::load(static_cast<const raw*>(p.dy), e) *
-                  sigmoidf_(In::load(static_cast<const raw*>(p.gate), e));
+    constexpr int PER = C * D / NT;  // elements per thread
+    constexpr int BATCH = 8;
+    static_assert(PER % BATCH == 0, "batches of loads");
+#pragma unroll 1
+    for (int b0 = 0; b0 < PER; b0 += BATCH) {
+        float kv[BATCH], qv[BATCH], vv[BATCH], lv[BATCH], dov[BATCH];
+#pragma unroll
+        for (int u = 0; u < BATCH; ++u) {
+            const int idx = threadIdx.x + (b0 + u) * NT;
+            const int r = idx / D, c = idx - r * D;
+            kv[u] = qv[u] = vv[u] = lv[u] = dov[u] = 0.f;
+            if (r < cp.L) {
+                const int64_t e = elem<D>(p, cp, r, c);
+                kv[u] = In::load(static_cast<const raw*>(p.k), e);
+                qv[u] = In::load(static_cast<const raw*>(p.q), e);
+                vv[u] = In::load(static_cast<const raw*>(p.v), e);
+                lv[u] = clamp_log_alpha(In::load(static_cast<const raw*>(p.la), e), p.clamp != 0);
+                dov[u] = In::load(static_cast<const raw*>(p.dy), e) *
+                         sigmoidf_(In::load(static_cast<const raw*>(p.gate), e));
+            }
         }
-        s[S::K + idx] = kv;
-        s[S::Q + idx] = qv;
-        s[S::V + idx] = vv;
-        s[S::G + idx] = lv;
-        s[S::DO + idx] = dov;
-        s[S::KTR + c * C + r] = kv;
-        s[S::QTR + c * C + r] = qv;
+#pragma unroll
+        for (int u = 0; u < BATCH; ++u) {
+            const int idx = threadIdx.x + (b0 + u) * NT;
+            const int r = idx / D, c = idx - r * D;
+            s[S::K + idx] = kv[u];
+            s[S::Q + idx] = qv[u];
+            s[S::V + idx] = vv[u];
+            s[S::G + idx] = lv[u];
+            s[S::DO + idx] = dov[u];
+            s[S::KTR + c * C + r] = kv[u];
+            s[S::QTR + c * C + r] = qv[u];
+        }
     }
     if (threadIdx.x < C) {
         const int r = threadIdx.x;
-        s[S::BETA + r] =
+        const float b =
             r < cp.L ? In::load(static_cast<const raw*>(p.beta), (cp.b * p.T + cp.t0 + r) * p.H + cp.h) : 0.f;
+        s[S::BETA + r] = b;
+        lds[LL::BETA + r] = b;
     }
     __syncthreads();
-    // g_r = sum_{s <= r} lambda_s, per key channel
+    // g_r = sum_{s <= r} lambda_s, per key channel (the column read whole, then summed)
     if (threadIdx.x < D) {
         const int c = threadIdx.x;
         float acc = 0.f;
-        for (int r = 0; r < C; ++r) {
-            acc += s[S::G + r * D + c];
-            s[S::G + r * D + c] = acc;
-            s[S::GTR + c * C + r] = acc;
+#pragma unroll 1
+        for (int r0 = 0; r0 < C; r0 += 16) {
+            float col[16];
+#pragma unroll
+            for (int u = 0; u < 16; ++u) col[u] = s[S::G + (r0 + u) * D + c];
+#pragma unroll
+            for (int u = 0; u < 16; ++u) {
+                acc += col[u];
+                s[S::G + (r0 + u) * D + c] = acc;
+                s[S::GTR + c * C + r0 + u] = acc;
+                lds[LL::A2 + c * C + r0 + u] = acc;
+            }
         }
     }
     __syncthreads();
+    to_lds<C * D>(lds + LL::A0, s + S::KTR);
+    to_lds<C * D>(lds + LL::A1, s + S::QTR);
     for (int idx = threadIdx.x; idx < C * D; idx += NT) {
         const int c = idx % D;
         const float g = s[S::G + idx], gc = s[S::G + (C - 1) * D + c];
@@ -166,28 +229,36 @@ __device__ void chunk_common(const BwdParams& p, const ChunkPos& cp, float* s) {
         s[S::QT + idx] = s[S::Q + idx] * eg;
         s[S::KB + idx] = kv * ex(gc - g);
     }
+    __syncthreads();
+    // pair products from LDS: channel-major k (A0), q (A1) and g (A2)
     for (int idx = threadIdx.x; idx < C * C; idx += NT) {
         const int r = idx / C, sc = idx - r * C;
         float bs = 0.f, ps = 0.f;
         if (sc <= r) {
+#pragma unroll 8
             for (int c = 0; c < D; ++c) {
-                const float e = ex(s[S::GTR + c * C + r] - s[S::GTR + c * C + sc]);
-                const float ks = s[S::KTR + c * C + sc] * e;
-                bs = fmaf(s[S::KTR + c * C + r], ks, bs);
-                ps = fmaf(s[S::QTR + c * C + r], ks, ps);
+                const float e = ex(lds[LL::A2 + c * C + r] - lds[LL::A2 + c * C + sc]);
+                const float ks = lds[LL::A0 + c * C + sc] * e;
+                bs = fmaf(lds[LL::A0 + c * C + r], ks, bs);
+                ps = fmaf(lds[LL::A1 + c * C + r], ks, ps);
             }
         }
-        s[S::BM + idx] = sc < r ? bs : 0.f;
+        const float bm = sc < r ? bs : 0.f;
+        s[S::BM + idx] = bm;
         s[S::PM + idx] = sc <= r ? ps : 0.f;
+        lds[LL::B0 + idx] = bm;
     }
     __syncthreads();
-    // Li = (I + diag(beta) Bm)^-1 by forward substitution, one column per lane
+    // Li = (I + diag(beta) Bm)^-1 by forward substitution in LDS, one column per lane
     if (threadIdx.x < C) {
         const int sc = threadIdx.x;
+        float* li = lds + LL::B1;
         for (int r = 0; r < C; ++r) {
             float acc = 0.f;
-            for (int m = 0; m < r; ++m) acc = fmaf(s[S::BM + r * C + m], s[S::LI + m * C + sc], acc);
-            s[S::LI + r * C + sc] = r == sc ? 1.f : (r < sc ? 0.f : -s[S::BETA + r] * acc);
+            for (int m = 0; m < r; ++m) acc = fmaf(lds[LL::B0 + r * C + m], li[m * C + sc], acc);
+            const float v = r == sc ? 1.f : (r < sc ? 0.f : -lds[LL::BETA + r] * acc);
+            li[r * C + sc] = v;
+            s[S::LI + r * C + sc] = v;
         }
     }
     __syncthreads();
@@ -196,36 +267,37 @@ __device__ void chunk_common(const BwdParams& p, const ChunkPos& cp, float* s) {
 template <int D, class In>
 __global__ __launch_bounds__(NT) void kda_bwd_prep_kernel(BwdParams p) {
     using S = Scr<D>;
+    extern __shared__ __align__(16) float lds[];
     using RC = Rec<D>;
     float* s = p.scratch + (int64_t)blockIdx.x * S::SIZE;
     const int64_t items = p.B * p.H * p.NC;
     for (int64_t item = blockIdx.x; item < items; item += gridDim.x) {
         const ChunkPos cp = chunk_pos(p, item);
-        chunk_common<D, In>(p, cp, s);
+        chunk_common<D, In>(p, cp, s, lds);
         float* tr = p.trans + item * RC::SIZE;
         const float* beta = s + S::BETA;
         // W = Li diag(beta) Kt;  U~ = Li diag(beta) V (kept in the X block)
-        mm<C, D, C, 4>([&](int m, int k) { return s[S::LI + m * C + k] * beta[k]; },
+        mm<D, C, D, C>([&](int m, int k) { return s[S::LI + m * C + k] * beta[k]; },
                     [&](int k, int n) { return s[S::KT + k * D + n]; },
-                    [&](int m, int n, float a) { tr[RC::W + m * D + n] = a; });
-        mm<C, D, C, 4>([&](int m, int k) { return s[S::LI + m * C + k] * beta[k]; },
+                    [&](int m, int n, float a) { tr[RC::W + m * D + n] = a; }, lds);
+        mm<D, C, D, C>([&](int m, int k) { return s[S::LI + m * C + k] * beta[k]; },
                     [&](int k, int n) { return s[S::V + k * D + n]; },
-                    [&](int m, int n, float a) { s[S::X + m * D + n] = a; });
+                    [&](int m, int n, float a) { s[S::X + m * D + n] = a; }, lds);
         for (int idx = threadIdx.x; idx < C * D; idx += NT) tr[RC::KBAR + idx] = s[S::KB + idx];
         if (threadIdx.x < D) tr[RC::GC + threadIdx.x] = s[S::EG + (C - 1) * D + threadIdx.x];
         __syncthreads();
         // Qe = Qt - P W (kept in the U block);  b = Kb^T U~
-        mm<C, D, C, 4>([&](int m, int k) { return s[S::PM + m * C + k]; },
+        mm<D, C, D, C>([&](int m, int k) { return s[S::PM + m * C + k]; },
                     [&](int k, int n) { return tr[RC::W + k * D + n]; },
-                    [&](int m, int n, float a) { s[S::U + m * D + n] = s[S::QT + m * D + n] - a; });
-        mm<D, D, C, 4>([&](int m, int k) { return s[S::KB + k * D + m]; },
+                    [&](int m, int n, float a) { s[S::U + m * D + n] = s[S::QT + m * D + n] - a; }, lds);
+        mm<D, D, D, C>([&](int m, int k) { return s[S::KB + k * D + m]; },
                     [&](int k, int n) { return s[S::X + k * D + n]; },
-                    [&](int m, int n, float a) { tr[RC::BV + m * D + n] = a; });
+                    [&](int m, int n, float a) { tr[RC::BV + m * D + n] = a; }, lds);
         __syncthreads();
         // R = Qe^T dO
-        mm<D, D, C, 4>([&](int m, int k) { return s[S::U + k * D + m]; },
+        mm<D, D, D, C>([&](int m, int k) { return s[S::U + k * D + m]; },
                     [&](int k, int n) { return s[S::DO + k * D + n]; },
-                    [&](int m, int n, float a) { tr[RC::R + m * D + n] = a; });
+                    [&](int m, int n, float a) { tr[RC::R + m * D + n] = a; }, lds);
         __syncthreads();  // the slot is reused by the next chunk
     }
 }
@@ -377,45 +449,47 @@ __global__ __launch_bounds__(NT) void kda_bwd_sweep_kernel(BwdParams p) {
 template <int D, class In>
 __global__ __launch_bounds__(NT) void kda_bwd_grad_kernel(BwdParams p) {
     using S = Scr<D>;
+    using LL = ChunkLds<D>;
+    extern __shared__ __align__(16) float lds[];
     using raw = typename In::raw_t;
     float* s = p.scratch + (int64_t)blockIdx.x * S::SIZE;
     const int64_t items = p.B * p.H * p.NC;
     const int64_t DD = (int64_t)D * D;
     for (int64_t item = blockIdx.x; item < items; item += gridDim.x) {
         const ChunkPos cp = chunk_pos(p, item);
-        chunk_common<D, In>(p, cp, s);
+        chunk_common<D, In>(p, cp, s, lds);
         const float* S0 = p.states + item * DD;
         const float* dSC = p.dstates + item * DD;
         const float* beta = s + S::BETA;
         // X = V - Kt S0
-        mm<C, D, D, 4>([&](int m, int k) { return s[S::KT + m * D + k]; },
+        mm<D, C, D, D>([&](int m, int k) { return s[S::KT + m * D + k]; },
                     [&](int k, int n) { return S0[k * D + n]; },
-                    [&](int m, int n, float a) { s[S::X + m * D + n] = s[S::V + m * D + n] - a; });
+                    [&](int m, int n, float a) { s[S::X + m * D + n] = s[S::V + m * D + n] - a; }, lds);
         __syncthreads();
         // U = Li diag(beta) X
-        mm<C, D, C, 4>([&](int m, int k) { return s[S::LI + m * C + k] * beta[k]; },
+        mm<D, C, D, C>([&](int m, int k) { return s[S::LI + m * C + k] * beta[k]; },
                     [&](int k, int n) { return s[S::X + k * D + n]; },
-                    [&](int m, int n, float a) { s[S::U + m * D + n] = a; });
+                    [&](int m, int n, float a) { s[S::U + m * D + n] = a; }, lds);
         __syncthreads();
         // O = Qt S0 + P U;  dP = lower(dO U^T);  dKb = U dS_C^T;  dU = P^T dO + Kb dS_C
-        mm<C, D, D, 4>([&](int m, int k) { return s[S::QT + m * D + k]; },
+        mm<D, C, D, D>([&](int m, int k) { return s[S::QT + m * D + k]; },
                     [&](int k, int n) { return S0[k * D + n]; },
-                    [&](int m, int n, float a) { s[S::O + m * D + n] = a; });
-        mm<C, D, C, 4>([&](int m, int k) { return s[S::PM + m * C + k]; },
+                    [&](int m, int n, float a) { s[S::O + m * D + n] = a; }, lds);
+        mm<D, C, D, C>([&](int m, int k) { return s[S::PM + m * C + k]; },
                     [&](int k, int n) { return s[S::U + k * D + n]; },
-                    [&](int m, int n, float a) { s[S::O + m * D + n] += a; });
-        mm<C, C, D, 4>([&](int m, int k) { return s[S::DO + m * D + k]; },
+                    [&](int m, int n, float a) { s[S::O + m * D + n] += a; }, lds);
+        mm<D, C, C, D>([&](int m, int k) { return s[S::DO + m * D + k]; },
                     [&](int k, int n) { return s[S::U + n * D + k]; },
-                    [&](int m, int n, float a) { s[S::DP + m * C + n] = n <= m ? a : 0.f; });
-        mm<C, D, D, 4>([&](int m, int k) { return s[S::U + m * D + k]; },
+                    [&](int m, int n, float a) { s[S::DP + m * C + n] = n <= m ? a : 0.f; }, lds);
+        mm<D, C, D, D>([&](int m, int k) { return s[S::U + m * D + k]; },
                     [&](int k, int n) { return dSC[n * D + k]; },
-                    [&](int m, int n, float a) { s[S::DKB + m * D + n] = a; });
-        mm<C, D, C, 4>([&](int m, int k) { return s[S::PM + k * C + m]; },
+                    [&](int m, int n, float a) { s[S::DKB + m * D + n] = a; }, lds);
+        mm<D, C, D, C>([&](int m, int k) { return s[S::PM + k * C + m]; },
                     [&](int k, int n) { return s[S::DO + k * D + n]; },
-                    [&](int m, int n, float a) { s[S::DU + m * D + n] = a; });
-        mm<C, D, D, 4>([&](int m, int k) { return s[S::KB + m * D + k]; },
+                    [&](int m, int n, float a) { s[S::DU + m * D + n] = a; }, lds);
+        mm<D, C, D, D>([&](int m, int k) { return s[S::KB + m * D + k]; },
                     [&](int k, int n) { return dSC[k * D + n]; },
-                    [&](int m, int n, float a) { s[S::DU + m * D + n] += a; });
+                    [&](int m, int n, float a) { s[S::DU + m * D + n] += a; }, lds);
         __syncthreads();
         // dZ = dY * O * sigmoid'(Z);  dLi = dU (diag(beta) X)^T, strictly lower part;  dW = Li^T dU
         for (int idx = threadIdx.x; idx < cp.L * D; idx += NT) {
@@ -424,12 +498,12 @@ __global__ __launch_bounds__(NT) void kda_bwd_grad_kernel(BwdParams p) {
             const float sg = sigmoidf_(In::load(static_cast<const raw*>(p.gate), e));
             p.dgate[e] = In::load(static_cast<const raw*>(p.dy), e) * s[S::O + idx] * sg * (1.f - sg);
         }
-        mm<C, C, D, 4>([&](int m, int k) { return s[S::DU + m * D + k]; },
+        mm<D, C, C, D>([&](int m, int k) { return s[S::DU + m * D + k]; },
                     [&](int k, int n) { return beta[n] * s[S::X + n * D + k]; },
-                    [&](int m, int n, float a) { s[S::DLI + m * C + n] = n < m ? a : 0.f; });
-        mm<C, D, C, 4>([&](int m, int k) { return s[S::LI + k * C + m]; },
+                    [&](int m, int n, float a) { s[S::DLI + m * C + n] = n < m ? a : 0.f; }, lds);
+        mm<D, C, D, C>([&](int m, int k) { return s[S::LI + k * C + m]; },
                     [&](int k, int n) { return s[S::DU + k * D + n]; },
-                    [&](int m, int n, float a) { s[S::DW + m * D + n] = a; });
+                    [&](int m, int n, float a) { s[S::DW + m * D + n] = a; }, lds);
         __syncthreads();
         // dV = diag(beta) dW;  dbeta's X part;  E = Li^T dLi;  the S0 parts of dQ and dKt
         for (int idx = threadIdx.x; idx < cp.L * D; idx += NT) {
@@ -442,41 +516,56 @@ __global__ __launch_bounds__(NT) void kda_bwd_grad_kernel(BwdParams p) {
             for (int j = 0; j < D; ++j) acc = fmaf(s[S::DW + r * D + j], s[S::X + r * D + j], acc);
             s[S::DBX + r] = acc;
         }
-        mm<C, C, C, 4>([&](int m, int k) { return s[S::LI + k * C + m]; },
+        mm<D, C, C, C>([&](int m, int k) { return s[S::LI + k * C + m]; },
                     [&](int k, int n) { return s[S::DLI + k * C + n]; },
-                    [&](int m, int n, float a) { s[S::EM + m * C + n] = a; });
-        mm<C, D, D, 4>([&](int m, int k) { return s[S::DO + m * D + k]; },
+                    [&](int m, int n, float a) { s[S::EM + m * C + n] = a; }, lds);
+        mm<D, C, D, D>([&](int m, int k) { return s[S::DO + m * D + k]; },
                     [&](int k, int n) { return S0[n * D + k]; },
-                    [&](int m, int n, float a) { s[S::DQ + m * D + n] = a * s[S::EG + m * D + n]; });
-        mm<C, D, D, 4>([&](int m, int k) { return beta[m] * s[S::DW + m * D + k]; },
+                    [&](int m, int n, float a) { s[S::DQ + m * D + n] = a * s[S::EG + m * D + n]; }, lds);
+        mm<D, C, D, D>([&](int m, int k) { return beta[m] * s[S::DW + m * D + k]; },
                     [&](int k, int n) { return S0[n * D + k]; },
-                    [&](int m, int n, float a) { s[S::DKT + m * D + n] = -a * s[S::EG + m * D + n]; });
+                    [&](int m, int n, float a) { s[S::DKT + m * D + n] = -a * s[S::EG + m * D + n]; }, lds);
         __syncthreads();
         // dA = -(E Li^T), strictly lower part (the gradient with respect to diag(beta) Bm)
-        mm<C, C, C, 4>([&](int m, int k) { return s[S::EM + m * C + k]; },
+        mm<D, C, C, C>([&](int m, int k) { return s[S::EM + m * C + k]; },
                     [&](int k, int n) { return s[S::LI + n * C + k]; },
-                    [&](int m, int n, float a) { s[S::DA + m * C + n] = n < m ? -a : 0.f; });
+                    [&](int m, int n, float a) { s[S::DA + m * C + n] = n < m ? -a : 0.f; }, lds);
         __syncthreads();
-        // pair terms of dq and dk (through P and Bm), the K-bar term, dg; dbeta
+        // pair terms of dq and dk (through P and Bm), the K-bar term, dg; dbeta.  The
+        // loops read k, q, g (row-major), dP, dA and beta from LDS.
+        to_lds<C * D>(lds + LL::A0, s + S::K);
+        to_lds<C * D>(lds + LL::A1, s + S::Q);
+        to_lds<C * D>(lds + LL::A2, s + S::G);
+        to_lds<C * C>(lds + LL::B0, s + S::DP);
+        to_lds<C * C>(lds + LL::B1, s + S::DA);
+        __syncthreads();
+        const float* lk = lds + LL::A0;
+        const float* lq = lds + LL::A1;
+        const float* lg = lds + LL::A2;
+        const float* ldp = lds + LL::B0;
+        const float* lda = lds + LL::B1;
+        const float* lbeta = lds + LL::BETA;
         for (int idx = threadIdx.x; idx < C * D; idx += NT) {
             const int r = idx / D, c = idx - r * D;
-            const float gr = s[S::G + idx];
+            const float gr = lg[idx];
             float pq = 0.f, aq = 0.f, ak = 0.f, pk = 0.f;
+#pragma unroll 4
             for (int j = 0; j <= r; ++j) {
-                const float ke = s[S::K + j * D + c] * ex(gr - s[S::G + j * D + c]);
-                pq = fmaf(s[S::DP + r * C + j], ke, pq);
-                aq = fmaf(s[S::DA + r * C + j], ke, aq);
+                const float ke = lk[j * D + c] * ex(gr - lg[j * D + c]);
+                pq = fmaf(ldp[r * C + j], ke, pq);
+                aq = fmaf(lda[r * C + j], ke, aq);
             }
+#pragma unroll 4
             for (int j = r; j < C; ++j) {
-                const float e = ex(s[S::G + j * D + c] - gr);
-                ak = fmaf(beta[j] * s[S::DA + j * C + r], s[S::K + j * D + c] * e, ak);
-                pk = fmaf(s[S::DP + j * C + r], s[S::Q + j * D + c] * e, pk);
+                const float e = ex(lg[j * D + c] - gr);
+                ak = fmaf(lbeta[j] * lda[j * C + r], lk[j * D + c] * e, ak);
+                pk = fmaf(ldp[j * C + r], lq[j * D + c] * e, pk);
             }
             const float dqf = s[S::DQ + idx] + pq;
-            const float dktf = s[S::DKT + idx] + beta[r] * aq;
+            const float dktf = s[S::DKT + idx] + lbeta[r] * aq;
             const float dkif = ak + pk;
-            const float dkbf = s[S::DKB + idx] * ex(s[S::G + (C - 1) * D + c] - gr);
-            const float kv = s[S::K + idx], qv = s[S::Q + idx];
+            const float dkbf = s[S::DKB + idx] * ex(lg[(C - 1) * D + c] - gr);
+            const float kv = lk[idx], qv = lq[idx];
             if (r < cp.L) {
                 const int64_t e = elem<D>(p, cp, r, c);
                 p.dq[e] = dqf;
@@ -499,13 +588,20 @@ __global__ __launch_bounds__(NT) void kda_bwd_grad_kernel(BwdParams p) {
             for (int j = 0; j < D; ++j) dgc = fmaf(dSC[c * D + j], S0[c * D + j], dgc);
             float acc = dgc * s[S::EG + (C - 1) * D + c];
             for (int r = 0; r < C; ++r) acc += s[S::DKT + r * D + c];
-            for (int r = C - 1; r >= 0; --r) {
-                acc += s[S::DQ + r * D + c];
-                if (r < cp.L) {
-                    const int64_t e = elem<D>(p, cp, r, c);
-                    const float l = In::load(static_cast<const raw*>(p.la), e);
-                    const bool live = p.clamp == 0 || (l >= kLogAlphaMin && l <= 0.f);
-                    p.dla[e] = live ? acc : 0.f;
+#pragma unroll 1
+            for (int r0 = C - 16; r0 >= 0; r0 -= 16) {
+                float col[16];  // 16 rows of g's gradient, read before their stores
+#pragma unroll
+                for (int u = 0; u < 16; ++u) col[u] = s[S::DQ + (r0 + u) * D + c];
+                for (int u = 15; u >= 0; --u) {
+                    const int r = r0 + u;
+                    acc += col[u];
+                    if (r < cp.L) {
+                        const int64_t e = elem<D>(p, cp, r, c);
+                        const float l = In::load(static_cast<const raw*>(p.la), e);
+                        const bool live = p.clamp == 0 || (l >= kLogAlphaMin && l <= 0.f);
+                        p.dla[e] = live ? acc : 0.f;
+                    }
                 }
             }
         }
@@ -527,9 +623,14 @@ int64_t section_bytes(int64_t bh, int64_t nc, int64_t* trans, int64_t* states, i
 template <int D, class In>
 hipError_t launch_d(const BwdParams& p, hipStream_t stream) {
     const int64_t items = p.B * p.H * p.NC;
+    constexpr int clds = ChunkLds<D>::TOTAL * 4;
     if (items > 0) {
-        hipLaunchKernelGGL((kda_bwd_prep_kernel<D, In>), dim3((unsigned)p.slots), dim3(NT), 0, stream, p);
-        const hipError_t e = hipGetLastError();
+        auto kp = kda_bwd_prep_kernel<D, In>;
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kp),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, clds);
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(kp, dim3((unsigned)p.slots), dim3(NT), clds, stream, p);
+        e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
     const int64_t bh = p.B * p.H;
@@ -543,8 +644,13 @@ hipError_t launch_d(const BwdParams& p, hipStream_t stream) {
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    if (items > 0)
-        hipLaunchKernelGGL((kda_bwd_grad_kernel<D, In>), dim3((unsigned)p.slots), dim3(NT), 0, stream, p);
+    if (items > 0) {
+        auto kg = kda_bwd_grad_kernel<D, In>;
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kg),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, clds);
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(kg, dim3((unsigned)p.slots), dim3(NT), clds, stream, p);
+    }
     return hipGetLastError();
 }
 
