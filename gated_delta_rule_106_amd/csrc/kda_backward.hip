@@ -457,7 +457,14 @@ __global__ __launch_bounds__(NT) void kda_bwd_grad_kernel(BwdParams p) {
     const int64_t DD = (int64_t)D * D;
     for (int64_t item = blockIdx.x; item < items; item += gridDim.x) {
         const ChunkPos cp = chunk_pos(p, item);
-        chunk_common<D, In>(p, cp, s, lds);
+        if (items <= p.slots) {
+            // one chunk per slot: the prep kernel ran this chunk's shared steps in this
+            // same slot (workgroup b takes chunk b in both launches) and left them there
+            if (threadIdx.x < C) lds[LL::BETA + threadIdx.x] = s[S::BETA + threadIdx.x];
+            __syncthreads();
+        } else {
+            chunk_common<D, In>(p, cp, s, lds);
+        }
         const float* S0 = p.states + item * DD;
         const float* dSC = p.dstates + item * DD;
         const float* beta = s + S::BETA;

@@ -148,3 +148,12 @@ def test_full_size_headline_sampled_heads():
         ref = _oracle(xs, dy[:, :, h:h + 1].contiguous(), None)
         gh = {n: (g[n][:, :, h:h + 1] if n != "dinitial_state" else g[n][:, h:h + 1]) for n in GRADS}
         _check(f"B1 H8 T4096 d128 bf16, head {h}", gh, ref)
+
+
+def test_more_chunks_than_workgroups():
+    """520 chunks on at most 512 workgroups: some workgroups take two chunks, and the
+    gradient kernel recomputes the shared per-chunk steps instead of reusing the prep's."""
+    wl = small(CONFIGS[2], B=1, H=2, T=260 * 64, Dk=64, Dv=64)
+    x = make_inputs(wl)
+    dy, dst = _cotangents(wl, 31, True)
+    _check("B1 H2 T16640 d64 bf16 (520 chunks)", _run(x, dy, dst), _oracle(x, dy, dst))
