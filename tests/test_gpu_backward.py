@@ -157,3 +157,19 @@ def test_more_chunks_than_workgroups():
     x = make_inputs(wl)
     dy, dst = _cotangents(wl, 31, True)
     _check("B1 H2 T16640 d64 bf16 (520 chunks)", _run(x, dy, dst), _oracle(x, dy, dst))
+
+
+def test_full_size_state_in_out_sampled_units():
+    """B2 H32 T8192 d128 bf16 with an initial state and dS_T: 8192 chunks over 512
+    workgroups (the recompute path); (batch, head) units are independent, so the oracle
+    runs on two of them."""
+    wl = CONFIGS[2]
+    x = make_inputs(wl)
+    dy, dst = _cotangents(wl, 41, True)
+    g = _run(x, dy, dst)
+    for b, h in ((0, 3), (1, 17)):
+        xs = {n: x[n][b:b + 1, :, h:h + 1].contiguous() for n in KEYS}
+        xs["initial_state"] = x["initial_state"][b:b + 1, h:h + 1].contiguous()
+        ref = _oracle(xs, dy[b:b + 1, :, h:h + 1].contiguous(), dst[b:b + 1, h:h + 1].contiguous())
+        gh = {n: (g[n][b:b + 1, :, h:h + 1] if n != "dinitial_state" else g[n][b:b + 1, h:h + 1]) for n in GRADS}
+        _check(f"B2 H32 T8192 d128 bf16 state in/out, unit (b={b}, h={h})", gh, ref)
