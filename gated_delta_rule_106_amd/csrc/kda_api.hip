@@ -119,7 +119,7 @@ int check_bwd(const kda_bwd_args* a, int64_t* nchunks, int64_t* ws_total) {
     if (!mul_ok(a->B, a->T, &bt) || !mul_ok(bt, a->H, &bth) || !mul_ok(bth, a->Dk, &elems) ||
         !mul_ok(a->B, a->H, &bh) || !mul_ok(bh, a->Dk * a->Dv, &st))
         return KDA_ERR_SHAPE;
-    if (bh > INT_MAX / 8) return KDA_ERR_SHAPE;  // one sweep workgroup per (b, h, 16 value columns)
+    if (bh > INT_MAX / 16) return KDA_ERR_SHAPE;  // two sweep workgroups per (b, h, 16 value columns)
     const int64_t nc = (a->T + 63) / 64;
     // per chunk: a record, two states and their scratch share stay below 1 MiB
     if (!mul_ok(bh, nc, &items) || !mul_ok(items, (int64_t)1 << 20, &tmp)) return KDA_ERR_SHAPE;

@@ -16,10 +16,11 @@
 // Three launches:
 //  1. kda_bwd_prep_kernel, one chunk per workgroup: W = Li diag(beta) Kt, Kb, Gc,
 //     b = Kb^T Li diag(beta) V and R = (Qt - P W)^T dO with dO = dY * sigmoid(Z).
-//  2. kda_bwd_sweep_kernel, one (b, h, 16 value columns) per workgroup (columns of
-//     the state evolve independently): the states at every chunk start,
-//     S_{n+1} = Diag(Gc) S_n - Kb^T (W S_n) + b, then the state gradients in reverse,
-//     dS_n = Diag(Gc) dS_{n+1} - W^T (Kb dS_{n+1}) + R (the transposed map).
+//  2. kda_bwd_sweep_kernel, one (direction, b, h, 16 value columns) per workgroup
+//     (columns of the state evolve independently): forwards the states at every
+//     chunk start, S_{n+1} = Diag(Gc) S_n - Kb^T (W S_n) + b; backwards the state
+//     gradients, dS_n = Diag(Gc) dS_{n+1} - W^T (Kb dS_{n+1}) + R (the transposed
+//     map).  R does not depend on the states, so the two directions run at once.
 //  3. kda_bwd_grad_kernel, one chunk per workgroup: the adjoint of the chunk's
 //     steps above from S_n and dS_{n+1}; log alpha's gradient is the reverse
 //     cumulative sum of g's gradient within the chunk.
@@ -324,7 +325,8 @@ __device__ __forceinline__ floatx4 mma16x4(const float (&a)[4], const float (&b)
 }
 
 // Forwards: S <- Diag(Gc) S - Kb^T (W S) + b; backwards: dS <- Diag(Gc) dS - W^T (Kb dS) + R.
-// Both products run on the fp32 MFMA: wave w forms rows 16 w .. 16 w + 15 of Y, then
+// One workgroup runs one direction.  Both products run on the fp32 MFMA: wave w
+// forms rows 16 w .. 16 w + 15 of Y, then
 // row blocks w, w + 4, .. of the new state.  The record of the next chunk is read into
 // registers while the current one is used.
 template <int D>
@@ -336,8 +338,13 @@ __global__ __launch_bounds__(NT) void kda_bwd_sweep_kernel(BwdParams p) {
     float* St = lds + L::ST;
     float* Y = lds + L::Y;
     constexpr int tiles = D / TILE;
-    const int64_t bh = blockIdx.x / tiles;
-    const int col0 = (int)(blockIdx.x - bh * tiles) * TILE;
+    // the two sweeps are independent (R does not depend on the states): the first half
+    // of the grid runs the forward one, the second half the backward one
+    const int64_t half = gridDim.x / 2;
+    const int dir = blockIdx.x >= half ? 1 : 0;
+    const int64_t bid = blockIdx.x - dir * half;
+    const int64_t bh = bid / tiles;
+    const int col0 = (int)(bid - bh * tiles) * TILE;
     const int64_t DD = (int64_t)D * D;
     const float* rec0 = p.trans + bh * p.NC * RC::SIZE;
     const int lane = lane_id(), wave = wave_id();
@@ -379,8 +386,7 @@ __global__ __launch_bounds__(NT) void kda_bwd_sweep_kernel(BwdParams p) {
         }
         if (threadIdx.x < D / 4) reinterpret_cast<float4*>(lds + L::GC)[threadIdx.x] = rg;
     };
-#pragma unroll
-    for (int dir = 0; dir < 2; ++dir) {
+    {
         const float* init = dir == 0 ? p.s0 : p.dsT;
         for (int idx = threadIdx.x; idx < D * TILE; idx += NT) {
             const int c = idx / TILE, j = idx - c * TILE;
@@ -438,7 +444,7 @@ __global__ __launch_bounds__(NT) void kda_bwd_sweep_kernel(BwdParams p) {
         }
         __syncthreads();
     }
-    if (p.ds0) {
+    if (dir == 1 && p.ds0) {
         for (int idx = threadIdx.x; idx < D * TILE; idx += NT) {
             const int c = idx / TILE, j = idx - c * TILE;
             p.ds0[bh * DD + c * D + col0 + j] = St[c * TP + j];
@@ -647,7 +653,7 @@ hipError_t launch_d(const BwdParams& p, hipStream_t stream) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(ks),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, lds);
         if (e != hipSuccess) return e;
-        hipLaunchKernelGGL(ks, dim3((unsigned)(bh * (D / TILE))), dim3(NT), lds, stream, p);
+        hipLaunchKernelGGL(ks, dim3((unsigned)(2 * bh * (D / TILE))), dim3(NT), lds, stream, p);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
