@@ -64,11 +64,12 @@ struct Scr {
 
 // out(m, n) for m < M, n < N of sum_{k < K} a(m, k) b(k, n) over the workgroup, on
 // the fp32 MFMA.  A and B are first copied into LDS (row pitches K + 4 and N + 4, so
-// the lane groups of an operand read fall on different banks); wave w then forms the
+// the lane groups of an operand read fall on different banks), in the order of their
+// sources' contiguous index (TA, TB: the source is stored transposed); wave w then forms the
 // 16 x 16 output tiles w, w + 4, ..: lane (l, g) gives A[l][k] and B[k][l] for
 // k = 16 kk + 4 g + c in the c-th MFMA of a 16-wide k step and receives
 // out[4 g + i][l] in acc[i].  Starts with a barrier (LDS free) and ends without one.
-template <int D, int M, int N, int K, class FA, class FB, class FO>
+template <int D, int M, int N, int K, bool TA = false, bool TB = false, class FA, class FB, class FO>
 __device__ __forceinline__ void mm(FA a, FB b, FO o, float* lds) {
     constexpr int KP = K + 4, NP = N + 4;
     static_assert(M % 16 == 0 && N % 16 == 0 && K % 16 == 0, "16 x 16 tiles");
@@ -78,12 +79,14 @@ __device__ __forceinline__ void mm(FA a, FB b, FO o, float* lds) {
     __syncthreads();
 #pragma unroll 8
     for (int i = threadIdx.x; i < M * K; i += NT) {
-        const int m = i / K, k = i - m * K;
+        // TA: a(m, k) is read from a k-major source, so consecutive lanes take consecutive m
+        const int m = TA ? i % M : i / K, k = TA ? i / M : i % K;
         la[m * KP + k] = a(m, k);
     }
 #pragma unroll 8
     for (int i = threadIdx.x; i < K * N; i += NT) {
-        const int k = i / N, n = i - k * N;
+        // TB: b(k, n) is read from an n-major source, so consecutive lanes take consecutive k
+        const int k = TB ? i % K : i / N, n = TB ? i / K : i % N;
         lb[k * NP + n] = b(k, n);
     }
     __syncthreads();
@@ -291,12 +294,12 @@ __global__ __launch_bounds__(NT) void kda_bwd_prep_kernel(BwdParams p) {
         mm<D, C, D, C>([&](int m, int k) { return s[S::PM + m * C + k]; },
                     [&](int k, int n) { return tr[RC::W + k * D + n]; },
                     [&](int m, int n, float a) { s[S::U + m * D + n] = s[S::QT + m * D + n] - a; }, lds);
-        mm<D, D, D, C>([&](int m, int k) { return s[S::KB + k * D + m]; },
+        mm<D, D, D, C, true, false>([&](int m, int k) { return s[S::KB + k * D + m]; },
                     [&](int k, int n) { return s[S::X + k * D + n]; },
                     [&](int m, int n, float a) { tr[RC::BV + m * D + n] = a; }, lds);
         __syncthreads();
         // R = Qe^T dO
-        mm<D, D, D, C>([&](int m, int k) { return s[S::U + k * D + m]; },
+        mm<D, D, D, C, true, false>([&](int m, int k) { return s[S::U + k * D + m]; },
                     [&](int k, int n) { return s[S::DO + k * D + n]; },
                     [&](int m, int n, float a) { tr[RC::R + m * D + n] = a; }, lds);
         __syncthreads();  // the slot is reused by the next chunk
