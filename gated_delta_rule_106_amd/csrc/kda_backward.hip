@@ -25,7 +25,9 @@
 //     steps above from S_n and dS_{n+1}; log alpha's gradient is the reverse
 //     cumulative sum of g's gradient within the chunk.
 // All arithmetic is fp32; the chunk kernels keep their intermediates in a scratch
-// slot of the workspace (one per workgroup, reused chunk after chunk).
+// slot of the workspace (one per workgroup, reused chunk after chunk).  When every
+// chunk has a slot of its own, the gradient kernel finds the shared per-chunk steps
+// where the prep kernel left them instead of recomputing them.
 #include "kda_backward.h"
 #include "kda_device.h"
 
@@ -65,8 +67,8 @@ struct Scr {
 // out(m, n) for m < M, n < N of sum_{k < K} a(m, k) b(k, n) over the workgroup, on
 // the fp32 MFMA.  A and B are first copied into LDS (row pitches K + 4 and N + 4, so
 // the lane groups of an operand read fall on different banks), in the order of their
-// sources' contiguous index (TA, TB: the source is stored transposed); wave w then forms the
-// 16 x 16 output tiles w, w + 4, ..: lane (l, g) gives A[l][k] and B[k][l] for
+// sources' contiguous index (TA, TB: that source is stored transposed).  Wave w then
+// forms the 16 x 16 output tiles w, w + 4, ..: lane (l, g) gives A[l][k] and B[k][l] for
 // k = 16 kk + 4 g + c in the c-th MFMA of a 16-wide k step and receives
 // out[4 g + i][l] in acc[i].  Starts with a barrier (LDS free) and ends without one.
 template <int D, int M, int N, int K, bool TA = false, bool TB = false, class FA, class FB, class FO>
@@ -329,9 +331,8 @@ __device__ __forceinline__ floatx4 mma16x4(const float (&a)[4], const float (&b)
 
 // Forwards: S <- Diag(Gc) S - Kb^T (W S) + b; backwards: dS <- Diag(Gc) dS - W^T (Kb dS) + R.
 // One workgroup runs one direction.  Both products run on the fp32 MFMA: wave w
-// forms rows 16 w .. 16 w + 15 of Y, then
-// row blocks w, w + 4, .. of the new state.  The record of the next chunk is read into
-// registers while the current one is used.
+// forms rows 16 w .. 16 w + 15 of Y, then row blocks w, w + 4, .. of the new state.
+// The record of the next chunk is read into registers while the current one is used.
 template <int D>
 __global__ __launch_bounds__(NT) void kda_bwd_sweep_kernel(BwdParams p) {
     using RC = Rec<D>;
