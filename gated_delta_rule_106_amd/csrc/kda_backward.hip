@@ -67,11 +67,13 @@ struct Scr {
 // out(m, n) for m < M, n < N of sum_{k < K} a(m, k) b(k, n) over the workgroup, on
 // the fp32 MFMA.  A and B are first copied into LDS (row pitches K + 4 and N + 4, so
 // the lane groups of an operand read fall on different banks), in the order of their
-// sources' contiguous index (TA, TB: that source is stored transposed).  Wave w then
+// sources' contiguous index (TA, TB: that source is stored transposed), one element
+// per lane and step or (V4) four neighbours per lane merged into a 16-byte load.  Wave w then
 // forms the 16 x 16 output tiles w, w + 4, ..: lane (l, g) gives A[l][k] and B[k][l] for
 // k = 16 kk + 4 g + c in the c-th MFMA of a 16-wide k step and receives
 // out[4 g + i][l] in acc[i].  Starts with a barrier (LDS free) and ends without one.
-template <int D, int M, int N, int K, bool TA = false, bool TB = false, class FA, class FB, class FO>
+template <int D, int M, int N, int K, bool TA = false, bool TB = false, bool V4 = false, class FA, class FB,
+          class FO>
 __device__ __forceinline__ void mm(FA a, FB b, FO o, float* lds) {
     constexpr int KP = K + 4, NP = N + 4;
     static_assert(M % 16 == 0 && N % 16 == 0 && K % 16 == 0, "16 x 16 tiles");
@@ -79,17 +81,43 @@ __device__ __forceinline__ void mm(FA a, FB b, FO o, float* lds) {
     float* la = lds;
     float* lb = lds + M * KP;
     __syncthreads();
+    if (V4) {
+        // each lane copies four neighbours along the source's contiguous index, which the
+        // compiler merges into one 16-byte load
+#pragma unroll 2
+        for (int i = threadIdx.x; i < M * K / 4; i += NT) {
+            if (TA) {  // a(m, k) is read from a k-major source: four consecutive m
+                const int k = i / (M / 4), m = 4 * (i - k * (M / 4));
+#pragma unroll
+                for (int j = 0; j < 4; ++j) la[(m + j) * KP + k] = a(m + j, k);
+            } else {
+                const int m = i / (K / 4), k = 4 * (i - m * (K / 4));
+                *reinterpret_cast<float4*>(la + m * KP + k) = make_float4(a(m, k), a(m, k + 1), a(m, k + 2), a(m, k + 3));
+            }
+        }
+#pragma unroll 2
+        for (int i = threadIdx.x; i < K * N / 4; i += NT) {
+            if (TB) {  // b(k, n) is read from an n-major source: four consecutive k
+                const int n = i / (K / 4), k = 4 * (i - n * (K / 4));
+#pragma unroll
+                for (int j = 0; j < 4; ++j) lb[(k + j) * NP + n] = b(k + j, n);
+            } else {
+                const int k = i / (N / 4), n = 4 * (i - k * (N / 4));
+                *reinterpret_cast<float4*>(lb + k * NP + n) = make_float4(b(k, n), b(k, n + 1), b(k, n + 2), b(k, n + 3));
+            }
+        }
+    } else {
+        // one element per lane and step, consecutive lanes along the source's contiguous index
 #pragma unroll 8
-    for (int i = threadIdx.x; i < M * K; i += NT) {
-        // TA: a(m, k) is read from a k-major source, so consecutive lanes take consecutive m
-        const int m = TA ? i % M : i / K, k = TA ? i / M : i % K;
-        la[m * KP + k] = a(m, k);
-    }
+        for (int i = threadIdx.x; i < M * K; i += NT) {
+            const int m = TA ? i % M : i / K, k = TA ? i / M : i % K;
+            la[m * KP + k] = a(m, k);
+        }
 #pragma unroll 8
-    for (int i = threadIdx.x; i < K * N; i += NT) {
-        // TB: b(k, n) is read from an n-major source, so consecutive lanes take consecutive k
-        const int k = TB ? i % K : i / N, n = TB ? i / K : i % N;
-        lb[k * NP + n] = b(k, n);
+        for (int i = threadIdx.x; i < K * N; i += NT) {
+            const int k = TB ? i % K : i / N, n = TB ? i / K : i % N;
+            lb[k * NP + n] = b(k, n);
+        }
     }
     __syncthreads();
     const int lane = lane_id(), wave = wave_id();
@@ -479,32 +507,32 @@ __global__ __launch_bounds__(NT) void kda_bwd_grad_kernel(BwdParams p) {
         const float* dSC = p.dstates + item * DD;
         const float* beta = s + S::BETA;
         // X = V - Kt S0
-        mm<D, C, D, D>([&](int m, int k) { return s[S::KT + m * D + k]; },
+        mm<D, C, D, D, false, false, true>([&](int m, int k) { return s[S::KT + m * D + k]; },
                     [&](int k, int n) { return S0[k * D + n]; },
                     [&](int m, int n, float a) { s[S::X + m * D + n] = s[S::V + m * D + n] - a; }, lds);
         __syncthreads();
         // U = Li diag(beta) X
-        mm<D, C, D, C>([&](int m, int k) { return s[S::LI + m * C + k] * beta[k]; },
+        mm<D, C, D, C, false, false, true>([&](int m, int k) { return s[S::LI + m * C + k] * beta[k]; },
                     [&](int k, int n) { return s[S::X + k * D + n]; },
                     [&](int m, int n, float a) { s[S::U + m * D + n] = a; }, lds);
         __syncthreads();
         // O = Qt S0 + P U;  dP = lower(dO U^T);  dKb = U dS_C^T;  dU = P^T dO + Kb dS_C
-        mm<D, C, D, D>([&](int m, int k) { return s[S::QT + m * D + k]; },
+        mm<D, C, D, D, false, false, true>([&](int m, int k) { return s[S::QT + m * D + k]; },
                     [&](int k, int n) { return S0[k * D + n]; },
                     [&](int m, int n, float a) { s[S::O + m * D + n] = a; }, lds);
-        mm<D, C, D, C>([&](int m, int k) { return s[S::PM + m * C + k]; },
+        mm<D, C, D, C, false, false, true>([&](int m, int k) { return s[S::PM + m * C + k]; },
                     [&](int k, int n) { return s[S::U + k * D + n]; },
                     [&](int m, int n, float a) { s[S::O + m * D + n] += a; }, lds);
-        mm<D, C, C, D>([&](int m, int k) { return s[S::DO + m * D + k]; },
+        mm<D, C, C, D, false, false, true>([&](int m, int k) { return s[S::DO + m * D + k]; },
                     [&](int k, int n) { return s[S::U + n * D + k]; },
                     [&](int m, int n, float a) { s[S::DP + m * C + n] = n <= m ? a : 0.f; }, lds);
-        mm<D, C, D, D>([&](int m, int k) { return s[S::U + m * D + k]; },
+        mm<D, C, D, D, false, false, true>([&](int m, int k) { return s[S::U + m * D + k]; },
                     [&](int k, int n) { return dSC[n * D + k]; },
                     [&](int m, int n, float a) { s[S::DKB + m * D + n] = a; }, lds);
-        mm<D, C, D, C>([&](int m, int k) { return s[S::PM + k * C + m]; },
+        mm<D, C, D, C, false, false, true>([&](int m, int k) { return s[S::PM + k * C + m]; },
                     [&](int k, int n) { return s[S::DO + k * D + n]; },
                     [&](int m, int n, float a) { s[S::DU + m * D + n] = a; }, lds);
-        mm<D, C, D, D>([&](int m, int k) { return s[S::KB + m * D + k]; },
+        mm<D, C, D, D, false, false, true>([&](int m, int k) { return s[S::KB + m * D + k]; },
                     [&](int k, int n) { return dSC[k * D + n]; },
                     [&](int m, int n, float a) { s[S::DU + m * D + n] += a; }, lds);
         __syncthreads();
@@ -515,10 +543,10 @@ __global__ __launch_bounds__(NT) void kda_bwd_grad_kernel(BwdParams p) {
             const float sg = sigmoidf_(In::load(static_cast<const raw*>(p.gate), e));
             p.dgate[e] = In::load(static_cast<const raw*>(p.dy), e) * s[S::O + idx] * sg * (1.f - sg);
         }
-        mm<D, C, C, D>([&](int m, int k) { return s[S::DU + m * D + k]; },
+        mm<D, C, C, D, false, false, true>([&](int m, int k) { return s[S::DU + m * D + k]; },
                     [&](int k, int n) { return beta[n] * s[S::X + n * D + k]; },
                     [&](int m, int n, float a) { s[S::DLI + m * C + n] = n < m ? a : 0.f; }, lds);
-        mm<D, C, D, C>([&](int m, int k) { return s[S::LI + k * C + m]; },
+        mm<D, C, D, C, false, false, true>([&](int m, int k) { return s[S::LI + k * C + m]; },
                     [&](int k, int n) { return s[S::DU + k * D + n]; },
                     [&](int m, int n, float a) { s[S::DW + m * D + n] = a; }, lds);
         __syncthreads();
@@ -533,18 +561,18 @@ __global__ __launch_bounds__(NT) void kda_bwd_grad_kernel(BwdParams p) {
             for (int j = 0; j < D; ++j) acc = fmaf(s[S::DW + r * D + j], s[S::X + r * D + j], acc);
             s[S::DBX + r] = acc;
         }
-        mm<D, C, C, C>([&](int m, int k) { return s[S::LI + k * C + m]; },
+        mm<D, C, C, C, false, false, true>([&](int m, int k) { return s[S::LI + k * C + m]; },
                     [&](int k, int n) { return s[S::DLI + k * C + n]; },
                     [&](int m, int n, float a) { s[S::EM + m * C + n] = a; }, lds);
-        mm<D, C, D, D>([&](int m, int k) { return s[S::DO + m * D + k]; },
+        mm<D, C, D, D, false, false, true>([&](int m, int k) { return s[S::DO + m * D + k]; },
                     [&](int k, int n) { return S0[n * D + k]; },
                     [&](int m, int n, float a) { s[S::DQ + m * D + n] = a * s[S::EG + m * D + n]; }, lds);
-        mm<D, C, D, D>([&](int m, int k) { return beta[m] * s[S::DW + m * D + k]; },
+        mm<D, C, D, D, false, false, true>([&](int m, int k) { return beta[m] * s[S::DW + m * D + k]; },
                     [&](int k, int n) { return S0[n * D + k]; },
                     [&](int m, int n, float a) { s[S::DKT + m * D + n] = -a * s[S::EG + m * D + n]; }, lds);
         __syncthreads();
         // dA = -(E Li^T), strictly lower part (the gradient with respect to diag(beta) Bm)
-        mm<D, C, C, C>([&](int m, int k) { return s[S::EM + m * C + k]; },
+        mm<D, C, C, C, false, false, true>([&](int m, int k) { return s[S::EM + m * C + k]; },
                     [&](int k, int n) { return s[S::LI + n * C + k]; },
                     [&](int m, int n, float a) { s[S::DA + m * C + n] = n < m ? -a : 0.f; }, lds);
         __syncthreads();
