@@ -523,13 +523,13 @@ __global__ __launch_bounds__(NT) void kda_bwd_grad_kernel(BwdParams p) {
         mm<D, C, D, C, false, false, true>([&](int m, int k) { return s[S::PM + m * C + k]; },
                     [&](int k, int n) { return s[S::U + k * D + n]; },
                     [&](int m, int n, float a) { s[S::O + m * D + n] += a; }, lds);
-        mm<D, C, C, D, false, false, true>([&](int m, int k) { return s[S::DO + m * D + k]; },
+        mm<D, C, C, D, false, true, true>([&](int m, int k) { return s[S::DO + m * D + k]; },
                     [&](int k, int n) { return s[S::U + n * D + k]; },
                     [&](int m, int n, float a) { s[S::DP + m * C + n] = n <= m ? a : 0.f; }, lds);
-        mm<D, C, D, D, false, false, true>([&](int m, int k) { return s[S::U + m * D + k]; },
+        mm<D, C, D, D, false, true, true>([&](int m, int k) { return s[S::U + m * D + k]; },
                     [&](int k, int n) { return dSC[n * D + k]; },
                     [&](int m, int n, float a) { s[S::DKB + m * D + n] = a; }, lds);
-        mm<D, C, D, C, false, false, true>([&](int m, int k) { return s[S::PM + k * C + m]; },
+        mm<D, C, D, C, true, false, true>([&](int m, int k) { return s[S::PM + k * C + m]; },
                     [&](int k, int n) { return s[S::DO + k * D + n]; },
                     [&](int m, int n, float a) { s[S::DU + m * D + n] = a; }, lds);
         mm<D, C, D, D, false, false, true>([&](int m, int k) { return s[S::KB + m * D + k]; },
@@ -543,10 +543,10 @@ __global__ __launch_bounds__(NT) void kda_bwd_grad_kernel(BwdParams p) {
             const float sg = sigmoidf_(In::load(static_cast<const raw*>(p.gate), e));
             p.dgate[e] = In::load(static_cast<const raw*>(p.dy), e) * s[S::O + idx] * sg * (1.f - sg);
         }
-        mm<D, C, C, D, false, false, true>([&](int m, int k) { return s[S::DU + m * D + k]; },
+        mm<D, C, C, D, false, true, true>([&](int m, int k) { return s[S::DU + m * D + k]; },
                     [&](int k, int n) { return beta[n] * s[S::X + n * D + k]; },
                     [&](int m, int n, float a) { s[S::DLI + m * C + n] = n < m ? a : 0.f; }, lds);
-        mm<D, C, D, C, false, false, true>([&](int m, int k) { return s[S::LI + k * C + m]; },
+        mm<D, C, D, C, true, false, true>([&](int m, int k) { return s[S::LI + k * C + m]; },
                     [&](int k, int n) { return s[S::DU + k * D + n]; },
                     [&](int m, int n, float a) { s[S::DW + m * D + n] = a; }, lds);
         __syncthreads();
@@ -561,18 +561,18 @@ __global__ __launch_bounds__(NT) void kda_bwd_grad_kernel(BwdParams p) {
             for (int j = 0; j < D; ++j) acc = fmaf(s[S::DW + r * D + j], s[S::X + r * D + j], acc);
             s[S::DBX + r] = acc;
         }
-        mm<D, C, C, C, false, false, true>([&](int m, int k) { return s[S::LI + k * C + m]; },
+        mm<D, C, C, C, true, false, true>([&](int m, int k) { return s[S::LI + k * C + m]; },
                     [&](int k, int n) { return s[S::DLI + k * C + n]; },
                     [&](int m, int n, float a) { s[S::EM + m * C + n] = a; }, lds);
-        mm<D, C, D, D, false, false, true>([&](int m, int k) { return s[S::DO + m * D + k]; },
+        mm<D, C, D, D, false, true, true>([&](int m, int k) { return s[S::DO + m * D + k]; },
                     [&](int k, int n) { return S0[n * D + k]; },
                     [&](int m, int n, float a) { s[S::DQ + m * D + n] = a * s[S::EG + m * D + n]; }, lds);
-        mm<D, C, D, D, false, false, true>([&](int m, int k) { return beta[m] * s[S::DW + m * D + k]; },
+        mm<D, C, D, D, false, true, true>([&](int m, int k) { return beta[m] * s[S::DW + m * D + k]; },
                     [&](int k, int n) { return S0[n * D + k]; },
                     [&](int m, int n, float a) { s[S::DKT + m * D + n] = -a * s[S::EG + m * D + n]; }, lds);
         __syncthreads();
         // dA = -(E Li^T), strictly lower part (the gradient with respect to diag(beta) Bm)
-        mm<D, C, C, C, false, false, true>([&](int m, int k) { return s[S::EM + m * C + k]; },
+        mm<D, C, C, C, false, true, true>([&](int m, int k) { return s[S::EM + m * C + k]; },
                     [&](int k, int n) { return s[S::LI + n * C + k]; },
                     [&](int m, int n, float a) { s[S::DA + m * C + n] = n < m ? -a : 0.f; }, lds);
         __syncthreads();
