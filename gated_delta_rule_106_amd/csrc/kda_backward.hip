@@ -183,6 +183,27 @@ __device__ __forceinline__ void to_lds(float* dst, const float* src) {
     for (int i = 0; i < per; ++i) reinterpret_cast<float4*>(dst)[threadIdx.x + i * NT] = v[i];
 }
 
+// Eight consecutive input elements as fp32 (e is a multiple of 8, so the bf16 load is
+// 16-byte aligned and the fp32 loads 32-byte aligned), and eight fp32 to scratch.
+__device__ __forceinline__ void load8(const uint16_t* p, int64_t e, float (&o)[8]) {
+    const uint4 w = *reinterpret_cast<const uint4*>(p + e);
+    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {  // little-endian: element 2 j is the low half-word
+        o[2 * j] = __uint_as_float(ws[j] << 16);
+        o[2 * j + 1] = __uint_as_float(ws[j] & 0xffff0000u);
+    }
+}
+__device__ __forceinline__ void load8(const float* p, int64_t e, float (&o)[8]) {
+    const float4 a = *reinterpret_cast<const float4*>(p + e);
+    const float4 b = *reinterpret_cast<const float4*>(p + e + 4);
+    o[0] = a.x, o[1] = a.y, o[2] = a.z, o[3] = a.w, o[4] = b.x, o[5] = b.y, o[6] = b.z, o[7] = b.w;
+}
+__device__ __forceinline__ void store8(float* d, const float (&v)[8]) {
+    *reinterpret_cast<float4*>(d) = make_float4(v[0], v[1], v[2], v[3]);
+    *reinterpret_cast<float4*>(d + 4) = make_float4(v[4], v[5], v[6], v[7]);
+}
+
 // Steps shared by the prep and gradient kernels: the chunk's inputs in fp32 (zero
 // past the sequence's end, which makes the padding tokens identity steps), g, the
 // decayed operands, Bm, P and Li.
@@ -191,38 +212,52 @@ __device__ void chunk_common(const BwdParams& p, const ChunkPos& cp, float* s, f
     using S = Scr<D>;
     using LL = ChunkLds<D>;
     using raw = typename In::raw_t;
-    constexpr int PER = C * D / NT;  // elements per thread
-    constexpr int BATCH = 8;
-    static_assert(PER % BATCH == 0, "batches of loads");
+    // eight neighbouring channels of one token per lane and step (one 16-byte load per
+    // bf16 input), two steps in flight
+    constexpr int G8 = C * D / 8 / NT;  // groups of eight per thread
+    static_assert(G8 % 2 == 0, "pairs of groups");
 #pragma unroll 1
-    for (int b0 = 0; b0 < PER; b0 += BATCH) {
-        float kv[BATCH], qv[BATCH], vv[BATCH], lv[BATCH], dov[BATCH];
+    for (int g0 = 0; g0 < G8; g0 += 2) {
+        float k8[2][8], q8[2][8], v8[2][8], l8[2][8], y8[2][8], z8[2][8];
 #pragma unroll
-        for (int u = 0; u < BATCH; ++u) {
-            const int idx = threadIdx.x + (b0 + u) * NT;
-            const int r = idx / D, c = idx - r * D;
-            kv[u] = qv[u] = vv[u] = lv[u] = dov[u] = 0.f;
+        for (int u = 0; u < 2; ++u) {
+            const int grp = threadIdx.x + (g0 + u) * NT;
+            const int r = grp / (D / 8), c8 = 8 * (grp - r * (D / 8));
             if (r < cp.L) {
-                const int64_t e = elem<D>(p, cp, r, c);
-                kv[u] = In::load(static_cast<const raw*>(p.k), e);
-                qv[u] = In::load(static_cast<const raw*>(p.q), e);
-                vv[u] = In::load(static_cast<const raw*>(p.v), e);
-                lv[u] = clamp_log_alpha(In::load(static_cast<const raw*>(p.la), e), p.clamp != 0);
-                dov[u] = In::load(static_cast<const raw*>(p.dy), e) *
-                         sigmoidf_(In::load(static_cast<const raw*>(p.gate), e));
+                const int64_t e = elem<D>(p, cp, r, c8);
+                load8(static_cast<const raw*>(p.k), e, k8[u]);
+                load8(static_cast<const raw*>(p.q), e, q8[u]);
+                load8(static_cast<const raw*>(p.v), e, v8[u]);
+                load8(static_cast<const raw*>(p.la), e, l8[u]);
+                load8(static_cast<const raw*>(p.dy), e, y8[u]);
+                load8(static_cast<const raw*>(p.gate), e, z8[u]);
+            } else {
+#pragma unroll
+                for (int j = 0; j < 8; ++j) k8[u][j] = q8[u][j] = v8[u][j] = l8[u][j] = y8[u][j] = z8[u][j] = 0.f;
             }
         }
 #pragma unroll
-        for (int u = 0; u < BATCH; ++u) {
-            const int idx = threadIdx.x + (b0 + u) * NT;
-            const int r = idx / D, c = idx - r * D;
-            s[S::K + idx] = kv[u];
-            s[S::Q + idx] = qv[u];
-            s[S::V + idx] = vv[u];
-            s[S::G + idx] = lv[u];
-            s[S::DO + idx] = dov[u];
-            s[S::KTR + c * C + r] = kv[u];
-            s[S::QTR + c * C + r] = qv[u];
+        for (int u = 0; u < 2; ++u) {
+            const int grp = threadIdx.x + (g0 + u) * NT;
+            const int r = grp / (D / 8), c8 = 8 * (grp - r * (D / 8));
+            const bool live = r < cp.L;
+            float lv[8], dov[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                lv[j] = live ? clamp_log_alpha(l8[u][j], p.clamp != 0) : 0.f;
+                dov[j] = live ? y8[u][j] * sigmoidf_(z8[u][j]) : 0.f;
+            }
+            const int idx = r * D + c8;
+            store8(s + S::K + idx, k8[u]);
+            store8(s + S::Q + idx, q8[u]);
+            store8(s + S::V + idx, v8[u]);
+            store8(s + S::G + idx, lv);
+            store8(s + S::DO + idx, dov);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                s[S::KTR + (c8 + j) * C + r] = k8[u][j];
+                s[S::QTR + (c8 + j) * C + r] = q8[u][j];
+            }
         }
     }
     if (threadIdx.x < C) {
