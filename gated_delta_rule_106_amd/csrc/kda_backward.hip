@@ -289,14 +289,26 @@ __device__ void chunk_common(const BwdParams& p, const ChunkPos& cp, float* s, f
     __syncthreads();
     to_lds<C * D>(lds + LL::A0, s + S::KTR);
     to_lds<C * D>(lds + LL::A1, s + S::QTR);
-    for (int idx = threadIdx.x; idx < C * D; idx += NT) {
-        const int c = idx % D;
-        const float g = s[S::G + idx], gc = s[S::G + (C - 1) * D + c];
-        const float eg = ex(g), kv = s[S::K + idx];
-        s[S::EG + idx] = eg;
-        s[S::KT + idx] = kv * eg;
-        s[S::QT + idx] = s[S::Q + idx] * eg;
-        s[S::KB + idx] = kv * ex(gc - g);
+    // decayed operands, eight neighbouring channels per lane and step
+#pragma unroll 2
+    for (int grp = threadIdx.x; grp < C * D / 8; grp += NT) {
+        const int idx = 8 * grp, c8 = idx % D;
+        float g[8], gc[8], kv[8], qv[8], eg[8], kt[8], qt[8], kb[8];
+        load8(s + S::G + idx, 0, g);
+        load8(s + S::G + (C - 1) * D + c8, 0, gc);
+        load8(s + S::K + idx, 0, kv);
+        load8(s + S::Q + idx, 0, qv);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            eg[j] = ex(g[j]);
+            kt[j] = kv[j] * eg[j];
+            qt[j] = qv[j] * eg[j];
+            kb[j] = kv[j] * ex(gc[j] - g[j]);
+        }
+        store8(s + S::EG + idx, eg);
+        store8(s + S::KT + idx, kt);
+        store8(s + S::QT + idx, qt);
+        store8(s + S::KB + idx, kb);
     }
     __syncthreads();
     // pair products from LDS: channel-major k (A0), q (A1) and g (A2)
@@ -572,11 +584,20 @@ __global__ __launch_bounds__(NT) void kda_bwd_grad_kernel(BwdParams p) {
                     [&](int m, int n, float a) { s[S::DU + m * D + n] += a; }, lds);
         __syncthreads();
         // dZ = dY * O * sigmoid'(Z);  dLi = dU (diag(beta) X)^T, strictly lower part;  dW = Li^T dU
-        for (int idx = threadIdx.x; idx < cp.L * D; idx += NT) {
-            const int r = idx / D, c = idx - r * D;
-            const int64_t e = elem<D>(p, cp, r, c);
-            const float sg = sigmoidf_(In::load(static_cast<const raw*>(p.gate), e));
-            p.dgate[e] = In::load(static_cast<const raw*>(p.dy), e) * s[S::O + idx] * sg * (1.f - sg);
+#pragma unroll 2
+        for (int grp = threadIdx.x; grp < cp.L * D / 8; grp += NT) {
+            const int idx = 8 * grp, r = idx / D, c8 = idx - r * D;
+            const int64_t e = elem<D>(p, cp, r, c8);
+            float z[8], y[8], o[8], dz[8];
+            load8(static_cast<const raw*>(p.gate), e, z);
+            load8(static_cast<const raw*>(p.dy), e, y);
+            load8(s + S::O + idx, 0, o);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const float sg = sigmoidf_(z[j]);
+                dz[j] = y[j] * o[j] * sg * (1.f - sg);
+            }
+            store8(p.dgate + e, dz);
         }
         mm<D, C, C, D, false, true, true>([&](int m, int k) { return s[S::DU + m * D + k]; },
                     [&](int k, int n) { return beta[n] * s[S::X + n * D + k]; },
@@ -586,9 +607,15 @@ __global__ __launch_bounds__(NT) void kda_bwd_grad_kernel(BwdParams p) {
                     [&](int m, int n, float a) { s[S::DW + m * D + n] = a; }, lds);
         __syncthreads();
         // dV = diag(beta) dW;  dbeta's X part;  E = Li^T dLi;  the S0 parts of dQ and dKt
-        for (int idx = threadIdx.x; idx < cp.L * D; idx += NT) {
-            const int r = idx / D, c = idx - r * D;
-            p.dv[elem<D>(p, cp, r, c)] = beta[r] * s[S::DW + idx];
+#pragma unroll 2
+        for (int grp = threadIdx.x; grp < cp.L * D / 8; grp += NT) {
+            const int idx = 8 * grp, r = idx / D, c8 = idx - r * D;
+            float w[8];
+            load8(s + S::DW + idx, 0, w);
+            const float br = beta[r];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) w[j] *= br;
+            store8(p.dv + elem<D>(p, cp, r, c8), w);
         }
         if (threadIdx.x < C) {
             const int r = threadIdx.x;
@@ -628,6 +655,8 @@ __global__ __launch_bounds__(NT) void kda_bwd_grad_kernel(BwdParams p) {
         for (int idx = threadIdx.x; idx < C * D; idx += NT) {
             const int r = idx / D, c = idx - r * D;
             const float gr = lg[idx];
+            // scratch values first: their latency is covered by the LDS loops below
+            const float dq0 = s[S::DQ + idx], dkt0 = s[S::DKT + idx], dkb0 = s[S::DKB + idx];
             float pq = 0.f, aq = 0.f, ak = 0.f, pk = 0.f;
 #pragma unroll 4
             for (int j = 0; j <= r; ++j) {
@@ -641,10 +670,10 @@ __global__ __launch_bounds__(NT) void kda_bwd_grad_kernel(BwdParams p) {
                 ak = fmaf(lbeta[j] * lda[j * C + r], lk[j * D + c] * e, ak);
                 pk = fmaf(ldp[j * C + r], lq[j * D + c] * e, pk);
             }
-            const float dqf = s[S::DQ + idx] + pq;
-            const float dktf = s[S::DKT + idx] + lbeta[r] * aq;
+            const float dqf = dq0 + pq;
+            const float dktf = dkt0 + lbeta[r] * aq;
             const float dkif = ak + pk;
-            const float dkbf = s[S::DKB + idx] * ex(lg[(C - 1) * D + c] - gr);
+            const float dkbf = dkb0 * ex(lg[(C - 1) * D + c] - gr);
             const float kv = lk[idx], qv = lq[idx];
             if (r < cp.L) {
                 const int64_t e = elem<D>(p, cp, r, c);
