@@ -699,17 +699,21 @@ __global__ __launch_bounds__(NT) void kda_bwd_grad_kernel(BwdParams p) {
             for (int r = 0; r < C; ++r) acc += s[S::DKT + r * D + c];
 #pragma unroll 1
             for (int r0 = C - 16; r0 >= 0; r0 -= 16) {
-                float col[16];  // 16 rows of g's gradient, read before their stores
+                // 16 rows of g's gradient and of the raw log alpha, read before their stores
+                float col[16], raw_la[16];
 #pragma unroll
-                for (int u = 0; u < 16; ++u) col[u] = s[S::DQ + (r0 + u) * D + c];
+                for (int u = 0; u < 16; ++u) {
+                    col[u] = s[S::DQ + (r0 + u) * D + c];
+                    raw_la[u] = r0 + u < cp.L ? In::load(static_cast<const raw*>(p.la), elem<D>(p, cp, r0 + u, c)) : 0.f;
+                }
+#pragma unroll
                 for (int u = 15; u >= 0; --u) {
                     const int r = r0 + u;
                     acc += col[u];
                     if (r < cp.L) {
-                        const int64_t e = elem<D>(p, cp, r, c);
-                        const float l = In::load(static_cast<const raw*>(p.la), e);
+                        const float l = raw_la[u];
                         const bool live = p.clamp == 0 || (l >= kLogAlphaMin && l <= 0.f);
-                        p.dla[e] = live ? acc : 0.f;
+                        p.dla[elem<D>(p, cp, r, c)] = live ? acc : 0.f;
                     }
                 }
             }
