@@ -84,23 +84,40 @@ __device__ __forceinline__ void mm(FA a, FB b, FO o, float* lds) {
     if (V4) {
         // each lane copies four neighbours along the source's contiguous index, which the
         // compiler merges into one 16-byte load
+        constexpr int NA = TA ? M * K / 16 : M * K / 4, NB4 = TB ? K * N / 16 : K * N / 4;
 #pragma unroll 2
-        for (int i = threadIdx.x; i < M * K / 4; i += NT) {
-            if (TA) {  // a(m, k) is read from a k-major source: four consecutive m
-                const int k = i / (M / 4), m = 4 * (i - k * (M / 4));
+        for (int i = threadIdx.x; i < NA; i += NT) {
+            if (TA) {
+                // a(m, k) is read from a k-major source: a 4 x 4 block per lane, four
+                // 16-byte loads along m, transposed in registers into four rows of LDS
+                const int k = 4 * (i / (M / 4)), m = 4 * (i - (i / (M / 4)) * (M / 4));
+                float v[4][4];
 #pragma unroll
-                for (int j = 0; j < 4; ++j) la[(m + j) * KP + k] = a(m + j, k);
+                for (int t = 0; t < 4; ++t)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) v[t][j] = a(m + j, k + t);
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    *reinterpret_cast<float4*>(la + (m + j) * KP + k) = make_float4(v[0][j], v[1][j], v[2][j], v[3][j]);
             } else {
                 const int m = i / (K / 4), k = 4 * (i - m * (K / 4));
                 *reinterpret_cast<float4*>(la + m * KP + k) = make_float4(a(m, k), a(m, k + 1), a(m, k + 2), a(m, k + 3));
             }
         }
 #pragma unroll 2
-        for (int i = threadIdx.x; i < K * N / 4; i += NT) {
-            if (TB) {  // b(k, n) is read from an n-major source: four consecutive k
-                const int n = i / (K / 4), k = 4 * (i - n * (K / 4));
+        for (int i = threadIdx.x; i < NB4; i += NT) {
+            if (TB) {
+                // b(k, n) is read from an n-major source: a 4 x 4 block per lane, four
+                // 16-byte loads along k, transposed in registers into four rows of LDS
+                const int n = 4 * (i / (K / 4)), k = 4 * (i - (i / (K / 4)) * (K / 4));
+                float v[4][4];
 #pragma unroll
-                for (int j = 0; j < 4; ++j) lb[(k + j) * NP + n] = b(k + j, n);
+                for (int t = 0; t < 4; ++t)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) v[t][j] = b(k + j, n + t);
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    *reinterpret_cast<float4*>(lb + (k + j) * NP + n) = make_float4(v[0][j], v[1][j], v[2][j], v[3][j]);
             } else {
                 const int k = i / (N / 4), n = 4 * (i - k * (N / 4));
                 *reinterpret_cast<float4*>(lb + k * NP + n) = make_float4(b(k, n), b(k, n + 1), b(k, n + 2), b(k, n + 3));
