@@ -49,8 +49,8 @@ struct Rec {
     static constexpr int64_t SIZE = 2 * CD + 2 * DD + D;
 };
 
-// fp32 offsets inside one scratch slot.  C x D row-major blocks, then D x C
-// (channel-major) copies, then C x C blocks, then two C-vectors.
+// fp32 offsets inside one scratch slot.  C x D row-major blocks, then three spare
+// C x D blocks (KTR, QTR, GTR: not written), then C x C blocks, then two C-vectors.
 template <int D>
 struct Scr {
     static constexpr int64_t CD = (int64_t)C * D, CC = (int64_t)C * C;
@@ -183,10 +183,29 @@ __device__ __forceinline__ int64_t elem(const BwdParams& p, const ChunkPos& cp, 
 // read three row-major C x D blocks, two C x C blocks and beta.
 template <int D>
 struct ChunkLds {
-    static constexpr int CD = C * D, CC = C * C;
-    static constexpr int A0 = 0, A1 = CD, A2 = 2 * CD, B0 = 3 * CD, B1 = 3 * CD + CC, BETA = 3 * CD + 2 * CC;
+    static constexpr int CP = C + 4;  // pitch of the channel-major copies (bank spread)
+    static constexpr int CC = C * C, DCP = D * CP;
+    static constexpr int A0 = 0, A1 = DCP, A2 = 2 * DCP, B0 = 3 * DCP, B1 = 3 * DCP + CC, BETA = 3 * DCP + 2 * CC;
     static constexpr int TOTAL = BETA + C;
 };
+
+// dst[c * (C + 4) + r] = src[r * D + c] for a C x D row-major block of scratch: a 4 x 4
+// block per lane and step, four 16-byte loads along the channels, four 16-byte LDS
+// stores along the tokens.
+template <int D>
+__device__ __forceinline__ void to_lds_cm(float* dst, const float* src) {
+    constexpr int CP = C + 4;
+    for (int i = threadIdx.x; i < (C / 4) * (D / 4); i += NT) {
+        const int rb = i / (D / 4), c = 4 * (i - rb * (D / 4)), r = 4 * rb;
+        float4 v[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) v[t] = *reinterpret_cast<const float4*>(src + (r + t) * D + c);
+        *reinterpret_cast<float4*>(dst + (c + 0) * CP + r) = make_float4(v[0].x, v[1].x, v[2].x, v[3].x);
+        *reinterpret_cast<float4*>(dst + (c + 1) * CP + r) = make_float4(v[0].y, v[1].y, v[2].y, v[3].y);
+        *reinterpret_cast<float4*>(dst + (c + 2) * CP + r) = make_float4(v[0].z, v[1].z, v[2].z, v[3].z);
+        *reinterpret_cast<float4*>(dst + (c + 3) * CP + r) = make_float4(v[0].w, v[1].w, v[2].w, v[3].w);
+    }
+}
 
 // Copies n floats (a multiple of 4 * NT) from global scratch to LDS, all loads of a
 // thread issued before its stores.
@@ -270,11 +289,6 @@ __device__ void chunk_common(const BwdParams& p, const ChunkPos& cp, float* s, f
             store8(s + S::V + idx, v8[u]);
             store8(s + S::G + idx, lv);
             store8(s + S::DO + idx, dov);
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                s[S::KTR + (c8 + j) * C + r] = k8[u][j];
-                s[S::QTR + (c8 + j) * C + r] = q8[u][j];
-            }
         }
     }
     if (threadIdx.x < C) {
@@ -298,14 +312,13 @@ __device__ void chunk_common(const BwdParams& p, const ChunkPos& cp, float* s, f
             for (int u = 0; u < 16; ++u) {
                 acc += col[u];
                 s[S::G + (r0 + u) * D + c] = acc;
-                s[S::GTR + c * C + r0 + u] = acc;
-                lds[LL::A2 + c * C + r0 + u] = acc;
             }
         }
     }
     __syncthreads();
-    to_lds<C * D>(lds + LL::A0, s + S::KTR);
-    to_lds<C * D>(lds + LL::A1, s + S::QTR);
+    to_lds_cm<D>(lds + LL::A0, s + S::K);
+    to_lds_cm<D>(lds + LL::A1, s + S::Q);
+    to_lds_cm<D>(lds + LL::A2, s + S::G);
     // decayed operands, eight neighbouring channels per lane and step
 #pragma unroll 2
     for (int grp = threadIdx.x; grp < C * D / 8; grp += NT) {
@@ -328,17 +341,17 @@ __device__ void chunk_common(const BwdParams& p, const ChunkPos& cp, float* s, f
         store8(s + S::KB + idx, kb);
     }
     __syncthreads();
-    // pair products from LDS: channel-major k (A0), q (A1) and g (A2)
+    // pair products from LDS: channel-major k (A0), q (A1) and g (A2), row pitch C + 4
     for (int idx = threadIdx.x; idx < C * C; idx += NT) {
         const int r = idx / C, sc = idx - r * C;
         float bs = 0.f, ps = 0.f;
         if (sc <= r) {
 #pragma unroll 8
             for (int c = 0; c < D; ++c) {
-                const float e = ex(lds[LL::A2 + c * C + r] - lds[LL::A2 + c * C + sc]);
-                const float ks = lds[LL::A0 + c * C + sc] * e;
-                bs = fmaf(lds[LL::A0 + c * C + r], ks, bs);
-                ps = fmaf(lds[LL::A1 + c * C + r], ks, ps);
+                const float e = ex(lds[LL::A2 + c * LL::CP + r] - lds[LL::A2 + c * LL::CP + sc]);
+                const float ks = lds[LL::A0 + c * LL::CP + sc] * e;
+                bs = fmaf(lds[LL::A0 + c * LL::CP + r], ks, bs);
+                ps = fmaf(lds[LL::A1 + c * LL::CP + r], ks, ps);
             }
         }
         const float bm = sc < r ? bs : 0.f;
