@@ -49,16 +49,15 @@ struct Rec {
     static constexpr int64_t SIZE = 2 * CD + 2 * DD + D;
 };
 
-// fp32 offsets inside one scratch slot.  C x D row-major blocks, then three spare
-// C x D blocks (KTR, QTR, GTR: not written), then C x C blocks, then two C-vectors.
+// fp32 offsets inside one scratch slot: C x D row-major blocks, then C x C blocks,
+// then two C-vectors.
 template <int D>
 struct Scr {
     static constexpr int64_t CD = (int64_t)C * D, CC = (int64_t)C * C;
     static constexpr int64_t K = 0, Q = CD, V = 2 * CD, G = 3 * CD, DO = 4 * CD, EG = 5 * CD, KT = 6 * CD,
                              QT = 7 * CD, KB = 8 * CD, X = 9 * CD, U = 10 * CD, O = 11 * CD, DU = 12 * CD,
-                             DW = 13 * CD, DKB = 14 * CD, DQ = 15 * CD, DKT = 16 * CD, KTR = 17 * CD,
-                             QTR = 18 * CD, GTR = 19 * CD;
-    static constexpr int64_t BM = 20 * CD, PM = BM + CC, LI = BM + 2 * CC, DP = BM + 3 * CC,
+                             DW = 13 * CD, DKB = 14 * CD, DQ = 15 * CD, DKT = 16 * CD;
+    static constexpr int64_t BM = 17 * CD, PM = BM + CC, LI = BM + 2 * CC, DP = BM + 3 * CC,
                              DLI = BM + 4 * CC, EM = BM + 5 * CC, DA = BM + 6 * CC;
     static constexpr int64_t BETA = BM + 7 * CC, DBX = BETA + C;
     static constexpr int64_t SIZE = DBX + C;

@@ -342,7 +342,7 @@ def test_bwd_workspace_size(lib):
         assert lib.kda_chunk_bwd_workspace_size(ctypes.byref(a), ctypes.byref(n)) == _abi.KDA_OK
         items = B * H * ((T + 63) // 64)
         rec = 2 * 64 * D + 2 * D * D + D
-        slot = 20 * 64 * D + 7 * 64 * 64 + 2 * 64
+        slot = 17 * 64 * D + 7 * 64 * 64 + 2 * 64
         want = r256(items * rec * 4) + 2 * r256(items * D * D * 4) + r256(min(items, 512) * slot * 4)
         assert n.value == want
     a = _good_bwd(T=0)
