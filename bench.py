@@ -253,7 +253,7 @@ def counter_pass(kda, head, dec_wl, n_sets, dev, stream):
     """A short run for hardware-counter collection (FETCH_SIZE / WRITE_SIZE):
     a copy-shaped elementwise kernel of known size (1 GiB read, 1 GiB
     written) to calibrate the counters, then the headline prefill over the
-    rotating input sets and a few decode steps."""
+    rotating input sets, a few decode steps and two backward calls."""
     import torch
     n = 1 << 28
     src = torch.randn(n, device=dev)
@@ -265,7 +265,17 @@ def counter_pass(kda, head, dec_wl, n_sets, dev, stream):
     torch.cuda.empty_cache()
     pre, _ = bench_prefill(kda, head, n_sets, 0, n_sets, dev, stream)
     dec = bench_decode(kda, dec_wl, 4, 0, dev, stream)
-    return {"counter_pass": True, "calibration": {"kernel": "torch.neg fp32, 2^28 elements",
+    # two backward calls on the headline shape
+    from kda_workloads import make_inputs
+    x = to_dev(make_inputs(head, seed=head.seed), dev)
+    dy = torch.randn((head.B, head.T, head.H, head.Dv), generator=torch.Generator().manual_seed(head.seed + 7))
+    dy = dy.to(head.torch_dtype).to(dev)
+    ws = torch.empty(kda_bwd_workspace_bytes(head), dtype=torch.uint8, device=dev)
+    for _ in range(2):
+        kda.chunk_bwd(*(x[k] for k in KEYS), dy, initial_state=x.get("initial_state"), workspace=ws,
+                      need_initial_state_grad=False)
+    torch.cuda.synchronize()
+    return {"counter_pass": True, "backward_calls": 2, "backward_workload": head.name, "calibration": {"kernel": "torch.neg fp32, 2^28 elements",
                                                   "bytes_read": 4 * n, "bytes_written": 4 * n},
             "prefill_calls": n_sets, "prefill_workload": head.name,
             "decode_calls": 4, "decode_workload": dec_wl.name,
@@ -376,37 +386,45 @@ def backward_bytes(wl) -> int:
     return wl.B * wl.T * per_tok + states
 
 
-def bench_backward(kda, wl, steps, warmup, dev, stream):
-    """kda_chunk_bwd on the headline shape (gradients of sum(d_out * y) through the
-    forward; fp32 arithmetic), timed like the forward, and the forward call beside it."""
-    import torch
-    from kda_workloads import make_inputs
-    x = to_dev(make_inputs(wl, seed=wl.seed), dev)
-    g = torch.Generator(device="cpu").manual_seed(wl.seed + 7)
-    x["dy"] = torch.randn((wl.B, wl.T, wl.H, wl.Dv), generator=g).to(wl.torch_dtype).to(dev)
-    x["bws"] = None
-
-    def bwd(x):
-        kda.chunk_bwd(*(x[k] for k in KEYS), x["dy"], initial_state=x.get("initial_state"),
-                      workspace=x["bws"], need_initial_state_grad=False)
-    # first call sizes the workspace; keep it for the timed calls
-    out = kda.chunk_bwd(*(x[k] for k in KEYS), x["dy"], initial_state=x.get("initial_state"))
-    del out
+def kda_bwd_workspace_bytes(wl) -> int:
+    """Workspace bytes of one kda_chunk_bwd call on this workload (host-side query)."""
     import ctypes
     from gated_delta_rule_106_amd import _abi
     a = _abi.BwdArgs()
     a.B, a.T, a.H, a.Dk, a.Dv = wl.B, wl.T, wl.H, wl.Dk, wl.Dv
     a.dtype = _abi.KDA_BF16 if wl.dtype == "bf16" else _abi.KDA_F32
     n = ctypes.c_size_t(0)
-    assert _abi.load().kda_chunk_bwd_workspace_size(ctypes.byref(a), ctypes.byref(n)) == 0
-    x["bws"] = torch.empty(int(n.value), dtype=torch.uint8, device=dev)
+    rc = _abi.load().kda_chunk_bwd_workspace_size(ctypes.byref(a), ctypes.byref(n))
+    if rc != 0:
+        raise RuntimeError(f"kda_chunk_bwd_workspace_size: status {rc}")
+    return max(int(n.value), 16)
+
+
+def bench_backward(kda, wl, steps, warmup, dev, stream):
+    """kda_chunk_bwd on the headline shape (gradients of sum(d_out * y) through the
+    forward; fp32 arithmetic), timed like the forward."""
+    import torch
+    from kda_workloads import make_inputs
+    x = to_dev(make_inputs(wl, seed=wl.seed), dev)
+    g = torch.Generator(device="cpu").manual_seed(wl.seed + 7)
+    x["dy"] = torch.randn((wl.B, wl.T, wl.H, wl.Dv), generator=g).to(wl.torch_dtype).to(dev)
+    n_ws = kda_bwd_workspace_bytes(wl)
+    x["bws"] = torch.empty(n_ws, dtype=torch.uint8, device=dev)
+
+    def bwd(x):
+        kda.chunk_bwd(*(x[k] for k in KEYS), x["dy"], initial_state=x.get("initial_state"),
+                      workspace=x["bws"], need_initial_state_grad=False)
     _, t_b = time_calls(bwd, [x], steps, warmup, stream)
     toks = wl.B * wl.T
     byt = backward_bytes(wl)
+    gbs = byt / (t_b / 1e3) / 1e9
     res = {"workload": wl.name, "us_per_call": 1e3 * t_b, "tokens_per_s": toks / (t_b / 1e3),
-           "alg_bytes_per_call": byt, "alg_gbs": byt / (t_b / 1e3) / 1e9,
-           "workspace_bytes": int(n.value),
-           "compute": "fp32 (inputs bf16, gradients fp32)"}
+           "alg_bytes_per_call": byt, "alg_gbs": gbs, "workspace_bytes": n_ws,
+           "compute": "fp32 (inputs bf16, gradients fp32)",
+           "roofline": {"kernel": "kda_chunk_bwd = kda_bwd_prep_kernel + kda_bwd_sweep_kernel + "
+                                  "kda_bwd_grad_kernel (one call, three launches)",
+                        "bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                        "frac": gbs / HBM_PEAK_GBS, "traffic": stored_traffic("backward_" + wl.name)}}
     log(f"backward {wl.name}: {res['us_per_call']:.1f} us/call, {res['tokens_per_s']:.3e} tok/s")
     del x
     torch.cuda.empty_cache()
