@@ -446,11 +446,16 @@ __global__ __launch_bounds__(NT) void kda_bwd_sweep_kernel(BwdParams p) {
     float* St = lds + L::ST;
     float* Y = lds + L::Y;
     constexpr int tiles = D / TILE;
+    // consecutive workgroups go to different XCDs: the logical order puts the column
+    // tiles of one (direction, b, h), which all read the same chunk records, on blocks
+    // that share blockIdx % 8 and so one XCD's L2 (the grid is a multiple of 8)
+    const int64_t nblk = gridDim.x;
+    const int64_t logical = (int64_t)(blockIdx.x % 8) * (nblk / 8) + blockIdx.x / 8;
     // the two sweeps are independent (R does not depend on the states): the first half
-    // of the grid runs the forward one, the second half the backward one
-    const int64_t half = gridDim.x / 2;
-    const int dir = blockIdx.x >= half ? 1 : 0;
-    const int64_t bid = blockIdx.x - dir * half;
+    // of the logical grid runs the forward one, the second half the backward one
+    const int64_t half = nblk / 2;
+    const int dir = logical >= half ? 1 : 0;
+    const int64_t bid = logical - dir * half;
     const int64_t bh = bid / tiles;
     const int col0 = (int)(bid - bh * tiles) * TILE;
     const int64_t DD = (int64_t)D * D;
@@ -782,6 +787,7 @@ hipError_t launch_d(const BwdParams& p, hipStream_t stream) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(ks),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, lds);
         if (e != hipSuccess) return e;
+        static_assert((2 * (D / TILE)) % 8 == 0, "the sweep grid is a multiple of 8 (XCD mapping)");
         hipLaunchKernelGGL(ks, dim3((unsigned)(2 * bh * (D / TILE))), dim3(NT), lds, stream, p);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
