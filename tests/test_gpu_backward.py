@@ -173,3 +173,21 @@ def test_full_size_state_in_out_sampled_units():
         ref = _oracle(xs, dy[b:b + 1, :, h:h + 1].contiguous(), dst[b:b + 1, h:h + 1].contiguous())
         gh = {n: (g[n][b:b + 1, :, h:h + 1] if n != "dinitial_state" else g[n][b:b + 1, h:h + 1]) for n in GRADS}
         _check(f"B2 H32 T8192 d128 bf16 state in/out, unit (b={b}, h={h})", gh, ref)
+
+
+def test_without_initial_state_gradient():
+    """d_initial_state NULL (the launch configuration the bench times): every other
+    gradient is bit for bit the one of a call that also returns dS0."""
+    wl = small(CONFIGS[2], B=1, H=2, T=150, Dk=64, Dv=64)
+    x = make_inputs(wl)
+    dy, dst = _cotangents(wl, 51, True)
+    d = {n: x[n].cuda() for n in KEYS}
+    s0, dstc, dyc = x["initial_state"].cuda(), dst.cuda(), dy.cuda()
+    full = kda().chunk_bwd(*(d[n] for n in KEYS), dyc, initial_state=s0, d_final_state=dstc)
+    part = kda().chunk_bwd(*(d[n] for n in KEYS), dyc, initial_state=s0, d_final_state=dstc,
+                           need_initial_state_grad=False)
+    torch.cuda.synchronize()
+    assert part["dinitial_state"] is None
+    for n in GRADS[:-1]:
+        assert torch.equal(full[n], part[n]), n
+    say("[bwd] without dS0: the other gradients are unchanged")
