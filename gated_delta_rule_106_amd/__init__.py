@@ -108,7 +108,8 @@ def workspace_bytes(B, T, H, D, dtype=torch.bfloat16, chunk=0) -> int:
 
 def chunk_fwd(q, k, v, log_alpha, beta, gate, initial_state=None, output_final_state=False,
               chunk=0, clamp=True, out_dtype=torch.float32, out=None, final_state=None,
-              workspace=None, segment_scan=True, qk_norm=False, gate_logits=False, cards_ready=False):
+              workspace=None, segment_scan=True, qk_norm=False, gate_logits=False, cards_ready=False,
+              no_alloc=False):
     """Chunkwise-parallel KDA forward on the current HIP stream.
 
     q, k, log_alpha: [B, T, H, Dk]; v, gate: [B, T, H, Dv]; beta: [B, T, H];
@@ -121,7 +122,10 @@ def chunk_fwd(q, k, v, log_alpha, beta, gate, initial_state=None, output_final_s
     ``gate_logits``: ``log_alpha`` holds forget-gate logits x and the kernel uses
     max(logsigmoid(x), ln 0.0067).  ``cards_ready``: ``workspace`` already holds the
     cards of these inputs (from ``chunk_summary(..., q=q, workspace=workspace)``), so
-    the card builder is skipped.
+    the card builder is skipped.  ``no_alloc``: call ``kda_chunk_fwd_noalloc``, which
+    keeps the cards in the library's fixed per-device scratch instead of a workspace
+    (``workspace`` must then be None; pass ``out`` and ``final_state`` too for a call
+    that allocates nothing at all).
     """
     lib = _abi.load()
     dev = q.device
@@ -145,20 +149,29 @@ def chunk_fwd(q, k, v, log_alpha, beta, gate, initial_state=None, output_final_s
         raise ValueError("out must be [B, T, H, Dv] of out_dtype")
     if output_final_state and final_state is None:
         final_state = torch.empty((B, H, Dk, Dv), dtype=torch.float32, device=dev)
-    n = ctypes.c_size_t(0)
-    rc = lib.kda_chunk_fwd_workspace_size(ctypes.byref(a), ctypes.byref(n))
-    if rc != _abi.KDA_OK:
-        raise KDAError(rc, "kda_chunk_fwd_workspace_size")
-    if workspace is None or workspace.numel() < n.value:
-        workspace = torch.empty(max(int(n.value), 16), dtype=torch.uint8, device=dev)
+    if no_alloc:
+        if workspace is not None or cards_ready:
+            raise ValueError("no_alloc takes no workspace (the cards go to the library's scratch)")
+    else:
+        n = ctypes.c_size_t(0)
+        rc = lib.kda_chunk_fwd_workspace_size(ctypes.byref(a), ctypes.byref(n))
+        if rc != _abi.KDA_OK:
+            raise KDAError(rc, "kda_chunk_fwd_workspace_size")
+        if workspace is None or workspace.numel() < n.value:
+            workspace = torch.empty(max(int(n.value), 16), dtype=torch.uint8, device=dev)
     _check_dev(dict(q=q, k=k, v=v, log_alpha=log_alpha, beta=beta, gate=gate, out=out,
                     initial_state=initial_state, final_state=final_state), dev)
     a.q, a.k, a.v = _ptr(q), _ptr(k), _ptr(v)
     a.log_alpha, a.beta, a.gate, a.out = _ptr(log_alpha), _ptr(beta), _ptr(gate), _ptr(out)
     a.initial_state = _ptr(initial_state)
     a.final_state = _ptr(final_state) if output_final_state else None
-    a.workspace, a.workspace_bytes = _ptr(workspace), workspace.numel()
     stream = torch.cuda.current_stream(dev).cuda_stream
+    if no_alloc:
+        rc = lib.kda_chunk_fwd_noalloc(ctypes.byref(a), ctypes.c_void_p(stream))
+        if rc != _abi.KDA_OK:
+            raise KDAError(rc, "kda_chunk_fwd_noalloc")
+        return out, (final_state if output_final_state else None)
+    a.workspace, a.workspace_bytes = _ptr(workspace), workspace.numel()
     rc = lib.kda_chunk_fwd(ctypes.byref(a), ctypes.c_void_p(stream))
     if rc != _abi.KDA_OK:
         raise KDAError(rc, "kda_chunk_fwd")

@@ -15,6 +15,8 @@ KDA_ERR_UNSUPPORTED = -3
 KDA_ERR_WORKSPACE = -4
 KDA_ERR_ALIGN = -5
 KDA_ERR_HIP = -6
+KDA_ERR_TOO_LARGE = -7
+KDA_NOALLOC_SCRATCH_BYTES = 64 << 20
 KDA_FLAG_NO_CLAMP = 1
 KDA_FLAG_NO_SEGMENT_SCAN = 2
 KDA_FLAG_QK_L2NORM = 4
@@ -22,7 +24,7 @@ KDA_FLAG_GATE_LOGITS = 8
 KDA_FLAG_CARDS_READY = 16
 
 # every extern "C" entry point of include/kda.h
-EXPORTS = ("kda_chunk_fwd_workspace_size", "kda_chunk_fwd", "kda_chunk_fwd_varlen_workspace_size",
+EXPORTS = ("kda_chunk_fwd_workspace_size", "kda_chunk_fwd", "kda_chunk_fwd_noalloc", "kda_chunk_fwd_varlen_workspace_size",
            "kda_chunk_fwd_varlen", "kda_chunk_summary",
            "kda_combine_states", "kda_chunk_bwd_workspace_size", "kda_chunk_bwd", "kda_decode_step", "kda_status_str", "kda_version")
 
@@ -110,6 +112,8 @@ def load(path: str = LIB_PATH):
     lib.kda_chunk_fwd_workspace_size.restype = ctypes.c_int
     lib.kda_chunk_fwd.argtypes = [ctypes.POINTER(FwdArgs), ctypes.c_void_p]
     lib.kda_chunk_fwd.restype = ctypes.c_int
+    lib.kda_chunk_fwd_noalloc.argtypes = [ctypes.POINTER(FwdArgs), ctypes.c_void_p]
+    lib.kda_chunk_fwd_noalloc.restype = ctypes.c_int
     lib.kda_chunk_fwd_varlen_workspace_size.argtypes = [ctypes.POINTER(VarlenArgs),
                                                         ctypes.POINTER(ctypes.c_size_t)]
     lib.kda_chunk_fwd_varlen_workspace_size.restype = ctypes.c_int

@@ -2,12 +2,19 @@
 // Every check runs before the first HIP call; see include/kda.h for the contract.
 #include <limits.h>
 
+#include <mutex>
+
 #include "../../include/kda.h"
 #include "kda_backward.h"
 #include "kda_decode.h"
 #include "kda_prefill.h"
 #include "kda_segment.h"
 #include "kda_varlen.h"
+
+// Scratch of kda_chunk_fwd_noalloc: the per-chunk cards (and segment summaries) that
+// kda_chunk_fwd keeps in the caller's workspace.  Each device holds its own copy from the
+// loading of the library's code until the process ends; every call on a device shares it.
+static __device__ __align__(256) unsigned char scratch[KDA_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -128,6 +135,46 @@ int check_bwd(const kda_bwd_args* a, int64_t* nchunks, int64_t* ws_total) {
     return KDA_OK;
 }
 
+// Token tensors present and aligned, states aligned (after check_shape).
+int check_fwd_tensors(const kda_fwd_args* a) {
+    if (a->B * a->T * a->H > 0) {
+        const void* req[] = {a->q, a->k, a->v, a->log_alpha, a->beta, a->gate, a->out};
+        for (const void* p : req)
+            if (!p) return KDA_ERR_NULL;
+        for (const void* p : req)
+            if (!aligned16(p)) return KDA_ERR_ALIGN;
+    }
+    if (!aligned16(a->initial_state) || !aligned16(a->final_state)) return KDA_ERR_ALIGN;
+    return KDA_OK;
+}
+
+int run_chunk_fwd(const kda_fwd_args* a, int c, int64_t nc, int64_t cb, void* workspace, hipStream_t stream);
+
+// Device address of `scratch` on the stream's device, looked up once per device (with
+// that device current) and kept.  The array's host-side name is only a handle for the
+// runtime: kernels and copies take the address returned here.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+int scratch_address(hipStream_t stream, void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return KDA_ERR_HIP;
+    if (stream) {  // the work goes to the stream's device: it must be the current one
+        hipDevice_t sdev = -1;
+        if (hipStreamGetDevice(stream, &sdev) != hipSuccess) return KDA_ERR_HIP;
+        if ((int)sdev != dev) return KDA_ERR_UNSUPPORTED;
+    }
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return KDA_ERR_HIP;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return KDA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -191,6 +238,7 @@ const char* kda_status_str(int status) {
         case KDA_ERR_WORKSPACE: return "workspace missing or too small";
         case KDA_ERR_ALIGN: return "a pointer is not 16-byte aligned";
         case KDA_ERR_HIP: return "the HIP runtime reported a launch error";
+        case KDA_ERR_TOO_LARGE: return "the call needs more scratch than the fixed no-allocation buffer holds";
         default: return "unknown status";
     }
 }
@@ -211,28 +259,49 @@ int kda_chunk_fwd(const kda_fwd_args* a, hipStream_t stream) {
     int64_t nc, cb, need;
     int st = check_shape(a, &c, &nc, &cb, &need);
     if (st != KDA_OK) return st;
-    const bool has_tokens = a->B * a->T * a->H > 0;
-    if (has_tokens) {
-        const void* req[] = {a->q, a->k, a->v, a->log_alpha, a->beta, a->gate, a->out};
-        for (const void* p : req)
-            if (!p) return KDA_ERR_NULL;
-        for (const void* p : req)
-            if (!aligned16(p)) return KDA_ERR_ALIGN;
-    }
-    if (!aligned16(a->initial_state) || !aligned16(a->final_state)) return KDA_ERR_ALIGN;
+    st = check_fwd_tensors(a);
+    if (st != KDA_OK) return st;
     if (need > 0) {
         if (!a->workspace) return KDA_ERR_WORKSPACE;
         if ((int64_t)a->workspace_bytes < need) return KDA_ERR_WORKSPACE;
         if (!aligned16(a->workspace)) return KDA_ERR_ALIGN;
     }
+    return run_chunk_fwd(a, c, nc, cb, a->workspace, stream);
+}
+
+int kda_chunk_fwd_noalloc(const kda_fwd_args* a, hipStream_t stream) {
+    if (!a) return KDA_ERR_NULL;
+    int c;
+    int64_t nc, cb, need;
+    int st = check_shape(a, &c, &nc, &cb, &need);
+    if (st != KDA_OK) return st;
+    // the cards of an earlier call are not known to be in the shared buffer
+    if (a->flags & KDA_FLAG_CARDS_READY) return KDA_ERR_UNSUPPORTED;
+    if ((uint64_t)need > (uint64_t)KDA_NOALLOC_SCRATCH_BYTES) return KDA_ERR_TOO_LARGE;
+    st = check_fwd_tensors(a);
+    if (st != KDA_OK) return st;
+    if (a->B * a->H == 0) return KDA_OK;
+    if (a->B * a->T * a->H == 0 && !a->final_state) return KDA_OK;
+    void* ws = nullptr;
+    st = scratch_address(stream, &ws);
+    if (st != KDA_OK) return st;
+    return run_chunk_fwd(a, c, nc, cb, ws, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+int run_chunk_fwd(const kda_fwd_args* a, int c, int64_t nc, int64_t cb, void* workspace, hipStream_t stream) {
+    const bool has_tokens = a->B * a->T * a->H > 0;
     if (a->B * a->H == 0) return KDA_OK;
     if (!has_tokens && !a->final_state) return KDA_OK;
 
-    kda::PrepParams pp{a->q, a->k, a->v, a->log_alpha, a->beta, a->workspace,
+    kda::PrepParams pp{a->q, a->k, a->v, a->log_alpha, a->beta, workspace,
                        a->B, a->T, a->H, nc, (a->flags & KDA_FLAG_NO_CLAMP) ? 0 : 1,
                        (a->flags & KDA_FLAG_QK_L2NORM) ? 1 : 0, (a->flags & KDA_FLAG_GATE_LOGITS) ? 1 : 0};
     pp.cards_ready = (a->flags & KDA_FLAG_CARDS_READY) ? 1 : 0;
-    kda::RecurParams rp{a->gate, a->out, a->initial_state, a->final_state, a->workspace,
+    kda::RecurParams rp{a->gate, a->out, a->initial_state, a->final_state, workspace,
                         a->B, a->T, a->H, nc, nc, 1, nullptr};
     // the state pass of every segment reads initial_state at its start while the last
     // segment writes final_state at its end: no segments when the two overlap
@@ -244,13 +313,17 @@ int kda_chunk_fwd(const kda_fwd_args* a, hipStream_t stream) {
         if (P > 1) {
             rp.nseg = P;
             rp.seg_len = (nc + P - 1) / P;
-            rp.sums = reinterpret_cast<float*>(static_cast<unsigned char*>(a->workspace) + a->B * a->H * nc * cb);
+            rp.sums = reinterpret_cast<float*>(static_cast<unsigned char*>(workspace) + a->B * a->H * nc * cb);
         }
     }
     const hipError_t e = kda::launch_prefill(a->dtype == KDA_BF16, a->out_dtype == KDA_BF16, c,
                                              (int)a->Dk, pp, rp, stream);
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
+
+}  // namespace
+
+extern "C" {
 
 int kda_chunk_summary(const kda_fwd_args* a, float* transition, hipStream_t stream) {
     if (!a) return KDA_ERR_NULL;

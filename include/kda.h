@@ -35,7 +35,8 @@
  *  - Supported head sizes: Dk == Dv, 64 or 128.
  *  - The caller owns every buffer.  The library allocates nothing, keeps no
  *    global mutable state and is reentrant; calls on distinct streams may run
- *    concurrently.  Work is enqueued on `stream` and the call returns without
+ *    concurrently.  The one exception is kda_chunk_fwd_noalloc, whose fixed
+ *    per-device scratch buffer is shared by all its calls (see there).  Work is enqueued on `stream` and the call returns without
  *    synchronising; results are valid once the stream has completed.
  *  - Arguments are validated on the host before any HIP call; on failure the
  *    call returns a negative status and touches no memory.  A launch error
@@ -55,7 +56,7 @@
 extern "C" {
 #endif
 
-#define KDA_VERSION 3
+#define KDA_VERSION 4
 
 /* element types */
 #define KDA_F32 0  /* IEEE binary32 */
@@ -69,6 +70,7 @@ extern "C" {
 #define KDA_ERR_WORKSPACE (-4)   /* workspace missing or too small */
 #define KDA_ERR_ALIGN (-5)       /* a pointer is not 16-byte aligned */
 #define KDA_ERR_HIP (-6)         /* the HIP runtime reported a launch error */
+#define KDA_ERR_TOO_LARGE (-7)   /* needs more scratch than kda_chunk_fwd_noalloc's fixed buffer */
 
 /* flags */
 #define KDA_FLAG_NO_CLAMP 1u /* use log_alpha as given (no clamp to [ln 0.0067, 0]) */
@@ -148,6 +150,31 @@ int kda_chunk_fwd_workspace_size(const kda_fwd_args *a, size_t *bytes);
 
 /* Chunkwise-parallel forward over whole sequences (prefill).  Returns a status. */
 int kda_chunk_fwd(const kda_fwd_args *a, hipStream_t stream);
+
+/*
+ * kda_chunk_fwd without a caller workspace, for callers that cannot allocate
+ * device memory: code recorded under HIP graph capture, tight serving loops and
+ * harnesses that forbid allocation.  Same arguments, kernels and result as
+ * kda_chunk_fwd, except that a->workspace and a->workspace_bytes are ignored:
+ * the per-chunk cards (and segment summaries) go to a fixed scratch array of
+ * KDA_NOALLOC_SCRATCH_BYTES that the library's device code holds on every
+ * device it runs on, from the loading of that code until the process ends.
+ *   - A call whose kda_chunk_fwd_workspace_size() exceeds
+ *     KDA_NOALLOC_SCRATCH_BYTES returns KDA_ERR_TOO_LARGE before any HIP call
+ *     (at Dk = 128, bf16, chunk 64: up to 814 (b, h, chunk) cards, e.g.
+ *     B1 H8 T4096 fits; one card is 82 432 bytes).
+ *   - KDA_FLAG_CARDS_READY returns KDA_ERR_UNSUPPORTED.
+ *   - The first call on a device looks up the array's address on that device
+ *     (hipGetSymbolAddress) and keeps it; `stream` must belong to the calling
+ *     thread's current device (KDA_ERR_UNSUPPORTED otherwise).  No call
+ *     allocates or frees memory.
+ *   - Every call on one device shares the one array: calls that can overlap
+ *     on one device (other streams, other threads) race and give wrong
+ *     results.  Serialise them, e.g. on one stream.  Nothing in the array
+ *     needs to start at zero; it keeps the last call's cards.
+ */
+#define KDA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int kda_chunk_fwd_noalloc(const kda_fwd_args *a, hipStream_t stream);
 
 /*
  * Variable-length batch with block-granular state snapshots.  N independent

@@ -36,8 +36,8 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.kda_version() == 3
-    for code in range(-6, 1):
+    assert lib.kda_version() == 4
+    for code in range(-7, 1):
         assert lib.kda_status_str(code).decode()
     assert lib.kda_status_str(12345).decode() == "unknown status"
 
@@ -151,6 +151,40 @@ def test_fwd_validation_rejects_before_any_hip_call(lib, mutate, code):
     a = _good_fwd()
     mutate(a)
     assert lib.kda_chunk_fwd(ctypes.byref(a), None) == code
+
+
+@pytest.mark.parametrize("mutate,code", [
+    (lambda a: setattr(a, "B", -1), _abi.KDA_ERR_SHAPE),
+    (lambda a: setattr(a, "Dk", 96), _abi.KDA_ERR_UNSUPPORTED),
+    (lambda a: setattr(a, "chunk", 128), _abi.KDA_ERR_UNSUPPORTED),
+    (lambda a: setattr(a, "flags", 16), _abi.KDA_ERR_UNSUPPORTED),  # the shared scratch holds no known cards
+    (lambda a: setattr(a, "q", None), _abi.KDA_ERR_NULL),
+    (lambda a: setattr(a, "v", 0x10008), _abi.KDA_ERR_ALIGN),
+    # B1 H16 T65536: 16384 cards of 82 432 B, far beyond the fixed buffer
+    (lambda a: (setattr(a, "H", 16), setattr(a, "T", 65536)), _abi.KDA_ERR_TOO_LARGE),
+    # 815 cards of five chunks (too short for segments): one more than the buffer holds
+    (lambda a: (setattr(a, "H", 163), setattr(a, "T", 5 * 64)), _abi.KDA_ERR_TOO_LARGE),
+])
+def test_noalloc_validation_rejects_before_any_hip_call(lib, mutate, code):
+    a = _good_fwd()
+    mutate(a)
+    assert lib.kda_chunk_fwd_noalloc(ctypes.byref(a), None) == code
+
+
+def test_noalloc_limit_and_empty_calls(lib):
+    """The fixed buffer holds 814 chunk-64 cards at d = 128 (one card is 82 432 B); the
+    workspace query of the ordinary call is what is compared against it.  Empty calls
+    return before any HIP call."""
+    card = 5 * 64 * 128 * 2 + 128 * 4
+    assert _abi.KDA_NOALLOC_SCRATCH_BYTES // card == 814
+    assert _ws(lib, _good_fwd(B=1, T=4096, H=8, D=128))[1] <= _abi.KDA_NOALLOC_SCRATCH_BYTES
+    assert _ws(lib, _good_fwd(B=1, T=5 * 64, H=162, D=128))[1] == 810 * card
+    assert _ws(lib, _good_fwd(B=1, T=5 * 64, H=163, D=128))[1] > _abi.KDA_NOALLOC_SCRATCH_BYTES
+    f = _good_fwd(B=0)
+    assert lib.kda_chunk_fwd_noalloc(ctypes.byref(f), None) == 0
+    f = _good_fwd(T=0)  # no final state requested: nothing to do
+    assert lib.kda_chunk_fwd_noalloc(ctypes.byref(f), None) == 0
+    assert lib.kda_chunk_fwd_noalloc(None, None) == _abi.KDA_ERR_NULL
 
 
 def test_fp32_chunk64_d128_is_unsupported(lib):
