@@ -80,6 +80,11 @@ __device__ __forceinline__ float row_last(float x) {
     return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x1F0));
 }
 
+// value held by lane 7 of this lane's 16-lane row (swizzle bitmask mode: lane & 16 | 7)
+__device__ __forceinline__ float row_mid(float x) {
+    return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x0F0));
+}
+
 // physical index of logical K element j (0..7) of lane group g in K-step x
 __device__ __forceinline__ constexpr int cmap(int x, int g, int j) {
     return 32 * x + 4 * g + (j & 3) + ((j >> 2) << 4);
@@ -203,7 +208,12 @@ __device__ __forceinline__ constexpr int64_t frag_piece(int ct, int u, int hf) {
 // chunk; everything that depends on A is resolved at compile time.
 // MODE bit 0: raw q, k (per-token L2 normalisation); bit 1: log_alpha holds forget
 // logits.  Compile-time, so the decay loop of the plain mode carries no extra work.
-constexpr int kModeQkNorm = 1, kModeLogits = 2;
+// MODE bit 2 (taken with the clamp off, where a token's log alpha may lie below the
+// floor): the in-tile pairs take their reference point at token 7 of the tile instead of
+// the tile start, so each of their factors spans at most eight tokens of decay and stays
+// finite down to about -11 nats per token (the clamp's floor keeps a whole tile within
+// 80.1 nats, so the default mode needs no such care).
+constexpr int kModeQkNorm = 1, kModeLogits = 2, kModeWide = 4;
 
 // Where a card's tokens are: chunk n of a sequence of slen tokens starting at packed
 // row tb, head h; item is the card's index in the workspace.  Formed once per
@@ -235,6 +245,7 @@ __device__ __forceinline__ void prep_tile(const PrepParams& p, unsigned char* sm
     const int64_t H = p.H;
     const bool clamp = p.clamp != 0;
     constexpr bool logits = (MODE & kModeLogits) != 0, qk_norm = (MODE & kModeQkNorm) != 0;
+    constexpr bool wide = (MODE & kModeWide) != 0;
 
     // raw inputs of token rl: per 32-channel block kb, the 8 bf16 channels 32 kb + 8 g4 .. +7
     // (16 bytes; the four lane groups of a token cover 64 contiguous bytes of its row)
@@ -322,20 +333,29 @@ __device__ __forceinline__ void prep_tile(const PrepParams& p, unsigned char* sm
             const float l = (clamp ? __builtin_amdgcn_fmed3f(la, kLogAlphaMin, 0.f) : la) * kLog2e;
             const float P = row_scan16(l);      // log2 decay from the tile start, inclusive
             const float E = fast_exp2(P);       // <= 1
-            const float Einv = fast_exp2(-P);   // >= 1, < 2^116 under the floor
             const float Et = row_last(E);       // decay over the whole tile
             float kf = elem(rk[kb], j), qf = elem(rq[kb], j);
             if constexpr (qk_norm) {
                 kf *= ks;
                 qf *= qs;
             }
-            const float KR = kf * E, QR = qf * E, KC = kf * Einv;
+            const float KR = kf * E, QR = qf * E;
             // K-step (kb, j): lane group g4 supplies channel 32 kb + 8 g4 + j to both operands
-            accA = mma_f32_k4(KR, KC, accA);
-            accP = mma_f32_k4(QR, KC, accP);
+            if constexpr (wide) {
+                const float Pm = P - row_mid(P);  // from token 7 of the tile
+                const float Em = fast_exp2(Pm), Emi = fast_exp2(-Pm);
+                accA = mma_f32_k4(kf * Em, kf * Emi, accA);
+                accP = mma_f32_k4(qf * Em, kf * Emi, accP);
+                ke16[kb][j] = static_cast<_Float16>(kf * fast_exp2(row_last(P) - P));
+            } else {
+                const float Einv = fast_exp2(-P);  // >= 1, < 2^116 under the floor
+                const float KC = kf * Einv;
+                accA = mma_f32_k4(KR, KC, accA);
+                accP = mma_f32_k4(QR, KC, accP);
+                ke16[kb][j] = static_cast<_Float16>(kf * (Einv * Et));  // decay from after this token to the tile end
+            }
             kr16[kb][j] = static_cast<_Float16>(KR);
             qr16[kb][j] = static_cast<_Float16>(QR);
-            ke16[kb][j] = static_cast<_Float16>(kf * (Einv * Et));  // decay from after this token to the tile end
             v16[j] = static_cast<_Float16>(elem(rv[kb], j));
             s_etau[A * D + 32 * kb + 8 * g4 + j] = Et;  // the 16 lanes of a row store the same value
         }
@@ -660,8 +680,14 @@ __device__ __forceinline__ void lds_copy16(const void* g, uint32_t lds) {
 #pragma clang diagnostic pop
 __device__ __forceinline__ uint32_t lds_offset(const void* p) { return (uint32_t)(uintptr_t)p; }
 
-template <int D, class Out, int NCONS>
-__global__ __launch_bounds__((2 * NCONS + 4) * 64) __attribute__((amdgpu_waves_per_eu(1, 2)))
+// PF: one more wave that touches the cards (and gate rows) of chunk n + 2 + kPfAhead in
+// iteration n, a G-th of each card per workgroup, so that the producers' and the output
+// wave's loads of cards the card builder wrote long before (no longer in the Infinity
+// Cache) find them in the L2 their XCD shares.
+constexpr int kPfAhead = 4;
+
+template <int D, class Out, int NCONS, bool PF>
+__global__ __launch_bounds__((2 * NCONS + 4 + (PF ? 1 : 0)) * 64) __attribute__((amdgpu_waves_per_eu(1, 2)))
 void kda_rec64_kernel(RecurParams p) {
     using CD = Card<D>;
     using L = RecL<D, NCONS>;
@@ -705,6 +731,7 @@ void kda_rec64_kernel(RecurParams p) {
     const int64_t cbytes = cstride * CD::BYTES;  // from one chunk's card to the next
     const bool chain = wave < NCONS;
     const bool outw = wave >= NCONS && wave < 2 * NCONS;
+    const bool pfw = PF && wave == L::WAVES;  // the prefetch wave
     const int pw = wave - 2 * NCONS;                          // producer index (producers only)
     const int cs = chain ? wave : (outw ? wave - NCONS : 0);  // value tile of a chain / output wave
     const uint16_t* gz = static_cast<const uint16_t*>(p.gate);
@@ -831,6 +858,55 @@ void kda_rec64_kernel(RecurParams p) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) sT[(16 * ct + 4 * g4 + i) * D + col] = S[ct][i];
         }
+    } else if (pfw) {
+        // a G-th of each card, one 4-byte load per 128-byte line, and 64 / G tokens' gate
+        // rows (the head's 256 bytes of z per token, two lines); every value is folded into
+        // `sink` kPfAhead iterations later, so each load has that long to land
+        constexpr int64_t PART = (CD::BYTES + G - 1) / G;
+        constexpr int NPF = (int)((PART + 128 * 64 - 1) / (128 * 64));
+        constexpr int ZT = 64 / G;  // tokens whose gate rows this workgroup touches
+        static_assert(2 * ZT <= 64, "gate lines");
+        uint32_t ring[kPfAhead][NPF + 1];
+#pragma unroll
+        for (int s2 = 0; s2 < kPfAhead; ++s2)
+#pragma unroll
+            for (int j = 0; j <= NPF; ++j) ring[s2][j] = 0u;
+        uint32_t sink = 0u;
+        auto touch = [&](uint32_t (&r)[NPF + 1], int64_t ci) __attribute__((always_inline)) {
+#pragma unroll
+            for (int j = 0; j <= NPF; ++j) sink ^= r[j];
+            if (ci >= NL) return;
+            const unsigned char* card = cards + (c0 + ci) * cbytes;
+#pragma unroll
+            for (int j = 0; j < NPF; ++j) {
+                int64_t off = grp * PART + 128 * (int64_t)(j * 64 + lane);
+                off = off < CD::BYTES - 4 ? off : CD::BYTES - 4;
+                r[j] = *reinterpret_cast<const uint32_t*>(card + off);
+            }
+            int64_t t = (c0 + ci) * C + grp * ZT + ((lane >> 1) % ZT);
+            t = t < T ? t : T - 1;
+            const int zline = D == 128 ? (lane & 1) : 0;  // a head's gate row is D * 2 bytes
+            r[NPF] = *reinterpret_cast<const uint32_t*>(gz + zrow0 + t * zstride + 64 * zline);
+        };
+        // the producers copy chunks 0 and 1 before the first barrier and chunk n + 2 in
+        // iteration n: chunks 2 .. 1 + kPfAhead now, chunk n + 2 + kPfAhead in iteration n
+#pragma unroll
+        for (int s2 = 0; s2 < kPfAhead; ++s2) touch(ring[s2], 2 + s2);
+        lds_barrier();  // the first card is resident
+        for (int64_t n = 0; n <= NL; n += kPfAhead) {
+#pragma unroll
+            for (int s2 = 0; s2 < kPfAhead; ++s2) {
+                if (n + s2 <= NL) {
+                    touch(ring[s2], n + s2 + 2 + kPfAhead);
+                    lds_barrier();  // X(n + s2)
+                }
+            }
+        }
+#pragma unroll
+        for (int s2 = 0; s2 < kPfAhead; ++s2)
+#pragma unroll
+            for (int j = 0; j <= NPF; ++j) sink ^= ring[s2][j];
+        asm volatile("" ::"v"(sink));  // every load has landed before the wave ends
     } else if (outw) {
         // Qe and Uo of one chunk, straight from the card into registers; two sets, the next
         // chunk's in flight while this one is used
@@ -1151,6 +1227,11 @@ int segments(int D, int64_t units, int64_t nc) {
     return 1;
 }
 
+#ifndef KDA_PREFETCH_MIN_BYTES
+#define KDA_PREFETCH_MIN_BYTES (256ll << 20)
+#endif
+bool prefetch_cards(int64_t card_bytes) { return card_bytes >= KDA_PREFETCH_MIN_BYTES; }
+
 // Launches the card builder, the segment summaries (rp.nseg > 1) and, unless
 // summary_only, the state pass.
 template <int D, class Out, int NCONS>
@@ -1165,11 +1246,16 @@ static hipError_t launch_d(const PrepParams& pp, const RecurParams& rp0, hipStre
     // its offsets can give (pp.T = packed rows) and the surplus groups leave at once
     const int64_t items = pp.vco ? varlen_max_chunks(pp.vN, pp.T, C) * pp.H : units * pp.NC;
     if (items > 0 && !pp.cards_ready) {
-        const int mode = (pp.qk_norm ? kModeQkNorm : 0) | (pp.logits ? kModeLogits : 0);
+        const int mode = (pp.qk_norm ? kModeQkNorm : 0) | (pp.logits ? kModeLogits : 0) |
+                         (pp.clamp ? 0 : kModeWide);
         auto kp = mode == 0   ? kda_prep64_kernel<D, 0>
                   : mode == 1 ? kda_prep64_kernel<D, 1>
                   : mode == 2 ? kda_prep64_kernel<D, 2>
-                              : kda_prep64_kernel<D, 3>;
+                  : mode == 3 ? kda_prep64_kernel<D, 3>
+                  : mode == 4 ? kda_prep64_kernel<D, 4>
+                  : mode == 5 ? kda_prep64_kernel<D, 5>
+                  : mode == 6 ? kda_prep64_kernel<D, 6>
+                              : kda_prep64_kernel<D, 7>;
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kp),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)LP::TOTAL);
         if (e != hipSuccess) return e;
@@ -1193,13 +1279,16 @@ static hipError_t launch_d(const PrepParams& pp, const RecurParams& rp0, hipStre
         if (e != hipSuccess) return e;
     }
     if (summary_only) return hipSuccess;
-    auto kr = kda_rec64_kernel<D, Out, NCONS>;
+    // the prefetch wave pays where the cards outgrow the 256 MB Infinity Cache; with two
+    // value tiles per workgroup a ninth wave would leave too few registers per wave
+    const bool pf = NCONS == 1 && prefetch_cards(items * Card<D>::BYTES);
+    auto kr = pf ? kda_rec64_kernel<D, Out, NCONS, NCONS == 1> : kda_rec64_kernel<D, Out, NCONS, false>;
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kr),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)LR::TOTAL);
     if (e != hipSuccess) return e;
     constexpr int G = D / (16 * NCONS);
     const int64_t blocks = (units * rp.nseg * G + 7) / 8 * 8;
-    hipLaunchKernelGGL(kr, dim3((unsigned)blocks), dim3(LR::WAVES * 64), LR::TOTAL, stream, rp);
+    hipLaunchKernelGGL(kr, dim3((unsigned)blocks), dim3((LR::WAVES + (pf ? 1 : 0)) * 64), LR::TOTAL, stream, rp);
     return hipGetLastError();
 }
 

@@ -43,6 +43,17 @@
  *    reported by the runtime returns KDA_ERR_HIP.  The library never aborts,
  *    prints or throws.
  *  - Non-finite inputs are not checked for; they propagate.
+ *  - Value range of the bf16 chunk-64 path (kda_chunk_fwd with bf16 inputs and
+ *    chunk 0 or 64, kda_chunk_fwd_varlen, kda_chunk_summary): v, the chunk's
+ *    corrected values U = beta (v - S^T k) and fp16 copies of the state are
+ *    MFMA operands in fp16, so every |v|, every state entry (initial state
+ *    included) and every |U| must stay below 65504; results beyond that are
+ *    not defined (inf or NaN).  fp32 inputs and the bf16 chunk 16 / 32 path
+ *    carry fp32 ranges.
+ *  - With KDA_FLAG_NO_CLAMP, log_alpha may lie below ln 0.0067 down to about
+ *    -11 per token (retention e^-11): inside a 16-token tile, the decay over
+ *    any eight consecutive tokens must stay above e^-88 (the fp32 range of the
+ *    tile-relative factors).  With the clamp every tile stays within e^-80.1.
  */
 #ifndef KDA_H
 #define KDA_H
@@ -73,7 +84,7 @@ extern "C" {
 #define KDA_ERR_TOO_LARGE (-7)   /* needs more scratch than kda_chunk_fwd_noalloc's fixed buffer */
 
 /* flags */
-#define KDA_FLAG_NO_CLAMP 1u /* use log_alpha as given (no clamp to [ln 0.0067, 0]) */
+#define KDA_FLAG_NO_CLAMP 1u /* use log_alpha as given (no clamp to [ln 0.0067, 0]); range above */
 /* One sequential pass per (b, h) even where the segment scan would be used (see
  * kda_chunk_fwd).  The result is the same up to rounding; the flag exists for
  * comparisons. */

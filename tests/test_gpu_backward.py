@@ -8,10 +8,13 @@ computable", in reverse; the GPU side works chunk by chunk, page "Kimi K3 report
 walk-through", section "Compute paradigm").
 
 Error measure: max |gpu - oracle| / rms(oracle) over each gradient tensor.  Both
-sides read the same input bits; the GPU computes in fp32 (the oracle in fp64), so
-the bound is 1e-3 for either input dtype: about 100x the fp32 rounding of sums
-over a 64-token chunk and 128 channels, far below any error of the algebra (a
-dropped term moves a gradient by a sizeable fraction of its RMS).
+sides read the same input bits and the GPU side computes every step in fp32 (the
+oracle in fp64), so the bound is the one the forward is held to for fp32
+arithmetic, 1e-4 of the RMS, for either input dtype.  fp32 rounding of the sums
+over a 64-token chunk and 128 channels, carried through the non-expansive
+recurrence, stays well below it (the largest error measured over these cases is
+about 3e-5); a dropped or misplaced term moves a gradient by a sizeable fraction
+of its RMS.
 """
 import math
 
@@ -24,7 +27,7 @@ from kda_workloads import CONFIGS, make_inputs, small
 
 pytestmark = pytest.mark.gpu
 
-TOL = 1e-3
+TOL = 1e-4
 KEYS = ("q", "k", "v", "log_alpha", "beta", "gate")
 GRADS = ("dq", "dk", "dv", "dlog_alpha", "dbeta", "dgate", "dinitial_state")
 
@@ -82,6 +85,8 @@ CASES = [
     ("bf16 d128 T200 floor channels, dS_T", small(CONFIGS[3], H=2, T=200), False, True),
     ("bf16 d128 T1", small(CONFIGS[2], B=2, H=1, T=1), True, True),
     ("fp32 d64 T300 state in", small(CONFIGS[0], B=1, H=2, T=300, init_state=True), True, False),
+    ("fp32 d128 T230 (ragged tail) state in, dS_T",
+     small(CONFIGS[0], B=1, H=2, T=230, Dk=128, Dv=128, chunk=64), True, True),
 ]
 
 

@@ -4,9 +4,11 @@ Error measure: max |gpu - oracle| / rms(oracle) over the compared tensor.
 Limits (fixed for the method): 1e-4 for fp32 inputs, 2e-2 for bf16 inputs
 with fp32 accumulation.  Outputs are fp32 unless a test says otherwise: rounding
 the exact result itself to bf16 costs ~2.8e-2 on these outputs (peaks ~10x the
-RMS), so bf16 outputs are compared with the oracle rounded the same way.  Full-size configurations compare every output where
-the oracle finishes in seconds, otherwise every output of a sample of whole
-(b, h) sequences (the oracle runs the same sequences end to end).
+RMS), so bf16 outputs are held element by element to the budget plus the half
+unit in the last place that rounding the exact value to bf16 may cost.  Every
+full-size configuration is compared in full: the oracle runs every (b, h)
+sequence end to end, and the worst single (b, h) unit is reported beside the
+whole-tensor figure.
 """
 import math
 
@@ -81,28 +83,31 @@ def test_config1_bf16_full():
     check(x, chunk=64, tag="cfg1")
 
 
-def _sampled(wl, heads, chunk=64, tag=""):
+def _full(wl, chunk=64, tag=""):
+    """Every output and the final state of a full-size workload against the oracle run
+    over every (b, h) sequence: the whole-tensor error and the worst unit's."""
     x = make_inputs(wl)
     tol = TOL[x["q"].dtype]
-    say(f"[parity] {tag}: full size {wl.B}x{wl.T}x{wl.H}, sampled (b,h) {heads}")
+    say(f"[parity] {tag}: full size B{wl.B} T{wl.T} H{wl.H} D{wl.Dk}, every (b, h) unit")
     y, sT = run_gpu(x, chunk=chunk)
-    for (b, h) in heads:
-        sub = {k: x[k][b:b + 1, :, h:h + 1].contiguous() for k in KEYS}
-        s0 = x["initial_state"]
-        sub["initial_state"] = None if s0 is None else s0[b:b + 1, h:h + 1].contiguous()
-        yo, so = run_oracle(sub)
-        ey = rel_err(y[b:b + 1, :, h:h + 1], yo)
-        es = rel_err(sT[b:b + 1, h:h + 1], so)
-        say(f"[parity] {tag} (b={b}, h={h}): y err/rms={ey:.3e} state err/rms={es:.3e}")
-        assert ey <= tol and es <= tol
+    y = y.double().cpu().numpy()
+    sT = sT.double().cpu().numpy()
+    yo, so = run_oracle(x)
+    ey, es = rel_err(y, yo), rel_err(sT, so)
+    worst = max((rel_err(y[b, :, h], yo[b, :, h]), b, h) for b in range(wl.B) for h in range(wl.H))
+    say(f"[parity] {tag}: y err/rms={ey:.3e} state err/rms={es:.3e}; worst unit (b={worst[1]}, "
+        f"h={worst[2]}) y err/own rms={worst[0]:.3e} (tol {tol})")
+    assert np.isfinite(ey) and ey <= tol
+    assert np.isfinite(es) and es <= tol
+    assert worst[0] <= tol
 
 
-def test_config2_full_size_sampled_heads():
-    _sampled(CONFIGS[2], [(0, 0), (0, 17), (1, 5), (1, 31)], tag="cfg2")
+def test_config2_full_size_every_unit():
+    _full(CONFIGS[2], tag="cfg2")
 
 
-def test_config3_full_size_sampled_heads():
-    _sampled(CONFIGS[3], [(0, 0), (0, 11)], tag="cfg3")
+def test_config3_full_size_every_unit():
+    _full(CONFIGS[3], tag="cfg3")
 
 
 def test_config4_decode_full():
@@ -264,29 +269,96 @@ def test_clamp_flag_off_uses_raw_log_alpha():
     check(x, chunk=16, tag="clamp", clamp=True)
 
 
-def test_bf16_output_matches_rounded_oracle():
-    """bf16 outputs: the error against the oracle is at most the cost of rounding the
-    exact result to bf16 (measured on the same data) plus the bf16 tolerance."""
+def _bf16_bound(got, ref, budget=2e-2):
+    """Element by element: |got - ref| <= budget * rms(ref) + ulp_bf16(ref) / 2, where the
+    half unit in the last place of bf16 at |ref| is what rounding even the exact value
+    to bf16 may cost (two roundings of nearly equal values can differ by a whole unit
+    at the peaks, so a bf16 copy of the oracle is not a stricter reference).  Returns
+    the largest ratio of the error to that bound."""
+    got = got.detach().double().cpu().numpy()
+    ref = np.asarray(ref, dtype=np.float64)
+    rms = math.sqrt(float((ref ** 2).mean()))
+    # the binade of the larger of the two values: a result that rounds across a power of
+    # two takes the coarser spacing
+    mag = np.maximum(np.maximum(np.abs(ref), np.abs(got)), np.finfo(np.float32).tiny)
+    half_ulp = np.exp2(np.floor(np.log2(mag)) - 8)  # bf16: 8 significant bits
+    return float((np.abs(got - ref) / (budget * rms + half_ulp)).max())
+
+
+@pytest.mark.parametrize("la", [-6.0, -10.5])
+@pytest.mark.parametrize("dtype,chunk", [("bf16", 64), ("f32", 16)])
+def test_clamp_off_below_the_floor_on_every_token(la, dtype, chunk):
+    """With the clamp off, log alpha far below the floor on every token (a 16-token tile
+    then decays by up to 168 nats, beyond the fp32 range): the card builder's in-tile
+    pairs take a mid-tile reference point, so every factor stays finite down to about
+    -11 nats per token; a third of the channels keep the common recipe's decay."""
+    base = CONFIGS[2] if dtype == "bf16" else CONFIGS[0]
+    wl = base.scaled(B=1, H=2, T=200, Dk=128, Dv=128, init_state=True, dtype=dtype, chunk=chunk)
+    x = make_inputs(wl, seed=61)
+    slow = x["log_alpha"].clone()
+    x["log_alpha"] = torch.full_like(slow, la)
+    x["log_alpha"][..., ::3] = slow[..., ::3]
+    check(x, chunk=chunk, tag=f"no clamp, log alpha {la} ({dtype}, chunk {chunk})", clamp=False)
+
+
+def test_large_state_and_values_within_fp16_range():
+    """The chunk-64 path carries values, the chunk's corrected values and fp16 copies of
+    the state as fp16 MFMA operands, whose largest finite value is 65504: a state with
+    entries up to about 4e4 and values up to about 5e3 stay inside it and keep the bf16
+    tolerance (fp16 keeps 11 significant bits)."""
+    wl = CONFIGS[2].scaled(B=1, H=3, T=300)
+    x = make_inputs(wl, seed=71)
+    x["initial_state"] = x["initial_state"] * 5e5  # std 1e4
+    x["v"] = (x["v"].float() * 1000.0).to(torch.bfloat16)
+    assert float(x["initial_state"].abs().max()) < 6.0e4
+    check(x, chunk=64, tag="large state and values")
+
+
+def test_bf16_output_element_bound():
+    """bf16 outputs of the prefill and the decode step, element by element against the
+    exact oracle: within the bf16 budget plus the half unit that rounding to bf16 costs."""
     wl = CONFIGS[2].scaled(B=1, H=4, T=700)
     x = make_inputs(wl)
     d = dev(x)
     y, _ = kda().chunk_fwd(*(d[k] for k in KEYS), initial_state=d["initial_state"],
                            out_dtype=torch.bfloat16)
-    st = dev(make_inputs(CONFIGS[4].scaled(B=8, H=4)))
+    xd = make_inputs(CONFIGS[4].scaled(B=8, H=4))
+    st = dev(xd)
     s_dec = st["state"].clone()
     yd = kda().decode_step(*(st[k] for k in KEYS), s_dec, out_dtype=torch.bfloat16)
     torch.cuda.synchronize()
     assert y.dtype == torch.bfloat16 and yd.dtype == torch.bfloat16
     yo, _ = run_oracle(x)
-    yo_r = torch.from_numpy(yo).float().to(torch.bfloat16).double().numpy()
-    floor = rel_err(torch.from_numpy(yo_r), yo)
-    e = rel_err(y, yo)
-    say(f"[parity] bf16 out: err/rms {e:.3e}, rounding floor {floor:.3e}")
-    assert e <= floor + 2e-2
-    xd = make_inputs(CONFIGS[4].scaled(B=8, H=4))
+    r = _bf16_bound(y, yo)
     ydo, _ = oracle.decode(*(xd[k] for k in KEYS), xd["state"])
-    ydo_r = torch.from_numpy(ydo).float().to(torch.bfloat16).double().numpy()
-    assert rel_err(yd, ydo) <= rel_err(torch.from_numpy(ydo_r), ydo) + 2e-2
+    rd = _bf16_bound(yd, ydo)
+    say(f"[parity] bf16 out: largest error / element bound {r:.3f} (prefill), {rd:.3f} (decode)")
+    assert r <= 1.0 and rd <= 1.0
+
+
+def test_value_column_permutation():
+    """Page-derived column independence (the value channels of S evolve independently
+    given k, beta and alpha): permuting the d_v channels of v, the gate logits and the
+    initial state permutes the columns of y and of the final state the same way."""
+    wl = CONFIGS[2].scaled(B=2, H=3, T=333)
+    x = make_inputs(wl, seed=31)
+    perm = torch.randperm(wl.Dv, generator=torch.Generator().manual_seed(5))
+    xp = dict(x)
+    xp["v"] = x["v"][..., perm].contiguous()
+    xp["gate"] = x["gate"][..., perm].contiguous()
+    xp["initial_state"] = x["initial_state"][..., perm].contiguous()
+    say("[parity] value-column permutation B2 H3 T333")
+    y, sT = run_gpu(x)
+    yp, sTp = run_gpu(xp)
+    yo, so = run_oracle(x)
+    # the permuted call against the oracle's columns permuted, and against the plain call
+    assert rel_err(yp, yo[..., perm.numpy()]) <= 2e-2
+    assert rel_err(sTp, so[..., perm.numpy()]) <= 2e-2
+    e_y = rel_err(yp, y[..., perm].double().cpu().numpy())
+    e_s = rel_err(sTp, sT[..., perm].double().cpu().numpy())
+    say(f"[parity] permuted against plain call, columns permuted: y {e_y:.2e}, state {e_s:.2e}")
+    # each column is computed from its own inputs with the same instructions wherever it sits
+    assert e_y <= 1e-6 and e_s <= 1e-6
 
 
 def test_bitwise_deterministic():
