@@ -573,14 +573,24 @@ __device__ __forceinline__ void prep_tile(const PrepParams& p, unsigned char* sm
     }
 }
 
+// One card: workgroup item `item` of the card builder's grid, 16-token tile `tile` of it
+// (one wave per tile).  Returns without a barrier when the item has no card.
 template <int D, int MODE>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void kda_prep64_kernel(PrepParams p) {
-    extern __shared__ __align__(16) unsigned char smem[];
+__device__ __forceinline__ void prep64_card(const PrepParams& p, unsigned char* smem, int64_t item, int tile) {
     // a variable-length grid is sized for the most chunks the offsets can give
     CardPos cp;
-    cp.item = blockIdx.x;
-    if (p.vco) {  // variable-length batch: card (co_i + n) H + h
+    cp.item = item;
+    if (p.ring_len > 0) {  // one piece of the sequences, chunk-major, into its half of the ring
+        const int64_t units = p.B * p.H;
+        const int64_t j = cp.item / units;  // chunk within the piece
+        const int64_t unit = cp.item - j * units;
+        cp.n = p.piece * p.ring_len + j;
+        cp.item = ((p.piece & 1) * units + unit) * p.ring_len + j;
+        const int64_t b = unit / p.H;
+        cp.h = unit - b * p.H;
+        cp.tb = b * p.T;
+        cp.slen = p.T;
+    } else if (p.vco) {  // variable-length batch: card (co_i + n) H + h
         const int64_t g = cp.item / p.H;
         if (g >= p.vco[p.vN]) return;  // the whole group leaves
         const int64_t i = p.vsoc[g];
@@ -601,12 +611,19 @@ void kda_prep64_kernel(PrepParams p) {
         cp.tb = b * p.T;
         cp.slen = p.T;
     }
-    switch (__builtin_amdgcn_readfirstlane(threadIdx.x >> 6)) {
+    switch (__builtin_amdgcn_readfirstlane(tile)) {
         case 0: prep_tile<D, 0, MODE>(p, smem, cp); break;
         case 1: prep_tile<D, 1, MODE>(p, smem, cp); break;
         case 2: prep_tile<D, 2, MODE>(p, smem, cp); break;
         default: prep_tile<D, 3, MODE>(p, smem, cp); break;
     }
+}
+
+template <int D, int MODE>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void kda_prep64_kernel(PrepParams p) {
+    extern __shared__ __align__(16) unsigned char smem[];
+    prep64_card<D, MODE>(p, smem, blockIdx.x, threadIdx.x >> 6);
 }
 
 // ---------------------------------------------------------------------------
@@ -686,21 +703,20 @@ __device__ __forceinline__ uint32_t lds_offset(const void* p) { return (uint32_t
 // Cache) find them in the L2 their XCD shares.
 constexpr int kPfAhead = 4;
 
+// Workgroup `bid` of the `nblk` (a multiple of 8) state-pass workgroups of a launch;
+// waves past the roles (and the prefetch wave) only keep the barrier count.
 template <int D, class Out, int NCONS, bool PF>
-__global__ __launch_bounds__((2 * NCONS + 4 + (PF ? 1 : 0)) * 64) __attribute__((amdgpu_waves_per_eu(1, 2)))
-void kda_rec64_kernel(RecurParams p) {
+__device__ __forceinline__ void rec64_body(const RecurParams& p, unsigned char* smem, int bid, int nblk) {
     using CD = Card<D>;
     using L = RecL<D, NCONS>;
     constexpr int NCT = D / 16, KB = D / 32, NP = L::NP, KP = L::KP;
     constexpr int G = D / (16 * NCONS);  // workgroups per head
     constexpr int OST = L::OST;
     static_assert(L::WAVES == 2 * NCONS + 4, "launch bounds");
-    extern __shared__ __align__(16) unsigned char smem[];
 
     const int lane = lane_id(), wave = wave_id();
     const int m16 = lane & 15, g4 = lane >> 4;
     // XCD-aware placement: the G workgroups of one head share bid % 8
-    const int nblk = gridDim.x, bid = blockIdx.x;
     const int logical = (bid % 8) * (nblk / 8) + bid / 8;
     const int64_t useg = logical / G;  // (b, h) * nseg + segment
     const int grp = logical % G;
@@ -725,13 +741,23 @@ void kda_rec64_kernel(RecurParams p) {
         cbase = unit * NC;
         cstride = 1;
     }
-    // this workgroup's chunks: [c0, c0 + NL) of its (b, h)
-    const int64_t c0 = seg * p.seg_len, NL = p.vco ? NC : (c0 + p.seg_len < NC ? c0 + p.seg_len : NC) - c0;
-    const unsigned char* cards = static_cast<const unsigned char*>(p.ws) + cbase * CD::BYTES;
+    // this workgroup's chunks: [c0, c0 + NL) of its (b, h); card0 is chunk c0's card
+    int64_t c0, NL;
+    const unsigned char* card0;
+    if (p.ring_len > 0) {  // one piece, whose cards are that piece's half of the ring
+        c0 = p.piece * p.ring_len;
+        NL = (c0 + p.ring_len < NC ? c0 + p.ring_len : NC) - c0;
+        card0 = static_cast<const unsigned char*>(p.ws) + ((p.piece & 1) * units + unit) * p.ring_len * CD::BYTES;
+    } else {
+        c0 = seg * p.seg_len;
+        NL = p.vco ? NC : (c0 + p.seg_len < NC ? c0 + p.seg_len : NC) - c0;
+        card0 = static_cast<const unsigned char*>(p.ws) + (cbase + c0 * cstride) * CD::BYTES;
+    }
     const int64_t cbytes = cstride * CD::BYTES;  // from one chunk's card to the next
     const bool chain = wave < NCONS;
     const bool outw = wave >= NCONS && wave < 2 * NCONS;
     const bool pfw = PF && wave == L::WAVES;  // the prefetch wave
+    const bool idle = wave > L::WAVES || (!PF && wave == L::WAVES);
     const int pw = wave - 2 * NCONS;                          // producer index (producers only)
     const int cs = chain ? wave : (outw ? wave - NCONS : 0);  // value tile of a chain / output wave
     const uint16_t* gz = static_cast<const uint16_t*>(p.gate);
@@ -876,7 +902,7 @@ void kda_rec64_kernel(RecurParams p) {
 #pragma unroll
             for (int j = 0; j <= NPF; ++j) sink ^= r[j];
             if (ci >= NL) return;
-            const unsigned char* card = cards + (c0 + ci) * cbytes;
+            const unsigned char* card = card0 + ci * cbytes;
 #pragma unroll
             for (int j = 0; j < NPF; ++j) {
                 int64_t off = grp * PART + 128 * (int64_t)(j * 64 + lane);
@@ -907,13 +933,15 @@ void kda_rec64_kernel(RecurParams p) {
 #pragma unroll
             for (int j = 0; j <= NPF; ++j) sink ^= ring[s2][j];
         asm volatile("" ::"v"(sink));  // every load has landed before the wave ends
+    } else if (idle) {
+        for (int64_t n = 0; n < NL + 2; ++n) lds_barrier();  // as many barriers as every role
     } else if (outw) {
         // Qe and Uo of one chunk, straight from the card into registers; two sets, the next
         // chunk's in flight while this one is used
         const int nt = grp * NCONS + cs;
         auto load_q = [&](half8 (&qf)[4][KB], half4 (&uo)[4], int64_t c) __attribute__((always_inline)) {
             if (NL == 0) return;  // an empty sequence has no card to read (nothing is read out)
-            const unsigned char* card = cards + (c0 + (c < NL ? c : NL - 1)) * cbytes;
+            const unsigned char* card = card0 + (c < NL ? c : NL - 1) * cbytes;
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt) {
 #pragma unroll
@@ -968,7 +996,7 @@ void kda_rec64_kernel(RecurParams p) {
             auto piece = [&](int64_t ci, int k) __attribute__((always_inline)) {
                 const int j0 = PW + k * NP, j = j0 < L::NPC ? j0 : L::NPC - 1;
                 const int64_t c = c0 + ci;  // chunk of the sequence
-                const unsigned char* card = cards + c * cbytes;
+                const unsigned char* card = card0 + ci * cbytes;
                 const void* src;
                 if (j < L::NW) {
                     src = card + CD::W + j * 1024 + lane * 16;
@@ -1053,6 +1081,36 @@ void kda_rec64_kernel(RecurParams p) {
             case 2: producer(Int<2>{}); break;
             default: producer(Int<3>{}); break;
         }
+    }
+}
+
+template <int D, class Out, int NCONS, bool PF>
+__global__ __launch_bounds__((2 * NCONS + 4 + (PF ? 1 : 0)) * 64) __attribute__((amdgpu_waves_per_eu(1, 2)))
+void kda_rec64_kernel(RecurParams p) {
+    extern __shared__ __align__(16) unsigned char smem[];
+    rec64_body<D, Out, NCONS, PF>(p, smem, blockIdx.x, gridDim.x);
+}
+
+// One launch of the pipelined long-sequence pass: workgroups 0 .. nstate - 1 run the state
+// pass over piece rp.piece from its half of the card ring (one value tile each, with the
+// prefetch wave and one more wave that only keeps the barriers), while the others build
+// the cards of piece pp.piece = rp.piece + 1 into the other half, two cards per workgroup
+// (waves 0-3 and 4-7, each pair of 16-token-tile waves with its own half of the LDS).
+// Nothing in a launch waits on another workgroup: the pieces are ordered by the stream.
+template <int D, class Out>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void kda_piece64_kernel(PrepParams pp, RecurParams rp, int nstate) {
+    extern __shared__ __align__(16) unsigned char smem[];
+    if ((int)blockIdx.x < nstate) {
+        rec64_body<D, Out, 1, true>(rp, smem, blockIdx.x, nstate);
+    } else {
+        const int half = wave_id() >> 2;
+        const int64_t c0 = pp.piece * pp.ring_len;
+        const int64_t nl = (c0 + pp.ring_len < pp.NC ? c0 + pp.ring_len : pp.NC) - c0;
+        const int64_t items = pp.B * pp.H * nl;
+        int64_t item = 2 * ((int64_t)blockIdx.x - nstate) + half;
+        item = item < items ? item : items - 1;  // an odd count: the last card twice, same bytes
+        prep64_card<D, 0>(pp, smem + half * PrepL<D>::TOTAL, item, wave_id() & 3);
     }
 }
 
@@ -1232,6 +1290,66 @@ int segments(int D, int64_t units, int64_t nc) {
 #endif
 bool prefetch_cards(int64_t card_bytes) { return card_bytes >= KDA_PREFETCH_MIN_BYTES; }
 
+// Pipelined pass over few, long sequences: when the one-tile state pass leaves at least
+// half of the CUs idle, the sequence is cut into pieces of kPieceLen chunks and launch i
+// runs the state pass over piece i beside the card builder of piece i + 1 (pieces are
+// ordered by the stream alone).  The cards live in a ring of two pieces at the start of
+// the workspace, followed by the fp32 state carried from one piece to the next.
+constexpr int64_t kPieceLen = 64;
+
+bool use_pieces(int D, int64_t units, int64_t nc) {
+    return D == 128 && units * (D / 16) <= kSlots / 2 && nc >= 4 * kPieceLen;
+}
+
+template <int D, class Out>
+static hipError_t launch_pieces(const PrepParams& pp, const RecurParams& rp0, hipStream_t stream) {
+    using LP = PrepL<D>;
+    using LR = RecL<D, 1>;
+    using CD = Card<D>;
+    const int64_t units = rp0.B * rp0.H, NC = pp.NC, L = kPieceLen;
+    const int64_t npieces = (NC + L - 1) / L;
+    float* carry = reinterpret_cast<float*>(static_cast<unsigned char*>(pp.ws) + 2 * units * L * CD::BYTES);
+    PrepParams q = pp;
+    q.ring_len = L;
+    RecurParams r = rp0;
+    r.ring_len = L;
+    r.nseg = 1;
+    r.seg_len = NC;
+    const int nstate = (int)((units * (D / 16) + 7) / 8 * 8);
+    // piece 0's cards: the card builder alone, on every CU
+    auto k0 = kda_prep64_kernel<D, 0>;
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k0), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       (int)LP::TOTAL);
+    if (e != hipSuccess) return e;
+    q.piece = 0;
+    hipLaunchKernelGGL(k0, dim3((unsigned)(units * (L < NC ? L : NC))), dim3(256), LP::TOTAL, stream, q);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    auto kp = kda_piece64_kernel<D, Out>;
+    constexpr int64_t LDS2 = 2 * LP::TOTAL;
+    static_assert(LDS2 >= LR::TOTAL && LDS2 <= 160 * 1024, "two cards or one state tile per workgroup");
+    if ((e = hipFuncSetAttribute(reinterpret_cast<const void*>(kp), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                 (int)LDS2)) != hipSuccess)
+        return e;
+    auto kr = kda_rec64_kernel<D, Out, 1, true>;
+    if ((e = hipFuncSetAttribute(reinterpret_cast<const void*>(kr), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                 (int)LR::TOTAL)) != hipSuccess)
+        return e;
+    for (int64_t i = 0; i < npieces; ++i) {
+        r.piece = i;
+        r.s0 = i == 0 ? rp0.s0 : carry;
+        r.sT = i == npieces - 1 ? rp0.sT : carry;
+        if (i + 1 < npieces) {
+            q.piece = i + 1;
+            const int64_t c1 = (i + 1) * L, items = units * ((c1 + L < NC ? c1 + L : NC) - c1);
+            hipLaunchKernelGGL(kp, dim3((unsigned)(nstate + (items + 1) / 2)), dim3(512), LDS2, stream, q, r, nstate);
+        } else {
+            hipLaunchKernelGGL(kr, dim3((unsigned)nstate), dim3((LR::WAVES + 1) * 64), LR::TOTAL, stream, r);
+        }
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
 // Launches the card builder, the segment summaries (rp.nseg > 1) and, unless
 // summary_only, the state pass.
 template <int D, class Out, int NCONS>
@@ -1241,6 +1359,11 @@ static hipError_t launch_d(const PrepParams& pp, const RecurParams& rp0, hipStre
     using LR = RecL<D, NCONS>;
     using LS = SumL<D, kSumTiles>;
     const int64_t units = rp0.B * rp0.H;
+    if constexpr (NCONS == 1 && D == 128) {
+        if (!summary_only && !pp.vco && !pp.cards_ready && !pp.qk_norm && !pp.logits && pp.clamp &&
+            rp0.nseg <= 1 && use_pieces(D, units, pp.NC))
+            return launch_pieces<D, Out>(pp, rp0, stream);
+    }
     RecurParams rp = rp0;
     // one workgroup per card, two per CU; a variable-length grid covers the most chunks
     // its offsets can give (pp.T = packed rows) and the surplus groups leave at once

@@ -25,6 +25,11 @@ struct PrepParams {
     const int32_t* vsoc;
     int64_t vN;
     int cards_ready;  // the workspace already holds these inputs' cards: no card builder
+    // pipelined long sequences (chunk-64 path): ring_len > 0 builds the cards of chunks
+    // [piece ring_len, (piece + 1) ring_len) into half piece % 2 of a two-piece ring,
+    // card ((piece % 2) B H + unit) ring_len + j for chunk j of the piece
+    int64_t ring_len;
+    int64_t piece;
 };
 
 struct RecurParams {
@@ -54,6 +59,10 @@ struct RecurParams {
     // state goes to slot floor(s_i / (64 snap_chunks)) + i + k of snap [slots, H, D, D]
     float* snap;
     int64_t snap_chunks;
+    // pipelined long sequences: ring_len > 0 runs piece `piece` only (chunks
+    // [piece ring_len, ...)), from its half of the card ring (PrepParams), from s0 to sT
+    int64_t ring_len;
+    int64_t piece;
 };
 
 // bytes of one per-chunk card in the workspace (or -1 if unsupported)

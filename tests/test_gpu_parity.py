@@ -222,6 +222,28 @@ def test_segment_scan_matches_oracle_and_single_pass(B, H, T, D):
     assert rel_err(y_s, y_1.double().cpu().numpy()) <= 2e-2
 
 
+def test_pipelined_pieces_ragged_with_state():
+    """Few, long sequences that leave half of the GPU to the card builder take the
+    pipelined pass (pieces of 64 chunks, the builder of piece i + 1 beside the state pass
+    of piece i, cards in a two-piece ring, the state carried between pieces): 258 chunks
+    in five pieces, the last with two chunks and a ragged tail, two batch rows, an
+    initial and a final state; against the oracle and the single pass of every chunk's
+    card at once (the variable-length call takes the unpipelined path)."""
+    wl = CONFIGS[2].scaled(B=2, H=6, T=257 * 64 + 100)
+    x = make_inputs(wl, seed=81)
+    say(f"[parity] pipelined pieces B2 H6 T{wl.T}")
+    check(x, chunk=64, tag="pipelined pieces")
+    d = dev(x)
+    y, sT = kda().chunk_fwd(*(d[k] for k in KEYS), initial_state=d["initial_state"], output_final_state=True)
+    cu = torch.tensor([0, wl.T, 2 * wl.T], dtype=torch.int64, device="cuda:0")
+    flat = {k: d[k].reshape((2 * wl.T,) + tuple(d[k].shape[2:])) for k in KEYS}
+    yv, sv = kda().chunk_fwd_varlen(*(flat[k] for k in KEYS), cu, initial_state=d["initial_state"],
+                                    output_final_state=True)[:2]
+    torch.cuda.synchronize()
+    # the same cards and the same chain arithmetic in both: equal bit for bit
+    assert torch.equal(y.reshape(yv.shape), yv) and torch.equal(sT, sv)
+
+
 def test_decode_chain_equals_prefill_and_handoff():
     """T decode steps equal one prefill; a prefill's final state continues in decode."""
     wl = CONFIGS[2].scaled(B=2, H=4, T=24, Dk=64, Dv=64)
