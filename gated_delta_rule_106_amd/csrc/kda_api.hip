@@ -128,8 +128,9 @@ int check_bwd(const kda_bwd_args* a, int64_t* nchunks, int64_t* ws_total) {
         return KDA_ERR_SHAPE;
     if (bh > INT_MAX / 16) return KDA_ERR_SHAPE;  // two sweep workgroups per (b, h, 16 value columns)
     const int64_t nc = (a->T + 63) / 64;
-    // per chunk: a record, two states and their scratch share stay below 1 MiB
+    // per chunk: the two records and two states stay below 1 MiB
     if (!mul_ok(bh, nc, &items) || !mul_ok(items, (int64_t)1 << 20, &tmp)) return KDA_ERR_SHAPE;
+    if (items > INT_MAX) return KDA_ERR_SHAPE;  // one workgroup per (b, h, chunk)
     *nchunks = nc;
     *ws_total = kda::bwd_workspace_bytes((int)a->Dk, bh, nc);
     return KDA_OK;

@@ -23,19 +23,18 @@ struct BwdParams {
     float* dbeta;
     float* dgate;
     float* ds0;        // gradient of the initial state or null
-    float* trans;      // per chunk: W, K-bar, b, R, Gamma_C
+    float* trans;      // per chunk: W, K-bar, b, R, Gamma_C (the sweep's record)
+    float* pairs;      // per chunk: g, Li, P, Bm (the gradient kernel's record)
     float* states;     // per chunk: the state at the chunk's start
     float* dstates;    // per chunk: the gradient of the state at the chunk's end
-    float* scratch;    // per workgroup slot of the chunk kernels
     int64_t B, T, H;
     int64_t NC;        // chunks per sequence
-    int64_t slots;     // workgroups of the chunk kernels
     int clamp;
 };
 
-// Workspace bytes of one call (sections: trans, states, dstates, scratch).
+// Workspace bytes of one call (sections: trans, pairs, states, dstates).
 int64_t bwd_workspace_bytes(int D, int64_t bh, int64_t nc);
-// Splits the workspace into its sections and fills p.slots.
+// Splits the workspace into its sections.
 void bwd_layout(int D, int64_t bh, int64_t nc, void* ws, BwdParams& p);
 hipError_t launch_bwd(int dtype_bf16, int D, const BwdParams& p, hipStream_t stream);
 

@@ -11,23 +11,26 @@
 //   Li = (I + diag(beta) Bm)^-1
 //   X = V - Kt S0,  U = Li diag(beta) X,  O = Qt S0 + P U,  Y = O * sigmoid(Z)
 //   S_C = Diag(Gc) S0 + Kb^T U
-// Every pair factor is e^{g_r - g_s} with r >= s, so none exceeds 1.
 //
 // Three launches:
-//  1. kda_bwd_prep_kernel, one chunk per workgroup: W = Li diag(beta) Kt, Kb, Gc,
-//     b = Kb^T Li diag(beta) V and R = (Qt - P W)^T dO with dO = dY * sigmoid(Z).
+//  1. kda_bwd_chunk_kernel, one workgroup per chunk: g, Bm, P, Li, and the sweep's
+//     record W = Li diag(beta) Kt, Kb, Gc, b = Kb^T Li diag(beta) V and
+//     R = (Qt - P W)^T dO with dO = dY * sigmoid(Z); g, Li, P and Bm stay in a pair
+//     record for the gradient kernel.
 //  2. kda_bwd_sweep_kernel, one (direction, b, h, 16 value columns) per workgroup
 //     (columns of the state evolve independently): forwards the states at every
 //     chunk start, S_{n+1} = Diag(Gc) S_n - Kb^T (W S_n) + b; backwards the state
 //     gradients, dS_n = Diag(Gc) dS_{n+1} - W^T (Kb dS_{n+1}) + R (the transposed
 //     map).  R does not depend on the states, so the two directions run at once.
-//  3. kda_bwd_grad_kernel, one chunk per workgroup: the adjoint of the chunk's
-//     steps above from S_n and dS_{n+1}; log alpha's gradient is the reverse
-//     cumulative sum of g's gradient within the chunk.
-// All arithmetic is fp32; the chunk kernels keep their intermediates in a scratch
-// slot of the workspace (one per workgroup, reused chunk after chunk).  When every
-// chunk has a slot of its own, the gradient kernel finds the shared per-chunk steps
-// where the prep kernel left them instead of recomputing them.
+//  3. kda_bwd_grad_kernel, one workgroup per chunk: the adjoint of the chunk's steps
+//     above from S_n and dS_{n+1}; log alpha's gradient is the reverse cumulative sum
+//     of g's gradient within the chunk.
+// All arithmetic is fp32 (the fp32 MFMA).  The chunk kernels keep every intermediate
+// in registers and LDS; the pair products, and the pair terms of the gradients, are
+// products over 16-token blocks with a reference point between the two blocks, so
+// that no factor exceeds e^{8 tokens of decay} (the same 16-token tile the forward uses
+// to keep decay factors in range, page "Kimi K3 report walk-through", section
+// "Numerical stability & co-design").
 #include "kda_backward.h"
 #include "kda_device.h"
 
@@ -35,9 +38,8 @@ namespace kda {
 namespace {
 
 constexpr int C = 64;             // tokens per chunk
-constexpr int NT = 256;           // threads per workgroup
+constexpr int NT = 256;           // threads per sweep workgroup
 constexpr int TILE = 16;          // value columns per sweep workgroup
-constexpr int64_t kMaxSlots = 512;
 
 __device__ __forceinline__ float ex(float x) { return fast_exp2(x * kLog2e); }
 
@@ -48,114 +50,6 @@ struct Rec {
     static constexpr int64_t W = 0, KBAR = CD, BV = 2 * CD, R = 2 * CD + DD, GC = 2 * CD + 2 * DD;
     static constexpr int64_t SIZE = 2 * CD + 2 * DD + D;
 };
-
-// fp32 offsets inside one scratch slot: C x D row-major blocks, then C x C blocks,
-// then two C-vectors.
-template <int D>
-struct Scr {
-    static constexpr int64_t CD = (int64_t)C * D, CC = (int64_t)C * C;
-    static constexpr int64_t K = 0, Q = CD, V = 2 * CD, G = 3 * CD, DO = 4 * CD, EG = 5 * CD, KT = 6 * CD,
-                             QT = 7 * CD, KB = 8 * CD, X = 9 * CD, U = 10 * CD, O = 11 * CD, DU = 12 * CD,
-                             DW = 13 * CD, DKB = 14 * CD, DQ = 15 * CD, DKT = 16 * CD;
-    static constexpr int64_t BM = 17 * CD, PM = BM + CC, LI = BM + 2 * CC, DP = BM + 3 * CC,
-                             DLI = BM + 4 * CC, EM = BM + 5 * CC, DA = BM + 6 * CC;
-    static constexpr int64_t BETA = BM + 7 * CC, DBX = BETA + C;
-    static constexpr int64_t SIZE = DBX + C;
-};
-
-// out(m, n) for m < M, n < N of sum_{k < K} a(m, k) b(k, n) over the workgroup, on
-// the fp32 MFMA.  A and B are first copied into LDS (row pitches K + 4 and N + 4, so
-// the lane groups of an operand read fall on different banks), in the order of their
-// sources' contiguous index (TA, TB: that source is stored transposed), one element
-// per lane and step or (V4) four neighbours per lane merged into a 16-byte load.  Wave w then
-// forms the 16 x 16 output tiles w, w + 4, ..: lane (l, g) gives A[l][k] and B[k][l] for
-// k = 16 kk + 4 g + c in the c-th MFMA of a 16-wide k step and receives
-// out[4 g + i][l] in acc[i].  Starts with a barrier (LDS free) and ends without one.
-template <int D, int M, int N, int K, bool TA = false, bool TB = false, bool V4 = false, class FA, class FB,
-          class FO>
-__device__ __forceinline__ void mm(FA a, FB b, FO o, float* lds) {
-    constexpr int KP = K + 4, NP = N + 4;
-    static_assert(M % 16 == 0 && N % 16 == 0 && K % 16 == 0, "16 x 16 tiles");
-    static_assert(M * KP + K * NP <= 3 * C * D + 2 * C * C, "fits the chunk kernels' LDS");
-    float* la = lds;
-    float* lb = lds + M * KP;
-    __syncthreads();
-    if (V4) {
-        // each lane copies four neighbours along the source's contiguous index, which the
-        // compiler merges into one 16-byte load
-        constexpr int NA = TA ? M * K / 16 : M * K / 4, NB4 = TB ? K * N / 16 : K * N / 4;
-#pragma unroll 2
-        for (int i = threadIdx.x; i < NA; i += NT) {
-            if (TA) {
-                // a(m, k) is read from a k-major source: a 4 x 4 block per lane, four
-                // 16-byte loads along m, transposed in registers into four rows of LDS
-                const int k = 4 * (i / (M / 4)), m = 4 * (i - (i / (M / 4)) * (M / 4));
-                float v[4][4];
-#pragma unroll
-                for (int t = 0; t < 4; ++t)
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) v[t][j] = a(m + j, k + t);
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    *reinterpret_cast<float4*>(la + (m + j) * KP + k) = make_float4(v[0][j], v[1][j], v[2][j], v[3][j]);
-            } else {
-                const int m = i / (K / 4), k = 4 * (i - m * (K / 4));
-                *reinterpret_cast<float4*>(la + m * KP + k) = make_float4(a(m, k), a(m, k + 1), a(m, k + 2), a(m, k + 3));
-            }
-        }
-#pragma unroll 2
-        for (int i = threadIdx.x; i < NB4; i += NT) {
-            if (TB) {
-                // b(k, n) is read from an n-major source: a 4 x 4 block per lane, four
-                // 16-byte loads along k, transposed in registers into four rows of LDS
-                const int n = 4 * (i / (K / 4)), k = 4 * (i - (i / (K / 4)) * (K / 4));
-                float v[4][4];
-#pragma unroll
-                for (int t = 0; t < 4; ++t)
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) v[t][j] = b(k + j, n + t);
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    *reinterpret_cast<float4*>(lb + (k + j) * NP + n) = make_float4(v[0][j], v[1][j], v[2][j], v[3][j]);
-            } else {
-                const int k = i / (N / 4), n = 4 * (i - k * (N / 4));
-                *reinterpret_cast<float4*>(lb + k * NP + n) = make_float4(b(k, n), b(k, n + 1), b(k, n + 2), b(k, n + 3));
-            }
-        }
-    } else {
-        // one element per lane and step, consecutive lanes along the source's contiguous index
-#pragma unroll 8
-        for (int i = threadIdx.x; i < M * K; i += NT) {
-            const int m = TA ? i % M : i / K, k = TA ? i / M : i % K;
-            la[m * KP + k] = a(m, k);
-        }
-#pragma unroll 8
-        for (int i = threadIdx.x; i < K * N; i += NT) {
-            const int k = TB ? i % K : i / N, n = TB ? i / K : i % N;
-            lb[k * NP + n] = b(k, n);
-        }
-    }
-    __syncthreads();
-    const int lane = lane_id(), wave = wave_id();
-    const int l = lane & 15, g = lane >> 4;
-    constexpr int TN = N / 16, TILES = (M / 16) * TN;
-    for (int t = wave; t < TILES; t += NT / 64) {
-        const int tm = t / TN, tn = t - tm * TN;
-        floatx4 acc = zero4();
-#pragma unroll 4
-        for (int kk = 0; kk < K / 16; ++kk) {
-            const int k0 = 16 * kk + 4 * g;
-            const float4 av = *reinterpret_cast<const float4*>(la + (16 * tm + l) * KP + k0);
-            const float* bp = lb + k0 * NP + 16 * tn + l;
-            acc = mma_f32_k4(av.x, bp[0], acc);
-            acc = mma_f32_k4(av.y, bp[NP], acc);
-            acc = mma_f32_k4(av.z, bp[2 * NP], acc);
-            acc = mma_f32_k4(av.w, bp[3 * NP], acc);
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) o(16 * tm + 4 * g + i, 16 * tn + l, acc[i]);
-    }
-}
 
 struct ChunkPos {
     int64_t b, h, t0;
@@ -175,241 +69,6 @@ __device__ __forceinline__ ChunkPos chunk_pos(const BwdParams& p, int64_t item) 
 template <int D>
 __device__ __forceinline__ int64_t elem(const BwdParams& p, const ChunkPos& cp, int r, int c) {
     return ((cp.b * p.T + cp.t0 + r) * p.H + cp.h) * D + c;
-}
-
-// LDS of the chunk kernels (fp32 offsets).  The pair products and the inverse read
-// three channel-major C x D blocks and two C x C blocks; the gradient's pair terms
-// read three row-major C x D blocks, two C x C blocks and beta.
-template <int D>
-struct ChunkLds {
-    static constexpr int CP = C + 4;  // pitch of the channel-major copies (bank spread)
-    static constexpr int CC = C * C, DCP = D * CP;
-    static constexpr int A0 = 0, A1 = DCP, A2 = 2 * DCP, B0 = 3 * DCP, B1 = 3 * DCP + CC, BETA = 3 * DCP + 2 * CC;
-    static constexpr int TOTAL = BETA + C;
-};
-
-// dst[c * (C + 4) + r] = src[r * D + c] for a C x D row-major block of scratch: a 4 x 4
-// block per lane and step, four 16-byte loads along the channels, four 16-byte LDS
-// stores along the tokens.
-template <int D>
-__device__ __forceinline__ void to_lds_cm(float* dst, const float* src) {
-    constexpr int CP = C + 4;
-    for (int i = threadIdx.x; i < (C / 4) * (D / 4); i += NT) {
-        const int rb = i / (D / 4), c = 4 * (i - rb * (D / 4)), r = 4 * rb;
-        float4 v[4];
-#pragma unroll
-        for (int t = 0; t < 4; ++t) v[t] = *reinterpret_cast<const float4*>(src + (r + t) * D + c);
-        *reinterpret_cast<float4*>(dst + (c + 0) * CP + r) = make_float4(v[0].x, v[1].x, v[2].x, v[3].x);
-        *reinterpret_cast<float4*>(dst + (c + 1) * CP + r) = make_float4(v[0].y, v[1].y, v[2].y, v[3].y);
-        *reinterpret_cast<float4*>(dst + (c + 2) * CP + r) = make_float4(v[0].z, v[1].z, v[2].z, v[3].z);
-        *reinterpret_cast<float4*>(dst + (c + 3) * CP + r) = make_float4(v[0].w, v[1].w, v[2].w, v[3].w);
-    }
-}
-
-// Copies n floats (a multiple of 4 * NT) from global scratch to LDS, all loads of a
-// thread issued before its stores.
-template <int N>
-__device__ __forceinline__ void to_lds(float* dst, const float* src) {
-    constexpr int per = N / 4 / NT;
-    float4 v[per];
-#pragma unroll
-    for (int i = 0; i < per; ++i) v[i] = reinterpret_cast<const float4*>(src)[threadIdx.x + i * NT];
-#pragma unroll
-    for (int i = 0; i < per; ++i) reinterpret_cast<float4*>(dst)[threadIdx.x + i * NT] = v[i];
-}
-
-// Eight consecutive input elements as fp32 (e is a multiple of 8, so the bf16 load is
-// 16-byte aligned and the fp32 loads 32-byte aligned), and eight fp32 to scratch.
-__device__ __forceinline__ void load8(const uint16_t* p, int64_t e, float (&o)[8]) {
-    const uint4 w = *reinterpret_cast<const uint4*>(p + e);
-    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {  // little-endian: element 2 j is the low half-word
-        o[2 * j] = __uint_as_float(ws[j] << 16);
-        o[2 * j + 1] = __uint_as_float(ws[j] & 0xffff0000u);
-    }
-}
-__device__ __forceinline__ void load8(const float* p, int64_t e, float (&o)[8]) {
-    const float4 a = *reinterpret_cast<const float4*>(p + e);
-    const float4 b = *reinterpret_cast<const float4*>(p + e + 4);
-    o[0] = a.x, o[1] = a.y, o[2] = a.z, o[3] = a.w, o[4] = b.x, o[5] = b.y, o[6] = b.z, o[7] = b.w;
-}
-__device__ __forceinline__ void store8(float* d, const float (&v)[8]) {
-    *reinterpret_cast<float4*>(d) = make_float4(v[0], v[1], v[2], v[3]);
-    *reinterpret_cast<float4*>(d + 4) = make_float4(v[4], v[5], v[6], v[7]);
-}
-
-// Steps shared by the prep and gradient kernels: the chunk's inputs in fp32 (zero
-// past the sequence's end, which makes the padding tokens identity steps), g, the
-// decayed operands, Bm, P and Li.
-template <int D, class In>
-__device__ void chunk_common(const BwdParams& p, const ChunkPos& cp, float* s, float* lds) {
-    using S = Scr<D>;
-    using LL = ChunkLds<D>;
-    using raw = typename In::raw_t;
-    // eight neighbouring channels of one token per lane and step (one 16-byte load per
-    // bf16 input), two steps in flight
-    constexpr int G8 = C * D / 8 / NT;  // groups of eight per thread
-    static_assert(G8 % 2 == 0, "pairs of groups");
-#pragma unroll 1
-    for (int g0 = 0; g0 < G8; g0 += 2) {
-        float k8[2][8], q8[2][8], v8[2][8], l8[2][8], y8[2][8], z8[2][8];
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const int grp = threadIdx.x + (g0 + u) * NT;
-            const int r = grp / (D / 8), c8 = 8 * (grp - r * (D / 8));
-            if (r < cp.L) {
-                const int64_t e = elem<D>(p, cp, r, c8);
-                load8(static_cast<const raw*>(p.k), e, k8[u]);
-                load8(static_cast<const raw*>(p.q), e, q8[u]);
-                load8(static_cast<const raw*>(p.v), e, v8[u]);
-                load8(static_cast<const raw*>(p.la), e, l8[u]);
-                load8(static_cast<const raw*>(p.dy), e, y8[u]);
-                load8(static_cast<const raw*>(p.gate), e, z8[u]);
-            } else {
-#pragma unroll
-                for (int j = 0; j < 8; ++j) k8[u][j] = q8[u][j] = v8[u][j] = l8[u][j] = y8[u][j] = z8[u][j] = 0.f;
-            }
-        }
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const int grp = threadIdx.x + (g0 + u) * NT;
-            const int r = grp / (D / 8), c8 = 8 * (grp - r * (D / 8));
-            const bool live = r < cp.L;
-            float lv[8], dov[8];
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                lv[j] = live ? clamp_log_alpha(l8[u][j], p.clamp != 0) : 0.f;
-                dov[j] = live ? y8[u][j] * sigmoidf_(z8[u][j]) : 0.f;
-            }
-            const int idx = r * D + c8;
-            store8(s + S::K + idx, k8[u]);
-            store8(s + S::Q + idx, q8[u]);
-            store8(s + S::V + idx, v8[u]);
-            store8(s + S::G + idx, lv);
-            store8(s + S::DO + idx, dov);
-        }
-    }
-    if (threadIdx.x < C) {
-        const int r = threadIdx.x;
-        const float b =
-            r < cp.L ? In::load(static_cast<const raw*>(p.beta), (cp.b * p.T + cp.t0 + r) * p.H + cp.h) : 0.f;
-        s[S::BETA + r] = b;
-        lds[LL::BETA + r] = b;
-    }
-    __syncthreads();
-    // g_r = sum_{s <= r} lambda_s, per key channel (the column read whole, then summed)
-    if (threadIdx.x < D) {
-        const int c = threadIdx.x;
-        float acc = 0.f;
-#pragma unroll 1
-        for (int r0 = 0; r0 < C; r0 += 16) {
-            float col[16];
-#pragma unroll
-            for (int u = 0; u < 16; ++u) col[u] = s[S::G + (r0 + u) * D + c];
-#pragma unroll
-            for (int u = 0; u < 16; ++u) {
-                acc += col[u];
-                s[S::G + (r0 + u) * D + c] = acc;
-            }
-        }
-    }
-    __syncthreads();
-    to_lds_cm<D>(lds + LL::A0, s + S::K);
-    to_lds_cm<D>(lds + LL::A1, s + S::Q);
-    to_lds_cm<D>(lds + LL::A2, s + S::G);
-    // decayed operands, eight neighbouring channels per lane and step
-#pragma unroll 2
-    for (int grp = threadIdx.x; grp < C * D / 8; grp += NT) {
-        const int idx = 8 * grp, c8 = idx % D;
-        float g[8], gc[8], kv[8], qv[8], eg[8], kt[8], qt[8], kb[8];
-        load8(s + S::G + idx, 0, g);
-        load8(s + S::G + (C - 1) * D + c8, 0, gc);
-        load8(s + S::K + idx, 0, kv);
-        load8(s + S::Q + idx, 0, qv);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            eg[j] = ex(g[j]);
-            kt[j] = kv[j] * eg[j];
-            qt[j] = qv[j] * eg[j];
-            kb[j] = kv[j] * ex(gc[j] - g[j]);
-        }
-        store8(s + S::EG + idx, eg);
-        store8(s + S::KT + idx, kt);
-        store8(s + S::QT + idx, qt);
-        store8(s + S::KB + idx, kb);
-    }
-    __syncthreads();
-    // pair products from LDS: channel-major k (A0), q (A1) and g (A2), row pitch C + 4
-    for (int idx = threadIdx.x; idx < C * C; idx += NT) {
-        const int r = idx / C, sc = idx - r * C;
-        float bs = 0.f, ps = 0.f;
-        if (sc <= r) {
-#pragma unroll 8
-            for (int c = 0; c < D; ++c) {
-                const float e = ex(lds[LL::A2 + c * LL::CP + r] - lds[LL::A2 + c * LL::CP + sc]);
-                const float ks = lds[LL::A0 + c * LL::CP + sc] * e;
-                bs = fmaf(lds[LL::A0 + c * LL::CP + r], ks, bs);
-                ps = fmaf(lds[LL::A1 + c * LL::CP + r], ks, ps);
-            }
-        }
-        const float bm = sc < r ? bs : 0.f;
-        s[S::BM + idx] = bm;
-        s[S::PM + idx] = sc <= r ? ps : 0.f;
-        lds[LL::B0 + idx] = bm;
-    }
-    __syncthreads();
-    // Li = (I + diag(beta) Bm)^-1 by forward substitution in LDS, one column per lane
-    if (threadIdx.x < C) {
-        const int sc = threadIdx.x;
-        float* li = lds + LL::B1;
-        for (int r = 0; r < C; ++r) {
-            float acc = 0.f;
-            for (int m = 0; m < r; ++m) acc = fmaf(lds[LL::B0 + r * C + m], li[m * C + sc], acc);
-            const float v = r == sc ? 1.f : (r < sc ? 0.f : -lds[LL::BETA + r] * acc);
-            li[r * C + sc] = v;
-            s[S::LI + r * C + sc] = v;
-        }
-    }
-    __syncthreads();
-}
-
-template <int D, class In>
-__global__ __launch_bounds__(NT) void kda_bwd_prep_kernel(BwdParams p) {
-    using S = Scr<D>;
-    extern __shared__ __align__(16) float lds[];
-    using RC = Rec<D>;
-    float* s = p.scratch + (int64_t)blockIdx.x * S::SIZE;
-    const int64_t items = p.B * p.H * p.NC;
-    for (int64_t item = blockIdx.x; item < items; item += gridDim.x) {
-        const ChunkPos cp = chunk_pos(p, item);
-        chunk_common<D, In>(p, cp, s, lds);
-        float* tr = p.trans + item * RC::SIZE;
-        const float* beta = s + S::BETA;
-        // W = Li diag(beta) Kt;  U~ = Li diag(beta) V (kept in the X block)
-        mm<D, C, D, C>([&](int m, int k) { return s[S::LI + m * C + k] * beta[k]; },
-                    [&](int k, int n) { return s[S::KT + k * D + n]; },
-                    [&](int m, int n, float a) { tr[RC::W + m * D + n] = a; }, lds);
-        mm<D, C, D, C>([&](int m, int k) { return s[S::LI + m * C + k] * beta[k]; },
-                    [&](int k, int n) { return s[S::V + k * D + n]; },
-                    [&](int m, int n, float a) { s[S::X + m * D + n] = a; }, lds);
-        for (int idx = threadIdx.x; idx < C * D; idx += NT) tr[RC::KBAR + idx] = s[S::KB + idx];
-        if (threadIdx.x < D) tr[RC::GC + threadIdx.x] = s[S::EG + (C - 1) * D + threadIdx.x];
-        __syncthreads();
-        // Qe = Qt - P W (kept in the U block);  b = Kb^T U~
-        mm<D, C, D, C>([&](int m, int k) { return s[S::PM + m * C + k]; },
-                    [&](int k, int n) { return tr[RC::W + k * D + n]; },
-                    [&](int m, int n, float a) { s[S::U + m * D + n] = s[S::QT + m * D + n] - a; }, lds);
-        mm<D, D, D, C, true, false>([&](int m, int k) { return s[S::KB + k * D + m]; },
-                    [&](int k, int n) { return s[S::X + k * D + n]; },
-                    [&](int m, int n, float a) { tr[RC::BV + m * D + n] = a; }, lds);
-        __syncthreads();
-        // R = Qe^T dO
-        mm<D, D, D, C, true, false>([&](int m, int k) { return s[S::U + k * D + m]; },
-                    [&](int k, int n) { return s[S::DO + k * D + n]; },
-                    [&](int m, int n, float a) { tr[RC::R + m * D + n] = a; }, lds);
-        __syncthreads();  // the slot is reused by the next chunk
-    }
 }
 
 // LDS of the sweep kernel (fp32 offsets): the chunk's W and K-bar (row pitch D + 4),
@@ -565,218 +224,724 @@ __global__ __launch_bounds__(NT) void kda_bwd_sweep_kernel(BwdParams p) {
     }
 }
 
+// fp32 offsets of the per-chunk pair record the chunk kernel leaves for the gradient
+// kernel: g (C x D), Li, P and Bm (C x C, row-major).
+template <int D>
+struct Pr {
+    static constexpr int64_t CD = (int64_t)C * D, CC = (int64_t)C * C;
+    static constexpr int64_t G = 0, LI = CD, PM = CD + CC, BM = CD + 2 * CC, SIZE = CD + 3 * CC;
+};
+
+// Four K-steps of the fp32 MFMA: lane (g, l) gives A[l][k_j] and B[k_j][l] with
+// k_j = 16 t + 4 g + j for j = 0..3 (any K-block t).  An accumulator tile, whose lane
+// (g, l) holds rows 16 t + 4 g + i of column l, is such a B operand as it stands.
+__device__ __forceinline__ floatx4 mma4(const float4& a, const float4& b, floatx4 acc) {
+    acc = mma_f32_k4(a.x, b.x, acc);
+    acc = mma_f32_k4(a.y, b.y, acc);
+    acc = mma_f32_k4(a.z, b.z, acc);
+    return mma_f32_k4(a.w, b.w, acc);
+}
+__device__ __forceinline__ float4 f4(const floatx4& x) { return make_float4(x[0], x[1], x[2], x[3]); }
+__device__ __forceinline__ float4 ld4(const float* p) { return *reinterpret_cast<const float4*>(p); }
+__device__ __forceinline__ float4 mul4(const float4& a, const float4& b) {
+    return make_float4(a.x * b.x, a.y * b.y, a.z * b.z, a.w * b.w);
+}
+
+// Block (a, b), b <= a, of the 4 x 4 grid of 16 x 16 blocks, for task 0..9.
+__device__ __forceinline__ void lower_block(int task, int& a, int& b) {
+    a = 0;
+    while ((a + 1) * (a + 2) / 2 <= task) ++a;
+    b = task - a * (a + 1) / 2;
+}
+
+// LDS of the chunk kernel (floats; C x D blocks with row pitch D + 4, C x C with C + 4).
+template <int D>
+struct ChunkL {
+    static constexpr int DP = D + 4, CP = C + 4;
+    static constexpr int SK = 0, SQ = C * DP, SG = 2 * C * DP, SLI = 3 * C * DP, SP = SLI + C * CP,
+                         SBM = SP + C * CP, BETA = SBM + C * CP, TOTAL = BETA + C;
+    static_assert(TOTAL * 4 <= 160 * 1024, "chunk kernel LDS");
+};
+
+// Chunk kernel: one workgroup of D / 16 waves per (b, h, chunk).  From the chunk's
+// inputs: g, the pair blocks Bm (strictly lower) and P (lower), Li = (I + diag(beta) Bm)^-1,
+// then, wave w on the value (or key) columns 16 w .. 16 w + 15: W = Li diag(beta) Kt,
+// U~ = Li diag(beta) V, Qe = Qt - P W, Kb, Gamma_C, b = Kb^T U~ and R = Qe^T dO.  Writes
+// the sweep's record (W, Kb, b, R, Gamma_C) and the pair record (g, Li, P, Bm).
+// Pairs: block (a, b) is a product over the channels with a reference point rho between
+// the two tiles, k_r e^{g_r - rho} against k_s e^{rho - g_s}: the end of tile a - 1 for
+// b < a (both factors <= 1), token 7 of the tile for a diagonal block (each factor spans
+// at most eight tokens of decay).
 template <int D, class In>
-__global__ __launch_bounds__(NT) void kda_bwd_grad_kernel(BwdParams p) {
-    using S = Scr<D>;
-    using LL = ChunkLds<D>;
-    extern __shared__ __align__(16) float lds[];
+__global__ __launch_bounds__(64 * (D / 16)) void kda_bwd_chunk_kernel(BwdParams p) {
+    using L = ChunkL<D>;
+    using RC = Rec<D>;
+    using PR = Pr<D>;
     using raw = typename In::raw_t;
-    float* s = p.scratch + (int64_t)blockIdx.x * S::SIZE;
-    const int64_t items = p.B * p.H * p.NC;
-    const int64_t DD = (int64_t)D * D;
-    for (int64_t item = blockIdx.x; item < items; item += gridDim.x) {
-        const ChunkPos cp = chunk_pos(p, item);
-        if (items <= p.slots) {
-            // one chunk per slot: the prep kernel ran this chunk's shared steps in this
-            // same slot (workgroup b takes chunk b in both launches) and left them there
-            if (threadIdx.x < C) lds[LL::BETA + threadIdx.x] = s[S::BETA + threadIdx.x];
-            __syncthreads();
-        } else {
-            chunk_common<D, In>(p, cp, s, lds);
+    constexpr int NW = D / 16, NTT = 64 * NW, DP = L::DP, CP = L::CP;
+    extern __shared__ __align__(16) float lds[];
+    float* sk = lds + L::SK;
+    float* sq = lds + L::SQ;
+    float* sg = lds + L::SG;
+    float* sli = lds + L::SLI;
+    float* sp = lds + L::SP;
+    float* sbm = lds + L::SBM;
+    float* sbeta = lds + L::BETA;
+    const int64_t item = blockIdx.x;
+    const ChunkPos cp = chunk_pos(p, item);
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l = lane & 15, g = lane >> 4;
+    float* pr = p.pairs + item * PR::SIZE;
+    float* tr = p.trans + item * RC::SIZE;
+    auto in = [&](const void* ptr, int r, int c) -> float {
+        return r < cp.L ? In::load(static_cast<const raw*>(ptr), elem<D>(p, cp, r, c)) : 0.f;
+    };
+
+    // inputs; tokens past the sequence's end are identity steps (all zero, log alpha 0)
+    for (int i = tid; i < C * D; i += NTT) {
+        const int r = i / D, c = i - r * D;
+        sk[r * DP + c] = in(p.k, r, c);
+        sq[r * DP + c] = in(p.q, r, c);
+        sg[r * DP + c] = r < cp.L ? clamp_log_alpha(in(p.la, r, c), p.clamp != 0) : 0.f;
+    }
+    if (tid < C)
+        sbeta[tid] = tid < cp.L
+                         ? In::load(static_cast<const raw*>(p.beta), (cp.b * p.T + cp.t0 + tid) * p.H + cp.h)
+                         : 0.f;
+    __syncthreads();
+    if (tid < D) {  // g: inclusive cumulative sum over the chunk per key channel
+        float acc = 0.f;
+        for (int r = 0; r < C; ++r) {
+            acc += sg[r * DP + tid];
+            sg[r * DP + tid] = acc;
+            pr[PR::G + r * D + tid] = acc;
         }
-        const float* S0 = p.states + item * DD;
-        const float* dSC = p.dstates + item * DD;
-        const float* beta = s + S::BETA;
-        // X = V - Kt S0
-        mm<D, C, D, D, false, false, true>([&](int m, int k) { return s[S::KT + m * D + k]; },
-                    [&](int k, int n) { return S0[k * D + n]; },
-                    [&](int m, int n, float a) { s[S::X + m * D + n] = s[S::V + m * D + n] - a; }, lds);
-        __syncthreads();
-        // U = Li diag(beta) X
-        mm<D, C, D, C, false, false, true>([&](int m, int k) { return s[S::LI + m * C + k] * beta[k]; },
-                    [&](int k, int n) { return s[S::X + k * D + n]; },
-                    [&](int m, int n, float a) { s[S::U + m * D + n] = a; }, lds);
-        __syncthreads();
-        // O = Qt S0 + P U;  dP = lower(dO U^T);  dKb = U dS_C^T;  dU = P^T dO + Kb dS_C
-        mm<D, C, D, D, false, false, true>([&](int m, int k) { return s[S::QT + m * D + k]; },
-                    [&](int k, int n) { return S0[k * D + n]; },
-                    [&](int m, int n, float a) { s[S::O + m * D + n] = a; }, lds);
-        mm<D, C, D, C, false, false, true>([&](int m, int k) { return s[S::PM + m * C + k]; },
-                    [&](int k, int n) { return s[S::U + k * D + n]; },
-                    [&](int m, int n, float a) { s[S::O + m * D + n] += a; }, lds);
-        mm<D, C, C, D, false, true, true>([&](int m, int k) { return s[S::DO + m * D + k]; },
-                    [&](int k, int n) { return s[S::U + n * D + k]; },
-                    [&](int m, int n, float a) { s[S::DP + m * C + n] = n <= m ? a : 0.f; }, lds);
-        mm<D, C, D, D, false, true, true>([&](int m, int k) { return s[S::U + m * D + k]; },
-                    [&](int k, int n) { return dSC[n * D + k]; },
-                    [&](int m, int n, float a) { s[S::DKB + m * D + n] = a; }, lds);
-        mm<D, C, D, C, true, false, true>([&](int m, int k) { return s[S::PM + k * C + m]; },
-                    [&](int k, int n) { return s[S::DO + k * D + n]; },
-                    [&](int m, int n, float a) { s[S::DU + m * D + n] = a; }, lds);
-        mm<D, C, D, D, false, false, true>([&](int m, int k) { return s[S::KB + m * D + k]; },
-                    [&](int k, int n) { return dSC[k * D + n]; },
-                    [&](int m, int n, float a) { s[S::DU + m * D + n] += a; }, lds);
-        __syncthreads();
-        // dZ = dY * O * sigmoid'(Z);  dLi = dU (diag(beta) X)^T, strictly lower part;  dW = Li^T dU
-#pragma unroll 2
-        for (int grp = threadIdx.x; grp < cp.L * D / 8; grp += NT) {
-            const int idx = 8 * grp, r = idx / D, c8 = idx - r * D;
-            const int64_t e = elem<D>(p, cp, r, c8);
-            float z[8], y[8], o[8], dz[8];
-            load8(static_cast<const raw*>(p.gate), e, z);
-            load8(static_cast<const raw*>(p.dy), e, y);
-            load8(s + S::O + idx, 0, o);
+    }
+    // the blocks above the diagonal are zero
+    for (int i = tid; i < C * C; i += NTT) {
+        const int r = i / C, s = i - r * C;
+        if (s / 16 > r / 16) {
+            sbm[r * CP + s] = sp[r * CP + s] = 0.f;
+            pr[PR::BM + i] = pr[PR::PM + i] = 0.f;
+        }
+    }
+    __syncthreads();
+
+    // pair blocks
+    for (int task = wave; task < 10; task += NW) {
+        int a, bt;
+        lower_block(task, a, bt);
+        const int rref = bt < a ? 16 * a - 1 : 16 * a + 7;
+        const float* gr = sg + (16 * a + l) * DP;
+        const float* gs = sg + (16 * bt + l) * DP;
+        const float* gf = sg + rref * DP;
+        floatx4 accB = zero4(), accP = zero4();
+#pragma unroll 4
+        for (int t = 0; t < D / 16; ++t) {
+            const int c0 = 16 * t + 4 * g;
+            const float4 rho = ld4(gf + c0), g4r = ld4(gr + c0), g4s = ld4(gs + c0);
+            const float4 k4r = ld4(sk + (16 * a + l) * DP + c0), q4r = ld4(sq + (16 * a + l) * DP + c0);
+            const float4 k4s = ld4(sk + (16 * bt + l) * DP + c0);
+            const float4 ea = make_float4(ex(g4r.x - rho.x), ex(g4r.y - rho.y), ex(g4r.z - rho.z), ex(g4r.w - rho.w));
+            const float4 eb = make_float4(ex(rho.x - g4s.x), ex(rho.y - g4s.y), ex(rho.z - g4s.z), ex(rho.w - g4s.w));
+            const float4 ks = mul4(k4s, eb);
+            accB = mma4(mul4(k4r, ea), ks, accB);
+            accP = mma4(mul4(q4r, ea), ks, accP);
+        }
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const float sg = sigmoidf_(z[j]);
-                dz[j] = y[j] * o[j] * sg * (1.f - sg);
-            }
-            store8(p.dgate + e, dz);
+        for (int i = 0; i < 4; ++i) {
+            const int r = 16 * a + 4 * g + i, s = 16 * bt + l;
+            const float bm = s < r ? accB[i] : 0.f, pm = s <= r ? accP[i] : 0.f;
+            sbm[r * CP + s] = bm;
+            sp[r * CP + s] = pm;
+            pr[PR::BM + r * C + s] = bm;
+            pr[PR::PM + r * C + s] = pm;
         }
-        mm<D, C, C, D, false, true, true>([&](int m, int k) { return s[S::DU + m * D + k]; },
-                    [&](int k, int n) { return beta[n] * s[S::X + n * D + k]; },
-                    [&](int m, int n, float a) { s[S::DLI + m * C + n] = n < m ? a : 0.f; }, lds);
-        mm<D, C, D, C, true, false, true>([&](int m, int k) { return s[S::LI + k * C + m]; },
-                    [&](int k, int n) { return s[S::DU + k * D + n]; },
-                    [&](int m, int n, float a) { s[S::DW + m * D + n] = a; }, lds);
-        __syncthreads();
-        // dV = diag(beta) dW;  dbeta's X part;  E = Li^T dLi;  the S0 parts of dQ and dKt
-#pragma unroll 2
-        for (int grp = threadIdx.x; grp < cp.L * D / 8; grp += NT) {
-            const int idx = 8 * grp, r = idx / D, c8 = idx - r * D;
-            float w[8];
-            load8(s + S::DW + idx, 0, w);
-            const float br = beta[r];
-#pragma unroll
-            for (int j = 0; j < 8; ++j) w[j] *= br;
-            store8(p.dv + elem<D>(p, cp, r, c8), w);
-        }
-        if (threadIdx.x < C) {
-            const int r = threadIdx.x;
+    }
+    __syncthreads();
+    // Li = (I + diag(beta) Bm)^-1 by forward substitution, one column per lane of wave 0
+    if (wave == 0) {
+        const int s = lane;
+        for (int r = 0; r < C; ++r) {
             float acc = 0.f;
-            for (int j = 0; j < D; ++j) acc = fmaf(s[S::DW + r * D + j], s[S::X + r * D + j], acc);
-            s[S::DBX + r] = acc;
+            for (int m = s; m < r; ++m) acc = fmaf(sbm[r * CP + m], sli[m * CP + s], acc);
+            sli[r * CP + s] = r == s ? 1.f : (r < s ? 0.f : -sbeta[r] * acc);
         }
-        mm<D, C, C, C, true, false, true>([&](int m, int k) { return s[S::LI + k * C + m]; },
-                    [&](int k, int n) { return s[S::DLI + k * C + n]; },
-                    [&](int m, int n, float a) { s[S::EM + m * C + n] = a; }, lds);
-        mm<D, C, D, D, false, true, true>([&](int m, int k) { return s[S::DO + m * D + k]; },
-                    [&](int k, int n) { return S0[n * D + k]; },
-                    [&](int m, int n, float a) { s[S::DQ + m * D + n] = a * s[S::EG + m * D + n]; }, lds);
-        mm<D, C, D, D, false, true, true>([&](int m, int k) { return beta[m] * s[S::DW + m * D + k]; },
-                    [&](int k, int n) { return S0[n * D + k]; },
-                    [&](int m, int n, float a) { s[S::DKT + m * D + n] = -a * s[S::EG + m * D + n]; }, lds);
-        __syncthreads();
-        // dA = -(E Li^T), strictly lower part (the gradient with respect to diag(beta) Bm)
-        mm<D, C, C, C, false, true, true>([&](int m, int k) { return s[S::EM + m * C + k]; },
-                    [&](int k, int n) { return s[S::LI + n * C + k]; },
-                    [&](int m, int n, float a) { s[S::DA + m * C + n] = n < m ? -a : 0.f; }, lds);
-        __syncthreads();
-        // pair terms of dq and dk (through P and Bm), the K-bar term, dg; dbeta.  The
-        // loops read k, q, g (row-major), dP, dA and beta from LDS.
-        to_lds<C * D>(lds + LL::A0, s + S::K);
-        to_lds<C * D>(lds + LL::A1, s + S::Q);
-        to_lds<C * D>(lds + LL::A2, s + S::G);
-        to_lds<C * C>(lds + LL::B0, s + S::DP);
-        to_lds<C * C>(lds + LL::B1, s + S::DA);
-        __syncthreads();
-        const float* lk = lds + LL::A0;
-        const float* lq = lds + LL::A1;
-        const float* lg = lds + LL::A2;
-        const float* ldp = lds + LL::B0;
-        const float* lda = lds + LL::B1;
-        const float* lbeta = lds + LL::BETA;
-        for (int idx = threadIdx.x; idx < C * D; idx += NT) {
-            const int r = idx / D, c = idx - r * D;
-            const float gr = lg[idx];
-            // scratch values first: their latency is covered by the LDS loops below
-            const float dq0 = s[S::DQ + idx], dkt0 = s[S::DKT + idx], dkb0 = s[S::DKB + idx];
-            float pq = 0.f, aq = 0.f, ak = 0.f, pk = 0.f;
+    }
+    __syncthreads();
+    for (int i = tid; i < C * C; i += NTT) pr[PR::LI + i] = sli[(i / C) * CP + (i % C)];
+
+    // the products of the value (and key) columns c = 16 w + l; K-block t of a token
+    // operand holds tokens 16 t + 4 g + j
+    const int c = 16 * wave + l;
+    float4 ktb[4], vb[4], dob[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        float kt[4], vv[4], dd[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int r = 16 * t + 4 * g + j;
+            kt[j] = sk[r * DP + c] * ex(sg[r * DP + c]);
+            vv[j] = in(p.v, r, c);
+            dd[j] = in(p.dy, r, c) * sigmoidf_(in(p.gate, r, c));
+        }
+        ktb[t] = make_float4(kt[0], kt[1], kt[2], kt[3]);
+        vb[t] = make_float4(vv[0], vv[1], vv[2], vv[3]);
+        dob[t] = make_float4(dd[0], dd[1], dd[2], dd[3]);
+    }
+    floatx4 Wt[4], Ut[4], Qe[4];
+#pragma unroll
+    for (int ma = 0; ma < 4; ++ma) {
+        floatx4 aw = zero4(), au = zero4();
+#pragma unroll
+        for (int t = 0; t <= ma; ++t) {
+            const float4 a4 = mul4(ld4(sli + (16 * ma + l) * CP + 16 * t + 4 * g), ld4(sbeta + 16 * t + 4 * g));
+            aw = mma4(a4, ktb[t], aw);
+            au = mma4(a4, vb[t], au);
+        }
+        Wt[ma] = aw;
+        Ut[ma] = au;
+    }
+#pragma unroll
+    for (int ma = 0; ma < 4; ++ma) {
+        floatx4 pw = zero4();
+#pragma unroll
+        for (int t = 0; t <= ma; ++t) pw = mma4(ld4(sp + (16 * ma + l) * CP + 16 * t + 4 * g), f4(Wt[t]), pw);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = 16 * ma + 4 * g + i;
+            Qe[ma][i] = sq[r * DP + c] * ex(sg[r * DP + c]) - pw[i];
+        }
+    }
+    float kbv[4][4];
+    const float gC = sg[(C - 1) * DP + c];
+#pragma unroll
+    for (int ma = 0; ma < 4; ++ma)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = 16 * ma + 4 * g + i;
+            kbv[ma][i] = sk[r * DP + c] * ex(gC - sg[r * DP + c]);
+            tr[RC::W + r * D + c] = Wt[ma][i];
+            tr[RC::KBAR + r * D + c] = kbv[ma][i];
+        }
+    if (g == 0) tr[RC::GC + c] = ex(gC);
+    __syncthreads();  // k, q no longer read: their blocks take Kb and Qe
+#pragma unroll
+    for (int ma = 0; ma < 4; ++ma)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = 16 * ma + 4 * g + i;
+            sk[r * DP + c] = kbv[ma][i];
+            sq[r * DP + c] = Qe[ma][i];
+        }
+    __syncthreads();
+    // b = Kb^T U~ and R = Qe^T dO: rows = key channels (D / 16 blocks), columns c
+#pragma unroll 2
+    for (int mb = 0; mb < D / 16; ++mb) {
+        floatx4 ab = zero4(), ar = zero4();
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const int r0 = 16 * t + 4 * g;
+            const float4 kb4 = make_float4(sk[(r0 + 0) * DP + 16 * mb + l], sk[(r0 + 1) * DP + 16 * mb + l],
+                                           sk[(r0 + 2) * DP + 16 * mb + l], sk[(r0 + 3) * DP + 16 * mb + l]);
+            const float4 qe4 = make_float4(sq[(r0 + 0) * DP + 16 * mb + l], sq[(r0 + 1) * DP + 16 * mb + l],
+                                           sq[(r0 + 2) * DP + 16 * mb + l], sq[(r0 + 3) * DP + 16 * mb + l]);
+            ab = mma4(kb4, f4(Ut[t]), ab);
+            ar = mma4(qe4, dob[t], ar);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            tr[RC::BV + (16 * mb + 4 * g + i) * D + c] = ab[i];
+            tr[RC::R + (16 * mb + 4 * g + i) * D + c] = ar[i];
+        }
+    }
+}
+
+// LDS of the gradient kernel (floats): three C x D blocks (pitch D + 4), three C x C
+// blocks (pitch C + 4), beta, and the per-wave partial sums of dGamma_C and dbeta.
+template <int D>
+struct GradL {
+    static constexpr int NW = D / 16, DP = D + 4, CP = C + 4;
+    static constexpr int RA = 0, RB = C * DP, RCc = 2 * C * DP, RL = 3 * C * DP, RP = RL + C * CP,
+                         RQ = RP + C * CP, BETA = RQ + C * CP, DGC = BETA + C, DB1 = DGC + NW * D,
+                         TOTAL = DB1 + NW * C;
+    static_assert(TOTAL * 4 <= 160 * 1024, "gradient kernel LDS");
+};
+
+// Sum over the 16 lanes l of a lane group (lanes 16 g .. 16 g + 15).
+__device__ __forceinline__ float sum16(float v) {
+    v += __shfl_xor(v, 1);
+    v += __shfl_xor(v, 2);
+    v += __shfl_xor(v, 4);
+    v += __shfl_xor(v, 8);
+    return v;
+}
+
+// Gradient kernel: one workgroup of D / 16 waves per (b, h, chunk), from the state at the
+// chunk's start S0, the gradient of the state at its end dS_C and the pair record; the
+// adjoint of the chunk's steps (X = V - Kt S0, U = Li diag(beta) X, O = Qt S0 + P U,
+// S_C = Diag(Gamma_C) S0 + Kb^T U, Y = O sigmoid(Z)).  Every intermediate stays in
+// registers or LDS: wave w carries the value columns 16 w .. of X, U, O, dO, dU and dX
+// (left products read their other operand from LDS), and then forms the key columns
+// 16 w .. of the products over the value dimension (dO S0^T, dX S0^T, U dS_C^T) and of the
+// pair terms of dq, dk and dg.
+template <int D, class In>
+__global__ __launch_bounds__(64 * (D / 16)) void kda_bwd_grad_kernel(BwdParams p) {
+    using L = GradL<D>;
+    using PR = Pr<D>;
+    using raw = typename In::raw_t;
+    constexpr int NW = L::NW, NTT = 64 * NW, DP = L::DP, CP = L::CP;
+    constexpr int NT4 = D / 16;  // K-blocks of 16 over a D-long index
+    extern __shared__ __align__(16) float lds[];
+    float* ra = lds + L::RA;
+    float* rb = lds + L::RB;
+    float* rc = lds + L::RCc;
+    float* rl = lds + L::RL;
+    float* rp = lds + L::RP;
+    float* rq = lds + L::RQ;
+    float* sbeta = lds + L::BETA;
+    float* dgcp = lds + L::DGC;
+    float* db1p = lds + L::DB1;
+    const int64_t item = blockIdx.x;
+    const ChunkPos cp = chunk_pos(p, item);
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l = lane & 15, g = lane >> 4;
+    const int64_t DD = (int64_t)D * D;
+    const float* pr = p.pairs + item * PR::SIZE;
+    const float* gg = pr + PR::G;
+    const float* S0 = p.states + item * DD;
+    const float* dSC = p.dstates + item * DD;
+    auto in = [&](const void* ptr, int r, int c) -> float {
+        return r < cp.L ? In::load(static_cast<const raw*>(ptr), elem<D>(p, cp, r, c)) : 0.f;
+    };
+
+    // Li, P, beta; Kt and Qt
+    for (int i = tid; i < C * C; i += NTT) {
+        const int r = i / C, s = i - r * C;
+        rl[r * CP + s] = pr[PR::LI + i];
+        rp[r * CP + s] = pr[PR::PM + i];
+    }
+    if (tid < C)
+        sbeta[tid] = tid < cp.L
+                         ? In::load(static_cast<const raw*>(p.beta), (cp.b * p.T + cp.t0 + tid) * p.H + cp.h)
+                         : 0.f;
+    for (int i = tid; i < C * D; i += NTT) {
+        const int r = i / D, c = i - r * D;
+        const float e = ex(gg[i]);
+        ra[r * DP + c] = in(p.k, r, c) * e;
+        rb[r * DP + c] = in(p.q, r, c) * e;
+    }
+    __syncthreads();
+
+    const int c = 16 * wave + l;  // this wave's value column (and, later, key channel)
+    // S0 and dS_C columns as B operands: K-block t holds key channels 16 t + 4 g + j
+    float4 s0b[NT4], dsb[NT4];
+#pragma unroll
+    for (int t = 0; t < NT4; ++t) {
+        const int k0 = 16 * t + 4 * g;
+        s0b[t] = make_float4(S0[(k0 + 0) * D + c], S0[(k0 + 1) * D + c], S0[(k0 + 2) * D + c], S0[(k0 + 3) * D + c]);
+        dsb[t] = make_float4(dSC[(k0 + 0) * D + c], dSC[(k0 + 1) * D + c], dSC[(k0 + 2) * D + c],
+                             dSC[(k0 + 3) * D + c]);
+    }
+    // dGamma_C over this wave's value columns: sum of dS_C S0 along the row
+#pragma unroll
+    for (int t = 0; t < NT4; ++t) {
+        const float4 pv = mul4(s0b[t], dsb[t]);
+        const float v0 = sum16(pv.x), v1 = sum16(pv.y), v2 = sum16(pv.z), v3 = sum16(pv.w);
+        if (l == 0) {
+            const int k0 = 16 * t + 4 * g;
+            dgcp[wave * D + k0 + 0] = v0;
+            dgcp[wave * D + k0 + 1] = v1;
+            dgcp[wave * D + k0 + 2] = v2;
+            dgcp[wave * D + k0 + 3] = v3;
+        }
+    }
+    // X = V - Kt S0, O = Qt S0
+    floatx4 X[4], O[4];
+#pragma unroll
+    for (int ma = 0; ma < 4; ++ma) {
+        floatx4 ax = zero4(), ao = zero4();
+#pragma unroll
+        for (int t = 0; t < NT4; ++t) {
+            ax = mma4(ld4(ra + (16 * ma + l) * DP + 16 * t + 4 * g), s0b[t], ax);
+            ao = mma4(ld4(rb + (16 * ma + l) * DP + 16 * t + 4 * g), s0b[t], ao);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) X[ma][i] = in(p.v, 16 * ma + 4 * g + i, c) - ax[i];
+        O[ma] = ao;
+    }
+    // U = Li diag(beta) X;  O += P U
+    floatx4 U[4];
+#pragma unroll
+    for (int ma = 0; ma < 4; ++ma) {
+        floatx4 au = zero4();
+#pragma unroll
+        for (int t = 0; t <= ma; ++t)
+            au = mma4(mul4(ld4(rl + (16 * ma + l) * CP + 16 * t + 4 * g), ld4(sbeta + 16 * t + 4 * g)), f4(X[t]), au);
+        U[ma] = au;
+    }
+#pragma unroll
+    for (int ma = 0; ma < 4; ++ma)
+#pragma unroll
+        for (int t = 0; t <= ma; ++t) O[ma] = mma4(ld4(rp + (16 * ma + l) * CP + 16 * t + 4 * g), f4(U[t]), O[ma]);
+    // dO = dY sigmoid(Z);  dZ = dY O sigmoid'(Z)
+    floatx4 dO[4];
+#pragma unroll
+    for (int ma = 0; ma < 4; ++ma)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = 16 * ma + 4 * g + i;
+            const float dy = in(p.dy, r, c), sz = sigmoidf_(in(p.gate, r, c));
+            dO[ma][i] = dy * sz;
+            if (r < cp.L) p.dgate[elem<D>(p, cp, r, c)] = dy * O[ma][i] * sz * (1.f - sz);
+        }
+    __syncthreads();  // Kt, Qt no longer read: U and dO take their blocks, Kb the third
+#pragma unroll
+    for (int ma = 0; ma < 4; ++ma)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = 16 * ma + 4 * g + i;
+            ra[r * DP + c] = U[ma][i];
+            rb[r * DP + c] = dO[ma][i];
+        }
+    for (int i = tid; i < C * D; i += NTT) {
+        const int r = i / D, cc = i - r * D;
+        rc[r * DP + cc] = in(p.k, r, cc) * ex(gg[(C - 1) * D + cc] - gg[i]);
+    }
+    __syncthreads();
+    // dU = P^T dO + Kb dS_C
+    floatx4 dU[4];
+#pragma unroll
+    for (int ma = 0; ma < 4; ++ma) {
+        floatx4 acc = zero4();
+#pragma unroll
+        for (int t = ma; t < 4; ++t) {
+            const int r0 = 16 * t + 4 * g;
+            const float4 a4 = make_float4(rp[(r0 + 0) * CP + 16 * ma + l], rp[(r0 + 1) * CP + 16 * ma + l],
+                                          rp[(r0 + 2) * CP + 16 * ma + l], rp[(r0 + 3) * CP + 16 * ma + l]);
+            acc = mma4(a4, f4(dO[t]), acc);
+        }
+#pragma unroll
+        for (int t = 0; t < NT4; ++t) acc = mma4(ld4(rc + (16 * ma + l) * DP + 16 * t + 4 * g), dsb[t], acc);
+        dU[ma] = acc;
+    }
+    // dW = Li^T dU;  dX = diag(beta) dW = dV;  dbeta (first part) = rowsum(dW X)
+    floatx4 dX[4];
+#pragma unroll
+    for (int ma = 0; ma < 4; ++ma) {
+        floatx4 acc = zero4();
+#pragma unroll
+        for (int t = ma; t < 4; ++t) {
+            const int r0 = 16 * t + 4 * g;
+            const float4 a4 = make_float4(rl[(r0 + 0) * CP + 16 * ma + l], rl[(r0 + 1) * CP + 16 * ma + l],
+                                          rl[(r0 + 2) * CP + 16 * ma + l], rl[(r0 + 3) * CP + 16 * ma + l]);
+            acc = mma4(a4, f4(dU[t]), acc);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = 16 * ma + 4 * g + i;
+            dX[ma][i] = sbeta[r] * acc[i];
+            const float db = sum16(acc[i] * X[ma][i]);
+            if (l == 0) db1p[wave * C + r] = db;
+            if (r < cp.L) p.dv[elem<D>(p, cp, r, c)] = dX[ma][i];
+        }
+    }
+    __syncthreads();  // Kb no longer read: dX takes its block
+#pragma unroll
+    for (int ma = 0; ma < 4; ++ma)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) rc[(16 * ma + 4 * g + i) * DP + c] = dX[ma][i];
+    __syncthreads();
+    // dQt = dO S0^T, dKt = -dX S0^T, dKb = U dS_C^T: key channel c = 16 w + l as column
+    floatx4 dQt[4], dKt[4], dKb[4];
+#pragma unroll
+    for (int ma = 0; ma < 4; ++ma) dQt[ma] = dKt[ma] = dKb[ma] = zero4();
+#pragma unroll 2
+    for (int t = 0; t < NT4; ++t) {
+        const int v0 = 16 * t + 4 * g;
+        const float4 bs = ld4(S0 + (int64_t)c * D + v0), bd = ld4(dSC + (int64_t)c * D + v0);
+#pragma unroll
+        for (int ma = 0; ma < 4; ++ma) {
+            const int ro = (16 * ma + l) * DP + v0;
+            dQt[ma] = mma4(ld4(rb + ro), bs, dQt[ma]);
+            dKt[ma] = mma4(ld4(rc + ro), bs, dKt[ma]);
+            dKb[ma] = mma4(ld4(ra + ro), bd, dKb[ma]);
+        }
+    }
+    // dP = lower(dO U^T), into the P block (P is no longer read)
+    for (int task = wave; task < 10; task += NW) {
+        int a, bt;
+        lower_block(task, a, bt);
+        floatx4 acc = zero4();
 #pragma unroll 4
-            for (int j = 0; j <= r; ++j) {
-                const float ke = lk[j * D + c] * ex(gr - lg[j * D + c]);
-                pq = fmaf(ldp[r * C + j], ke, pq);
-                aq = fmaf(lda[r * C + j], ke, aq);
-            }
+        for (int t = 0; t < NT4; ++t)
+            acc = mma4(ld4(rb + (16 * a + l) * DP + 16 * t + 4 * g), ld4(ra + (16 * bt + l) * DP + 16 * t + 4 * g), acc);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = 16 * a + 4 * g + i, s = 16 * bt + l;
+            rp[r * CP + s] = s <= r ? acc[i] : 0.f;
+        }
+    }
+    __syncthreads();  // U, dO, dX no longer read
+    // dLinv = dU (diag(beta) X)^T, strictly lower part (only it reaches the free entries of A)
+#pragma unroll
+    for (int ma = 0; ma < 4; ++ma)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = 16 * ma + 4 * g + i;
+            ra[r * DP + c] = dU[ma][i];
+            rb[r * DP + c] = sbeta[r] * X[ma][i];
+        }
+    __syncthreads();
+    for (int task = wave; task < 10; task += NW) {
+        int a, bt;
+        lower_block(task, a, bt);
+        floatx4 acc = zero4();
 #pragma unroll 4
-            for (int j = r; j < C; ++j) {
-                const float e = ex(lg[j * D + c] - gr);
-                ak = fmaf(lbeta[j] * lda[j * C + r], lk[j * D + c] * e, ak);
-                pk = fmaf(ldp[j * C + r], lq[j * D + c] * e, pk);
+        for (int t = 0; t < NT4; ++t)
+            acc = mma4(ld4(ra + (16 * a + l) * DP + 16 * t + 4 * g), ld4(rb + (16 * bt + l) * DP + 16 * t + 4 * g), acc);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = 16 * a + 4 * g + i, s = 16 * bt + l;
+            rq[r * CP + s] = s < r ? acc[i] : 0.f;
+        }
+    }
+    for (int i = tid; i < C * C; i += NTT) {
+        const int r = i / C, s = i - r * C;
+        if (s / 16 > r / 16) rq[r * CP + s] = 0.f;
+        rc[r * CP + s] = pr[PR::BM + i];  // Bm, over the dX block (pitch C + 4)
+    }
+    __syncthreads();
+    // Z = dLinv Li^T (strictly lower part is all that dA reads), over the dU block
+    float* rz = ra;  // pitch C + 4
+    for (int task = wave; task < 10; task += NW) {
+        int a, bt;
+        lower_block(task, a, bt);
+        floatx4 acc = zero4();
+        for (int t = 0; t <= bt; ++t)
+            acc = mma4(ld4(rq + (16 * a + l) * CP + 16 * t + 4 * g), ld4(rl + (16 * bt + l) * CP + 16 * t + 4 * g), acc);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = 16 * a + 4 * g + i, s = 16 * bt + l;
+            rz[r * CP + s] = s < r ? acc[i] : 0.f;
+        }
+    }
+    for (int i = tid; i < C * C; i += NTT) {
+        const int r = i / C, s = i - r * C;
+        if (s / 16 > r / 16) rz[r * CP + s] = 0.f;
+    }
+    __syncthreads();
+    // dA = strict_lower(-Li^T Z), over the (beta X) block (pitch C + 4)
+    float* rda = rb;
+    for (int task = wave; task < 10; task += NW) {
+        int mr, sb;
+        lower_block(task, mr, sb);
+        floatx4 acc = zero4();
+        for (int t = mr; t < 4; ++t) {
+            const int a0 = 16 * t + 4 * g;
+            const float4 a4 = make_float4(rl[(a0 + 0) * CP + 16 * mr + l], rl[(a0 + 1) * CP + 16 * mr + l],
+                                          rl[(a0 + 2) * CP + 16 * mr + l], rl[(a0 + 3) * CP + 16 * mr + l]);
+            const float4 b4 = make_float4(rz[(a0 + 0) * CP + 16 * sb + l], rz[(a0 + 1) * CP + 16 * sb + l],
+                                          rz[(a0 + 2) * CP + 16 * sb + l], rz[(a0 + 3) * CP + 16 * sb + l]);
+            acc = mma4(a4, b4, acc);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = 16 * mr + 4 * g + i, s = 16 * sb + l;
+            rda[r * CP + s] = s < r ? -acc[i] : 0.f;
+        }
+    }
+    for (int i = tid; i < C * C; i += NTT) {
+        const int r = i / C, s = i - r * C;
+        if (s / 16 > r / 16) rda[r * CP + s] = 0.f;
+    }
+    __syncthreads();
+    // dbeta = rowsum(dW X) + rowsum(dA Bm)
+    if (tid < C) {
+        const int r = tid;
+        float acc = 0.f;
+        for (int w = 0; w < NW; ++w) acc += db1p[w * C + r];
+        for (int s = 0; s < r; ++s) acc = fmaf(rda[r * CP + s], rc[r * CP + s], acc);
+        if (r < cp.L) p.dbeta[(cp.b * p.T + cp.t0 + r) * p.H + cp.h] = acc;
+    }
+    // pair terms over F = diag(beta) dA (strictly lower) and dP (lower), key channel c:
+    //   query side QP_r = sum_s dP_rs k_s e^{g_r - g_s},  QB_r = sum_s F_rs k_s e^{g_r - g_s}
+    //   key side   KP_s = sum_r dP_rs q_r e^{g_r - g_s},  KB_s = sum_r F_rs k_r e^{g_r - g_s}
+    // with the reference points of the chunk kernel's pair blocks
+    auto gat = [&](int r) { return gg[r * D + c]; };
+    auto kin = [&](int r) { return in(p.k, r, c); };
+    auto qin = [&](int r) { return in(p.q, r, c); };
+    const float gC = gat(C - 1);
+    float dg[4][4];
+    float dgc = 0.f;
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+        // query side, row tile a: the earlier tiles against the end of tile a - 1, then the tile itself
+        floatx4 QP = zero4(), QB = zero4();
+        if (a > 0) {
+            const float rho = gat(16 * a - 1);
+            const float br = sbeta[16 * a + l];
+            for (int t = 0; t < a; ++t) {
+                const int s0 = 16 * t + 4 * g;
+                const float4 k4 = make_float4(kin(s0) * ex(rho - gat(s0)), kin(s0 + 1) * ex(rho - gat(s0 + 1)),
+                                              kin(s0 + 2) * ex(rho - gat(s0 + 2)), kin(s0 + 3) * ex(rho - gat(s0 + 3)));
+                QP = mma4(ld4(rp + (16 * a + l) * CP + s0), k4, QP);
+                const float4 f = ld4(rda + (16 * a + l) * CP + s0);
+                QB = mma4(make_float4(br * f.x, br * f.y, br * f.z, br * f.w), k4, QB);
             }
-            const float dqf = dq0 + pq;
-            const float dktf = dkt0 + lbeta[r] * aq;
-            const float dkif = ak + pk;
-            const float dkbf = dkb0 * ex(lg[(C - 1) * D + c] - gr);
-            const float kv = lk[idx], qv = lq[idx];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float e = ex(gat(16 * a + 4 * g + i) - rho);
+                QP[i] *= e;
+                QB[i] *= e;
+            }
+        }
+        {
+            const float rho = gat(16 * a + 7);
+            const int s0 = 16 * a + 4 * g;
+            const float4 k4 = make_float4(kin(s0) * ex(rho - gat(s0)), kin(s0 + 1) * ex(rho - gat(s0 + 1)),
+                                          kin(s0 + 2) * ex(rho - gat(s0 + 2)), kin(s0 + 3) * ex(rho - gat(s0 + 3)));
+            const float br = sbeta[16 * a + l];
+            const floatx4 dp = mma4(ld4(rp + (16 * a + l) * CP + s0), k4, zero4());
+            const float4 f = ld4(rda + (16 * a + l) * CP + s0);
+            const floatx4 db = mma4(make_float4(br * f.x, br * f.y, br * f.z, br * f.w), k4, zero4());
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float e = ex(gat(16 * a + 4 * g + i) - rho);
+                QP[i] += dp[i] * e;
+                QB[i] += db[i] * e;
+            }
+        }
+        // key side, column tile a: the later tiles against the end of tile a, then the tile itself
+        floatx4 KP = zero4(), KB = zero4();
+        if (a < 3) {
+            const float rho = gat(16 * a + 15);
+            for (int t = a + 1; t < 4; ++t) {
+                const int r0 = 16 * t + 4 * g;
+                float qv[4], kv[4], ap[4], af[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const float e = ex(gat(r0 + j) - rho);
+                    qv[j] = qin(r0 + j) * e;
+                    kv[j] = kin(r0 + j) * e;
+                    ap[j] = rp[(r0 + j) * CP + 16 * a + l];
+                    af[j] = sbeta[r0 + j] * rda[(r0 + j) * CP + 16 * a + l];
+                }
+                KP = mma4(make_float4(ap[0], ap[1], ap[2], ap[3]), make_float4(qv[0], qv[1], qv[2], qv[3]), KP);
+                KB = mma4(make_float4(af[0], af[1], af[2], af[3]), make_float4(kv[0], kv[1], kv[2], kv[3]), KB);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float e = ex(rho - gat(16 * a + 4 * g + i));
+                KP[i] *= e;
+                KB[i] *= e;
+            }
+        }
+        {
+            const float rho = gat(16 * a + 7);
+            const int r0 = 16 * a + 4 * g;
+            float qv[4], kv[4], ap[4], af[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float e = ex(gat(r0 + j) - rho);
+                qv[j] = qin(r0 + j) * e;
+                kv[j] = kin(r0 + j) * e;
+                ap[j] = rp[(r0 + j) * CP + 16 * a + l];
+                af[j] = sbeta[r0 + j] * rda[(r0 + j) * CP + 16 * a + l];
+            }
+            const floatx4 dp =
+                mma4(make_float4(ap[0], ap[1], ap[2], ap[3]), make_float4(qv[0], qv[1], qv[2], qv[3]), zero4());
+            const floatx4 db =
+                mma4(make_float4(af[0], af[1], af[2], af[3]), make_float4(kv[0], kv[1], kv[2], kv[3]), zero4());
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float e = ex(rho - gat(16 * a + 4 * g + i));
+                KP[i] += dp[i] * e;
+                KB[i] += db[i] * e;
+            }
+        }
+        // back to q, k and g for the rows of tile a
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = 16 * a + 4 * g + i;
+            const float gr = gat(r), E = ex(gr), eb = ex(gC - gr), kv = kin(r), qv = qin(r);
+            const float dqt = dQt[a][i] * E, dkt = -dKt[a][i] * E, dkb = dKb[a][i] * eb;
+            const float dq = QP[i] + dqt;
+            const float dk = QB[i] + KP[i] + KB[i] + dkt + dkb;
+            dg[a][i] = qv * dq + kv * (QB[i] + dkt - KP[i] - KB[i] - dkb);
+            dgc += kv * dkb;
             if (r < cp.L) {
                 const int64_t e = elem<D>(p, cp, r, c);
-                p.dq[e] = dqf;
-                p.dk[e] = dktf + dkif + dkbf;
-            }
-            s[S::DQ + idx] = qv * dqf + kv * (dktf - dkif - dkbf);  // gradient of g
-            s[S::DKT + idx] = kv * dkbf;                             // its g_C share
-        }
-        if (threadIdx.x < C) {
-            const int r = threadIdx.x;
-            float acc = s[S::DBX + r];
-            for (int j = 0; j < r; ++j) acc = fmaf(s[S::DA + r * C + j], s[S::BM + r * C + j], acc);
-            if (r < cp.L) p.dbeta[(cp.b * p.T + cp.t0 + r) * p.H + cp.h] = acc;
-        }
-        __syncthreads();
-        // dlambda_r = sum_{r' >= r} dg_r', with g_C's extra terms from Kb and Diag(Gc) S0
-        if (threadIdx.x < D) {
-            const int c = threadIdx.x;
-            float dgc = 0.f;
-            for (int j = 0; j < D; ++j) dgc = fmaf(dSC[c * D + j], S0[c * D + j], dgc);
-            float acc = dgc * s[S::EG + (C - 1) * D + c];
-            for (int r = 0; r < C; ++r) acc += s[S::DKT + r * D + c];
-#pragma unroll 1
-            for (int r0 = C - 16; r0 >= 0; r0 -= 16) {
-                // 16 rows of g's gradient and of the raw log alpha, read before their stores
-                float col[16], raw_la[16];
-#pragma unroll
-                for (int u = 0; u < 16; ++u) {
-                    col[u] = s[S::DQ + (r0 + u) * D + c];
-                    raw_la[u] = r0 + u < cp.L ? In::load(static_cast<const raw*>(p.la), elem<D>(p, cp, r0 + u, c)) : 0.f;
-                }
-#pragma unroll
-                for (int u = 15; u >= 0; --u) {
-                    const int r = r0 + u;
-                    acc += col[u];
-                    if (r < cp.L) {
-                        const float l = raw_la[u];
-                        const bool live = p.clamp == 0 || (l >= kLogAlphaMin && l <= 0.f);
-                        p.dla[elem<D>(p, cp, r, c)] = live ? acc : 0.f;
-                    }
-                }
+                p.dq[e] = dq;
+                p.dk[e] = dk;
             }
         }
-        __syncthreads();  // the slot is reused by the next chunk
+    }
+    // log alpha's gradient: the reverse cumulative sum of g's, plus that of g_C
+    dgc += __shfl_xor(dgc, 16);
+    dgc += __shfl_xor(dgc, 32);
+    {
+        float dG = 0.f;
+        for (int w = 0; w < NW; ++w) dG += dgcp[w * D + c];
+        dgc += dG * ex(gC);
+    }
+    // rows 16 ma + 4 g + i: suffix sums within the lane, then over the lane groups and blocks
+    float tot[4];
+#pragma unroll
+    for (int ma = 0; ma < 4; ++ma) {
+        float acc = 0.f;
+#pragma unroll
+        for (int i = 3; i >= 0; --i) {
+            acc += dg[ma][i];
+            dg[ma][i] = acc;
+        }
+        tot[ma] = acc;
+    }
+    float later = dgc;  // the sum over every row after the current block, plus dg_C
+#pragma unroll
+    for (int ma = 3; ma >= 0; --ma) {
+        const float t0 = __shfl(tot[ma], l), t1 = __shfl(tot[ma], 16 + l), t2 = __shfl(tot[ma], 32 + l),
+                    t3 = __shfl(tot[ma], 48 + l);
+        const float after_g = g == 0 ? t1 + t2 + t3 : g == 1 ? t2 + t3 : g == 2 ? t3 : 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = 16 * ma + 4 * g + i;
+            if (r < cp.L) {
+                const int64_t e = elem<D>(p, cp, r, c);
+                float d = dg[ma][i] + after_g + later;
+                if (p.clamp) {
+                    const float raw_la = In::load(static_cast<const raw*>(p.la), e);
+                    if (!(raw_la >= kLogAlphaMin && raw_la <= 0.f)) d = 0.f;
+                }
+                p.dla[e] = d;
+            }
+        }
+        later += t0 + t1 + t2 + t3;
     }
 }
 
 int64_t align256(int64_t x) { return (x + 255) / 256 * 256; }
 
+// Workspace sections: the sweep's record per chunk, the pair record per chunk, the state
+// at every chunk start and the state gradient at every chunk end (each 256-byte aligned).
 template <int D>
-int64_t section_bytes(int64_t bh, int64_t nc, int64_t* trans, int64_t* states, int64_t* slots) {
+int64_t section_bytes(int64_t bh, int64_t nc, int64_t* trans, int64_t* pairs, int64_t* states) {
     const int64_t items = bh * nc;
     *trans = align256(items * Rec<D>::SIZE * 4);
+    *pairs = align256(items * Pr<D>::SIZE * 4);
     *states = align256(items * (int64_t)D * D * 4);
-    *slots = items < kMaxSlots ? items : kMaxSlots;
-    return *trans + 2 * *states + align256(*slots * Scr<D>::SIZE * 4);
+    return *trans + *pairs + 2 * *states;
 }
 
 template <int D, class In>
 hipError_t launch_d(const BwdParams& p, hipStream_t stream) {
     const int64_t items = p.B * p.H * p.NC;
-    constexpr int clds = ChunkLds<D>::TOTAL * 4;
+    constexpr int NTC = 64 * (D / 16);
     if (items > 0) {
-        auto kp = kda_bwd_prep_kernel<D, In>;
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kp),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, clds);
+        auto kc = kda_bwd_chunk_kernel<D, In>;
+        constexpr int lds = ChunkL<D>::TOTAL * 4;
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kc),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, lds);
         if (e != hipSuccess) return e;
-        hipLaunchKernelGGL(kp, dim3((unsigned)p.slots), dim3(NT), clds, stream, p);
+        hipLaunchKernelGGL(kc, dim3((unsigned)items), dim3(NTC), lds, stream, p);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
@@ -794,10 +959,11 @@ hipError_t launch_d(const BwdParams& p, hipStream_t stream) {
     }
     if (items > 0) {
         auto kg = kda_bwd_grad_kernel<D, In>;
+        constexpr int lds = GradL<D>::TOTAL * 4;
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kg),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, clds);
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, lds);
         if (e != hipSuccess) return e;
-        hipLaunchKernelGGL(kg, dim3((unsigned)p.slots), dim3(NT), clds, stream, p);
+        hipLaunchKernelGGL(kg, dim3((unsigned)items), dim3(NTC), lds, stream, p);
     }
     return hipGetLastError();
 }
@@ -805,22 +971,21 @@ hipError_t launch_d(const BwdParams& p, hipStream_t stream) {
 }  // namespace
 
 int64_t bwd_workspace_bytes(int D, int64_t bh, int64_t nc) {
-    int64_t t, s, k;
-    return D == 64 ? section_bytes<64>(bh, nc, &t, &s, &k) : section_bytes<128>(bh, nc, &t, &s, &k);
+    int64_t t, r, s;
+    return D == 64 ? section_bytes<64>(bh, nc, &t, &r, &s) : section_bytes<128>(bh, nc, &t, &r, &s);
 }
 
 void bwd_layout(int D, int64_t bh, int64_t nc, void* ws, BwdParams& p) {
-    int64_t t, s, k;
+    int64_t t, r, s;
     if (D == 64)
-        section_bytes<64>(bh, nc, &t, &s, &k);
+        section_bytes<64>(bh, nc, &t, &r, &s);
     else
-        section_bytes<128>(bh, nc, &t, &s, &k);
+        section_bytes<128>(bh, nc, &t, &r, &s);
     unsigned char* w = static_cast<unsigned char*>(ws);
     p.trans = reinterpret_cast<float*>(w);
-    p.states = reinterpret_cast<float*>(w + t);
-    p.dstates = reinterpret_cast<float*>(w + t + s);
-    p.scratch = reinterpret_cast<float*>(w + t + 2 * s);
-    p.slots = k;
+    p.pairs = reinterpret_cast<float*>(w + t);
+    p.states = reinterpret_cast<float*>(w + t + r);
+    p.dstates = reinterpret_cast<float*>(w + t + r + s);
 }
 
 hipError_t launch_bwd(int dtype_bf16, int D, const BwdParams& p, hipStream_t stream) {

@@ -312,9 +312,12 @@ int kda_combine_states(const kda_combine_args *a, hipStream_t stream);
  *   d_initial_state: fp32 [B, H, Dk, Dv] or NULL (not returned).
  *   flags: KDA_FLAG_NO_CLAMP only.
  *   workspace: at least kda_chunk_bwd_workspace_size bytes, 256-byte aligned.
- *     It holds a per-chunk record (two chunk x Dk blocks, two Dk x Dv blocks),
- *     the state at every chunk start and its gradient at every chunk end, and
- *     one scratch slot per workgroup of the chunk kernels (at most 512).
+ *     Per (b, h, 64-token chunk) it holds, in fp32 and each section rounded up
+ *     to 256 bytes: a record for the state sweeps (2*64*Dk + 2*Dk*Dv + Dk
+ *     floats), a record for the gradient kernel (64*Dk + 3*64*64 floats), the
+ *     state at the chunk's start and its gradient at the chunk's end (Dk*Dv
+ *     floats each): 400.5 KiB per chunk at Dk = Dv = 128, e.g. 200 MiB for
+ *     B1 H8 T4096.
  * No output may overlap an input or another output.
  */
 typedef struct kda_bwd_args {

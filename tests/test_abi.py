@@ -366,9 +366,9 @@ def _good_bwd(B=1, T=100, H=2, D=128):
 
 
 def test_bwd_workspace_size(lib):
-    """Per (b, h, chunk of 64): a record (2 x 64 x D + 2 x D x D + D floats), the state at
-    the chunk start and the gradient at its end (D x D floats each), and one scratch slot
-    per chunk-kernel workgroup (at most 512), every section rounded up to 256 bytes."""
+    """Per (b, h, chunk of 64): the sweep's record (2 x 64 x D + 2 x D x D + D floats), the
+    pair record (64 x D + 3 x 64 x 64 floats), the state at the chunk start and the
+    gradient at its end (D x D floats each), every section rounded up to 256 bytes."""
     r256 = lambda x: (x + 255) // 256 * 256
     for B, T, H, D in ((1, 100, 2, 128), (2, 64, 3, 64), (1, 4096, 8, 128), (1, 1, 1, 64)):
         a = _good_bwd(B, T, H, D)
@@ -376,8 +376,8 @@ def test_bwd_workspace_size(lib):
         assert lib.kda_chunk_bwd_workspace_size(ctypes.byref(a), ctypes.byref(n)) == _abi.KDA_OK
         items = B * H * ((T + 63) // 64)
         rec = 2 * 64 * D + 2 * D * D + D
-        slot = 17 * 64 * D + 7 * 64 * 64 + 2 * 64
-        want = r256(items * rec * 4) + 2 * r256(items * D * D * 4) + r256(min(items, 512) * slot * 4)
+        pairs = 64 * D + 3 * 64 * 64
+        want = r256(items * rec * 4) + r256(items * pairs * 4) + 2 * r256(items * D * D * 4)
         assert n.value == want
     a = _good_bwd(T=0)
     assert lib.kda_chunk_bwd_workspace_size(ctypes.byref(a), ctypes.byref(n)) == _abi.KDA_OK and n.value == 0
