@@ -247,6 +247,40 @@ __device__ __forceinline__ float4 mul4(const float4& a, const float4& b) {
     return make_float4(a.x * b.x, a.y * b.y, a.z * b.z, a.w * b.w);
 }
 
+// Eight consecutive input elements (channels c8 .. c8 + 7, c8 a multiple of 8) of token row
+// r of the chunk as fp32: one 16-byte load for bf16, two for fp32; zero past the end.
+template <int D, class In>
+__device__ __forceinline__ void in8(const BwdParams& p, const ChunkPos& cp, const void* ptr, int r, int c8,
+                                    float (&o)[8]) {
+    if (r >= cp.L) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) o[j] = 0.f;
+        return;
+    }
+    const int64_t e = elem<D>(p, cp, r, c8);
+    if constexpr (sizeof(typename In::raw_t) == 2) {
+        const uint4 w = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(ptr) + e);
+        const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {  // little-endian: element 2 j is the low half-word
+            o[2 * j] = __uint_as_float(ws[j] << 16);
+            o[2 * j + 1] = __uint_as_float(ws[j] & 0xffff0000u);
+        }
+    } else {
+        const float4 a = *reinterpret_cast<const float4*>(static_cast<const float*>(ptr) + e);
+        const float4 b = *reinterpret_cast<const float4*>(static_cast<const float*>(ptr) + e + 4);
+        o[0] = a.x, o[1] = a.y, o[2] = a.z, o[3] = a.w, o[4] = b.x, o[5] = b.y, o[6] = b.z, o[7] = b.w;
+    }
+}
+__device__ __forceinline__ void st8(float* d, const float (&v)[8]) {
+    *reinterpret_cast<float4*>(d) = make_float4(v[0], v[1], v[2], v[3]);
+    *reinterpret_cast<float4*>(d + 4) = make_float4(v[4], v[5], v[6], v[7]);
+}
+__device__ __forceinline__ void ld8(const float* s, float (&v)[8]) {
+    const float4 a = *reinterpret_cast<const float4*>(s), b = *reinterpret_cast<const float4*>(s + 4);
+    v[0] = a.x, v[1] = a.y, v[2] = a.z, v[3] = a.w, v[4] = b.x, v[5] = b.y, v[6] = b.z, v[7] = b.w;
+}
+
 // Block (a, b), b <= a, of the 4 x 4 grid of 16 x 16 blocks, for task 0..9.
 __device__ __forceinline__ void lower_block(int task, int& a, int& b) {
     a = 0;
@@ -297,11 +331,27 @@ __global__ __launch_bounds__(64 * (D / 16)) void kda_bwd_chunk_kernel(BwdParams 
     };
 
     // inputs; tokens past the sequence's end are identity steps (all zero, log alpha 0)
-    for (int i = tid; i < C * D; i += NTT) {
-        const int r = i / D, c = i - r * D;
-        sk[r * DP + c] = in(p.k, r, c);
-        sq[r * DP + c] = in(p.q, r, c);
-        sg[r * DP + c] = r < cp.L ? clamp_log_alpha(in(p.la, r, c), p.clamp != 0) : 0.f;
+    // eight neighbouring channels per lane and step, every load of a thread issued first
+    constexpr int G8 = C * D / 8 / NTT;
+    static_assert(G8 * 8 * NTT == C * D, "groups of eight");
+    {
+        float k8[G8][8], q8[G8][8], l8[G8][8];
+#pragma unroll
+        for (int u = 0; u < G8; ++u) {
+            const int grp = tid + u * NTT, r = grp / (D / 8), c8 = 8 * (grp - r * (D / 8));
+            in8<D, In>(p, cp, p.k, r, c8, k8[u]);
+            in8<D, In>(p, cp, p.q, r, c8, q8[u]);
+            in8<D, In>(p, cp, p.la, r, c8, l8[u]);
+        }
+#pragma unroll
+        for (int u = 0; u < G8; ++u) {
+            const int grp = tid + u * NTT, r = grp / (D / 8), c8 = 8 * (grp - r * (D / 8));
+#pragma unroll
+            for (int j = 0; j < 8; ++j) l8[u][j] = r < cp.L ? clamp_log_alpha(l8[u][j], p.clamp != 0) : 0.f;
+            st8(sk + r * DP + c8, k8[u]);
+            st8(sq + r * DP + c8, q8[u]);
+            st8(sg + r * DP + c8, l8[u]);
+        }
     }
     if (tid < C)
         sbeta[tid] = tid < cp.L
@@ -358,14 +408,27 @@ __global__ __launch_bounds__(64 * (D / 16)) void kda_bwd_chunk_kernel(BwdParams 
         }
     }
     __syncthreads();
-    // Li = (I + diag(beta) Bm)^-1 by forward substitution, one column per lane of wave 0
+    // Li = (I + diag(beta) Bm)^-1 by forward substitution, one column per lane of wave 0,
+    // the column in registers (fully unrolled; rows of Bm read as float4 broadcasts)
     if (wave == 0) {
         const int s = lane;
+        float x[C];
+#pragma unroll
         for (int r = 0; r < C; ++r) {
             float acc = 0.f;
-            for (int m = s; m < r; ++m) acc = fmaf(sbm[r * CP + m], sli[m * CP + s], acc);
-            sli[r * CP + s] = r == s ? 1.f : (r < s ? 0.f : -sbeta[r] * acc);
+#pragma unroll
+            for (int m4 = 0; m4 < r; m4 += 4) {
+                const float4 b4 = ld4(sbm + r * CP + m4);
+                acc = fmaf(b4.x, x[m4], acc);
+                if (m4 + 1 < r) acc = fmaf(b4.y, x[m4 + 1], acc);
+                if (m4 + 2 < r) acc = fmaf(b4.z, x[m4 + 2], acc);
+                if (m4 + 3 < r) acc = fmaf(b4.w, x[m4 + 3], acc);
+            }
+            // rows above the lane's column stay zero: every x[m] they sum is zero
+            x[r] = r == s ? 1.f : -sbeta[r] * acc;
         }
+#pragma unroll
+        for (int r = 0; r < C; ++r) sli[r * CP + s] = x[r];
     }
     __syncthreads();
     for (int i = tid; i < C * C; i += NTT) pr[PR::LI + i] = sli[(i / C) * CP + (i % C)];
@@ -513,6 +576,17 @@ __global__ __launch_bounds__(64 * (D / 16)) void kda_bwd_grad_kernel(BwdParams p
         return r < cp.L ? In::load(static_cast<const raw*>(ptr), elem<D>(p, cp, r, c)) : 0.f;
     };
 
+    const int c = 16 * wave + l;  // this wave's value column (and, later, key channel)
+    // (issued first: their latency overlaps the staging below)
+    // S0 and dS_C columns as B operands: K-block t holds key channels 16 t + 4 g + j
+    float4 s0b[NT4], dsb[NT4];
+#pragma unroll
+    for (int t = 0; t < NT4; ++t) {
+        const int k0 = 16 * t + 4 * g;
+        s0b[t] = make_float4(S0[(k0 + 0) * D + c], S0[(k0 + 1) * D + c], S0[(k0 + 2) * D + c], S0[(k0 + 3) * D + c]);
+        dsb[t] = make_float4(dSC[(k0 + 0) * D + c], dSC[(k0 + 1) * D + c], dSC[(k0 + 2) * D + c],
+                             dSC[(k0 + 3) * D + c]);
+    }
     // Li, P, beta; Kt and Qt
     for (int i = tid; i < C * C; i += NTT) {
         const int r = i / C, s = i - r * C;
@@ -523,24 +597,32 @@ __global__ __launch_bounds__(64 * (D / 16)) void kda_bwd_grad_kernel(BwdParams p
         sbeta[tid] = tid < cp.L
                          ? In::load(static_cast<const raw*>(p.beta), (cp.b * p.T + cp.t0 + tid) * p.H + cp.h)
                          : 0.f;
-    for (int i = tid; i < C * D; i += NTT) {
-        const int r = i / D, c = i - r * D;
-        const float e = ex(gg[i]);
-        ra[r * DP + c] = in(p.k, r, c) * e;
-        rb[r * DP + c] = in(p.q, r, c) * e;
+    constexpr int G8 = C * D / 8 / NTT;
+    static_assert(G8 * 8 * NTT == C * D, "groups of eight");
+    {
+        float k8[G8][8], q8[G8][8], g8[G8][8];
+#pragma unroll
+        for (int u = 0; u < G8; ++u) {
+            const int grp = tid + u * NTT, r = grp / (D / 8), c8 = 8 * (grp - r * (D / 8));
+            in8<D, In>(p, cp, p.k, r, c8, k8[u]);
+            in8<D, In>(p, cp, p.q, r, c8, q8[u]);
+            ld8(gg + r * D + c8, g8[u]);
+        }
+#pragma unroll
+        for (int u = 0; u < G8; ++u) {
+            const int grp = tid + u * NTT, r = grp / (D / 8), c8 = 8 * (grp - r * (D / 8));
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const float e = ex(g8[u][j]);
+                k8[u][j] *= e;
+                q8[u][j] *= e;
+            }
+            st8(ra + r * DP + c8, k8[u]);
+            st8(rb + r * DP + c8, q8[u]);
+        }
     }
     __syncthreads();
 
-    const int c = 16 * wave + l;  // this wave's value column (and, later, key channel)
-    // S0 and dS_C columns as B operands: K-block t holds key channels 16 t + 4 g + j
-    float4 s0b[NT4], dsb[NT4];
-#pragma unroll
-    for (int t = 0; t < NT4; ++t) {
-        const int k0 = 16 * t + 4 * g;
-        s0b[t] = make_float4(S0[(k0 + 0) * D + c], S0[(k0 + 1) * D + c], S0[(k0 + 2) * D + c], S0[(k0 + 3) * D + c]);
-        dsb[t] = make_float4(dSC[(k0 + 0) * D + c], dSC[(k0 + 1) * D + c], dSC[(k0 + 2) * D + c],
-                             dSC[(k0 + 3) * D + c]);
-    }
     // dGamma_C over this wave's value columns: sum of dS_C S0 along the row
 #pragma unroll
     for (int t = 0; t < NT4; ++t) {
@@ -602,9 +684,22 @@ __global__ __launch_bounds__(64 * (D / 16)) void kda_bwd_grad_kernel(BwdParams p
             ra[r * DP + c] = U[ma][i];
             rb[r * DP + c] = dO[ma][i];
         }
-    for (int i = tid; i < C * D; i += NTT) {
-        const int r = i / D, cc = i - r * D;
-        rc[r * DP + cc] = in(p.k, r, cc) * ex(gg[(C - 1) * D + cc] - gg[i]);
+    {
+        float k8[G8][8], g8[G8][8], c8v[G8][8];
+#pragma unroll
+        for (int u = 0; u < G8; ++u) {
+            const int grp = tid + u * NTT, r = grp / (D / 8), c8 = 8 * (grp - r * (D / 8));
+            in8<D, In>(p, cp, p.k, r, c8, k8[u]);
+            ld8(gg + r * D + c8, g8[u]);
+            ld8(gg + (C - 1) * D + c8, c8v[u]);
+        }
+#pragma unroll
+        for (int u = 0; u < G8; ++u) {
+            const int grp = tid + u * NTT, r = grp / (D / 8), c8 = 8 * (grp - r * (D / 8));
+#pragma unroll
+            for (int j = 0; j < 8; ++j) k8[u][j] *= ex(c8v[u][j] - g8[u][j]);
+            st8(rc + r * DP + c8, k8[u]);
+        }
     }
     __syncthreads();
     // dU = P^T dO + Kb dS_C
@@ -707,7 +802,6 @@ __global__ __launch_bounds__(64 * (D / 16)) void kda_bwd_grad_kernel(BwdParams p
     for (int i = tid; i < C * C; i += NTT) {
         const int r = i / C, s = i - r * C;
         if (s / 16 > r / 16) rq[r * CP + s] = 0.f;
-        rc[r * CP + s] = pr[PR::BM + i];  // Bm, over the dX block (pitch C + 4)
     }
     __syncthreads();
     // Z = dLinv Li^T (strictly lower part is all that dA reads), over the dU block
@@ -754,21 +848,45 @@ __global__ __launch_bounds__(64 * (D / 16)) void kda_bwd_grad_kernel(BwdParams p
         if (s / 16 > r / 16) rda[r * CP + s] = 0.f;
     }
     __syncthreads();
+    // k, q and g of the chunk for the pair terms, over the blocks no longer read: g over
+    // Z's, k over dX's, q over Li's (rows 0 .. 31) and dLinv's (rows 32 .. 63); pitch D
+    float* sgg = ra;
+    float* skk = rc;
+    {
+        float k8[G8][8], q8[G8][8], g8[G8][8];
+#pragma unroll
+        for (int u = 0; u < G8; ++u) {
+            const int grp = tid + u * NTT, r = grp / (D / 8), c8 = 8 * (grp - r * (D / 8));
+            in8<D, In>(p, cp, p.k, r, c8, k8[u]);
+            in8<D, In>(p, cp, p.q, r, c8, q8[u]);
+            ld8(gg + r * D + c8, g8[u]);
+        }
+#pragma unroll
+        for (int u = 0; u < G8; ++u) {
+            const int grp = tid + u * NTT, r = grp / (D / 8), c8 = 8 * (grp - r * (D / 8));
+            const int i = r * D + c8;
+            st8(sgg + i, g8[u]);
+            st8(skk + i, k8[u]);
+            st8(r < C / 2 ? rl + i : rq + (i - (C / 2) * D), q8[u]);
+        }
+    }
     // dbeta = rowsum(dW X) + rowsum(dA Bm)
     if (tid < C) {
         const int r = tid;
         float acc = 0.f;
         for (int w = 0; w < NW; ++w) acc += db1p[w * C + r];
-        for (int s = 0; s < r; ++s) acc = fmaf(rda[r * CP + s], rc[r * CP + s], acc);
+        const float* bm = pr + PR::BM + r * C;
+        for (int s = 0; s < r; ++s) acc = fmaf(rda[r * CP + s], bm[s], acc);
         if (r < cp.L) p.dbeta[(cp.b * p.T + cp.t0 + r) * p.H + cp.h] = acc;
     }
+    __syncthreads();
     // pair terms over F = diag(beta) dA (strictly lower) and dP (lower), key channel c:
     //   query side QP_r = sum_s dP_rs k_s e^{g_r - g_s},  QB_r = sum_s F_rs k_s e^{g_r - g_s}
     //   key side   KP_s = sum_r dP_rs q_r e^{g_r - g_s},  KB_s = sum_r F_rs k_r e^{g_r - g_s}
     // with the reference points of the chunk kernel's pair blocks
-    auto gat = [&](int r) { return gg[r * D + c]; };
-    auto kin = [&](int r) { return in(p.k, r, c); };
-    auto qin = [&](int r) { return in(p.q, r, c); };
+    auto gat = [&](int r) { return sgg[r * D + c]; };
+    auto kin = [&](int r) { return skk[r * D + c]; };
+    auto qin = [&](int r) { return r < C / 2 ? rl[r * D + c] : rq[(r - C / 2) * D + c]; };
     const float gC = gat(C - 1);
     float dg[4][4];
     float dgc = 0.f;
