@@ -97,7 +97,7 @@ __device__ __forceinline__ floatx4 mma16x4(const float (&a)[4], const float (&b)
 // forms rows 16 w .. 16 w + 15 of Y, then row blocks w, w + 4, .. of the new state.
 // The record of the next chunk is read into registers while the current one is used.
 template <int D>
-__global__ __launch_bounds__(NT) void kda_bwd_sweep_kernel(BwdParams p) {
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void kda_bwd_sweep_kernel(BwdParams p) {
     using RC = Rec<D>;
     using L = SweepLds<D>;
     constexpr int DP = L::DP, TP = L::TP;
@@ -181,7 +181,8 @@ __global__ __launch_bounds__(NT) void kda_bwd_sweep_kernel(BwdParams p) {
             const float* A1 = lds + (dir == 0 ? L::W : L::KBAR);
             const float* A2 = lds + (dir == 0 ? L::KBAR : L::W);
             {
-                floatx4 acc = zero4();
+                // two accumulator chains (even and odd K-blocks), summed at the end
+                floatx4 acc0 = zero4(), acc1 = zero4();
 #pragma unroll
                 for (int kk = 0; kk < D / 16; ++kk) {
                     const int k0 = 16 * kk + 4 * g;
@@ -189,28 +190,41 @@ __global__ __launch_bounds__(NT) void kda_bwd_sweep_kernel(BwdParams p) {
                     const float a[4] = {av.x, av.y, av.z, av.w};
                     const float b[4] = {St[(k0 + 0) * TP + m], St[(k0 + 1) * TP + m], St[(k0 + 2) * TP + m],
                                         St[(k0 + 3) * TP + m]};
-                    acc = mma16x4(a, b, acc);
+                    if (kk & 1)
+                        acc1 = mma16x4(a, b, acc1);
+                    else
+                        acc0 = mma16x4(a, b, acc0);
                 }
 #pragma unroll
-                for (int r = 0; r < 4; ++r) Y[(16 * wave + 4 * g + r) * TP + m] = acc[r];
+                for (int r = 0; r < 4; ++r) Y[(16 * wave + 4 * g + r) * TP + m] = acc0[r] + acc1[r];
             }
             __syncthreads();
-            // state <- Diag(Gc) state - A2^T Y + offset, row blocks wave, wave + 4, ..
-            for (int rb = wave; rb < D / 16; rb += NT / 64) {
-                floatx4 acc = zero4();
+            // state <- Diag(Gc) state - A2^T Y + offset, row blocks wave, wave + 4, .. (their
+            // accumulator chains interleaved)
+            constexpr int RBW = D / 16 / (NT / 64);  // row blocks per wave
+            floatx4 acc[RBW];
 #pragma unroll
-                for (int kk = 0; kk < C / 16; ++kk) {
-                    const int k0 = 16 * kk + 4 * g;
+            for (int j = 0; j < RBW; ++j) acc[j] = zero4();
+#pragma unroll
+            for (int kk = 0; kk < C / 16; ++kk) {
+                const int k0 = 16 * kk + 4 * g;
+                const float b[4] = {Y[(k0 + 0) * TP + m], Y[(k0 + 1) * TP + m], Y[(k0 + 2) * TP + m],
+                                    Y[(k0 + 3) * TP + m]};
+#pragma unroll
+                for (int j = 0; j < RBW; ++j) {
+                    const int rb = wave + j * (NT / 64);
                     const float a[4] = {A2[(k0 + 0) * DP + 16 * rb + m], A2[(k0 + 1) * DP + 16 * rb + m],
                                         A2[(k0 + 2) * DP + 16 * rb + m], A2[(k0 + 3) * DP + 16 * rb + m]};
-                    const float b[4] = {Y[(k0 + 0) * TP + m], Y[(k0 + 1) * TP + m], Y[(k0 + 2) * TP + m],
-                                        Y[(k0 + 3) * TP + m]};
-                    acc = mma16x4(a, b, acc);
+                    acc[j] = mma16x4(a, b, acc[j]);
                 }
+            }
+#pragma unroll
+            for (int j = 0; j < RBW; ++j) {
+                const int rb = wave + j * (NT / 64);
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int row = 16 * rb + 4 * g + r;
-                    St[row * TP + m] = lds[L::GC + row] * St[row * TP + m] - acc[r] + lds[L::OFF + row * TP + m];
+                    St[row * TP + m] = lds[L::GC + row] * St[row * TP + m] - acc[j][r] + lds[L::OFF + row * TP + m];
                 }
             }
         }
