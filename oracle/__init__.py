@@ -68,6 +68,9 @@ def _open(path):
     lib.kda_oracle_bwd.argtypes = [i64, i64, i64, i64, i64, ci, vp, vp, vp, vp, vp, vp, dp, dp, dp,
                                    dp, dp, dp, dp, dp, dp, dp, ci, ci]
     lib.kda_oracle_bwd.restype = ci
+    lib.kda_oracle_bwd_ex.argtypes = [i64, i64, i64, i64, i64, ci, vp, vp, vp, vp, vp, vp, dp, dp, dp,
+                                      dp, dp, dp, dp, dp, dp, dp, ci, ci, ci, ci]
+    lib.kda_oracle_bwd_ex.restype = ci
     lib.kda_oracle_default_threads.argtypes = []
     lib.kda_oracle_default_threads.restype = ci
     return lib
@@ -277,14 +280,16 @@ def combine(M, b, initial_state=None):
 
 
 def bwd(q, k, v, log_alpha, beta, gate, dy, initial_state=None, d_final_state=None, clamp=True,
-        threads=0, _lib_handle=None):
+        threads=0, qk_norm=False, gate_logits=False, _lib_handle=None):
     """Gradients of L = sum(dy * y) + sum(d_final_state * S_T) for the forward above
     (reverse mode through the token steps; page "3T models are no longer magic",
     section "Gate 1: KDA makes it computable", taken backwards).
 
     Returns a dict of float64 arrays: dq, dk, dlog_alpha [B, T, H, Dk]; dv, dgate
     [B, T, H, Dv]; dbeta [B, T, H]; dinitial_state [B, H, Dk, Dv].  Keeps every
-    state of a sequence: small cases only.
+    state of a sequence: small cases only.  ``qk_norm`` / ``gate_logits``: the inputs
+    are raw (as in ``fwd``) and dq, dk, dlog_alpha are the gradients with respect to
+    the raw q, k and forget logits.
     """
     qa, dt = _raw(q)
     ka, _ = _raw(k)
@@ -303,11 +308,11 @@ def bwd(q, k, v, log_alpha, beta, gate, dy, initial_state=None, d_final_state=No
                dlog_alpha=np.zeros((B, T, H, Dk)), dbeta=np.zeros((B, T, H)),
                dgate=np.zeros((B, T, H, Dv)), dinitial_state=np.zeros((B, H, Dk, Dv)))
     lib = _lib_handle if _lib_handle is not None else _load()
-    rc = lib.kda_oracle_bwd(B, T, H, Dk, Dv, dt, _ptr(qa), _ptr(ka), _ptr(va), _ptr(la), _ptr(ba),
-                            _ptr(ga), _ptr(s0), _ptr(dya), _ptr(dST), _ptr(out["dq"]), _ptr(out["dk"]),
-                            _ptr(out["dv"]), _ptr(out["dlog_alpha"]), _ptr(out["dbeta"]),
-                            _ptr(out["dgate"]), _ptr(out["dinitial_state"]), 1 if clamp else 0,
-                            int(threads))
+    rc = lib.kda_oracle_bwd_ex(B, T, H, Dk, Dv, dt, _ptr(qa), _ptr(ka), _ptr(va), _ptr(la), _ptr(ba),
+                               _ptr(ga), _ptr(s0), _ptr(dya), _ptr(dST), _ptr(out["dq"]), _ptr(out["dk"]),
+                               _ptr(out["dv"]), _ptr(out["dlog_alpha"]), _ptr(out["dbeta"]),
+                               _ptr(out["dgate"]), _ptr(out["dinitial_state"]), 1 if clamp else 0,
+                               1 if qk_norm else 0, 1 if gate_logits else 0, int(threads))
     if rc != 0:
         raise RuntimeError(f"kda_oracle_bwd failed with code {rc}")
     return out

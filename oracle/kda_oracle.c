@@ -322,12 +322,34 @@ int kda_oracle_summary(int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv,
  * is kept (T * Dk * Dv doubles per (b, h)): meant for small cases.
  * Returns 0, -1 on bad sizes, -2 on allocation failure.
  */
-int kda_oracle_bwd(int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv, int dtype,
-                   const void *q, const void *k, const void *v, const void *log_alpha,
-                   const void *beta, const void *gate, const double *init_state,
-                   const double *dy, const double *dST, double *dq, double *dk, double *dv,
-                   double *dla, double *dbeta, double *dgate, double *dS0, int clamp,
-                   int nthreads) {
+/*
+ * With qk_norm / logits the forward reads raw q, k and forget logits as the forward
+ * oracle does (k / |k|, q / (|q| sqrt(Dk)), log alpha = logsigmoid(x), then the
+ * clamp), and the gradients are taken with respect to those raw inputs: per token,
+ *   unit vector e = x / n (n = max(|x|, 1e-12)), x^ = x / (n s):
+ *     dx = (dx^ - e (e . dx^)) / (n s)    (n > 1e-12; below it x^ = x / (1e-12 s) is
+ *     linear and dx = dx^ / (1e-12 s)),  s = sqrt(Dk) for q, 1 for k;
+ *   dlogit = dlog_alpha * sigmoid(-x)  (d logsigmoid(x) / dx), zero where the clamp
+ *     of logsigmoid(x) is active.
+ */
+static void orc_unit_back(const double *raw, double *g, int64_t n, double extra) {
+    double ss = 0.0, dot = 0.0;
+    for (int64_t c = 0; c < n; ++c) ss += raw[c] * raw[c];
+    const double nrm = sqrt(ss);
+    if (nrm < 1e-12) {
+        for (int64_t c = 0; c < n; ++c) g[c] /= 1e-12 * extra;
+        return;
+    }
+    for (int64_t c = 0; c < n; ++c) dot += raw[c] / nrm * g[c];
+    for (int64_t c = 0; c < n; ++c) g[c] = (g[c] - raw[c] / nrm * dot) / (nrm * extra);
+}
+
+int kda_oracle_bwd_ex(int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv, int dtype,
+                      const void *q, const void *k, const void *v, const void *log_alpha,
+                      const void *beta, const void *gate, const double *init_state,
+                      const double *dy, const double *dST, double *dq, double *dk, double *dv,
+                      double *dla, double *dbeta, double *dgate, double *dS0, int clamp,
+                      int qk_norm, int logits, int nthreads) {
     if (B < 0 || T < 0 || H < 0 || Dk <= 0 || Dv <= 0) return -1;
     if (dtype != ORC_F32 && dtype != ORC_BF16) return -1;
     const int64_t units = B * H, SZ = Dk * Dv;
@@ -342,7 +364,7 @@ int kda_oracle_bwd(int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv, int 
         double *Sall = (double *)malloc(sizeof(double) * (size_t)((T + 1) * SZ));
         double *G = (double *)malloc(sizeof(double) * (size_t)SZ);
         double *Sh = (double *)malloc(sizeof(double) * (size_t)SZ);
-        double *w = (double *)malloc(sizeof(double) * (size_t)(4 * Dk + 6 * Dv));
+        double *w = (double *)malloc(sizeof(double) * (size_t)(6 * Dk + 6 * Dv));
         if (!Sall || !G || !Sh || !w) {
             free(Sall); free(G); free(Sh); free(w);
 #ifdef _OPENMP
@@ -353,6 +375,7 @@ int kda_oracle_bwd(int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv, int 
         }
         double *kk = w, *qv = kk + Dk, *a = qv + Dk, *xg = a + Dk;  /* xg: raw log alpha */
         double *r = xg + Dk, *u = r + Dv, *o = u + Dv, *dov = o + Dv, *duv = dov + Dv, *drv = duv + Dv;
+        double *kraw = drv + Dv, *qraw = kraw + Dk;  /* raw q and k of the token (qk_norm) */
         if (init_state)
             memcpy(Sall, init_state + unit * SZ, sizeof(double) * (size_t)SZ);
         else
@@ -366,7 +389,11 @@ int kda_oracle_bwd(int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv, int 
             for (int64_t c = 0; c < Dk; ++c) {
                 kk[c] = orc_load(k, dtype, tok * Dk + c);
                 const double x = orc_load(log_alpha, dtype, tok * Dk + c);
-                a[c] = exp(clamp ? fmin(fmax(x, ORC_LOG_ALPHA_MIN), 0.0) : x);
+                const double l = logits ? orc_logsigmoid(x) : x;
+                a[c] = exp(clamp ? fmin(fmax(l, ORC_LOG_ALPHA_MIN), 0.0) : l);
+            }
+            if (qk_norm) { /* the unit key the forward uses */
+                orc_unit(kk, Dk, 1.0);
             }
             for (int64_t c = 0; c < Dk; ++c)
                 for (int64_t j = 0; j < Dv; ++j) Sn[c * Dv + j] = a[c] * Sp[c * Dv + j];
@@ -388,10 +415,15 @@ int kda_oracle_bwd(int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv, int 
             const double bt = orc_load(beta, dtype, tok);
             const double *Sp = Sall + t * SZ, *St = Sall + (t + 1) * SZ;
             for (int64_t c = 0; c < Dk; ++c) {
-                kk[c] = orc_load(k, dtype, tok * Dk + c);
-                qv[c] = orc_load(q, dtype, tok * Dk + c);
+                kk[c] = kraw[c] = orc_load(k, dtype, tok * Dk + c);
+                qv[c] = qraw[c] = orc_load(q, dtype, tok * Dk + c);
                 xg[c] = orc_load(log_alpha, dtype, tok * Dk + c);
-                a[c] = exp(clamp ? fmin(fmax(xg[c], ORC_LOG_ALPHA_MIN), 0.0) : xg[c]);
+                const double l = logits ? orc_logsigmoid(xg[c]) : xg[c];
+                a[c] = exp(clamp ? fmin(fmax(l, ORC_LOG_ALPHA_MIN), 0.0) : l);
+            }
+            if (qk_norm) {
+                orc_unit(kk, Dk, 1.0);
+                orc_unit(qv, Dk, sqrt((double)Dk));
             }
             /* recompute S^ = Diag(a) S_{t-1}, r = S^T k, u = beta (v - r), o = S_t^T q */
             for (int64_t c = 0; c < Dk; ++c)
@@ -445,12 +477,28 @@ int kda_oracle_bwd(int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv, int 
                     dl += Sh[c * Dv + j] * dsh;
                     G[c * Dv + j] = a[c] * dsh;
                 }
-                const int pass = !clamp || (xg[c] >= ORC_LOG_ALPHA_MIN && xg[c] <= 0.0);
-                dla[tok * Dk + c] = pass ? dl : 0.0;
+                const double l = logits ? orc_logsigmoid(xg[c]) : xg[c];
+                const int pass = !clamp || (l >= ORC_LOG_ALPHA_MIN && l <= 0.0);
+                /* d logsigmoid(x) / dx = sigmoid(-x) */
+                dla[tok * Dk + c] = pass ? (logits ? dl / (1.0 + exp(xg[c])) : dl) : 0.0;
+            }
+            if (qk_norm) { /* back through the per-token normalisation to the raw q and k */
+                orc_unit_back(qraw, dq + tok * Dk, Dk, sqrt((double)Dk));
+                orc_unit_back(kraw, dk + tok * Dk, Dk, 1.0);
             }
         }
         memcpy(dS0 + unit * SZ, G, sizeof(double) * (size_t)SZ);
         free(Sall); free(G); free(Sh); free(w);
     }
     return failed ? -2 : 0;
+}
+
+int kda_oracle_bwd(int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv, int dtype,
+                   const void *q, const void *k, const void *v, const void *log_alpha,
+                   const void *beta, const void *gate, const double *init_state,
+                   const double *dy, const double *dST, double *dq, double *dk, double *dv,
+                   double *dla, double *dbeta, double *dgate, double *dS0, int clamp,
+                   int nthreads) {
+    return kda_oracle_bwd_ex(B, T, H, Dk, Dv, dtype, q, k, v, log_alpha, beta, gate, init_state, dy,
+                             dST, dq, dk, dv, dla, dbeta, dgate, dS0, clamp, 0, 0, nthreads);
 }

@@ -23,19 +23,19 @@ def _inputs(rng, B, T, H, Dk, Dv, la_lo=-2.0):
                 gate=rng.standard_normal((B, T, H, Dv)))
 
 
-def _loss(x, s0, dy, dST, clamp=True):
-    y, sT = oracle.fwd(*(x[k].astype(np.float32) for k in KEYS), initial_state=s0, clamp=clamp)
+def _loss(x, s0, dy, dST, clamp=True, **opts):
+    y, sT = oracle.fwd(*(x[k].astype(np.float32) for k in KEYS), initial_state=s0, clamp=clamp, **opts)
     return float((y * dy).sum() + (sT * dST).sum())
 
 
-def _fd(x, s0, dy, dST, name, idx, h=1e-3, clamp=True):
+def _fd(x, s0, dy, dST, name, idx, h=1e-3, clamp=True, **opts):
     """Central difference in float32 input space (the oracle reads fp32): the step is a
     power of two, so x +- h is exact for |x| < 2^13 h and the quotient is (L+ - L-) / 2h."""
     xp = {k: v.astype(np.float32).copy() for k, v in x.items()}
     xm = {k: v.astype(np.float32).copy() for k, v in x.items()}
     xp[name][idx] += np.float32(h)
     xm[name][idx] -= np.float32(h)
-    return (_loss(xp, s0, dy, dST, clamp) - _loss(xm, s0, dy, dST, clamp)) / (2 * h)
+    return (_loss(xp, s0, dy, dST, clamp, **opts) - _loss(xm, s0, dy, dST, clamp, **opts)) / (2 * h)
 
 
 @pytest.mark.parametrize("B,T,H,Dk,Dv", [(1, 1, 1, 2, 3), (1, 5, 2, 3, 2), (2, 4, 1, 4, 4)])
@@ -106,3 +106,40 @@ def test_closed_form_without_writes(oracle_lib):
             Gt = q[0, t:, h].T @ do[t:]                     # [Dk, Dv]
             want = (Gt.T @ k[0, t, h]) @ (v[0, t, h] - S0.T @ k[0, t, h])
             assert abs(g["dbeta"][0, t, h] - want) <= 1e-12 * (1 + abs(want))
+
+
+@pytest.mark.parametrize("opts", [dict(qk_norm=True), dict(gate_logits=True), dict(qk_norm=True, gate_logits=True)],
+                         ids=["qk_norm", "gate_logits", "both"])
+def test_gradients_with_fused_preparation_match_central_differences(oracle_lib, opts):
+    """Raw q, k (normalised per token inside, q also by 1/sqrt(Dk)) and forget logits
+    (log alpha = logsigmoid(x), then the clamp): the gradients with respect to the raw
+    inputs against central differences of the forward oracle given the same raw inputs.
+    Logits around -5 put some tokens' retention under the floor, where the clamp stops
+    the gradient."""
+    rng = np.random.default_rng(740)
+    B, T, H, Dk, Dv = 1, 4, 2, 3, 2
+    x = {k: v.astype(np.float32) for k, v in _inputs(rng, B, T, H, Dk, Dv).items()}
+    x["q"] = (x["q"] * 3.0).astype(np.float32)  # raw projections of any size
+    x["k"] = (x["k"] * 0.3).astype(np.float32)
+    if opts.get("gate_logits"):
+        x["log_alpha"] = rng.uniform(-6.5, 3.0, x["log_alpha"].shape).astype(np.float32)
+    s0 = rng.standard_normal((B, H, Dk, Dv)) * 0.5
+    dy = rng.standard_normal((B, T, H, Dv))
+    dST = rng.standard_normal((B, H, Dk, Dv))
+    g = oracle.bwd(*(x[k] for k in KEYS), dy, initial_state=s0, d_final_state=dST, **opts)
+    h = 2.0 ** -11
+    clamped = 0
+    for name, gname in (("q", "dq"), ("k", "dk"), ("v", "dv"), ("log_alpha", "dlog_alpha"),
+                        ("beta", "dbeta"), ("gate", "dgate")):
+        for idx in np.ndindex(x[name].shape):
+            xv = float(x[name][idx])
+            if name == "log_alpha" and opts.get("gate_logits"):
+                ls = min(xv, 0.0) - np.log1p(np.exp(-abs(xv)))
+                if abs(ls - oracle.LOG_ALPHA_MIN) < 4 * h:  # the clamp's kink: no difference there
+                    continue
+                clamped += ls < oracle.LOG_ALPHA_MIN
+            fd = _fd(x, s0, dy, dST, name, idx, h=h, **opts)
+            an = g[gname][idx]
+            assert abs(fd - an) <= 5e-5 * (1 + abs(an)), (name, idx, fd, an)
+    if opts.get("gate_logits"):
+        assert clamped > 0  # some logits sit under the floor: their gradient is zero

@@ -37,7 +37,8 @@ MUTANTS = {
     "summary starts from zero instead of the identity": ("(i == j) ? 1.0 : 0.0", "0.0"),
     "summary value dropped": ("(vv ? bt * vv[j] : 0.0)", "0.0"),
     # fused preprocessing (raw q/k normalisation, forget-gate logits)
-    "query scale dropped": ("orc_unit(qv, Dk, sqrt((double)Dk));", "orc_unit(qv, Dk, 1.0);"),
+    "query scale dropped": ("orc_unit(kv, Dk, 1.0);\n            orc_unit(qv, Dk, sqrt((double)Dk));",
+                            "orc_unit(kv, Dk, 1.0);\n            orc_unit(qv, Dk, 1.0);"),
     "key not normalised": ("orc_unit(kv, Dk, 1.0);", ""),
     "logsigmoid sign flipped": ("return x >= 0.0 ? -log1p(exp(-x))", "return x >= 0.0 ? log1p(exp(-x))"),
     "summary key not normalised": ("if (qk_norm) orc_unit(kk, Dk, 1.0);", ""),
@@ -53,36 +54,44 @@ BWD_MUTANTS = {
     "backward: query gradient added after the write": ("G[c * Dv + j] += qv[c] * dov[j];",
                                                        "G[c * Dv + j] += 0.0 * qv[c] * dov[j];"),
     "backward: update strength dropped from dv": ("dv[tok * Dv + j] = bt * acc;", "dv[tok * Dv + j] = acc;"),
+    "backward: log-sigmoid derivative dropped": ("(logits ? dl / (1.0 + exp(xg[c])) : dl)", "(logits ? dl : dl)"),
+    "backward: normalisation's projection dropped": ("g[c] = (g[c] - raw[c] / nrm * dot) / (nrm * extra);",
+                                                      "g[c] = g[c] / (nrm * extra);"),
 }
 
 
 def _bwd_pins_pass(handle) -> bool:
-    """Gradients against central differences of the variant's own (unchanged) forward."""
+    """Gradients against central differences of the variant's own (unchanged) forward,
+    on prepared inputs and on raw q, k and forget logits with the fused preparation."""
     rng = np.random.default_rng(78)
     B, T, H, Dk, Dv = 1, 3, 1, 2, 2
+    keys = ("q", "k", "v", "log_alpha", "beta", "gate")
+    cases = []
     x = dict(q=rng.standard_normal((B, T, H, Dk)) * 0.5, k=rng.standard_normal((B, T, H, Dk)) * 0.5,
              v=rng.standard_normal((B, T, H, Dv)), log_alpha=rng.uniform(-2, -0.1, (B, T, H, Dk)),
              beta=rng.uniform(0.1, 0.9, (B, T, H)), gate=rng.standard_normal((B, T, H, Dv)))
-    x = {k: a.astype(np.float32) for k, a in x.items()}
-    keys = ("q", "k", "v", "log_alpha", "beta", "gate")
+    cases.append(({k: a.astype(np.float32) for k, a in x.items()}, {}))
+    xr = dict(x, q=x["q"] * 3.0, k=x["k"] * 0.4, log_alpha=rng.uniform(-3, 3, (B, T, H, Dk)))
+    cases.append(({k: a.astype(np.float32) for k, a in xr.items()}, dict(qk_norm=True, gate_logits=True)))
     s0 = rng.standard_normal((B, H, Dk, Dv))
     dy = rng.standard_normal((B, T, H, Dv))
-    g = handle.bwd(*(x[n] for n in keys), dy, initial_state=s0)
+    for x, opts in cases:
+        g = handle.bwd(*(x[n] for n in keys), dy, initial_state=s0, **opts)
 
-    def loss(xx):
-        y, _ = handle.fwd(*(xx[n] for n in keys), initial_state=s0)
-        return float((y * dy).sum())
-    h = np.float32(2.0 ** -10)
-    for name, gname in (("q", "dq"), ("k", "dk"), ("v", "dv"), ("log_alpha", "dlog_alpha"),
-                        ("beta", "dbeta"), ("gate", "dgate")):
-        for idx in np.ndindex(x[name].shape):
-            xp = {n: a.copy() for n, a in x.items()}
-            xm = {n: a.copy() for n, a in x.items()}
-            xp[name][idx] += h
-            xm[name][idx] -= h
-            fd = (loss(xp) - loss(xm)) / (2 * float(h))
-            if abs(fd - g[gname][idx]) > 2e-5 * (1 + abs(fd)):
-                return False
+        def loss(xx):
+            y, _ = handle.fwd(*(xx[n] for n in keys), initial_state=s0, **opts)
+            return float((y * dy).sum())
+        h = np.float32(2.0 ** -10)
+        for name, gname in (("q", "dq"), ("k", "dk"), ("v", "dv"), ("log_alpha", "dlog_alpha"),
+                            ("beta", "dbeta"), ("gate", "dgate")):
+            for idx in np.ndindex(x[name].shape):
+                xp = {n: a.copy() for n, a in x.items()}
+                xm = {n: a.copy() for n, a in x.items()}
+                xp[name][idx] += h
+                xm[name][idx] -= h
+                fd = (loss(xp) - loss(xm)) / (2 * float(h))
+                if abs(fd - g[gname][idx]) > 2e-5 * (1 + abs(fd)):
+                    return False
     return True
 
 
