@@ -304,9 +304,12 @@ def chunk_summary(k, v, log_alpha, beta, clamp=True, transition=None, offset=Non
 
 
 def chunk_bwd(q, k, v, log_alpha, beta, gate, d_out, initial_state=None, d_final_state=None,
-              clamp=True, workspace=None, need_initial_state_grad=True):
+              clamp=True, workspace=None, need_initial_state_grad=True, qk_norm=False,
+              gate_logits=False):
     """Gradients of ``sum(d_out * y) + sum(d_final_state * S_T)`` through ``chunk_fwd``
-    (fp32 output, no preparation options), on the current HIP stream.
+    (fp32 output, the same ``clamp``, ``qk_norm`` and ``gate_logits``), on the current
+    HIP stream: with ``qk_norm`` those of the raw q and k, with ``gate_logits`` that of
+    the logits.
 
     Inputs as for ``chunk_fwd``; ``d_out`` has their shape [B, T, H, Dv] and dtype.
     Returns a dict of fp32 tensors: dq, dk, dlog_alpha [B, T, H, Dk]; dv, dgate
@@ -331,7 +334,7 @@ def chunk_bwd(q, k, v, log_alpha, beta, gate, d_out, initial_state=None, d_final
             raise ValueError(f"{name} must be fp32 [B, H, Dk, Dv]")
     a = _abi.BwdArgs()
     a.B, a.T, a.H, a.Dk, a.Dv, a.dtype = B, T, H, Dk, Dv, code
-    a.flags = 0 if clamp else _abi.KDA_FLAG_NO_CLAMP
+    a.flags = _prep_flags(clamp, qk_norm, gate_logits)
     n = ctypes.c_size_t(0)
     rc = lib.kda_chunk_bwd_workspace_size(ctypes.byref(a), ctypes.byref(n))
     if rc != _abi.KDA_OK:

@@ -121,7 +121,8 @@ int check_bwd(const kda_bwd_args* a, int64_t* nchunks, int64_t* ws_total) {
     if (a->B < 0 || a->T < 0 || a->H < 0 || a->Dk <= 0 || a->Dv <= 0) return KDA_ERR_SHAPE;
     if (a->dtype != KDA_F32 && a->dtype != KDA_BF16) return KDA_ERR_UNSUPPORTED;
     if (a->Dk != a->Dv || (a->Dk != 64 && a->Dk != 128)) return KDA_ERR_UNSUPPORTED;
-    if ((a->flags & ~KDA_FLAG_NO_CLAMP) != 0) return KDA_ERR_UNSUPPORTED;
+    if ((a->flags & ~(KDA_FLAG_NO_CLAMP | KDA_FLAG_QK_L2NORM | KDA_FLAG_GATE_LOGITS)) != 0)
+        return KDA_ERR_UNSUPPORTED;
     int64_t bt, bth, elems, bh, st, items, tmp;
     if (!mul_ok(a->B, a->T, &bt) || !mul_ok(bt, a->H, &bth) || !mul_ok(bth, a->Dk, &elems) ||
         !mul_ok(a->B, a->H, &bh) || !mul_ok(bh, a->Dk * a->Dv, &st))
@@ -422,6 +423,8 @@ int kda_chunk_bwd(const kda_bwd_args* a, hipStream_t stream) {
     p.H = a->H;
     p.NC = nc;
     p.clamp = (a->flags & KDA_FLAG_NO_CLAMP) ? 0 : 1;
+    p.qk_norm = (a->flags & KDA_FLAG_QK_L2NORM) ? 1 : 0;
+    p.logits = (a->flags & KDA_FLAG_GATE_LOGITS) ? 1 : 0;
     kda::bwd_layout((int)a->Dk, a->B * a->H, nc, a->workspace, p);
     const hipError_t e = kda::launch_bwd(a->dtype == KDA_BF16, (int)a->Dk, p, stream);
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;

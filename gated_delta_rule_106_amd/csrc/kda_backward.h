@@ -30,6 +30,8 @@ struct BwdParams {
     int64_t B, T, H;
     int64_t NC;        // chunks per sequence
     int clamp;
+    int qk_norm;       // q, k are raw: the gradients are taken through k / |k|, q / (|q| sqrt(D))
+    int logits;        // la holds forget-gate logits: log alpha = logsigmoid(la)
 };
 
 // Workspace bytes of one call (sections: trans, pairs, states, dstates).

@@ -302,6 +302,30 @@ __device__ __forceinline__ void lower_block(int task, int& a, int& b) {
     b = task - a * (a + 1) / 2;
 }
 
+// Sum over the D / 8 neighbouring lanes that hold one token's channels in the staging
+// loops (eight channels per lane, consecutive lanes on consecutive groups).
+template <int D>
+__device__ __forceinline__ float token_sum(float v) {
+#pragma unroll
+    for (int m = 1; m < D / 8; m <<= 1) v += __shfl_xor(v, m);
+    return v;
+}
+// Per-token L2 normalisation of raw q or k (the fused preparation): scales a lane's
+// eight channels by s = 1 / (c max(|x|, 1e-12)) and returns s; c = 1 for k, sqrt(D)
+// for q.  Every lane of the wave takes part.
+template <int D>
+__device__ __forceinline__ float unit8(float (&x)[8], float inv_c) {
+    float ss = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) ss = fmaf(x[j], x[j], ss);
+    const float s = inv_norm(token_sum<D>(ss)) * inv_c;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) x[j] *= s;
+    return s;
+}
+template <int D>
+constexpr float kInvSqrtD = D == 128 ? 0.08838834764831845f : 0.125f;
+
 // LDS of the chunk kernel (floats; C x D blocks with row pitch D + 4, C x C with C + 4).
 template <int D>
 struct ChunkL {
@@ -320,7 +344,8 @@ struct ChunkL {
 // the two tiles, k_r e^{g_r - rho} against k_s e^{rho - g_s}: the end of tile a - 1 for
 // b < a (both factors <= 1), token 7 of the tile for a diagonal block (each factor spans
 // at most eight tokens of decay).
-template <int D, class In>
+// PREP: the inputs take the fused preparation first (flags qk_norm, logits).
+template <int D, class In, bool PREP>
 __global__ __launch_bounds__(64 * (D / 16)) void kda_bwd_chunk_kernel(BwdParams p) {
     using L = ChunkL<D>;
     using RC = Rec<D>;
@@ -360,8 +385,13 @@ __global__ __launch_bounds__(64 * (D / 16)) void kda_bwd_chunk_kernel(BwdParams 
 #pragma unroll
         for (int u = 0; u < G8; ++u) {
             const int grp = tid + u * NTT, r = grp / (D / 8), c8 = 8 * (grp - r * (D / 8));
+            if (PREP && p.qk_norm) {
+                unit8<D>(k8[u], 1.f);
+                unit8<D>(q8[u], kInvSqrtD<D>);
+            }
 #pragma unroll
-            for (int j = 0; j < 8; ++j) l8[u][j] = r < cp.L ? clamp_log_alpha(l8[u][j], p.clamp != 0) : 0.f;
+            for (int j = 0; j < 8; ++j)
+                l8[u][j] = r < cp.L ? log_alpha_in(l8[u][j], PREP && p.logits, p.clamp != 0) : 0.f;
             st8(sk + r * DP + c8, k8[u]);
             st8(sq + r * DP + c8, q8[u]);
             st8(sg + r * DP + c8, l8[u]);
@@ -540,7 +570,7 @@ struct GradL {
     static constexpr int NW = D / 16, DP = D + 4, CP = C + 4;
     static constexpr int RA = 0, RB = C * DP, RCc = 2 * C * DP, RL = 3 * C * DP, RP = RL + C * CP,
                          RQ = RP + C * CP, BETA = RQ + C * CP, DGC = BETA + C, DB1 = DGC + NW * D,
-                         TOTAL = DB1 + NW * C;
+                         SCL = DB1 + NW * C, TOTAL = SCL + 2 * C;
     static_assert(TOTAL * 4 <= 160 * 1024, "gradient kernel LDS");
 };
 
@@ -561,7 +591,9 @@ __device__ __forceinline__ float sum16(float v) {
 // (left products read their other operand from LDS), and then forms the key columns
 // 16 w .. of the products over the value dimension (dO S0^T, dX S0^T, U dS_C^T) and of the
 // pair terms of dq, dk and dg.
-template <int D, class In>
+// PREP: the inputs take the fused preparation (flags qk_norm, logits); the gradients of
+// q and k go back through the normalisation, that of log alpha through logsigmoid.
+template <int D, class In, bool PREP>
 __global__ __launch_bounds__(64 * (D / 16)) void kda_bwd_grad_kernel(BwdParams p) {
     using L = GradL<D>;
     using PR = Pr<D>;
@@ -578,6 +610,8 @@ __global__ __launch_bounds__(64 * (D / 16)) void kda_bwd_grad_kernel(BwdParams p
     float* sbeta = lds + L::BETA;
     float* dgcp = lds + L::DGC;
     float* db1p = lds + L::DB1;
+    float* sclq = lds + L::SCL;  // per token: the normalisation factors of q and k
+    float* sclk = sclq + C;
     const int64_t item = blockIdx.x;
     const ChunkPos cp = chunk_pos(p, item);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l = lane & 15, g = lane >> 4;
@@ -625,6 +659,10 @@ __global__ __launch_bounds__(64 * (D / 16)) void kda_bwd_grad_kernel(BwdParams p
 #pragma unroll
         for (int u = 0; u < G8; ++u) {
             const int grp = tid + u * NTT, r = grp / (D / 8), c8 = 8 * (grp - r * (D / 8));
+            if (PREP && p.qk_norm) {
+                unit8<D>(k8[u], 1.f);
+                unit8<D>(q8[u], kInvSqrtD<D>);
+            }
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
                 const float e = ex(g8[u][j]);
@@ -710,6 +748,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void kda_bwd_grad_kernel(BwdParams p
 #pragma unroll
         for (int u = 0; u < G8; ++u) {
             const int grp = tid + u * NTT, r = grp / (D / 8), c8 = 8 * (grp - r * (D / 8));
+            if (PREP && p.qk_norm) unit8<D>(k8[u], 1.f);
 #pragma unroll
             for (int j = 0; j < 8; ++j) k8[u][j] *= ex(c8v[u][j] - g8[u][j]);
             st8(rc + r * DP + c8, k8[u]);
@@ -879,6 +918,13 @@ __global__ __launch_bounds__(64 * (D / 16)) void kda_bwd_grad_kernel(BwdParams p
         for (int u = 0; u < G8; ++u) {
             const int grp = tid + u * NTT, r = grp / (D / 8), c8 = 8 * (grp - r * (D / 8));
             const int i = r * D + c8;
+            if (PREP && p.qk_norm) {
+                const float ks = unit8<D>(k8[u], 1.f), qs = unit8<D>(q8[u], kInvSqrtD<D>);
+                if (c8 == 0) {
+                    sclk[r] = ks;
+                    sclq[r] = qs;
+                }
+            }
             st8(sgg + i, g8[u]);
             st8(skk + i, k8[u]);
             st8(r < C / 2 ? rl + i : rq + (i - (C / 2) * D), q8[u]);
@@ -1000,7 +1046,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void kda_bwd_grad_kernel(BwdParams p
             const float dk = QB[i] + KP[i] + KB[i] + dkt + dkb;
             dg[a][i] = qv * dq + kv * (QB[i] + dkt - KP[i] - KB[i] - dkb);
             dgc += kv * dkb;
-            if (r < cp.L) {
+            if (r < cp.L) {  // with the normalisation, the gradients of y: finished below
                 const int64_t e = elem<D>(p, cp, r, c);
                 p.dq[e] = dq;
                 p.dk[e] = dk;
@@ -1039,14 +1085,51 @@ __global__ __launch_bounds__(64 * (D / 16)) void kda_bwd_grad_kernel(BwdParams p
             if (r < cp.L) {
                 const int64_t e = elem<D>(p, cp, r, c);
                 float d = dg[ma][i] + after_g + later;
-                if (p.clamp) {
-                    const float raw_la = In::load(static_cast<const raw*>(p.la), e);
-                    if (!(raw_la >= kLogAlphaMin && raw_la <= 0.f)) d = 0.f;
+                const bool logits = PREP && p.logits;
+                if (p.clamp || logits) {
+                    const float x = In::load(static_cast<const raw*>(p.la), e);
+                    const float lv = logits ? log_sigmoid(x) : x;  // log alpha before the clamp
+                    if (p.clamp && !(lv >= kLogAlphaMin && lv <= 0.f)) d = 0.f;
+                    if (logits) d *= sigmoidf_(-x);                 // d logsigmoid(x) / dx
                 }
                 p.dla[e] = d;
             }
         }
         later += t0 + t1 + t2 + t3;
+    }
+    if (PREP && p.qk_norm) {
+        // back through the normalisation, a token's channels eight to a lane as in the
+        // staging: dx = s (dy - c^2 y (y . dy)) for y = s x, s = 1 / (c |x|) (c = sqrt(D)
+        // for q, 1 for k), dy read back from the outputs once every wave has written them
+        __syncthreads();
+#pragma unroll
+        for (int u = 0; u < G8; ++u) {
+            const int grp = tid + u * NTT, r = grp / (D / 8), c8 = 8 * (grp - r * (D / 8));
+            if (r < cp.L) {  // uniform over the D / 8 lanes of a token
+                const int64_t e = elem<D>(p, cp, r, c8);
+                float dq8[8], dk8[8], yq[8], yk[8];
+                ld8(p.dq + e, dq8);
+                ld8(p.dk + e, dk8);
+                ld8(r < C / 2 ? rl + r * D + c8 : rq + (r - C / 2) * D + c8, yq);
+                ld8(skk + r * D + c8, yk);
+                float pq = 0.f, pk = 0.f;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    pq = fmaf(yq[j], dq8[j], pq);
+                    pk = fmaf(yk[j], dk8[j], pk);
+                }
+                pq = token_sum<D>(pq) * (float)D;
+                pk = token_sum<D>(pk);
+                const float sq = sclq[r], sk = sclk[r];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    dq8[j] = sq * (dq8[j] - yq[j] * pq);
+                    dk8[j] = sk * (dk8[j] - yk[j] * pk);
+                }
+                st8(p.dq + e, dq8);
+                st8(p.dk + e, dk8);
+            }
+        }
     }
 }
 
@@ -1063,12 +1146,12 @@ int64_t section_bytes(int64_t bh, int64_t nc, int64_t* trans, int64_t* pairs, in
     return *trans + *pairs + 2 * *states;
 }
 
-template <int D, class In>
+template <int D, class In, bool PREP>
 hipError_t launch_d(const BwdParams& p, hipStream_t stream) {
     const int64_t items = p.B * p.H * p.NC;
     constexpr int NTC = 64 * (D / 16);
     if (items > 0) {
-        auto kc = kda_bwd_chunk_kernel<D, In>;
+        auto kc = kda_bwd_chunk_kernel<D, In, PREP>;
         constexpr int lds = ChunkL<D>::TOTAL * 4;
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kc),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, lds);
@@ -1090,7 +1173,7 @@ hipError_t launch_d(const BwdParams& p, hipStream_t stream) {
         if (e != hipSuccess) return e;
     }
     if (items > 0) {
-        auto kg = kda_bwd_grad_kernel<D, In>;
+        auto kg = kda_bwd_grad_kernel<D, In, PREP>;
         constexpr int lds = GradL<D>::TOTAL * 4;
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kg),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, lds);
@@ -1120,9 +1203,15 @@ void bwd_layout(int D, int64_t bh, int64_t nc, void* ws, BwdParams& p) {
     p.dstates = reinterpret_cast<float*>(w + t + r + s);
 }
 
+template <bool PREP>
+hipError_t launch_prep(int dtype_bf16, int D, const BwdParams& p, hipStream_t stream) {
+    if (D == 64) return dtype_bf16 ? launch_d<64, InBF16, PREP>(p, stream) : launch_d<64, InF32, PREP>(p, stream);
+    return dtype_bf16 ? launch_d<128, InBF16, PREP>(p, stream) : launch_d<128, InF32, PREP>(p, stream);
+}
+
 hipError_t launch_bwd(int dtype_bf16, int D, const BwdParams& p, hipStream_t stream) {
-    if (D == 64) return dtype_bf16 ? launch_d<64, InBF16>(p, stream) : launch_d<64, InF32>(p, stream);
-    return dtype_bf16 ? launch_d<128, InBF16>(p, stream) : launch_d<128, InF32>(p, stream);
+    return p.qk_norm || p.logits ? launch_prep<true>(dtype_bf16, D, p, stream)
+                                 : launch_prep<false>(dtype_bf16, D, p, stream);
 }
 
 }  // namespace kda

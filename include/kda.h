@@ -296,8 +296,10 @@ int kda_combine_states(const kda_combine_args *a, hipStream_t stream);
 /*
  * Arguments of kda_chunk_bwd: the gradients of a scalar loss
  *   L = sum(d_out * out) + sum(d_final_state * S_T)
- * through the forward that kda_chunk_fwd computes (fp32 out, no preparation
- * flags), with respect to every input.  The reverse mode of the per-token step
+ * through the forward that kda_chunk_fwd computes (fp32 out, the same flags),
+ * with respect to every input as passed: with KDA_FLAG_QK_L2NORM the gradients
+ * of the raw q and k (through the per-token normalisation), with
+ * KDA_FLAG_GATE_LOGITS that of the forget-gate logits (through logsigmoid).  The reverse mode of the per-token step
  * (page "3T models are no longer magic", section "Gate 1: KDA makes it
  * computable") is taken over the chunk-recurrent form (page "Kimi K3 report
  * walk-through", section "Compute paradigm") with 64-token chunks.
@@ -308,9 +310,11 @@ int kda_combine_states(const kda_combine_args *a, hipStream_t stream);
  *   d_final_state: fp32 [B, H, Dk, Dv] or NULL (zeros).
  *   dq, dk, dlog_alpha: fp32 [B, T, H, Dk]; dv, dgate: fp32 [B, T, H, Dv];
  *   dbeta: fp32 [B, T, H]; all required when B*T*H > 0.  dlog_alpha is zero
- *     where the clamp of log alpha is active (outside [ln 0.0067, 0]).
+ *     where the clamp of log alpha is active (its value, after logsigmoid for
+ *     logits, outside [ln 0.0067, 0]).
  *   d_initial_state: fp32 [B, H, Dk, Dv] or NULL (not returned).
- *   flags: KDA_FLAG_NO_CLAMP only.
+ *   flags: KDA_FLAG_NO_CLAMP, KDA_FLAG_QK_L2NORM, KDA_FLAG_GATE_LOGITS; other
+ *     bits give KDA_ERR_UNSUPPORTED.
  *   workspace: at least kda_chunk_bwd_workspace_size bytes, 256-byte aligned.
  *     Per (b, h, 64-token chunk) it holds, in fp32 and each section rounded up
  *     to 256 bytes: a record for the state sweeps (2*64*Dk + 2*Dk*Dv + Dk

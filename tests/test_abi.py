@@ -389,8 +389,12 @@ def test_bwd_workspace_size(lib):
     (lambda a: setattr(a, "T", 2 ** 62), _abi.KDA_ERR_SHAPE),
     (lambda a: setattr(a, "dtype", 7), _abi.KDA_ERR_UNSUPPORTED),
     (lambda a: setattr(a, "Dv", 64), _abi.KDA_ERR_UNSUPPORTED),
-    (lambda a: setattr(a, "flags", _abi.KDA_FLAG_QK_L2NORM), _abi.KDA_ERR_UNSUPPORTED),
     (lambda a: setattr(a, "flags", _abi.KDA_FLAG_NO_SEGMENT_SCAN), _abi.KDA_ERR_UNSUPPORTED),
+    (lambda a: setattr(a, "flags", _abi.KDA_FLAG_CARDS_READY), _abi.KDA_ERR_UNSUPPORTED),
+    (lambda a: setattr(a, "flags", 32), _abi.KDA_ERR_UNSUPPORTED),
+    # the preparation flags are accepted: the next check (no workspace) decides
+    (lambda a: setattr(a, "flags", _abi.KDA_FLAG_QK_L2NORM | _abi.KDA_FLAG_GATE_LOGITS | _abi.KDA_FLAG_NO_CLAMP),
+     _abi.KDA_ERR_WORKSPACE),
     (lambda a: setattr(a, "d_out", None), _abi.KDA_ERR_NULL),
     (lambda a: setattr(a, "dbeta", None), _abi.KDA_ERR_NULL),
     (lambda a: setattr(a, "dgate", 0x700008), _abi.KDA_ERR_ALIGN),

@@ -23,7 +23,7 @@ import pytest
 import torch
 
 import oracle
-from kda_workloads import CONFIGS, make_inputs, small
+from kda_workloads import CONFIGS, make_inputs, make_raw_inputs, small
 
 pytestmark = pytest.mark.gpu
 
@@ -57,18 +57,18 @@ def _cotangents(wl, seed, with_dst):
     return dy, dst
 
 
-def _run(x, dy, dst, clamp=True):
+def _run(x, dy, dst, clamp=True, **opts):
     d = {n: x[n].cuda() for n in KEYS}
     s0 = x["initial_state"].cuda() if x.get("initial_state") is not None else None
     g = kda().chunk_bwd(*(d[n] for n in KEYS), dy.cuda(), initial_state=s0,
-                        d_final_state=dst.cuda() if dst is not None else None, clamp=clamp)
+                        d_final_state=dst.cuda() if dst is not None else None, clamp=clamp, **opts)
     torch.cuda.synchronize()
     return g
 
 
-def _oracle(x, dy, dst, clamp=True):
+def _oracle(x, dy, dst, clamp=True, **opts):
     return oracle.bwd(*(x[n] for n in KEYS), dy.double().numpy(), initial_state=x.get("initial_state"),
-                      d_final_state=dst, clamp=clamp)
+                      d_final_state=dst, clamp=clamp, **opts)
 
 
 def _check(tag, g, ref):
@@ -196,3 +196,64 @@ def test_without_initial_state_gradient():
     for n in GRADS[:-1]:
         assert torch.equal(full[n], part[n]), n
     say("[bwd] without dS0: the other gradients are unchanged")
+
+
+# The fused preparation (page "3T models are no longer magic", section "FlashKDA": the
+# Q and K normalisation and the forget-gate computation belong to the preparation
+# step): raw q and k, forget-gate logits, the gradients taken with respect to them.
+# Raw inputs: each token's q and k scaled by a random factor in [0.1, 10); channels
+# at the floor carry logits of -12 (log-sigmoid below ln 0.0067: clamped, zero gradient).
+PREP = dict(qk_norm=True, gate_logits=True)
+PREP_CASES = [
+    ("bf16 d128 T200 (ragged tail) state in, dS_T", small(CONFIGS[3], H=2, T=200), True, True),
+    ("fp32 d64 T150 state in", small(CONFIGS[0], B=1, H=2, T=150, Dk=64, Dv=64, chunk=64), True, False),
+    ("bf16 d64 T64 (one chunk), dS_T", small(CONFIGS[2], B=2, H=1, T=64, Dk=64, Dv=64), False, True),
+    ("fp32 d128 T130 state in, dS_T", small(CONFIGS[0], B=1, H=1, T=130, Dk=128, Dv=128, chunk=64), True, True),
+]
+
+
+@pytest.mark.parametrize("tag,wl,init,with_dst", PREP_CASES, ids=[c[0] for c in PREP_CASES])
+def test_backward_with_fused_preparation(tag, wl, init, with_dst):
+    say(f"[bwd] prepared case {tag}: B{wl.B} H{wl.H} T{wl.T} d{wl.Dk} {wl.dtype}")
+    x = make_raw_inputs(wl.scaled(init_state=init), seed=200 + wl.T)
+    dy, dst = _cotangents(wl, 13 + wl.T, with_dst)
+    g = _run(x, dy, dst, **PREP)
+    ref = _oracle(x, dy, dst, **PREP)
+    _check("prepared " + tag, g, ref)
+    dead = x["log_alpha"].float() < -11.0  # the floor channels' logits
+    if dead.any():
+        assert bool((g["dlog_alpha"].cpu()[dead] == 0).all())
+
+
+@pytest.mark.parametrize("opts", [dict(qk_norm=True), dict(gate_logits=True),
+                                  dict(gate_logits=True, clamp=False)],
+                         ids=["qk_norm", "gate_logits", "gate_logits no clamp"])
+def test_backward_each_preparation_option(opts):
+    """One option on, the other input arriving prepared.  Without the clamp the recipe
+    has no floor channels (the logits keep the decay within the exponent range)."""
+    clamp = opts.pop("clamp", True)
+    wl = small(CONFIGS[1], B=1, H=2, T=170)
+    if not clamp:
+        wl = wl.scaled(floor_frac=0.0)
+    raw, x = make_raw_inputs(wl, seed=97), make_inputs(wl, seed=97)
+    if opts.get("qk_norm"):
+        x["q"], x["k"] = raw["q"], raw["k"]
+    if opts.get("gate_logits"):
+        x["log_alpha"] = raw["log_alpha"]
+    dy, dst = _cotangents(wl, 19, True)
+    _check(f"option {opts} clamp={clamp}", _run(x, dy, dst, clamp=clamp, **opts),
+           _oracle(x, dy, dst, clamp=clamp, **opts))
+
+
+def test_backward_fused_preparation_full_size_sampled_heads():
+    """B1 H8 T4096 d128 bf16 with raw q, k and logits; heads are independent, so the
+    oracle runs on two of them."""
+    wl = CONFIGS[1]
+    x = make_raw_inputs(wl, seed=23)
+    dy, _ = _cotangents(wl, 29, False)
+    g = _run(x, dy, None, **PREP)
+    for h in (2, 7):
+        xs = {n: x[n][:, :, h:h + 1].contiguous() for n in KEYS}
+        ref = _oracle(xs, dy[:, :, h:h + 1].contiguous(), None, **PREP)
+        gh = {n: (g[n][:, :, h:h + 1] if n != "dinitial_state" else g[n][:, h:h + 1]) for n in GRADS}
+        _check(f"prepared B1 H8 T4096 d128 bf16, head {h}", gh, ref)
