@@ -9,12 +9,15 @@
 // independent of the segment lengths.
 //
 // One workgroup per ((b, h), 16-column tile of the state): the tile (D x 16 fp32)
-// stays in LDS across the segments; D / 16 waves each own one block of 16 rows and
+// stays in LDS across the segments (two buffers, read one, write the other: one
+// barrier per segment); D / 16 waves each own one block of 16 rows and
 // form it with the fp32 MFMA (v_mfma_f32_16x16x4_f32) from its rows of M_p (held in
-// registers as float4 A operands) and b_p (the starting accumulator).  The rows of
-// M_{p+1} and b_{p+1} are loaded while segment p is combined, so each step waits on
-// memory at most once.  Everything stays in fp32: the state keeps its full
-// precision from segment to segment.
+// registers as float4 A operands) and b_p (the starting accumulator).  Three register
+// sets rotate: the rows of M_{p+1} and M_{p+2} (and b) are in flight while segment p
+// is combined.  Every step issues its loads unconditionally (past the last segment it
+// loads the last one again), so that the count of loads in flight is the same on
+// every path and each step waits only for its own segment.  Everything stays in
+// fp32: the state keeps its full precision from segment to segment.
 #include "kda_device.h"
 #include "kda_segment.h"
 
@@ -37,8 +40,9 @@ template <int D>
 __global__ __launch_bounds__(D * 4) void kda_combine_kernel(CombineParams p) {
     constexpr int NT = D / 16;  // column tiles per state; also waves per workgroup
     constexpr int NK = D / 16;  // 16-wide k steps of one row block
+    static_assert(NK % 2 == 0, "two accumulator chains");
     constexpr int NTH = D * 4;  // threads
-    __shared__ __align__(16) float S[D * kPad];
+    __shared__ __align__(16) float S[2 * D * kPad];
     const int lane = lane_id(), wave = wave_id();
     const int m = lane & 15, g = lane >> 4;
     // consecutive workgroups go to different XCDs; the NT tiles of one (b, h), which all
@@ -55,11 +59,13 @@ __global__ __launch_bounds__(D * 4) void kda_combine_kernel(CombineParams p) {
     static_assert(D * 16 == 4 * NTH, "one float4 of the tile per thread");
     const int tr = threadIdx.x >> 2, tc = 4 * (threadIdx.x & 3);  // row, first column
 
-    // this wave's 16 rows of M_s (as MFMA A operands) and its b_s accumulator start,
-    // in two register sets: segment s + 1 loads while segment s is combined
-    float4 MA[NK], MB[NK];
-    floatx4 bA, bB;
+    // this wave's 16 rows of M_s (as MFMA A operands) and its b_s accumulator start, in
+    // three register sets: segments s + 1 and s + 2 load while segment s is combined
+    float4 M0[NK], M1[NK], M2[NK];
+    floatx4 b0, b1, b2;
+    const int64_t last = p.P - 1;
     auto load_seg = [&](int64_t s, float4(&Ma)[NK], floatx4& bb) __attribute__((always_inline)) {
+        s = s < last ? s : last;
         const float* Mp = p.M + (s * p.units + unit) * DD + (int64_t)arow * D + 4 * g;
         const float* bp = p.b + (s * p.units + unit) * DD + (int64_t)crow * D + col0 + m;
 #pragma unroll
@@ -67,28 +73,42 @@ __global__ __launch_bounds__(D * 4) void kda_combine_kernel(CombineParams p) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) bb[i] = bp[(int64_t)i * D];
     };
+    // combines segment s from (Ma, bb) and loads segment s + 2 into (Mn, bn); S_s is in
+    // buffer s % 2, S_{s+1} goes to the other
     auto step = [&](int64_t s, const float4(&Ma)[NK], const floatx4& bb, float4(&Mn)[NK], floatx4& bn)
         __attribute__((always_inline)) {
-        if (s + 1 < p.P) load_seg(s + 1, Mn, bn);
+        load_seg(s + 2, Mn, bn);
+        const float* Sc = S + (s & 1) * D * kPad;
+        float* Sn = S + ((s + 1) & 1) * D * kPad;
         if (p.seg) {
             float* dst = p.seg + (s * p.units + unit) * DD;
             *reinterpret_cast<float4*>(dst + (int64_t)tr * D + col0 + tc) =
-                *reinterpret_cast<const float4*>(&S[tr * kPad + tc]);
+                *reinterpret_cast<const float4*>(&Sc[tr * kPad + tc]);
         }
-        floatx4 acc = bb;
+        floatx4 sv[NK];  // every B operand of the step read first: one wait on LDS
 #pragma unroll
         for (int kk = 0; kk < NK; ++kk) {
             const int k0 = 16 * kk + 4 * g;
-            const floatx4 sv = {S[(k0 + 0) * kPad + m], S[(k0 + 1) * kPad + m], S[(k0 + 2) * kPad + m],
-                                S[(k0 + 3) * kPad + m]};
-            acc = mma16(Ma[kk], sv, acc);
+            sv[kk] = floatx4{Sc[(k0 + 0) * kPad + m], Sc[(k0 + 1) * kPad + m], Sc[(k0 + 2) * kPad + m],
+                             Sc[(k0 + 3) * kPad + m]};
         }
-        lds_barrier();  // every wave has read S_s (loads of segment s + 1 stay in flight)
+        __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of the products
+        floatx4 acc0 = bb, acc1 = zero4();  // two chains over alternate k blocks
 #pragma unroll
-        for (int i = 0; i < 4; ++i) S[(crow + i) * kPad + m] = acc[i];
-        lds_barrier();  // S_{s+1} is complete
+        for (int kk = 0; kk < NK; kk += 2) {
+            acc0 = mma16(Ma[kk], sv[kk], acc0);
+            acc1 = mma16(Ma[kk + 1], sv[kk + 1], acc1);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) Sn[(crow + i) * kPad + m] = acc0[i] + acc1[i];
+        // S_{s+1} is complete (the later segments' loads stay in flight); buffer s % 2 is
+        // written again only after the next step's barrier, when every wave has read it
+        lds_barrier();
     };
-    if (p.P > 0) load_seg(0, MA, bA);
+    if (p.P > 0) {
+        load_seg(0, M0, b0);
+        load_seg(1, M1, b1);
+    }
 
     // the tile of the incoming state, one float4 per thread (D x 16 = 4 NTH floats), read
     // before anything of this tile is written, so the final state may alias it
@@ -98,13 +118,17 @@ __global__ __launch_bounds__(D * 4) void kda_combine_kernel(CombineParams p) {
         *reinterpret_cast<float4*>(&S[tr * kPad + tc]) = v;
     }
     __syncthreads();
-    for (int64_t s = 0; s < p.P; s += 2) {
-        step(s, MA, bA, MB, bB);
-        if (s + 1 < p.P) step(s + 1, MB, bB, MA, bA);
+    int64_t s = 0;
+    for (; s + 3 <= p.P; s += 3) {  // the register sets in turn; every step of a trip runs
+        step(s, M0, b0, M2, b2);
+        step(s + 1, M1, b1, M0, b0);
+        step(s + 2, M2, b2, M1, b1);
     }
+    if (s < p.P) step(s, M0, b0, M2, b2);
+    if (s + 1 < p.P) step(s + 1, M1, b1, M0, b0);
     if (p.sT)
         *reinterpret_cast<float4*>(p.sT + unit * DD + (int64_t)tr * D + col0 + tc) =
-            *reinterpret_cast<const float4*>(&S[tr * kPad + tc]);
+            *reinterpret_cast<const float4*>(&S[(p.P & 1) * D * kPad + tr * kPad + tc]);
 }
 
 // M = I and b = 0 for every (b, h): one workgroup per (b, h)
