@@ -191,10 +191,19 @@ def prefill_call(kda, wl):
 
 
 # ---------------------------------------------------------------- the legs
-PREFILL_KERNEL = {
-    "bf16": "kda_chunk_fwd = kda_prep64_kernel + kda_rec64_kernel (one call, two launches)",
-    "f32": "kda_chunk_fwd = kda_prep_kernel + kda_recur_kernel (one call, two launches)",
-}
+def prefill_kernel(wl) -> str:
+    """The kernels one kda_chunk_fwd call of this workload launches.  Few long bf16
+    sequences (at most 128 one-tile state-pass workgroups, at least 256 chunks) take
+    the pipelined pieces of 64 chunks."""
+    if wl.dtype != "bf16":
+        return "kda_chunk_fwd = kda_prep_kernel + kda_recur_kernel (one call, two launches)"
+    nc = (wl.T + 63) // 64
+    if wl.Dk == 128 and wl.B * wl.H * (wl.Dk // 16) <= 128 and nc >= 256:
+        n = (nc + 63) // 64
+        return (f"kda_chunk_fwd in {n} pieces of 64 chunks = kda_prep64_kernel (piece 0's cards) + "
+                f"{n - 1} x kda_piece64_kernel (state pass over piece i beside the card builder of piece "
+                f"i + 1) + kda_rec64_kernel (last piece): one call, {n + 1} launches")
+    return "kda_chunk_fwd = kda_prep64_kernel + kda_rec64_kernel (one call, two launches)"
 
 
 def bench_prefill(kda, wl, steps, warmup, n_sets, dev, stream):
@@ -215,7 +224,7 @@ def bench_prefill(kda, wl, steps, warmup, n_sets, dev, stream):
     res["hbm_frac"] = res["hbm_gbs"] / HBM_PEAK_GBS
     res["mfma_frac"] = res["mfma_tflops"] / BF16_MFMA_PEAK_TFLOPS
     res["roofline"] = {
-        "kernel": PREFILL_KERNEL[wl.dtype], "bound": "hbm", "achieved": res["hbm_gbs"],
+        "kernel": prefill_kernel(wl), "bound": "hbm", "achieved": res["hbm_gbs"],
         "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": res["hbm_frac"],
         "traffic": stored_traffic("prefill_" + wl.name),
         "bytes_per_launch": nbytes, "launch_ms": ev_ms,
@@ -479,7 +488,7 @@ def bench_backward(kda, wl, steps, warmup, dev, stream):
     res = {"workload": wl.name, "us_per_call": 1e3 * t_b, "tokens_per_s": toks / (t_b / 1e3),
            "alg_bytes_per_call": byt, "alg_gbs": gbs, "workspace_bytes": n_ws,
            "compute": "fp32 (inputs bf16, gradients fp32)",
-           "roofline": {"kernel": "kda_chunk_bwd = kda_bwd_prep_kernel + kda_bwd_sweep_kernel + "
+           "roofline": {"kernel": "kda_chunk_bwd = kda_bwd_chunk_kernel + kda_bwd_sweep_kernel + "
                                   "kda_bwd_grad_kernel (one call, three launches)",
                         "bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                         "frac": gbs / HBM_PEAK_GBS, "traffic": stored_traffic("backward_" + wl.name)}}
