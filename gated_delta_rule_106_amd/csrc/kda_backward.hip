@@ -403,9 +403,13 @@ __global__ __launch_bounds__(64 * (D / 16)) void kda_bwd_chunk_kernel(BwdParams 
                          : 0.f;
     __syncthreads();
     if (tid < D) {  // g: inclusive cumulative sum over the chunk per key channel
+        float gv[C];  // every load issued before the sums
+#pragma unroll
+        for (int r = 0; r < C; ++r) gv[r] = sg[r * DP + tid];
         float acc = 0.f;
+#pragma unroll
         for (int r = 0; r < C; ++r) {
-            acc += sg[r * DP + tid];
+            acc += gv[r];
             sg[r * DP + tid] = acc;
             pr[PR::G + r * D + tid] = acc;
         }
@@ -414,7 +418,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void kda_bwd_chunk_kernel(BwdParams 
     for (int i = tid; i < C * C; i += NTT) {
         const int r = i / C, s = i - r * C;
         if (s / 16 > r / 16) {
-            sbm[r * CP + s] = sp[r * CP + s] = 0.f;
+            sbm[r * CP + s] = sp[r * CP + s] = sli[r * CP + s] = 0.f;
             pr[PR::BM + i] = pr[PR::PM + i] = 0.f;
         }
     }
@@ -452,29 +456,46 @@ __global__ __launch_bounds__(64 * (D / 16)) void kda_bwd_chunk_kernel(BwdParams 
         }
     }
     __syncthreads();
-    // Li = (I + diag(beta) Bm)^-1 by forward substitution, one column per lane of wave 0,
-    // the column in registers (fully unrolled; rows of Bm read as float4 broadcasts)
+    // Li = (I + F)^-1 with F = diag(beta) Bm, blocked by 16 tokens: the diagonal blocks
+    // X_a = (I + F_aa)^-1 by forward substitution in wave 0 (lane group = block, lane =
+    // column, the column in registers), then block diagonal d = 1, 2, 3:
+    //   Li_{a,a-d} = -X_a sum_{c = a-d}^{a-1} F_{a,c} Li_{c,a-d}
+    // on the fp32 MFMA, one block per wave
     if (wave == 0) {
-        const int s = lane;
-        float x[C];
+        const int a = g, j = l;
+        const float* fb = sbm + (16 * a) * CP + 16 * a;
+        float x[16];
+        x[0] = j == 0 ? 1.f : 0.f;
 #pragma unroll
-        for (int r = 0; r < C; ++r) {
+        for (int r = 1; r < 16; ++r) {
             float acc = 0.f;
 #pragma unroll
-            for (int m4 = 0; m4 < r; m4 += 4) {
-                const float4 b4 = ld4(sbm + r * CP + m4);
-                acc = fmaf(b4.x, x[m4], acc);
-                if (m4 + 1 < r) acc = fmaf(b4.y, x[m4 + 1], acc);
-                if (m4 + 2 < r) acc = fmaf(b4.z, x[m4 + 2], acc);
-                if (m4 + 3 < r) acc = fmaf(b4.w, x[m4 + 3], acc);
-            }
-            // rows above the lane's column stay zero: every x[m] they sum is zero
-            x[r] = r == s ? 1.f : -sbeta[r] * acc;
+            for (int q = 0; q < r; ++q) acc = fmaf(fb[r * CP + q], x[q], acc);
+            x[r] = (r == j ? 1.f : 0.f) - sbeta[16 * a + r] * acc;  // zero above the column
         }
 #pragma unroll
-        for (int r = 0; r < C; ++r) sli[r * CP + s] = x[r];
+        for (int r = 0; r < 16; ++r) sli[(16 * a + r) * CP + 16 * a + j] = x[r];
     }
     __syncthreads();
+#pragma unroll
+    for (int d = 1; d < 4; ++d) {
+        if (wave < 4 - d) {
+            const int a = wave + d, bb = a - d;
+            const float br = sbeta[16 * a + l];
+            floatx4 y = zero4();
+            for (int c = bb; c < a; ++c) {
+                const float4 f = ld4(sbm + (16 * a + l) * CP + 16 * c + 4 * g);
+                const int r0 = 16 * c + 4 * g;
+                const float4 lv = make_float4(sli[(r0 + 0) * CP + 16 * bb + l], sli[(r0 + 1) * CP + 16 * bb + l],
+                                              sli[(r0 + 2) * CP + 16 * bb + l], sli[(r0 + 3) * CP + 16 * bb + l]);
+                y = mma4(make_float4(br * f.x, br * f.y, br * f.z, br * f.w), lv, y);
+            }
+            const floatx4 z = mma4(ld4(sli + (16 * a + l) * CP + 16 * a + 4 * g), f4(y), zero4());
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sli[(16 * a + 4 * g + i) * CP + 16 * bb + l] = -z[i];
+        }
+        __syncthreads();
+    }
     for (int i = tid; i < C * C; i += NTT) pr[PR::LI + i] = sli[(i / C) * CP + (i % C)];
 
     // the products of the value (and key) columns c = 16 w + l; K-block t of a token
