@@ -71,17 +71,16 @@ __device__ __forceinline__ int64_t elem(const BwdParams& p, const ChunkPos& cp, 
     return ((cp.b * p.T + cp.t0 + r) * p.H + cp.h) * D + c;
 }
 
-// LDS of the sweep kernel (fp32 offsets): the chunk's W and K-bar (row pitch D + 4),
-// the 16 columns of its offset (b forwards, R backwards), Gamma_C, the state tile and
-// Y (row pitch 20).  The pitches put the four lane groups of an MFMA operand read on
-// disjoint banks.
+// LDS of the sweep kernel (fp32 offsets): two buffers of one chunk's W and K-bar (row
+// pitch D + 4), the state tile and Y (row pitch 20).  The pitches put the four lane
+// groups of an MFMA operand read on disjoint banks.
 template <int D>
 struct SweepLds {
     static constexpr int DP = D + 4, TP = 20;
-    static constexpr int W = 0, KBAR = C * DP, OFF = 2 * C * DP, GC = OFF + D * TP, ST = GC + D,
-                         Y = ST + D * TP, TOTAL = Y + C * TP;
+    static constexpr int W = 0, KBAR = C * DP, BUF = 2 * C * DP;  // within a buffer
+    static constexpr int ST = 2 * BUF, Y = ST + D * TP, TOTAL = Y + C * TP;
     static constexpr int NW4 = C * D / 4 / NT;    // float4 of W (and of K-bar) per thread
-    static constexpr int NO4 = D * TILE / 4 / NT; // float4 of the offset tile per thread
+    static_assert(TOTAL * 4 <= 160 * 1024, "sweep LDS");
 };
 
 // 16 k-steps of the fp32 MFMA: lane (m, g) gives A[m][k] and B[k][m] for
@@ -95,12 +94,17 @@ __device__ __forceinline__ floatx4 mma16x4(const float (&a)[4], const float (&b)
 // Forwards: S <- Diag(Gc) S - Kb^T (W S) + b; backwards: dS <- Diag(Gc) dS - W^T (Kb dS) + R.
 // One workgroup runs one direction.  Both products run on the fp32 MFMA: wave w
 // forms rows 16 w .. 16 w + 15 of Y, then row blocks w, w + 4, .. of the new state.
-// The record of the next chunk is read into registers while the current one is used.
+// Chunk i + 1's W and K-bar are staged into the other LDS buffer while chunk i's products
+// run (from registers loaded one chunk earlier), and each lane keeps the offset and
+// Gamma_C entries of its own state rows in registers, loaded two chunks ahead: two
+// barriers per chunk.  Loads past the last chunk repeat the last one (same bytes), so
+// that every chunk issues the same loads.
 template <int D>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void kda_bwd_sweep_kernel(BwdParams p) {
     using RC = Rec<D>;
     using L = SweepLds<D>;
     constexpr int DP = L::DP, TP = L::TP;
+    constexpr int RBW = D / 16 / (NT / 64);  // row blocks of the state per wave
     extern __shared__ __align__(16) float lds[];
     float* St = lds + L::ST;
     float* Y = lds + L::Y;
@@ -118,17 +122,21 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
     const int64_t bh = bid / tiles;
     const int col0 = (int)(bid - bh * tiles) * TILE;
     const int64_t DD = (int64_t)D * D;
-    const float* rec0 = p.trans + bh * p.NC * RC::SIZE;
+    const int64_t NC = p.NC;
+    const float* rec0 = p.trans + bh * NC * RC::SIZE;
+    const int64_t off_base = dir == 0 ? RC::BV : RC::R;
     const int lane = lane_id(), wave = wave_id();
     const int m = lane & 15, g = lane >> 4;
-    // the next chunk's W, K-bar, offset tile and Gamma_C, in registers
-    float4 rw[L::NW4], rk[L::NW4], ro[L::NO4];
-    float4 rg = make_float4(0.f, 0.f, 0.f, 0.f);
+    // the record of step i (chunk i forwards, NC - 1 - i backwards), clamped to the last step
+    auto rec = [&](int64_t i) __attribute__((always_inline)) {
+        i = i < NC - 1 ? i : NC - 1;
+        return rec0 + (dir == 0 ? i : NC - 1 - i) * RC::SIZE;
+    };
+    // W and K-bar of a later chunk, in registers until staged
+    float4 rw[L::NW4], rk[L::NW4];
 #pragma unroll
-    for (int i = 0; i < L::NW4; ++i) rw[i] = rk[i] = rg;
-#pragma unroll
-    for (int i = 0; i < L::NO4; ++i) ro[i] = rg;
-    auto fetch = [&](const float* tr, int64_t off_base) {
+    for (int i = 0; i < L::NW4; ++i) rw[i] = rk[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+    auto fetch_wk = [&](const float* tr) __attribute__((always_inline)) {
         const float4* w4 = reinterpret_cast<const float4*>(tr + RC::W);
         const float4* k4 = reinterpret_cast<const float4*>(tr + RC::KBAR);
 #pragma unroll
@@ -136,27 +144,98 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
             rw[i] = w4[threadIdx.x + i * NT];
             rk[i] = k4[threadIdx.x + i * NT];
         }
-#pragma unroll
-        for (int i = 0; i < L::NO4; ++i) {
-            const int q = threadIdx.x + i * NT;  // row q / 4, columns col0 + 4 (q % 4) ..
-            ro[i] = *reinterpret_cast<const float4*>(tr + off_base + (q >> 2) * D + col0 + 4 * (q & 3));
-        }
-        if (threadIdx.x < D / 4) rg = reinterpret_cast<const float4*>(tr + RC::GC)[threadIdx.x];
     };
-    auto stage = [&]() {
+    auto stage = [&](float* buf) __attribute__((always_inline)) {
 #pragma unroll
         for (int i = 0; i < L::NW4; ++i) {
             const int q = threadIdx.x + i * NT;  // row q / (D / 4), columns 4 (q % (D / 4)) ..
             const int at = (q / (D / 4)) * DP + 4 * (q % (D / 4));
-            *reinterpret_cast<float4*>(lds + L::W + at) = rw[i];
-            *reinterpret_cast<float4*>(lds + L::KBAR + at) = rk[i];
+            *reinterpret_cast<float4*>(buf + L::W + at) = rw[i];
+            *reinterpret_cast<float4*>(buf + L::KBAR + at) = rk[i];
+        }
+    };
+    // this lane's state rows 16 (wave + j (NT / 64)) + 4 g + r: offset (column col0 + m)
+    // and Gamma_C, in two register sets
+    float oA[RBW][4], gA[RBW][4], oB[RBW][4], gB[RBW][4];
+#pragma unroll
+    for (int j = 0; j < RBW; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) oA[j][r] = gA[j][r] = oB[j][r] = gB[j][r] = 0.f;
+    auto fetch_rows = [&](const float* tr, float (&o)[RBW][4], float (&gm)[RBW][4]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int j = 0; j < RBW; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = 16 * (wave + j * (NT / 64)) + 4 * g + r;
+                o[j][r] = tr[off_base + (int64_t)row * D + col0 + m];
+                gm[j][r] = tr[RC::GC + row];
+            }
+    };
+    // step i: the state of its chunk out, Y = A1 S, chunk i + 1 staged, the new state from
+    // the rows in (o, gm), which then take chunk i + 2's
+    auto step = [&](int64_t i, float (&o)[RBW][4], float (&gm)[RBW][4]) __attribute__((always_inline)) {
+        const int64_t n = dir == 0 ? i : NC - 1 - i;
+        const float* buf = lds + (i & 1) * L::BUF;
+        float* out = (dir == 0 ? p.states : p.dstates) + (bh * NC + n) * DD;
+        for (int idx = threadIdx.x; idx < D * TILE; idx += NT) {
+            const int c = idx / TILE, j = idx - c * TILE;
+            out[c * D + col0 + j] = St[c * TP + j];
+        }
+        // Y = W S (forwards) or Kb dS (backwards): wave w owns rows 16 w ..
+        const float* A1 = buf + (dir == 0 ? L::W : L::KBAR);
+        const float* A2 = buf + (dir == 0 ? L::KBAR : L::W);
+        {
+            // two accumulator chains (even and odd K-blocks), summed at the end
+            floatx4 acc0 = zero4(), acc1 = zero4();
+#pragma unroll
+            for (int kk = 0; kk < D / 16; ++kk) {
+                const int k0 = 16 * kk + 4 * g;
+                const float4 av = *reinterpret_cast<const float4*>(A1 + (16 * wave + m) * DP + k0);
+                const float a[4] = {av.x, av.y, av.z, av.w};
+                const float b[4] = {St[(k0 + 0) * TP + m], St[(k0 + 1) * TP + m], St[(k0 + 2) * TP + m],
+                                    St[(k0 + 3) * TP + m]};
+                if (kk & 1)
+                    acc1 = mma16x4(a, b, acc1);
+                else
+                    acc0 = mma16x4(a, b, acc0);
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) Y[(16 * wave + 4 * g + r) * TP + m] = acc0[r] + acc1[r];
+        }
+        // chunk i + 1 into the other buffer (read by step i - 1, which every wave has left),
+        // then chunk i + 2's W and K-bar into the registers
+        stage(lds + ((i + 1) & 1) * L::BUF);
+        fetch_wk(rec(i + 2));
+        __syncthreads();  // Y and the staged chunk are complete
+        // state <- Diag(Gc) state - A2^T Y + offset, row blocks wave, wave + 4, .. (their
+        // accumulator chains interleaved)
+        floatx4 acc[RBW];
+#pragma unroll
+        for (int j = 0; j < RBW; ++j) acc[j] = zero4();
+#pragma unroll
+        for (int kk = 0; kk < C / 16; ++kk) {
+            const int k0 = 16 * kk + 4 * g;
+            const float b[4] = {Y[(k0 + 0) * TP + m], Y[(k0 + 1) * TP + m], Y[(k0 + 2) * TP + m],
+                                Y[(k0 + 3) * TP + m]};
+#pragma unroll
+            for (int j = 0; j < RBW; ++j) {
+                const int rb = wave + j * (NT / 64);
+                const float a[4] = {A2[(k0 + 0) * DP + 16 * rb + m], A2[(k0 + 1) * DP + 16 * rb + m],
+                                    A2[(k0 + 2) * DP + 16 * rb + m], A2[(k0 + 3) * DP + 16 * rb + m]};
+                acc[j] = mma16x4(a, b, acc[j]);
+            }
         }
 #pragma unroll
-        for (int i = 0; i < L::NO4; ++i) {
-            const int q = threadIdx.x + i * NT;
-            *reinterpret_cast<float4*>(lds + L::OFF + (q >> 2) * TP + 4 * (q & 3)) = ro[i];
+        for (int j = 0; j < RBW; ++j) {
+            const int rb = wave + j * (NT / 64);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = 16 * rb + 4 * g + r;
+                St[row * TP + m] = gm[j][r] * St[row * TP + m] - acc[j][r] + o[j][r];
+            }
         }
-        if (threadIdx.x < D / 4) reinterpret_cast<float4*>(lds + L::GC)[threadIdx.x] = rg;
+        fetch_rows(rec(i + 2), o, gm);
+        __syncthreads();  // the new state is complete; buffer i % 2 is no longer read
     };
     {
         const float* init = dir == 0 ? p.s0 : p.dsT;
@@ -164,71 +243,20 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
             const int c = idx / TILE, j = idx - c * TILE;
             St[c * TP + j] = init ? init[bh * DD + c * D + col0 + j] : 0.f;
         }
-        const int64_t off_base = dir == 0 ? RC::BV : RC::R;
-        if (p.NC > 0) fetch(rec0 + (dir == 0 ? 0 : p.NC - 1) * RC::SIZE, off_base);
-        for (int64_t i = 0; i < p.NC; ++i) {
-            const int64_t n = dir == 0 ? i : p.NC - 1 - i;
-            __syncthreads();  // the previous chunk's operands are no longer read
-            stage();
-            __syncthreads();
-            if (i + 1 < p.NC) fetch(rec0 + (dir == 0 ? n + 1 : n - 1) * RC::SIZE, off_base);
-            float* out = (dir == 0 ? p.states : p.dstates) + (bh * p.NC + n) * DD;
-            for (int idx = threadIdx.x; idx < D * TILE; idx += NT) {
-                const int c = idx / TILE, j = idx - c * TILE;
-                out[c * D + col0 + j] = St[c * TP + j];
-            }
-            // Y = W S (forwards) or Kb dS (backwards): wave w owns rows 16 w ..
-            const float* A1 = lds + (dir == 0 ? L::W : L::KBAR);
-            const float* A2 = lds + (dir == 0 ? L::KBAR : L::W);
-            {
-                // two accumulator chains (even and odd K-blocks), summed at the end
-                floatx4 acc0 = zero4(), acc1 = zero4();
-#pragma unroll
-                for (int kk = 0; kk < D / 16; ++kk) {
-                    const int k0 = 16 * kk + 4 * g;
-                    const float4 av = *reinterpret_cast<const float4*>(A1 + (16 * wave + m) * DP + k0);
-                    const float a[4] = {av.x, av.y, av.z, av.w};
-                    const float b[4] = {St[(k0 + 0) * TP + m], St[(k0 + 1) * TP + m], St[(k0 + 2) * TP + m],
-                                        St[(k0 + 3) * TP + m]};
-                    if (kk & 1)
-                        acc1 = mma16x4(a, b, acc1);
-                    else
-                        acc0 = mma16x4(a, b, acc0);
-                }
-#pragma unroll
-                for (int r = 0; r < 4; ++r) Y[(16 * wave + 4 * g + r) * TP + m] = acc0[r] + acc1[r];
-            }
-            __syncthreads();
-            // state <- Diag(Gc) state - A2^T Y + offset, row blocks wave, wave + 4, .. (their
-            // accumulator chains interleaved)
-            constexpr int RBW = D / 16 / (NT / 64);  // row blocks per wave
-            floatx4 acc[RBW];
-#pragma unroll
-            for (int j = 0; j < RBW; ++j) acc[j] = zero4();
-#pragma unroll
-            for (int kk = 0; kk < C / 16; ++kk) {
-                const int k0 = 16 * kk + 4 * g;
-                const float b[4] = {Y[(k0 + 0) * TP + m], Y[(k0 + 1) * TP + m], Y[(k0 + 2) * TP + m],
-                                    Y[(k0 + 3) * TP + m]};
-#pragma unroll
-                for (int j = 0; j < RBW; ++j) {
-                    const int rb = wave + j * (NT / 64);
-                    const float a[4] = {A2[(k0 + 0) * DP + 16 * rb + m], A2[(k0 + 1) * DP + 16 * rb + m],
-                                        A2[(k0 + 2) * DP + 16 * rb + m], A2[(k0 + 3) * DP + 16 * rb + m]};
-                    acc[j] = mma16x4(a, b, acc[j]);
-                }
-            }
-#pragma unroll
-            for (int j = 0; j < RBW; ++j) {
-                const int rb = wave + j * (NT / 64);
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int row = 16 * rb + 4 * g + r;
-                    St[row * TP + m] = lds[L::GC + row] * St[row * TP + m] - acc[j][r] + lds[L::OFF + row * TP + m];
-                }
-            }
+        if (NC > 0) {
+            fetch_wk(rec(0));
+            stage(lds);
+            fetch_wk(rec(1));
+            fetch_rows(rec(0), oA, gA);
+            fetch_rows(rec(1), oB, gB);
         }
         __syncthreads();
+        int64_t i = 0;
+        for (; i + 2 <= NC; i += 2) {  // the register sets in turn
+            step(i, oA, gA);
+            step(i + 1, oB, gB);
+        }
+        if (i < NC) step(i, oA, gA);
     }
     if (dir == 1 && p.ds0) {
         for (int idx = threadIdx.x; idx < D * TILE; idx += NT) {
