@@ -684,11 +684,24 @@ __global__ __launch_bounds__(64 * (D / 16)) void kda_bwd_grad_kernel(BwdParams p
         dsb[t] = make_float4(dSC[(k0 + 0) * D + c], dSC[(k0 + 1) * D + c], dSC[(k0 + 2) * D + c],
                              dSC[(k0 + 3) * D + c]);
     }
-    // Li, P, beta; Kt and Qt
-    for (int i = tid; i < C * C; i += NTT) {
-        const int r = i / C, s = i - r * C;
-        rl[r * CP + s] = pr[PR::LI + i];
-        rp[r * CP + s] = pr[PR::PM + i];
+    // Li, P, beta; Kt and Qt (Li and P four neighbouring entries per thread and step,
+    // every load issued first)
+    {
+        constexpr int N4 = C * C / 4 / NTT;
+        static_assert(N4 * 4 * NTT == C * C, "Li and P in float4");
+        float4 li4[N4], pm4[N4];
+#pragma unroll
+        for (int u = 0; u < N4; ++u) {
+            const int i = 4 * (tid + u * NTT);
+            li4[u] = ld4(pr + PR::LI + i);
+            pm4[u] = ld4(pr + PR::PM + i);
+        }
+#pragma unroll
+        for (int u = 0; u < N4; ++u) {
+            const int i = 4 * (tid + u * NTT), r = i / C, s = i - r * C;
+            *reinterpret_cast<float4*>(rl + r * CP + s) = li4[u];
+            *reinterpret_cast<float4*>(rp + r * CP + s) = pm4[u];
+        }
     }
     if (tid < C)
         sbeta[tid] = tid < cp.L
@@ -979,14 +992,28 @@ __global__ __launch_bounds__(64 * (D / 16)) void kda_bwd_grad_kernel(BwdParams p
             st8(r < C / 2 ? rl + i : rq + (i - (C / 2) * D), q8[u]);
         }
     }
-    // dbeta = rowsum(dW X) + rowsum(dA Bm)
-    if (tid < C) {
-        const int r = tid;
+    // dbeta = rowsum(dW X) + rowsum(dA Bm): each row split over neighbouring threads, a
+    // slice of its columns each (dA and Bm are zero on and above the diagonal)
+    {
+        constexpr int TPR = NTT / C, SPAN = C / TPR;  // threads per row, columns per thread
+        static_assert(TPR * C == NTT && (TPR & (TPR - 1)) == 0 && SPAN % 4 == 0, "row split");
+        const int r = tid / TPR, s0 = (tid % TPR) * SPAN;
+        const float* bm = pr + PR::BM + r * C + s0;
         float acc = 0.f;
-        for (int w = 0; w < NW; ++w) acc += db1p[w * C + r];
-        const float* bm = pr + PR::BM + r * C;
-        for (int s = 0; s < r; ++s) acc = fmaf(rda[r * CP + s], bm[s], acc);
-        if (r < cp.L) p.dbeta[(cp.b * p.T + cp.t0 + r) * p.H + cp.h] = acc;
+#pragma unroll
+        for (int s4 = 0; s4 < SPAN; s4 += 4) {
+            const float4 b4 = ld4(bm + s4), d4 = ld4(rda + r * CP + s0 + s4);
+            acc = fmaf(d4.x, b4.x, acc);
+            acc = fmaf(d4.y, b4.y, acc);
+            acc = fmaf(d4.z, b4.z, acc);
+            acc = fmaf(d4.w, b4.w, acc);
+        }
+#pragma unroll
+        for (int m = 1; m < TPR; m <<= 1) acc += __shfl_xor(acc, m);
+        if (tid % TPR == 0) {
+            for (int w = 0; w < NW; ++w) acc += db1p[w * C + r];
+            if (r < cp.L) p.dbeta[(cp.b * p.T + cp.t0 + r) * p.H + cp.h] = acc;
+        }
     }
     __syncthreads();
     // pair terms over F = diag(beta) dA (strictly lower) and dP (lower), key channel c:
