@@ -294,12 +294,10 @@ __device__ __forceinline__ float4 mul4(const float4& a, const float4& b) {
 template <int D, class In>
 __device__ __forceinline__ void in8(const BwdParams& p, const ChunkPos& cp, const void* ptr, int r, int c8,
                                     float (&o)[8]) {
-    if (r >= cp.L) {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) o[j] = 0.f;
-        return;
-    }
-    const int64_t e = elem<D>(p, cp, r, c8);
+    // the load itself is unconditional (a row inside the sequence; cp.L >= 1), so that a
+    // run of them issues at once; rows past the end are zeroed afterwards
+    const bool in_seq = r < cp.L;
+    const int64_t e = elem<D>(p, cp, in_seq ? r : cp.L - 1, c8);
     if constexpr (sizeof(typename In::raw_t) == 2) {
         const uint4 w = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(ptr) + e);
         const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
@@ -313,6 +311,8 @@ __device__ __forceinline__ void in8(const BwdParams& p, const ChunkPos& cp, cons
         const float4 b = *reinterpret_cast<const float4*>(static_cast<const float*>(ptr) + e + 4);
         o[0] = a.x, o[1] = a.y, o[2] = a.z, o[3] = a.w, o[4] = b.x, o[5] = b.y, o[6] = b.z, o[7] = b.w;
     }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) o[j] = in_seq ? o[j] : 0.f;
 }
 __device__ __forceinline__ void st8(float* d, const float (&v)[8]) {
     *reinterpret_cast<float4*>(d) = make_float4(v[0], v[1], v[2], v[3]);
@@ -393,8 +393,11 @@ __global__ __launch_bounds__(64 * (D / 16)) void kda_bwd_chunk_kernel(BwdParams 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l = lane & 15, g = lane >> 4;
     float* pr = p.pairs + item * PR::SIZE;
     float* tr = p.trans + item * RC::SIZE;
+    // element (r, c) of a token tensor, zero past the sequence's end: the load itself is
+    // unconditional (from a row inside the sequence), so that a run of them issues at once
     auto in = [&](const void* ptr, int r, int c) -> float {
-        return r < cp.L ? In::load(static_cast<const raw*>(ptr), elem<D>(p, cp, r, c)) : 0.f;
+        const float x = In::load(static_cast<const raw*>(ptr), elem<D>(p, cp, r < cp.L ? r : cp.L - 1, c));
+        return r < cp.L ? x : 0.f;
     };
 
     // inputs; tokens past the sequence's end are identity steps (all zero, log alpha 0)
@@ -669,8 +672,11 @@ __global__ __launch_bounds__(64 * (D / 16)) void kda_bwd_grad_kernel(BwdParams p
     const float* gg = pr + PR::G;
     const float* S0 = p.states + item * DD;
     const float* dSC = p.dstates + item * DD;
+    // element (r, c) of a token tensor, zero past the sequence's end: the load itself is
+    // unconditional (from a row inside the sequence), so that a run of them issues at once
     auto in = [&](const void* ptr, int r, int c) -> float {
-        return r < cp.L ? In::load(static_cast<const raw*>(ptr), elem<D>(p, cp, r, c)) : 0.f;
+        const float x = In::load(static_cast<const raw*>(ptr), elem<D>(p, cp, r < cp.L ? r : cp.L - 1, c));
+        return r < cp.L ? x : 0.f;
     };
 
     const int c = 16 * wave + l;  // this wave's value column (and, later, key channel)
