@@ -756,8 +756,19 @@ __global__ __launch_bounds__(64 * (D / 16)) void kda_bwd_grad_kernel(BwdParams p
             dgcp[wave * D + k0 + 3] = v3;
         }
     }
-    // X = V - Kt S0, O = Qt S0
+    // X = V - Kt S0, O = Qt S0 (V, dY and Z of this wave's value column loaded first, ahead
+    // of the products and of the dZ stores)
     floatx4 X[4], O[4];
+    float vv[4][4], dyv[4][4], zv[4][4];
+#pragma unroll
+    for (int ma = 0; ma < 4; ++ma)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = 16 * ma + 4 * g + i;
+            vv[ma][i] = in(p.v, r, c);
+            dyv[ma][i] = in(p.dy, r, c);
+            zv[ma][i] = in(p.gate, r, c);
+        }
 #pragma unroll
     for (int ma = 0; ma < 4; ++ma) {
         floatx4 ax = zero4(), ao = zero4();
@@ -767,7 +778,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void kda_bwd_grad_kernel(BwdParams p
             ao = mma4(ld4(rb + (16 * ma + l) * DP + 16 * t + 4 * g), s0b[t], ao);
         }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) X[ma][i] = in(p.v, 16 * ma + 4 * g + i, c) - ax[i];
+        for (int i = 0; i < 4; ++i) X[ma][i] = vv[ma][i] - ax[i];
         O[ma] = ao;
     }
     // U = Li diag(beta) X;  O += P U
@@ -791,7 +802,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void kda_bwd_grad_kernel(BwdParams p
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int r = 16 * ma + 4 * g + i;
-            const float dy = in(p.dy, r, c), sz = sigmoidf_(in(p.gate, r, c));
+            const float dy = dyv[ma][i], sz = sigmoidf_(zv[ma][i]);
             dO[ma][i] = dy * sz;
             if (r < cp.L) p.dgate[elem<D>(p, cp, r, c)] = dy * O[ma][i] * sz * (1.f - sz);
         }
@@ -1143,6 +1154,14 @@ __global__ __launch_bounds__(64 * (D / 16)) void kda_bwd_grad_kernel(BwdParams p
         for (int w = 0; w < NW; ++w) dG += dgcp[w * D + c];
         dgc += dG * ex(gC);
     }
+    // log alpha as given (for the clamp's mask and the logits' derivative), every load issued
+    // ahead of the gradient's stores
+    const bool logits = PREP && p.logits;
+    float xla[4][4];
+#pragma unroll
+    for (int ma = 0; ma < 4; ++ma)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) xla[ma][i] = (p.clamp || logits) ? in(p.la, 16 * ma + 4 * g + i, c) : 0.f;
     // rows 16 ma + 4 g + i: suffix sums within the lane, then over the lane groups and blocks
     float tot[4];
 #pragma unroll
@@ -1167,9 +1186,8 @@ __global__ __launch_bounds__(64 * (D / 16)) void kda_bwd_grad_kernel(BwdParams p
             if (r < cp.L) {
                 const int64_t e = elem<D>(p, cp, r, c);
                 float d = dg[ma][i] + after_g + later;
-                const bool logits = PREP && p.logits;
                 if (p.clamp || logits) {
-                    const float x = In::load(static_cast<const raw*>(p.la), e);
+                    const float x = xla[ma][i];
                     const float lv = logits ? log_sigmoid(x) : x;  // log alpha before the clamp
                     if (p.clamp && !(lv >= kLogAlphaMin && lv <= 0.f)) d = 0.f;
                     if (logits) d *= sigmoidf_(-x);                 // d logsigmoid(x) / dx
