@@ -145,15 +145,17 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
             rk[i] = k4[threadIdx.x + i * NT];
         }
     };
+    auto stage_one = [&](float* buf, int i) __attribute__((always_inline)) {
+        const int q = threadIdx.x + i * NT;  // row q / (D / 4), columns 4 (q % (D / 4)) ..
+        const int at = (q / (D / 4)) * DP + 4 * (q % (D / 4));
+        *reinterpret_cast<float4*>(buf + L::W + at) = rw[i];
+        *reinterpret_cast<float4*>(buf + L::KBAR + at) = rk[i];
+    };
     auto stage = [&](float* buf) __attribute__((always_inline)) {
 #pragma unroll
-        for (int i = 0; i < L::NW4; ++i) {
-            const int q = threadIdx.x + i * NT;  // row q / (D / 4), columns 4 (q % (D / 4)) ..
-            const int at = (q / (D / 4)) * DP + 4 * (q % (D / 4));
-            *reinterpret_cast<float4*>(buf + L::W + at) = rw[i];
-            *reinterpret_cast<float4*>(buf + L::KBAR + at) = rk[i];
-        }
+        for (int i = 0; i < L::NW4; ++i) stage_one(buf, i);
     };
+    static_assert(L::NW4 == D / 16, "one staged pair of float4 per K-block of Y");
     // this lane's state rows 16 (wave + j (NT / 64)) + 4 g + r: offset (column col0 + m)
     // and Gamma_C, in two register sets
     float oA[RBW][4], gA[RBW][4], oB[RBW][4], gB[RBW][4];
@@ -184,6 +186,10 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
         // Y = W S (forwards) or Kb dS (backwards): wave w owns rows 16 w ..
         const float* A1 = buf + (dir == 0 ? L::W : L::KBAR);
         const float* A2 = buf + (dir == 0 ? L::KBAR : L::W);
+        // chunk i + 1 goes into the other buffer (read by step i - 1, which every wave has
+        // left), one piece after each K-block of Y so that the LDS stores run beside the MFMAs;
+        // then chunk i + 2's W and K-bar into the registers
+        float* nbuf = lds + ((i + 1) & 1) * L::BUF;
         {
             // two accumulator chains (even and odd K-blocks), summed at the end
             floatx4 acc0 = zero4(), acc1 = zero4();
@@ -198,13 +204,11 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
                     acc1 = mma16x4(a, b, acc1);
                 else
                     acc0 = mma16x4(a, b, acc0);
+                stage_one(nbuf, kk);
             }
 #pragma unroll
             for (int r = 0; r < 4; ++r) Y[(16 * wave + 4 * g + r) * TP + m] = acc0[r] + acc1[r];
         }
-        // chunk i + 1 into the other buffer (read by step i - 1, which every wave has left),
-        // then chunk i + 2's W and K-bar into the registers
-        stage(lds + ((i + 1) & 1) * L::BUF);
         fetch_wk(rec(i + 2));
         __syncthreads();  // Y and the staged chunk are complete
         // state <- Diag(Gc) state - A2^T Y + offset, row blocks wave, wave + 4, .. (their
