@@ -182,12 +182,17 @@ void kda_prep_kernel(PrepParams p) {
     const int c = tid % D, part = tid / D, r0 = part * TPT;
     float gl[TPT];
     {
-        float acc = 0.f;
+        // every load issued first, each from a token inside the sequence (T >= 1 here);
+        // tokens past the end count as zero
 #pragma unroll
         for (int j = 0; j < TPT; ++j) {
             const int64_t t = t0 + r0 + j;
-            float l = 0.f;
-            if (t < T) l = log_alpha_in(In::load(gla, row(t) * D + c), logits, clamp);
+            gl[j] = In::load(gla, row(t < T ? t : T - 1) * D + c);
+        }
+        float acc = 0.f;
+#pragma unroll
+        for (int j = 0; j < TPT; ++j) {
+            const float l = t0 + r0 + j < T ? log_alpha_in(gl[j], logits, clamp) : 0.f;
             acc += l * kLog2e;
             gl[j] = acc;
         }
@@ -217,13 +222,11 @@ void kda_prep_kernel(PrepParams p) {
         const int64_t t = t0 + r;
         const float mref = ML[(r >> 4) * D + c];
         const float F = fast_exp2(gl[j] - mref), G = fast_exp2(mref - gl[j]);
-        float kk = 0.f, qq = 0.f;
-        raw_t vv = In::from_float(0.f);
-        if (t < T) {
-            kk = In::load(gk, row(t) * D + c) * NS[C + r];
-            qq = In::load(gq, row(t) * D + c) * NS[r];
-            vv = gv[row(t) * D + c];
-        }
+        const int64_t tr = row(t < T ? t : T - 1) * D + c;  // a token inside the sequence
+        const float kl = In::load(gk, tr), ql = In::load(gq, tr);
+        const raw_t vl = gv[tr];
+        const float kk = t < T ? kl * NS[C + r] : 0.f, qq = t < T ? ql * NS[r] : 0.f;
+        const raw_t vv = t < T ? vl : In::from_float(0.f);
         XF[r * SX + c] = kk * F;
         XQ[r * SX + c] = qq * F;
         XG[r * SX + c] = kk * G;
@@ -557,6 +560,8 @@ void kda_recur_kernel(RecurParams p) {
     const raw_t* gz = static_cast<const raw_t*>(p.gate);
     typename Out::raw_t* gy = static_cast<typename Out::raw_t*>(p.out);
     uint4 reg[PER];
+#pragma unroll
+    for (int j = 0; j < PER; ++j) reg[j] = make_uint4(0u, 0u, 0u, 0u);
     if (NC > 0) {
         const uint4* src = reinterpret_cast<const uint4*>(cards);
 #pragma unroll
@@ -584,6 +589,16 @@ void kda_recur_kernel(RecurParams p) {
         const float* Gl = reinterpret_cast<const float*>(smem + buf * L::B_BUF + 2 * L::B_W + L::B_K);
         const op_t* card = reinterpret_cast<const op_t*>(cards + ci * CD::BYTES);
         const int64_t tbase = ci * C;
+        // this lane's gate logits of the chunk (rows 16 mt + 4 g4 + i, column col), loaded ahead
+        // of the products and of the output stores, each from a token inside the sequence
+        float zl[NMT][4];
+#pragma unroll
+        for (int mt = 0; mt < NMT; ++mt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int64_t t = tbase + 16 * mt + 4 * g4 + i;
+                zl[mt][i] = In::load(gz, ((b * T + (t < T ? t : T - 1)) * H + h) * D + col);
+            }
 
         floatx4 U[NMT];
         if constexpr (F32) {
@@ -609,7 +624,7 @@ void kda_recur_kernel(RecurParams p) {
                     const int64_t t = tbase + 16 * mt + 4 * g4 + i;
                     if (t < T) {
                         const int64_t gi = ((b * T + t) * H + h) * D + col;
-                        gy[gi] = Out::from_float((uov[i] + aq[i]) * sigmoidf_(In::load(gz, gi)));
+                        gy[gi] = Out::from_float((uov[i] + aq[i]) * sigmoidf_(zl[mt][i]));
                     }
                 }
             }
@@ -663,7 +678,7 @@ void kda_recur_kernel(RecurParams p) {
                     const int64_t t = tbase + 16 * mt + 4 * g4 + i;
                     if (t < T) {
                         const int64_t gi = ((b * T + t) * H + h) * D + col;
-                        gy[gi] = Out::from_float((static_cast<float>(uo[i]) + aq[i]) * sigmoidf_(In::load(gz, gi)));
+                        gy[gi] = Out::from_float((static_cast<float>(uo[i]) + aq[i]) * sigmoidf_(zl[mt][i]));
                     }
                 }
             }
