@@ -41,6 +41,14 @@ __global__ __launch_bounds__(256) void kda_decode_kernel(DecodeParams p) {
     const raw_t* q = static_cast<const raw_t*>(p.q);
     const raw_t* k = static_cast<const raw_t*>(p.k);
     const raw_t* la = static_cast<const raw_t*>(p.la);
+    // this thread's value-column inputs (tid < DV), loaded first so that their latency
+    // overlaps the state's
+    float vin = 0.f, zin = 0.f, bin = 0.f;
+    if (tid < DV) {
+        vin = In::load(static_cast<const raw_t*>(p.v), unit * DV + tid);
+        zin = In::load(static_cast<const raw_t*>(p.gate), unit * DV + tid);
+        bin = In::load(static_cast<const raw_t*>(p.beta), unit);
+    }
 
     if (tid < DK) {
         const float qv = In::load(q, unit * DK + tid), kv = In::load(k, unit * DK + tid);
@@ -111,12 +119,9 @@ __global__ __launch_bounds__(256) void kda_decode_kernel(DecodeParams p) {
         float r = 0.f, o = 0.f;
 #pragma unroll
         for (int g = 0; g < RG; ++g) { r += s_red_r[g][tid]; o += s_red_o[g][tid]; }
-        const raw_t* v = static_cast<const raw_t*>(p.v);
-        const raw_t* z = static_cast<const raw_t*>(p.gate);
-        const raw_t* bt = static_cast<const raw_t*>(p.beta);
-        const float u = In::load(bt, unit) * (In::load(v, unit * DV + tid) - r);
+        const float u = bin * (vin - r);
         s_u[tid] = u;
-        const float y = (o + s_qk * u) * sigmoidf_(In::load(z, unit * DV + tid));
+        const float y = (o + s_qk * u) * sigmoidf_(zin);
         static_cast<typename Out::raw_t*>(p.out)[unit * DV + tid] = Out::from_float(y);
     }
     __syncthreads();
