@@ -203,6 +203,28 @@ __device__ __forceinline__ half8 sel_operand(int cl, int lane) {
 // 32u + 16 half + 4g .. +3 of column 16 ct + n
 __device__ __forceinline__ constexpr int64_t frag_piece(int ct, int u, int hf) { return ((ct * 2 + u) * 2 + hf) * 512; }
 
+// 16 bytes of an input row; non-temporal with STREAM (below).
+template <bool STREAM>
+__device__ __forceinline__ u32x4 in_ld(const uint16_t* p) {
+    if constexpr (STREAM)
+        return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    else
+        return *reinterpret_cast<const u32x4*>(p);
+}
+
+// A card store.  STREAM (the pipelined pass, whose cards are read a whole piece later,
+// from other XCDs): the store is non-temporal, so the cards stream past the L2 rather than
+// evicting the lines the state pass running beside the card builder reuses.  Otherwise the
+// state pass reads the cards right after this launch and the ordinary policy keeps them
+// close.
+template <bool STREAM, class T>
+__device__ __forceinline__ void card_st(unsigned char* p, const T& v) {
+    if constexpr (STREAM)
+        __builtin_nontemporal_store(v, reinterpret_cast<T*>(p));
+    else
+        *reinterpret_cast<T*>(p) = v;
+}
+
 // ---------------------------------------------------------------------------
 // kernel 1: one update card per workgroup.  Wave A owns the 16-token tile A of the
 // chunk; everything that depends on A is resolved at compile time.
@@ -213,7 +235,7 @@ __device__ __forceinline__ constexpr int64_t frag_piece(int ct, int u, int hf) {
 // the tile start, so each of their factors spans at most eight tokens of decay and stays
 // finite down to about -11 nats per token (the clamp's floor keeps a whole tile within
 // 80.1 nats, so the default mode needs no such care).
-constexpr int kModeQkNorm = 1, kModeLogits = 2, kModeWide = 4;
+constexpr int kModeQkNorm = 1, kModeLogits = 2, kModeWide = 4, kModeStream = 8;
 
 // Where a card's tokens are: chunk n of a sequence of slen tokens starting at packed
 // row tb, head h; item is the card's index in the workspace.  Formed once per
@@ -246,9 +268,11 @@ __device__ __forceinline__ void prep_tile(const PrepParams& p, unsigned char* sm
     const bool clamp = p.clamp != 0;
     constexpr bool logits = (MODE & kModeLogits) != 0, qk_norm = (MODE & kModeQkNorm) != 0;
     constexpr bool wide = (MODE & kModeWide) != 0;
+    constexpr bool stream = (MODE & kModeStream) != 0;
 
     // raw inputs of token rl: per 32-channel block kb, the 8 bf16 channels 32 kb + 8 g4 .. +7
-    // (16 bytes; the four lane groups of a token cover 64 contiguous bytes of its row)
+    // (16 bytes; the four lane groups of a token cover 64 contiguous bytes of its row).
+    // STREAM: non-temporal loads, which leave the L2's lines to the state pass beside.
     u32x4 rq[KB], rk[KB], rv[KB], rla[KB];
     uint32_t rbeta;
     const int64_t item = cp.item, n = cp.n, h = cp.h, tb = cp.tb, slen = cp.slen;
@@ -265,10 +289,10 @@ __device__ __forceinline__ void prep_tile(const PrepParams& p, unsigned char* sm
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
             const int64_t off = row * D + 32 * kb + 8 * g4;
-            rla[kb] = *reinterpret_cast<const u32x4*>(gla + off);
-            rk[kb] = *reinterpret_cast<const u32x4*>(gk + off);
-            rq[kb] = *reinterpret_cast<const u32x4*>(gq + off);
-            rv[kb] = *reinterpret_cast<const u32x4*>(gv + off);
+            rla[kb] = in_ld<stream>(gla + off);
+            rk[kb] = in_ld<stream>(gk + off);
+            rq[kb] = in_ld<stream>(gq + off);
+            rv[kb] = in_ld<stream>(gv + off);
         }
     };
     auto elem = [](const u32x4 w, int j) -> float {  // bf16 element j of 8
@@ -404,7 +428,12 @@ __device__ __forceinline__ void prep_tile(const PrepParams& p, unsigned char* sm
             kbar[j] = static_cast<_Float16>(static_cast<float>(ke16[kb][j]) * eaft);  // Kbar = k 2^{g_C - g}
         }
         put_transposed(s_kf, kb, kt);
-        put_transposed(card + CD::KBT, kb, kbar);
+        {
+            const floatx4 t0 = mma_f16_k32(kbar, sel0, zero4());
+            const floatx4 t1 = mma_f16_k32(kbar, sel1, zero4());
+            card_st<stream>(card + CD::KBT + frag_piece(2 * kb, A >> 1, A & 1) + lane * 8, pack_h4(t0));
+            card_st<stream>(card + CD::KBT + frag_piece(2 * kb + 1, A >> 1, A & 1) + lane * 8, pack_h4(t1));
+        }
         // pairs (A, bb), bb < A: reference point at the end of tile A-1; both operands <= |k|
         float f[8];
 #pragma unroll
@@ -440,7 +469,7 @@ __device__ __forceinline__ void prep_tile(const PrepParams& p, unsigned char* sm
         float gm = 1.f;
 #pragma unroll
         for (int a2 = 0; a2 < NSUB; ++a2) gm *= s_etau[a2 * D + c];
-        reinterpret_cast<float*>(card + CD::GAM)[c] = gm;
+        card_st<stream>(card + CD::GAM + 4 * c, gm);
     }
     lds_barrier();  // (2) A, P, K~ fragments complete; KE fragments no longer needed
 
@@ -557,8 +586,8 @@ __device__ __forceinline__ void prep_tile(const PrepParams& p, unsigned char* sm
             w = mma_f16_k32(kf, ta[u], w);
             qm = mma_f16_k32(kf, ma[u], qm);
         }
-        *reinterpret_cast<half4*>(card + CD::UT + ((x * 4 + A) * 64 + lane) * 8) = pack_h4(ut);
-        *reinterpret_cast<half4*>(card + CD::UO + ((x * 4 + A) * 64 + lane) * 8) = pack_h4(uo);
+        card_st<stream>(card + CD::UT + ((x * 4 + A) * 64 + lane) * 8, pack_h4(ut));
+        card_st<stream>(card + CD::UO + ((x * 4 + A) * 64 + lane) * 8, pack_h4(uo));
         const int kb = x >> 1, cl = x & 1;
         const floatx4 q0 = mma_f16_k32(cl ? sel1 : sel0, q16[kb], zero4());  // Q~^T rows of this tile
 #pragma unroll
@@ -567,8 +596,8 @@ __device__ __forceinline__ void prep_tile(const PrepParams& p, unsigned char* sm
             qe[cl][i] = q0[i] - qm[i];
         }
         if (cl == 1) {
-            *reinterpret_cast<half8*>(card + CD::W + ((A * KB + kb) * 64 + lane) * 16) = pack_h8(wt[0], wt[1]);
-            *reinterpret_cast<half8*>(card + CD::QE + ((A * KB + kb) * 64 + lane) * 16) = pack_h8(qe[0], qe[1]);
+            card_st<stream>(card + CD::W + ((A * KB + kb) * 64 + lane) * 16, pack_h8(wt[0], wt[1]));
+            card_st<stream>(card + CD::QE + ((A * KB + kb) * 64 + lane) * 16, pack_h8(qe[0], qe[1]));
         }
     }
 }
@@ -1110,7 +1139,7 @@ void kda_piece64_kernel(PrepParams pp, RecurParams rp, int nstate) {
         const int64_t items = pp.B * pp.H * nl;
         int64_t item = 2 * ((int64_t)blockIdx.x - nstate) + half;
         item = item < items ? item : items - 1;  // an odd count: the last card twice, same bytes
-        prep64_card<D, 0>(pp, smem + half * PrepL<D>::TOTAL, item, wave_id() & 3);
+        prep64_card<D, kModeStream>(pp, smem + half * PrepL<D>::TOTAL, item, wave_id() & 3);
     }
 }
 
@@ -1317,7 +1346,7 @@ static hipError_t launch_pieces(const PrepParams& pp, const RecurParams& rp0, hi
     r.seg_len = NC;
     const int nstate = (int)((units * (D / 16) + 7) / 8 * 8);
     // piece 0's cards: the card builder alone, on every CU
-    auto k0 = kda_prep64_kernel<D, 0>;
+    auto k0 = kda_prep64_kernel<D, kModeStream>;
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k0), hipFuncAttributeMaxDynamicSharedMemorySize,
                                        (int)LP::TOTAL);
     if (e != hipSuccess) return e;
