@@ -194,13 +194,14 @@ def prefill_call(kda, wl):
 def prefill_kernel(wl) -> str:
     """The kernels one kda_chunk_fwd call of this workload launches.  Few long bf16
     sequences (at most 128 one-tile state-pass workgroups, at least 256 chunks) take
-    the pipelined pieces of 64 chunks."""
+    the pipelined pieces (of 128 chunks from 512 chunks on, else of 64)."""
     if wl.dtype != "bf16":
         return "kda_chunk_fwd = kda_prep_kernel + kda_recur_kernel (one call, two launches)"
     nc = (wl.T + 63) // 64
     if wl.Dk == 128 and wl.B * wl.H * (wl.Dk // 16) <= 128 and nc >= 256:
-        n = (nc + 63) // 64
-        return (f"kda_chunk_fwd in {n} pieces of 64 chunks = kda_prep64_kernel (piece 0's cards) + "
+        pl = 128 if nc >= 512 else 64
+        n = (nc + pl - 1) // pl
+        return (f"kda_chunk_fwd in {n} pieces of {pl} chunks = kda_prep64_kernel (piece 0's cards) + "
                 f"{n - 1} x kda_piece64_kernel (state pass over piece i beside the card builder of piece "
                 f"i + 1) + kda_rec64_kernel (last piece): one call, {n + 1} launches")
     return "kda_chunk_fwd = kda_prep64_kernel + kda_rec64_kernel (one call, two launches)"

@@ -1320,11 +1320,19 @@ int segments(int D, int64_t units, int64_t nc) {
 bool prefetch_cards(int64_t card_bytes) { return card_bytes >= KDA_PREFETCH_MIN_BYTES; }
 
 // Pipelined pass over few, long sequences: when the one-tile state pass leaves at least
-// half of the CUs idle, the sequence is cut into pieces of kPieceLen chunks and launch i
-// runs the state pass over piece i beside the card builder of piece i + 1 (pieces are
+// half of the CUs idle, the sequence is cut into pieces of piece_len() chunks and launch
+// i runs the state pass over piece i beside the card builder of piece i + 1 (pieces are
 // ordered by the stream alone).  The cards live in a ring of two pieces at the start of
-// the workspace, followed by the fp32 state carried from one piece to the next.
+// the workspace, followed by the fp32 state carried from one piece to the next.  Pieces
+// of 128 chunks where at least four fit (each launch boundary costs the state pass a
+// refill of its card pipeline), else of 64.  (Pieces that grow from a short first one
+// to a long last one, which runs without the card builder beside it, measured slower:
+// a launch whose card builder has more chunks than its state pass waits for the
+// builder, which runs at about 3/4 of the state pass's pace per chunk when the two
+// share the GPU.)
 constexpr int64_t kPieceLen = 64;
+
+int64_t piece_len(int64_t nc) { return nc >= 8 * kPieceLen ? 2 * kPieceLen : kPieceLen; }
 
 bool use_pieces(int D, int64_t units, int64_t nc) {
     return D == 128 && units * (D / 16) <= kSlots / 2 && nc >= 4 * kPieceLen;
@@ -1335,7 +1343,7 @@ static hipError_t launch_pieces(const PrepParams& pp, const RecurParams& rp0, hi
     using LP = PrepL<D>;
     using LR = RecL<D, 1>;
     using CD = Card<D>;
-    const int64_t units = rp0.B * rp0.H, NC = pp.NC, L = kPieceLen;
+    const int64_t units = rp0.B * rp0.H, NC = pp.NC, L = piece_len(NC);
     const int64_t npieces = (NC + L - 1) / L;
     float* carry = reinterpret_cast<float*>(static_cast<unsigned char*>(pp.ws) + 2 * units * L * CD::BYTES);
     PrepParams q = pp;

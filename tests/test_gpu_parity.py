@@ -222,21 +222,23 @@ def test_segment_scan_matches_oracle_and_single_pass(B, H, T, D):
     assert rel_err(y_s, y_1.double().cpu().numpy()) <= 2e-2
 
 
-def test_pipelined_pieces_ragged_with_state():
+@pytest.mark.parametrize("B, H, T", [(2, 6, 257 * 64 + 100), (1, 3, 520 * 64 + 30)])
+def test_pipelined_pieces_ragged_with_state(B, H, T):
     """Few, long sequences that leave half of the GPU to the card builder take the
-    pipelined pass (pieces of 64 chunks, the builder of piece i + 1 beside the state pass
-    of piece i, cards in a two-piece ring, the state carried between pieces): 258 chunks
-    in five pieces, the last with two chunks and a ragged tail, two batch rows, an
-    initial and a final state; against the oracle and the single pass of every chunk's
-    card at once (the variable-length call takes the unpipelined path)."""
-    wl = CONFIGS[2].scaled(B=2, H=6, T=257 * 64 + 100)
+    pipelined pass (the builder of piece i + 1 beside the state pass of piece i, cards in
+    a two-piece ring, the state carried between pieces): 259 chunks in pieces of 64 (the
+    last with two chunks and a ragged tail, two batch rows), and 521 chunks in pieces of
+    128 (the last with nine chunks and a ragged tail); an initial and a final state;
+    against the oracle and the single pass of every chunk's card at once (the
+    variable-length call takes the unpipelined path)."""
+    wl = CONFIGS[2].scaled(B=B, H=H, T=T)
     x = make_inputs(wl, seed=81)
-    say(f"[parity] pipelined pieces B2 H6 T{wl.T}")
+    say(f"[parity] pipelined pieces B{B} H{H} T{wl.T}")
     check(x, chunk=64, tag="pipelined pieces")
     d = dev(x)
     y, sT = kda().chunk_fwd(*(d[k] for k in KEYS), initial_state=d["initial_state"], output_final_state=True)
-    cu = torch.tensor([0, wl.T, 2 * wl.T], dtype=torch.int64, device="cuda:0")
-    flat = {k: d[k].reshape((2 * wl.T,) + tuple(d[k].shape[2:])) for k in KEYS}
+    cu = torch.arange(B + 1, dtype=torch.int64, device="cuda:0") * wl.T
+    flat = {k: d[k].reshape((B * wl.T,) + tuple(d[k].shape[2:])) for k in KEYS}
     yv, sv = kda().chunk_fwd_varlen(*(flat[k] for k in KEYS), cu, initial_state=d["initial_state"],
                                     output_final_state=True)[:2]
     torch.cuda.synchronize()
