@@ -23,7 +23,7 @@ import torch
 
 from . import _abi
 
-__all__ = ["chunk_fwd", "chunk_bwd", "chunk_fwd_varlen", "snapshot_slot", "chunk_summary", "combine_states", "decode_step", "workspace_bytes",
+__all__ = ["chunk_fwd", "chunk_bwd", "chunk_bwd_varlen", "chunk_fwd_varlen", "snapshot_slot", "chunk_summary", "combine_states", "decode_step", "workspace_bytes",
            "library_path", "KDAError"]
 
 
@@ -357,6 +357,69 @@ def chunk_bwd(q, k, v, log_alpha, beta, gate, d_out, initial_state=None, d_final
     rc = lib.kda_chunk_bwd(ctypes.byref(a), ctypes.c_void_p(stream))
     if rc != _abi.KDA_OK:
         raise KDAError(rc, "kda_chunk_bwd")
+    return g
+
+
+def chunk_bwd_varlen(q, k, v, log_alpha, beta, gate, d_out, cu_seqlens, initial_state=None,
+                     d_final_state=None, clamp=True, workspace=None, need_initial_state_grad=True,
+                     qk_norm=False, gate_logits=False):
+    """Gradients of ``sum(d_out * y) + sum(d_final_state * S_T)`` through
+    ``chunk_fwd_varlen`` (fp32 output, the same ``clamp``, ``qk_norm`` and
+    ``gate_logits``) on the current HIP stream, for N sequences packed along the rows:
+    q, k, log_alpha [rows, H, Dk], v, gate, d_out [rows, H, Dv], beta [rows, H] (fp32
+    or bf16, one dtype), sequence i being rows cu_seqlens[i] .. cu_seqlens[i+1] - 1
+    (int64 device tensor [N + 1]).  initial_state, d_final_state: fp32 [N, H, Dk, Dv]
+    or None.  Returns a dict of fp32 tensors: dq, dk, dlog_alpha [rows, H, Dk]; dv,
+    dgate [rows, H, Dv]; dbeta [rows, H] (zero on rows outside the sequences);
+    dinitial_state [N, H, Dk, Dv] (or None).
+    """
+    lib = _abi.load()
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("chunk_bwd_varlen needs GPU tensors (the HIP kernels are the only implementation)")
+    rows, H, Dk = q.shape
+    Dv = v.shape[-1]
+    if k.shape != q.shape or log_alpha.shape != q.shape or v.shape != (rows, H, Dv) or \
+            gate.shape != v.shape or d_out.shape != v.shape or beta.shape != (rows, H):
+        raise ValueError("q, k, log_alpha must be [rows, H, Dk], v, gate, d_out [rows, H, Dv], beta [rows, H]")
+    if cu_seqlens.dtype != torch.int64 or cu_seqlens.dim() != 1 or cu_seqlens.device != dev:
+        raise ValueError("cu_seqlens must be an int64 vector [N + 1] on the same GPU")
+    N = cu_seqlens.numel() - 1
+    code = _dtype_code(q)
+    for t in (k, v, log_alpha, beta, gate, d_out):
+        if t.dtype != q.dtype:
+            raise TypeError("q, k, v, log_alpha, beta, gate and d_out must share one dtype")
+    st_shape = (N, H, Dk, Dv)
+    for name, t in (("initial_state", initial_state), ("d_final_state", d_final_state)):
+        if t is not None and (t.dtype != torch.float32 or tuple(t.shape) != st_shape):
+            raise ValueError(f"{name} must be fp32 [N, H, Dk, Dv]")
+    a = _abi.BwdVarlenArgs()
+    a.N, a.rows, a.H, a.Dk, a.Dv, a.dtype = N, rows, H, Dk, Dv, code
+    a.flags = _prep_flags(clamp, qk_norm, gate_logits)
+    n = ctypes.c_size_t(0)
+    rc = lib.kda_chunk_bwd_varlen_workspace_size(ctypes.byref(a), ctypes.byref(n))
+    if rc != _abi.KDA_OK:
+        raise KDAError(rc, "kda_chunk_bwd_varlen_workspace_size")
+    if workspace is None or workspace.numel() < n.value:
+        workspace = torch.empty(max(int(n.value), 16), dtype=torch.uint8, device=dev)
+    f32 = dict(dtype=torch.float32, device=dev)
+    # zeros: rows outside the sequences are not written
+    g = dict(dq=torch.zeros((rows, H, Dk), **f32), dk=torch.zeros((rows, H, Dk), **f32),
+             dv=torch.zeros((rows, H, Dv), **f32), dlog_alpha=torch.zeros((rows, H, Dk), **f32),
+             dbeta=torch.zeros((rows, H), **f32), dgate=torch.zeros((rows, H, Dv), **f32),
+             dinitial_state=torch.empty(st_shape, **f32) if need_initial_state_grad else None)
+    _check_dev(dict(q=q, k=k, v=v, log_alpha=log_alpha, beta=beta, gate=gate, d_out=d_out,
+                    initial_state=initial_state, d_final_state=d_final_state, cu_seqlens=cu_seqlens), dev)
+    a.cu_seqlens = _ptr(cu_seqlens)
+    a.q, a.k, a.v, a.log_alpha, a.beta, a.gate = (_ptr(t) for t in (q, k, v, log_alpha, beta, gate))
+    a.d_out, a.initial_state, a.d_final_state = _ptr(d_out), _ptr(initial_state), _ptr(d_final_state)
+    a.dq, a.dk, a.dv, a.dlog_alpha = _ptr(g["dq"]), _ptr(g["dk"]), _ptr(g["dv"]), _ptr(g["dlog_alpha"])
+    a.dbeta, a.dgate, a.d_initial_state = _ptr(g["dbeta"]), _ptr(g["dgate"]), _ptr(g["dinitial_state"])
+    a.workspace, a.workspace_bytes = _ptr(workspace), workspace.numel()
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    rc = lib.kda_chunk_bwd_varlen(ctypes.byref(a), ctypes.c_void_p(stream))
+    if rc != _abi.KDA_OK:
+        raise KDAError(rc, "kda_chunk_bwd_varlen")
     return g
 
 

@@ -26,7 +26,9 @@ KDA_FLAG_CARDS_READY = 16
 # every extern "C" entry point of include/kda.h
 EXPORTS = ("kda_chunk_fwd_workspace_size", "kda_chunk_fwd", "kda_chunk_fwd_noalloc", "kda_chunk_fwd_varlen_workspace_size",
            "kda_chunk_fwd_varlen", "kda_chunk_summary",
-           "kda_combine_states", "kda_chunk_bwd_workspace_size", "kda_chunk_bwd", "kda_decode_step", "kda_status_str", "kda_version")
+           "kda_combine_states", "kda_chunk_bwd_workspace_size", "kda_chunk_bwd",
+           "kda_chunk_bwd_varlen_workspace_size", "kda_chunk_bwd_varlen", "kda_decode_step", "kda_status_str",
+           "kda_version")
 
 
 class FwdArgs(ctypes.Structure):
@@ -85,6 +87,23 @@ class BwdArgs(ctypes.Structure):
     ]
 
 
+class BwdVarlenArgs(ctypes.Structure):
+    _fields_ = [
+        ("N", ctypes.c_int64), ("rows", ctypes.c_int64), ("H", ctypes.c_int64),
+        ("Dk", ctypes.c_int64), ("Dv", ctypes.c_int64),
+        ("dtype", ctypes.c_int32), ("flags", ctypes.c_uint32),
+        ("cu_seqlens", ctypes.c_void_p),
+        ("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+        ("log_alpha", ctypes.c_void_p), ("beta", ctypes.c_void_p), ("gate", ctypes.c_void_p),
+        ("d_out", ctypes.c_void_p), ("initial_state", ctypes.c_void_p),
+        ("d_final_state", ctypes.c_void_p),
+        ("dq", ctypes.c_void_p), ("dk", ctypes.c_void_p), ("dv", ctypes.c_void_p),
+        ("dlog_alpha", ctypes.c_void_p), ("dbeta", ctypes.c_void_p), ("dgate", ctypes.c_void_p),
+        ("d_initial_state", ctypes.c_void_p), ("workspace", ctypes.c_void_p),
+        ("workspace_bytes", ctypes.c_size_t),
+    ]
+
+
 class DecodeArgs(ctypes.Structure):
     _fields_ = [
         ("B", ctypes.c_int64), ("H", ctypes.c_int64), ("Dk", ctypes.c_int64),
@@ -127,6 +146,11 @@ def load(path: str = LIB_PATH):
     lib.kda_chunk_bwd_workspace_size.restype = ctypes.c_int
     lib.kda_chunk_bwd.argtypes = [ctypes.POINTER(BwdArgs), ctypes.c_void_p]
     lib.kda_chunk_bwd.restype = ctypes.c_int
+    lib.kda_chunk_bwd_varlen_workspace_size.argtypes = [ctypes.POINTER(BwdVarlenArgs),
+                                                        ctypes.POINTER(ctypes.c_size_t)]
+    lib.kda_chunk_bwd_varlen_workspace_size.restype = ctypes.c_int
+    lib.kda_chunk_bwd_varlen.argtypes = [ctypes.POINTER(BwdVarlenArgs), ctypes.c_void_p]
+    lib.kda_chunk_bwd_varlen.restype = ctypes.c_int
     lib.kda_decode_step.argtypes = [ctypes.POINTER(DecodeArgs), ctypes.c_void_p]
     lib.kda_decode_step.restype = ctypes.c_int
     lib.kda_status_str.argtypes = [ctypes.c_int]

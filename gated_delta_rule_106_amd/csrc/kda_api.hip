@@ -137,6 +137,36 @@ int check_bwd(const kda_bwd_args* a, int64_t* nchunks, int64_t* ws_total) {
     return KDA_OK;
 }
 
+// Variable-length backward: sizes, dtype, head size and flags; the workspace layout (the
+// per-chunk sections for the most chunks the offsets can give, then the sequence map).
+struct BwdVarlenLayout {
+    int64_t max_chunks, off_s, off_co, off_soc, total;
+};
+
+int check_bwd_varlen(const kda_bwd_varlen_args* a, BwdVarlenLayout* L) {
+    if (!a) return KDA_ERR_NULL;
+    if (a->N < 0 || a->rows < 0 || a->H < 0 || a->Dk <= 0 || a->Dv <= 0) return KDA_ERR_SHAPE;
+    if (a->dtype != KDA_F32 && a->dtype != KDA_BF16) return KDA_ERR_UNSUPPORTED;
+    if (a->Dk != a->Dv || (a->Dk != 64 && a->Dk != 128)) return KDA_ERR_UNSUPPORTED;
+    if ((a->flags & ~(KDA_FLAG_NO_CLAMP | KDA_FLAG_QK_L2NORM | KDA_FLAG_GATE_LOGITS)) != 0)
+        return KDA_ERR_UNSUPPORTED;
+    int64_t elems, nh, st, items, tmp;
+    if (!mul_ok(a->rows, a->H, &elems) || !mul_ok(elems, a->Dk, &elems) || !mul_ok(a->N, a->H, &nh) ||
+        !mul_ok(nh, a->Dk * a->Dv, &st))
+        return KDA_ERR_SHAPE;
+    if (a->N >= INT32_MAX || nh > INT_MAX / 16) return KDA_ERR_SHAPE;  // sequence ids; sweep grid
+    const int64_t mc = kda::varlen_max_chunks(a->N, a->rows, 64);
+    // per chunk: the two records and two states stay below 1 MiB; one workgroup per chunk
+    if (!mul_ok(mc, a->H, &items) || !mul_ok(items, (int64_t)1 << 20, &tmp) || items > INT_MAX)
+        return KDA_ERR_SHAPE;
+    L->max_chunks = mc;
+    L->off_s = kda::bwd_workspace_bytes((int)a->Dk, a->H, mc);
+    L->off_co = L->off_s + align256((a->N + 1) * 8);
+    L->off_soc = L->off_co + align256((a->N + 1) * 8);
+    L->total = L->off_soc + align256(mc * 4);
+    return KDA_OK;
+}
+
 // Token tensors present and aligned, states aligned (after check_shape).
 int check_fwd_tensors(const kda_fwd_args* a) {
     if (a->B * a->T * a->H > 0) {
@@ -427,6 +457,59 @@ int kda_chunk_bwd(const kda_bwd_args* a, hipStream_t stream) {
     p.logits = (a->flags & KDA_FLAG_GATE_LOGITS) ? 1 : 0;
     kda::bwd_layout((int)a->Dk, a->B * a->H, nc, a->workspace, p);
     const hipError_t e = kda::launch_bwd(a->dtype == KDA_BF16, (int)a->Dk, p, stream);
+    return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+int kda_chunk_bwd_varlen_workspace_size(const kda_bwd_varlen_args* a, size_t* bytes) {
+    if (!a || !bytes) return KDA_ERR_NULL;
+    BwdVarlenLayout L;
+    const int st = check_bwd_varlen(a, &L);
+    if (st != KDA_OK) return st;
+    *bytes = (size_t)L.total;
+    return KDA_OK;
+}
+
+int kda_chunk_bwd_varlen(const kda_bwd_varlen_args* a, hipStream_t stream) {
+    BwdVarlenLayout L;
+    const int st = check_bwd_varlen(a, &L);
+    if (st != KDA_OK) return st;
+    if (a->N == 0 || a->H == 0) return KDA_OK;
+    if (!a->cu_seqlens) return KDA_ERR_NULL;
+    if ((reinterpret_cast<uintptr_t>(a->cu_seqlens) & 7u) != 0) return KDA_ERR_ALIGN;
+    const bool has_rows = a->rows > 0;
+    if (has_rows) {
+        const void* req[] = {a->q, a->k, a->v, a->log_alpha, a->beta, a->gate, a->d_out,
+                             a->dq, a->dk, a->dv, a->dlog_alpha, a->dbeta, a->dgate};
+        for (const void* p : req)
+            if (!p) return KDA_ERR_NULL;
+        for (const void* p : req)
+            if (!aligned16(p)) return KDA_ERR_ALIGN;
+    }
+    if (!aligned16(a->initial_state) || !aligned16(a->d_final_state) || !aligned16(a->d_initial_state))
+        return KDA_ERR_ALIGN;
+    if (!has_rows && !a->d_initial_state) return KDA_OK;
+    if (!a->workspace || (int64_t)a->workspace_bytes < L.total) return KDA_ERR_WORKSPACE;
+    if (!aligned16(a->workspace)) return KDA_ERR_ALIGN;
+    unsigned char* ws = static_cast<unsigned char*>(a->workspace);
+    kda::VarlenMap m{reinterpret_cast<int64_t*>(ws + L.off_s), reinterpret_cast<int64_t*>(ws + L.off_co),
+                     reinterpret_cast<int32_t*>(ws + L.off_soc)};
+    hipError_t e = kda::launch_varlen_map(m, a->cu_seqlens, a->N, a->rows, 64, stream);
+    if (e != hipSuccess) return KDA_ERR_HIP;
+    kda::BwdParams p{a->q, a->k, a->v, a->log_alpha, a->beta, a->gate, a->d_out,
+                     a->initial_state, a->d_final_state, a->dq, a->dk, a->dv, a->dlog_alpha,
+                     a->dbeta, a->dgate, a->d_initial_state};
+    p.B = a->N;
+    p.T = a->rows;
+    p.H = a->H;
+    p.NC = L.max_chunks;
+    p.vs = m.s;
+    p.vco = m.co;
+    p.vsoc = m.soc;
+    p.clamp = (a->flags & KDA_FLAG_NO_CLAMP) ? 0 : 1;
+    p.qk_norm = (a->flags & KDA_FLAG_QK_L2NORM) ? 1 : 0;
+    p.logits = (a->flags & KDA_FLAG_GATE_LOGITS) ? 1 : 0;
+    kda::bwd_layout((int)a->Dk, a->H, L.max_chunks, a->workspace, p);
+    e = kda::launch_bwd(a->dtype == KDA_BF16, (int)a->Dk, p, stream);
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 

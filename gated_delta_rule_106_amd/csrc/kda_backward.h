@@ -28,7 +28,13 @@ struct BwdParams {
     float* states;     // per chunk: the state at the chunk's start
     float* dstates;    // per chunk: the gradient of the state at the chunk's end
     int64_t B, T, H;
-    int64_t NC;        // chunks per sequence
+    int64_t NC;        // chunks per sequence (variable-length: the most the offsets can give)
+    // variable-length batch (NULL: B sequences of T tokens): the sequence map of
+    // kda_varlen.h, B = N sequences over T packed rows.  Chunk n of sequence i, head h
+    // is item (co_i + n) H + h of the per-chunk sections; NC H items in all.
+    const int64_t* vs;
+    const int64_t* vco;
+    const int32_t* vsoc;
     int clamp;
     int qk_norm;       // q, k are raw: the gradients are taken through k / |k|, q / (|q| sqrt(D))
     int logits;        // la holds forget-gate logits: log alpha = logsigmoid(la)

@@ -52,23 +52,39 @@ struct Rec {
 };
 
 struct ChunkPos {
-    int64_t b, h, t0;
-    int L;  // tokens of the chunk inside the sequence (the rest is padding)
+    int64_t row0, h;  // packed row of the chunk's first token; head
+    int L;  // tokens of the chunk inside the sequence (the rest is padding); 0: no chunk
 };
 
+// Where chunk item `item` is: B sequences of T tokens (item (b H + h) NC + n), or a
+// variable-length batch (item g H + h for the batch's chunk g; past the last chunk the
+// item has none, L = 0, and its workgroup leaves at once).
 __device__ __forceinline__ ChunkPos chunk_pos(const BwdParams& p, int64_t item) {
     ChunkPos cp;
-    const int64_t bh = item / p.NC, n = item - bh * p.NC;
-    cp.b = bh / p.H;
-    cp.h = bh - cp.b * p.H;
-    cp.t0 = n * C;
-    cp.L = (int)(p.T - cp.t0 < C ? p.T - cp.t0 : C);
+    if (p.vs) {
+        const int64_t g = item / p.H;
+        cp.h = item - g * p.H;
+        cp.row0 = 0;
+        cp.L = 0;
+        if (g < p.vco[p.B]) {
+            const int64_t i = p.vsoc[g];
+            cp.row0 = p.vs[i] + (g - p.vco[i]) * C;
+            const int64_t left = p.vs[i + 1] - cp.row0;  // >= 1: the sequence owns this chunk
+            cp.L = (int)(left < C ? left : C);
+        }
+    } else {
+        const int64_t bh = item / p.NC, n = item - bh * p.NC;
+        const int64_t b = bh / p.H;
+        cp.h = bh - b * p.H;
+        cp.row0 = b * p.T + n * C;
+        cp.L = (int)(p.T - n * C < C ? p.T - n * C : C);
+    }
     return cp;
 }
 
 template <int D>
 __device__ __forceinline__ int64_t elem(const BwdParams& p, const ChunkPos& cp, int r, int c) {
-    return ((cp.b * p.T + cp.t0 + r) * p.H + cp.h) * D + c;
+    return ((cp.row0 + r) * p.H + cp.h) * D + c;
 }
 
 // LDS of the sweep kernel (fp32 offsets): two buffers of one chunk's W and K-bar (row
@@ -122,15 +138,26 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
     const int64_t bh = bid / tiles;
     const int col0 = (int)(bid - bh * tiles) * TILE;
     const int64_t DD = (int64_t)D * D;
-    const int64_t NC = p.NC;
-    const float* rec0 = p.trans + bh * NC * RC::SIZE;
+    // the NC chunks of this (b, h): chunk n is item cbase + n cstride (its records and
+    // states); B sequences of T tokens, or sequence bh / H of a variable-length batch
+    int64_t NC, cbase, cstride;
+    if (p.vs) {
+        const int64_t i = bh / p.H;
+        NC = p.vco[i + 1] - p.vco[i];
+        cbase = p.vco[i] * p.H + (bh - i * p.H);
+        cstride = p.H;
+    } else {
+        NC = p.NC;
+        cbase = bh * NC;
+        cstride = 1;
+    }
     const int64_t off_base = dir == 0 ? RC::BV : RC::R;
     const int lane = lane_id(), wave = wave_id();
     const int m = lane & 15, g = lane >> 4;
     // the record of step i (chunk i forwards, NC - 1 - i backwards), clamped to the last step
     auto rec = [&](int64_t i) __attribute__((always_inline)) {
         i = i < NC - 1 ? i : NC - 1;
-        return rec0 + (dir == 0 ? i : NC - 1 - i) * RC::SIZE;
+        return p.trans + (cbase + (dir == 0 ? i : NC - 1 - i) * cstride) * RC::SIZE;
     };
     // W and K-bar of a later chunk, in registers until staged
     float4 rw[L::NW4], rk[L::NW4];
@@ -178,7 +205,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
     auto step = [&](int64_t i, float (&o)[RBW][4], float (&gm)[RBW][4]) __attribute__((always_inline)) {
         const int64_t n = dir == 0 ? i : NC - 1 - i;
         const float* buf = lds + (i & 1) * L::BUF;
-        float* out = (dir == 0 ? p.states : p.dstates) + (bh * NC + n) * DD;
+        float* out = (dir == 0 ? p.states : p.dstates) + (cbase + n * cstride) * DD;
         for (int idx = threadIdx.x; idx < D * TILE; idx += NT) {
             const int c = idx / TILE, j = idx - c * TILE;
             out[c * D + col0 + j] = St[c * TP + j];
@@ -394,6 +421,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void kda_bwd_chunk_kernel(BwdParams 
     float* sbeta = lds + L::BETA;
     const int64_t item = blockIdx.x;
     const ChunkPos cp = chunk_pos(p, item);
+    if (cp.L == 0) return;  // no chunk here (the whole workgroup leaves)
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l = lane & 15, g = lane >> 4;
     float* pr = p.pairs + item * PR::SIZE;
     float* tr = p.trans + item * RC::SIZE;
@@ -434,7 +462,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void kda_bwd_chunk_kernel(BwdParams 
     }
     if (tid < C)
         sbeta[tid] = tid < cp.L
-                         ? In::load(static_cast<const raw*>(p.beta), (cp.b * p.T + cp.t0 + tid) * p.H + cp.h)
+                         ? In::load(static_cast<const raw*>(p.beta), (cp.row0 + tid) * p.H + cp.h)
                          : 0.f;
     __syncthreads();
     if (tid < D) {  // g: inclusive cumulative sum over the chunk per key channel
@@ -670,6 +698,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void kda_bwd_grad_kernel(BwdParams p
     float* sclk = sclq + C;
     const int64_t item = blockIdx.x;
     const ChunkPos cp = chunk_pos(p, item);
+    if (cp.L == 0) return;  // no chunk here (the whole workgroup leaves)
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l = lane & 15, g = lane >> 4;
     const int64_t DD = (int64_t)D * D;
     const float* pr = p.pairs + item * PR::SIZE;
@@ -715,7 +744,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void kda_bwd_grad_kernel(BwdParams p
     }
     if (tid < C)
         sbeta[tid] = tid < cp.L
-                         ? In::load(static_cast<const raw*>(p.beta), (cp.b * p.T + cp.t0 + tid) * p.H + cp.h)
+                         ? In::load(static_cast<const raw*>(p.beta), (cp.row0 + tid) * p.H + cp.h)
                          : 0.f;
     constexpr int G8 = C * D / 8 / NTT;
     static_assert(G8 * 8 * NTT == C * D, "groups of eight");
@@ -1033,7 +1062,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void kda_bwd_grad_kernel(BwdParams p
         for (int m = 1; m < TPR; m <<= 1) acc += __shfl_xor(acc, m);
         if (tid % TPR == 0) {
             for (int w = 0; w < NW; ++w) acc += db1p[w * C + r];
-            if (r < cp.L) p.dbeta[(cp.b * p.T + cp.t0 + r) * p.H + cp.h] = acc;
+            if (r < cp.L) p.dbeta[(cp.row0 + r) * p.H + cp.h] = acc;
         }
     }
     __syncthreads();
@@ -1252,7 +1281,7 @@ int64_t section_bytes(int64_t bh, int64_t nc, int64_t* trans, int64_t* pairs, in
 
 template <int D, class In, bool PREP>
 hipError_t launch_d(const BwdParams& p, hipStream_t stream) {
-    const int64_t items = p.B * p.H * p.NC;
+    const int64_t items = p.vs ? p.NC * p.H : p.B * p.H * p.NC;  // one workgroup per chunk item
     constexpr int NTC = 64 * (D / 16);
     if (items > 0) {
         auto kc = kda_bwd_chunk_kernel<D, In, PREP>;

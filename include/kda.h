@@ -67,7 +67,7 @@
 extern "C" {
 #endif
 
-#define KDA_VERSION 4
+#define KDA_VERSION 5
 
 /* element types */
 #define KDA_F32 0  /* IEEE binary32 */
@@ -352,6 +352,60 @@ typedef struct kda_bwd_args {
 int kda_chunk_bwd_workspace_size(const kda_bwd_args *a, size_t *bytes);
 /* Chunkwise backward pass.  Returns a status. */
 int kda_chunk_bwd(const kda_bwd_args *a, hipStream_t stream);
+
+/*
+ * Backward pass of a variable-length batch: the gradients of
+ *   L = sum(d_out * out) + sum_i sum(d_final_state[i] * S_T(i))
+ * through what kda_chunk_fwd_varlen computes (fp32 out, the same flags), for N
+ * independent sequences packed along the rows (the layout, cu_seqlens and its
+ * sanitising as in kda_varlen_args; the per-sequence reverse mode as in
+ * kda_chunk_bwd: page "3T models are no longer magic", section "Gate 1: KDA makes
+ * it computable", over the chunk-recurrent form of page "Kimi K3 report
+ * walk-through", section "Compute paradigm").  Every sequence starts its own
+ * chunks, so no chunk spans two sequences.
+ *   q, k, v, log_alpha, beta, gate, d_out: [rows, H, D] ([rows, H] for beta), all of
+ *     `dtype` (fp32 or bf16).
+ *   initial_state, d_final_state: fp32 [N, H, Dk, Dv] or NULL (zeros).
+ *   dq, dk, dlog_alpha: fp32 [rows, H, Dk]; dv, dgate: fp32 [rows, H, Dv]; dbeta:
+ *     fp32 [rows, H]; all required when rows * H > 0.  Rows outside the sanitised
+ *     sequences are not written.
+ *   d_initial_state: fp32 [N, H, Dk, Dv] or NULL (not returned).  An empty sequence
+ *     passes d_final_state through unchanged.
+ *   flags: as in kda_chunk_bwd.  Dk == Dv in {64, 128}.
+ *   workspace: at least kda_chunk_bwd_varlen_workspace_size bytes (a function of N,
+ *     rows, H and Dk), 256-byte aligned: kda_chunk_bwd's per-chunk sections for
+ *     ceil(rows / 64) + N chunks per head, then the sequence map.
+ * No output may overlap an input or another output.
+ */
+typedef struct kda_bwd_varlen_args {
+    int64_t N, rows, H, Dk, Dv;
+    int32_t dtype;  /* q, k, v, log_alpha, beta, gate, d_out */
+    uint32_t flags;
+    const int64_t *cu_seqlens;
+    const void *q;
+    const void *k;
+    const void *v;
+    const void *log_alpha;
+    const void *beta;
+    const void *gate;
+    const void *d_out;
+    const float *initial_state;
+    const float *d_final_state;
+    float *dq;
+    float *dk;
+    float *dv;
+    float *dlog_alpha;
+    float *dbeta;
+    float *dgate;
+    float *d_initial_state;
+    void *workspace;
+    size_t workspace_bytes;
+} kda_bwd_varlen_args;
+
+/* Workspace bytes kda_chunk_bwd_varlen needs (host only).  Returns a status. */
+int kda_chunk_bwd_varlen_workspace_size(const kda_bwd_varlen_args *a, size_t *bytes);
+/* Backward pass of a variable-length batch.  Returns a status. */
+int kda_chunk_bwd_varlen(const kda_bwd_varlen_args *a, hipStream_t stream);
 
 /*
  * Arguments of kda_decode_step: one token per (b, h).

@@ -36,7 +36,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.kda_version() == 4
+    assert lib.kda_version() == 5
     for code in range(-7, 1):
         assert lib.kda_status_str(code).decode()
     assert lib.kda_status_str(12345).decode() == "unknown status"
@@ -56,9 +56,12 @@ int main(void) {
          offsetof(kda_combine_args, final_state));
   printf("%zu %zu %zu %zu ", sizeof(kda_varlen_args), offsetof(kda_varlen_args, cu_seqlens),
          offsetof(kda_varlen_args, snapshot_every), offsetof(kda_varlen_args, workspace_bytes));
-  printf("%zu %zu %zu %zu %zu\n", sizeof(kda_bwd_args), offsetof(kda_bwd_args, q),
+  printf("%zu %zu %zu %zu %zu ", sizeof(kda_bwd_args), offsetof(kda_bwd_args, q),
          offsetof(kda_bwd_args, d_final_state), offsetof(kda_bwd_args, d_initial_state),
          offsetof(kda_bwd_args, workspace_bytes));
+  printf("%zu %zu %zu %zu %zu %zu\n", sizeof(kda_bwd_varlen_args), offsetof(kda_bwd_varlen_args, cu_seqlens),
+         offsetof(kda_bwd_varlen_args, q), offsetof(kda_bwd_varlen_args, d_final_state),
+         offsetof(kda_bwd_varlen_args, d_initial_state), offsetof(kda_bwd_varlen_args, workspace_bytes));
   return 0;
 }''')
     exe = tmp_path / "layout"
@@ -73,7 +76,10 @@ int main(void) {
             ctypes.sizeof(_abi.VarlenArgs), _abi.VarlenArgs.cu_seqlens.offset,
             _abi.VarlenArgs.snapshot_every.offset, _abi.VarlenArgs.workspace_bytes.offset,
             ctypes.sizeof(_abi.BwdArgs), _abi.BwdArgs.q.offset, _abi.BwdArgs.d_final_state.offset,
-            _abi.BwdArgs.d_initial_state.offset, _abi.BwdArgs.workspace_bytes.offset]
+            _abi.BwdArgs.d_initial_state.offset, _abi.BwdArgs.workspace_bytes.offset,
+            ctypes.sizeof(_abi.BwdVarlenArgs), _abi.BwdVarlenArgs.cu_seqlens.offset, _abi.BwdVarlenArgs.q.offset,
+            _abi.BwdVarlenArgs.d_final_state.offset, _abi.BwdVarlenArgs.d_initial_state.offset,
+            _abi.BwdVarlenArgs.workspace_bytes.offset]
     assert got == want
 
 
@@ -354,6 +360,9 @@ def test_binding_refuses_cpu_tensors():
         kda.combine_states(torch.zeros(2, 1, 1, 64, 64), torch.zeros(2, 1, 1, 64, 64))
     with pytest.raises(ValueError):
         kda.chunk_bwd(x, x, x, x, torch.zeros(1, 16, 1), x, x)
+    with pytest.raises(ValueError):
+        kda.chunk_bwd_varlen(x[0], x[0], x[0], x[0], torch.zeros(16, 1), x[0], x[0],
+                             torch.tensor([0, 16], dtype=torch.int64))
 
 
 def _good_bwd(B=1, T=100, H=2, D=128):
@@ -409,3 +418,60 @@ def test_bwd_validation(lib, mutate, code):
     mutate(a)
     assert lib.kda_chunk_bwd(ctypes.byref(a), None) == code
     assert lib.kda_chunk_bwd(None, None) == _abi.KDA_ERR_NULL
+
+
+def _good_bwd_var(N=3, rows=1000, H=2, D=128):
+    a = _abi.BwdVarlenArgs()
+    a.N, a.rows, a.H, a.Dk, a.Dv, a.dtype = N, rows, H, D, D, _abi.KDA_BF16
+    for i, name in enumerate(("cu_seqlens", "q", "k", "v", "log_alpha", "beta", "gate", "d_out", "dq", "dk", "dv",
+                              "dlog_alpha", "dbeta", "dgate")):
+        setattr(a, name, 0x100000 * (i + 1))
+    return a
+
+
+def test_bwd_varlen_workspace_size(lib):
+    """The backward's per-chunk sections for the most chunks any offsets can give
+    (ceil(rows / 64) + N per head), then the sequence map: N + 1 starts, N + 1 chunk
+    offsets (int64) and a sequence index per chunk (int32), each rounded up to 256 bytes."""
+    r256 = lambda x: (x + 255) // 256 * 256
+    for N, rows, H, D in ((3, 1000, 2, 128), (1, 64, 3, 64), (5, 0, 1, 64)):
+        a = _good_bwd_var(N, rows, H, D)
+        n = ctypes.c_size_t(0)
+        assert lib.kda_chunk_bwd_varlen_workspace_size(ctypes.byref(a), ctypes.byref(n)) == _abi.KDA_OK
+        chunks = (rows + 63) // 64 + N
+        items = H * chunks
+        rec = 2 * 64 * D + 2 * D * D + D
+        pairs = 64 * D + 3 * 64 * 64
+        want = r256(items * rec * 4) + r256(items * pairs * 4) + 2 * r256(items * D * D * 4)
+        want += 2 * r256((N + 1) * 8) + r256(chunks * 4)
+        assert n.value == want
+    assert lib.kda_chunk_bwd_varlen_workspace_size(None, ctypes.byref(n)) == _abi.KDA_ERR_NULL
+
+
+@pytest.mark.parametrize("mutate,code", [
+    (lambda a: setattr(a, "N", -1), _abi.KDA_ERR_SHAPE),
+    (lambda a: setattr(a, "rows", -1), _abi.KDA_ERR_SHAPE),
+    (lambda a: setattr(a, "rows", 2 ** 62), _abi.KDA_ERR_SHAPE),
+    (lambda a: setattr(a, "dtype", 7), _abi.KDA_ERR_UNSUPPORTED),
+    (lambda a: setattr(a, "Dv", 64), _abi.KDA_ERR_UNSUPPORTED),
+    (lambda a: setattr(a, "flags", _abi.KDA_FLAG_NO_SEGMENT_SCAN), _abi.KDA_ERR_UNSUPPORTED),
+    (lambda a: setattr(a, "flags", 32), _abi.KDA_ERR_UNSUPPORTED),
+    (lambda a: setattr(a, "flags", _abi.KDA_FLAG_QK_L2NORM | _abi.KDA_FLAG_GATE_LOGITS | _abi.KDA_FLAG_NO_CLAMP),
+     _abi.KDA_ERR_WORKSPACE),
+    (lambda a: setattr(a, "cu_seqlens", None), _abi.KDA_ERR_NULL),
+    (lambda a: setattr(a, "cu_seqlens", 0x100004), _abi.KDA_ERR_ALIGN),
+    (lambda a: setattr(a, "d_out", None), _abi.KDA_ERR_NULL),
+    (lambda a: setattr(a, "dbeta", None), _abi.KDA_ERR_NULL),
+    (lambda a: setattr(a, "dgate", 0x700008), _abi.KDA_ERR_ALIGN),
+    (lambda a: setattr(a, "d_initial_state", 0x900004), _abi.KDA_ERR_ALIGN),
+    (lambda a: None, _abi.KDA_ERR_WORKSPACE),
+    (lambda a: (setattr(a, "workspace", 0x2000000), setattr(a, "workspace_bytes", 4096)), _abi.KDA_ERR_WORKSPACE),
+    (lambda a: setattr(a, "N", 0), _abi.KDA_OK),
+    (lambda a: setattr(a, "H", 0), _abi.KDA_OK),
+    (lambda a: setattr(a, "rows", 0), _abi.KDA_OK),  # no tokens and no initial-state gradient asked for
+])
+def test_bwd_varlen_validation(lib, mutate, code):
+    a = _good_bwd_var()
+    mutate(a)
+    assert lib.kda_chunk_bwd_varlen(ctypes.byref(a), None) == code
+    assert lib.kda_chunk_bwd_varlen(None, None) == _abi.KDA_ERR_NULL
