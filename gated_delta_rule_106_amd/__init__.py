@@ -186,11 +186,11 @@ def snapshot_slot(cu_seqlens, i: int, k: int, snapshot_every: int) -> int:
 
 def chunk_fwd_varlen(q, k, v, log_alpha, beta, gate, cu_seqlens, initial_state=None,
                      output_final_state=False, snapshot_every=0, clamp=True, out_dtype=torch.float32,
-                     qk_norm=False, gate_logits=False, out=None, workspace=None):
+                     qk_norm=False, gate_logits=False, out=None, workspace=None, chunk=0):
     """Variable-length batch on the current HIP stream: N sequences packed along the
     rows of q, k, log_alpha [rows, H, Dk], v, gate [rows, H, Dv], beta [rows, H]
-    (bf16), sequence i being rows cu_seqlens[i] .. cu_seqlens[i+1] - 1 (int64 device
-    tensor [N + 1]).  initial_state: fp32 [N, H, Dk, Dv] or None.  With
+    (fp32 or bf16), sequence i being rows cu_seqlens[i] .. cu_seqlens[i+1] - 1 (int64
+    device tensor [N + 1]); ``chunk`` as for ``chunk_fwd`` (0: the default).  initial_state: fp32 [N, H, Dk, Dv] or None.  With
     ``snapshot_every`` P > 0 (a multiple of 64) the state after every P tokens of
     each sequence is returned in an fp32 [rows // P + N, H, Dk, Dv] tensor, the k-th
     of sequence i in slot ``snapshot_slot(cu_seqlens, i, k, P)``.  Returns
@@ -224,7 +224,7 @@ def chunk_fwd_varlen(q, k, v, log_alpha, beta, gate, cu_seqlens, initial_state=N
         snaps = torch.empty((rows // snapshot_every + N, H, Dk, Dv), dtype=torch.float32, device=dev)
     a = _abi.VarlenArgs()
     a.N, a.rows, a.H, a.Dk, a.Dv = N, rows, H, Dk, Dv
-    a.dtype, a.out_dtype, a.chunk = code, _out_code(out_dtype), 0
+    a.dtype, a.out_dtype, a.chunk = code, _out_code(out_dtype), int(chunk)
     a.flags = _prep_flags(clamp, qk_norm, gate_logits)
     a.snapshot_every = int(snapshot_every)
     n = ctypes.c_size_t(0)

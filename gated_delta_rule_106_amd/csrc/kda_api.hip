@@ -77,6 +77,7 @@ int check_shape(const kda_fwd_args* a, int* chunk, int64_t* nchunks, int64_t* ca
 // Varlen: sizes, dtype, chunk, flags and snapshot interval; fills the workspace
 // layout (cards, then the sequence map).
 struct VarlenLayout {
+    int chunk;
     int64_t max_chunks, card, cards_bytes, off_s, off_co, off_soc, total;
 };
 
@@ -86,9 +87,10 @@ int check_varlen(const kda_varlen_args* a, VarlenLayout* L) {
     if (!a) return KDA_ERR_NULL;
     if (a->N < 0 || a->rows < 0 || a->H < 0 || a->Dk <= 0 || a->Dv <= 0 || a->snapshot_every < 0)
         return KDA_ERR_SHAPE;
-    if (a->dtype != KDA_BF16) return KDA_ERR_UNSUPPORTED;
-    if (a->chunk != 0 && a->chunk != 64) return KDA_ERR_UNSUPPORTED;
+    if (a->dtype != KDA_F32 && a->dtype != KDA_BF16) return KDA_ERR_UNSUPPORTED;
     if (a->Dk != a->Dv || (a->Dk != 64 && a->Dk != 128)) return KDA_ERR_UNSUPPORTED;
+    const int c = a->chunk != 0 ? a->chunk : (a->dtype == KDA_BF16 ? kDefaultChunkBf16 : kDefaultChunkF32);
+    if (!kda::prefill_supported(a->dtype == KDA_BF16, c, (int)a->Dk)) return KDA_ERR_UNSUPPORTED;
     if (a->out_dtype != KDA_F32 && a->out_dtype != KDA_BF16) return KDA_ERR_UNSUPPORTED;
     if ((a->flags & ~(KDA_FLAG_NO_CLAMP | KDA_FLAG_NO_SEGMENT_SCAN | kPrepFlags)) != 0) return KDA_ERR_UNSUPPORTED;
     if (a->snapshot_every % 64 != 0) return KDA_ERR_UNSUPPORTED;
@@ -97,14 +99,15 @@ int check_varlen(const kda_varlen_args* a, VarlenLayout* L) {
         !mul_ok(nh, a->Dk * a->Dv, &st))
         return KDA_ERR_SHAPE;
     if (a->N >= INT32_MAX || a->H > INT_MAX || nh > INT_MAX) return KDA_ERR_SHAPE;
-    const int64_t mc = kda::varlen_max_chunks(a->N, a->rows, 64);
-    const int64_t cb = kda::prefill64_card_bytes((int)a->Dk);
+    const int64_t mc = kda::varlen_max_chunks(a->N, a->rows, c);
+    const int64_t cb = kda::prefill_card_bytes(a->dtype == KDA_BF16, c, (int)a->Dk);
     int64_t items, cards;
     if (!mul_ok(mc, a->H, &items) || items > INT_MAX || !mul_ok(items, cb, &cards)) return KDA_ERR_SHAPE;
     if (a->snapshot_every > 0) {
         int64_t slots = a->rows / a->snapshot_every + a->N, sb;
         if (!mul_ok(slots, st / (a->N > 0 ? a->N : 1), &sb)) return KDA_ERR_SHAPE;
     }
+    L->chunk = c;
     L->max_chunks = mc;
     L->card = cb;
     L->cards_bytes = align256(cards);
@@ -243,10 +246,11 @@ int kda_chunk_fwd_varlen(const kda_varlen_args* a, hipStream_t stream) {
     unsigned char* ws = static_cast<unsigned char*>(a->workspace);
     kda::VarlenMap m{reinterpret_cast<int64_t*>(ws + L.off_s), reinterpret_cast<int64_t*>(ws + L.off_co),
                      reinterpret_cast<int32_t*>(ws + L.off_soc)};
-    hipError_t e = kda::launch_varlen_map(m, a->cu_seqlens, a->N, a->rows, 64, stream);
+    hipError_t e = kda::launch_varlen_map(m, a->cu_seqlens, a->N, a->rows, L.chunk, stream);
     if (e != hipSuccess) return KDA_ERR_HIP;
+    // NC: the most chunks the offsets can give (the card builder's grid)
     kda::PrepParams pp{a->q, a->k, a->v, a->log_alpha, a->beta, a->workspace,
-                       1, a->rows, a->H, 0, (a->flags & KDA_FLAG_NO_CLAMP) ? 0 : 1,
+                       1, a->rows, a->H, L.max_chunks, (a->flags & KDA_FLAG_NO_CLAMP) ? 0 : 1,
                        (a->flags & KDA_FLAG_QK_L2NORM) ? 1 : 0, (a->flags & KDA_FLAG_GATE_LOGITS) ? 1 : 0,
                        m.s, m.co, m.soc, a->N};
     kda::RecurParams rp{a->gate, a->out, a->initial_state, a->final_state, a->workspace,
@@ -254,8 +258,8 @@ int kda_chunk_fwd_varlen(const kda_varlen_args* a, hipStream_t stream) {
     rp.vs = m.s;
     rp.vco = m.co;
     rp.snap = a->snapshot_every > 0 ? a->snapshots : nullptr;
-    rp.snap_chunks = a->snapshot_every > 0 ? a->snapshot_every / 64 : 1;
-    e = kda::launch_prefill64((int)a->Dk, a->out_dtype == KDA_BF16, pp, rp, stream);
+    rp.snap_chunks = a->snapshot_every > 0 ? a->snapshot_every / L.chunk : 1;
+    e = kda::launch_prefill(a->dtype == KDA_BF16, a->out_dtype == KDA_BF16, L.chunk, (int)a->Dk, pp, rp, stream);
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 

@@ -55,8 +55,9 @@ struct RecurParams {
     // variable-length batch (as in PrepParams; B = N, T unused)
     const int64_t* vs;
     const int64_t* vco;
-    // block-granular state snapshots: after every snap_chunks chunks of a sequence the
-    // state goes to slot floor(s_i / (64 snap_chunks)) + i + k of snap [slots, H, D, D]
+    // block-granular state snapshots: after every snap_chunks chunks of C tokens of a
+    // sequence the state goes to slot floor(s_i / (C snap_chunks)) + i + k of snap
+    // [slots, H, D, D]
     float* snap;
     int64_t snap_chunks;
     // pipelined long sequences: ring_len > 0 runs piece `piece` only (chunks

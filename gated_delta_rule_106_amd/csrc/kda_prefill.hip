@@ -139,8 +139,26 @@ void kda_prep_kernel(PrepParams p) {
 
     const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
     const int m16 = lane & 15, g4 = lane >> 4;
-    const int64_t T = p.T, H = p.H;
-    const int64_t n = blockIdx.x % p.NC, b = (blockIdx.x / p.NC) / H, h = (blockIdx.x / p.NC) % H;
+    const int64_t H = p.H;
+    // this card's chunk n of a sequence of T tokens from packed row tb, head h: B
+    // sequences of p.T tokens (card (b H + h) NC + n), or a variable-length batch (card
+    // g H + h for the batch's chunk g); either way the card index is blockIdx.x
+    int64_t n, h, tb, T;
+    if (p.vco) {
+        const int64_t g = blockIdx.x / H;
+        h = blockIdx.x - g * H;
+        if (g >= p.vco[p.vN]) return;  // no chunk here (the whole group leaves)
+        const int64_t i = p.vsoc[g];
+        n = g - p.vco[i];
+        tb = p.vs[i];
+        T = p.vs[i + 1] - tb;  // >= 1: the sequence owns this chunk
+    } else {
+        const int64_t bh = blockIdx.x / p.NC;
+        n = blockIdx.x - bh * p.NC;
+        h = bh % H;
+        tb = (bh / H) * p.T;
+        T = p.T;
+    }
     const int64_t t0 = (int64_t)n * C;
     const raw_t* gq = static_cast<const raw_t*>(p.q);
     const raw_t* gk = static_cast<const raw_t*>(p.k);
@@ -149,8 +167,8 @@ void kda_prep_kernel(PrepParams p) {
     const raw_t* gbeta = static_cast<const raw_t*>(p.beta);
     const bool clamp = p.clamp != 0, logits = p.logits != 0;
     float* NS = reinterpret_cast<float*>(smem + L::OFF_NS);  // [0][r]: q scale, [1][r]: k scale
-    // token (b, t, h) row offset in a [B, T, H, D] tensor
-    auto row = [&](int64_t t) { return ((int64_t)b * T + t) * H + h; };
+    // row of token t of the sequence (head h) in a packed [rows, H, D] tensor
+    auto row = [&](int64_t t) { return (tb + t) * H + h; };
 
     // per-token L2 normalisation factors of raw q and k (one wave per token, visible
     // after the first barrier below; 1 for inputs that arrive normalised)
@@ -289,7 +307,7 @@ void kda_prep_kernel(PrepParams p) {
     __syncthreads();
 
     // ---- phase 1.5: Kbar^T and Gamma to the card (frees the k*G tile)
-    const int64_t chunk_index = ((int64_t)b * H + h) * p.NC + n;
+    const int64_t chunk_index = blockIdx.x;
     op_t* card = reinterpret_cast<op_t*>(static_cast<unsigned char*>(p.ws) + chunk_index * CD::BYTES);
     float* gam = reinterpret_cast<float*>(card + CD::OP_ELEMS);
     for (int i = tid; i < D * (C / 8); i += NT) {
@@ -518,8 +536,24 @@ void kda_recur_kernel(RecurParams p) {
     constexpr int GROUPS = D / (16 * NWV);
     const int cgrp = logical % GROUPS;
     const int64_t unit = logical / GROUPS;  // b * H + h
-    const int64_t H = p.H, T = p.T, NC = p.NC;
+    const int64_t H = p.H;
     const int64_t b = unit / H, h = unit % H;
+    // the sequence of this (b, h): T tokens from packed row tb, NC chunks whose cards are
+    // cbase + ci cstride (B sequences of p.T tokens, or a variable-length batch)
+    int64_t T, NC, tb, cbase, cstride;
+    if (p.vco) {
+        tb = p.vs[b];
+        T = p.vs[b + 1] - tb;
+        NC = (T + C - 1) / C;
+        cbase = p.vco[b] * H + h;
+        cstride = H;
+    } else {
+        T = p.T;
+        NC = p.NC;
+        tb = b * T;
+        cbase = unit * NC;
+        cstride = 1;
+    }
     const int col = 16 * (cgrp * NWV + wave) + m16;  // this lane's value column
     const int nt = col >> 4;
 
@@ -533,7 +567,8 @@ void kda_recur_kernel(RecurParams p) {
             for (int i = 0; i < 4; ++i) S[ct][i] = s0 ? s0[(16 * ct + 4 * g4 + i) * D + col] : 0.f;
     }
 
-    const unsigned char* cards = static_cast<const unsigned char*>(p.ws) + unit * NC * CD::BYTES;
+    const unsigned char* cards = static_cast<const unsigned char*>(p.ws) + cbase * CD::BYTES;
+    const int64_t cbytes = cstride * CD::BYTES;  // from one chunk's card to the next
     // cooperative copy of one card's W, Qe, Kbar^T (+ Gamma) into an LDS buffer
     constexpr int VPR_W = D * (int)sizeof(op_t) / 16;   // 16-byte vectors per [C][D] row
     constexpr int VPR_K = C * (int)sizeof(op_t) / 16;   // per [D][C] row
@@ -576,7 +611,7 @@ void kda_recur_kernel(RecurParams p) {
         const int buf = (int)(ci & 1);
         const bool more = ci + 1 < NC;
         {   // prefetch the next card into registers (unconditional loads keep them in VGPRs)
-            const uint4* src = reinterpret_cast<const uint4*>(cards + (more ? ci + 1 : ci) * CD::BYTES);
+            const uint4* src = reinterpret_cast<const uint4*>(cards + (more ? ci + 1 : ci) * cbytes);
 #pragma unroll
             for (int j = 0; j < PER; ++j) {
                 const int v = tid + j * NT;
@@ -587,7 +622,7 @@ void kda_recur_kernel(RecurParams p) {
         const op_t* Ql = reinterpret_cast<const op_t*>(smem + buf * L::B_BUF + L::B_W);
         const op_t* Kl = reinterpret_cast<const op_t*>(smem + buf * L::B_BUF + 2 * L::B_W);
         const float* Gl = reinterpret_cast<const float*>(smem + buf * L::B_BUF + 2 * L::B_W + L::B_K);
-        const op_t* card = reinterpret_cast<const op_t*>(cards + ci * CD::BYTES);
+        const op_t* card = reinterpret_cast<const op_t*>(cards + ci * cbytes);
         const int64_t tbase = ci * C;
         // this lane's gate logits of the chunk (rows 16 mt + 4 g4 + i, column col), loaded ahead
         // of the products and of the output stores, each from a token inside the sequence
@@ -597,7 +632,7 @@ void kda_recur_kernel(RecurParams p) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int64_t t = tbase + 16 * mt + 4 * g4 + i;
-                zl[mt][i] = In::load(gz, ((b * T + (t < T ? t : T - 1)) * H + h) * D + col);
+                zl[mt][i] = In::load(gz, ((tb + (t < T ? t : T - 1)) * H + h) * D + col);
             }
 
         floatx4 U[NMT];
@@ -623,7 +658,7 @@ void kda_recur_kernel(RecurParams p) {
                     U[mt][i] = utv[i] - aw[i];
                     const int64_t t = tbase + 16 * mt + 4 * g4 + i;
                     if (t < T) {
-                        const int64_t gi = ((b * T + t) * H + h) * D + col;
+                        const int64_t gi = ((tb + t) * H + h) * D + col;
                         gy[gi] = Out::from_float((uov[i] + aq[i]) * sigmoidf_(zl[mt][i]));
                     }
                 }
@@ -677,7 +712,7 @@ void kda_recur_kernel(RecurParams p) {
                     U[mt][i] = static_cast<float>(ut[i]) - aw[i];
                     const int64_t t = tbase + 16 * mt + 4 * g4 + i;
                     if (t < T) {
-                        const int64_t gi = ((b * T + t) * H + h) * D + col;
+                        const int64_t gi = ((tb + t) * H + h) * D + col;
                         gy[gi] = Out::from_float((static_cast<float>(uo[i]) + aq[i]) * sigmoidf_(zl[mt][i]));
                     }
                 }
@@ -716,6 +751,15 @@ void kda_recur_kernel(RecurParams p) {
                 }
                 S[ct] = acc;
             }
+        }
+        if (p.snap && (ci + 1) % p.snap_chunks == 0 && (ci + 1) * C <= T) {
+            // block-granular snapshot: the state after (ci + 1) C tokens of the sequence
+            const int64_t slot = tb / (C * p.snap_chunks) + b + (ci + 1) / p.snap_chunks - 1;
+            float* dst = p.snap + (slot * H + h) * (int64_t)D * D;
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) dst[(16 * ct + 4 * g4 + i) * D + col] = S[ct][i];
         }
         if (more) {
             unsigned char* base = smem + (buf ^ 1) * L::B_BUF;
@@ -758,7 +802,8 @@ static hipError_t launch_t(const PrepParams& pp, const RecurParams& rp, hipStrea
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kp),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)LP::TOTAL);
         if (e != hipSuccess) return e;
-        dim3 grid((unsigned)(pp.NC * pp.H * pp.B));
+        // a variable-length grid covers the most chunks its offsets can give (pp.NC)
+        dim3 grid((unsigned)(pp.vco ? pp.NC * pp.H : pp.NC * pp.H * pp.B));
         hipLaunchKernelGGL(kp, grid, dim3(256), LP::TOTAL, stream, pp);
         e = hipGetLastError();
         if (e != hipSuccess) return e;

@@ -210,10 +210,12 @@ int kda_chunk_fwd_noalloc(const kda_fwd_args *a, hipStream_t stream);
  *     the k-th snapshot of sequence i (after (k + 1) * snapshot_every of its
  *     tokens, k < len_i / snapshot_every) is slot
  *     s_i / snapshot_every + i + k (integer division).  Other slots are not written.
- *   Supported: bf16 inputs, chunk 0 or 64, Dk == Dv in {64, 128}; flags as in
- *   kda_chunk_fwd (KDA_FLAG_NO_SEGMENT_SCAN has no effect: no segments here).
- *   The workspace size comes from kda_chunk_fwd_varlen_workspace_size() (it
- *   depends on N, rows, H and Dk only).
+ *   Supported: fp32 or bf16 inputs, the chunk sizes kda_chunk_fwd takes for that
+ *   dtype and head size (0 picks the same default), Dk == Dv in {64, 128}; flags as
+ *   in kda_chunk_fwd (KDA_FLAG_NO_SEGMENT_SCAN has no effect: no segments here).
+ *   Every sequence starts its own chunks.  The workspace size comes from
+ *   kda_chunk_fwd_varlen_workspace_size() (it depends on N, rows, H, Dk, dtype and
+ *   chunk only).
  * The packed layout with cu_seqlens[i] = i T is the memory of a [N, T, H, D]
  * batch, so this also adds snapshots to ordinary batches.
  */

@@ -317,6 +317,17 @@ def test_varlen_workspace_size(lib):
     chunks = (1000 + 63) // 64 + 3  # the most chunks any offsets can give
     r256 = lambda x: (x + 255) // 256 * 256
     assert n.value == r256(chunks * 2 * card) + 2 * r256(4 * 8) + r256(chunks * 4)
+    # the general path (fp32 inputs, default chunk 16; bf16 with chunk 32): one card per
+    # chunk of its size, as kda_chunk_fwd sizes a one-chunk call
+    for dtype, chunk, c in ((_abi.KDA_F32, 0, 16), (_abi.KDA_BF16, 32, 32)):
+        a = _good_var()
+        a.dtype, a.chunk = dtype, chunk
+        assert lib.kda_chunk_fwd_varlen_workspace_size(ctypes.byref(a), ctypes.byref(n)) == 0
+        one = _good_fwd(B=1, T=c, H=1, D=128, dtype=dtype, chunk=c)
+        rc, card = _ws(lib, one)
+        assert rc == 0
+        chunks = (1000 + c - 1) // c + 3
+        assert n.value == r256(chunks * 2 * card) + 2 * r256(4 * 8) + r256(chunks * 4)
 
 
 @pytest.mark.parametrize("mutate,code", [
@@ -324,8 +335,12 @@ def test_varlen_workspace_size(lib):
     (lambda a: setattr(a, "rows", -1), _abi.KDA_ERR_SHAPE),
     (lambda a: setattr(a, "snapshot_every", -64), _abi.KDA_ERR_SHAPE),
     (lambda a: setattr(a, "snapshot_every", 100), _abi.KDA_ERR_UNSUPPORTED),
-    (lambda a: setattr(a, "dtype", _abi.KDA_F32), _abi.KDA_ERR_UNSUPPORTED),
-    (lambda a: setattr(a, "chunk", 32), _abi.KDA_ERR_UNSUPPORTED),
+    (lambda a: setattr(a, "dtype", 7), _abi.KDA_ERR_UNSUPPORTED),
+    (lambda a: setattr(a, "chunk", 48), _abi.KDA_ERR_UNSUPPORTED),
+    (lambda a: (setattr(a, "dtype", _abi.KDA_F32), setattr(a, "chunk", 64)), _abi.KDA_ERR_UNSUPPORTED),
+    # fp32 inputs and the general path's chunk sizes are accepted: the workspace check decides
+    (lambda a: setattr(a, "dtype", _abi.KDA_F32), _abi.KDA_ERR_WORKSPACE),
+    (lambda a: setattr(a, "chunk", 32), _abi.KDA_ERR_WORKSPACE),
     (lambda a: setattr(a, "Dv", 64), _abi.KDA_ERR_UNSUPPORTED),
     (lambda a: setattr(a, "flags", 16), _abi.KDA_ERR_UNSUPPORTED),
     (lambda a: setattr(a, "cu_seqlens", None), _abi.KDA_ERR_NULL),

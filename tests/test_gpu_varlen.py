@@ -230,3 +230,58 @@ def test_sequences_may_start_after_row_zero():
         yo, so = oracle_seq(x, s0, cu, i)
         assert rel_err(y[cu2[i]:cu2[i + 1]], yo[0]) <= TOL and rel_err(fin[i], so[0]) <= TOL
     say("[varlen] sequences starting at row 20: outside rows untouched, parity held")
+
+
+# The general path (fp32 inputs, or chunks of 16 / 32 tokens): the same sequence map
+# places its cards and its state pass.  Limits as for kda_chunk_fwd: 1e-4 for fp32
+# inputs, 2e-2 for bf16.
+GENERAL = [
+    # (dtype, D, chunk, workload of the recipe)
+    (torch.float32, 64, 0, 0),
+    (torch.float32, 128, 32, 0),
+    (torch.bfloat16, 128, 16, 2),
+    (torch.bfloat16, 64, 32, 2),
+]
+
+
+@pytest.mark.parametrize("dtype,D,chunk,wl_id", GENERAL,
+                         ids=[f"{'fp32' if g[0] == torch.float32 else 'bf16'} d{g[1]} chunk {g[2] or 16}"
+                              for g in GENERAL])
+def test_varlen_general_path_matches_oracle(dtype, D, chunk, wl_id):
+    """Empty, one-token, ragged and exact-chunk sequences, with snapshots every 64
+    tokens, against the oracle run on each sequence alone."""
+    lengths = [0, 1, 15, 16, 17, 200, 0, 65, 128]
+    x, s0, cu = packed(lengths, 2, D, seed=240 + D + chunk, wl_id=wl_id)
+    x = {k: v.to(dtype) for k, v in x.items()}
+    tol = 1e-4 if dtype == torch.float32 else TOL
+    say(f"[varlen general] {dtype} D={D} chunk={chunk} lengths={lengths}")
+    y, fin, snaps = run(x, s0, cu, snapshot_every=64, chunk=chunk)
+    worst = 0.0
+    for i, L in enumerate(lengths):
+        yo, so = oracle_seq(x, s0, cu, i)
+        ey, es = rel_err(y[cu[i]:cu[i + 1]], yo[0]), rel_err(fin[i], so[0])
+        worst = max(worst, ey, es)
+        assert ey <= tol and es <= tol, (i, ey, es)
+        for kk in range(L // 64):
+            _, sk = oracle_seq(x, s0, cu, i, upto=(kk + 1) * 64)
+            e = rel_err(snaps[kda().snapshot_slot(cu, i, kk, 64)], sk[0])
+            worst = max(worst, e)
+            assert e <= tol, (i, kk, e)
+    say(f"[varlen general] worst err/rms over outputs, final states and snapshots: {worst:.3e}")
+
+
+def test_varlen_general_path_equal_lengths_bitwise_equal_to_batch():
+    """fp32, chunk 16: cu = i T over a [N, T, H, D] batch gives the batch call's
+    results bit for bit."""
+    N, T, H = 3, 100, 2
+    wl = CONFIGS[0].scaled(B=N, H=H, T=T, init_state=True)
+    x = {k: v.cuda() for k, v in make_inputs(wl, seed=250).items() if v is not None}
+    s0 = x["initial_state"]
+    yb, sb = kda().chunk_fwd(*(x[k] for k in KEYS), initial_state=s0, output_final_state=True, chunk=16)
+    cu = torch.arange(0, (N + 1) * T, T, dtype=torch.int64, device="cuda")
+    flat = {k: x[k].reshape(N * T, *x[k].shape[2:]) for k in KEYS}
+    yv, sv, _ = kda().chunk_fwd_varlen(*(flat[k] for k in KEYS), cu, initial_state=s0, output_final_state=True,
+                                       chunk=16)
+    torch.cuda.synchronize()
+    assert torch.equal(yv.reshape(N, T, H, -1), yb) and torch.equal(sv, sb)
+    say("[varlen general] equal lengths vs batch: identical")
