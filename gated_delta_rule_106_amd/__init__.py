@@ -249,14 +249,15 @@ def chunk_fwd_varlen(q, k, v, log_alpha, beta, gate, cu_seqlens, initial_state=N
 
 
 def chunk_summary(k, v, log_alpha, beta, clamp=True, transition=None, offset=None, workspace=None,
-                  qk_norm=False, gate_logits=False, q=None):
+                  qk_norm=False, gate_logits=False, q=None, chunk=0):
     """Segment summary of every (b, h) sequence on the current HIP stream.
 
     The T tokens map an incoming state S to ``M @ S + b`` (``M`` the product of the
     per-token transitions, ``b`` the state reached from zero).  k, log_alpha:
-    bf16 [B, T, H, Dk]; v: bf16 [B, T, H, Dv]; beta: bf16 [B, T, H].  Returns
-    ``(M, b)``: fp32 [B, H, Dk, Dk] and [B, H, Dk, Dv].  Given ``q`` (and a
-    ``workspace``), the cards left in the workspace also serve a following
+    [B, T, H, Dk]; v: [B, T, H, Dv]; beta: [B, T, H] (fp32 or bf16, one dtype);
+    ``chunk`` as for ``chunk_fwd``.  Returns ``(M, b)``: fp32 [B, H, Dk, Dk] and
+    [B, H, Dk, Dv].  Given ``q`` (and a ``workspace``), with bf16 inputs and chunk 64
+    the cards left in the workspace also serve a following
     ``chunk_fwd(..., workspace=workspace, cards_ready=True)`` over the same inputs.
     """
     lib = _abi.load()
@@ -272,7 +273,7 @@ def chunk_summary(k, v, log_alpha, beta, clamp=True, transition=None, offset=Non
         if t.dtype != k.dtype:
             raise TypeError("k, v, log_alpha and beta must share one dtype")
     a = _abi.FwdArgs()
-    a.B, a.T, a.H, a.Dk, a.Dv, a.dtype = B, T, H, Dk, Dv, code
+    a.B, a.T, a.H, a.Dk, a.Dv, a.dtype, a.chunk = B, T, H, Dk, Dv, code, int(chunk)
     a.flags = _prep_flags(clamp, qk_norm, gate_logits)
     if transition is None:
         transition = torch.empty((B, H, Dk, Dk), dtype=torch.float32, device=dev)

@@ -367,7 +367,6 @@ int kda_chunk_summary(const kda_fwd_args* a, float* transition, hipStream_t stre
     int64_t nc, cb, need;
     int st = check_shape(a, &c, &nc, &cb, &need);
     if (st != KDA_OK) return st;
-    if (a->dtype != KDA_BF16 || c != 64) return KDA_ERR_UNSUPPORTED;
     if (a->flags & ~(KDA_FLAG_NO_CLAMP | kPrepFlags)) return KDA_ERR_UNSUPPORTED;
     const int64_t units = a->B * a->H;
     if (!aligned16(a->q)) return KDA_ERR_ALIGN;
@@ -393,7 +392,7 @@ int kda_chunk_summary(const kda_fwd_args* a, float* transition, hipStream_t stre
     kda::PrepParams pp{a->q ? a->q : a->k, a->k, a->v, a->log_alpha, a->beta, a->workspace,
                        a->B, a->T, a->H, nc, (a->flags & KDA_FLAG_NO_CLAMP) ? 0 : 1,
                        (a->flags & KDA_FLAG_QK_L2NORM) ? 1 : 0, (a->flags & KDA_FLAG_GATE_LOGITS) ? 1 : 0};
-    const hipError_t e = kda::launch_summary64(D, pp, transition, a->final_state, stream);
+    const hipError_t e = kda::launch_summary(a->dtype == KDA_BF16, c, D, pp, transition, a->final_state, stream);
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 

@@ -71,6 +71,10 @@ int64_t prefill_card_bytes(int bf16, int C, int D);
 bool prefill_supported(int bf16, int C, int D);
 hipError_t launch_prefill(int bf16, int out_bf16, int C, int D, const PrepParams& pp,
                           const RecurParams& rp, hipStream_t stream);
+// summary of whole sequences (NC >= 1) on either path: M [units, D, D] and b [units, D, D]
+// in fp32 (the chunk-64 bf16 path below, else the general path's cards and state pass)
+hipError_t launch_summary(int bf16, int C, int D, const PrepParams& pp, float* M, float* b,
+                          hipStream_t stream);
 
 // bf16 inputs, 64-token chunks (kda_chunk64.hip)
 int64_t prefill64_card_bytes(int D);

@@ -515,7 +515,12 @@ struct RecurLds {
 };
 
 // One workgroup per CU (LDS-bound): let each wave use the whole register file.
-template <int C, int D, bool F32, class In, class Out, int NWV>
+// SUM: the segment summary instead of the outputs (page "Kimi K3 report walk-through",
+// section "KDA Context Parallelism"): blocks of the first half of each (b, h)'s range
+// carry b (the state from zero, U = U~ - W S), the second half M (from the identity,
+// U = -W S: the same map on a state whose columns are the unit vectors, without the
+// values); nothing is read out, and the end state goes to p.sum_b or p.sum_m.
+template <int C, int D, bool F32, class In, class Out, int NWV, bool SUM>
 __global__ __launch_bounds__(NWV * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void kda_recur_kernel(RecurParams p) {
     using L = RecurLds<C, D, F32>;
@@ -534,8 +539,10 @@ void kda_recur_kernel(RecurParams p) {
     const int bid = blockIdx.x;
     const int logical = (nblk % 8 == 0) ? (bid % 8) * (nblk / 8) + bid / 8 : bid;
     constexpr int GROUPS = D / (16 * NWV);
+    constexpr int PARTS = SUM ? 2 : 1;  // SUM: b, then M
     const int cgrp = logical % GROUPS;
-    const int64_t unit = logical / GROUPS;  // b * H + h
+    const int part = SUM ? (logical / GROUPS) % PARTS : 0;  // 1: this block carries M
+    const int64_t unit = logical / (GROUPS * PARTS);  // b * H + h
     const int64_t H = p.H;
     const int64_t b = unit / H, h = unit % H;
     // the sequence of this (b, h): T tokens from packed row tb, NC chunks whose cards are
@@ -559,8 +566,13 @@ void kda_recur_kernel(RecurParams p) {
 
     // state S[ct] rows 16ct + 4g + i, column col
     floatx4 S[NCT];
-    {
-        const float* s0 = p.s0 ? p.s0 + unit * (int64_t)D * D : nullptr;
+    if (SUM && part == 1) {  // M starts from the identity
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) S[ct][i] = (16 * ct + 4 * g4 + i == col) ? 1.f : 0.f;
+    } else {
+        const float* s0 = (!SUM && p.s0) ? p.s0 + unit * (int64_t)D * D : nullptr;
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
@@ -632,7 +644,7 @@ void kda_recur_kernel(RecurParams p) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int64_t t = tbase + 16 * mt + 4 * g4 + i;
-                zl[mt][i] = In::load(gz, ((tb + (t < T ? t : T - 1)) * H + h) * D + col);
+                zl[mt][i] = SUM ? 0.f : In::load(gz, ((tb + (t < T ? t : T - 1)) * H + h) * D + col);
             }
 
         floatx4 U[NMT];
@@ -648,16 +660,16 @@ void kda_recur_kernel(RecurParams p) {
                     for (int i = 0; i < 4; ++i) {
                         const int cc = 16 * ct + 4 * g4 + i;
                         aw = mma_f32_k4(wr[cc], S[ct][i], aw);
-                        aq = mma_f32_k4(qr[cc], S[ct][i], aq);
+                        if constexpr (!SUM) aq = mma_f32_k4(qr[cc], S[ct][i], aq);
                     }
                 const float4 ut = *reinterpret_cast<const float4*>(card + CD::UT + ((int64_t)(nt * NMT + mt) * 64 + lane) * 4);
                 const float4 uo = *reinterpret_cast<const float4*>(card + CD::UO + ((int64_t)(nt * NMT + mt) * 64 + lane) * 4);
                 const float utv[4] = {ut.x, ut.y, ut.z, ut.w}, uov[4] = {uo.x, uo.y, uo.z, uo.w};
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    U[mt][i] = utv[i] - aw[i];
+                    U[mt][i] = ((SUM && part == 1) ? 0.f : utv[i]) - aw[i];
                     const int64_t t = tbase + 16 * mt + 4 * g4 + i;
-                    if (t < T) {
+                    if (!SUM && t < T) {
                         const int64_t gi = ((tb + t) * H + h) * D + col;
                         gy[gi] = Out::from_float((uov[i] + aq[i]) * sigmoidf_(zl[mt][i]));
                     }
@@ -703,15 +715,15 @@ void kda_recur_kernel(RecurParams p) {
                         a2[j] = q0[j]; a2[4 + j] = q1[j];
                     }
                     aw = mma_f16_k32(a1, Sb[kb], aw);
-                    aq = mma_f16_k32(a2, Sb[kb], aq);
+                    if constexpr (!SUM) aq = mma_f16_k32(a2, Sb[kb], aq);
                 }
                 const half4 ut = *reinterpret_cast<const half4*>(card + CD::UT + ((int64_t)(nt * NMT + mt) * 64 + lane) * 4);
                 const half4 uo = *reinterpret_cast<const half4*>(card + CD::UO + ((int64_t)(nt * NMT + mt) * 64 + lane) * 4);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    U[mt][i] = static_cast<float>(ut[i]) - aw[i];
+                    U[mt][i] = ((SUM && part == 1) ? 0.f : static_cast<float>(ut[i])) - aw[i];
                     const int64_t t = tbase + 16 * mt + 4 * g4 + i;
-                    if (t < T) {
+                    if (!SUM && t < T) {
                         const int64_t gi = ((tb + t) * H + h) * D + col;
                         gy[gi] = Out::from_float((static_cast<float>(uo[i]) + aq[i]) * sigmoidf_(zl[mt][i]));
                     }
@@ -752,7 +764,7 @@ void kda_recur_kernel(RecurParams p) {
                 S[ct] = acc;
             }
         }
-        if (p.snap && (ci + 1) % p.snap_chunks == 0 && (ci + 1) * C <= T) {
+        if (!SUM && p.snap && (ci + 1) % p.snap_chunks == 0 && (ci + 1) * C <= T) {
             // block-granular snapshot: the state after (ci + 1) C tokens of the sequence
             const int64_t slot = tb / (C * p.snap_chunks) + b + (ci + 1) / p.snap_chunks - 1;
             float* dst = p.snap + (slot * H + h) * (int64_t)D * D;
@@ -772,7 +784,13 @@ void kda_recur_kernel(RecurParams p) {
         __syncthreads();
     }
 
-    if (p.sT) {
+    if (SUM) {
+        float* dst = (part == 1 ? p.sum_m : p.sum_b) + unit * p.sum_stride;
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) dst[(16 * ct + 4 * g4 + i) * D + col] = S[ct][i];
+    } else if (p.sT) {
         float* sT = p.sT + unit * (int64_t)D * D;
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct)
@@ -793,7 +811,7 @@ int64_t prefill_card_bytes(int bf16, int C, int D) {
     return -1;
 }
 
-template <int C, int D, bool F32, class In, class Out, int NWV>
+template <int C, int D, bool F32, class In, class Out, int NWV, bool SUM = false>
 static hipError_t launch_t(const PrepParams& pp, const RecurParams& rp, hipStream_t stream) {
     using LP = PrepLds<C, D, F32, In>;
     using LR = RecurLds<C, D, F32>;
@@ -808,11 +826,11 @@ static hipError_t launch_t(const PrepParams& pp, const RecurParams& rp, hipStrea
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    auto kr = kda_recur_kernel<C, D, F32, In, Out, NWV>;
+    auto kr = kda_recur_kernel<C, D, F32, In, Out, NWV, SUM>;
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kr),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)LR::TOTAL);
     if (e != hipSuccess) return e;
-    const int64_t blocks = rp.B * rp.H * (D / (16 * NWV));
+    const int64_t blocks = rp.B * rp.H * (D / (16 * NWV)) * (SUM ? 2 : 1);
     hipLaunchKernelGGL(kr, dim3((unsigned)blocks), dim3(NWV * 64), LR::TOTAL, stream, rp);
     return hipGetLastError();
 }
@@ -830,6 +848,32 @@ static hipError_t launch_o(int out_bf16, const PrepParams& pp, const RecurParams
     constexpr int NWV = D == 128 ? 4 : 2;
     return out_bf16 ? launch_t<C, D, F32, In, InBF16, NWV>(pp, rp, stream)
                     : launch_t<C, D, F32, In, InF32, NWV>(pp, rp, stream);
+}
+
+// Segment summary on the general path: the cards, then one state pass per (b, h) that
+// carries b (from zero) and M (from the identity) in separate column blocks.
+hipError_t launch_summary(int bf16, int C, int D, const PrepParams& pp, float* M, float* b,
+                          hipStream_t stream) {
+    if (C == 64 && bf16) return launch_summary64(D, pp, M, b, stream);
+    RecurParams rp{};
+    rp.B = pp.B;
+    rp.T = pp.T;
+    rp.H = pp.H;
+    rp.NC = pp.NC;
+    rp.ws = pp.ws;
+    rp.nseg = 1;
+    rp.seg_len = pp.NC;
+    rp.sum_b = b;
+    rp.sum_m = M;
+    rp.sum_stride = (int64_t)D * D;
+    if (pp.NC < 1) return hipErrorInvalidValue;
+#define KDA_S(CC, DD)                                                                                     \
+    if (C == CC && D == DD)                                                                               \
+        return bf16 ? launch_t<CC, DD, false, InBF16, InF32, DD == 128 ? 4 : 2, true>(pp, rp, stream)    \
+                    : launch_t<CC, DD, true, InF32, InF32, DD == 128 ? 4 : 2, true>(pp, rp, stream);
+    KDA_S(16, 64) KDA_S(32, 64) KDA_S(64, 64) KDA_S(16, 128) KDA_S(32, 128)
+#undef KDA_S
+    return hipErrorInvalidValue;
 }
 
 hipError_t launch_prefill(int bf16, int out_bf16, int C, int D, const PrepParams& pp,

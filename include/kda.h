@@ -261,12 +261,15 @@ int kda_chunk_fwd_varlen(const kda_varlen_args *a, hipStream_t stream);
  *   transition: fp32 [B, H, Dk, Dk], receives M (required).
  *   a->final_state: fp32 [B, H, Dk, Dv], receives b (required).
  *   The two outputs must not overlap each other, the inputs or the workspace.
- *   Supported: bf16 inputs, chunk 0 or 64, Dk == Dv in {64, 128};
+ *   Supported: the dtypes, chunk sizes and head sizes of kda_chunk_fwd (Dk == Dv);
  *   KDA_FLAG_NO_CLAMP, KDA_FLAG_QK_L2NORM and KDA_FLAG_GATE_LOGITS apply as in
- *   kda_chunk_fwd, KDA_FLAG_NO_SEGMENT_SCAN returns KDA_ERR_UNSUPPORTED.  The workspace that
- *   kda_chunk_fwd_workspace_size() reports for the same *a is sufficient.
- *   T == 0 gives M = I and b = 0.  M and b are accumulated in fp32 from fp16
- *   MFMA operands, like the state of kda_chunk_fwd.
+ *   kda_chunk_fwd, KDA_FLAG_NO_SEGMENT_SCAN and KDA_FLAG_CARDS_READY return
+ *   KDA_ERR_UNSUPPORTED.  The workspace that kda_chunk_fwd_workspace_size() reports
+ *   for the same *a is sufficient.  Cards left for a KDA_FLAG_CARDS_READY re-run:
+ *   bf16 inputs with chunk 64 only.
+ *   T == 0 gives M = I and b = 0.  M and b are accumulated in fp32, from the MFMA
+ *   operands of the path the inputs take (fp16 for bf16 inputs, fp32 for fp32
+ *   inputs), like the state of kda_chunk_fwd.
  */
 int kda_chunk_summary(const kda_fwd_args *a, float *transition, hipStream_t stream);
 

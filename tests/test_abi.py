@@ -243,9 +243,13 @@ def _good_sum():
 
 
 @pytest.mark.parametrize("mutate,code", [
-    (lambda a: setattr(a, "dtype", _abi.KDA_F32), _abi.KDA_ERR_UNSUPPORTED),
-    (lambda a: setattr(a, "chunk", 32), _abi.KDA_ERR_UNSUPPORTED),
+    # every path kda_chunk_fwd takes: fp32 inputs and chunks of 16 / 32 are accepted
+    (lambda a: setattr(a, "dtype", _abi.KDA_F32), _abi.KDA_ERR_WORKSPACE),
+    (lambda a: setattr(a, "chunk", 32), _abi.KDA_ERR_WORKSPACE),
+    (lambda a: (setattr(a, "dtype", _abi.KDA_F32), setattr(a, "chunk", 64)), _abi.KDA_ERR_UNSUPPORTED),
+    (lambda a: setattr(a, "chunk", 128), _abi.KDA_ERR_UNSUPPORTED),
     (lambda a: setattr(a, "flags", _abi.KDA_FLAG_NO_SEGMENT_SCAN), _abi.KDA_ERR_UNSUPPORTED),
+    (lambda a: setattr(a, "flags", _abi.KDA_FLAG_CARDS_READY), _abi.KDA_ERR_UNSUPPORTED),
     (lambda a: setattr(a, "flags", 16), _abi.KDA_ERR_UNSUPPORTED),
     (lambda a: setattr(a, "flags", 13), _abi.KDA_ERR_WORKSPACE),  # clamp off, q/k norm, logits: accepted
     (lambda a: setattr(a, "Dk", 96), _abi.KDA_ERR_UNSUPPORTED),

@@ -181,3 +181,38 @@ def test_rerun_takes_the_summary_cards(H, T):
     torch.cuda.synchronize()
     say(f"[kcp] cards reused H={H} T={T}: identical y {torch.equal(y0, y1)}, final {torch.equal(s0, s1)}")
     assert torch.equal(y0, y1) and torch.equal(s0, s1)
+
+
+# The general path (fp32 inputs, or chunks of 16 / 32 tokens): its cards and one state
+# pass per (b, h) that carries b from zero and M from the identity.  Same error measures;
+# the fp32 bound for fp32 inputs.
+GENERAL = [
+    # (dtype, D, chunk, T, alpha_mu, beta_mu)
+    ("f32", 64, 0, 300, 2.0, 0.0),
+    ("f32", 128, 32, 257, 6.0, 0.0),
+    ("f32", 128, 16, 100, 7.0, -3.0),
+    ("bf16", 128, 16, 300, 2.0, 0.0),
+    ("bf16", 64, 32, 190, 6.0, -3.0),
+]
+
+
+@pytest.mark.parametrize("dtype,D,chunk,T,alpha_mu,beta_mu", GENERAL,
+                         ids=[f"{g[0]} d{g[1]} chunk {g[2] or 16} T{g[3]}" for g in GENERAL])
+def test_summary_general_path_matches_oracle(dtype, D, chunk, T, alpha_mu, beta_mu):
+    wl = CONFIGS[1].scaled(B=1, H=2, T=T, Dk=D, Dv=D, dtype=dtype, alpha_mu=alpha_mu, beta_mu=beta_mu,
+                           init_state=True)
+    x = make_inputs(wl, seed=60 + T)
+    tol = TOL_F32 if dtype == "f32" else TOL_BF16
+    say(f"[summary general] {dtype} D={D} chunk={chunk} T={T} alpha_mu={alpha_mu} beta_mu={beta_mu}")
+    d = {k: x[k].cuda() for k in ("k", "v", "log_alpha", "beta")}
+    M, b = kda().chunk_summary(d["k"], d["v"], d["log_alpha"], d["beta"], chunk=chunk)
+    torch.cuda.synchronize()
+    Mo, bo = oracle.summary(x["k"], x["v"], x["log_alpha"], x["beta"])
+    eM, eb = rel_err(M, Mo, floor=1 / math.sqrt(D)), rel_err(b, bo)
+    s0 = x["initial_state"].double().numpy() * 50
+    _, so = oracle.fwd(*(x[k] for k in KEYS), initial_state=s0)
+    eS = rel_err(np.matmul(_np(M), s0) + _np(b), so)
+    say(f"[summary general] M err={eM:.3e} b err/rms={eb:.3e} M S0 + b err/rms={eS:.3e} (tol {tol})")
+    assert np.isfinite(eM) and eM <= tol
+    assert np.isfinite(eb) and eb <= tol
+    assert np.isfinite(eS) and eS <= tol
