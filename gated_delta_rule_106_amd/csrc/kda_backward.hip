@@ -14,12 +14,12 @@
 //
 // Three launches:
 //  1. kda_bwd_chunk_kernel, one workgroup per chunk: g, Bm, P, Li, and the sweep's
-//     record W = Li diag(beta) Kt, Kb, Gc, b = Kb^T Li diag(beta) V and
+//     record W = Li diag(beta) Kt, Kb, Gc, U~ = Li diag(beta) V and
 //     R = (Qt - P W)^T dO with dO = dY * sigmoid(Z); g, Li, P and Bm stay in a pair
 //     record for the gradient kernel.
 //  2. kda_bwd_sweep_kernel, one (direction, b, h, 16 value columns) per workgroup
 //     (columns of the state evolve independently): forwards the states at every
-//     chunk start, S_{n+1} = Diag(Gc) S_n - Kb^T (W S_n) + b; backwards the state
+//     chunk start, S_{n+1} = Diag(Gc) S_n - Kb^T (W S_n - U~); backwards the state
 //     gradients, dS_n = Diag(Gc) dS_{n+1} - W^T (Kb dS_{n+1}) + R (the transposed
 //     map).  R does not depend on the states, so the two directions run at once.
 //  3. kda_bwd_grad_kernel, one workgroup per chunk: the adjoint of the chunk's steps
@@ -43,12 +43,13 @@ constexpr int TILE = 16;          // value columns per sweep workgroup
 
 __device__ __forceinline__ float ex(float x) { return fast_exp2(x * kLog2e); }
 
-// fp32 offsets of the per-chunk record written by the prep kernel.
+// fp32 offsets of the per-chunk record written by the chunk kernel (row-major blocks:
+// W, K-bar and U~ token x channel, R key channel x value column).
 template <int D>
 struct Rec {
     static constexpr int64_t CD = (int64_t)C * D, DD = (int64_t)D * D;
-    static constexpr int64_t W = 0, KBAR = CD, BV = 2 * CD, R = 2 * CD + DD, GC = 2 * CD + 2 * DD;
-    static constexpr int64_t SIZE = 2 * CD + 2 * DD + D;
+    static constexpr int64_t W = 0, KBAR = CD, UT = 2 * CD, R = 3 * CD, GC = 3 * CD + DD;
+    static constexpr int64_t SIZE = 3 * CD + DD + D;
 };
 
 struct ChunkPos {
@@ -151,7 +152,8 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
         cbase = bh * NC;
         cstride = 1;
     }
-    const int64_t off_base = dir == 0 ? RC::BV : RC::R;
+    // forwards: U~ (rows of Y); backwards: R (rows of the state)
+    const int64_t off_base = dir == 0 ? RC::UT : RC::R;
     const int lane = lane_id(), wave = wave_id();
     const int m = lane & 15, g = lane >> 4;
     // the record of step i (chunk i forwards, NC - 1 - i backwards), clamped to the last step
@@ -183,8 +185,9 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
         for (int i = 0; i < L::NW4; ++i) stage_one(buf, i);
     };
     static_assert(L::NW4 == D / 16, "one staged pair of float4 per K-block of Y");
-    // this lane's state rows 16 (wave + j (NT / 64)) + 4 g + r: offset (column col0 + m)
-    // and Gamma_C, in two register sets
+    // this lane's rows 16 (wave + j (NT / 64)) + 4 g + r, column col0 + m, in two register
+    // sets: Gamma_C of its state rows, and the offset: backwards R of its state rows,
+    // forwards U~ of its rows of Y (j = 0; the state update takes none)
     float oA[RBW][4], gA[RBW][4], oB[RBW][4], gB[RBW][4];
 #pragma unroll
     for (int j = 0; j < RBW; ++j)
@@ -196,7 +199,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int row = 16 * (wave + j * (NT / 64)) + 4 * g + r;
-                o[j][r] = tr[off_base + (int64_t)row * D + col0 + m];
+                o[j][r] = (dir == 1 || j == 0) ? tr[off_base + (int64_t)row * D + col0 + m] : 0.f;
                 gm[j][r] = tr[RC::GC + row];
             }
     };
@@ -210,7 +213,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
             const int c = idx / TILE, j = idx - c * TILE;
             out[c * D + col0 + j] = St[c * TP + j];
         }
-        // Y = W S (forwards) or Kb dS (backwards): wave w owns rows 16 w ..
+        // Y = W S - U~ (forwards) or Kb dS (backwards): wave w owns rows 16 w ..
         const float* A1 = buf + (dir == 0 ? L::W : L::KBAR);
         const float* A2 = buf + (dir == 0 ? L::KBAR : L::W);
         // chunk i + 1 goes into the other buffer (read by step i - 1, which every wave has
@@ -218,8 +221,10 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
         // then chunk i + 2's W and K-bar into the registers
         float* nbuf = lds + ((i + 1) & 1) * L::BUF;
         {
-            // two accumulator chains (even and odd K-blocks), summed at the end
+            // two accumulator chains (even and odd K-blocks), summed at the end; forwards the
+            // first starts from -U~
             floatx4 acc0 = zero4(), acc1 = zero4();
+            if (dir == 0) acc0 = floatx4{-o[0][0], -o[0][1], -o[0][2], -o[0][3]};
 #pragma unroll
             for (int kk = 0; kk < D / 16; ++kk) {
                 const int k0 = 16 * kk + 4 * g;
@@ -238,8 +243,8 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
         }
         fetch_wk(rec(i + 2));
         __syncthreads();  // Y and the staged chunk are complete
-        // state <- Diag(Gc) state - A2^T Y + offset, row blocks wave, wave + 4, .. (their
-        // accumulator chains interleaved)
+        // state <- Diag(Gc) state - A2^T Y (+ R backwards), row blocks wave, wave + 4, ..
+        // (their accumulator chains interleaved)
         floatx4 acc[RBW];
 #pragma unroll
         for (int j = 0; j < RBW; ++j) acc[j] = zero4();
@@ -262,7 +267,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int row = 16 * rb + 4 * g + r;
-                St[row * TP + m] = gm[j][r] * St[row * TP + m] - acc[j][r] + o[j][r];
+                St[row * TP + m] = gm[j][r] * St[row * TP + m] - acc[j][r] + (dir == 1 ? o[j][r] : 0.f);
             }
         }
         fetch_rows(rec(i + 2), o, gm);
@@ -613,37 +618,28 @@ __global__ __launch_bounds__(64 * (D / 16)) void kda_bwd_chunk_kernel(BwdParams 
             kbv[ma][i] = sk[r * DP + c] * ex(gC - sg[r * DP + c]);
             tr[RC::W + r * D + c] = Wt[ma][i];
             tr[RC::KBAR + r * D + c] = kbv[ma][i];
+            tr[RC::UT + r * D + c] = Ut[ma][i];
         }
     if (g == 0) tr[RC::GC + c] = ex(gC);
-    __syncthreads();  // k, q no longer read: their blocks take Kb and Qe
+    __syncthreads();  // q no longer read: its block takes Qe
 #pragma unroll
     for (int ma = 0; ma < 4; ++ma)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int r = 16 * ma + 4 * g + i;
-            sk[r * DP + c] = kbv[ma][i];
-            sq[r * DP + c] = Qe[ma][i];
-        }
+        for (int i = 0; i < 4; ++i) sq[(16 * ma + 4 * g + i) * DP + c] = Qe[ma][i];
     __syncthreads();
-    // b = Kb^T U~ and R = Qe^T dO: rows = key channels (D / 16 blocks), columns c
+    // R = Qe^T dO: rows = key channels (D / 16 blocks), columns c
 #pragma unroll 2
     for (int mb = 0; mb < D / 16; ++mb) {
-        floatx4 ab = zero4(), ar = zero4();
+        floatx4 ar = zero4();
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
             const int r0 = 16 * t + 4 * g;
-            const float4 kb4 = make_float4(sk[(r0 + 0) * DP + 16 * mb + l], sk[(r0 + 1) * DP + 16 * mb + l],
-                                           sk[(r0 + 2) * DP + 16 * mb + l], sk[(r0 + 3) * DP + 16 * mb + l]);
             const float4 qe4 = make_float4(sq[(r0 + 0) * DP + 16 * mb + l], sq[(r0 + 1) * DP + 16 * mb + l],
                                            sq[(r0 + 2) * DP + 16 * mb + l], sq[(r0 + 3) * DP + 16 * mb + l]);
-            ab = mma4(kb4, f4(Ut[t]), ab);
             ar = mma4(qe4, dob[t], ar);
         }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            tr[RC::BV + (16 * mb + 4 * g + i) * D + c] = ab[i];
-            tr[RC::R + (16 * mb + 4 * g + i) * D + c] = ar[i];
-        }
+        for (int i = 0; i < 4; ++i) tr[RC::R + (16 * mb + 4 * g + i) * D + c] = ar[i];
     }
 }
 

@@ -322,10 +322,10 @@ int kda_combine_states(const kda_combine_args *a, hipStream_t stream);
  *     bits give KDA_ERR_UNSUPPORTED.
  *   workspace: at least kda_chunk_bwd_workspace_size bytes, 256-byte aligned.
  *     Per (b, h, 64-token chunk) it holds, in fp32 and each section rounded up
- *     to 256 bytes: a record for the state sweeps (2*64*Dk + 2*Dk*Dv + Dk
+ *     to 256 bytes: a record for the state sweeps (3*64*Dk + Dk*Dv + Dk
  *     floats), a record for the gradient kernel (64*Dk + 3*64*64 floats), the
  *     state at the chunk's start and its gradient at the chunk's end (Dk*Dv
- *     floats each): 400.5 KiB per chunk at Dk = Dv = 128, e.g. 200 MiB for
+ *     floats each): 368.5 KiB per chunk at Dk = Dv = 128, e.g. 184.3 MiB for
  *     B1 H8 T4096.
  * No output may overlap an input or another output.
  */

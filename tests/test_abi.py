@@ -394,7 +394,7 @@ def _good_bwd(B=1, T=100, H=2, D=128):
 
 
 def test_bwd_workspace_size(lib):
-    """Per (b, h, chunk of 64): the sweep's record (2 x 64 x D + 2 x D x D + D floats), the
+    """Per (b, h, chunk of 64): the sweep's record (3 x 64 x D + D x D + D floats), the
     pair record (64 x D + 3 x 64 x 64 floats), the state at the chunk start and the
     gradient at its end (D x D floats each), every section rounded up to 256 bytes."""
     r256 = lambda x: (x + 255) // 256 * 256
@@ -403,7 +403,7 @@ def test_bwd_workspace_size(lib):
         n = ctypes.c_size_t(0)
         assert lib.kda_chunk_bwd_workspace_size(ctypes.byref(a), ctypes.byref(n)) == _abi.KDA_OK
         items = B * H * ((T + 63) // 64)
-        rec = 2 * 64 * D + 2 * D * D + D
+        rec = 3 * 64 * D + D * D + D
         pairs = 64 * D + 3 * 64 * 64
         want = r256(items * rec * 4) + r256(items * pairs * 4) + 2 * r256(items * D * D * 4)
         assert n.value == want
@@ -459,7 +459,7 @@ def test_bwd_varlen_workspace_size(lib):
         assert lib.kda_chunk_bwd_varlen_workspace_size(ctypes.byref(a), ctypes.byref(n)) == _abi.KDA_OK
         chunks = (rows + 63) // 64 + N
         items = H * chunks
-        rec = 2 * 64 * D + 2 * D * D + D
+        rec = 3 * 64 * D + D * D + D
         pairs = 64 * D + 3 * 64 * 64
         want = r256(items * rec * 4) + r256(items * pairs * 4) + 2 * r256(items * D * D * 4)
         want += 2 * r256((N + 1) * 8) + r256(chunks * 4)
