@@ -89,13 +89,14 @@ __device__ __forceinline__ int64_t elem(const BwdParams& p, const ChunkPos& cp, 
 }
 
 // LDS of the sweep kernel (fp32 offsets): two buffers of one chunk's W and K-bar (row
-// pitch D + 4), the state tile and Y (row pitch 20).  The pitches put the four lane
-// groups of an MFMA operand read on disjoint banks.
+// pitch D + 4), the state tile and Y, both transposed (one row per value column, pitch
+// D + 4 and C + 4), so that an MFMA's B operand and a lane's four accumulator rows are
+// 16-byte accesses.  The pitches put the lanes of a 16-lane group on disjoint banks.
 template <int D>
 struct SweepLds {
-    static constexpr int DP = D + 4, TP = 20;
+    static constexpr int DP = D + 4, SP = D + 4, YP = C + 4;
     static constexpr int W = 0, KBAR = C * DP, BUF = 2 * C * DP;  // within a buffer
-    static constexpr int ST = 2 * BUF, Y = ST + D * TP, TOTAL = Y + C * TP;
+    static constexpr int ST = 2 * BUF, Y = ST + TILE * SP, TOTAL = Y + TILE * YP;
     static constexpr int NW4 = C * D / 4 / NT;    // float4 of W (and of K-bar) per thread
     static_assert(TOTAL * 4 <= 160 * 1024, "sweep LDS");
 };
@@ -120,7 +121,7 @@ template <int D>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void kda_bwd_sweep_kernel(BwdParams p) {
     using RC = Rec<D>;
     using L = SweepLds<D>;
-    constexpr int DP = L::DP, TP = L::TP;
+    constexpr int DP = L::DP, SP = L::SP, YP = L::YP;
     constexpr int RBW = D / 16 / (NT / 64);  // row blocks of the state per wave
     extern __shared__ __align__(16) float lds[];
     float* St = lds + L::ST;
@@ -203,16 +204,24 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
                 gm[j][r] = tr[RC::GC + row];
             }
     };
+    // the state tile to its (row-major, D x D) place in HBM, four columns of a row per
+    // 16-byte store
+    static_assert(D * TILE % (4 * NT) == 0, "whole float4 of the tile per thread");
+    auto put_state = [&](float* out) __attribute__((always_inline)) {
+#pragma unroll
+        for (int q = 0; q < D * TILE / 4 / NT; ++q) {
+            const int idx = threadIdx.x + q * NT, c = idx >> 2, j = 4 * (idx & 3);
+            *reinterpret_cast<float4*>(out + c * D + col0 + j) =
+                make_float4(St[j * SP + c], St[(j + 1) * SP + c], St[(j + 2) * SP + c], St[(j + 3) * SP + c]);
+        }
+    };
     // step i: the state of its chunk out, Y = A1 S, chunk i + 1 staged, the new state from
     // the rows in (o, gm), which then take chunk i + 2's
     auto step = [&](int64_t i, float (&o)[RBW][4], float (&gm)[RBW][4]) __attribute__((always_inline)) {
         const int64_t n = dir == 0 ? i : NC - 1 - i;
         const float* buf = lds + (i & 1) * L::BUF;
         float* out = (dir == 0 ? p.states : p.dstates) + (cbase + n * cstride) * DD;
-        for (int idx = threadIdx.x; idx < D * TILE; idx += NT) {
-            const int c = idx / TILE, j = idx - c * TILE;
-            out[c * D + col0 + j] = St[c * TP + j];
-        }
+        put_state(out);
         // Y = W S - U~ (forwards) or Kb dS (backwards): wave w owns rows 16 w ..
         const float* A1 = buf + (dir == 0 ? L::W : L::KBAR);
         const float* A2 = buf + (dir == 0 ? L::KBAR : L::W);
@@ -229,17 +238,17 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
             for (int kk = 0; kk < D / 16; ++kk) {
                 const int k0 = 16 * kk + 4 * g;
                 const float4 av = *reinterpret_cast<const float4*>(A1 + (16 * wave + m) * DP + k0);
+                const float4 bv = *reinterpret_cast<const float4*>(St + m * SP + k0);
                 const float a[4] = {av.x, av.y, av.z, av.w};
-                const float b[4] = {St[(k0 + 0) * TP + m], St[(k0 + 1) * TP + m], St[(k0 + 2) * TP + m],
-                                    St[(k0 + 3) * TP + m]};
+                const float b[4] = {bv.x, bv.y, bv.z, bv.w};
                 if (kk & 1)
                     acc1 = mma16x4(a, b, acc1);
                 else
                     acc0 = mma16x4(a, b, acc0);
                 stage_one(nbuf, kk);
             }
-#pragma unroll
-            for (int r = 0; r < 4; ++r) Y[(16 * wave + 4 * g + r) * TP + m] = acc0[r] + acc1[r];
+            *reinterpret_cast<float4*>(Y + m * YP + 16 * wave + 4 * g) =
+                make_float4(acc0[0] + acc1[0], acc0[1] + acc1[1], acc0[2] + acc1[2], acc0[3] + acc1[3]);
         }
         fetch_wk(rec(i + 2));
         __syncthreads();  // Y and the staged chunk are complete
@@ -251,8 +260,8 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
 #pragma unroll
         for (int kk = 0; kk < C / 16; ++kk) {
             const int k0 = 16 * kk + 4 * g;
-            const float b[4] = {Y[(k0 + 0) * TP + m], Y[(k0 + 1) * TP + m], Y[(k0 + 2) * TP + m],
-                                Y[(k0 + 3) * TP + m]};
+            const float4 yv = *reinterpret_cast<const float4*>(Y + m * YP + k0);
+            const float b[4] = {yv.x, yv.y, yv.z, yv.w};
 #pragma unroll
             for (int j = 0; j < RBW; ++j) {
                 const int rb = wave + j * (NT / 64);
@@ -263,12 +272,14 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
         }
 #pragma unroll
         for (int j = 0; j < RBW; ++j) {
-            const int rb = wave + j * (NT / 64);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int row = 16 * rb + 4 * g + r;
-                St[row * TP + m] = gm[j][r] * St[row * TP + m] - acc[j][r] + (dir == 1 ? o[j][r] : 0.f);
-            }
+            float4* sp = reinterpret_cast<float4*>(St + m * SP + 16 * (wave + j * (NT / 64)) + 4 * g);
+            float4 sv = *sp;
+            const bool off = dir == 1;
+            sv.x = gm[j][0] * sv.x - acc[j][0] + (off ? o[j][0] : 0.f);
+            sv.y = gm[j][1] * sv.y - acc[j][1] + (off ? o[j][1] : 0.f);
+            sv.z = gm[j][2] * sv.z - acc[j][2] + (off ? o[j][2] : 0.f);
+            sv.w = gm[j][3] * sv.w - acc[j][3] + (off ? o[j][3] : 0.f);
+            *sp = sv;
         }
         fetch_rows(rec(i + 2), o, gm);
         __syncthreads();  // the new state is complete; buffer i % 2 is no longer read
@@ -277,7 +288,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
         const float* init = dir == 0 ? p.s0 : p.dsT;
         for (int idx = threadIdx.x; idx < D * TILE; idx += NT) {
             const int c = idx / TILE, j = idx - c * TILE;
-            St[c * TP + j] = init ? init[bh * DD + c * D + col0 + j] : 0.f;
+            St[j * SP + c] = init ? init[bh * DD + c * D + col0 + j] : 0.f;
         }
         if (NC > 0) {
             fetch_wk(rec(0));
@@ -294,12 +305,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
         }
         if (i < NC) step(i, oA, gA);
     }
-    if (dir == 1 && p.ds0) {
-        for (int idx = threadIdx.x; idx < D * TILE; idx += NT) {
-            const int c = idx / TILE, j = idx - c * TILE;
-            p.ds0[bh * DD + c * D + col0 + j] = St[c * TP + j];
-        }
-    }
+    if (dir == 1 && p.ds0) put_state(p.ds0 + bh * DD);
 }
 
 // fp32 offsets of the per-chunk pair record the chunk kernel leaves for the gradient
