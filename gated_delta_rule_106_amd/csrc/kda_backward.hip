@@ -109,13 +109,13 @@ __device__ __forceinline__ floatx4 mma16x4(const float (&a)[4], const float (&b)
     return acc;
 }
 
-// Forwards: S <- Diag(Gc) S - Kb^T (W S) + b; backwards: dS <- Diag(Gc) dS - W^T (Kb dS) + R.
+// Forwards: S <- Diag(Gc) S - Kb^T (W S - U~); backwards: dS <- Diag(Gc) dS - W^T (Kb dS) + R.
 // One workgroup runs one direction.  Both products run on the fp32 MFMA: wave w
 // forms rows 16 w .. 16 w + 15 of Y, then row blocks w, w + 4, .. of the new state.
 // Chunk i + 1's W and K-bar are staged into the other LDS buffer while chunk i's products
-// run (from registers loaded one chunk earlier), and each lane keeps the offset and
-// Gamma_C entries of its own state rows in registers, loaded two chunks ahead: two
-// barriers per chunk.  Loads past the last chunk repeat the last one (same bytes), so
+// run (from registers loaded one chunk earlier), and each lane keeps the offset (U~ of its
+// rows of Y, or R of its state rows) and Gamma_C entries in registers, loaded two chunks
+// ahead: two barriers per chunk.  Loads past the last chunk repeat the last one (same bytes), so
 // that every chunk issues the same loads.
 template <int D>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void kda_bwd_sweep_kernel(BwdParams p) {
@@ -408,8 +408,8 @@ struct ChunkL {
 // Chunk kernel: one workgroup of D / 16 waves per (b, h, chunk).  From the chunk's
 // inputs: g, the pair blocks Bm (strictly lower) and P (lower), Li = (I + diag(beta) Bm)^-1,
 // then, wave w on the value (or key) columns 16 w .. 16 w + 15: W = Li diag(beta) Kt,
-// U~ = Li diag(beta) V, Qe = Qt - P W, Kb, Gamma_C, b = Kb^T U~ and R = Qe^T dO.  Writes
-// the sweep's record (W, Kb, b, R, Gamma_C) and the pair record (g, Li, P, Bm).
+// U~ = Li diag(beta) V, Qe = Qt - P W, Kb, Gamma_C and R = Qe^T dO.  Writes the sweep's
+// record (W, Kb, U~, R, Gamma_C) and the pair record (g, Li, P, Bm).
 // Pairs: block (a, b) is a product over the channels with a reference point rho between
 // the two tiles, k_r e^{g_r - rho} against k_s e^{rho - g_s}: the end of tile a - 1 for
 // b < a (both factors <= 1), token 7 of the tile for a diagonal block (each factor spans
