@@ -729,8 +729,10 @@ __device__ __forceinline__ uint32_t lds_offset(const void* p) { return (uint32_t
 // PF: one more wave that touches the cards (and gate rows) of chunk n + 2 + kPfAhead in
 // iteration n, a G-th of each card per workgroup, so that the producers' and the output
 // wave's loads of cards the card builder wrote long before (no longer in the Infinity
-// Cache) find them in the L2 their XCD shares.
-constexpr int kPfAhead = 4;
+// Cache) find them in the L2 their XCD shares.  Two chunks beyond the producers' copies:
+// 1, 2, 3, 4, 6 and 8 gave 1 395, 1 387, 1 399, 1 397, 1 424 and 1 449 us for B1 H16
+// T65536 in pieces of 128 chunks (the touched lines must still be in the L2 when read).
+constexpr int kPfAhead = 2;
 
 // Workgroup `bid` of the `nblk` (a multiple of 8) state-pass workgroups of a launch;
 // waves past the roles (and the prefetch wave) only keep the barrier count.
