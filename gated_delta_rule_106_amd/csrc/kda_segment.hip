@@ -105,18 +105,20 @@ __global__ __launch_bounds__(D * 4) void kda_combine_kernel(CombineParams p) {
         // written again only after the next step's barrier, when every wave has read it
         lds_barrier();
     };
-    if (p.P > 0) {
-        load_seg(0, M0, b0);
-        load_seg(1, M1, b1);
-    }
-
     // the tile of the incoming state, one float4 per thread (D x 16 = 4 NTH floats), read
-    // before anything of this tile is written, so the final state may alias it
-    {
-        const float4 v = p.s0 ? *reinterpret_cast<const float4*>(p.s0 + unit * DD + (int64_t)tr * D + col0 + tc)
-                              : make_float4(0.f, 0.f, 0.f, 0.f);
-        *reinterpret_cast<float4*>(&S[tr * kPad + tc]) = v;
+    // before anything of this tile is written, so the final state may alias it; loaded
+    // before the first segments' rows, so that the wait for it leaves theirs in flight
+    const float4 v0 = p.s0 ? *reinterpret_cast<const float4*>(p.s0 + unit * DD + (int64_t)tr * D + col0 + tc)
+                           : make_float4(0.f, 0.f, 0.f, 0.f);
+    float* const sT = p.sT ? p.sT + unit * DD + (int64_t)tr * D + col0 + tc : nullptr;
+    if (p.P == 0) {  // no segment: the state passes through (the whole workgroup leaves)
+        if (sT) *reinterpret_cast<float4*>(sT) = v0;
+        return;
     }
+    // unconditional on every path, so that the wait for the state tile leaves them in flight
+    load_seg(0, M0, b0);
+    load_seg(1, M1, b1);
+    *reinterpret_cast<float4*>(&S[tr * kPad + tc]) = v0;
     __syncthreads();
     int64_t s = 0;
     for (; s + 3 <= p.P; s += 3) {  // the register sets in turn; every step of a trip runs
@@ -126,9 +128,7 @@ __global__ __launch_bounds__(D * 4) void kda_combine_kernel(CombineParams p) {
     }
     if (s < p.P) step(s, M0, b0, M2, b2);
     if (s + 1 < p.P) step(s + 1, M1, b1, M0, b0);
-    if (p.sT)
-        *reinterpret_cast<float4*>(p.sT + unit * DD + (int64_t)tr * D + col0 + tc) =
-            *reinterpret_cast<const float4*>(&S[(p.P & 1) * D * kPad + tr * kPad + tc]);
+    if (sT) *reinterpret_cast<float4*>(sT) = *reinterpret_cast<const float4*>(&S[(p.P & 1) * D * kPad + tr * kPad + tc]);
 }
 
 // M = I and b = 0 for every (b, h): one workgroup per (b, h)
