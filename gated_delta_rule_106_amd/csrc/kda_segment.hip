@@ -9,8 +9,9 @@
 // independent of the segment lengths.
 //
 // One workgroup per ((b, h), 16-column tile of the state): the tile (D x 16 fp32)
-// stays in LDS across the segments (two buffers, read one, write the other: one
-// barrier per segment); D / 16 waves each own one block of 16 rows and
+// stays in LDS across the segments, transposed (one row per column, so that an MFMA's B
+// operand and a lane's four result rows are 16-byte accesses), in two buffers (read one,
+// write the other: one barrier per segment); D / 16 waves each own one block of 16 rows and
 // form it with the fp32 MFMA (v_mfma_f32_16x16x4_f32) from its rows of M_p (held in
 // registers as float4 A operands) and b_p (the starting accumulator).  Three register
 // sets rotate: the rows of M_{p+1} and M_{p+2} (and b) are in flight while segment p
@@ -24,7 +25,10 @@
 namespace kda {
 namespace seg {
 
-constexpr int kPad = 20;  // LDS row pitch (floats): lane groups land on disjoint banks
+// LDS pitch (floats) of the transposed tile's rows: the lanes of a 16-lane group land on
+// disjoint banks
+template <int D>
+constexpr int kPitch = D + 4;
 
 // 16 k-steps of the fp32 MFMA: k = 16 kk + 4 g + c, c = 0..3 (A[m][k] from a.c,
 // B[k][m] from b[c]); both operands use the same assignment of k.
@@ -42,7 +46,8 @@ __global__ __launch_bounds__(D * 4) void kda_combine_kernel(CombineParams p) {
     constexpr int NK = D / 16;  // 16-wide k steps of one row block
     static_assert(NK % 2 == 0, "two accumulator chains");
     constexpr int NTH = D * 4;  // threads
-    __shared__ __align__(16) float S[2 * D * kPad];
+    constexpr int SP = kPitch<D>;
+    __shared__ __align__(16) float S[2 * 16 * SP];
     const int lane = lane_id(), wave = wave_id();
     const int m = lane & 15, g = lane >> 4;
     // consecutive workgroups go to different XCDs; the NT tiles of one (b, h), which all
@@ -59,6 +64,10 @@ __global__ __launch_bounds__(D * 4) void kda_combine_kernel(CombineParams p) {
     static_assert(D * 16 == 4 * NTH, "one float4 of the tile per thread");
     const int tr = threadIdx.x >> 2, tc = 4 * (threadIdx.x & 3);  // row, first column
 
+    // four columns tc .. tc + 3 of row tr of a (transposed) state tile
+    auto row4 = [&](const float* St) __attribute__((always_inline)) {
+        return make_float4(St[tc * SP + tr], St[(tc + 1) * SP + tr], St[(tc + 2) * SP + tr], St[(tc + 3) * SP + tr]);
+    };
     // this wave's 16 rows of M_s (as MFMA A operands) and its b_s accumulator start, in
     // three register sets: segments s + 1 and s + 2 load while segment s is combined
     float4 M0[NK], M1[NK], M2[NK];
@@ -78,19 +87,14 @@ __global__ __launch_bounds__(D * 4) void kda_combine_kernel(CombineParams p) {
     auto step = [&](int64_t s, const float4(&Ma)[NK], const floatx4& bb, float4(&Mn)[NK], floatx4& bn)
         __attribute__((always_inline)) {
         load_seg(s + 2, Mn, bn);
-        const float* Sc = S + (s & 1) * D * kPad;
-        float* Sn = S + ((s + 1) & 1) * D * kPad;
-        if (p.seg) {
-            float* dst = p.seg + (s * p.units + unit) * DD;
-            *reinterpret_cast<float4*>(dst + (int64_t)tr * D + col0 + tc) =
-                *reinterpret_cast<const float4*>(&Sc[tr * kPad + tc]);
-        }
+        const float* Sc = S + (s & 1) * 16 * SP;
+        float* Sn = S + ((s + 1) & 1) * 16 * SP;
+        if (p.seg) *reinterpret_cast<float4*>(p.seg + (s * p.units + unit) * DD + (int64_t)tr * D + col0 + tc) = row4(Sc);
         floatx4 sv[NK];  // every B operand of the step read first: one wait on LDS
 #pragma unroll
         for (int kk = 0; kk < NK; ++kk) {
-            const int k0 = 16 * kk + 4 * g;
-            sv[kk] = floatx4{Sc[(k0 + 0) * kPad + m], Sc[(k0 + 1) * kPad + m], Sc[(k0 + 2) * kPad + m],
-                             Sc[(k0 + 3) * kPad + m]};
+            const float4 v = *reinterpret_cast<const float4*>(Sc + m * SP + 16 * kk + 4 * g);
+            sv[kk] = floatx4{v.x, v.y, v.z, v.w};
         }
         __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of the products
         floatx4 acc0 = bb, acc1 = zero4();  // two chains over alternate k blocks
@@ -99,8 +103,8 @@ __global__ __launch_bounds__(D * 4) void kda_combine_kernel(CombineParams p) {
             acc0 = mma16(Ma[kk], sv[kk], acc0);
             acc1 = mma16(Ma[kk + 1], sv[kk + 1], acc1);
         }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) Sn[(crow + i) * kPad + m] = acc0[i] + acc1[i];
+        *reinterpret_cast<float4*>(Sn + m * SP + crow) =
+            make_float4(acc0[0] + acc1[0], acc0[1] + acc1[1], acc0[2] + acc1[2], acc0[3] + acc1[3]);
         // S_{s+1} is complete (the later segments' loads stay in flight); buffer s % 2 is
         // written again only after the next step's barrier, when every wave has read it
         lds_barrier();
@@ -118,7 +122,10 @@ __global__ __launch_bounds__(D * 4) void kda_combine_kernel(CombineParams p) {
     // unconditional on every path, so that the wait for the state tile leaves them in flight
     load_seg(0, M0, b0);
     load_seg(1, M1, b1);
-    *reinterpret_cast<float4*>(&S[tr * kPad + tc]) = v0;
+    S[tc * SP + tr] = v0.x;
+    S[(tc + 1) * SP + tr] = v0.y;
+    S[(tc + 2) * SP + tr] = v0.z;
+    S[(tc + 3) * SP + tr] = v0.w;
     __syncthreads();
     int64_t s = 0;
     for (; s + 3 <= p.P; s += 3) {  // the register sets in turn; every step of a trip runs
@@ -128,7 +135,7 @@ __global__ __launch_bounds__(D * 4) void kda_combine_kernel(CombineParams p) {
     }
     if (s < p.P) step(s, M0, b0, M2, b2);
     if (s + 1 < p.P) step(s + 1, M1, b1, M0, b0);
-    if (sT) *reinterpret_cast<float4*>(sT) = *reinterpret_cast<const float4*>(&S[(p.P & 1) * D * kPad + tr * kPad + tc]);
+    if (sT) *reinterpret_cast<float4*>(sT) = row4(S + (p.P & 1) * 16 * SP);
 }
 
 // M = I and b = 0 for every (b, h): one workgroup per (b, h)
