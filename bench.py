@@ -167,14 +167,15 @@ def time_calls(fn, sets, steps, warmup, stream):
     return wall, e0.elapsed_time(e1) / steps
 
 
-def prefill_sets(kda, wl, n_sets, dev):
+def prefill_sets(kda, wl, n_sets, dev, out_dtype=None):
     import torch
     from kda_workloads import make_inputs
+    out_dtype = torch.float32 if out_dtype is None else out_dtype
     sets = []
     ws_n = kda.workspace_bytes(wl.B, wl.T, wl.H, wl.Dk, dtype=wl.torch_dtype, chunk=wl.chunk)
     for i in range(n_sets):
         x = to_dev(make_inputs(wl, seed=wl.seed + 100 * i), dev)
-        x["out"] = torch.empty((wl.B, wl.T, wl.H, wl.Dv), dtype=torch.float32, device=dev)
+        x["out"] = torch.empty((wl.B, wl.T, wl.H, wl.Dv), dtype=out_dtype, device=dev)
         x["ws"] = torch.empty(max(ws_n, 16), dtype=torch.uint8, device=dev)
         x["final"] = (torch.empty((wl.B, wl.H, wl.Dk, wl.Dv), dtype=torch.float32, device=dev)
                       if wl.final_state else None)
@@ -186,7 +187,7 @@ def prefill_call(kda, wl):
     def fn(x):
         kda.chunk_fwd(*(x[k] for k in KEYS), initial_state=x.get("initial_state"),
                       output_final_state=wl.final_state, chunk=wl.chunk, out=x["out"],
-                      final_state=x["final"], workspace=x["ws"])
+                      out_dtype=x["out"].dtype, final_state=x["final"], workspace=x["ws"])
     return fn
 
 
@@ -239,6 +240,24 @@ def bench_prefill(kda, wl, steps, warmup, n_sets, dev, stream):
         f"({100 * res['hbm_frac']:.1f} % of HBM peak), {100 * res['mfma_frac']:.2f} % MFMA alg")
     del sets
     return res, wall
+
+
+def bench_bf16_output(kda, wl, steps, warmup, n_sets, dev, stream):
+    """The same prefill call with y written in bf16 (the input dtype) instead of the
+    default fp32: the bytes the call moves then equal the algorithmic count.  The
+    default stays fp32 because rounding y to bf16 alone costs more than the 2e-2
+    max-error-to-RMS budget on these outputs."""
+    import torch
+    sets = prefill_sets(kda, wl, n_sets, dev, out_dtype=torch.bfloat16)
+    wall, ev_ms = time_calls(prefill_call(kda, wl), sets, steps, warmup, stream)
+    del sets
+    nbytes = prefill_bytes(wl)
+    res = {"workload": wl.name, "out_dtype": "bf16", "input_sets": n_sets, "kernel_ms_mean": ev_ms,
+           "tokens_per_s": wl.B * wl.T / (ev_ms / 1e3), "hbm_gbs": nbytes / (ev_ms / 1e3) / 1e9}
+    res["hbm_frac"] = res["hbm_gbs"] / HBM_PEAK_GBS
+    log(f"prefill {wl.name}, bf16 y: {ev_ms * 1e3:.1f} us/call (events), "
+        f"{100 * res['hbm_frac']:.1f} % of HBM peak")
+    return res
 
 
 def bench_decode(kda, wl, steps, warmup, dev, stream):
@@ -583,9 +602,11 @@ def main():
     ap.add_argument("--no-varlen", action="store_true",
                     help="skip the mixed-length batch (variable-length call, snapshots)")
     ap.add_argument("--no-fused-prep", action="store_true",
-                    help="skip the headline prefill with the preparation fused in")
+                    help="skip B1 H8 T4096 with the preparation fused in")
     ap.add_argument("--no-backward", action="store_true",
-                    help="skip the backward pass on the headline shape")
+                    help="skip the backward pass on B1 H8 T4096")
+    ap.add_argument("--no-bf16-output", action="store_true",
+                    help="skip the headline prefill with y written in bf16")
     ap.add_argument("--no-context-parallel", action="store_true",
                     help="skip the per-GPU share of the context-parallel split")
     ap.add_argument("--segment-sweep", action="store_true",
@@ -625,6 +646,9 @@ def main():
     # the headline's inputs (1.6 GB) are far beyond the Infinity Cache: one input set
     pre, wall = bench_prefill(kda, head, args.steps, args.warmup, 1, dev, stream)
     torch.cuda.empty_cache()
+    if not args.no_bf16_output:
+        pre["bf16_output"] = bench_bf16_output(kda, head, args.steps, args.warmup, 1, dev, stream)
+        torch.cuda.empty_cache()
     dec = bench_decode(kda, CONFIGS[4], max(args.steps, 10), args.warmup, dev, stream)
     ctx = {}
     if not args.no_context:
