@@ -23,8 +23,8 @@ import torch
 
 from . import _abi
 
-__all__ = ["chunk_fwd", "chunk_bwd", "chunk_bwd_varlen", "chunk_fwd_varlen", "snapshot_slot", "chunk_summary", "combine_states", "decode_step", "workspace_bytes",
-           "library_path", "KDAError"]
+__all__ = ["chunk_fwd", "chunk_bwd", "chunk_bwd_varlen", "chunk_fwd_varlen", "snapshot_slot", "chunk_summary",
+           "combine_states", "decode_step", "workspace_bytes", "library_path", "KDAError"]
 
 
 class KDAError(RuntimeError):
@@ -190,8 +190,8 @@ def chunk_fwd_varlen(q, k, v, log_alpha, beta, gate, cu_seqlens, initial_state=N
     """Variable-length batch on the current HIP stream: N sequences packed along the
     rows of q, k, log_alpha [rows, H, Dk], v, gate [rows, H, Dv], beta [rows, H]
     (fp32 or bf16), sequence i being rows cu_seqlens[i] .. cu_seqlens[i+1] - 1 (int64
-    device tensor [N + 1]); ``chunk`` as for ``chunk_fwd`` (0: the default).  initial_state: fp32 [N, H, Dk, Dv] or None.  With
-    ``snapshot_every`` P > 0 (a multiple of 64) the state after every P tokens of
+    device tensor [N + 1]); ``chunk`` as for ``chunk_fwd`` (0: the default).
+    initial_state: fp32 [N, H, Dk, Dv] or None.  With ``snapshot_every`` P > 0 (a multiple of 64) the state after every P tokens of
     each sequence is returned in an fp32 [rows // P + N, H, Dk, Dv] tensor, the k-th
     of sequence i in slot ``snapshot_slot(cu_seqlens, i, k, P)``.  Returns
     (y [rows, H, Dv], final_state or None, snapshots or None); rows outside the

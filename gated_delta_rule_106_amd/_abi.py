@@ -24,8 +24,8 @@ KDA_FLAG_GATE_LOGITS = 8
 KDA_FLAG_CARDS_READY = 16
 
 # every extern "C" entry point of include/kda.h
-EXPORTS = ("kda_chunk_fwd_workspace_size", "kda_chunk_fwd", "kda_chunk_fwd_noalloc", "kda_chunk_fwd_varlen_workspace_size",
-           "kda_chunk_fwd_varlen", "kda_chunk_summary",
+EXPORTS = ("kda_chunk_fwd_workspace_size", "kda_chunk_fwd", "kda_chunk_fwd_noalloc",
+           "kda_chunk_fwd_varlen_workspace_size", "kda_chunk_fwd_varlen", "kda_chunk_summary",
            "kda_combine_states", "kda_chunk_bwd_workspace_size", "kda_chunk_bwd",
            "kda_chunk_bwd_varlen_workspace_size", "kda_chunk_bwd_varlen", "kda_decode_step", "kda_status_str",
            "kda_version")
