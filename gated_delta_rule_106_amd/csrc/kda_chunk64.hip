@@ -265,9 +265,9 @@ __device__ __forceinline__ void prep_tile(const PrepParams& p, unsigned char* sm
     const int m16 = lane & 15, g4 = lane >> 4;
     const int rl = 16 * A + m16;  // this lane's token within the chunk
     const int64_t H = p.H;
-    const bool clamp = p.clamp != 0;
     constexpr bool logits = (MODE & kModeLogits) != 0, qk_norm = (MODE & kModeQkNorm) != 0;
     constexpr bool wide = (MODE & kModeWide) != 0;
+    constexpr bool clamp = !wide;  // the wide mode is taken exactly when the clamp is off
     constexpr bool stream = (MODE & kModeStream) != 0;
 
     // raw inputs of token rl: per 32-channel block kb, the 8 bf16 channels 32 kb + 8 g4 .. +7
@@ -349,12 +349,15 @@ __device__ __forceinline__ void prep_tile(const PrepParams& p, unsigned char* sm
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
         half8 v16;
+        float et8[8];  // decay over the whole tile of this lane's eight channels
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             const float x = elem(rla[kb], j);
             float la = x;
             if constexpr (logits) la = log_sigmoid(x);
-            const float l = (clamp ? __builtin_amdgcn_fmed3f(la, kLogAlphaMin, 0.f) : la) * kLog2e;
+            // log2 units; clamping after the scaling gives the same bits (the scaling is
+            // monotone) and leaves no product for the scan's first add to fuse with
+            const float l = clamp ? __builtin_amdgcn_fmed3f(la * kLog2e, kLogAlphaMin * kLog2e, 0.f) : la * kLog2e;
             const float P = row_scan16(l);      // log2 decay from the tile start, inclusive
             const float E = fast_exp2(P);       // <= 1
             const float Et = row_last(E);       // decay over the whole tile
@@ -376,12 +379,17 @@ __device__ __forceinline__ void prep_tile(const PrepParams& p, unsigned char* sm
                 const float KC = kf * Einv;
                 accA = mma_f32_k4(KR, KC, accA);
                 accP = mma_f32_k4(QR, KC, accP);
-                ke16[kb][j] = static_cast<_Float16>(kf * (Einv * Et));  // decay from after this token to the tile end
+                ke16[kb][j] = static_cast<_Float16>(KC * Et);  // decay from after this token to the tile end
             }
             kr16[kb][j] = static_cast<_Float16>(KR);
             qr16[kb][j] = static_cast<_Float16>(QR);
             v16[j] = static_cast<_Float16>(elem(rv[kb], j));
-            s_etau[A * D + 32 * kb + 8 * g4 + j] = Et;  // the 16 lanes of a row store the same value
+            et8[j] = Et;
+        }
+        if (m16 == 0) {  // the 16 lanes of a row hold the same values
+            float* et = s_etau + A * D + 32 * kb + 8 * g4;
+            *reinterpret_cast<float4*>(et) = make_float4(et8[0], et8[1], et8[2], et8[3]);
+            *reinterpret_cast<float4*>(et + 4) = make_float4(et8[4], et8[5], et8[6], et8[7]);
         }
         // KE fragment of this tile: the B operand of the pairs (later tile, this tile)
         *reinterpret_cast<half8*>(s_ke + ((A * KB + kb) * 64 + lane) * 8) = ke16[kb];
