@@ -423,18 +423,22 @@ __device__ __forceinline__ void prep_tile(const PrepParams& p, unsigned char* sm
             et[a2][0] = lo.x; et[a2][1] = lo.y; et[a2][2] = lo.z; et[a2][3] = lo.w;
             et[a2][4] = hi.x; et[a2][5] = hi.y; et[a2][6] = hi.z; et[a2][7] = hi.w;
         }
-        half8 kt, kbar;
+        // decay before this tile and after it, formed in fp32 and applied to the fp16 operands
+        // as packed fp16 products
+        half8 erho, eaft;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            float erho = 1.f, eaft = 1.f;  // decay before this tile / after this tile
+            float e0 = 1.f, e1 = 1.f;
 #pragma unroll
-            for (int a2 = 0; a2 < A; ++a2) erho *= et[a2][j];
+            for (int a2 = 0; a2 < A; ++a2) e0 *= et[a2][j];
 #pragma unroll
-            for (int a2 = A + 1; a2 < NSUB; ++a2) eaft *= et[a2][j];
-            kt[j] = static_cast<_Float16>(static_cast<float>(kr16[kb][j]) * erho);    // K~ = k 2^{g}
-            q16[kb][j] = static_cast<_Float16>(static_cast<float>(qr16[kb][j]) * erho);  // Q~ = q 2^{g}
-            kbar[j] = static_cast<_Float16>(static_cast<float>(ke16[kb][j]) * eaft);  // Kbar = k 2^{g_C - g}
+            for (int a2 = A + 1; a2 < NSUB; ++a2) e1 *= et[a2][j];
+            erho[j] = static_cast<_Float16>(e0);
+            eaft[j] = static_cast<_Float16>(e1);
         }
+        const half8 kt = A == 0 ? kr16[kb] : kr16[kb] * erho;                // K~ = k 2^{g}
+        q16[kb] = A == 0 ? qr16[kb] : qr16[kb] * erho;                      // Q~ = q 2^{g}
+        const half8 kbar = A == NSUB - 1 ? ke16[kb] : ke16[kb] * eaft;      // Kbar = k 2^{g_C - g}
         put_transposed(s_kf, kb, kt);
         {
             const floatx4 t0 = mma_f16_k32(kbar, sel0, zero4());
@@ -449,10 +453,13 @@ __device__ __forceinline__ void prep_tile(const PrepParams& p, unsigned char* sm
 #pragma unroll
         for (int bb = A - 1; bb >= 0; --bb) {  // f = decay over the tiles strictly between bb and A
             const half8 keb = ld_h8(s_ke + ((bb * KB + kb) * 64 + lane) * 8);
-            half8 col;
+            half8 col = keb;
+            if (bb != A - 1) {
+                half8 fh;
 #pragma unroll
-            for (int j = 0; j < 8; ++j)
-                col[j] = (bb == A - 1) ? keb[j] : static_cast<_Float16>(static_cast<float>(keb[j]) * f[j]);
+                for (int j = 0; j < 8; ++j) fh[j] = static_cast<_Float16>(f[j]);
+                col = keb * fh;
+            }
             pa[bb] = mma_f16_k32(kr16[kb], col, pa[bb]);
             pp[bb] = mma_f16_k32(qr16[kb], col, pp[bb]);
             if (bb > 0) {
