@@ -230,7 +230,7 @@ def test_pipelined_pieces_ragged_with_state(B, H, T):
     last with two chunks and a ragged tail, two batch rows), and 521 chunks in pieces of
     128 (the last with nine chunks and a ragged tail); an initial and a final state;
     against the oracle and the single pass of every chunk's card at once (the
-    variable-length call takes the unpipelined path)."""
+    variable-length call takes the unpipelined path), and with y written in bf16."""
     wl = CONFIGS[2].scaled(B=B, H=H, T=T)
     x = make_inputs(wl, seed=81)
     say(f"[parity] pipelined pieces B{B} H{H} T{wl.T}")
@@ -244,6 +244,12 @@ def test_pipelined_pieces_ragged_with_state(B, H, T):
     torch.cuda.synchronize()
     # the same cards and the same chain arithmetic in both: equal bit for bit
     assert torch.equal(y.reshape(yv.shape), yv) and torch.equal(sT, sv)
+    # y written in bf16: the same fp32 values, rounded to nearest even at the store
+    y16, s16 = kda().chunk_fwd(*(d[k] for k in KEYS), initial_state=d["initial_state"], output_final_state=True,
+                               out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert y16.dtype == torch.bfloat16
+    assert torch.equal(y16, y.to(torch.bfloat16)) and torch.equal(s16, sT)
 
 
 def test_decode_chain_equals_prefill_and_handoff():
